@@ -1,0 +1,322 @@
+"""Plain float64 CPU oracle of the Pixtral-class vision tower.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and ``bench.py``'s ``cpu_baseline`` leg, never by the product path.  It shares
+no code, header, table or constant generator with the HIP library.
+
+Sources (cited by page title and section):
+
+* "Mistral 3" (KerasFormers model page).  The ``Mistral3VisionModel`` entry
+  describes the tower: a convolutional patch embedding, an RMS pre-norm, then
+  blocks with a two-dimensional rotary embedding, run over all images packed
+  into one variable-resolution patch sequence.  The ``Mistral3Model`` argument
+  table gives the vision width 1024, MLP width 4096, depth 24, 16 heads,
+  patch 14, rotary base 1e4, ``spatial_merge_size`` 2, a projector without
+  bias, and text width 5120; its description names the 2x2 patch-merging
+  projector.  The ``Mistral3ImageProcessor`` table gives the normalisation
+  mean/std.  "Several images in one conversation" says every image expands to
+  its own patch count.
+* "Pixtral-12B-2409" (inference-research model record), part (1) Vision and
+  the VISION TOKENS paragraph: patch 16, no spatial merge (one token per
+  patch), 1024x1024 tiles of 4,096 tokens, a 4096x4096 image as 16 tiles.
+* "nemo_automodel.components.models.mistral3_vlm" (NeMo Automodel API page),
+  ``forward``: the tower input is float ``pixel_values`` plus ``image_sizes``.
+
+Readings taken where the pages are silent (each is also listed in the design
+notes of the repository):
+
+1. MLP: gated SiLU with three bias-free matrices, down(silu(gate y) * up y).
+2. Pre-norm residual blocks; ``ln_pre`` after the patch embedding; no final
+   norm after the last block.
+3. 2-D RoPE on head_dim dh: dh/2 rotation pairs on adjacent dims (2j, 2j+1);
+   pairs j < dh/4 turn by the patch row r, pairs j >= dh/4 by the patch
+   column c, each axis with the ordinary 1-D ladder
+   omega_m = theta^(-2m/(dh/2)), m = 0..dh/4-1.  Positions are 0-based within
+   the image (tile).
+4. Attention scale 1/sqrt(dh), non-causal, block-diagonal per image.
+5. No biases anywhere.
+6. 2x2 merge concatenates window offsets (dy,dx) in order 00,01,10,11, channel
+   fastest; merged tokens row-major per image, images in input order.
+7. The projector is a single bias-free linear map 4*D -> out_dim.
+8. RMSNorm: x / sqrt(mean(x^2) + eps) * g with eps = 1e-5.
+
+Pinning: every function here is pinned in ``tests/test_oracle_pins.py`` by a
+check that does not reuse this code path (closed-form counts printed on the
+pages, direct convolution loops, textbook dense masked softmax, rotation
+identities, identity/zero weights).  The full tower against a trained model is
+parity unpinned: neither weights nor another implementation exist here.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class TowerConfig:
+    """Tower hyper-parameters ("Mistral 3", Mistral3Model argument table;
+    "Pixtral-12B-2409", part (1) Vision)."""
+
+    patch: int = 14
+    hidden: int = 1024
+    heads: int = 16
+    mlp: int = 4096
+    layers: int = 24
+    merge: int = 2  # 1 = no spatial merge (Pixtral-12B)
+    out_dim: int = 5120
+    rope_theta: float = 1.0e4
+    rms_eps: float = 1.0e-5
+
+    @property
+    def head_dim(self) -> int:
+        return self.hidden // self.heads
+
+    @property
+    def out_cols(self) -> int:
+        return self.out_dim if self.merge == 2 else self.hidden
+
+
+# --------------------------------------------------------------------------
+# a0: per-image counts and index maps
+# --------------------------------------------------------------------------
+def plan_maps(image_hw: Sequence[Sequence[int]], patch: int, merge: int) -> Dict[str, np.ndarray]:
+    """Patch counts, ``cu_seqlens``, (row, col) map and 2x2 merge source map.
+
+    "Mistral 3", Mistral3VisionModel (packed variable-resolution sequence) and
+    "Several images in one conversation" (each image keeps its own count);
+    "Pixtral-12B-2409", VISION TOKENS (one token per patch without merge).
+
+    Written as explicit loops over images, patches and merged tokens.
+    """
+    if merge not in (1, 2):
+        raise ValueError("merge must be 1 or 2")
+    cu = [0]
+    rc: List[List[int]] = []
+    src: List[List[int]] = []
+    for (h, w) in image_hw:
+        h, w = int(h), int(w)
+        if h <= 0 or w <= 0 or h % (patch * merge) or w % (patch * merge):
+            raise ValueError(f"image {h}x{w} is not on the {patch * merge}-pixel grid")
+        hp, wp = h // patch, w // patch
+        base = cu[-1]
+        for j in range(hp * wp):
+            rc.append([j // wp, j % wp])
+        if merge == 2:
+            for big_r in range(hp // 2):
+                for big_c in range(wp // 2):
+                    row = []
+                    for dy in (0, 1):
+                        for dx in (0, 1):
+                            row.append(base + (2 * big_r + dy) * wp + (2 * big_c + dx))
+                    src.append(row)
+        cu.append(base + hp * wp)
+    out = {
+        "cu_seqlens": np.asarray(cu, dtype=np.int64),
+        "patch_rc": np.asarray(rc, dtype=np.int64).reshape(-1, 2),
+        "n_patches": cu[-1],
+    }
+    if merge == 2:
+        out["merge_src"] = np.asarray(src, dtype=np.int64).reshape(-1, 4)
+        out["out_rows"] = len(src)
+    else:
+        out["out_rows"] = cu[-1]
+    return out
+
+
+# --------------------------------------------------------------------------
+# a1: convolutional patch embedding (stride = kernel = patch, no bias)
+# --------------------------------------------------------------------------
+def patch_embed(pixels: np.ndarray, image_hw, w_patch: np.ndarray, patch: int) -> np.ndarray:
+    """X[g, o] = sum_{c,u,v} W[o,c,u,v] * px_i[c, r*p+u, col*p+v].
+
+    "Mistral 3", Mistral3VisionModel (convolutional patch embedding).
+    ``pixels`` is the flat concatenation of each image's C x H x W plane set,
+    images in input order.  Each image's patches are cut out with a reshape
+    (the im2col rows, K order (c,u,v)) and multiplied by the flattened kernel.
+    """
+    w = np.asarray(w_patch, dtype=np.float64)
+    d = w.shape[0]
+    wmat = w.reshape(d, -1)
+    pix = np.asarray(pixels, dtype=np.float64).reshape(-1)
+    rows = []
+    off = 0
+    for (h, wd) in image_hw:
+        h, wd = int(h), int(wd)
+        img = pix[off: off + 3 * h * wd].reshape(3, h, wd)
+        off += 3 * h * wd
+        hp, wp = h // patch, wd // patch
+        cols = (img.reshape(3, hp, patch, wp, patch)
+                .transpose(1, 3, 0, 2, 4)
+                .reshape(hp * wp, 3 * patch * patch))
+        rows.append(cols @ wmat.T)
+    return np.concatenate(rows, axis=0)
+
+
+# --------------------------------------------------------------------------
+# a2/a3: RMSNorm
+# --------------------------------------------------------------------------
+def rms_norm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * g, per row ("Mistral 3", Mistral3VisionModel:
+    RMS pre-norm)."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(g, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# a5 (part): 2-D rotary position embedding
+# --------------------------------------------------------------------------
+def rope_omega(head_dim: int, theta: float) -> np.ndarray:
+    """Per-axis frequency ladder omega_m = theta^(-2m/(head_dim/2)),
+    m = 0..head_dim/4-1 (rotary base from "Mistral 3", Mistral3Model table,
+    vision_rope_theta; split between axes per reading 3)."""
+    per_axis = head_dim // 4
+    m = np.arange(per_axis, dtype=np.float64)
+    return np.power(float(theta), -2.0 * m / (head_dim / 2.0))
+
+
+def rope_2d(x: np.ndarray, patch_rc: np.ndarray, heads: int, theta: float) -> np.ndarray:
+    """Rotate every head's adjacent pairs (2j, 2j+1) by the patch's row (first
+    half of the pairs) or column (second half) times omega.
+
+    "Mistral 3", Mistral3VisionModel (2-D rotary blocks).
+    (x0, x1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n, width = x.shape
+    dh = width // heads
+    om = rope_omega(dh, theta)
+    rc = np.asarray(patch_rc, dtype=np.float64)
+    ang = np.concatenate([rc[:, 0:1] * om[None, :], rc[:, 1:2] * om[None, :]], axis=1)  # [n, dh/2]
+    cos = np.cos(ang)[:, None, :]
+    sin = np.sin(ang)[:, None, :]
+    xp = x.reshape(n, heads, dh // 2, 2)
+    x0 = xp[..., 0]
+    x1 = xp[..., 1]
+    out = np.empty_like(xp)
+    out[..., 0] = x0 * cos - x1 * sin
+    out[..., 1] = x0 * sin + x1 * cos
+    return out.reshape(n, width)
+
+
+# --------------------------------------------------------------------------
+# a5: block-diagonal multi-head attention over the packed sequence
+# --------------------------------------------------------------------------
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens, heads: int) -> np.ndarray:
+    """For each image i and head h: softmax(q k^T / sqrt(dh)) v over the
+    image's own patches only ("Mistral 3", Mistral3VisionModel: attention over
+    a packed variable-resolution sequence, each image its own block).
+
+    q and k are already rotated.  The row maximum is subtracted before the
+    exponential (the softmax is unchanged by it).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, width = q.shape
+    dh = width // heads
+    scale = 1.0 / np.sqrt(dh)
+    out = np.zeros_like(q)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    for i in range(len(cu) - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if b == a:
+            continue
+        for h in range(heads):
+            cs = slice(h * dh, (h + 1) * dh)
+            s = (q[a:b, cs] @ k[a:b, cs].T) * scale
+            s -= s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p /= p.sum(axis=1, keepdims=True)
+            out[a:b, cs] = p @ v[a:b, cs]
+    return out
+
+
+# --------------------------------------------------------------------------
+# a7/a8: vision MLP (reading 1: gated SiLU)
+# --------------------------------------------------------------------------
+def swiglu_mlp(y: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """down(silu(y gate^T) * (y up^T)), silu(x) = x / (1 + exp(-x))
+    ("Mistral 3", Mistral3Model table, vision_mlp_dim 4096)."""
+    y = np.asarray(y, dtype=np.float64)
+    g = y @ np.asarray(w_gate, dtype=np.float64).T
+    u = y @ np.asarray(w_up, dtype=np.float64).T
+    hmid = g / (1.0 + np.exp(-g)) * u
+    return hmid @ np.asarray(w_down, dtype=np.float64).T
+
+
+# --------------------------------------------------------------------------
+# a11/a12: 2x2 patch merge + projection to the text width
+# --------------------------------------------------------------------------
+def merge_project(h: np.ndarray, merge_src: np.ndarray, w_merge: np.ndarray) -> np.ndarray:
+    """out[t] = concat(h[src[t,0]], h[src[t,1]], h[src[t,2]], h[src[t,3]]) W^T.
+
+    "Mistral 3", Mistral3Model description (2x2 patch-merging projector) and
+    argument table (spatial_merge_size 2, projector_bias False, embed_dim 5120).
+    """
+    h = np.asarray(h, dtype=np.float64)
+    src = np.asarray(merge_src, dtype=np.int64)
+    z = np.concatenate([h[src[:, 0]], h[src[:, 1]], h[src[:, 2]], h[src[:, 3]]], axis=1)
+    return z @ np.asarray(w_merge, dtype=np.float64).T
+
+
+# --------------------------------------------------------------------------
+# whole tower
+# --------------------------------------------------------------------------
+def tower_forward(
+    pixels: np.ndarray,
+    image_hw,
+    weights: dict,
+    cfg: TowerConfig,
+    layers: Optional[int] = None,
+    collect: bool = False,
+) -> Dict[str, np.ndarray]:
+    """Pixels + image sizes -> merged embeddings (or per-patch states when
+    merge == 1).
+
+    "Mistral 3", Mistral3VisionModel: patch embedding -> RMS pre-norm -> blocks;
+    each block: h += attn(rope(norm(h))), h += mlp(norm(h)).  Then the 2x2
+    merging projector ("Mistral 3", Mistral3Model), or no merge
+    ("Pixtral-12B-2409", part (1) Vision).
+
+    ``weights``: ``patch_w`` [D,3,p,p], ``ln_pre`` [D], ``layers`` (list of dicts
+    with ``attn_norm``, ``wq``, ``wk``, ``wv``, ``wo``, ``ffn_norm``,
+    ``w_gate``, ``w_up``, ``w_down``), ``merge_w`` [out_dim, 4D].
+    ``layers`` limits the depth (default cfg.layers).  With ``collect`` the
+    per-stage tensors are returned too.
+    """
+    n_layers = cfg.layers if layers is None else layers
+    maps = plan_maps(image_hw, cfg.patch, cfg.merge)
+    res: Dict[str, np.ndarray] = {"maps": maps}
+    x = patch_embed(pixels, image_hw, weights["patch_w"], cfg.patch)
+    if collect:
+        res["patch_embed"] = x.copy()
+    h = rms_norm(x, weights["ln_pre"], cfg.rms_eps)
+    if collect:
+        res["ln_pre"] = h.copy()
+        res["attn_out"] = []
+        res["block_out"] = []
+    cu = maps["cu_seqlens"]
+    rc = maps["patch_rc"]
+    for li in range(n_layers):
+        lw = weights["layers"][li]
+        y = rms_norm(h, lw["attn_norm"], cfg.rms_eps)
+        q = rope_2d(y @ np.asarray(lw["wq"], np.float64).T, rc, cfg.heads, cfg.rope_theta)
+        k = rope_2d(y @ np.asarray(lw["wk"], np.float64).T, rc, cfg.heads, cfg.rope_theta)
+        v = y @ np.asarray(lw["wv"], np.float64).T
+        a = attention(q, k, v, cu, cfg.heads)
+        h = h + a @ np.asarray(lw["wo"], np.float64).T
+        if collect:
+            res["attn_out"].append(h.copy())
+        y = rms_norm(h, lw["ffn_norm"], cfg.rms_eps)
+        h = h + swiglu_mlp(y, lw["w_gate"], lw["w_up"], lw["w_down"])
+        if collect:
+            res["block_out"].append(h.copy())
+    res["tower_out"] = h
+    if cfg.merge == 2:
+        res["out"] = merge_project(h, maps["merge_src"], weights["merge_w"])
+    else:
+        res["out"] = h
+    return res

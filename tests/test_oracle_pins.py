@@ -1,0 +1,429 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each test checks an oracle function against what the pages or mathematics
+fix: counts the pages print, a direct convolution written as loops, a
+textbook dense softmax with an explicit block mask, rotation identities,
+identity and zero weights.  None of them re-calls the oracle routine it checks
+to produce the expected value.  CPU only.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import pv_oracle as O
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+# ---------------------------------------------------------------- counts / maps
+def test_token_counts_from_pages():
+    with open(os.path.join(HERE, "golden", "token_counts.json")) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        m = O.plan_maps(c["image_hw"], c["patch"], c["merge"])
+        assert m["n_patches"] == c["n_patches"], c["source"]
+        assert m["out_rows"] == c["out_rows"], c["source"]
+        assert m["cu_seqlens"][-1] == c["n_patches"]
+
+
+@pytest.mark.parametrize("hw,patch,merge", [
+    ([(28, 28)], 14, 2), ([(28, 56)], 14, 2), ([(56, 28)], 14, 2), ([(42, 70)], 14, 1),
+    ([(56, 84), (28, 28), (112, 56)], 14, 2), ([(64, 32), (32, 96)], 16, 2), ([(48, 16)], 16, 1),
+])
+def test_maps_brute_force(hw, patch, merge):
+    m = O.plan_maps(hw, patch, merge)
+    # enumerate every pixel-grid position independently: patch index of pixel
+    # (y, x) of image i is base_i + (y // p) * Wp + (x // p)
+    base = 0
+    all_src = []
+    for i, (h, w) in enumerate(hw):
+        hp, wp = h // patch, w // patch
+        assert m["cu_seqlens"][i] == base
+        for y in range(0, h, patch):
+            for x in range(0, w, patch):
+                g = base + (y // patch) * wp + (x // patch)
+                assert tuple(m["patch_rc"][g]) == (y // patch, x // patch)
+        if merge == 2:
+            # merged token (R, C) covers the 2p x 2p pixel window at (2pR, 2pC)
+            for big_y in range(0, h, 2 * patch):
+                for big_x in range(0, w, 2 * patch):
+                    srcs = []
+                    for yy in (big_y, big_y + patch):
+                        for xx in (big_x, big_x + patch):
+                            srcs.append(base + (yy // patch) * wp + xx // patch)
+                    all_src.append(srcs)
+        base += hp * wp
+    assert m["cu_seqlens"][-1] == base
+    if merge == 2:
+        assert np.array_equal(m["merge_src"], np.array(all_src))
+        # every patch is used exactly once
+        assert sorted(m["merge_src"].reshape(-1).tolist()) == list(range(base))
+
+
+@pytest.mark.parametrize("hw,patch,merge", [([(30, 28)], 14, 2), ([(28, 14)], 14, 2), ([(0, 28)], 14, 1), ([(20, 16)], 16, 1)])
+def test_maps_reject_off_grid(hw, patch, merge):
+    with pytest.raises(ValueError):
+        O.plan_maps(hw, patch, merge)
+
+
+# ---------------------------------------------------------------- patch embed
+def _direct_conv(img, w, p):
+    """Stride-p, kernel-p convolution as six nested loops."""
+    c_in, h, wd = img.shape
+    d = w.shape[0]
+    hp, wp = h // p, wd // p
+    out = np.zeros((hp * wp, d))
+    for r in range(hp):
+        for c in range(wp):
+            for o in range(d):
+                s = 0.0
+                for ch in range(c_in):
+                    for u in range(p):
+                        for v in range(p):
+                            s += w[o, ch, u, v] * img[ch, r * p + u, c * p + v]
+                out[r * wp + c, o] = s
+    return out
+
+
+def test_patch_embed_direct_convolution():
+    rng = np.random.default_rng(11)
+    p = 4
+    hw = [(8, 12), (4, 8)]
+    imgs = [rng.standard_normal((3, h, w)) for h, w in hw]
+    wts = rng.standard_normal((5, 3, p, p))
+    flat = np.concatenate([im.reshape(-1) for im in imgs])
+    got = O.patch_embed(flat, hw, wts, p)
+    want = np.concatenate([_direct_conv(im, wts, p) for im in imgs])
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_patch_embed_one_hot_selects_pixel():
+    rng = np.random.default_rng(3)
+    p = 14
+    hw = [(28, 42)]
+    img = rng.random((3, 28, 42))
+    w = np.zeros((3, 3, p, p))
+    w[0, 2, 5, 7] = 1.0   # output 0 <- channel 2, (5, 7) inside each patch
+    w[1, 0, 13, 0] = 1.0
+    w[2, 1, 0, 13] = 1.0
+    x = O.patch_embed(img.reshape(-1), hw, w, p)
+    for r in range(2):
+        for c in range(3):
+            g = r * 3 + c
+            assert x[g, 0] == img[2, r * p + 5, c * p + 7]
+            assert x[g, 1] == img[0, r * p + 13, c * p + 0]
+            assert x[g, 2] == img[1, r * p + 0, c * p + 13]
+
+
+# ---------------------------------------------------------------- RMSNorm
+def test_rms_norm_closed_form():
+    x = np.array([[3.0, 4.0]])
+    g = np.array([2.0, 0.5])
+    # mean(x^2) = 12.5 ; with eps = 1e-5
+    want = np.array([[3.0 / math.sqrt(12.5 + 1e-5) * 2.0, 4.0 / math.sqrt(12.5 + 1e-5) * 0.5]])
+    np.testing.assert_allclose(O.rms_norm(x, g, 1e-5), want, rtol=1e-15)
+    # eps matters for tiny rows: x = 1e-3 everywhere -> 1e-3 / sqrt(1e-6 + 1e-5)
+    t = np.full((1, 4), 1e-3)
+    np.testing.assert_allclose(O.rms_norm(t, np.ones(4), 1e-5), 1e-3 / math.sqrt(1.1e-5), rtol=1e-12)
+
+
+def test_rms_norm_unit_rms_and_scale_invariance():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((7, 64)) * 5.0
+    y = O.rms_norm(x, np.ones(64), 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0, rtol=1e-12)
+    np.testing.assert_allclose(O.rms_norm(3.7 * x, np.ones(64), 0.0), y, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- RoPE
+def _rope_complex(x, r, c, heads, theta):
+    """Same rotation written with complex numbers: pair j of a head is the
+    complex number x[2j] + i x[2j+1], multiplied by exp(i * pos * omega)."""
+    dh = x.shape[0] // heads
+    per_axis = dh // 4
+    out = np.empty_like(x)
+    for h in range(heads):
+        for j in range(dh // 2):
+            m = j % per_axis
+            omega = theta ** (-(2.0 * m) / (dh / 2))
+            pos = r if j < per_axis else c
+            z = complex(x[h * dh + 2 * j], x[h * dh + 2 * j + 1]) * complex(math.cos(pos * omega), math.sin(pos * omega))
+            out[h * dh + 2 * j] = z.real
+            out[h * dh + 2 * j + 1] = z.imag
+    return out
+
+
+def test_rope_matches_complex_form():
+    rng = np.random.default_rng(5)
+    heads, dh = 2, 64
+    x = rng.standard_normal((4, heads * dh))
+    rc = np.array([[0, 0], [3, 7], [109, 1], [12, 109]])
+    got = O.rope_2d(x, rc, heads, 1e4)
+    for i in range(4):
+        np.testing.assert_allclose(got[i], _rope_complex(x[i], rc[i, 0], rc[i, 1], heads, 1e4), rtol=1e-12, atol=1e-12)
+
+
+def test_rope_ladder_values():
+    om = O.rope_omega(64, 1e4)
+    assert om.shape == (16,)
+    assert om[0] == 1.0
+    np.testing.assert_allclose(om[1], 1e4 ** (-1.0 / 16.0), rtol=1e-15)
+    np.testing.assert_allclose(om[15], 1e4 ** (-15.0 / 16.0), rtol=1e-15)
+
+
+def test_rope_identity_norm_and_axis_split():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((5, 128))
+    zero = np.zeros((5, 2), dtype=np.int64)
+    np.testing.assert_array_equal(O.rope_2d(x, zero, 2, 1e4), x)
+    rc = rng.integers(0, 110, size=(5, 2))
+    y = O.rope_2d(x, rc, 2, 1e4)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-12)
+    # rows turn the first 16 pairs of each head, columns the last 16
+    row_only = O.rope_2d(x, np.stack([rc[:, 0], np.zeros(5, np.int64)], 1), 2, 1e4)
+    col_only = O.rope_2d(x, np.stack([np.zeros(5, np.int64), rc[:, 1]], 1), 2, 1e4)
+    for h in range(2):
+        first = slice(h * 64, h * 64 + 32)
+        second = slice(h * 64 + 32, h * 64 + 64)
+        np.testing.assert_array_equal(row_only[:, second], x[:, second])
+        np.testing.assert_array_equal(col_only[:, first], x[:, first])
+
+
+def test_rope_relative_offset_invariance_and_composition():
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((1, 64))
+    k = rng.standard_normal((1, 64))
+    for (p1, p2, d) in [((3, 5), (10, 2), (4, 9)), ((0, 0), (7, 7), (50, 1))]:
+        a = np.dot(O.rope_2d(q, np.array([p1]), 1, 1e4)[0], O.rope_2d(k, np.array([p2]), 1, 1e4)[0])
+        s1 = (p1[0] + d[0], p1[1] + d[1])
+        s2 = (p2[0] + d[0], p2[1] + d[1])
+        b = np.dot(O.rope_2d(q, np.array([s1]), 1, 1e4)[0], O.rope_2d(k, np.array([s2]), 1, 1e4)[0])
+        np.testing.assert_allclose(a, b, rtol=1e-10)
+    # R(p) R(p') = R(p + p')
+    two = O.rope_2d(O.rope_2d(q, np.array([[2, 3]]), 1, 1e4), np.array([[5, 11]]), 1, 1e4)
+    one = O.rope_2d(q, np.array([[7, 14]]), 1, 1e4)
+    np.testing.assert_allclose(two, one, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- attention
+def _dense_masked_attention(q, k, v, cu, heads):
+    """Textbook softmax over the whole packed sequence with -inf outside each
+    image's block, element by element."""
+    n, width = q.shape
+    dh = width // heads
+    img = np.zeros(n, dtype=np.int64)
+    for i in range(len(cu) - 1):
+        img[cu[i]:cu[i + 1]] = i
+    out = np.zeros((n, width))
+    for h in range(heads):
+        for t in range(n):
+            logits = []
+            for u in range(n):
+                if img[u] == img[t]:
+                    logits.append(sum(q[t, h * dh + e] * k[u, h * dh + e] for e in range(dh)) / math.sqrt(dh))
+                else:
+                    logits.append(-math.inf)
+            mx = max(logits)
+            w = [math.exp(s - mx) if s != -math.inf else 0.0 for s in logits]
+            z = sum(w)
+            for e in range(dh):
+                out[t, h * dh + e] = sum(w[u] * v[u, h * dh + e] for u in range(n)) / z
+    return out
+
+
+def test_attention_dense_masked_brute_force():
+    rng = np.random.default_rng(8)
+    cu = np.array([0, 5, 6, 13])
+    n, heads, dh = 13, 2, 4
+    q, k, v = (rng.standard_normal((n, heads * dh)) * 2 for _ in range(3))
+    np.testing.assert_allclose(O.attention(q, k, v, cu, heads), _dense_masked_attention(q, k, v, cu, heads),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_attention_packed_equals_each_image_alone():
+    rng = np.random.default_rng(9)
+    lens = [7, 1, 12, 4]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    n = cu[-1]
+    q, k, v = (rng.standard_normal((n, 64)) for _ in range(3))
+    packed = O.attention(q, k, v, cu, 2)
+    for i in range(len(lens)):
+        a, b = cu[i], cu[i + 1]
+        alone = O.attention(q[a:b], k[a:b], v[a:b], np.array([0, b - a]), 2)
+        np.testing.assert_allclose(packed[a:b], alone, rtol=1e-13, atol=1e-13)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(10)
+    # single-patch image: output = v
+    q, k, v = (rng.standard_normal((1, 64)) for _ in range(3))
+    np.testing.assert_allclose(O.attention(q, k, v, np.array([0, 1]), 1), v, rtol=1e-14)
+    # equal keys: uniform weights -> mean of v
+    q = rng.standard_normal((6, 64))
+    k = np.tile(rng.standard_normal((1, 64)), (6, 1))
+    v = rng.standard_normal((6, 64))
+    np.testing.assert_allclose(O.attention(q, k, v, np.array([0, 6]), 1), np.tile(v.mean(0), (6, 1)), rtol=1e-12)
+    # permuting the patches permutes the outputs
+    q, k, v = (rng.standard_normal((9, 64)) for _ in range(3))
+    perm = rng.permutation(9)
+    a = O.attention(q, k, v, np.array([0, 9]), 2)
+    b = O.attention(q[perm], k[perm], v[perm], np.array([0, 9]), 2)
+    np.testing.assert_allclose(b, a[perm], rtol=1e-12, atol=1e-12)
+
+
+def test_attention_scale_is_inverse_sqrt_head_dim():
+    # two keys with logits differing by exactly sqrt(dh) * ln(3) give weights 3:1
+    dh = 64
+    q = np.zeros((1, dh)); q[0, 0] = 1.0
+    k = np.zeros((2, dh)); k[0, 0] = math.sqrt(dh) * math.log(3.0)
+    v = np.zeros((2, dh)); v[0, 1] = 1.0; v[1, 2] = 1.0
+    # query 0 attends over both keys (one image of 2 patches, query row duplicated)
+    qq = np.vstack([q, q])
+    out = O.attention(qq, k, v, np.array([0, 2]), 1)
+    np.testing.assert_allclose(out[0, 1], 0.75, rtol=1e-12)
+    np.testing.assert_allclose(out[0, 2], 0.25, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- MLP
+def test_swiglu_scalar_example():
+    y = np.array([[1.0, -2.0]])
+    wg = np.array([[0.5, 0.25]])      # gate = 0.0
+    wu = np.array([[1.0, 1.0]])       # up = -1
+    wd = np.array([[2.0], [3.0]])
+    np.testing.assert_allclose(O.swiglu_mlp(y, wg, wu, wd), [[0.0, 0.0]], atol=1e-15)
+    wg = np.array([[1.0, 0.0]])       # gate = 1 -> silu = 1/(1+e^-1)
+    s = 1.0 / (1.0 + math.exp(-1.0))
+    np.testing.assert_allclose(O.swiglu_mlp(y, wg, wu, wd), [[2.0 * s * -1.0, 3.0 * s * -1.0]], rtol=1e-14)
+
+
+def test_swiglu_zero_down_is_zero():
+    rng = np.random.default_rng(1)
+    y = rng.standard_normal((4, 8))
+    assert np.all(O.swiglu_mlp(y, rng.standard_normal((16, 8)), rng.standard_normal((16, 8)), np.zeros((8, 16))) == 0)
+
+
+# ---------------------------------------------------------------- merge
+@pytest.mark.parametrize("hw", [[(28, 56)], [(56, 28)], [(56, 84), (28, 28)]])
+def test_identity_merger_gathers_windows(hw):
+    p, d = 14, 3
+    m = O.plan_maps(hw, p, 2)
+    n = m["n_patches"]
+    h = np.arange(n * d, dtype=np.float64).reshape(n, d)
+    out = O.merge_project(h, m["merge_src"], np.eye(4 * d))
+    t = 0
+    base = 0
+    for (hh, ww) in hw:
+        hp, wp = hh // p, ww // p
+        for big_r in range(hp // 2):
+            for big_c in range(wp // 2):
+                want = np.concatenate([
+                    h[base + (2 * big_r) * wp + 2 * big_c], h[base + (2 * big_r) * wp + 2 * big_c + 1],
+                    h[base + (2 * big_r + 1) * wp + 2 * big_c], h[base + (2 * big_r + 1) * wp + 2 * big_c + 1]])
+                np.testing.assert_array_equal(out[t], want)
+                t += 1
+        base += hp * wp
+    assert t == m["out_rows"]
+
+
+# ---------------------------------------------------------------- whole tower
+def _tiny_weights(rng, d, f, p, layers, out_dim, zero_blocks=False):
+    w = {"patch_w": rng.standard_normal((d, 3, p, p)) * 0.1, "ln_pre": 1 + 0.1 * rng.standard_normal(d), "layers": []}
+    for _ in range(layers):
+        w["layers"].append({
+            "attn_norm": 1 + 0.1 * rng.standard_normal(d),
+            "wq": rng.standard_normal((d, d)) * 0.2, "wk": rng.standard_normal((d, d)) * 0.2,
+            "wv": rng.standard_normal((d, d)) * 0.2,
+            "wo": np.zeros((d, d)) if zero_blocks else rng.standard_normal((d, d)) * 0.2,
+            "ffn_norm": 1 + 0.1 * rng.standard_normal(d),
+            "w_gate": rng.standard_normal((f, d)) * 0.2, "w_up": rng.standard_normal((f, d)) * 0.2,
+            "w_down": np.zeros((d, f)) if zero_blocks else rng.standard_normal((d, f)) * 0.2,
+        })
+    w["merge_w"] = rng.standard_normal((out_dim, 4 * d)) * 0.1
+    return w
+
+
+def test_tower_zero_blocks_reduce_to_embed_norm_merge():
+    rng = np.random.default_rng(12)
+    cfg = O.TowerConfig(patch=4, hidden=16, heads=2, mlp=24, layers=2, merge=2, out_dim=20)
+    hw = [(16, 8), (8, 8)]
+    w = _tiny_weights(rng, 16, 24, 4, 2, 20, zero_blocks=True)
+    pix = rng.standard_normal(sum(3 * h * ww for h, ww in hw))
+    out = O.tower_forward(pix, hw, w, cfg)["out"]
+    # independent composition: direct conv -> explicit RMSNorm -> explicit window gather -> matmul
+    x = np.concatenate([_direct_conv(pix[:3 * 128].reshape(3, 16, 8), w["patch_w"], 4),
+                        _direct_conv(pix[3 * 128:].reshape(3, 8, 8), w["patch_w"], 4)])
+    hn = x / np.sqrt((x ** 2).mean(1, keepdims=True) + 1e-5) * w["ln_pre"]
+    rows = []
+    for base, (hp, wp) in [(0, (4, 2)), (8, (2, 2))]:
+        for r in range(hp // 2):
+            for c in range(wp // 2):
+                g = [base + (2 * r + a) * wp + 2 * c + b for a in (0, 1) for b in (0, 1)]
+                rows.append(np.concatenate([hn[i] for i in g]))
+    np.testing.assert_allclose(out, np.array(rows) @ w["merge_w"].T, rtol=1e-11, atol=1e-11)
+
+
+def test_tower_brute_force_tiny():
+    """One block computed step by step with the loop-based helpers above."""
+    rng = np.random.default_rng(13)
+    d, f, p, heads = 8, 12, 2, 2
+    cfg = O.TowerConfig(patch=p, hidden=d, heads=heads, mlp=f, layers=1, merge=2, out_dim=6, rope_theta=100.0)
+    hw = [(4, 8), (4, 4)]
+    w = _tiny_weights(rng, d, f, p, 1, 6)
+    pix = rng.standard_normal(3 * 32 + 3 * 16)
+    got = O.tower_forward(pix, hw, w, cfg)["out"]
+    x = np.concatenate([_direct_conv(pix[:96].reshape(3, 4, 8), w["patch_w"], p),
+                        _direct_conv(pix[96:].reshape(3, 4, 4), w["patch_w"], p)])
+    rc = [(r, c) for r in range(2) for c in range(4)] + [(r, c) for r in range(2) for c in range(2)]
+
+    def norm(a, g):
+        return a / np.sqrt((a ** 2).mean(1, keepdims=True) + 1e-5) * g
+
+    h = norm(x, w["ln_pre"])
+    lw = w["layers"][0]
+    y = norm(h, lw["attn_norm"])
+    q = y @ lw["wq"].T
+    k = y @ lw["wk"].T
+    v = y @ lw["wv"].T
+    q = np.array([_rope_complex(q[i], rc[i][0], rc[i][1], heads, 100.0) for i in range(12)])
+    k = np.array([_rope_complex(k[i], rc[i][0], rc[i][1], heads, 100.0) for i in range(12)])
+    a = _dense_masked_attention(q, k, v, [0, 8, 12], heads)
+    h = h + a @ lw["wo"].T
+    y = norm(h, lw["ffn_norm"])
+    gt = y @ lw["w_gate"].T
+    h = h + ((gt / (1 + np.exp(-gt))) * (y @ lw["w_up"].T)) @ lw["w_down"].T
+    rows = []
+    for base, (hp, wp) in [(0, (2, 4)), (8, (2, 2))]:
+        for r in range(hp // 2):
+            for c in range(wp // 2):
+                g = [base + (2 * r + a_) * wp + 2 * c + b_ for a_ in (0, 1) for b_ in (0, 1)]
+                rows.append(np.concatenate([h[i] for i in g]))
+    np.testing.assert_allclose(got, np.array(rows) @ w["merge_w"].T, rtol=1e-10, atol=1e-10)
+
+
+def test_tower_packing_order_invariance():
+    rng = np.random.default_rng(14)
+    cfg = O.TowerConfig(patch=4, hidden=16, heads=2, mlp=24, layers=2, merge=2, out_dim=10)
+    hw = [(16, 8), (8, 24), (8, 8)]
+    w = _tiny_weights(rng, 16, 24, 4, 2, 10)
+    imgs = [rng.standard_normal(3 * h * ww) for h, ww in hw]
+    a = O.tower_forward(np.concatenate(imgs), hw, w, cfg)["out"]
+    order = [2, 0, 1]
+    b = O.tower_forward(np.concatenate([imgs[i] for i in order]), [hw[i] for i in order], w, cfg)["out"]
+    counts = [(h // 8) * (ww // 8) for h, ww in hw]
+    starts = np.concatenate([[0], np.cumsum(counts)])
+    pieces_b = np.split(b, np.cumsum([counts[i] for i in order])[:-1])
+    for j, i in enumerate(order):
+        np.testing.assert_allclose(pieces_b[j], a[starts[i]:starts[i + 1]], rtol=1e-12, atol=1e-12)
+
+
+def test_tower_no_merge_returns_patch_states():
+    rng = np.random.default_rng(15)
+    cfg = O.TowerConfig(patch=4, hidden=16, heads=2, mlp=24, layers=1, merge=1)
+    hw = [(8, 12)]
+    w = _tiny_weights(rng, 16, 24, 4, 1, 10)
+    res = O.tower_forward(rng.standard_normal(3 * 96), hw, w, cfg)
+    assert res["out"].shape == (6, 16)
+    np.testing.assert_array_equal(res["out"], res["tower_out"])
