@@ -1,0 +1,228 @@
+"""Throughput benchmark of the vision tower on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ms31_1540]
+
+One step = one full tower forward (patch embedding, 24 blocks, 2x2 merge +
+projection) over one batch of seeded synthetic images already resident in HBM.
+Prints one JSON line with patches/s (value), merged tokens/s, the fraction of
+bf16 MFMA peak of the whole forward, the roofline of the dominant kernel
+(timed live with HIP events on the launch stream) and the float64 CPU oracle
+timed on a bounded sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+FP32_PEAK_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+
+CLASS_FOR_ROOFLINE = ("attn", "gateup", "down", "qkv", "oproj", "merge", "patch")
+
+
+def flops_by_class(wl):
+    """Algorithmic (unpadded) flops of one forward, by kernel class."""
+    D, F, L = wl.hidden, wl.mlp, wl.layers
+    N = wl.n_patches
+    p = wl.patch
+    lens = [(h // p) * (w // p) for h, w in wl.image_hw]
+    out = {
+        "patch": 2.0 * N * D * 3 * p * p,
+        "qkv": L * 2.0 * N * D * 3 * D,
+        "attn": L * sum(4.0 * n * n * D for n in lens),
+        "oproj": L * 2.0 * N * D * D,
+        "gateup": L * 2.0 * N * D * 2 * F,
+        "down": L * 2.0 * N * F * D,
+        "merge": 2.0 * wl.out_rows * 4 * D * wl.out_dim if wl.merge == 2 else 0.0,
+    }
+    return out
+
+
+def norm_bytes(wl):
+    """Algorithmic HBM bytes of the RMSNorm passes of one forward (bf16 path):
+    dual pass 4 read + 4 write + 2 write, single pass 4 read + 2 write."""
+    N, D, L = wl.n_patches, wl.hidden, wl.layers
+    return N * D * (10 + (2 * L - 1) * 6) if L > 0 else N * D * 8
+
+
+def cpu_baseline(wl, weights, pixels):
+    """The float64 oracle on a bounded sample: patch embedding + ln_pre + ONE
+    block + the merge projection of the full workload; the forward time is
+    extrapolated as embed + L x block + merge."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import pv_oracle as O
+    from vlm_vision_encoder_amd import synth
+
+    ow = synth.oracle_weights({"patch_w": weights["patch_w"], "ln_pre": weights["ln_pre"],
+                               "layers": weights["layers"][:1], **({"merge_w": weights["merge_w"]}
+                                                                   if "merge_w" in weights else {})})
+    cfg = O.TowerConfig(patch=wl.patch, hidden=wl.hidden, heads=wl.heads, mlp=wl.mlp, layers=1, merge=wl.merge,
+                        out_dim=wl.out_dim, rope_theta=wl.rope_theta, rms_eps=wl.rms_eps)
+    px = pixels.astype(np.float64)
+    t0 = time.perf_counter()
+    x = O.patch_embed(px, wl.image_hw, ow["patch_w"], wl.patch)
+    h = O.rms_norm(x, ow["ln_pre"], wl.rms_eps)
+    t1 = time.perf_counter()
+    maps = O.plan_maps(wl.image_hw, wl.patch, wl.merge)
+    lw = ow["layers"][0]
+    y = O.rms_norm(h, lw["attn_norm"], wl.rms_eps)
+    q = O.rope_2d(y @ lw["wq"].T, maps["patch_rc"], wl.heads, wl.rope_theta)
+    k = O.rope_2d(y @ lw["wk"].T, maps["patch_rc"], wl.heads, wl.rope_theta)
+    v = y @ lw["wv"].T
+    h = h + O.attention(q, k, v, maps["cu_seqlens"], wl.heads) @ lw["wo"].T
+    y = O.rms_norm(h, lw["ffn_norm"], wl.rms_eps)
+    h = h + O.swiglu_mlp(y, lw["w_gate"], lw["w_up"], lw["w_down"])
+    t2 = time.perf_counter()
+    if wl.merge == 2:
+        O.merge_project(h, maps["merge_src"], ow["merge_w"])
+    t3 = time.perf_counter()
+    fwd_s = (t1 - t0) + wl.layers * (t2 - t1) + (t3 - t2)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": wl.n_patches / fwd_s,
+        "unit": "patches/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle: patch embedding + ln_pre + 1 of {wl.layers} blocks + merge projection "
+                   f"of the full {wl.name} batch ({wl.n_patches} patches), timed {t3 - t0:.1f} s; forward time "
+                   f"extrapolated as embed + {wl.layers} x block + merge = {fwd_s:.1f} s"),
+        "merged_tokens_per_s": wl.out_rows / fwd_s,
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ms31_1540")
+    ap.add_argument("--profile-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the tower runs on a single MI355X here "
+              f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from vlm_vision_encoder_amd import synth
+    from vlm_vision_encoder_amd import tower as T
+
+    wl = synth.workload(args.workload)
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)  # noqa: E731
+    log(f"workload {wl.name}: {len(wl.image_hw)} images, {wl.n_patches} patches, {wl.out_rows} out rows, "
+        f"{wl.layers} layers, {wl.dtype}")
+    weights = synth.make_weights(wl)
+    pixels = synth.make_pixels(wl)
+    dev_w = T.weights_to_device(weights, wl.dtype)
+    tw = T.Tower(T.config_for(wl), dev_w)
+    pix = torch.from_numpy(pixels).cuda()
+    info = tw.plan(wl.image_hw)
+    out = torch.empty((info.out_rows, info.out_cols), dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32,
+                      device="cuda")
+    ws = tw.workspace(info.workspace_bytes)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    def step():
+        tw.forward_raw(pix.data_ptr(), wl.image_hw, out.data_ptr(), out.shape[0], ws.data_ptr(), ws.numel(), sptr)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (wall {t_wall * 1e3 / args.steps:.3f} ms/step)")
+    assert torch.isfinite(out.float()).all().item(), "non-finite output"
+
+    # per-kernel-class times, HIP events around each launch on the same stream
+    tw.set_profiling(True)
+    for _ in range(args.profile_steps):
+        step()
+    torch.cuda.synchronize()
+    prof = tw.read_profile(reset=True)
+    tw.set_profiling(False)
+    fl = flops_by_class(wl)
+    kernels = {}
+    for k, (ms, cnt) in prof.items():
+        if cnt == 0:
+            continue
+        per_launch_ms = ms / cnt
+        launches_per_fwd = cnt / args.profile_steps
+        d = {"avg_ms": round(per_launch_ms, 5), "launches_per_step": launches_per_fwd,
+             "ms_per_step": round(ms / args.profile_steps, 4)}
+        if fl.get(k):
+            d["tflops"] = round(fl[k] / (ms / args.profile_steps) / 1e9, 1)
+        if k == "norm":
+            d["gbs"] = round(norm_bytes(wl) / (ms / args.profile_steps) / 1e6, 1)
+        kernels[k] = d
+        log(f"  {k:7s} {per_launch_ms:9.4f} ms x {launches_per_fwd:5.1f}/step  {d.get('tflops', '')} TFLOP/s "
+            f"{d.get('gbs', '')}")
+    total_flops = sum(fl.values())
+    dom = max((k for k in fl if fl[k] > 0 and k in kernels), key=lambda k: kernels[k]["ms_per_step"])
+    dom_ms = kernels[dom]["avg_ms"]
+    dom_flops_launch = fl[dom] / kernels[dom]["launches_per_step"]
+    achieved = dom_flops_launch / (dom_ms * 1e-3) / 1e12
+    peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "flops_per_launch": dom_flops_launch, "avg_launch_ms": dom_ms}
+
+    patches_s = wl.n_patches / (ms_step * 1e-3)
+    tokens_s = wl.out_rows / (ms_step * 1e-3)
+    res = {
+        "metric": "vision patches/s + merged tokens/s at 1540x1540; % bf16 MFMA peak",
+        "value": round(patches_s, 1),
+        "unit": "patches/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "images": [list(hw) for hw in wl.image_hw][:8],
+                   "n_images": len(wl.image_hw), "patch": wl.patch, "layers": wl.layers, "merge": wl.merge,
+                   "n_patches": wl.n_patches, "out_rows": wl.out_rows, "out_cols": wl.out_cols},
+        "merged_tokens_per_s": round(tokens_s, 1),
+        "forward_tflops": round(total_flops / (ms_step * 1e-3) / 1e12, 1),
+        "forward_mfma_frac": round(total_flops / (ms_step * 1e-3) / 1e12 / peak, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(wl, weights, pixels)
+    else:
+        res["cpu_baseline"] = None
+    tw.close()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,212 @@
+/*
+ * pv_tower.h -- C ABI of the MI355X (gfx950) Pixtral-class vision tower.
+ *
+ * The tower maps normalised pixels of one or more images to merged image
+ * embeddings:
+ *
+ *   conv patch embedding -> RMS pre-norm -> L blocks of
+ *   [RMSNorm -> q,k,v -> 2-D rotary -> block-diagonal attention -> out-proj
+ *    + residual -> RMSNorm -> gated-SiLU MLP + residual]
+ *   -> 2x2 patch merge + bias-free projection to the text width
+ *      (or, without merge, one output row per patch).
+ *
+ * Sources: "Mistral 3" (KerasFormers model page) -- Mistral3VisionModel
+ * (patch embedding, RMS pre-norm, 2-D rotary blocks over a packed
+ * variable-resolution patch sequence), Mistral3Model argument table (vision
+ * width 1024, MLP 4096, depth 24, heads 16, patch 14, rotary base 1e4,
+ * spatial_merge_size 2, projector without bias, text width 5120), "Several
+ * images in one conversation" (each image keeps its own patch count);
+ * "Pixtral-12B-2409" (inference-research record), part (1) Vision and
+ * VISION TOKENS (patch 16, no merge, 1024x1024 tiles); NeMo Automodel
+ * "mistral3_vlm" API page, forward() (float pixel values plus image sizes).
+ *
+ * Conventions for every entry point:
+ *  - Every function returns a pv_status.  No C++ exception crosses this ABI.
+ *    On failure, pv_last_error() returns a thread-local message.
+ *  - Argument, shape and capacity checks happen on the host before anything
+ *    is enqueued, so they need no GPU.
+ *  - "device" pointers are HIP device memory; "host" pointers are ordinary
+ *    host memory.  All buffers are owned by the caller; the library keeps
+ *    borrowed weight pointers (they must outlive the tower).
+ *  - Work is enqueued on the caller's hipStream_t (passed as void*; NULL is
+ *    the null stream) and the call returns without synchronising.  Device
+ *    faults surface at the caller's next synchronisation.  One tower object
+ *    must not be used by two streams (or threads) at once.
+ */
+#ifndef PV_TOWER_H
+#define PV_TOWER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pv_status {
+  PV_OK = 0,
+  PV_ERR_ARG = -1,         /* null pointer, n_images < 1, bad config value   */
+  PV_ERR_SHAPE = -2,       /* H or W <= 0, off the patch*merge grid, > max_side */
+  PV_ERR_CAPACITY = -3,    /* output rows or workspace bytes too small        */
+  PV_ERR_HIP = -4,         /* a HIP runtime or launch error (message kept)    */
+  PV_ERR_UNSUPPORTED = -5  /* valid but not implemented (e.g. head_dim != 64) */
+} pv_status;
+
+typedef enum pv_dtype {
+  PV_BF16 = 0, /* bf16 matrices and activations, fp32 accumulation and residual */
+  PV_F32 = 1   /* fp32 everywhere */
+} pv_dtype;
+
+/* Tower hyper-parameters.  head_dim = hidden / heads must be 64. */
+typedef struct pv_config {
+  int32_t patch;      /* patch edge in pixels (14 for Mistral 3, 16 for Pixtral-12B) */
+  int32_t hidden;     /* D, a multiple of 256 (1024) */
+  int32_t heads;      /* attention heads (16) */
+  int32_t mlp;        /* F, MLP width, a multiple of 256 (4096) */
+  int32_t layers;     /* number of blocks L >= 0 (24) */
+  int32_t merge;      /* 2 = 2x2 patch merge + projection, 1 = no merge */
+  int32_t out_dim;    /* projection width when merge == 2 (5120), a multiple of 128 */
+  int32_t max_side;   /* largest accepted H or W in pixels (e.g. 1540 or 1024) */
+  double rope_theta;  /* rotary base (1e4) */
+  double rms_eps;     /* RMSNorm epsilon (1e-5) */
+  int32_t dtype;      /* pv_dtype */
+} pv_config;
+
+/* Per-block weights: borrowed device pointers, row-major, "out x in" like a
+ * linear layer (y = x W^T).  Gains are always fp32; matrices use cfg.dtype. */
+typedef struct pv_layer_weights {
+  const float* attn_norm; /* [D]    */
+  const void* wq;         /* [D][D] */
+  const void* wk;         /* [D][D] */
+  const void* wv;         /* [D][D] */
+  const void* wo;         /* [D][D] */
+  const float* ffn_norm;  /* [D]    */
+  const void* w_gate;     /* [F][D] */
+  const void* w_up;       /* [F][D] */
+  const void* w_down;     /* [D][F] */
+} pv_layer_weights;
+
+typedef struct pv_weights {
+  const void* patch_w;             /* [D][3][p][p] device, cfg.dtype (conv kernel, no bias) */
+  const float* ln_pre;             /* [D] device fp32 */
+  const pv_layer_weights* layers;  /* HOST array of cfg.layers entries; copied at create */
+  const void* merge_w;             /* [out_dim][4D] device, cfg.dtype; K order (dy,dx,channel)
+                                      with channel fastest; NULL when merge == 1 */
+} pv_weights;
+
+typedef struct pv_tower pv_tower;
+
+typedef struct pv_plan_info {
+  int64_t n_patches;       /* sum over images of (H/p)(W/p) */
+  int64_t out_rows;        /* merged tokens (merge 2) or n_patches (merge 1) */
+  int64_t out_cols;        /* out_dim (merge 2) or hidden (merge 1) */
+  int64_t workspace_bytes; /* device workspace that forward() needs */
+  int32_t n_images;
+  int32_t max_patches;     /* longest image, in patches */
+} pv_plan_info;
+
+/* Creates a tower.  cfg and w are read (w->layers is copied); the device
+ * pointers inside w are borrowed.  Builds the rotary cos/sin table on the host
+ * in double precision.  Allocates no device memory.
+ * Errors: PV_ERR_ARG (null, bad field), PV_ERR_UNSUPPORTED (head_dim != 64,
+ * hidden or mlp not a multiple of 256, out_dim not a multiple of 128). */
+pv_status pv_tower_create(const pv_config* cfg, const pv_weights* w, pv_tower** out);
+
+/* Frees the tower's host resources.  Waits for the tower's own pending
+ * host-to-device uploads first.  NULL is ignored. */
+void pv_tower_destroy(pv_tower* t);
+
+/* Host-only, pure: validates image_hw (host, [n_images][2] = (H, W) pixels)
+ * and fills *info.  Errors: PV_ERR_ARG, PV_ERR_SHAPE. */
+pv_status pv_tower_plan(const pv_tower* t, const int32_t* image_hw, int32_t n_images,
+                        pv_plan_info* info);
+
+/* Runs the whole tower.
+ *  pixels    device fp32, normalised; image i's 3 x H_i x W_i planes (channel,
+ *            row, column; column fastest) follow image i-1's.
+ *  image_hw  host int32 [n_images][2].
+ *  out       device [out_rows][out_cols] in cfg.dtype; images in input order,
+ *            merged tokens row-major within an image.
+ *  out_rows_cap  rows the caller allocated for out.
+ *  workspace device, at least pv_plan_info.workspace_bytes, 256-byte aligned.
+ *  stream    hipStream_t.
+ * Errors: PV_ERR_ARG, PV_ERR_SHAPE, PV_ERR_CAPACITY, PV_ERR_HIP. */
+pv_status pv_tower_forward(pv_tower* t, const float* pixels, const int32_t* image_hw,
+                           int32_t n_images, void* out, int64_t out_rows_cap,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/* Debug entry: runs the tower up to a stage and copies that tensor into dst
+ * (device, dst_bytes large enough).  Stages:
+ *   PV_STAGE_PATCH_EMBED  X = conv(pixels)               [N][D] fp32
+ *   PV_STAGE_LN_PRE       h0 = RMSNorm(X) * ln_pre       [N][D] fp32
+ *   PV_STAGE_QKV          layer l: [q|k|v], q,k rotated  [N][3D] cfg.dtype
+ *   PV_STAGE_ATTN         layer l: attention output      [N][D] cfg.dtype
+ *   PV_STAGE_ATTN_RESID   layer l: h after attention     [N][D] fp32
+ *   PV_STAGE_MLP_HIDDEN   layer l: silu(gate)*up         [N][F] cfg.dtype
+ *   PV_STAGE_BLOCK_OUT    layer l: h after the block     [N][D] fp32
+ * Errors: as pv_tower_forward, PV_ERR_ARG for a bad stage or layer. */
+enum {
+  PV_STAGE_PATCH_EMBED = 0,
+  PV_STAGE_LN_PRE = 1,
+  PV_STAGE_QKV = 2,
+  PV_STAGE_ATTN = 3,
+  PV_STAGE_ATTN_RESID = 4,
+  PV_STAGE_MLP_HIDDEN = 5,
+  PV_STAGE_BLOCK_OUT = 6
+};
+pv_status pv_tower_forward_stage(pv_tower* t, const float* pixels, const int32_t* image_hw,
+                                 int32_t n_images, int32_t stage, int32_t layer, void* dst,
+                                 int64_t dst_bytes, void* workspace, size_t ws_bytes,
+                                 void* stream);
+
+/* Index maps of a batch ("Mistral 3", Mistral3VisionModel: packed sequence;
+ * "Several images in one conversation": per-image counts):
+ *   cu_seqlens [n+1]     prefix sums of patch counts
+ *   patch_rc   [N][2]    (row, column) of every patch within its image
+ *   merge_src  [T][4]    the four patches of each merged token, order
+ *                        (0,0),(0,1),(1,0),(1,1); unused when merge == 1
+ * on_device == 0: host pointers, computed by the host planner.
+ * on_device == 1: device pointers, written by the same GPU kernel whose maps
+ *   the hot kernels read; workspace as for forward; enqueued on stream.
+ * merge_src may be NULL.  Errors: PV_ERR_ARG, PV_ERR_SHAPE, PV_ERR_CAPACITY,
+ * PV_ERR_HIP. */
+pv_status pv_tower_index_maps(pv_tower* t, const int32_t* image_hw, int32_t n_images,
+                              int32_t* cu_seqlens, int32_t* patch_rc, int32_t* merge_src,
+                              int32_t on_device, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+/* Per-kernel-class timing of forward calls, measured with HIP events
+ * recorded on the caller's stream around every launch of that class.
+ * pv_tower_set_profiling(t, 1) starts recording (and clears earlier records),
+ * 0 stops.  pv_tower_read_profile waits for the recorded events (host
+ * synchronisation), then writes, per class, the summed kernel time in
+ * milliseconds and the number of launches (host arrays of PV_K_COUNT
+ * entries); reset != 0 clears the records.  Recording adds two event records
+ * per launch; leave it off for throughput runs.
+ * Errors: PV_ERR_ARG (null), PV_ERR_HIP. */
+enum {
+  PV_K_MAPS = 0,     /* per-row index maps                     */
+  PV_K_PATCH = 1,    /* patch-embedding GEMM                   */
+  PV_K_NORM = 2,     /* RMSNorm passes                         */
+  PV_K_QKV = 3,      /* q,k,v GEMM with the rotary epilogue    */
+  PV_K_ATTN = 4,     /* block-diagonal attention               */
+  PV_K_OPROJ = 5,    /* out-projection GEMM (+ residual)       */
+  PV_K_GATEUP = 6,   /* MLP gate/up GEMM (silu * up)           */
+  PV_K_DOWN = 7,     /* MLP down GEMM (+ residual)             */
+  PV_K_MERGE = 8,    /* 2x2 merge + projection GEMM, or copy   */
+  PV_K_COUNT = 9
+};
+pv_status pv_tower_set_profiling(pv_tower* t, int32_t enable);
+pv_status pv_tower_read_profile(pv_tower* t, double* ms, int64_t* launches, int32_t reset);
+
+/* Thread-local message of the last failure in this thread ("" if none). */
+const char* pv_last_error(void);
+
+/* Static name of a status code. */
+const char* pv_status_str(pv_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PV_TOWER_H */

@@ -1,0 +1,178 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/pv_tower.h declares, validates arguments on the host before any HIP
+call, and its host planner's index maps equal the oracle's exactly."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import pv_oracle as O
+from vlm_vision_encoder_amd import synth
+from vlm_vision_encoder_amd import tower as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pv_tower.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(T.LIB_PATH), reason="libpv_tower.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(T.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = T.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+FAKE = 1 << 20  # an aligned, never-dereferenced stand-in for device pointers
+
+
+def fake_weights(layers=2, merge=True):
+    lw = [T.PvLayerWeights(*([FAKE] * 9)) for _ in range(layers)]
+    arr = (T.PvLayerWeights * max(1, layers))(*lw)
+    w = T.PvWeights(FAKE, FAKE, C.cast(arr, C.POINTER(T.PvLayerWeights)) if layers else None,
+                    FAKE if merge else None)
+    return w, arr
+
+
+def create(cfg, layers_present=True):
+    lib = T.load_library()
+    w, arr = fake_weights(cfg.layers if layers_present else 0, cfg.merge == 2)
+    h = C.c_void_p()
+    st = lib.pv_tower_create(C.byref(cfg), C.byref(w), C.byref(h))
+    return st, h, arr
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads=8), -5),            # head_dim 128
+    (dict(hidden=1000, heads=10), -5),
+    (dict(mlp=1000), -5),
+    (dict(out_dim=5000), -5),
+    (dict(merge=3), -1),
+    (dict(patch=0), -1),
+    (dict(layers=-1), -1),
+    (dict(dtype=7), -1),
+    (dict(dtype=1), 0),
+    (dict(max_side=10), -1),
+    (dict(rope_theta=0.0), -1),
+])
+def test_create_validation(kw, status):
+    dt = kw.pop("dtype", None)
+    cfg = T.make_config(**{"layers": 2, **kw})
+    if dt is not None:
+        cfg.dtype = dt
+    st, h, _ = create(cfg)
+    assert st == status, T.load_library().pv_last_error()
+    if st == 0:
+        T.load_library().pv_tower_destroy(h)
+    else:
+        assert T.load_library().pv_last_error()
+
+
+def test_create_null_pointers():
+    lib = T.load_library()
+    cfg = T.make_config(layers=1)
+    h = C.c_void_p()
+    assert lib.pv_tower_create(None, None, C.byref(h)) == -1
+    w, arr = fake_weights(1)
+    arr[0].wq = None
+    assert lib.pv_tower_create(C.byref(cfg), C.byref(w), C.byref(h)) == -1
+    assert b"null" in lib.pv_last_error()
+    w, arr = fake_weights(1)
+    arr[0].wo = FAKE + 2  # misaligned
+    assert lib.pv_tower_create(C.byref(cfg), C.byref(w), C.byref(h)) == -1
+
+
+def test_status_strings():
+    lib = T.load_library()
+    for code, name in T.STATUS.items():
+        assert lib.pv_status_str(code).decode() == name
+
+
+@pytest.fixture
+def tower_handle():
+    cfg = T.make_config(layers=2, max_side=1540)
+    st, h, arr = create(cfg)
+    assert st == 0
+    yield T.load_library(), h, cfg
+    T.load_library().pv_tower_destroy(h)
+
+
+def _plan(lib, h, hw):
+    arr, n = T._hw_array(hw)
+    info = T.PvPlanInfo()
+    st = lib.pv_tower_plan(h, arr, n, C.byref(info))
+    return st, info
+
+
+def test_plan_counts_and_shape_errors(tower_handle):
+    lib, h, cfg = tower_handle
+    st, info = _plan(lib, h, [(1540, 1540)])
+    assert st == 0 and info.n_patches == 12100 and info.out_rows == 3025 and info.out_cols == 5120
+    assert info.workspace_bytes > 12100 * 1024 * (4 + 2 + 8)
+    for bad in ([(1540, 1554)], [(30, 28)], [(0, 28)], [(28, -28)], [(28, 14)]):
+        st, _ = _plan(lib, h, bad)
+        assert st == -2, bad
+        assert lib.pv_last_error()
+    arr, _ = T._hw_array([(28, 28)])
+    assert lib.pv_tower_plan(h, arr, 0, C.byref(T.PvPlanInfo())) == -1
+    assert lib.pv_tower_plan(h, None, 1, C.byref(T.PvPlanInfo())) == -1
+
+
+def test_forward_validation_before_any_device_work(tower_handle):
+    """Every ARG/SHAPE/CAPACITY error returns before the first HIP call, so
+    these run without a GPU (fake device pointers are never touched)."""
+    lib, h, cfg = tower_handle
+    hw = [(56, 84)]
+    st, info = _plan(lib, h, hw)
+    arr, n = T._hw_array(hw)
+    big = 1 << 40
+    ws = FAKE * 256
+    assert lib.pv_tower_forward(None, FAKE, arr, n, FAKE, 99, ws, big, None) == -1
+    assert lib.pv_tower_forward(h, None, arr, n, FAKE, 99, ws, big, None) == -1
+    assert lib.pv_tower_forward(h, FAKE, arr, 0, FAKE, 99, ws, big, None) == -1
+    assert lib.pv_tower_forward(h, FAKE, arr, n, FAKE, 99, ws + 8, big, None) == -1       # misaligned ws
+    assert lib.pv_tower_forward(h, FAKE, arr, n, FAKE, info.out_rows - 1, ws, big, None) == -3
+    assert lib.pv_tower_forward(h, FAKE, arr, n, FAKE, info.out_rows, ws, info.workspace_bytes - 1, None) == -3
+    bad, nb = T._hw_array([(56, 70)])
+    assert lib.pv_tower_forward(h, FAKE, bad, nb, FAKE, 99, ws, big, None) == -2
+    assert lib.pv_tower_forward_stage(h, FAKE, arr, n, 9, 0, FAKE, big, ws, big, None) == -1
+    assert lib.pv_tower_forward_stage(h, FAKE, arr, n, 2, 5, FAKE, big, ws, big, None) == -1
+    assert lib.pv_tower_forward_stage(h, FAKE, arr, n, 2, 0, FAKE, 16, ws, big, None) == -3
+    assert lib.pv_tower_index_maps(h, arr, n, FAKE, FAKE, FAKE, 1, None, 0, None) == -1
+    assert lib.pv_tower_index_maps(h, arr, n, FAKE, FAKE, FAKE, 1, ws, 16, None) == -3
+
+
+@pytest.mark.parametrize("name", ["tiny", "ms31_1540", "packed8", "pixtral_tiles16", "sweep64"])
+def test_host_index_maps_equal_oracle(name):
+    wl = synth.workload(name)
+    cfg = T.config_for(wl)
+    st, h, _ = create(cfg)
+    assert st == 0
+    lib = T.load_library()
+    try:
+        n = len(wl.image_hw)
+        N, Tn = wl.n_patches, (wl.out_rows if wl.merge == 2 else 0)
+        cu = np.zeros(n + 1, np.int32)
+        rc = np.zeros((N, 2), np.int32)
+        ms = np.zeros((max(Tn, 1), 4), np.int32)
+        arr, _ = T._hw_array(wl.image_hw)
+        assert lib.pv_tower_index_maps(h, arr, n, cu.ctypes.data, rc.ctypes.data,
+                                       ms.ctypes.data if Tn else None, 0, None, 0, None) == 0
+        m = O.plan_maps(wl.image_hw, wl.patch, wl.merge)
+        np.testing.assert_array_equal(cu, m["cu_seqlens"])
+        np.testing.assert_array_equal(rc, m["patch_rc"])
+        if Tn:
+            np.testing.assert_array_equal(ms[:Tn], m["merge_src"])
+    finally:
+        lib.pv_tower_destroy(h)

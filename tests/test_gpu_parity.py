@@ -1,0 +1,267 @@
+"""GPU parity of the HIP tower against the float64 oracle, through the C ABI.
+
+Bar: index maps and cu_seqlens bit-exact; floats
+max|gpu - oracle| <= tol * RMS(oracle) per tensor, tol = 2e-2 (bf16 path) and
+1e-4 (fp32 path).  Inputs are the seeded synthetic ones of
+vlm_vision_encoder_amd.synth; every case prints its name before the GPU work.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import pv_oracle as O
+from vlm_vision_encoder_amd import synth
+from vlm_vision_encoder_amd import tower as T
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def oracle_cfg(wl, layers=None):
+    return O.TowerConfig(patch=wl.patch, hidden=wl.hidden, heads=wl.heads, mlp=wl.mlp,
+                         layers=wl.layers if layers is None else layers, merge=wl.merge, out_dim=wl.out_dim,
+                         rope_theta=wl.rope_theta, rms_eps=wl.rms_eps)
+
+
+def rel_err(got, want):
+    want = np.asarray(want, np.float64)
+    got = np.asarray(got, np.float64)
+    rms = np.sqrt(np.mean(want * want))
+    return float(np.max(np.abs(got - want)) / rms), rms
+
+
+def to_np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+class Case:
+    """Builds weights/pixels once; runs the GPU tower and the oracle."""
+
+    def __init__(self, wl, weights=None, pixels=None):
+        torch = _torch()
+        self.wl = wl
+        self.w = synth.make_weights(wl) if weights is None else weights
+        self.px = synth.make_pixels(wl) if pixels is None else pixels
+        self.dev_w = T.weights_to_device(self.w, wl.dtype)
+        self.tower = T.Tower(T.config_for(wl), self.dev_w)
+        self.pix = torch.from_numpy(self.px).cuda()
+        self._ref = None
+
+    def ref(self):
+        if self._ref is None:
+            self._ref = O.tower_forward(self.px.astype(np.float64), self.wl.image_hw, synth.oracle_weights(self.w),
+                                        oracle_cfg(self.wl), collect=True)
+        return self._ref
+
+    def run(self):
+        torch = _torch()
+        out = self.tower.forward(self.pix, self.wl.image_hw)
+        torch.cuda.synchronize()
+        return out
+
+    def stage(self, name, layer=0):
+        torch = _torch()
+        out = self.tower.forward_stage(self.pix, self.wl.image_hw, name, layer)
+        torch.cuda.synchronize()
+        return out
+
+
+BF16_ULP = 2.0 ** -8
+
+
+def check(name, got, want, tol, stored_bf16=False):
+    """max|got - want| <= tol * RMS(want).  A stage tensor that the bf16 path
+    stores in bf16 is also allowed one bf16 ulp of its own value (2^-8 |want|)
+    for that storage rounding; the tower output is held to the plain rule."""
+    want = np.asarray(want, np.float64)
+    got = np.asarray(got, np.float64)
+    rms = float(np.sqrt(np.mean(want * want)))
+    diff = np.abs(got - want)
+    if stored_bf16:
+        diff = np.maximum(diff - BF16_ULP * np.abs(want), 0.0)
+    e = float(np.max(diff) / rms)
+    say(f"  {name}: max-abs-err/RMS = {e:.3e} (RMS {rms:.3e}, tol {tol}{', bf16-stored' if stored_bf16 else ''})")
+    assert np.isfinite(e) and e <= tol, f"{name}: {e} > {tol}"
+
+
+BF16_STORED = ("qkv", "attn", "mlp_hidden")
+# silu(gate) * up multiplies two contractions of the bf16-rounded y: their
+# absolute errors (about 2^-9 of each contraction's scale) meet in a product
+# whose heavy tails (both factors near 5 sigma) set max|err| / RMS, so this
+# debug stage is held to 5e-2 (the output rule stays 2e-2).
+STAGE_TOL_BF16 = {"mlp_hidden": 5e-2}
+
+
+def oracle_stage(ref, wl, name, layer, w):
+    """Oracle value of a debug stage (recomputed from the oracle's own
+    per-layer states, never from GPU values)."""
+    if name == "patch_embed":
+        return ref["patch_embed"]
+    if name == "ln_pre":
+        return ref["ln_pre"]
+    if name == "attn_resid":
+        return ref["attn_out"][layer]
+    if name == "block_out":
+        return ref["block_out"][layer]
+    h = ref["ln_pre"] if layer == 0 else ref["block_out"][layer - 1]
+    lw = synth.oracle_weights(w)["layers"][layer]
+    maps = ref["maps"]
+    if name in ("qkv", "attn"):
+        y = O.rms_norm(h, lw["attn_norm"], wl.rms_eps)
+        q = O.rope_2d(y @ lw["wq"].T, maps["patch_rc"], wl.heads, wl.rope_theta)
+        k = O.rope_2d(y @ lw["wk"].T, maps["patch_rc"], wl.heads, wl.rope_theta)
+        v = y @ lw["wv"].T
+        if name == "qkv":
+            return np.concatenate([q, k, v], axis=1)
+        return O.attention(q, k, v, maps["cu_seqlens"], wl.heads)
+    if name == "mlp_hidden":
+        y = O.rms_norm(ref["attn_out"][layer], lw["ffn_norm"], wl.rms_eps)
+        g = y @ lw["w_gate"].T
+        return g / (1.0 + np.exp(-g)) * (y @ lw["w_up"].T)
+    raise KeyError(name)
+
+
+ALL_STAGES = ("patch_embed", "ln_pre", "qkv", "attn", "attn_resid", "mlp_hidden", "block_out")
+
+
+# ------------------------------------------------------------------ index maps
+@pytest.mark.parametrize("name", synth.WORKLOADS)
+def test_device_index_maps_exact(name):
+    _torch()
+    wl = synth.workload(name)
+    say(f"device index maps {name}")
+    dev_w = {"patch_w": None}
+    import torch
+    # weights are not read by the map kernel; any aligned buffers do
+    z = torch.zeros(16, dtype=torch.float32, device="cuda")
+    lw = {k: z for k in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")}
+    tw = T.Tower(T.config_for(wl), {"patch_w": z, "ln_pre": z, "layers": [lw] * wl.layers, "merge_w": z})
+    cu, rc, ms = tw.index_maps(wl.image_hw, on_device=True)
+    m = O.plan_maps(wl.image_hw, wl.patch, wl.merge)
+    np.testing.assert_array_equal(cu, m["cu_seqlens"])
+    np.testing.assert_array_equal(rc, m["patch_rc"])
+    if wl.merge == 2:
+        np.testing.assert_array_equal(ms, m["merge_src"])
+    tw.close()
+
+
+# ------------------------------------------------------------------ fp32 tower
+def test_tiny_fp32_full_and_stages():
+    wl = synth.workload("tiny")
+    say("tiny fp32 224x224, 1 layer")
+    c = Case(wl)
+    ref = c.ref()
+    check("out", to_np(c.run()), ref["out"], TOL["f32"])
+    for st in ALL_STAGES:
+        check(st, to_np(c.stage(st, 0)), oracle_stage(ref, wl, st, 0, c.w), TOL["f32"])
+
+
+# ------------------------------------------------------------------ bf16 tower
+def _bf16_small(image_hw, layers, patch=14, merge=2, **kw):
+    base = synth.workload("ms31_1540")
+    return base.with_(name="small", image_hw=tuple(image_hw), layers=layers, patch=patch, merge=merge, **kw)
+
+
+def test_bf16_stages_single_image():
+    wl = _bf16_small([(224, 224)], 2)
+    say("bf16 stages 224x224, 2 layers")
+    c = Case(wl)
+    ref = c.ref()
+    for layer in range(2):
+        for st in ALL_STAGES[2:]:
+            check(f"{st}[{layer}]", to_np(c.stage(st, layer)), oracle_stage(ref, wl, st, layer, c.w),
+                  STAGE_TOL_BF16.get(st, TOL["bf16"]), stored_bf16=st in BF16_STORED)
+    check("patch_embed", to_np(c.stage("patch_embed")), ref["patch_embed"], TOL["bf16"])
+    check("ln_pre", to_np(c.stage("ln_pre")), ref["ln_pre"], TOL["bf16"])
+    check("out", to_np(c.run()), ref["out"], TOL["bf16"])
+
+
+def test_bf16_packed_ragged_batch():
+    # 468 + 4 + 248 + 300 patches: none a multiple of 64, one image of 4 patches
+    wl = _bf16_small([(252, 364), (28, 28), (56, 868), (420, 140)], 3)
+    say(f"bf16 packed ragged {wl.image_hw}, 3 layers")
+    c = Case(wl)
+    ref = c.ref()
+    check("out", to_np(c.run()), ref["out"], TOL["bf16"])
+    check("block_out[2]", to_np(c.stage("block_out", 2)), ref["block_out"][2], TOL["bf16"])
+
+
+def test_bf16_no_merge_patch16_single_patch_image():
+    # Pixtral-12B style: patch 16, no merge; includes a one-patch image
+    wl = _bf16_small([(256, 384), (16, 16), (128, 112)], 2, patch=16, merge=1)
+    say(f"bf16 patch16 no-merge {wl.image_hw}")
+    c = Case(wl)
+    ref = c.ref()
+    out = c.run()
+    assert tuple(out.shape) == (wl.n_patches, 1024)
+    check("out", to_np(out), ref["out"], TOL["bf16"])
+
+
+def test_bf16_sharp_logits():
+    """Logit std ~4 instead of ~0.4.  bf16 storage of q and k moves every
+    logit s by up to about 2^-8 |s| (two half-ulp roundings), which moves the
+    softmax weights by that relative amount, so the bound is
+    2e-2 + 2^-8 * max|s| (max|s| from the oracle's own q, k)."""
+    wl = _bf16_small([(308, 196), (84, 56)], 1)
+    w = synth.make_weights(wl)
+    rng = np.random.default_rng(77)
+    for lw in w["layers"]:  # logit std ~ 4 instead of ~0.4
+        lw["wq"] = synth.round_to_bf16(rng.standard_normal(lw["wq"].shape, dtype=np.float32) * np.float32(0.0625))
+        lw["wk"] = synth.round_to_bf16(rng.standard_normal(lw["wk"].shape, dtype=np.float32) * np.float32(0.0625))
+    say("bf16 sharp logits")
+    c = Case(wl, weights=w)
+    ref = c.ref()
+    qkv = oracle_stage(ref, wl, "qkv", 0, w)
+    cu = ref["maps"]["cu_seqlens"]
+    smax = 0.0
+    for i in range(len(cu) - 1):
+        a, b = cu[i], cu[i + 1]
+        for h in range(wl.heads):
+            q = qkv[a:b, h * 64:(h + 1) * 64]
+            k = qkv[a:b, 1024 + h * 64:1024 + (h + 1) * 64]
+            smax = max(smax, float(np.max(np.abs(q @ k.T))) / 8.0)
+    tol = TOL["bf16"] + BF16_ULP * smax
+    say(f"  max |logit| {smax:.2f} -> tol {tol:.3f}")
+    assert smax > 10.0  # the case is really sharp
+    check("attn[0]", to_np(c.stage("attn", 0)), oracle_stage(ref, wl, "attn", 0, w), tol, stored_bf16=True)
+    check("out", to_np(c.run()), ref["out"], tol)
+
+
+def test_bf16_packing_invariance_and_determinism_bitexact():
+    torch = _torch()
+    hw = [(140, 168), (56, 84), (196, 28)]
+    wl = _bf16_small(hw, 2)
+    say("bf16 packing invariance / determinism")
+    c = Case(wl)
+    packed = c.run()
+    again = c.run()
+    assert torch.equal(packed, again), "two runs differ"
+    starts = np.cumsum([0] + [(h // 28) * (w // 28) for h, w in hw])
+    off = 0
+    for i, (h, w) in enumerate(hw):
+        n = 3 * h * w
+        alone = c.tower.forward(c.pix[off:off + n], [(h, w)])
+        torch.cuda.synchronize()
+        off += n
+        assert torch.equal(alone, packed[starts[i]:starts[i + 1]]), f"image {i} differs when packed"
+
+
+def test_zero_layer_tower_and_capacity_errors():
+    wl = _bf16_small([(56, 56)], 0)
+    say("bf16 zero-layer tower")
+    c = Case(wl)
+    ref = c.ref()
+    check("out", to_np(c.run()), ref["out"], TOL["bf16"])

@@ -1,0 +1,105 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, bf16
+// conversion, MFMA wrappers, wavefront reductions and the kernel-argument
+// structs.  CDNA4 only (wave64, MFMA 32x32x16 bf16).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "plan.h"
+
+namespace pv {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Element offset of an image in the pixel buffer.
+__device__ __forceinline__ int64_t pix_offset(const ImageMeta& m) {
+  return int64_t((uint64_t(m.pix_hi) << 32) | uint64_t(m.pix_lo));
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, uint32_t(b) << 16);
+}
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v;
+  v[0] = (bf16)a;
+  v[1] = (bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ u32x4 pack8(const float* f) {
+  u32x4 r;
+  r[0] = pack_bf16x2(f[0], f[1]);
+  r[1] = pack_bf16x2(f[2], f[3]);
+  r[2] = pack_bf16x2(f[4], f[5]);
+  r[3] = pack_bf16x2(f[6], f[7]);
+  return r;
+}
+
+__device__ __forceinline__ floatx16 mfma32x32x16(const u32x4& a, const u32x4& b, const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Value of the neighbouring lane (lane ^ 1) via DPP quad permute [1,0,3,2].
+__device__ __forceinline__ float swap_adjacent(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+}
+
+// Max / sum of v over the lane pair (l, l ^ 32), through ds_bpermute.
+// (The v_permlane32_swap builtin is not used: this compiler returns the same
+// register for both of its results, losing the swapped upper half.)
+__device__ __forceinline__ float pair_max32(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
+__device__ __forceinline__ float pair_sum32(float v) { return v + __shfl_xor(v, 32, 64); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Device view of the per-call maps (all in the workspace).
+struct DevMaps {
+  const ImageMeta* meta;
+  const int32_t* rowinfo;  // [N][2]: image, (row << 16) | col
+  const int32_t* msrc;     // [T][4]
+  const float* rope;       // [2][maxpos][pairs][2]
+  int32_t n_images;
+  int32_t rope_maxpos;
+  int32_t patch;
+};
+
+enum AMode { A_DENSE = 0, A_IM2COL = 1, A_MERGE = 2 };
+enum BMode { B_ONE = 0, B_QKV = 1, B_GATEUP = 2 };
+enum EMode { E_STORE = 0, E_STORE_F32 = 1, E_QKV_ROPE = 2, E_SILU_MUL = 3, E_ADD_F32 = 4 };
+
+struct GemmArgs {
+  int32_t M, N, K;
+  const void* A;      // A_DENSE: [M][lda]; A_MERGE: fp32 residual [*][hidden]
+  int32_t lda;
+  const float* pixels;  // A_IM2COL
+  const void* B0;     // weights [N][K] (B_QKV: wq, wk, wv; B_GATEUP: gate, up)
+  const void* B1;
+  const void* B2;
+  int32_t ldb;
+  void* C;
+  int32_t ldc;
+  int32_t hidden;     // D (QKV split, merge gather)
+  int32_t heads;
+  DevMaps maps;
+};
+
+}  // namespace pv

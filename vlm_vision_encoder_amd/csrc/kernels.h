@@ -1,0 +1,61 @@
+// Launch functions of the tower's kernels (host side).  All enqueue on the
+// given stream and return the launch status; none synchronises.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace pv {
+
+enum GemmKind {
+  GEMM_PATCH = 0,   // im2col(pixels) x patch_w^T -> fp32 X
+  GEMM_QKV = 1,     // y x [wq|wk|wv]^T -> bf16 q,k (rotated), v
+  GEMM_OPROJ = 2,   // attn x wo^T added into the fp32 residual
+  GEMM_GATEUP = 3,  // silu(y gate^T) * (y up^T) -> bf16
+  GEMM_DOWN = 4,    // hm x w_down^T added into the fp32 residual
+  GEMM_MERGE = 5,   // gather2x2(residual) x merge_w^T -> bf16 out
+  GEMM_PLAIN = 6    // dense A x B^T -> bf16 (tests and measurement)
+};
+
+// bf16 MFMA GEMM family (gemm_bf16.hip).
+hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s);
+
+// fp32 GEMM family, same kinds and operand conventions (f32_path.hip).
+hipError_t gemm_f32(GemmKind kind, const GemmArgs& g, hipStream_t s);
+
+// RMSNorm kernels (norm.hip).  Rows of width D (a multiple of 256).
+//   rmsnorm:      y = x / sqrt(mean(x^2) + eps) * g           (x fp32 -> y bf16 or fp32)
+//   rmsnorm_dual: h = norm(x) * g1 written back in place (fp32), y = norm(h) * g2
+hipError_t rmsnorm(const float* x, const float* g, void* y, int rows, int D, float eps,
+                   bool y_f32, hipStream_t s);
+hipError_t rmsnorm_dual(float* x, const float* g1, const float* g2, void* y, int rows, int D,
+                        float eps, bool y_f32, hipStream_t s);
+
+// Block-diagonal attention over the packed sequence (attn_bf16.hip, f32_path.hip).
+struct AttnArgs {
+  const void* qkv;   // [N][3D]: q (rotated) | k (rotated) | v
+  void* out;         // [N][D]
+  const ImageMeta* meta;
+  const AttnItem* items;
+  int32_t n_items;
+  int32_t heads;
+  int32_t hidden;
+};
+hipError_t attention_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t attention_f32(const AttnArgs& a, hipStream_t s);
+constexpr int kAttnQTileBf16 = 256;
+constexpr int kAttnQTileF32 = 64;
+
+// Per-row maps from per-image metadata (maps.hip):
+//   rowinfo[g] = (image, row << 16 | col), msrc[t] = 4 source patch rows.
+hipError_t build_maps(const ImageMeta* meta, int n_images, int n_patches, int out_rows,
+                      int merge, int32_t* rowinfo, int32_t* msrc, hipStream_t s);
+// rowinfo -> (row, col) pairs and cu_seqlens from meta (for the index-map entry).
+hipError_t export_maps(const ImageMeta* meta, const int32_t* rowinfo, int n_images,
+                       int n_patches, int32_t* cu_seqlens, int32_t* patch_rc, hipStream_t s);
+
+// fp32 -> bf16 copy (no-merge output of the bf16 path).
+hipError_t f32_to_bf16(const float* x, void* y, size_t n, hipStream_t s);
+
+}  // namespace pv

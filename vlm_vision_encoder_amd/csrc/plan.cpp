@@ -1,0 +1,138 @@
+// Host planner; see plan.h.
+#include "plan.h"
+
+#include <algorithm>
+#include <cmath>
+#include <numeric>
+
+namespace pv {
+
+namespace {
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+}  // namespace
+
+int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, Plan* out,
+               std::string* err) {
+  if (!image_hw || !out) {
+    *err = "image_hw and plan must not be null";
+    return -1;
+  }
+  if (n_images < 1) {
+    *err = "n_images must be >= 1 (the tower runs only on image input)";
+    return -1;
+  }
+  const int64_t grid = int64_t(p.patch) * p.merge;
+  Plan& pl = *out;
+  pl = Plan();
+  pl.n_images = n_images;
+  pl.meta.resize(n_images);
+  pl.cu.assign(n_images + 1, 0);
+  int64_t patches = 0, toks = 0, pix = 0;
+  int32_t maxp = 0, maxside_p = 0;
+  for (int32_t i = 0; i < n_images; ++i) {
+    const int32_t H = image_hw[2 * i], W = image_hw[2 * i + 1];
+    if (H <= 0 || W <= 0 || H % grid || W % grid || H > p.max_side || W > p.max_side) {
+      *err = "image " + std::to_string(i) + " is " + std::to_string(H) + "x" + std::to_string(W) +
+             ": each side must be a positive multiple of " + std::to_string(grid) +
+             " and at most " + std::to_string(p.max_side);
+      return -2;
+    }
+    ImageMeta& m = pl.meta[i];
+    m.H = H;
+    m.W = W;
+    m.Hp = H / p.patch;
+    m.Wp = W / p.patch;
+    m.patch_base = int32_t(patches);
+    m.tok_base = int32_t(toks);
+    m.pix_lo = uint32_t(uint64_t(pix) & 0xffffffffu);
+    m.pix_hi = uint32_t(uint64_t(pix) >> 32);
+    const int64_t n = int64_t(m.Hp) * m.Wp;
+    patches += n;
+    toks += (p.merge == 2) ? (n / 4) : n;
+    pix += int64_t(3) * H * W;
+    maxp = std::max<int32_t>(maxp, int32_t(n));
+    maxside_p = std::max(maxside_p, std::max(m.Hp, m.Wp));
+    pl.cu[i + 1] = int32_t(patches);
+    if (patches > (int64_t(1) << 30)) {
+      *err = "too many patches in one call (limit 2^30)";
+      return -2;
+    }
+  }
+  pl.n_patches = patches;
+  pl.out_rows = toks;
+  pl.max_patches = maxp;
+  pl.rope_maxpos = std::max(1, p.max_side / p.patch);
+
+  // Attention work list: q-tiles of every image, longest images first so the
+  // heaviest work items start earliest (longest-processing-time order).
+  std::vector<int32_t> order(n_images);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+    return (pl.cu[a + 1] - pl.cu[a]) > (pl.cu[b + 1] - pl.cu[b]);
+  });
+  for (int32_t i : order) {
+    const int32_t n = pl.cu[i + 1] - pl.cu[i];
+    for (int32_t q0 = 0; q0 < n; q0 += p.q_tile) pl.items.push_back({i, q0});
+  }
+
+  // Workspace layout.
+  Layout& L = pl.ws;
+  size_t off = 0;
+  L.meta = off;
+  off = align256(off + sizeof(ImageMeta) * n_images);
+  L.items = off;
+  off = align256(off + sizeof(AttnItem) * pl.items.size());
+  L.rope = off;
+  off = align256(off + sizeof(float) * 2 * 2 * size_t(pl.rope_maxpos) * p.rope_pairs);
+  L.upload_bytes = off;
+  L.rowinfo = off;
+  off = align256(off + sizeof(int32_t) * 2 * size_t(patches));
+  L.msrc = off;
+  off = align256(off + (p.merge == 2 ? sizeof(int32_t) * 4 * size_t(toks) : 0));
+  const size_t N = size_t(patches), D = size_t(p.hidden);
+  L.r = off;
+  off = align256(off + N * D * 4);
+  L.y = off;
+  off = align256(off + N * D * p.elem_bytes);
+  L.big = off;
+  off = align256(off + N * std::max(3 * D, size_t(p.mlp)) * p.elem_bytes);
+  L.total = off;
+  return 0;
+}
+
+void host_index_maps(const Plan& pl, int merge, int32_t* cu, int32_t* rc, int32_t* msrc) {
+  for (int32_t i = 0; i <= pl.n_images; ++i) cu[i] = pl.cu[i];
+  for (int32_t i = 0; i < pl.n_images; ++i) {
+    const ImageMeta& m = pl.meta[i];
+    for (int32_t j = 0; j < m.Hp * m.Wp; ++j) {
+      rc[2 * (int64_t(m.patch_base) + j)] = j / m.Wp;
+      rc[2 * (int64_t(m.patch_base) + j) + 1] = j % m.Wp;
+    }
+    if (merge == 2 && msrc) {
+      const int32_t hw = m.Wp / 2;
+      for (int32_t t = 0; t < (m.Hp / 2) * hw; ++t) {
+        const int32_t R = t / hw, C = t % hw;
+        int32_t* s = msrc + 4 * (int64_t(m.tok_base) + t);
+        s[0] = m.patch_base + (2 * R) * m.Wp + 2 * C;
+        s[1] = s[0] + 1;
+        s[2] = s[0] + m.Wp;
+        s[3] = s[2] + 1;
+      }
+    }
+  }
+}
+
+void build_rope_table(double theta, int32_t pairs, int32_t maxpos, std::vector<float>* out) {
+  out->assign(size_t(2) * 2 * maxpos * pairs, 0.f);
+  for (int axis = 0; axis < 2; ++axis)
+    for (int32_t pos = 0; pos < maxpos; ++pos)
+      for (int32_t m = 0; m < pairs; ++m) {
+        const double omega = std::pow(theta, -2.0 * m / (2.0 * pairs));
+        const double a = double(pos) * omega;
+        const size_t idx = ((size_t(axis) * maxpos + pos) * pairs + m) * 2;
+        (*out)[idx] = float(std::cos(a));
+        (*out)[idx + 1] = float(std::sin(a));
+      }
+}
+
+}  // namespace pv

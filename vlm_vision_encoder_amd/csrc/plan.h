@@ -1,0 +1,80 @@
+// Host planner of a tower call: validates image sizes, derives per-image
+// metadata, the attention work list and the device workspace layout.
+// Pure host C++ (no HIP), so it is testable without a GPU.
+//
+// Per-image counts follow "Mistral 3" (KerasFormers), Mistral3VisionModel
+// (all images packed into one patch sequence) and "Several images in one
+// conversation" (each image keeps its own patch count); without merge each
+// patch is one output row ("Pixtral-12B-2409", VISION TOKENS).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace pv {
+
+// Uploaded to the device as is (32 bytes, read by the kernels).
+struct ImageMeta {
+  int32_t H, W;            // pixels
+  int32_t Hp, Wp;          // patches
+  int32_t patch_base;      // first patch row of this image in the packed sequence
+  int32_t tok_base;        // first output row (merged token) of this image
+  uint32_t pix_lo, pix_hi; // 64-bit element offset of the image in the pixel buffer
+};
+static_assert(sizeof(ImageMeta) == 32, "ImageMeta layout");
+
+// One attention work item: q-tile starting at local query q0 of an image.
+struct AttnItem {
+  int32_t image;
+  int32_t q0;
+};
+
+struct PlanParams {
+  int32_t patch = 14;
+  int32_t merge = 2;
+  int32_t max_side = 1540;
+  int32_t hidden = 1024;
+  int32_t mlp = 4096;
+  int32_t out_dim = 5120;
+  int32_t elem_bytes = 2;   // 2 = bf16 activations, 4 = fp32
+  int32_t q_tile = 256;     // queries per attention work item
+  int32_t rope_pairs = 16;  // rotation pairs per axis (head_dim / 4)
+};
+
+// Byte offsets into the device workspace (all 256-byte aligned).
+struct Layout {
+  size_t meta = 0, items = 0, rope = 0, rowinfo = 0, msrc = 0;
+  size_t r = 0, y = 0, big = 0;
+  size_t upload_bytes = 0;  // [0, upload_bytes) is filled by one host->device copy
+  size_t total = 0;
+};
+
+struct Plan {
+  int32_t n_images = 0;
+  int64_t n_patches = 0;
+  int64_t out_rows = 0;
+  int32_t max_patches = 0;
+  int32_t rope_maxpos = 0;  // positions per axis in the rotary table
+  std::vector<ImageMeta> meta;
+  std::vector<int32_t> cu;  // n_images + 1
+  std::vector<AttnItem> items;
+  Layout ws;
+};
+
+// Returns 0 on success, -1 (argument) or -2 (shape) with *err set.
+int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, Plan* out,
+               std::string* err);
+
+// Host reference of the index maps (cu_seqlens [n+1], patch_rc [N][2],
+// merge_src [T][4]; merge_src may be null).
+void host_index_maps(const Plan& plan, int merge, int32_t* cu_seqlens, int32_t* patch_rc,
+                     int32_t* merge_src);
+
+// Rotary cos/sin table, built in double and rounded to float:
+// table[((axis * maxpos) + pos) * pairs + m] = (cos, sin)(pos * omega_m),
+// omega_m = theta^(-2m / (2 * pairs)), axis 0 = patch row, 1 = patch column.
+void build_rope_table(double theta, int32_t pairs, int32_t maxpos, std::vector<float>* out);
+
+}  // namespace pv

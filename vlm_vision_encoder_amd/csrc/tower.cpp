@@ -1,0 +1,497 @@
+// Tower engine and the C ABI declared in include/pv_tower.h.
+//
+// A forward call: validate + plan on the host, one host->device copy of the
+// per-image metadata, attention work list and rotary table into the head of
+// the caller's workspace, one kernel that expands the per-row maps, then the
+// layer loop
+//   patch GEMM -> dual RMSNorm (ln_pre, first attn_norm)
+//   L x [QKV GEMM (+RoPE) -> attention -> O GEMM (+= residual) -> RMSNorm
+//        -> gate/up GEMM (silu * up) -> down GEMM (+= residual) -> RMSNorm]
+//   -> merger GEMM with the 2x2 gather in its A load (or the no-merge copy).
+// The residual stream stays fp32 for the whole tower.  Nothing synchronises.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/pv_tower.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pv_status fail(pv_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+#define PV_HIP(call)                                                                        \
+  do {                                                                                      \
+    hipError_t e_ = (call);                                                                 \
+    if (e_ != hipSuccess)                                                                   \
+      return fail(PV_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_));           \
+  } while (0)
+
+// A timed launch: event before/after when the tower is profiling.
+#define PV_LAUNCH(kind, call)              \
+  do {                                     \
+    PV_HIP(prof_begin(t, (kind), s));      \
+    PV_HIP(call);                          \
+    PV_HIP(prof_end(t, s));                \
+  } while (0)
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+struct pv_tower {
+  pv_config cfg;
+  pv_weights w;
+  std::vector<pv_layer_weights> layers;
+  std::vector<float> rope;  // host rotary table
+  int32_t rope_maxpos = 0;
+  void* pinned = nullptr;   // staging of the per-call upload
+  size_t pinned_bytes = 0;
+  hipEvent_t upload_done = nullptr;
+  bool upload_pending = false;
+  // profiling: (class, start, end) per recorded launch; events are pooled
+  bool profiling = false;
+  struct Rec {
+    int kind;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+};
+
+namespace {
+
+pv::PlanParams plan_params(const pv_tower* t) {
+  pv::PlanParams p;
+  p.patch = t->cfg.patch;
+  p.merge = t->cfg.merge;
+  p.max_side = t->cfg.max_side;
+  p.hidden = t->cfg.hidden;
+  p.mlp = t->cfg.mlp;
+  p.out_dim = t->cfg.out_dim;
+  p.elem_bytes = t->cfg.dtype == PV_BF16 ? 2 : 4;
+  p.q_tile = t->cfg.dtype == PV_BF16 ? pv::kAttnQTileBf16 : pv::kAttnQTileF32;
+  p.rope_pairs = 16;
+  return p;
+}
+
+pv_status make_plan(const pv_tower* t, const int32_t* image_hw, int32_t n, pv::Plan* plan) {
+  std::string err;
+  const int rc = pv::build_plan(plan_params(t), image_hw, n, plan, &err);
+  if (rc == -1) return fail(PV_ERR_ARG, err);
+  if (rc == -2) return fail(PV_ERR_SHAPE, err);
+  return PV_OK;
+}
+
+hipError_t take_event(pv_tower* t, hipEvent_t* e) {
+  if (!t->pool.empty()) {
+    *e = t->pool.back();
+    t->pool.pop_back();
+    return hipSuccess;
+  }
+  return hipEventCreate(e);
+}
+
+// Records an event before a launch of class `kind` (no-op unless profiling).
+hipError_t prof_begin(pv_tower* t, int kind, hipStream_t s) {
+  if (!t->profiling) return hipSuccess;
+  pv_tower::Rec r{kind, nullptr, nullptr};
+  hipError_t e = take_event(t, &r.a);
+  if (e == hipSuccess) e = take_event(t, &r.b);
+  if (e == hipSuccess) e = hipEventRecord(r.a, s);
+  if (e != hipSuccess) return e;
+  t->recs.push_back(r);
+  return hipSuccess;
+}
+hipError_t prof_end(pv_tower* t, hipStream_t s) {
+  if (!t->profiling) return hipSuccess;
+  return hipEventRecord(t->recs.back().b, s);
+}
+
+// Host -> device upload of [meta | items | rope] and expansion of the row maps.
+pv_status upload_and_maps(pv_tower* t, const pv::Plan& plan, char* ws, hipStream_t s) {
+  const pv::Layout& L = plan.ws;
+  if (t->upload_pending) {
+    PV_HIP(hipEventSynchronize(t->upload_done));
+    t->upload_pending = false;
+  }
+  if (t->pinned_bytes < L.upload_bytes) {
+    if (t->pinned) PV_HIP(hipHostFree(t->pinned));
+    t->pinned = nullptr;
+    t->pinned_bytes = 0;
+    PV_HIP(hipHostMalloc(&t->pinned, L.upload_bytes, hipHostMallocDefault));
+    t->pinned_bytes = L.upload_bytes;
+  }
+  if (!t->upload_done) PV_HIP(hipEventCreateWithFlags(&t->upload_done, hipEventDisableTiming));
+  char* h = static_cast<char*>(t->pinned);
+  std::memset(h, 0, L.upload_bytes);
+  std::memcpy(h + L.meta, plan.meta.data(), sizeof(pv::ImageMeta) * plan.meta.size());
+  std::memcpy(h + L.items, plan.items.data(), sizeof(pv::AttnItem) * plan.items.size());
+  std::memcpy(h + L.rope, t->rope.data(), sizeof(float) * t->rope.size());
+  PV_HIP(hipMemcpyAsync(ws, h, L.upload_bytes, hipMemcpyHostToDevice, s));
+  PV_HIP(hipEventRecord(t->upload_done, s));
+  t->upload_pending = true;
+  PV_LAUNCH(PV_K_MAPS, pv::build_maps(reinterpret_cast<const pv::ImageMeta*>(ws + L.meta), plan.n_images,
+                                       int(plan.n_patches), int(plan.out_rows), t->cfg.merge,
+                                       reinterpret_cast<int32_t*>(ws + L.rowinfo),
+                                       reinterpret_cast<int32_t*>(ws + L.msrc), s));
+  return PV_OK;
+}
+
+struct StageStop {
+  int32_t stage = -1;  // -1: run to the end
+  int32_t layer = 0;
+  void* dst = nullptr;
+  int64_t dst_bytes = 0;
+};
+
+pv_status copy_stage(const StageStop& st, const void* src, size_t bytes, hipStream_t s) {
+  if (st.dst_bytes < int64_t(bytes))
+    return fail(PV_ERR_CAPACITY, "dst_bytes " + std::to_string(st.dst_bytes) + " < " + std::to_string(bytes));
+  PV_HIP(hipMemcpyAsync(st.dst, src, bytes, hipMemcpyDeviceToDevice, s));
+  return PV_OK;
+}
+
+pv_status run_tower(pv_tower* t, const float* pixels, const pv::Plan& plan, void* out, char* ws,
+                    const StageStop& st, hipStream_t s) {
+  const pv_config& c = t->cfg;
+  const bool bf = c.dtype == PV_BF16;
+  const size_t es = bf ? 2 : 4;
+  const pv::Layout& L = plan.ws;
+  const int N = int(plan.n_patches), D = c.hidden, F = c.mlp;
+  float* r = reinterpret_cast<float*>(ws + L.r);
+  void* y = ws + L.y;
+  void* big = ws + L.big;
+  auto gemm = [&](pv::GemmKind k, const pv::GemmArgs& g) { return bf ? pv::gemm_bf16(k, g, s) : pv::gemm_f32(k, g, s); };
+
+  pv::GemmArgs g{};
+  g.maps.meta = reinterpret_cast<const pv::ImageMeta*>(ws + L.meta);
+  g.maps.rowinfo = reinterpret_cast<const int32_t*>(ws + L.rowinfo);
+  g.maps.msrc = reinterpret_cast<const int32_t*>(ws + L.msrc);
+  g.maps.rope = reinterpret_cast<const float*>(ws + L.rope);
+  g.maps.n_images = plan.n_images;
+  g.maps.rope_maxpos = t->rope_maxpos;
+  g.maps.patch = c.patch;
+  g.hidden = D;
+  g.heads = c.heads;
+
+  // ---- patch embedding: X = im2col(pixels) W^T, fp32 into the residual buffer
+  {
+    pv::GemmArgs a = g;
+    a.M = N; a.N = D; a.K = 3 * c.patch * c.patch;
+    a.pixels = pixels;
+    a.B0 = t->w.patch_w; a.ldb = a.K;
+    a.C = r; a.ldc = D;
+    PV_LAUNCH(PV_K_PATCH, gemm(pv::GEMM_PATCH, a));
+  }
+  if (st.stage == PV_STAGE_PATCH_EMBED) return copy_stage(st, r, size_t(N) * D * 4, s);
+  const float eps = float(c.rms_eps);
+  if (c.layers == 0) {
+    PV_LAUNCH(PV_K_NORM, pv::rmsnorm(r, t->w.ln_pre, r, N, D, eps, true, s));  // in place, fp32 out
+    if (st.stage == PV_STAGE_LN_PRE) return copy_stage(st, r, size_t(N) * D * 4, s);
+  } else {
+    PV_LAUNCH(PV_K_NORM, pv::rmsnorm_dual(r, t->w.ln_pre, t->layers[0].attn_norm, y, N, D, eps, !bf, s));
+    if (st.stage == PV_STAGE_LN_PRE) return copy_stage(st, r, size_t(N) * D * 4, s);
+  }
+
+  pv::AttnArgs at{};
+  at.qkv = big;
+  at.out = y;  // y is free once q,k,v are computed
+  at.meta = g.maps.meta;
+  at.items = reinterpret_cast<const pv::AttnItem*>(ws + L.items);
+  at.n_items = int(plan.items.size());
+  at.heads = c.heads;
+  at.hidden = D;
+
+  for (int l = 0; l < c.layers; ++l) {
+    const pv_layer_weights& lw = t->layers[l];
+    const bool stop_here = st.layer == l;
+    {  // q,k,v with the 2-D rotary in the epilogue
+      pv::GemmArgs a = g;
+      a.M = N; a.N = 3 * D; a.K = D;
+      a.A = y; a.lda = D;
+      a.B0 = lw.wq; a.B1 = lw.wk; a.B2 = lw.wv; a.ldb = D;
+      a.C = big; a.ldc = 3 * D;
+      PV_LAUNCH(PV_K_QKV, gemm(pv::GEMM_QKV, a));
+    }
+    if (stop_here && st.stage == PV_STAGE_QKV) return copy_stage(st, big, size_t(N) * 3 * D * es, s);
+    PV_LAUNCH(PV_K_ATTN, bf ? pv::attention_bf16(at, s) : pv::attention_f32(at, s));
+    if (stop_here && st.stage == PV_STAGE_ATTN) return copy_stage(st, y, size_t(N) * D * es, s);
+    {  // out-projection added into the residual
+      pv::GemmArgs a = g;
+      a.M = N; a.N = D; a.K = D;
+      a.A = y; a.lda = D;
+      a.B0 = lw.wo; a.ldb = D;
+      a.C = r; a.ldc = D;
+      PV_LAUNCH(PV_K_OPROJ, gemm(pv::GEMM_OPROJ, a));
+    }
+    if (stop_here && st.stage == PV_STAGE_ATTN_RESID) return copy_stage(st, r, size_t(N) * D * 4, s);
+    PV_LAUNCH(PV_K_NORM, pv::rmsnorm(r, lw.ffn_norm, y, N, D, eps, !bf, s));
+    {  // gate/up with silu(gate) * up in the epilogue
+      pv::GemmArgs a = g;
+      a.M = N; a.N = F; a.K = D;
+      a.A = y; a.lda = D;
+      a.B0 = lw.w_gate; a.B1 = lw.w_up; a.ldb = D;
+      a.C = big; a.ldc = F;
+      PV_LAUNCH(PV_K_GATEUP, gemm(pv::GEMM_GATEUP, a));
+    }
+    if (stop_here && st.stage == PV_STAGE_MLP_HIDDEN) return copy_stage(st, big, size_t(N) * F * es, s);
+    {  // down-projection added into the residual
+      pv::GemmArgs a = g;
+      a.M = N; a.N = D; a.K = F;
+      a.A = big; a.lda = F;
+      a.B0 = lw.w_down; a.ldb = F;
+      a.C = r; a.ldc = D;
+      PV_LAUNCH(PV_K_DOWN, gemm(pv::GEMM_DOWN, a));
+    }
+    if (stop_here && st.stage == PV_STAGE_BLOCK_OUT) return copy_stage(st, r, size_t(N) * D * 4, s);
+    if (l + 1 < c.layers) PV_LAUNCH(PV_K_NORM, pv::rmsnorm(r, t->layers[l + 1].attn_norm, y, N, D, eps, !bf, s));
+  }
+  if (st.stage >= 0) return fail(PV_ERR_ARG, "stage/layer not reached");
+
+  if (c.merge == 2) {
+    pv::GemmArgs a = g;
+    a.M = int(plan.out_rows); a.N = c.out_dim; a.K = 4 * D;
+    a.A = r; a.lda = D;
+    a.B0 = t->w.merge_w; a.ldb = 4 * D;
+    a.C = out; a.ldc = c.out_dim;
+    PV_LAUNCH(PV_K_MERGE, gemm(pv::GEMM_MERGE, a));
+  } else if (bf) {
+    PV_LAUNCH(PV_K_MERGE, pv::f32_to_bf16(r, out, size_t(N) * D, s));
+  } else {
+    PV_HIP(hipMemcpyAsync(out, r, size_t(N) * D * 4, hipMemcpyDeviceToDevice, s));
+  }
+  return PV_OK;
+}
+
+pv_status check_call(const pv_tower* t, const float* pixels, const int32_t* image_hw, int32_t n, const void* dst,
+                     const void* ws) {
+  if (!t) return fail(PV_ERR_ARG, "tower is null");
+  if (!pixels || !image_hw || !dst || !ws) return fail(PV_ERR_ARG, "pixels, image_hw, output and workspace must not be null");
+  if (n < 1) return fail(PV_ERR_ARG, "n_images must be >= 1");
+  if (!aligned(pixels, 4)) return fail(PV_ERR_ARG, "pixels must be 4-byte aligned");
+  if (!aligned(dst, 16)) return fail(PV_ERR_ARG, "output must be 16-byte aligned");
+  if (!aligned(ws, 256)) return fail(PV_ERR_ARG, "workspace must be 256-byte aligned");
+  return PV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pv_last_error(void) { return g_last_error.c_str(); }
+
+const char* pv_status_str(pv_status s) {
+  switch (s) {
+    case PV_OK: return "PV_OK";
+    case PV_ERR_ARG: return "PV_ERR_ARG";
+    case PV_ERR_SHAPE: return "PV_ERR_SHAPE";
+    case PV_ERR_CAPACITY: return "PV_ERR_CAPACITY";
+    case PV_ERR_HIP: return "PV_ERR_HIP";
+    case PV_ERR_UNSUPPORTED: return "PV_ERR_UNSUPPORTED";
+  }
+  return "PV_ERR_UNKNOWN";
+}
+
+pv_status pv_tower_create(const pv_config* cfg, const pv_weights* w, pv_tower** out) {
+  g_last_error.clear();
+  if (!cfg || !w || !out) return fail(PV_ERR_ARG, "cfg, weights and out must not be null");
+  *out = nullptr;
+  const pv_config& c = *cfg;
+  if (c.dtype != PV_BF16 && c.dtype != PV_F32) return fail(PV_ERR_ARG, "dtype must be PV_BF16 or PV_F32");
+  if (c.patch < 1 || c.patch > 64) return fail(PV_ERR_ARG, "patch must be in [1, 64]");
+  if (c.merge != 1 && c.merge != 2) return fail(PV_ERR_ARG, "merge must be 1 or 2");
+  if (c.layers < 0) return fail(PV_ERR_ARG, "layers must be >= 0");
+  if (c.hidden <= 0 || c.heads <= 0 || c.mlp <= 0) return fail(PV_ERR_ARG, "hidden, heads and mlp must be > 0");
+  if (c.max_side < c.patch * c.merge || c.max_side / c.patch > 32767)
+    return fail(PV_ERR_ARG, "max_side must be >= patch*merge and < 32768 patches");
+  if (!(c.rope_theta > 0.0) || !(c.rms_eps >= 0.0)) return fail(PV_ERR_ARG, "rope_theta must be > 0 and rms_eps >= 0");
+  if (c.hidden % c.heads || c.hidden / c.heads != 64) return fail(PV_ERR_UNSUPPORTED, "head_dim must be 64");
+  const int nc = c.hidden / 256;
+  if (c.hidden % 256 || !(nc == 1 || nc == 2 || nc == 3 || nc == 4 || nc == 6 || nc == 8))
+    return fail(PV_ERR_UNSUPPORTED, "hidden must be 256, 512, 768, 1024, 1536 or 2048");
+  if (c.mlp % 256) return fail(PV_ERR_UNSUPPORTED, "mlp must be a multiple of 256");
+  if (c.merge == 2 && (c.out_dim <= 0 || c.out_dim % 128)) return fail(PV_ERR_UNSUPPORTED, "out_dim must be a positive multiple of 128");
+  if (!w->patch_w || !w->ln_pre) return fail(PV_ERR_ARG, "patch_w and ln_pre must not be null");
+  if (c.merge == 2 && !w->merge_w) return fail(PV_ERR_ARG, "merge_w must not be null when merge == 2");
+  if (c.layers > 0 && !w->layers) return fail(PV_ERR_ARG, "layers must not be null");
+  for (int l = 0; l < c.layers; ++l) {
+    const pv_layer_weights& lw = w->layers[l];
+    const void* ptrs[] = {lw.attn_norm, lw.wq, lw.wk, lw.wv, lw.wo, lw.ffn_norm, lw.w_gate, lw.w_up, lw.w_down};
+    for (const void* p : ptrs) {
+      if (!p) return fail(PV_ERR_ARG, "layer " + std::to_string(l) + " has a null weight pointer");
+      if (!aligned(p, 16)) return fail(PV_ERR_ARG, "layer " + std::to_string(l) + " weight not 16-byte aligned");
+    }
+  }
+  if (!aligned(w->ln_pre, 16) || (w->merge_w && !aligned(w->merge_w, 16)) || !aligned(w->patch_w, 4))
+    return fail(PV_ERR_ARG, "weights must be 16-byte aligned (patch_w 4-byte)");
+
+  pv_tower* t = new (std::nothrow) pv_tower();
+  if (!t) return fail(PV_ERR_ARG, "out of host memory");
+  t->cfg = c;
+  t->w = *w;
+  if (c.layers > 0) t->layers.assign(w->layers, w->layers + c.layers);
+  t->w.layers = t->layers.empty() ? nullptr : t->layers.data();
+  t->rope_maxpos = std::max(1, c.max_side / c.patch);
+  pv::build_rope_table(c.rope_theta, 16, t->rope_maxpos, &t->rope);
+  *out = t;
+  return PV_OK;
+}
+
+void pv_tower_destroy(pv_tower* t) {
+  if (!t) return;
+  if (t->upload_done) {
+    (void)hipEventSynchronize(t->upload_done);
+    (void)hipEventDestroy(t->upload_done);
+  }
+  if (t->pinned) (void)hipHostFree(t->pinned);
+  for (auto& r : t->recs) {
+    (void)hipEventSynchronize(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  for (hipEvent_t e : t->pool) (void)hipEventDestroy(e);
+  delete t;
+}
+
+pv_status pv_tower_plan(const pv_tower* t, const int32_t* image_hw, int32_t n_images, pv_plan_info* info) {
+  g_last_error.clear();
+  if (!t || !info) return fail(PV_ERR_ARG, "tower and info must not be null");
+  pv::Plan plan;
+  pv_status st = make_plan(t, image_hw, n_images, &plan);
+  if (st != PV_OK) return st;
+  info->n_patches = plan.n_patches;
+  info->out_rows = plan.out_rows;
+  info->out_cols = t->cfg.merge == 2 ? t->cfg.out_dim : t->cfg.hidden;
+  info->workspace_bytes = int64_t(plan.ws.total);
+  info->n_images = plan.n_images;
+  info->max_patches = plan.max_patches;
+  return PV_OK;
+}
+
+pv_status pv_tower_forward(pv_tower* t, const float* pixels, const int32_t* image_hw, int32_t n_images, void* out,
+                           int64_t out_rows_cap, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  pv_status st = check_call(t, pixels, image_hw, n_images, out, workspace);
+  if (st != PV_OK) return st;
+  pv::Plan plan;
+  if ((st = make_plan(t, image_hw, n_images, &plan)) != PV_OK) return st;
+  if (out_rows_cap < plan.out_rows)
+    return fail(PV_ERR_CAPACITY, "out_rows_cap " + std::to_string(out_rows_cap) + " < " + std::to_string(plan.out_rows));
+  if (ws_bytes < plan.ws.total)
+    return fail(PV_ERR_CAPACITY, "workspace " + std::to_string(ws_bytes) + " < " + std::to_string(plan.ws.total));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if ((st = upload_and_maps(t, plan, ws, s)) != PV_OK) return st;
+  return run_tower(t, pixels, plan, out, ws, StageStop(), s);
+}
+
+pv_status pv_tower_forward_stage(pv_tower* t, const float* pixels, const int32_t* image_hw, int32_t n_images,
+                                 int32_t stage, int32_t layer, void* dst, int64_t dst_bytes, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  pv_status st = check_call(t, pixels, image_hw, n_images, dst, workspace);
+  if (st != PV_OK) return st;
+  if (stage < PV_STAGE_PATCH_EMBED || stage > PV_STAGE_BLOCK_OUT) return fail(PV_ERR_ARG, "unknown stage");
+  if (stage >= PV_STAGE_QKV && (layer < 0 || layer >= t->cfg.layers)) return fail(PV_ERR_ARG, "layer out of range");
+  pv::Plan plan;
+  if ((st = make_plan(t, image_hw, n_images, &plan)) != PV_OK) return st;
+  if (ws_bytes < plan.ws.total)
+    return fail(PV_ERR_CAPACITY, "workspace " + std::to_string(ws_bytes) + " < " + std::to_string(plan.ws.total));
+  const size_t es = t->cfg.dtype == PV_BF16 ? 2 : 4;
+  const size_t N = size_t(plan.n_patches), D = size_t(t->cfg.hidden);
+  size_t need = N * D * 4;
+  if (stage == PV_STAGE_QKV) need = N * 3 * D * es;
+  if (stage == PV_STAGE_ATTN) need = N * D * es;
+  if (stage == PV_STAGE_MLP_HIDDEN) need = N * size_t(t->cfg.mlp) * es;
+  if (dst_bytes < int64_t(need))
+    return fail(PV_ERR_CAPACITY, "dst_bytes " + std::to_string(dst_bytes) + " < " + std::to_string(need));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if ((st = upload_and_maps(t, plan, ws, s)) != PV_OK) return st;
+  StageStop stop;
+  stop.stage = stage;
+  stop.layer = stage >= PV_STAGE_QKV ? layer : -1;
+  stop.dst = dst;
+  stop.dst_bytes = dst_bytes;
+  return run_tower(t, pixels, plan, nullptr, ws, stop, s);
+}
+
+pv_status pv_tower_index_maps(pv_tower* t, const int32_t* image_hw, int32_t n_images, int32_t* cu_seqlens,
+                              int32_t* patch_rc, int32_t* merge_src, int32_t on_device, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!t || !cu_seqlens || !patch_rc) return fail(PV_ERR_ARG, "tower, cu_seqlens and patch_rc must not be null");
+  pv::Plan plan;
+  pv_status st = make_plan(t, image_hw, n_images, &plan);
+  if (st != PV_OK) return st;
+  if (!on_device) {
+    pv::host_index_maps(plan, t->cfg.merge, cu_seqlens, patch_rc, merge_src);
+    return PV_OK;
+  }
+  if (!workspace) return fail(PV_ERR_ARG, "workspace must not be null when on_device != 0");
+  if (!aligned(workspace, 256)) return fail(PV_ERR_ARG, "workspace must be 256-byte aligned");
+  if (ws_bytes < plan.ws.total)
+    return fail(PV_ERR_CAPACITY, "workspace " + std::to_string(ws_bytes) + " < " + std::to_string(plan.ws.total));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if ((st = upload_and_maps(t, plan, ws, s)) != PV_OK) return st;
+  PV_HIP(pv::export_maps(reinterpret_cast<const pv::ImageMeta*>(ws + plan.ws.meta),
+                         reinterpret_cast<const int32_t*>(ws + plan.ws.rowinfo), plan.n_images,
+                         int(plan.n_patches), cu_seqlens, patch_rc, s));
+  if (merge_src && t->cfg.merge == 2 && plan.out_rows > 0)
+    PV_HIP(hipMemcpyAsync(merge_src, ws + plan.ws.msrc, size_t(plan.out_rows) * 16, hipMemcpyDeviceToDevice, s));
+  return PV_OK;
+}
+
+pv_status pv_tower_set_profiling(pv_tower* t, int32_t enable) {
+  g_last_error.clear();
+  if (!t) return fail(PV_ERR_ARG, "tower is null");
+  if (enable) {
+    for (auto& r : t->recs) {
+      PV_HIP(hipEventSynchronize(r.b));
+      t->pool.push_back(r.a);
+      t->pool.push_back(r.b);
+    }
+    t->recs.clear();
+  }
+  t->profiling = enable != 0;
+  return PV_OK;
+}
+
+pv_status pv_tower_read_profile(pv_tower* t, double* ms, int64_t* launches, int32_t reset) {
+  g_last_error.clear();
+  if (!t || !ms || !launches) return fail(PV_ERR_ARG, "tower, ms and launches must not be null");
+  for (int k = 0; k < PV_K_COUNT; ++k) {
+    ms[k] = 0.0;
+    launches[k] = 0;
+  }
+  for (auto& r : t->recs) {
+    PV_HIP(hipEventSynchronize(r.b));
+    float e = 0.f;
+    PV_HIP(hipEventElapsedTime(&e, r.a, r.b));
+    ms[r.kind] += e;
+    launches[r.kind] += 1;
+  }
+  if (reset) {
+    for (auto& r : t->recs) {
+      t->pool.push_back(r.a);
+      t->pool.push_back(r.b);
+    }
+    t->recs.clear();
+  }
+  return PV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,263 @@
+"""ctypes binding of libpv_tower.so (C ABI in include/pv_tower.h).
+
+Argument marshalling only: every step of the tower runs in the HIP library.
+PyTorch provides device memory and the current HIP stream.  If the library has
+not been built, loading it raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, List, Optional, Sequence, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpv_tower.so")
+
+PV_BF16, PV_F32 = 0, 1
+STAGES = {"patch_embed": 0, "ln_pre": 1, "qkv": 2, "attn": 3, "attn_resid": 4, "mlp_hidden": 5, "block_out": 6}
+STATUS = {0: "PV_OK", -1: "PV_ERR_ARG", -2: "PV_ERR_SHAPE", -3: "PV_ERR_CAPACITY", -4: "PV_ERR_HIP",
+          -5: "PV_ERR_UNSUPPORTED"}
+
+EXPORTED = ("pv_tower_create", "pv_tower_destroy", "pv_tower_plan", "pv_tower_forward",
+            "pv_tower_forward_stage", "pv_tower_index_maps", "pv_tower_set_profiling", "pv_tower_read_profile",
+            "pv_last_error", "pv_status_str")
+KERNEL_CLASSES = ("maps", "patch", "norm", "qkv", "attn", "oproj", "gateup", "down", "merge")
+
+
+class PvConfig(C.Structure):
+    _fields_ = [("patch", C.c_int32), ("hidden", C.c_int32), ("heads", C.c_int32), ("mlp", C.c_int32),
+                ("layers", C.c_int32), ("merge", C.c_int32), ("out_dim", C.c_int32), ("max_side", C.c_int32),
+                ("rope_theta", C.c_double), ("rms_eps", C.c_double), ("dtype", C.c_int32)]
+
+
+class PvLayerWeights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up",
+                                          "w_down")]
+
+
+class PvWeights(C.Structure):
+    _fields_ = [("patch_w", C.c_void_p), ("ln_pre", C.c_void_p), ("layers", C.POINTER(PvLayerWeights)),
+                ("merge_w", C.c_void_p)]
+
+
+class PvPlanInfo(C.Structure):
+    _fields_ = [("n_patches", C.c_int64), ("out_rows", C.c_int64), ("out_cols", C.c_int64),
+                ("workspace_bytes", C.c_int64), ("n_images", C.c_int32), ("max_patches", C.c_int32)]
+
+
+class PvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Loads the HIP library (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() "
+                           "(python -m vlm_vision_encoder_amd.build_lib)")
+    lib = C.CDLL(path)
+    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    lib.pv_tower_create.argtypes = [C.POINTER(PvConfig), C.POINTER(PvWeights), C.POINTER(vp)]
+    lib.pv_tower_create.restype = i32
+    lib.pv_tower_destroy.argtypes = [vp]
+    lib.pv_tower_destroy.restype = None
+    lib.pv_tower_plan.argtypes = [vp, vp, i32, C.POINTER(PvPlanInfo)]
+    lib.pv_tower_plan.restype = i32
+    lib.pv_tower_forward.argtypes = [vp, vp, vp, i32, vp, i64, vp, sz, vp]
+    lib.pv_tower_forward.restype = i32
+    lib.pv_tower_forward_stage.argtypes = [vp, vp, vp, i32, i32, i32, vp, i64, vp, sz, vp]
+    lib.pv_tower_forward_stage.restype = i32
+    lib.pv_tower_index_maps.argtypes = [vp, vp, i32, vp, vp, vp, i32, vp, sz, vp]
+    lib.pv_tower_index_maps.restype = i32
+    lib.pv_tower_set_profiling.argtypes = [vp, i32]
+    lib.pv_tower_set_profiling.restype = i32
+    lib.pv_tower_read_profile.argtypes = [vp, C.POINTER(C.c_double), C.POINTER(C.c_int64), i32]
+    lib.pv_tower_read_profile.restype = i32
+    lib.pv_last_error.argtypes = []
+    lib.pv_last_error.restype = C.c_char_p
+    lib.pv_status_str.argtypes = [i32]
+    lib.pv_status_str.restype = C.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise PvError(status, _lib.pv_last_error().decode())
+
+
+def make_config(patch=14, hidden=1024, heads=16, mlp=4096, layers=24, merge=2, out_dim=5120, max_side=1540,
+                rope_theta=1.0e4, rms_eps=1.0e-5, dtype="bf16") -> PvConfig:
+    if dtype not in ("bf16", "f32"):
+        raise ValueError("dtype must be 'bf16' or 'f32'")
+    return PvConfig(patch, hidden, heads, mlp, layers, merge, out_dim, max_side, float(rope_theta),
+                    float(rms_eps), PV_BF16 if dtype == "bf16" else PV_F32)
+
+
+def _hw_array(image_hw: Sequence[Sequence[int]]):
+    flat = [int(v) for hw in image_hw for v in hw]
+    return (C.c_int32 * max(1, len(flat)))(*flat), len(image_hw)
+
+
+class Tower:
+    """One tower object over borrowed device weights.
+
+    ``weights``: dict with torch tensors on the GPU: ``patch_w`` [D,3,p,p],
+    ``ln_pre`` [D] fp32, ``layers`` = list of dicts (``attn_norm``, ``wq``,
+    ``wk``, ``wv``, ``wo``, ``ffn_norm``, ``w_gate``, ``w_up``, ``w_down``),
+    ``merge_w`` [out_dim, 4D] (merge 2).  Matrices in the tower dtype; the
+    tensors are kept referenced for the tower's lifetime.
+    """
+
+    def __init__(self, cfg: PvConfig, weights: Dict):
+        self.lib = load_library()
+        self.cfg = cfg
+        self._keep = weights
+        lw = [PvLayerWeights(*[weights["layers"][i][k].data_ptr() for k, _ in PvLayerWeights._fields_])
+              for i in range(cfg.layers)]
+        self._layers = (PvLayerWeights * max(1, len(lw)))(*lw)
+        mw = weights.get("merge_w")
+        self._w = PvWeights(weights["patch_w"].data_ptr(), weights["ln_pre"].data_ptr(),
+                            C.cast(self._layers, C.POINTER(PvLayerWeights)) if lw else None,
+                            mw.data_ptr() if mw is not None else None)
+        h = C.c_void_p()
+        _check(self.lib.pv_tower_create(C.byref(cfg), C.byref(self._w), C.byref(h)))
+        self.handle = h
+        self._ws = None
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.pv_tower_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------ host-only
+    def plan(self, image_hw) -> PvPlanInfo:
+        arr, n = _hw_array(image_hw)
+        info = PvPlanInfo()
+        _check(self.lib.pv_tower_plan(self.handle, arr, n, C.byref(info)))
+        return info
+
+    # ------------------------------------------------------------ device
+    def workspace(self, nbytes: int):
+        import torch
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        return self._ws
+
+    def _out_dtype(self):
+        import torch
+        return torch.bfloat16 if self.cfg.dtype == PV_BF16 else torch.float32
+
+    def forward(self, pixels, image_hw, out=None, stream=None):
+        """pixels: flat fp32 CUDA tensor of the normalised C x H x W planes."""
+        import torch
+        arr, n = _hw_array(image_hw)
+        info = self.plan(image_hw)
+        if out is None:
+            out = torch.empty((info.out_rows, info.out_cols), dtype=self._out_dtype(), device="cuda")
+        ws = self.workspace(info.workspace_bytes)
+        s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+        _check(self.lib.pv_tower_forward(self.handle, pixels.data_ptr(), arr, n, out.data_ptr(), out.shape[0],
+                                         ws.data_ptr(), ws.numel(), s))
+        return out
+
+    def forward_raw(self, pixels_ptr: int, image_hw, out_ptr: int, out_rows_cap: int, ws_ptr: int,
+                    ws_bytes: int, stream: int):
+        arr, n = _hw_array(image_hw)
+        _check(self.lib.pv_tower_forward(self.handle, pixels_ptr, arr, n, out_ptr, out_rows_cap, ws_ptr,
+                                         ws_bytes, stream))
+
+    def set_profiling(self, enable: bool):
+        _check(self.lib.pv_tower_set_profiling(self.handle, 1 if enable else 0))
+
+    def read_profile(self, reset: bool = True) -> Dict[str, Tuple[float, int]]:
+        """{class: (summed ms, launches)} of the recorded forward calls."""
+        n = len(KERNEL_CLASSES)
+        ms = (C.c_double * n)()
+        cnt = (C.c_int64 * n)()
+        _check(self.lib.pv_tower_read_profile(self.handle, ms, cnt, 1 if reset else 0))
+        return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_CLASSES)}
+
+    def forward_stage(self, pixels, image_hw, stage: str, layer: int = 0):
+        import torch
+        arr, n = _hw_array(image_hw)
+        info = self.plan(image_hw)
+        N, D, F = info.n_patches, self.cfg.hidden, self.cfg.mlp
+        act = self._out_dtype()
+        shapes = {"patch_embed": ((N, D), torch.float32), "ln_pre": ((N, D), torch.float32),
+                  "qkv": ((N, 3 * D), act), "attn": ((N, D), act), "attn_resid": ((N, D), torch.float32),
+                  "mlp_hidden": ((N, F), act), "block_out": ((N, D), torch.float32)}
+        shape, dt = shapes[stage]
+        dst = torch.empty(shape, dtype=dt, device="cuda")
+        ws = self.workspace(info.workspace_bytes)
+        s = torch.cuda.current_stream().cuda_stream
+        _check(self.lib.pv_tower_forward_stage(self.handle, pixels.data_ptr(), arr, n, STAGES[stage], layer,
+                                               dst.data_ptr(), dst.numel() * dst.element_size(), ws.data_ptr(),
+                                               ws.numel(), s))
+        return dst
+
+    def index_maps(self, image_hw, on_device: bool):
+        import numpy as np
+        info = self.plan(image_hw)
+        n = len(image_hw)
+        T = info.out_rows if self.cfg.merge == 2 else 0
+        if not on_device:
+            cu = np.zeros(n + 1, np.int32)
+            rc = np.zeros((max(1, info.n_patches), 2), np.int32)
+            ms = np.zeros((max(1, T), 4), np.int32)
+            arr, _ = _hw_array(image_hw)
+            _check(self.lib.pv_tower_index_maps(self.handle, arr, n, cu.ctypes.data, rc.ctypes.data,
+                                                ms.ctypes.data if T else None, 0, None, 0, None))
+            return cu, rc[:info.n_patches], ms[:T]
+        import torch
+        cu = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
+        rc = torch.zeros((max(1, info.n_patches), 2), dtype=torch.int32, device="cuda")
+        ms = torch.zeros((max(1, T), 4), dtype=torch.int32, device="cuda")
+        ws = self.workspace(info.workspace_bytes)
+        arr, _ = _hw_array(image_hw)
+        _check(self.lib.pv_tower_index_maps(self.handle, arr, n, cu.data_ptr(), rc.data_ptr(),
+                                            ms.data_ptr() if T else None, 1, ws.data_ptr(), ws.numel(),
+                                            torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        return cu.cpu().numpy(), rc[:info.n_patches].cpu().numpy(), ms[:T].cpu().numpy()
+
+
+# ---------------------------------------------------------------- helpers
+def config_for(wl, max_side: Optional[int] = None) -> PvConfig:
+    """PvConfig of a synth.Workload."""
+    ms = max_side if max_side is not None else max(max(h, w) for h, w in wl.image_hw)
+    return make_config(patch=wl.patch, hidden=wl.hidden, heads=wl.heads, mlp=wl.mlp, layers=wl.layers,
+                       merge=wl.merge, out_dim=wl.out_dim, max_side=ms, rope_theta=wl.rope_theta,
+                       rms_eps=wl.rms_eps, dtype=wl.dtype)
+
+
+def weights_to_device(w: Dict, dtype: str) -> Dict:
+    """numpy weights (float32 arrays) -> CUDA tensors in the tower's layout."""
+    import torch
+    mdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def mat(a):
+        return torch.from_numpy(a.reshape(a.shape[0], -1)).to(device="cuda").to(mdt).contiguous()
+
+    def vec(a):
+        return torch.from_numpy(a).to(device="cuda", dtype=torch.float32).contiguous()
+
+    out = {"patch_w": mat(w["patch_w"]), "ln_pre": vec(w["ln_pre"]), "layers": []}
+    for lw in w["layers"]:
+        out["layers"].append({k: (vec(v) if k.endswith("norm") else mat(v)) for k, v in lw.items()})
+    if "merge_w" in w:
+        out["merge_w"] = mat(w["merge_w"])
+    return out
