@@ -69,7 +69,10 @@ typedef struct pv_config {
   int32_t max_side;   /* largest accepted H or W in pixels (e.g. 1540 or 1024) */
   double rope_theta;  /* rotary base (1e4) */
   double rms_eps;     /* RMSNorm epsilon (1e-5) */
-  int32_t dtype;      /* pv_dtype */
+  int32_t dtype;      /* pv_dtype of the weights and activations */
+  int32_t out_dtype;  /* pv_dtype of the output buffer for the bf16 tower: PV_BF16
+                         (default) or PV_F32 (keeps the result unrounded); the
+                         fp32 tower always writes fp32 */
 } pv_config;
 
 /* Per-block weights: borrowed device pointers, row-major, "out x in" like a
@@ -125,7 +128,8 @@ pv_status pv_tower_plan(const pv_tower* t, const int32_t* image_hw, int32_t n_im
  *  pixels    device fp32, normalised; image i's 3 x H_i x W_i planes (channel,
  *            row, column; column fastest) follow image i-1's.
  *  image_hw  host int32 [n_images][2].
- *  out       device [out_rows][out_cols] in cfg.dtype; images in input order,
+ *  out       device [out_rows][out_cols] in cfg.out_dtype (fp32 for the fp32
+ *            tower); images in input order,
  *            merged tokens row-major within an image.
  *  out_rows_cap  rows the caller allocated for out.
  *  workspace device, at least pv_plan_info.workspace_bytes, 256-byte aligned.

@@ -1,0 +1,65 @@
+"""Writes full-size expected values for the GPU parity tests.
+
+Runs the float64 oracle (and nothing else) over the full workloads of
+vlm_vision_encoder_amd.synth and stores, per workload, a seeded sample of
+output rows (float32), their row indices, and the RMS of the whole oracle
+output.  Usage:
+
+    python tests/golden/make_golden.py [workload ...]
+
+Output: tests/golden/<workload>.npz.  Several minutes per workload.
+"""
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+from oracle import pv_oracle as O  # noqa: E402
+from vlm_vision_encoder_amd import synth  # noqa: E402
+
+N_SAMPLE_ROWS = 32
+SAMPLE_SEED = 1234
+
+
+def sample_rows(out_rows: int, image_rows) -> np.ndarray:
+    """First and last row of the batch, the first row of every image (up to
+    8), and seeded random rows, sorted and unique."""
+    rng = np.random.default_rng(SAMPLE_SEED)
+    fixed = [0, out_rows - 1] + list(image_rows[:8])
+    rest = rng.choice(out_rows, size=N_SAMPLE_ROWS, replace=False)
+    return np.unique(np.array(fixed + list(rest), dtype=np.int64))
+
+
+def make(name: str) -> str:
+    wl = synth.workload(name)
+    t0 = time.time()
+    w = synth.oracle_weights(synth.make_weights(wl))
+    px = synth.make_pixels(wl).astype(np.float64)
+    cfg = O.TowerConfig(patch=wl.patch, hidden=wl.hidden, heads=wl.heads, mlp=wl.mlp, layers=wl.layers,
+                        merge=wl.merge, out_dim=wl.out_dim, rope_theta=wl.rope_theta, rms_eps=wl.rms_eps)
+    res = O.tower_forward(px, wl.image_hw, w, cfg)
+    out = res["out"]
+    maps = res["maps"]
+    if wl.merge == 2:
+        starts = np.cumsum([0] + [(h // wl.patch // 2) * (ww // wl.patch // 2) for h, ww in wl.image_hw])[:-1]
+    else:
+        starts = maps["cu_seqlens"][:-1]
+    rows = sample_rows(out.shape[0], list(starts))
+    path = os.path.join(HERE, f"{name}.npz")
+    np.savez_compressed(path, rows=rows, values=out[rows].astype(np.float32),
+                        rms=np.float64(np.sqrt(np.mean(out * out))), shape=np.array(out.shape, np.int64),
+                        image_hw=np.array(wl.image_hw, np.int64))
+    print(f"{name}: out {out.shape}, rms {np.sqrt(np.mean(out * out)):.6f}, {len(rows)} rows sampled, "
+          f"{time.time() - t0:.0f} s -> {path}", flush=True)
+    return path
+
+
+if __name__ == "__main__":
+    names = sys.argv[1:] or ["ms31_1540", "packed8", "sweep64", "pixtral_tiles16"]
+    for n in names:
+        make(n)

@@ -5,16 +5,32 @@
 // rotated by the 2-D RoPE, which the q,k,v projection applies in its epilogue
 // (once per element, instead of once per query tile that re-reads a key).
 //
-// Work item = (image, tile of 64*WAVES queries) x head.  Each wave owns 64
-// queries (two 32-column MFMA blocks) and walks all keys of its image in tiles
-// of 64.  The scores are computed transposed, S^T = K Q^T, so a lane holds one
-// query column: the row max and row sum are lane-local plus one exchange with
-// lane ^ 32, and the probabilities P^T are already in the B-operand layout of
-// the second product O^T = V^T P^T.  For that match the 64-key tile is stored
-// in LDS with bits 2 and 3 of the row index swapped (rows sigma(u)), so the 8
-// probabilities a lane holds per 16-key step are 8 consecutive keys.  V is
-// transposed into LDS (rows = head dims, 16-byte chunks XOR-swizzled by
-// d ^ (d >> 3)) so its A-operand fragments are single 16-byte reads.
+// Work item = (image, tile of 32*QB*WAVES queries) x head.  Each wave owns
+// 32*QB queries (QB column blocks of 32) and walks all keys of its image in
+// tiles of 64.
+//
+// * Scores are computed transposed, S^T = K Q^T, so a lane holds one query
+//   column: row max and row sum are lane-local plus one exchange with lane^32,
+//   and the probabilities P^T already sit in the B-operand layout of
+//   O^T = V^T P^T.  For that match, LDS row P of the key tile holds key
+//   sigma(P) (bits 2 and 3 swapped): the 8 probabilities a lane holds per
+//   16-key step are then 8 consecutive keys.
+// * Two LDS stages (tile kt in use, tile kt+1 in flight).  A three-stage
+//   variant computes tile kt+1's scores during tile kt's softmax; it needs 32
+//   more VGPRs, and the occupancy it costs outweighs the overlap it buys
+//   (measured), so the two-stage form is the default.
+// * K and V tiles go global -> LDS with global_load_lds_dwordx4 (no VGPR
+//   staging); the swizzles are applied by choosing which 16-byte chunk each
+//   lane fetches.  K chunks are XOR-swizzled by (row >> 1) & 7 for the
+//   16-byte fragment reads (64 banks, 16 lanes per pass); V stays row-major and its V^T A-operand fragments come
+//   from two ds_read_b64_tr_b16 transpose reads (each 16-lane group receives
+//   a 4-key x 16-dim block transposed), with chunks XOR-swizzled by
+//   2*(row & 3) so the four rows of a group hit distinct banks.
+// * Online softmax in the exp2 domain with the 1/8 scale folded into one FMA.
+//   The running max is only raised when a tile's max exceeds it by more than
+//   8 (log2 units), so most tiles skip the O rescale; probabilities are then
+//   bounded by 2^8.  Row sums use v_dot2 on the bf16 probabilities that feed
+//   the MFMA.
 #include "common.h"
 #include "kernels.h"
 
@@ -23,21 +39,40 @@ namespace pv {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int sigma_row(int r) {  // swap bits 2 and 3
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
 
-template <int WAVES>
+// K tile chunk swizzle: the LDS has 64 four-byte banks and serves a 16-byte
+// read for 16 lanes per pass, so the 16 rows a pass touches must differ in
+// (row parity, chunk): chunk ^ ((row >> 1) & 7) does that.
+__device__ __forceinline__ int kswz(int row) { return (row >> 1) & 7; }
+
+__device__ __forceinline__ float dot2_sum(uint32_t packed, float acc) {
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed), one, acc, false);
+}
+
+template <int QB, int WAVES, bool PIPE>
 __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NT = WAVES * 64;
-  constexpr int KCH = 512 / NT;  // K chunks (16 B) per thread per tile
-  constexpr int VIT = 256 / NT;  // V row-pair items per thread per tile
-  static_assert(KCH >= 1 && VIT >= 1, "WAVES must be 1, 2 or 4");
+  constexpr int SLOTS = 512;                 // 16-byte chunks per 64 x 64 bf16 tile
+  constexpr int LPT = SLOTS / NT;            // global_load_lds per thread per tile (K and V each)
+  // LDS stages.  PIPE: V(kt), K(kt+1) and tile kt+2 in flight, the scores of
+  // tile kt+1 computed during tile kt's softmax.  Otherwise: tile kt and
+  // tile kt+1 in flight.
+  constexpr int NS = PIPE ? 3 : 2;
+  static_assert(LPT >= 1 && SLOTS % NT == 0, "WAVES must divide 8");
 
-  __shared__ u32x4 kl[2][64 * 8];
-  __shared__ u32x4 vt[2][64 * 8];
+  __shared__ u32x4 kl[NS][SLOTS];
+  __shared__ u32x4 vl[NS][SLOTS];
 
   const int heads = a.heads;
   const int item = blockIdx.x / heads, head = blockIdx.x - item * heads;
@@ -52,13 +87,39 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 31, lhalf = lane >> 5;
-  const int wq0 = it.q0 + 64 * wave;  // first query of this wave
+  const int wq0 = it.q0 + 32 * QB * wave;  // first query of this wave
   const bool active = wq0 < n;
 
-  // ---- Q fragments (B operand of S^T = K Q^T), kept for the whole loop
-  u32x4 qf[2][4];
+  // ---- per-thread load plan: wave-instruction j covers slots
+  // [(wave*LPT + j) * 64, +64); lane l fetches slot p = that + l.
+  int k_row[LPT], k_chunk[LPT], v_row[LPT], v_chunk[LPT];
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
+  for (int j = 0; j < LPT; ++j) {
+    const int p = (wave * LPT + j) * 64 + lane;
+    const int P = p >> 3, pc = p & 7;
+    k_row[j] = sigma_row(P);
+    k_chunk[j] = pc ^ kswz(P);
+    v_row[j] = P;
+    v_chunk[j] = pc ^ (2 * (P & 3));
+  }
+  auto issue_loads = [&](int kt, int st) {
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      int uk = kt * 64 + k_row[j];
+      uk = uk < n ? uk : n - 1;
+      int uv = kt * 64 + v_row[j];
+      uv = uv < n ? uv : n - 1;
+      const uint16_t* gk = qkv + size_t(base + uk) * ld + koff + k_chunk[j] * 8;
+      const uint16_t* gv = qkv + size_t(base + uv) * ld + voff + v_chunk[j] * 8;
+      __builtin_amdgcn_global_load_lds(gk, (lds_void*)&kl[st][(wave * LPT + j) * 64], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(gv, (lds_void*)&vl[st][(wave * LPT + j) * 64], 16, 0, 0);
+    }
+  };
+
+  // ---- Q fragments (B operand of S^T = K Q^T), kept for the whole loop
+  u32x4 qf[QB][4];
+#pragma unroll
+  for (int tb = 0; tb < QB; ++tb) {
     int t = wq0 + 32 * tb + lrow;
     t = t < n ? t : n - 1;
     const uint16_t* qp = qkv + size_t(base + t) * ld + qoff + 8 * lhalf;
@@ -66,87 +127,72 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
     for (int ks = 0; ks < 4; ++ks) qf[tb][ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
   }
 
-  floatx16 o[2][2];
+  floatx16 o[2][QB];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < QB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) o[i][j][v] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
+  float m_sc[QB], l_run[QB];
+#pragma unroll
+  for (int tb = 0; tb < QB; ++tb) {
+    m_sc[tb] = -INFINITY;  // running max, in scaled (log2) units
+    l_run[tb] = 0.f;
+  }
   const float c = kLog2e * 0.125f;  // log2(e) / sqrt(64)
 
-  // ---- staging of one 64-key tile: registers <- global, LDS <- registers
-  u32x4 rk[KCH], rv[VIT][2];
-  auto gload = [&](int kt) {
+  // transposed-read addresses for the V^T fragments: 16-lane group g gets
+  // dims D0 + (lane % 16), keys U..U+3 (and U+4..U+7 from the second read)
+  const int g = lane >> 4, r16 = lane & 15;
+  const int tr_row = 8 * (g >> 1) + (r16 >> 2);          // + ub*32 + sp*16 (+4)
+  const int tr_col = 16 * (g & 1) + 4 * (r16 & 3);       // + db*32 (elements)
+
+  // S^T block of one key tile (stage st)
+  auto scores = [&](int st, floatx16 (&s)[2][QB]) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = tid + NT * i, row = id >> 3, ch = id & 7;
-      int u = kt * 64 + row;
-      u = u < n ? u : n - 1;
-      rk[i] = *reinterpret_cast<const u32x4*>(qkv + size_t(base + u) * ld + koff + ch * 8);
-    }
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-      const int id = tid + NT * i, pr = id >> 3, ch = id & 7;
-      int u0 = kt * 64 + 2 * pr, u1 = u0 + 1;
-      u0 = u0 < n ? u0 : n - 1;
-      u1 = u1 < n ? u1 : n - 1;
-      rv[i][0] = *reinterpret_cast<const u32x4*>(qkv + size_t(base + u0) * ld + voff + ch * 8);
-      rv[i][1] = *reinterpret_cast<const u32x4*>(qkv + size_t(base + u1) * ld + voff + ch * 8);
-    }
-  };
-  auto sstore = [&](int buf) {
+      for (int ub = 0; ub < 2; ++ub) {
+        const int row = ub * 32 + lrow;
+        const u32x4 kf = kl[st][row * 8 + ((2 * ks + lhalf) ^ kswz(row))];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = tid + NT * i, row = id >> 3, ch = id & 7;
-      const int srow = sigma_row(row);
-      kl[buf][srow * 8 + (ch ^ (srow & 7))] = rk[i];
-    }
-    uint32_t* vw = reinterpret_cast<uint32_t*>(vt[buf]);
-#pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-      const int id = tid + NT * i, pr = id >> 3, ch = id & 7;
-      // word (pr) of row d holds keys (2pr, 2pr+1) of head dim d
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int d = ch * 8 + j;
-        const uint32_t w0 = rv[i][0][j >> 1], w1 = rv[i][1][j >> 1];
-        const uint32_t lo = (j & 1) ? (w0 >> 16) : (w0 & 0xffffu);
-        const uint32_t hi = (j & 1) ? (w1 & 0xffff0000u) : (w1 << 16);
-        const int pchunk = (pr >> 2) ^ vt_swz(d);
-        vw[d * 32 + pchunk * 4 + (pr & 3)] = lo | hi;
+        for (int tb = 0; tb < QB; ++tb) {
+          if (ks == 0) {
+            const floatx16 z = {};
+            s[ub][tb] = mfma32x32x16(kf, qf[tb][ks], z);
+          } else {
+            s[ub][tb] = mfma32x32x16(kf, qf[tb][ks], s[ub][tb]);
+          }
+        }
       }
     }
   };
 
   const int nkt = (n + 63) / 64;
-  gload(0);
-  sstore(0);
+  issue_loads(0, 0);
+  if (PIPE && nkt > 1) issue_loads(1, 1);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  floatx16 s_cur[2][QB];
+  if (PIPE && active) scores(0, s_cur);
+
   for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) gload(kt + 1);
+    const int st_v = kt % NS, st_k = (kt + 1) % NS;
+    if (PIPE) {
+      if (kt + 2 < nkt) issue_loads(kt + 2, (kt + 2) % NS);
+    } else {
+      if (kt + 1 < nkt) issue_loads(kt + 1, st_k);
+    }
     if (active) {
-      // ---- S^T = K Q^T
-      floatx16 s[2][2];
-#pragma unroll
-      for (int ub = 0; ub < 2; ++ub)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) s[ub][tb][v] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int ub = 0; ub < 2; ++ub) {
-          const int row = ub * 32 + lrow;
-          const u32x4 kf = kl[buf][row * 8 + ((2 * ks + lhalf) ^ (row & 7))];
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb) s[ub][tb] = mfma32x32x16(kf, qf[tb][ks], s[ub][tb]);
-        }
+      // ---- PIPE: next tile's scores, independent of this tile's softmax, so
+      // their MFMAs can overlap the exp work below
+      floatx16 s_nxt[2][QB];
+      if (PIPE) {
+        if (kt + 1 < nkt) scores(st_k, s_nxt);
+      } else {
+        scores(st_v, s_cur);
       }
       // ---- mask keys past the image (last tile only)
       if (kt * 64 + 64 > n) {
@@ -156,56 +202,82 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
           for (int v = 0; v < 16; ++v) {
             const int u = kt * 64 + ub * 32 + 16 * (v >> 3) + 8 * lhalf + (v & 7);
             if (u >= n) {
-              s[ub][0][v] = -INFINITY;
-              s[ub][1][v] = -INFINITY;
+#pragma unroll
+              for (int tb = 0; tb < QB; ++tb) s_cur[ub][tb][v] = -INFINITY;
             }
           }
       }
-      // ---- online softmax (exp2 with the 1/8 scale folded in)
-      u32x4 pf[2][2][2];
+      // ---- online softmax
+      u32x4 pf[2][QB][2];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        float mx = s[0][tb][0];
+      for (int tb = 0; tb < QB; ++tb) {
+        float mx = s_cur[0][tb][0];
 #pragma unroll
         for (int ub = 0; ub < 2; ++ub)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[ub][tb][v]);
-        mx = pair_max32(mx);
-        const float m_new = fmaxf(m_run[tb], mx);
-        const float alpha = __builtin_amdgcn_exp2f((m_run[tb] - m_new) * c);
-        m_run[tb] = m_new;
-        l_run[tb] *= alpha;
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s_cur[ub][tb][v]);
+        mx = pair_max32(mx) * c;
+        if (__any(mx > m_sc[tb] + kRescaleSlack)) {
+          const float m_new = fmaxf(m_sc[tb], mx);
+          float alpha = __builtin_amdgcn_exp2f(m_sc[tb] - m_new);
+          // keeps the rescale a rarely-taken branch (otherwise it becomes an
+          // unconditional multiply by a selected factor)
+          asm volatile("" : "+v"(alpha));
+          m_sc[tb] = m_new;
+          l_run[tb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+          for (int db = 0; db < 2; ++db)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) o[db][tb][v] *= alpha;
-        const float mc = m_new * c;
+            for (int v = 0; v < 16; ++v) o[db][tb][v] *= alpha;
+        }
+        const float mneg = -m_sc[tb];
 #pragma unroll
         for (int ub = 0; ub < 2; ++ub) {
-          float p[16];
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ub][tb][v], c, -mc));
-            l_run[tb] += p[v];
+          for (int sp = 0; sp < 2; ++sp) {
+            float p[8];
+#pragma unroll
+            for (int v = 0; v < 8; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[ub][tb][8 * sp + v], c, mneg));
+            const u32x4 pk = pack8(p);
+            pf[ub][tb][sp] = pk;
+            l_run[tb] = dot2_sum(pk[0], l_run[tb]);
+            l_run[tb] = dot2_sum(pk[1], l_run[tb]);
+            l_run[tb] = dot2_sum(pk[2], l_run[tb]);
+            l_run[tb] = dot2_sum(pk[3], l_run[tb]);
           }
-          pf[ub][tb][0] = pack8(p);
-          pf[ub][tb][1] = pack8(p + 8);
         }
       }
       // ---- O^T += V^T P^T
+      const uint16_t* vb = reinterpret_cast<const uint16_t*>(vl[st_v]);
 #pragma unroll
       for (int ub = 0; ub < 2; ++ub)
 #pragma unroll
         for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
           for (int db = 0; db < 2; ++db) {
-            const int d = db * 32 + lrow;
-            const u32x4 vf = vt[buf][d * 8 + ((4 * ub + 2 * sp + lhalf) ^ vt_swz(d))];
+            u32x4 vf;
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) o[db][tb] = mfma32x32x16(vf, pf[ub][tb][sp], o[db][tb]);
+            for (int half = 0; half < 2; ++half) {
+              const int row = ub * 32 + sp * 16 + tr_row + 4 * half;
+              const int col = db * 32 + tr_col;  // element; chunk = col / 8
+              const int pchunk = (col >> 3) ^ (2 * (row & 3));
+              const uint16_t* addr = vb + row * 64 + pchunk * 8 + (col & 7);
+              const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)addr);
+              const u32x2 w = __builtin_bit_cast(u32x2, r);
+              vf[2 * half] = w[0];
+              vf[2 * half + 1] = w[1];
+            }
+#pragma unroll
+            for (int tb = 0; tb < QB; ++tb) o[db][tb] = mfma32x32x16(vf, pf[ub][tb][sp], o[db][tb]);
           }
+      if (PIPE) {
+#pragma unroll
+        for (int ub = 0; ub < 2; ++ub)
+#pragma unroll
+          for (int tb = 0; tb < QB; ++tb) s_cur[ub][tb] = s_nxt[ub][tb];
+      }
     }
-    if (kt + 1 < nkt) sstore(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -213,7 +285,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
   // ---- normalise and store: lane holds query column t, dims 8*(v/4)+4*half+(v%4)
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
+  for (int tb = 0; tb < QB; ++tb) {
     const float inv = 1.f / pair_sum32(l_run[tb]);
     const int t = wq0 + 32 * tb + lrow;
     if (t < n) {
@@ -235,8 +307,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
 
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.n_items <= 0) return hipSuccess;
-  static_assert(kAttnQTileBf16 == 256, "q tile must match the kernel's 4 waves x 64 queries");
-  hipLaunchKernelGGL(attn_bf16_kernel<4>, dim3(a.n_items * a.heads), dim3(256), 0, s, a);
+  static_assert(kAttnQTileBf16 == 32 * PV_ATTN_QB * PV_ATTN_WAVES, "q tile must match the kernel shape");
+  hipLaunchKernelGGL((attn_bf16_kernel<PV_ATTN_QB, PV_ATTN_WAVES, PV_ATTN_PIPE != 0>), dim3(a.n_items * a.heads),
+                     dim3(PV_ATTN_WAVES * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -200,6 +200,7 @@ hipError_t gemm_f32(GemmKind kind, const GemmArgs& g, hipStream_t s) {
     case GEMM_DOWN:   return launch<A_DENSE, B_ONE, E_ADD_F32>(g, s);
     case GEMM_MERGE:  return launch<A_MERGE, B_ONE, E_STORE>(g, s);
     case GEMM_PLAIN:  return launch<A_DENSE, B_ONE, E_STORE>(g, s);
+    case GEMM_MERGE_F32: return launch<A_MERGE, B_ONE, E_STORE>(g, s);
   }
   return hipErrorInvalidValue;
 }

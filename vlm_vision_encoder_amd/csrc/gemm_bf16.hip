@@ -14,8 +14,9 @@
 // each wave owns a (BM/2) x (BN/2) tile of 32x32 MFMA blocks.  A and B tiles
 // are staged through registers into double-buffered LDS (one barrier per
 // k-tile); rows are 128 bytes = 8 chunks of 16 bytes, and chunk c of row r is
-// stored at c ^ (r & 7) so the 16-byte fragment reads of 8 consecutive rows hit
-// distinct banks.  Blocks are renumbered so each XCD (blocks b with the same
+// stored at c ^ ((r >> 1) & 7): the LDS has 64 four-byte banks and serves a
+// 16-byte read for 16 lanes (16 consecutive rows) per pass, which then differ
+// in (row parity, chunk) and hit distinct banks.  Blocks are renumbered so each XCD (blocks b with the same
 // b % 8) works on a contiguous range of output tiles, which keeps the A panel
 // and the weights it shares in that XCD's L2.
 #include "common.h"
@@ -25,7 +26,16 @@ namespace pv {
 
 namespace {
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 constexpr int BK = 64;
+constexpr int kNumCUs = 256;  // MI355X: 8 XCDs x 32 CUs
+// tile rows per group of the persistent dense GEMM's tile order
+#ifndef PV_GEMM_GM
+#define PV_GEMM_GM 4
+#endif
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 __device__ __forceinline__ int xcd_remap(int b, int nblocks) {
   const int xcd = b & 7, idx = b >> 3;
@@ -40,11 +50,26 @@ struct ARow {
   int32_t src[4] = {0, 0, 0, 0};  // A_MERGE: source patch rows
 };
 
-// Loads the 8 bf16 values A[row][k0 .. k0+8) for one thread's chunk.
+// fp32 values -> bf16 hi and bf16 lo = bf16(x - hi): hi + lo carries about
+// 16 mantissa bits, so a product over both halves keeps the fp32 operand's
+// precision to within the accumulation error.
+__device__ __forceinline__ void split8(const float* f, u32x4& hi, u32x4& lo) {
+  hi = pack8(f);
+  float r[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[2 * e] = f[2 * e] - lo_bf16(hi[e]);
+    r[2 * e + 1] = f[2 * e + 1] - hi_bf16(hi[e]);
+  }
+  lo = pack8(r);
+}
+
+// Loads A[row][k0 .. k0+8) for one thread's chunk: bf16 rows are copied; the
+// fp32 operands (pixels, residual) are split into bf16 hi and lo parts.
 template <int AM>
-__device__ __forceinline__ u32x4 load_a_chunk(const GemmArgs& g, const ARow<AM>& r, int k0) {
+__device__ __forceinline__ void load_a_chunk(const GemmArgs& g, const ARow<AM>& r, int k0, u32x4& hi, u32x4& lo) {
   if constexpr (AM == A_DENSE) {
-    return *reinterpret_cast<const u32x4*>(r.p0 + size_t(k0) * 2);
+    hi = *reinterpret_cast<const u32x4*>(r.p0 + size_t(k0) * 2);
   } else if constexpr (AM == A_IM2COL) {
     const int p = g.maps.patch, pp = p * p;
     const float* base = reinterpret_cast<const float*>(r.p0);
@@ -60,7 +85,7 @@ __device__ __forceinline__ u32x4 load_a_chunk(const GemmArgs& g, const ARow<AM>&
       }
       f[e] = v;
     }
-    return pack8(f);
+    split8(f, hi, lo);
   } else {
     const int D = g.hidden;
     const int q = k0 / D, ch = k0 - q * D;
@@ -68,7 +93,7 @@ __device__ __forceinline__ u32x4 load_a_chunk(const GemmArgs& g, const ARow<AM>&
     const floatx4 a = *reinterpret_cast<const floatx4*>(src);
     const floatx4 b = *reinterpret_cast<const floatx4*>(src + 4);
     float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    return pack8(f);
+    split8(f, hi, lo);
   }
 }
 
@@ -114,6 +139,64 @@ __device__ __forceinline__ const char* b_row(const GemmArgs& g, int n) {
   }
 }
 
+// Epilogue of one wave's TM x TN grid of 32x32 accumulator blocks whose
+// top-left output element is (m_base, n_base).  C layout of a 32x32 block:
+// lane holds column (lane & 31) and rows 8*(v/4) + 4*(lane/32) + (v%4).
+template <int EM, int TM, int TN>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[TM][TN], int m_base, int n_base,
+                                         int lrow, int lhalf) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = m_base + 32 * i + 8 * (v >> 2) + 4 * lhalf + (v & 3);
+      const bool ok = row < g.M;
+      if constexpr (EM == E_SILU_MUL) {
+#pragma unroll
+        for (int jj = 0; jj < TN / 2; ++jj) {
+          const float gt = acc[i][2 * jj][v], up = acc[i][2 * jj + 1][v];
+          const float sv = gt / (1.f + __expf(-gt)) * up;
+          const int col = (n_base + 64 * jj) / 2 + lrow;
+          if (ok) reinterpret_cast<bf16*>(g.C)[size_t(row) * g.ldc + col] = (bf16)sv;
+        }
+      } else if constexpr (EM == E_QKV_ROPE) {
+        int rc = 0;
+        if (ok) rc = g.maps.rowinfo[2 * row + 1];
+        const int pr = rc >> 16, pc = rc & 0xffff;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = n_base + 32 * j + lrow;
+          float x = acc[i][j][v];
+          const float xp = swap_adjacent(x);
+          if (col < 2 * g.hidden) {
+            const int d = col & 63, pair = d >> 1;
+            const int axis = pair >> 4, m = pair & 15;
+            const int pos = axis ? pc : pr;
+            const float2 cs = reinterpret_cast<const float2*>(g.maps.rope)[(axis * g.maps.rope_maxpos + pos) * 16 + m];
+            // even lane: x0 cos - x1 sin ; odd lane: x0 sin + x1 cos
+            x = (d & 1) ? (xp * cs.y + x * cs.x) : (x * cs.x - xp * cs.y);
+          }
+          if (ok) reinterpret_cast<bf16*>(g.C)[size_t(row) * g.ldc + col] = (bf16)x;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = n_base + 32 * j + lrow;
+          if (!ok || col >= g.N) continue;
+          const size_t o = size_t(row) * g.ldc + col;
+          if constexpr (EM == E_STORE) {
+            reinterpret_cast<bf16*>(g.C)[o] = (bf16)acc[i][j][v];
+          } else if constexpr (EM == E_STORE_F32) {
+            reinterpret_cast<float*>(g.C)[o] = acc[i][j][v];
+          } else {
+            reinterpret_cast<float*>(g.C)[o] += acc[i][j][v];
+          }
+        }
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int AM, int BMD, int EM>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int WM = BM / 2, WN = BN / 2;
@@ -122,8 +205,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int BC = BN * 8 / 256;
   static_assert(AC >= 1 && BC >= 1, "tile too small");
   static_assert(EM != E_SILU_MUL || (TN % 2) == 0, "silu-mul needs gate/up block pairs in a wave");
+  // fp32 A operands (pixels, residual) run as two bf16 products, hi and lo
+  constexpr bool SPLIT = AM != A_DENSE;
+  constexpr int AROWS = SPLIT ? 2 * BM : BM;  // LDS rows of the A tile(s)
 
-  __shared__ u32x4 lds[2][(BM + BN) * 8];
+  __shared__ u32x4 lds[2][(AROWS + BN) * 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -142,11 +228,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   for (int i = 0; i < BC; ++i) brow[i] = b_row<BMD>(g, n0 + ((tid + 256 * i) >> 3));
   const int cchunk = tid & 7;
 
-  u32x4 ra[AC], rb[BC];
+  u32x4 ra[AC], ral[SPLIT ? AC : 1], rb[BC];
   auto gload = [&](int kt) {
     const int k0 = kt * BK + cchunk * 8;
 #pragma unroll
-    for (int i = 0; i < AC; ++i) ra[i] = load_a_chunk<AM>(g, arow[i], k0);
+    for (int i = 0; i < AC; ++i) load_a_chunk<AM>(g, arow[i], k0, ra[i], ral[SPLIT ? i : 0]);
 #pragma unroll
     for (int i = 0; i < BC; ++i) {
       if constexpr (AM == A_IM2COL) {
@@ -171,12 +257,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < AC; ++i) {
       const int row = (tid + 256 * i) >> 3;
-      lds[buf][row * 8 + (cchunk ^ (row & 7))] = ra[i];
+      lds[buf][row * 8 + (cchunk ^ swz(row))] = ra[i];
+      if constexpr (SPLIT) lds[buf][(BM + row) * 8 + (cchunk ^ swz(row))] = ral[i];
     }
 #pragma unroll
     for (int i = 0; i < BC; ++i) {
       const int row = (tid + 256 * i) >> 3;
-      lds[buf][(BM + row) * 8 + (cchunk ^ (row & 7))] = rb[i];
+      lds[buf][(AROWS + row) * 8 + (cchunk ^ swz(row))] = rb[i];
     }
   };
 
@@ -198,7 +285,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
     const int buf = kt & 1;
     if (kt + 1 < KT) gload(kt + 1);
     const u32x4* sa = lds[buf];
-    const u32x4* sb = lds[buf] + BM * 8;
+    const u32x4* sb = lds[buf] + AROWS * 8;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int ch = 2 * ks + lhalf;
@@ -206,75 +293,210 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int row = wm * WM + 32 * i + lrow;
-        fa[i] = sa[row * 8 + (ch ^ (row & 7))];
+        fa[i] = sa[row * 8 + (ch ^ swz(row))];
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int row = wn * WN + 32 * j + lrow;
-        fb[j] = sb[row * 8 + (ch ^ (row & 7))];
+        fb[j] = sb[row * 8 + (ch ^ swz(row))];
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
+      if constexpr (SPLIT) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int row = BM + wm * WM + 32 * i + lrow;
+          fa[i] = sa[row * 8 + (ch ^ swz(row))];
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
+      }
     }
     if (kt + 1 < KT) sstore(buf ^ 1);
     __syncthreads();
   }
 
-  // ---------------------------------------------------------------- epilogue
-  // C layout of a 32x32 block: lane holds column (lane & 31) and rows
-  // 8*(v/4) + 4*(lane/32) + (v%4), v = 0..15.
+  epilogue<EM, TM, TN>(g, acc, m0 + wm * WM, n0 + wn * WN, lrow, lhalf);
+}
+
+
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Dense-A GEMM (q,k,v, out-projection, gate/up, down), persistent: each
+// workgroup walks a fixed list of output tiles, and the global -> LDS load
+// ring (global_load_lds_dwordx4, NS stages, no VGPR staging) runs over the
+// flattened sequence of (tile, k-tile) steps, so the next tile's first
+// k-tiles are already in flight while the current tile finishes and writes
+// its epilogue.  The chunk swizzle is applied by choosing which chunk each
+// lane fetches.  Waves are arranged WMW x WNW; each computes a
+// (BM/WMW) x (BN/WNW) tile of 32x32 MFMA blocks.  Tiles are numbered so the
+// workgroups of one XCD (blocks b with equal b % 8) share a contiguous range
+// of tiles, grouped GM tile rows at a time, keeping the A and B panels they
+// share in that XCD's L2.
+template <int BM, int BN, int WMW, int WNW, int NS, int BMD, int EM>
+__global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) {
+  constexpr int NW = WMW * WNW, NT = NW * 64;
+  constexpr int TMW = BM / WMW, TNW = BN / WNW;  // wave tile
+  constexpr int TM = TMW / 32, TN = TNW / 32;
+  constexpr int A_LD = BM * 8 / NT, B_LD = BN * 8 / NT;  // global_load_lds per thread per k-tile
+  constexpr int LDT = A_LD + B_LD;
+  static_assert(A_LD >= 1 && B_LD >= 1 && (BM * 8) % NT == 0 && (BN * 8) % NT == 0, "tile/thread mismatch");
+  static_assert(EM != E_SILU_MUL || (TN % 2) == 0, "silu-mul needs gate/up block pairs in a wave");
+  static_assert((NS - 2) * LDT <= 63, "vmcnt range");
+
+  __shared__ u32x4 lds[NS][(BM + BN) * 8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WNW, wn = wave % WNW;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int tiles_n = (BMD == B_GATEUP ? 2 * g.N : g.N) / BN;
+  const int tiles_m = (g.M + BM - 1) / BM;
+  const int ntiles = tiles_m * tiles_n;
+  const int KT = g.K / BK;
+
+  // this workgroup's tiles: the blocks b with equal x = b % 8 (one XCD, nx
+  // of them populated) own tiles [lo_x, hi_x); the nb_x blocks of XCD x
+  // (index j = b / 8) take every nb_x-th of them
+  const int nblk = gridDim.x, b = blockIdx.x;
+  const int nx = nblk < 8 ? nblk : 8;
+  const int x = b & 7, j = b >> 3;
+  const int nb_x = (nblk - x + 7) >> 3;
+  const int lo_x = int((long long)ntiles * x / nx), hi_x = int((long long)ntiles * (x + 1) / nx);
+  const int my_tiles = (hi_x - lo_x > j) ? (hi_x - lo_x - j + nb_x - 1) / nb_x : 0;
+  const int steps = my_tiles * KT;
+  // logical tile L -> (tm, tn) in groups of GM tile rows, column-major inside
+  // a group: the ~32 consecutive tiles an XCD runs at once form a
+  // GM x (32/GM) block, so L2 serves both their A and their B panels
+  auto tile_of = [&](int i) { return lo_x + j + i * nb_x; };
+  auto tile_mn = [&](int L, int& tm, int& tn) {
+    const int per_group = PV_GEMM_GM * tiles_n;
+    const int grp = L / per_group, first_m = grp * PV_GEMM_GM;
+    const int rows = (tiles_m - first_m) < PV_GEMM_GM ? (tiles_m - first_m) : PV_GEMM_GM;
+    const int r = L - grp * per_group;
+    tm = first_m + r % rows;
+    tn = r / rows;
+  };
+
+  // load plan: wave instruction q of this wave fills LDS slots
+  // [(wave * X_LD + q) * 64, +64) of the A (B) tile; lane l takes slot p.
+  const char* ga[A_LD];
+  const char* gb[B_LD];
+  auto set_rows = [&](int t) {
+    int tm, tn;
+    tile_mn(t, tm, tn);
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+    for (int q = 0; q < A_LD; ++q) {
+      const int p = (wave * A_LD + q) * 64 + lane;
+      const int P = p >> 3, gc = (p & 7) ^ swz(P);
+      int m = tm * BM + P;
+      m = m < g.M ? m : g.M - 1;
+      ga[q] = reinterpret_cast<const char*>(g.A) + (size_t(m) * g.lda + gc * 8) * 2;
+    }
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * lhalf + (v & 3);
-      const bool ok = row < g.M;
-      if constexpr (EM == E_SILU_MUL) {
+    for (int q = 0; q < B_LD; ++q) {
+      const int p = (wave * B_LD + q) * 64 + lane;
+      const int P = p >> 3, gc = (p & 7) ^ swz(P);
+      gb[q] = b_row<BMD>(g, tn * BN + P) + gc * 16;
+    }
+  };
+  // (the global source is passed as a uint16_t pointer: with a char pointer
+  // the host pass drops the kernel's launch stub without a diagnostic)
+  int is_step = 0, is_kt = 0, is_tile = 0;  // next step to issue
+  auto issue_next = [&]() {
+    if (is_kt == 0) set_rows(tile_of(is_tile));
+    const int st = is_step % NS;
+    const size_t koff = size_t(is_kt) * BK * 2;
 #pragma unroll
-        for (int jj = 0; jj < TN / 2; ++jj) {
-          const float gt = acc[i][2 * jj][v], up = acc[i][2 * jj + 1][v];
-          const float s = gt / (1.f + __expf(-gt)) * up;
-          const int col = (n0 + wn * WN + 64 * jj) / 2 + lrow;
-          if (ok) reinterpret_cast<bf16*>(g.C)[size_t(row) * g.ldc + col] = (bf16)s;
-        }
-      } else if constexpr (EM == E_QKV_ROPE) {
-        int rc = 0;
-        if (ok) rc = g.maps.rowinfo[2 * row + 1];
-        const int pr = rc >> 16, pc = rc & 0xffff;
+    for (int q = 0; q < A_LD; ++q)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(ga[q] + koff),
+                                       (lds_void*)&lds[st][(wave * A_LD + q) * 64], 16, 0, 0);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = n0 + wn * WN + 32 * j + lrow;
-          float x = acc[i][j][v];
-          const float xp = swap_adjacent(x);
-          if (col < 2 * g.hidden) {
-            const int d = col & 63, pair = d >> 1;
-            const int axis = pair >> 4, m = pair & 15;
-            const int pos = axis ? pc : pr;
-            const float2 cs = reinterpret_cast<const float2*>(g.maps.rope)[(axis * g.maps.rope_maxpos + pos) * 16 + m];
-            // even lane: x0 cos - x1 sin ; odd lane: x0 sin + x1 cos
-            x = (d & 1) ? (xp * cs.y + x * cs.x) : (x * cs.x - xp * cs.y);
-          }
-          if (ok) reinterpret_cast<bf16*>(g.C)[size_t(row) * g.ldc + col] = (bf16)x;
-        }
-      } else {
+    for (int q = 0; q < B_LD; ++q)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(gb[q] + koff),
+                                       (lds_void*)&lds[st][BM * 8 + (wave * B_LD + q) * 64], 16, 0, 0);
+    ++is_step;
+    if (++is_kt == KT) {
+      is_kt = 0;
+      ++is_tile;
+    }
+  };
+
+  floatx16 acc[TM][TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = n0 + wn * WN + 32 * j + lrow;
-          if (!ok || col >= g.N) continue;
-          const size_t o = size_t(row) * g.ldc + col;
-          if constexpr (EM == E_STORE) {
-            reinterpret_cast<bf16*>(g.C)[o] = (bf16)acc[i][j][v];
-          } else if constexpr (EM == E_STORE_F32) {
-            reinterpret_cast<float*>(g.C)[o] = acc[i][j][v];
-          } else {
-            reinterpret_cast<float*>(g.C)[o] += acc[i][j][v];
-          }
-        }
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][jn][v] = 0.f;
+
+  for (int st = 0; st < NS - 1; ++st)
+    if (is_step < steps) issue_next();
+
+  int kt = 0, ti = 0;
+  for (int step = 0; step < steps; ++step) {
+    // step has landed once at most (steps issued after it) x LDT loads of
+    // this thread are outstanding; the barrier makes every thread's part
+    // visible and frees the stage read in the previous step
+    if (step + NS - 2 < steps) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LDT));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    __syncthreads();
+    if (is_step < steps) issue_next();
+    const u32x4* sa = lds[step % NS];
+    const u32x4* sb = lds[step % NS] + BM * 8;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int ch = 2 * ks + lhalf;
+      u32x4 fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * TMW + 32 * i + lrow;
+        fa[i] = sa[row * 8 + (ch ^ swz(row))];
       }
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn) {
+        const int row = wn * TNW + 32 * jn + lrow;
+        fb[jn] = sb[row * 8 + (ch ^ swz(row))];
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn) acc[i][jn] = mfma32x32x16(fa[i], fb[jn], acc[i][jn]);
+    }
+    if (++kt == KT) {
+      int tm, tn;
+      tile_mn(tile_of(ti), tm, tn);
+      epilogue<EM, TM, TN>(g, acc, tm * BM + wm * TMW, tn * BN + wn * TNW, lrow, lhalf);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[i][jn][v] = 0.f;
+      kt = 0;
+      ++ti;
     }
   }
+}
+
+template <int BM, int BN, int WMW, int WNW, int NS, int BMD, int EM>
+hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
+  const int ncols = (BMD == B_GATEUP) ? 2 * g.N : g.N;
+  if (ncols % BN || g.K % BK) return hipErrorInvalidValue;
+  const int tiles = ((g.M + BM - 1) / BM) * (ncols / BN);
+  // one resident workgroup per CU (the LDS ring takes most of the 160 KiB)
+  const int grid = tiles < kNumCUs ? tiles : kNumCUs;
+  hipLaunchKernelGGL((gemm_dense_kernel<BM, BN, WMW, WNW, NS, BMD, EM>), dim3(grid), dim3(WMW * WNW * 64), 0, s, g);
+  return hipGetLastError();
 }
 
 template <int BM, int BN, int AM, int BMD, int EM>
@@ -288,16 +510,26 @@ hipError_t launch(const GemmArgs& g, hipStream_t s) {
 
 }  // namespace
 
+// Tile configurations (BM, BN, waves along M, waves along N, LDS stages) of
+// the dense GEMMs: wide-N products and the N = hidden products.
+#ifndef PV_GEMM_CFG_BIG
+#define PV_GEMM_CFG_BIG 256, 256, 4, 2, 2
+#endif
+#ifndef PV_GEMM_CFG_N1K
+#define PV_GEMM_CFG_N1K 256, 128, 4, 2, 2
+#endif
+
 hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
   switch (kind) {
     case GEMM_PATCH:  return launch<128, 128, A_IM2COL, B_ONE, E_STORE_F32>(g, s);
-    case GEMM_QKV:    return launch<128, 128, A_DENSE, B_QKV, E_QKV_ROPE>(g, s);
-    case GEMM_OPROJ:  return launch<128, 128, A_DENSE, B_ONE, E_ADD_F32>(g, s);
-    case GEMM_GATEUP: return launch<128, 128, A_DENSE, B_GATEUP, E_SILU_MUL>(g, s);
-    case GEMM_DOWN:   return launch<128, 128, A_DENSE, B_ONE, E_ADD_F32>(g, s);
+    case GEMM_QKV:    return launch_dense<PV_GEMM_CFG_BIG, B_QKV, E_QKV_ROPE>(g, s);
+    case GEMM_OPROJ:  return launch_dense<PV_GEMM_CFG_N1K, B_ONE, E_ADD_F32>(g, s);
+    case GEMM_GATEUP: return launch_dense<PV_GEMM_CFG_BIG, B_GATEUP, E_SILU_MUL>(g, s);
+    case GEMM_DOWN:   return launch_dense<PV_GEMM_CFG_N1K, B_ONE, E_ADD_F32>(g, s);
     case GEMM_MERGE:  return launch<128, 128, A_MERGE, B_ONE, E_STORE>(g, s);
-    case GEMM_PLAIN:  return launch<128, 128, A_DENSE, B_ONE, E_STORE>(g, s);
+    case GEMM_PLAIN:  return launch_dense<PV_GEMM_CFG_N1K, B_ONE, E_STORE>(g, s);
+    case GEMM_MERGE_F32: return launch<128, 128, A_MERGE, B_ONE, E_STORE_F32>(g, s);
   }
   return hipErrorInvalidValue;
 }

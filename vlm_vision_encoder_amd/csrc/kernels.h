@@ -15,7 +15,8 @@ enum GemmKind {
   GEMM_GATEUP = 3,  // silu(y gate^T) * (y up^T) -> bf16
   GEMM_DOWN = 4,    // hm x w_down^T added into the fp32 residual
   GEMM_MERGE = 5,   // gather2x2(residual) x merge_w^T -> bf16 out
-  GEMM_PLAIN = 6    // dense A x B^T -> bf16 (tests and measurement)
+  GEMM_PLAIN = 6,   // dense A x B^T -> bf16 (tests and measurement)
+  GEMM_MERGE_F32 = 7  // as GEMM_MERGE with an fp32 output
 };
 
 // bf16 MFMA GEMM family (gemm_bf16.hip).
@@ -44,7 +45,18 @@ struct AttnArgs {
 };
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t attention_f32(const AttnArgs& a, hipStream_t s);
-constexpr int kAttnQTileBf16 = 256;
+// bf16 attention shape: each wave owns 32 * PV_ATTN_QB queries, a work item
+// PV_ATTN_WAVES waves.
+#ifndef PV_ATTN_QB
+#define PV_ATTN_QB 1
+#endif
+#ifndef PV_ATTN_WAVES
+#define PV_ATTN_WAVES 8
+#endif
+#ifndef PV_ATTN_PIPE
+#define PV_ATTN_PIPE 0
+#endif
+constexpr int kAttnQTileBf16 = 32 * PV_ATTN_QB * PV_ATTN_WAVES;
 constexpr int kAttnQTileF32 = 64;
 
 // Per-row maps from per-image metadata (maps.hip):

@@ -260,14 +260,15 @@ pv_status run_tower(pv_tower* t, const float* pixels, const pv::Plan& plan, void
   }
   if (st.stage >= 0) return fail(PV_ERR_ARG, "stage/layer not reached");
 
+  const bool out_bf16 = bf && c.out_dtype == PV_BF16;
   if (c.merge == 2) {
     pv::GemmArgs a = g;
     a.M = int(plan.out_rows); a.N = c.out_dim; a.K = 4 * D;
     a.A = r; a.lda = D;
     a.B0 = t->w.merge_w; a.ldb = 4 * D;
     a.C = out; a.ldc = c.out_dim;
-    PV_LAUNCH(PV_K_MERGE, gemm(pv::GEMM_MERGE, a));
-  } else if (bf) {
+    PV_LAUNCH(PV_K_MERGE, gemm(out_bf16 ? pv::GEMM_MERGE : pv::GEMM_MERGE_F32, a));
+  } else if (out_bf16) {
     PV_LAUNCH(PV_K_MERGE, pv::f32_to_bf16(r, out, size_t(N) * D, s));
   } else {
     PV_HIP(hipMemcpyAsync(out, r, size_t(N) * D * 4, hipMemcpyDeviceToDevice, s));
@@ -310,6 +311,7 @@ pv_status pv_tower_create(const pv_config* cfg, const pv_weights* w, pv_tower** 
   *out = nullptr;
   const pv_config& c = *cfg;
   if (c.dtype != PV_BF16 && c.dtype != PV_F32) return fail(PV_ERR_ARG, "dtype must be PV_BF16 or PV_F32");
+  if (c.out_dtype != PV_BF16 && c.out_dtype != PV_F32) return fail(PV_ERR_ARG, "out_dtype must be PV_BF16 or PV_F32");
   if (c.patch < 1 || c.patch > 64) return fail(PV_ERR_ARG, "patch must be in [1, 64]");
   if (c.merge != 1 && c.merge != 2) return fail(PV_ERR_ARG, "merge must be 1 or 2");
   if (c.layers < 0) return fail(PV_ERR_ARG, "layers must be >= 0");

@@ -11,7 +11,7 @@ import os
 from typing import Dict, List, Optional, Sequence, Tuple
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libpv_tower.so")
+LIB_PATH = os.environ.get("PV_TOWER_LIB") or os.path.join(PKG, "libpv_tower.so")
 
 PV_BF16, PV_F32 = 0, 1
 STAGES = {"patch_embed": 0, "ln_pre": 1, "qkv": 2, "attn": 3, "attn_resid": 4, "mlp_hidden": 5, "block_out": 6}
@@ -27,7 +27,8 @@ KERNEL_CLASSES = ("maps", "patch", "norm", "qkv", "attn", "oproj", "gateup", "do
 class PvConfig(C.Structure):
     _fields_ = [("patch", C.c_int32), ("hidden", C.c_int32), ("heads", C.c_int32), ("mlp", C.c_int32),
                 ("layers", C.c_int32), ("merge", C.c_int32), ("out_dim", C.c_int32), ("max_side", C.c_int32),
-                ("rope_theta", C.c_double), ("rms_eps", C.c_double), ("dtype", C.c_int32)]
+                ("rope_theta", C.c_double), ("rms_eps", C.c_double), ("dtype", C.c_int32),
+                ("out_dtype", C.c_int32)]
 
 
 class PvLayerWeights(C.Structure):
@@ -94,11 +95,14 @@ def _check(status: int):
 
 
 def make_config(patch=14, hidden=1024, heads=16, mlp=4096, layers=24, merge=2, out_dim=5120, max_side=1540,
-                rope_theta=1.0e4, rms_eps=1.0e-5, dtype="bf16") -> PvConfig:
+                rope_theta=1.0e4, rms_eps=1.0e-5, dtype="bf16", out_dtype=None) -> PvConfig:
     if dtype not in ("bf16", "f32"):
         raise ValueError("dtype must be 'bf16' or 'f32'")
+    out_dtype = dtype if out_dtype is None else out_dtype
+    if out_dtype not in ("bf16", "f32"):
+        raise ValueError("out_dtype must be 'bf16' or 'f32'")
     return PvConfig(patch, hidden, heads, mlp, layers, merge, out_dim, max_side, float(rope_theta),
-                    float(rms_eps), PV_BF16 if dtype == "bf16" else PV_F32)
+                    float(rms_eps), PV_BF16 if dtype == "bf16" else PV_F32, PV_BF16 if out_dtype == "bf16" else PV_F32)
 
 
 def _hw_array(image_hw: Sequence[Sequence[int]]):
@@ -157,9 +161,14 @@ class Tower:
             self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
         return self._ws
 
-    def _out_dtype(self):
+    def _act_dtype(self):
         import torch
         return torch.bfloat16 if self.cfg.dtype == PV_BF16 else torch.float32
+
+    def _out_dtype(self):
+        import torch
+        bf_out = self.cfg.dtype == PV_BF16 and self.cfg.out_dtype == PV_BF16
+        return torch.bfloat16 if bf_out else torch.float32
 
     def forward(self, pixels, image_hw, out=None, stream=None):
         """pixels: flat fp32 CUDA tensor of the normalised C x H x W planes."""
@@ -196,7 +205,7 @@ class Tower:
         arr, n = _hw_array(image_hw)
         info = self.plan(image_hw)
         N, D, F = info.n_patches, self.cfg.hidden, self.cfg.mlp
-        act = self._out_dtype()
+        act = self._act_dtype()
         shapes = {"patch_embed": ((N, D), torch.float32), "ln_pre": ((N, D), torch.float32),
                   "qkv": ((N, 3 * D), act), "attn": ((N, D), act), "attn_resid": ((N, D), torch.float32),
                   "mlp_hidden": ((N, F), act), "block_out": ((N, D), torch.float32)}
@@ -236,12 +245,12 @@ class Tower:
 
 
 # ---------------------------------------------------------------- helpers
-def config_for(wl, max_side: Optional[int] = None) -> PvConfig:
+def config_for(wl, max_side: Optional[int] = None, out_dtype: Optional[str] = None) -> PvConfig:
     """PvConfig of a synth.Workload."""
     ms = max_side if max_side is not None else max(max(h, w) for h, w in wl.image_hw)
     return make_config(patch=wl.patch, hidden=wl.hidden, heads=wl.heads, mlp=wl.mlp, layers=wl.layers,
                        merge=wl.merge, out_dim=wl.out_dim, max_side=ms, rope_theta=wl.rope_theta,
-                       rms_eps=wl.rms_eps, dtype=wl.dtype)
+                       rms_eps=wl.rms_eps, dtype=wl.dtype, out_dtype=out_dtype)
 
 
 def weights_to_device(w: Dict, dtype: str) -> Dict:
