@@ -159,37 +159,38 @@ def main():
     assert torch.isfinite(out.float()).all().item(), "non-finite output"
 
     # per-kernel-class times, HIP events around each launch on the same stream
-    tw.set_profiling(True)
-    for _ in range(args.profile_steps):
-        step()
-    torch.cuda.synchronize()
-    prof = tw.read_profile(reset=True)
-    tw.set_profiling(False)
     fl = flops_by_class(wl)
-    kernels = {}
-    for k, (ms, cnt) in prof.items():
-        if cnt == 0:
-            continue
-        per_launch_ms = ms / cnt
-        launches_per_fwd = cnt / args.profile_steps
-        d = {"avg_ms": round(per_launch_ms, 5), "launches_per_step": launches_per_fwd,
-             "ms_per_step": round(ms / args.profile_steps, 4)}
-        if fl.get(k):
-            d["tflops"] = round(fl[k] / (ms / args.profile_steps) / 1e9, 1)
-        if k == "norm":
-            d["gbs"] = round(norm_bytes(wl) / (ms / args.profile_steps) / 1e6, 1)
-        kernels[k] = d
-        log(f"  {k:7s} {per_launch_ms:9.4f} ms x {launches_per_fwd:5.1f}/step  {d.get('tflops', '')} TFLOP/s "
-            f"{d.get('gbs', '')}")
     total_flops = sum(fl.values())
-    dom = max((k for k in fl if fl[k] > 0 and k in kernels), key=lambda k: kernels[k]["ms_per_step"])
-    dom_ms = kernels[dom]["avg_ms"]
-    dom_flops_launch = fl[dom] / kernels[dom]["launches_per_step"]
-    achieved = dom_flops_launch / (dom_ms * 1e-3) / 1e12
     peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                "flops_per_launch": dom_flops_launch, "avg_launch_ms": dom_ms}
+    kernels, roofline = {}, None
+    if args.profile_steps > 0:
+        tw.set_profiling(True)
+        for _ in range(args.profile_steps):
+            step()
+        torch.cuda.synchronize()
+        prof = tw.read_profile(reset=True)
+        tw.set_profiling(False)
+        for k, (ms, cnt) in prof.items():
+            if cnt == 0:
+                continue
+            per_launch_ms = ms / cnt
+            launches_per_fwd = cnt / args.profile_steps
+            d = {"avg_ms": round(per_launch_ms, 5), "launches_per_step": launches_per_fwd,
+                 "ms_per_step": round(ms / args.profile_steps, 4)}
+            if fl.get(k):
+                d["tflops"] = round(fl[k] / (ms / args.profile_steps) / 1e9, 1)
+            if k == "norm":
+                d["gbs"] = round(norm_bytes(wl) / (ms / args.profile_steps) / 1e6, 1)
+            kernels[k] = d
+            log(f"  {k:7s} {per_launch_ms:9.4f} ms x {launches_per_fwd:5.1f}/step  {d.get('tflops', '')} TFLOP/s "
+                f"{d.get('gbs', '')}")
+        dom = max((k for k in fl if fl[k] > 0 and k in kernels), key=lambda k: kernels[k]["ms_per_step"])
+        dom_ms = kernels[dom]["avg_ms"]
+        dom_flops_launch = fl[dom] / kernels[dom]["launches_per_step"]
+        achieved = dom_flops_launch / (dom_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                    "flops_per_launch": dom_flops_launch, "avg_launch_ms": dom_ms}
 
     patches_s = wl.n_patches / (ms_step * 1e-3)
     tokens_s = wl.out_rows / (ms_step * 1e-3)
