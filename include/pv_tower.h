@@ -73,7 +73,14 @@ typedef struct pv_config {
   int32_t out_dtype;  /* pv_dtype of the output buffer for the bf16 tower: PV_BF16
                          (default) or PV_F32 (keeps the result unrounded); the
                          fp32 tower always writes fp32 */
+  int32_t flags;      /* PV_FLAG_* bits, 0 by default */
 } pv_config;
+
+/* pv_config.flags: the bf16 attention normally runs a softmax whose per-query
+ * offset is fixed from the first key tile and falls back to an online softmax
+ * with a running max only if the sums overflow or underflow; this bit makes it
+ * always take the online form (testing and diagnosis). */
+#define PV_FLAG_ATTN_ONLINE_MAX 1
 
 /* Per-block weights: borrowed device pointers, row-major, "out x in" like a
  * linear layer (y = x W^T).  Gains are always fp32; matrices use cfg.dtype. */
@@ -144,6 +151,8 @@ pv_status pv_tower_forward(pv_tower* t, const float* pixels, const int32_t* imag
  *   PV_STAGE_PATCH_EMBED  X = conv(pixels)               [N][D] fp32
  *   PV_STAGE_LN_PRE       h0 = RMSNorm(X) * ln_pre       [N][D] fp32
  *   PV_STAGE_QKV          layer l: [q|k|v], q,k rotated  [N][3D] cfg.dtype
+ *                         (bf16 tower: q is stored times log2(e)/sqrt(64),
+ *                         the units of its softmax)
  *   PV_STAGE_ATTN         layer l: attention output      [N][D] cfg.dtype
  *   PV_STAGE_ATTN_RESID   layer l: h after attention     [N][D] fp32
  *   PV_STAGE_MLP_HIDDEN   layer l: silu(gate)*up         [N][F] cfg.dtype

@@ -64,6 +64,8 @@ def create(cfg, layers_present=True):
     (dict(dtype=7), -1),
     (dict(dtype=1), 0),
     (dict(max_side=10), -1),
+    (dict(flags=2), -1),
+    (dict(flags=1), 0),
     (dict(rope_theta=0.0), -1),
 ])
 def test_create_validation(kw, status):

@@ -126,7 +126,9 @@ def oracle_stage(ref, wl, name, layer, w):
         k = O.rope_2d(y @ lw["wk"].T, maps["patch_rc"], wl.heads, wl.rope_theta)
         v = y @ lw["wv"].T
         if name == "qkv":
-            return np.concatenate([q, k, v], axis=1)
+            # the bf16 tower stores q in its softmax's exp2 units
+            qs = q * (np.log2(np.e) / 8.0) if wl.dtype == "bf16" else q
+            return np.concatenate([qs, k, v], axis=1)
         return O.attention(q, k, v, maps["cu_seqlens"], wl.heads)
     if name == "mlp_hidden":
         y = O.rms_norm(ref["attn_out"][layer], lw["ffn_norm"], wl.rms_eps)
@@ -232,7 +234,7 @@ def test_bf16_sharp_logits():
     say("bf16 sharp logits")
     c = Case(wl, weights=w)
     ref = c.ref()
-    qkv = oracle_stage(ref, wl, "qkv", 0, w)
+    qkv = oracle_stage(ref, wl.with_(dtype="f32"), "qkv", 0, w)  # unscaled q
     cu = ref["maps"]["cu_seqlens"]
     smax = 0.0
     for i in range(len(cu) - 1):
@@ -246,6 +248,59 @@ def test_bf16_sharp_logits():
     assert smax > 10.0  # the case is really sharp
     check("attn[0]", to_np(c.stage("attn", 0)), oracle_stage(ref, wl, "attn", 0, w), tol, stored_bf16=True)
     check("out", to_np(c.run()), ref["out"], tol, stored_bf16=True)
+
+
+def test_bf16_online_max_softmax_path():
+    """The running-max softmax (the fallback of the fixed-offset one), forced
+    on, on a ragged packed batch and on sharp logits."""
+    import torch
+    wl = _bf16_small([(252, 364), (28, 28), (420, 140)], 2)
+    say("bf16 online-max softmax, ragged batch")
+    c = Case(wl)
+    ref = c.ref()
+    tw = T.Tower(T.config_for(wl, flags=T.PV_FLAG_ATTN_ONLINE_MAX), c.dev_w)
+    out = tw.forward(c.pix, wl.image_hw)
+    torch.cuda.synchronize()
+    check("out", to_np(out), ref["out"], TOL["bf16"], stored_bf16=True)
+    att = to_np(tw.forward_stage(c.pix, wl.image_hw, "attn", 0))
+    torch.cuda.synchronize()
+    want = oracle_stage(ref, wl, "attn", 0, c.w)
+    # per image, against that image's own RMS: a 4-patch image's attention
+    # outputs are barely averaged, so they are large next to the batch RMS
+    cu = ref["maps"]["cu_seqlens"]
+    for i in range(len(cu) - 1):
+        check(f"attn[0] image {i}", att[cu[i]:cu[i + 1]], want[cu[i]:cu[i + 1]], TOL["bf16"], stored_bf16=True)
+
+
+def test_bf16_fixed_offset_overflow_falls_back():
+    """First key tile of the image all zero (zero pixels -> zero keys, offset
+    m0 = 0) and large q/k weights: later scores exceed m0 by far more than
+    2^127 can hold, so the fixed-offset pass overflows and the work item must
+    rerun with the running max -- giving exactly the forced-online result."""
+    import torch
+    wl = _bf16_small([(224, 224)], 1)
+    w = synth.make_weights(wl)
+    rng = np.random.default_rng(99)
+    lw = w["layers"][0]
+    lw["wq"] = synth.round_to_bf16(rng.standard_normal(lw["wq"].shape, dtype=np.float32) * np.float32(0.25))
+    lw["wk"] = synth.round_to_bf16(rng.standard_normal(lw["wk"].shape, dtype=np.float32) * np.float32(0.25))
+    px = synth.make_pixels(wl).reshape(3, 224, 224).copy()
+    px[:, :56, :] = 0.0  # patch rows 0..3 = the first 64 patches
+    px = px.reshape(-1)
+    say("bf16 fixed-offset overflow -> online-max fallback")
+    c = Case(wl, weights=w, pixels=px)
+    a0 = c.stage("attn", 0)
+    tw = T.Tower(T.config_for(wl, flags=T.PV_FLAG_ATTN_ONLINE_MAX), c.dev_w)
+    a1 = tw.forward_stage(c.pix, wl.image_hw, "attn", 0)
+    torch.cuda.synchronize()
+    assert torch.isfinite(a0.float()).all().item(), "fixed-offset pass left non-finite output"
+    assert torch.equal(a0, a1), "fallback result differs from the online-max pass"
+    # the scores really are far beyond the fixed offset's range
+    ref = c.ref()
+    qkv = oracle_stage(ref, wl.with_(dtype="f32"), "qkv", 0, w)  # unscaled q
+    s = qkv[64:, :64] @ qkv[64:, 1024:1088].T / 8.0 * np.log2(np.e)
+    say(f"  max score {s.max():.1f} (log2 units) vs first-tile offset 0")
+    assert s.max() > 130
 
 
 def test_bf16_packing_invariance_and_determinism_bitexact():

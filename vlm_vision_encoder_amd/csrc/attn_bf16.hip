@@ -1,36 +1,44 @@
 // Block-diagonal multi-head attention over the packed patch sequence, bf16
-// MFMA with fp32 online softmax ("Mistral 3" (KerasFormers),
-// Mistral3VisionModel: attention over a packed variable-resolution sequence,
-// every image its own block; head_dim 64, scale 1/8).  q and k arrive already
-// rotated by the 2-D RoPE, which the q,k,v projection applies in its epilogue
-// (once per element, instead of once per query tile that re-reads a key).
+// MFMA with an fp32 softmax ("Mistral 3" (KerasFormers), Mistral3VisionModel:
+// attention over a packed variable-resolution sequence, every image its own
+// block; head_dim 64, scale 1/8).  q and k arrive already rotated by the 2-D
+// RoPE, which the q,k,v projection applies in its epilogue (once per element,
+// instead of once per query tile that re-reads a key).
 //
 // Work item = (image, tile of 32*QB*WAVES queries) x head.  Each wave owns
 // 32*QB queries (QB column blocks of 32) and walks all keys of its image in
 // tiles of 64.
 //
 // * Scores are computed transposed, S^T = K Q^T, so a lane holds one query
-//   column: row max and row sum are lane-local plus one exchange with lane^32,
+//   column: row reductions are lane-local plus one exchange with lane^32,
 //   and the probabilities P^T already sit in the B-operand layout of
 //   O^T = V^T P^T.  For that match, LDS row P of the key tile holds key
 //   sigma(P) (bits 2 and 3 swapped): the 8 probabilities a lane holds per
 //   16-key step are then 8 consecutive keys.
-// * Two LDS stages (tile kt in use, tile kt+1 in flight).  A three-stage
-//   variant computes tile kt+1's scores during tile kt's softmax; it needs 32
-//   more VGPRs, and the occupancy it costs outweighs the overlap it buys
-//   (measured), so the two-stage form is the default.
 // * K and V tiles go global -> LDS with global_load_lds_dwordx4 (no VGPR
-//   staging); the swizzles are applied by choosing which 16-byte chunk each
-//   lane fetches.  K chunks are XOR-swizzled by (row >> 1) & 7 for the
-//   16-byte fragment reads (64 banks, 16 lanes per pass); V stays row-major and its V^T A-operand fragments come
-//   from two ds_read_b64_tr_b16 transpose reads (each 16-lane group receives
-//   a 4-key x 16-dim block transposed), with chunks XOR-swizzled by
-//   2*(row & 3) so the four rows of a group hit distinct banks.
-// * Online softmax in the exp2 domain with the 1/8 scale folded into one FMA.
-//   The running max is only raised when a tile's max exceeds it by more than
-//   8 (log2 units), so most tiles skip the O rescale; probabilities are then
-//   bounded by 2^8.  Row sums use v_dot2 on the bf16 probabilities that feed
-//   the MFMA.
+//   staging), two stages; the swizzles are applied by choosing which 16-byte
+//   chunk each lane fetches.  K chunks are XOR-swizzled by (row >> 1) & 7 for
+//   the 16-byte fragment reads (64 banks, 16 lanes per pass); V stays
+//   row-major and its V^T A-operand fragments come from two ds_read_b64_tr_b16
+//   transpose reads (each 16-lane group receives a 4-key x 16-dim block
+//   transposed), with chunks XOR-swizzled by 2*(row & 3).
+// * Softmax.  At head_dim 64 the kernel is bound by vector-ALU issue (one
+//   exp per score costs about three FMAs and shares their issue slots), so
+//   the per-score work is cut to exp + convert + half a dot2:
+//   - q arrives multiplied by log2(e)/8 (by the q,k,v projection's epilogue,
+//     before its one rounding to bf16), so scores come out in exp2 units;
+//   - softmax is unchanged by a per-query offset, so each query takes the
+//     max of its first key tile as offset m0 and the offset is folded into
+//     the score MFMA as a 65th dimension (keys carry 1, the query carries
+//     -m0): no per-score subtraction and no running max;
+//   - row sums use v_dot2 on the bf16 probabilities that feed the PV MFMA.
+//   The only risk of a fixed offset is range (a later score more than ~127
+//   above m0 overflows, or every score far below it underflows).  Each work
+//   item checks its sums and outputs for that and, if any is not finite,
+//   reruns with an online softmax that tracks the running max (raised only
+//   when a tile exceeds it by more than 2^8).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -38,7 +46,6 @@ namespace pv {
 
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -60,19 +67,17 @@ __device__ __forceinline__ float dot2_sum(uint32_t packed, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed), one, acc, false);
 }
 
-template <int QB, int WAVES, bool PIPE>
-__global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
+// Four waves per SIMD (two work items per CU) is worth more than the few
+// values the register cap moves to scratch outside the key loop (measured).
+template <int QB, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4))) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NT = WAVES * 64;
   constexpr int SLOTS = 512;                 // 16-byte chunks per 64 x 64 bf16 tile
   constexpr int LPT = SLOTS / NT;            // global_load_lds per thread per tile (K and V each)
-  // LDS stages.  PIPE: V(kt), K(kt+1) and tile kt+2 in flight, the scores of
-  // tile kt+1 computed during tile kt's softmax.  Otherwise: tile kt and
-  // tile kt+1 in flight.
-  constexpr int NS = PIPE ? 3 : 2;
   static_assert(LPT >= 1 && SLOTS % NT == 0, "WAVES must divide 8");
 
-  __shared__ u32x4 kl[NS][SLOTS];
-  __shared__ u32x4 vl[NS][SLOTS];
+  __shared__ u32x4 kl[2][SLOTS];
+  __shared__ u32x4 vl[2][SLOTS];
 
   const int heads = a.heads;
   const int item = blockIdx.x / heads, head = blockIdx.x - item * heads;
@@ -90,9 +95,11 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
   const int wq0 = it.q0 + 32 * QB * wave;  // first query of this wave
   const bool active = wq0 < n;
 
-  // ---- per-thread load plan: wave-instruction j covers slots
-  // [(wave*LPT + j) * 64, +64); lane l fetches slot p = that + l.
-  int k_row[LPT], k_chunk[LPT], v_row[LPT], v_chunk[LPT];
+  // ---- load plan: wave-instruction j covers slots [(wave*LPT + j) * 64, +64);
+  // lane l fetches slot p = that + l.
+  const uint16_t* kbase[LPT];
+  const uint16_t* vbase[LPT];
+  int k_row[LPT], v_row[LPT], k_chunk[LPT], v_chunk[LPT];
 #pragma unroll
   for (int j = 0; j < LPT; ++j) {
     const int p = (wave * LPT + j) * 64 + lane;
@@ -101,22 +108,31 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
     k_chunk[j] = pc ^ kswz(P);
     v_row[j] = P;
     v_chunk[j] = pc ^ (2 * (P & 3));
+    kbase[j] = qkv + size_t(base + k_row[j]) * ld + koff + k_chunk[j] * 8;
+    vbase[j] = qkv + size_t(base + v_row[j]) * ld + voff + v_chunk[j] * 8;
   }
   auto issue_loads = [&](int kt, int st) {
+    const bool partial = kt * 64 + 64 > n;  // rows past the image are clamped to its last row
+    const size_t toff = size_t(kt) * 64 * ld;
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
-      int uk = kt * 64 + k_row[j];
-      uk = uk < n ? uk : n - 1;
-      int uv = kt * 64 + v_row[j];
-      uv = uv < n ? uv : n - 1;
-      const uint16_t* gk = qkv + size_t(base + uk) * ld + koff + k_chunk[j] * 8;
-      const uint16_t* gv = qkv + size_t(base + uv) * ld + voff + v_chunk[j] * 8;
+      const uint16_t* gk = kbase[j] + toff;
+      const uint16_t* gv = vbase[j] + toff;
+      if (partial) {
+        int uk = kt * 64 + k_row[j];
+        uk = uk < n ? uk : n - 1;
+        int uv = kt * 64 + v_row[j];
+        uv = uv < n ? uv : n - 1;
+        gk = qkv + size_t(base + uk) * ld + koff + k_chunk[j] * 8;
+        gv = qkv + size_t(base + uv) * ld + voff + v_chunk[j] * 8;
+      }
       __builtin_amdgcn_global_load_lds(gk, (lds_void*)&kl[st][(wave * LPT + j) * 64], 16, 0, 0);
       __builtin_amdgcn_global_load_lds(gv, (lds_void*)&vl[st][(wave * LPT + j) * 64], 16, 0, 0);
     }
   };
 
-  // ---- Q fragments (B operand of S^T = K Q^T), kept for the whole loop
+  // ---- Q fragments (B operand of S^T = K Q^T); the q,k,v projection stores
+  // q already multiplied by log2(e)/8, so scores come out in exp2 units
   u32x4 qf[QB][4];
 #pragma unroll
   for (int tb = 0; tb < QB; ++tb) {
@@ -126,21 +142,12 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[tb][ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
   }
-
-  floatx16 o[2][QB];
+  // offset operands of the 65th score dimension: dimension 64 of every key
+  // is 1 and dimension 64 of query t is -m0(t) (lane half 0, element 0)
+  const u32x4 a_off = {lhalf == 0 ? 0x3F80u : 0u, 0u, 0u, 0u};
+  u32x4 q_off[QB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < QB; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[i][j][v] = 0.f;
-  float m_sc[QB], l_run[QB];
-#pragma unroll
-  for (int tb = 0; tb < QB; ++tb) {
-    m_sc[tb] = -INFINITY;  // running max, in scaled (log2) units
-    l_run[tb] = 0.f;
-  }
-  const float c = kLog2e * 0.125f;  // log2(e) / sqrt(64)
+  for (int tb = 0; tb < QB; ++tb) q_off[tb] = u32x4{0u, 0u, 0u, 0u};
 
   // transposed-read addresses for the V^T fragments: 16-lane group g gets
   // dims D0 + (lane % 16), keys U..U+3 (and U+4..U+7 from the second read)
@@ -148,8 +155,26 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
   const int tr_row = 8 * (g >> 1) + (r16 >> 2);          // + ub*32 + sp*16 (+4)
   const int tr_col = 16 * (g & 1) + 4 * (r16 & 3);       // + db*32 (elements)
 
-  // S^T block of one key tile (stage st)
-  auto scores = [&](int st, floatx16 (&s)[2][QB]) {
+  floatx16 o[2][QB];
+  float m_sc[QB], l_run[QB];
+  const int nkt = (n + 63) / 64;
+
+  // One key tile.  MODE 0: first tile of the fixed-offset pass (finds m0);
+  // MODE 1: later tiles of that pass (offset folded into the MFMA); MODE 2:
+  // online softmax with a running max (fallback pass).
+  auto tile = [&](auto mode_c, int kt) {
+    constexpr int MODE = decltype(mode_c)::value;
+    const int st = kt & 1;
+    // ---- S^T = K Q^T (minus the query offset in MODE 1)
+    floatx16 s[2][QB];
+#pragma unroll
+    for (int ub = 0; ub < 2; ++ub)
+#pragma unroll
+      for (int tb = 0; tb < QB; ++tb) {
+        const floatx16 z = {};
+        if constexpr (MODE == 1) s[ub][tb] = mfma32x32x16(a_off, q_off[tb], z);
+        else s[ub][tb] = z;
+      }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -157,128 +182,157 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
         const int row = ub * 32 + lrow;
         const u32x4 kf = kl[st][row * 8 + ((2 * ks + lhalf) ^ kswz(row))];
 #pragma unroll
-        for (int tb = 0; tb < QB; ++tb) {
-          if (ks == 0) {
-            const floatx16 z = {};
-            s[ub][tb] = mfma32x32x16(kf, qf[tb][ks], z);
-          } else {
-            s[ub][tb] = mfma32x32x16(kf, qf[tb][ks], s[ub][tb]);
-          }
-        }
+        for (int tb = 0; tb < QB; ++tb) s[ub][tb] = mfma32x32x16(kf, qf[tb][ks], s[ub][tb]);
       }
     }
-  };
-
-  const int nkt = (n + 63) / 64;
-  issue_loads(0, 0);
-  if (PIPE && nkt > 1) issue_loads(1, 1);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  floatx16 s_cur[2][QB];
-  if (PIPE && active) scores(0, s_cur);
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int st_v = kt % NS, st_k = (kt + 1) % NS;
-    if (PIPE) {
-      if (kt + 2 < nkt) issue_loads(kt + 2, (kt + 2) % NS);
-    } else {
-      if (kt + 1 < nkt) issue_loads(kt + 1, st_k);
-    }
-    if (active) {
-      // ---- PIPE: next tile's scores, independent of this tile's softmax, so
-      // their MFMAs can overlap the exp work below
-      floatx16 s_nxt[2][QB];
-      if (PIPE) {
-        if (kt + 1 < nkt) scores(st_k, s_nxt);
-      } else {
-        scores(st_v, s_cur);
-      }
-      // ---- mask keys past the image (last tile only)
-      if (kt * 64 + 64 > n) {
-#pragma unroll
-        for (int ub = 0; ub < 2; ++ub)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int u = kt * 64 + ub * 32 + 16 * (v >> 3) + 8 * lhalf + (v & 7);
-            if (u >= n) {
-#pragma unroll
-              for (int tb = 0; tb < QB; ++tb) s_cur[ub][tb][v] = -INFINITY;
-            }
-          }
-      }
-      // ---- online softmax
-      u32x4 pf[2][QB][2];
-#pragma unroll
-      for (int tb = 0; tb < QB; ++tb) {
-        float mx = s_cur[0][tb][0];
-#pragma unroll
-        for (int ub = 0; ub < 2; ++ub)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s_cur[ub][tb][v]);
-        mx = pair_max32(mx) * c;
-        if (__any(mx > m_sc[tb] + kRescaleSlack)) {
-          const float m_new = fmaxf(m_sc[tb], mx);
-          float alpha = __builtin_amdgcn_exp2f(m_sc[tb] - m_new);
-          // keeps the rescale a rarely-taken branch (otherwise it becomes an
-          // unconditional multiply by a selected factor)
-          asm volatile("" : "+v"(alpha));
-          m_sc[tb] = m_new;
-          l_run[tb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) o[db][tb][v] *= alpha;
-        }
-        const float mneg = -m_sc[tb];
-#pragma unroll
-        for (int ub = 0; ub < 2; ++ub) {
-#pragma unroll
-          for (int sp = 0; sp < 2; ++sp) {
-            float p[8];
-#pragma unroll
-            for (int v = 0; v < 8; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[ub][tb][8 * sp + v], c, mneg));
-            const u32x4 pk = pack8(p);
-            pf[ub][tb][sp] = pk;
-            l_run[tb] = dot2_sum(pk[0], l_run[tb]);
-            l_run[tb] = dot2_sum(pk[1], l_run[tb]);
-            l_run[tb] = dot2_sum(pk[2], l_run[tb]);
-            l_run[tb] = dot2_sum(pk[3], l_run[tb]);
-          }
-        }
-      }
-      // ---- O^T += V^T P^T
-      const uint16_t* vb = reinterpret_cast<const uint16_t*>(vl[st_v]);
+    // ---- mask keys past the image (last tile only)
+    if (kt * 64 + 64 > n) {
 #pragma unroll
       for (int ub = 0; ub < 2; ++ub)
 #pragma unroll
-        for (int sp = 0; sp < 2; ++sp)
+        for (int v = 0; v < 16; ++v) {
+          const int u = kt * 64 + ub * 32 + 16 * (v >> 3) + 8 * lhalf + (v & 7);
+          if (u >= n) {
 #pragma unroll
-          for (int db = 0; db < 2; ++db) {
-            u32x4 vf;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-              const int row = ub * 32 + sp * 16 + tr_row + 4 * half;
-              const int col = db * 32 + tr_col;  // element; chunk = col / 8
-              const int pchunk = (col >> 3) ^ (2 * (row & 3));
-              const uint16_t* addr = vb + row * 64 + pchunk * 8 + (col & 7);
-              const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)addr);
-              const u32x2 w = __builtin_bit_cast(u32x2, r);
-              vf[2 * half] = w[0];
-              vf[2 * half + 1] = w[1];
-            }
-#pragma unroll
-            for (int tb = 0; tb < QB; ++tb) o[db][tb] = mfma32x32x16(vf, pf[ub][tb][sp], o[db][tb]);
+            for (int tb = 0; tb < QB; ++tb) s[ub][tb][v] = -INFINITY;
           }
-      if (PIPE) {
+        }
+    }
+    // ---- probabilities
+    u32x4 pf[2][QB][2];
+#pragma unroll
+    for (int tb = 0; tb < QB; ++tb) {
+      float sub = 0.f;  // added to every score before exp2 (MODE 0 and 2)
+      if constexpr (MODE != 1) {
+        float mx = s[0][tb][0];
 #pragma unroll
         for (int ub = 0; ub < 2; ++ub)
 #pragma unroll
-          for (int tb = 0; tb < QB; ++tb) s_cur[ub][tb] = s_nxt[ub][tb];
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[ub][tb][v]);
+        mx = pair_max32(mx);
+        if constexpr (MODE == 0) {
+          // the offset is -m0 rounded to bf16, so that the later tiles'
+          // MFMA-folded offset is the very same number
+          const uint32_t mb = pack_bf16x2(-mx, 0.f) & 0xffffu;
+          q_off[tb] = u32x4{lhalf == 0 ? mb : 0u, 0u, 0u, 0u};
+          sub = lo_bf16(mb);
+        } else {
+          if (__any(mx > m_sc[tb] + kRescaleSlack)) {
+            const float m_new = fmaxf(m_sc[tb], mx);
+            float alpha = __builtin_amdgcn_exp2f(m_sc[tb] - m_new);
+            // keeps the rescale a rarely-taken branch
+            asm volatile("" : "+v"(alpha));
+            m_sc[tb] = m_new;
+            l_run[tb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) o[db][tb][v] *= alpha;
+          }
+          sub = -m_sc[tb];
+        }
+      }
+#pragma unroll
+      for (int ub = 0; ub < 2; ++ub) {
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+          float p[8];
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            if constexpr (MODE == 1) p[v] = __builtin_amdgcn_exp2f(s[ub][tb][8 * sp + v]);
+            else p[v] = __builtin_amdgcn_exp2f(s[ub][tb][8 * sp + v] + sub);
+          }
+          const u32x4 pk = pack8(p);
+          pf[ub][tb][sp] = pk;
+          l_run[tb] = dot2_sum(pk[0], l_run[tb]);
+          l_run[tb] = dot2_sum(pk[1], l_run[tb]);
+          l_run[tb] = dot2_sum(pk[2], l_run[tb]);
+          l_run[tb] = dot2_sum(pk[3], l_run[tb]);
+        }
       }
     }
+    // ---- O^T += V^T P^T
+    const uint16_t* vb = reinterpret_cast<const uint16_t*>(vl[st]);
+#pragma unroll
+    for (int ub = 0; ub < 2; ++ub)
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          u32x4 vf;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int row = ub * 32 + sp * 16 + tr_row + 4 * half;
+            const int col = db * 32 + tr_col;  // element; chunk = col / 8
+            const int pchunk = (col >> 3) ^ (2 * (row & 3));
+            const uint16_t* addr = vb + row * 64 + pchunk * 8 + (col & 7);
+            const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)addr);
+            const u32x2 w = __builtin_bit_cast(u32x2, r);
+            vf[2 * half] = w[0];
+            vf[2 * half + 1] = w[1];
+          }
+#pragma unroll
+          for (int tb = 0; tb < QB; ++tb) o[db][tb] = mfma32x32x16(vf, pf[ub][tb][sp], o[db][tb]);
+        }
+  };
+  auto reset = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jq = 0; jq < QB; ++jq)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[i][jq][v] = 0.f;
+#pragma unroll
+    for (int tb = 0; tb < QB; ++tb) {
+      m_sc[tb] = -INFINITY;
+      l_run[tb] = 0.f;
+    }
+    issue_loads(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  auto next = [&](int kt) {  // loads of tile kt+1 behind tile kt's compute
+    if (kt + 1 < nkt) issue_loads(kt + 1, (kt + 1) & 1);
+  };
+  auto done = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  bool online = a.online_max != 0;
+  if (!online) {
+    // ---- fixed-offset pass
+    reset();
+    next(0);
+    if (active) tile(std::integral_constant<int, 0>(), 0);
+    done();
+    for (int kt = 1; kt < nkt; ++kt) {
+      next(kt);
+      if (active) tile(std::integral_constant<int, 1>(), kt);
+      done();
+    }
+    // ---- range check: rerun with a running max if any sum or output overflowed
+    int bad = 0;
+    if (active) {
+#pragma unroll
+      for (int tb = 0; tb < QB; ++tb) {
+        const float l = pair_sum32(l_run[tb]);
+        bad |= !(l > 0.f && l < INFINITY);
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) bad |= !__builtin_isfinite(o[db][tb][v]);
+      }
+    }
+    online = __syncthreads_or(bad) != 0;
+  }
+  if (online) {
+    reset();
+    for (int kt = 0; kt < nkt; ++kt) {
+      next(kt);
+      if (active) tile(std::integral_constant<int, 2>(), kt);
+      done();
+    }
   }
 
   if (!active) return;
@@ -308,7 +362,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.n_items <= 0) return hipSuccess;
   static_assert(kAttnQTileBf16 == 32 * PV_ATTN_QB * PV_ATTN_WAVES, "q tile must match the kernel shape");
-  hipLaunchKernelGGL((attn_bf16_kernel<PV_ATTN_QB, PV_ATTN_WAVES, PV_ATTN_PIPE != 0>), dim3(a.n_items * a.heads),
+  hipLaunchKernelGGL((attn_bf16_kernel<PV_ATTN_QB, PV_ATTN_WAVES>), dim3(a.n_items * a.heads),
                      dim3(PV_ATTN_WAVES * 64), 0, s, a);
   return hipGetLastError();
 }

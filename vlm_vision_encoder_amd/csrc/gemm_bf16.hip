@@ -175,6 +175,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[TM][
             const float2 cs = reinterpret_cast<const float2*>(g.maps.rope)[(axis * g.maps.rope_maxpos + pos) * 16 + m];
             // even lane: x0 cos - x1 sin ; odd lane: x0 sin + x1 cos
             x = (d & 1) ? (xp * cs.y + x * cs.x) : (x * cs.x - xp * cs.y);
+            // q leaves in exp2 units of the attention softmax: times
+            // log2(e)/sqrt(64), before its single rounding to bf16
+            if (col < g.hidden) x *= 0.18033688011112042f;
           }
           if (ok) reinterpret_cast<bf16*>(g.C)[size_t(row) * g.ldc + col] = (bf16)x;
         }

@@ -42,6 +42,7 @@ struct AttnArgs {
   int32_t n_items;
   int32_t heads;
   int32_t hidden;
+  int32_t online_max;  // 1: always use the running-max softmax (bf16 path)
 };
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t attention_f32(const AttnArgs& a, hipStream_t s);
@@ -52,9 +53,6 @@ hipError_t attention_f32(const AttnArgs& a, hipStream_t s);
 #endif
 #ifndef PV_ATTN_WAVES
 #define PV_ATTN_WAVES 8
-#endif
-#ifndef PV_ATTN_PIPE
-#define PV_ATTN_PIPE 0
 #endif
 constexpr int kAttnQTileBf16 = 32 * PV_ATTN_QB * PV_ATTN_WAVES;
 constexpr int kAttnQTileF32 = 64;

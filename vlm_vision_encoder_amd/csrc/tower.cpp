@@ -213,6 +213,7 @@ pv_status run_tower(pv_tower* t, const float* pixels, const pv::Plan& plan, void
   at.n_items = int(plan.items.size());
   at.heads = c.heads;
   at.hidden = D;
+  at.online_max = (c.flags & PV_FLAG_ATTN_ONLINE_MAX) ? 1 : 0;
 
   for (int l = 0; l < c.layers; ++l) {
     const pv_layer_weights& lw = t->layers[l];
@@ -312,6 +313,7 @@ pv_status pv_tower_create(const pv_config* cfg, const pv_weights* w, pv_tower** 
   const pv_config& c = *cfg;
   if (c.dtype != PV_BF16 && c.dtype != PV_F32) return fail(PV_ERR_ARG, "dtype must be PV_BF16 or PV_F32");
   if (c.out_dtype != PV_BF16 && c.out_dtype != PV_F32) return fail(PV_ERR_ARG, "out_dtype must be PV_BF16 or PV_F32");
+  if (c.flags & ~PV_FLAG_ATTN_ONLINE_MAX) return fail(PV_ERR_ARG, "unknown bits in flags");
   if (c.patch < 1 || c.patch > 64) return fail(PV_ERR_ARG, "patch must be in [1, 64]");
   if (c.merge != 1 && c.merge != 2) return fail(PV_ERR_ARG, "merge must be 1 or 2");
   if (c.layers < 0) return fail(PV_ERR_ARG, "layers must be >= 0");

@@ -14,6 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PV_TOWER_LIB") or os.path.join(PKG, "libpv_tower.so")
 
 PV_BF16, PV_F32 = 0, 1
+PV_FLAG_ATTN_ONLINE_MAX = 1
 STAGES = {"patch_embed": 0, "ln_pre": 1, "qkv": 2, "attn": 3, "attn_resid": 4, "mlp_hidden": 5, "block_out": 6}
 STATUS = {0: "PV_OK", -1: "PV_ERR_ARG", -2: "PV_ERR_SHAPE", -3: "PV_ERR_CAPACITY", -4: "PV_ERR_HIP",
           -5: "PV_ERR_UNSUPPORTED"}
@@ -28,7 +29,7 @@ class PvConfig(C.Structure):
     _fields_ = [("patch", C.c_int32), ("hidden", C.c_int32), ("heads", C.c_int32), ("mlp", C.c_int32),
                 ("layers", C.c_int32), ("merge", C.c_int32), ("out_dim", C.c_int32), ("max_side", C.c_int32),
                 ("rope_theta", C.c_double), ("rms_eps", C.c_double), ("dtype", C.c_int32),
-                ("out_dtype", C.c_int32)]
+                ("out_dtype", C.c_int32), ("flags", C.c_int32)]
 
 
 class PvLayerWeights(C.Structure):
@@ -95,14 +96,15 @@ def _check(status: int):
 
 
 def make_config(patch=14, hidden=1024, heads=16, mlp=4096, layers=24, merge=2, out_dim=5120, max_side=1540,
-                rope_theta=1.0e4, rms_eps=1.0e-5, dtype="bf16", out_dtype=None) -> PvConfig:
+                rope_theta=1.0e4, rms_eps=1.0e-5, dtype="bf16", out_dtype=None, flags=0) -> PvConfig:
     if dtype not in ("bf16", "f32"):
         raise ValueError("dtype must be 'bf16' or 'f32'")
     out_dtype = dtype if out_dtype is None else out_dtype
     if out_dtype not in ("bf16", "f32"):
         raise ValueError("out_dtype must be 'bf16' or 'f32'")
     return PvConfig(patch, hidden, heads, mlp, layers, merge, out_dim, max_side, float(rope_theta),
-                    float(rms_eps), PV_BF16 if dtype == "bf16" else PV_F32, PV_BF16 if out_dtype == "bf16" else PV_F32)
+                    float(rms_eps), PV_BF16 if dtype == "bf16" else PV_F32, PV_BF16 if out_dtype == "bf16" else PV_F32,
+                    int(flags))
 
 
 def _hw_array(image_hw: Sequence[Sequence[int]]):
@@ -245,12 +247,12 @@ class Tower:
 
 
 # ---------------------------------------------------------------- helpers
-def config_for(wl, max_side: Optional[int] = None, out_dtype: Optional[str] = None) -> PvConfig:
+def config_for(wl, max_side: Optional[int] = None, out_dtype: Optional[str] = None, flags: int = 0) -> PvConfig:
     """PvConfig of a synth.Workload."""
     ms = max_side if max_side is not None else max(max(h, w) for h, w in wl.image_hw)
     return make_config(patch=wl.patch, hidden=wl.hidden, heads=wl.heads, mlp=wl.mlp, layers=wl.layers,
                        merge=wl.merge, out_dim=wl.out_dim, max_side=ms, rope_theta=wl.rope_theta,
-                       rms_eps=wl.rms_eps, dtype=wl.dtype, out_dtype=out_dtype)
+                       rms_eps=wl.rms_eps, dtype=wl.dtype, out_dtype=out_dtype, flags=flags)
 
 
 def weights_to_device(w: Dict, dtype: str) -> Dict:
