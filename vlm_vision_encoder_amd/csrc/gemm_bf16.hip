@@ -327,6 +327,104 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 }
 
 
+// Epilogue through LDS: each 32x32 accumulator block is written to a per-wave
+// LDS scratch in row-major order and read back so that every lane owns 8
+// consecutive bf16 outputs (16 bytes) or 4 consecutive fp32 values, which
+// turns 16 scattered 2/4-byte global accesses per lane and block into 2 (bf16)
+// or 4 + 4 (fp32 read-modify-write) 16-byte ones.  The RoPE and silu*up are
+// applied in the MFMA layout first (the rotation partner sits in the
+// neighbouring lane, gate and up of one unit in the same lane).
+// scratch: >= 32 * 36 floats of LDS private to the wave.
+template <int EM, int TM, int TN>
+__device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[TM][TN], int m_base, int n_base,
+                                             int lane, float* scratch) {
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  if constexpr (EM == E_ADD_F32 || EM == E_STORE_F32) {
+    constexpr int LDF = 36;  // row stride (floats): rows r, r+4 land 64 banks apart + 16
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) scratch[(8 * (v >> 2) + 4 * lhalf + (v & 3)) * LDF + lrow] = acc[i][j][v];
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int r = (lane >> 3) + 8 * it, c4 = 4 * (lane & 7);
+          const floatx4 val = *reinterpret_cast<const floatx4*>(scratch + r * LDF + c4);
+          const int row = m_base + 32 * i + r, col = n_base + 32 * j + c4;
+          if (row < g.M) {
+            floatx4* dst = reinterpret_cast<floatx4*>(reinterpret_cast<float*>(g.C) + size_t(row) * g.ldc + col);
+            if constexpr (EM == E_ADD_F32) *dst = *dst + val;
+            else *dst = val;
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next block's writes
+      }
+  } else {
+    // bf16 outputs: one 32 x 32 bf16 block staged per round
+    constexpr int LDH = 40;  // row stride (bf16 elements), 80 bytes
+    uint16_t* sh = reinterpret_cast<uint16_t*>(scratch);
+    constexpr int NB = (EM == E_SILU_MUL) ? TN / 2 : TN;  // output blocks per row of blocks
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      int rcv[16];  // packed (row, col) of the patch of each of this lane's rows
+      if constexpr (EM == E_QKV_ROPE) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m_base + 32 * i + 8 * (v >> 2) + 4 * lhalf + (v & 3);
+          rcv[v] = row < g.M ? g.maps.rowinfo[2 * row + 1] : 0;
+        }
+      }
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) {
+        int ocol0;  // first output column of the block
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rib = 8 * (v >> 2) + 4 * lhalf + (v & 3);  // row in block
+          float x;
+          if constexpr (EM == E_SILU_MUL) {
+            const float gt = acc[i][2 * jb][v], up = acc[i][2 * jb + 1][v];
+            x = gt / (1.f + __expf(-gt)) * up;
+            ocol0 = (n_base + 64 * jb) / 2;
+          } else if constexpr (EM == E_QKV_ROPE) {
+            x = acc[i][jb][v];
+            const float xp = swap_adjacent(x);
+            const int col = n_base + 32 * jb + lrow;
+            ocol0 = n_base + 32 * jb;
+            if (col < 2 * g.hidden) {
+              const int pr = rcv[v] >> 16, pc = rcv[v] & 0xffff;
+              const int d = col & 63, pair = d >> 1;
+              const int axis = pair >> 4, m = pair & 15;
+              const int pos = axis ? pc : pr;
+              const float2 cs = reinterpret_cast<const float2*>(g.maps.rope)[(axis * g.maps.rope_maxpos + pos) * 16 + m];
+              // even lane: x0 cos - x1 sin ; odd lane: x0 sin + x1 cos
+              x = (d & 1) ? (xp * cs.y + x * cs.x) : (x * cs.x - xp * cs.y);
+              // q leaves in exp2 units of the attention softmax: times
+              // log2(e)/sqrt(64), before its single rounding to bf16
+              if (col < g.hidden) x *= 0.18033688011112042f;
+            }
+          } else {
+            x = acc[i][jb][v];
+            ocol0 = n_base + 32 * jb;
+          }
+          sh[rib * LDH + lrow] = __builtin_bit_cast(uint16_t, (bf16)x);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          const int r = (lane >> 2) + 16 * it, c8 = 8 * (lane & 3);
+          const u32x4 val = *reinterpret_cast<const u32x4*>(sh + r * LDH + c8);
+          const int row = m_base + 32 * i + r;
+          if (row < g.M)
+            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.C) + size_t(row) * g.ldc + ocol0 + c8) = val;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+      }
+    }
+  }
+}
+
 // s_waitcnt immediate that waits until at most n vector-memory operations
 // are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
 // lgkmcnt left at their maxima).
@@ -355,6 +453,8 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
   static_assert((NS - 2) * LDT <= 63, "vmcnt range");
 
   __shared__ u32x4 lds[NS][(BM + BN) * 8];
+  constexpr int kScratchFloats = (BM + BN) * 8 * 4 / NW;  // per-wave slice of one stage
+  static_assert(kScratchFloats >= 32 * 36, "epilogue scratch does not fit a stage");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WNW, wn = wave % WNW;
@@ -478,7 +578,12 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
     if (++kt == KT) {
       int tm, tn;
       tile_mn(tile_of(ti), tm, tn);
-      epilogue<EM, TM, TN>(g, acc, tm * BM + wm * TMW, tn * BN + wn * TNW, lrow, lhalf);
+      // the stage just consumed is free until the next step's loads (issued
+      // after the next barrier): once every wave is done with it, each wave
+      // uses its own slice of it to stage the output
+      __syncthreads();
+      float* scratch = reinterpret_cast<float*>(lds[step % NS]) + wave * kScratchFloats;
+      epilogue_lds<EM, TM, TN>(g, acc, tm * BM + wm * TMW, tn * BN + wn * TNW, lane, scratch);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
