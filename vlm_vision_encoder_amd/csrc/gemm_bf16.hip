@@ -19,6 +19,8 @@
 // in (row parity, chunk) and hit distinct banks.  Blocks are renumbered so each XCD (blocks b with the same
 // b % 8) works on a contiguous range of output tiles, which keeps the A panel
 // and the weights it shares in that XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -34,8 +36,28 @@ constexpr int kNumCUs = 256;  // MI355X: 8 XCDs x 32 CUs
 #ifndef PV_GEMM_GM
 #define PV_GEMM_GM 4
 #endif
+#ifndef PV_GEMM_SCHED
+#define PV_GEMM_SCHED 1
+#endif
+
+template <int N, typename F, int I = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>());
+    static_for<N, F, I + 1>(static_cast<F&&>(f));
+  }
+}
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// The same for rows of CH chunks (CH = 8: 128-byte rows, as swz; CH = 4:
+// 64-byte rows, where four consecutive rows already span the 64 banks, so the
+// 16 rows of a pass must differ in (row % 4, chunk): chunk ^ ((row >> 2) & 3)).
+template <int CH>
+__device__ __forceinline__ int swzc(int row) {
+  static_assert(CH == 8 || CH == 4, "row width");
+  if constexpr (CH == 8) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
 
 __device__ __forceinline__ int xcd_remap(int b, int nblocks) {
   const int xcd = b & 7, idx = b >> 3;
@@ -329,38 +351,110 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 
 // Epilogue through LDS: each 32x32 accumulator block is written to a per-wave
 // LDS scratch in row-major order and read back so that every lane owns 8
-// consecutive bf16 outputs (16 bytes) or 4 consecutive fp32 values, which
-// turns 16 scattered 2/4-byte global accesses per lane and block into 2 (bf16)
-// or 4 + 4 (fp32 read-modify-write) 16-byte ones.  The RoPE and silu*up are
-// applied in the MFMA layout first (the rotation partner sits in the
-// neighbouring lane, gate and up of one unit in the same lane).
-// scratch: >= 32 * 36 floats of LDS private to the wave.
-template <int EM, int TM, int TN>
+// consecutive outputs of one row (bf16: one 16-byte store) or 4 consecutive
+// fp32 values, which turns 16 scattered 2/4-byte global accesses per lane and
+// block into 2 (bf16) or 4 + 4 (fp32 read-modify-write) 16-byte ones.
+//
+// fp32 staging uses 32-float rows with row r stored at r ^ ((r >> 2) & 1):
+// the MFMA layout writes rows R and R + 4 in one instruction, which then fall
+// in opposite halves of the 64 banks; read-back lanes that share a 16-lane
+// pass cover (row parity, 16-byte chunk) once each.
+//
+// RoPE (q and k columns) is applied after the read-back, where a lane holds 4
+// consecutive rotation pairs of one patch: their cos/sin are 32 contiguous
+// bytes of the table.  silu(gate) * up is applied in the MFMA layout, where
+// gate and up of one unit sit in the same lane.
+// scratch: LDS private to the wave, >= SR * 32 floats (fp32 outputs go
+// through it SR = 32 or 16 rows at a time), >= 32 * 32 floats for the q,k,v
+// epilogue and >= 32 * 20 floats for bf16 outputs.
+__device__ __forceinline__ int stage_row(int r) { return r ^ ((r >> 2) & 1); }
+
+template <int EM, int TM, int TN, int SR = 32>
 __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[TM][TN], int m_base, int n_base,
                                              int lane, float* scratch) {
   const int lrow = lane & 31, lhalf = lane >> 5;
   if constexpr (EM == E_ADD_F32 || EM == E_STORE_F32) {
-    constexpr int LDF = 36;  // row stride (floats): rows r, r+4 land 64 banks apart + 16
+    static_assert(SR == 32 || SR == 16, "staging rows");
+    constexpr int VP = SR / 2;  // accumulator values per lane and pass
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) scratch[(8 * (v >> 2) + 4 * lhalf + (v & 3)) * LDF + lrow] = acc[i][j][v];
+        for (int h = 0; h < 32 / SR; ++h) {
+#pragma unroll
+          for (int v = 0; v < VP; ++v)
+            scratch[stage_row(8 * (v >> 2) + 4 * lhalf + (v & 3)) * 32 + lrow] = acc[i][j][h * VP + v];
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+#pragma unroll
+          for (int it = 0; it < SR / 8; ++it) {
+            const int r = (lane >> 3) + 8 * it, c4 = 4 * (lane & 7);
+            const floatx4 val = *reinterpret_cast<const floatx4*>(scratch + stage_row(r) * 32 + c4);
+            const int row = m_base + 32 * i + h * SR + r, col = n_base + 32 * j + c4;
+            if (row < g.M) {
+              floatx4* dst = reinterpret_cast<floatx4*>(reinterpret_cast<float*>(g.C) + size_t(row) * g.ldc + col);
+              if constexpr (EM == E_ADD_F32) *dst = *dst + val;
+              else *dst = val;
+            }
+          }
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next pass's writes
+        }
+  } else if constexpr (EM == E_QKV_ROPE) {
+    const float4* rope = reinterpret_cast<const float4*>(g.maps.rope);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      int rc[2];  // packed (row, col) of the patch of the two rows this lane stores
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int row = m_base + 32 * i + (lane >> 2) + 16 * it;
+        rc[it] = row < g.M ? g.maps.rowinfo[2 * row + 1] : 0;
+      }
+#pragma unroll
+      for (int jb = 0; jb < TN; ++jb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          scratch[stage_row(8 * (v >> 2) + 4 * lhalf + (v & 3)) * 32 + lrow] = acc[i][jb][v];
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int r = (lane >> 3) + 8 * it, c4 = 4 * (lane & 7);
-          const floatx4 val = *reinterpret_cast<const floatx4*>(scratch + r * LDF + c4);
-          const int row = m_base + 32 * i + r, col = n_base + 32 * j + c4;
-          if (row < g.M) {
-            floatx4* dst = reinterpret_cast<floatx4*>(reinterpret_cast<float*>(g.C) + size_t(row) * g.ldc + col);
-            if constexpr (EM == E_ADD_F32) *dst = *dst + val;
-            else *dst = val;
+        for (int it = 0; it < 2; ++it) {
+          const int r = (lane >> 2) + 16 * it, c8 = 8 * (lane & 3);
+          // the two 16-byte halves are read in the order that keeps a pass
+          // conflict-free, then put back in column order
+          const int f = (r >> 1) & 1;
+          const float* src = scratch + stage_row(r) * 32 + c8;
+          const floatx4 first = *reinterpret_cast<const floatx4*>(src + 4 * f);
+          const floatx4 second = *reinterpret_cast<const floatx4*>(src + 4 * (1 - f));
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[e] = f ? second[e] : first[e];
+            x[4 + e] = f ? first[e] : second[e];
           }
+          const int row = m_base + 32 * i + r, col0 = n_base + 32 * jb + c8;
+          if (col0 < 2 * g.hidden) {
+            // dims d0 .. d0+7 of a head = rotation pairs m0 .. m0+3 of one axis
+            const int pair0 = (col0 & 63) >> 1;
+            const int axis = pair0 >> 4, m0 = pair0 & 15;
+            const int pos = axis ? (rc[it] & 0xffff) : (rc[it] >> 16);
+            const float4* cs = rope + ((axis * g.maps.rope_maxpos + pos) * 16 + m0) / 2;
+            const float4 c01 = cs[0], c23 = cs[1];  // {cos, sin} of pairs m0, m0+1 | m0+2, m0+3
+            const float cv[4] = {c01.x, c01.z, c23.x, c23.z}, sv[4] = {c01.y, c01.w, c23.y, c23.w};
+            // q leaves in exp2 units of the attention softmax: times
+            // log2(e)/sqrt(64), before its single rounding to bf16
+            const float sc = col0 < g.hidden ? 0.18033688011112042f : 1.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float x0 = x[2 * k], x1 = x[2 * k + 1];
+              x[2 * k] = (x0 * cv[k] - x1 * sv[k]) * sc;
+              x[2 * k + 1] = (x0 * sv[k] + x1 * cv[k]) * sc;
+            }
+          }
+          if (row < g.M)
+            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.C) + size_t(row) * g.ldc + col0) = pack8(x);
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next block's writes
       }
+    }
   } else {
     // bf16 outputs: one 32 x 32 bf16 block staged per round
     constexpr int LDH = 40;  // row stride (bf16 elements), 80 bytes
@@ -368,14 +462,6 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[
     constexpr int NB = (EM == E_SILU_MUL) ? TN / 2 : TN;  // output blocks per row of blocks
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      int rcv[16];  // packed (row, col) of the patch of each of this lane's rows
-      if constexpr (EM == E_QKV_ROPE) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = m_base + 32 * i + 8 * (v >> 2) + 4 * lhalf + (v & 3);
-          rcv[v] = row < g.M ? g.maps.rowinfo[2 * row + 1] : 0;
-        }
-      }
 #pragma unroll
       for (int jb = 0; jb < NB; ++jb) {
         int ocol0;  // first output column of the block
@@ -387,23 +473,6 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[
             const float gt = acc[i][2 * jb][v], up = acc[i][2 * jb + 1][v];
             x = gt / (1.f + __expf(-gt)) * up;
             ocol0 = (n_base + 64 * jb) / 2;
-          } else if constexpr (EM == E_QKV_ROPE) {
-            x = acc[i][jb][v];
-            const float xp = swap_adjacent(x);
-            const int col = n_base + 32 * jb + lrow;
-            ocol0 = n_base + 32 * jb;
-            if (col < 2 * g.hidden) {
-              const int pr = rcv[v] >> 16, pc = rcv[v] & 0xffff;
-              const int d = col & 63, pair = d >> 1;
-              const int axis = pair >> 4, m = pair & 15;
-              const int pos = axis ? pc : pr;
-              const float2 cs = reinterpret_cast<const float2*>(g.maps.rope)[(axis * g.maps.rope_maxpos + pos) * 16 + m];
-              // even lane: x0 cos - x1 sin ; odd lane: x0 sin + x1 cos
-              x = (d & 1) ? (xp * cs.y + x * cs.x) : (x * cs.x - xp * cs.y);
-              // q leaves in exp2 units of the attention softmax: times
-              // log2(e)/sqrt(64), before its single rounding to bf16
-              if (col < g.hidden) x *= 0.18033688011112042f;
-            }
           } else {
             x = acc[i][jb][v];
             ocol0 = n_base + 32 * jb;
@@ -441,20 +510,23 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 // workgroups of one XCD (blocks b with equal b % 8) share a contiguous range
 // of tiles, grouped GM tile rows at a time, keeping the A and B panels they
 // share in that XCD's L2.
-template <int BM, int BN, int WMW, int WNW, int NS, int BMD, int EM>
+template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int BMD, int EM>
 __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) {
   constexpr int NW = WMW * WNW, NT = NW * 64;
+  constexpr int CH = BKT / 8;                    // 16-byte chunks per tile row
   constexpr int TMW = BM / WMW, TNW = BN / WNW;  // wave tile
   constexpr int TM = TMW / 32, TN = TNW / 32;
-  constexpr int A_LD = BM * 8 / NT, B_LD = BN * 8 / NT;  // global_load_lds per thread per k-tile
+  constexpr int A_LD = BM * CH / NT, B_LD = BN * CH / NT;  // global_load_lds per thread per k-tile
   constexpr int LDT = A_LD + B_LD;
-  static_assert(A_LD >= 1 && B_LD >= 1 && (BM * 8) % NT == 0 && (BN * 8) % NT == 0, "tile/thread mismatch");
+  static_assert(A_LD >= 1 && B_LD >= 1 && (BM * CH) % NT == 0 && (BN * CH) % NT == 0, "tile/thread mismatch");
   static_assert(EM != E_SILU_MUL || (TN % 2) == 0, "silu-mul needs gate/up block pairs in a wave");
   static_assert((NS - 2) * LDT <= 63, "vmcnt range");
 
-  __shared__ u32x4 lds[NS][(BM + BN) * 8];
-  constexpr int kScratchFloats = (BM + BN) * 8 * 4 / NW;  // per-wave slice of one stage
-  static_assert(kScratchFloats >= 32 * 36, "epilogue scratch does not fit a stage");
+  __shared__ u32x4 lds[NS][(BM + BN) * CH];
+  constexpr int kScratchFloats = (BM + BN) * CH * 4 / NW;  // per-wave slice of one stage
+  constexpr int kEpiRows = kScratchFloats >= 32 * 32 ? 32 : 16;
+  static_assert(kScratchFloats >= 16 * 32 && kScratchFloats >= 32 * 20 && (EM != E_QKV_ROPE || kScratchFloats >= 32 * 32),
+                "epilogue scratch does not fit a stage");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WNW, wn = wave % WNW;
@@ -462,7 +534,7 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
   const int tiles_n = (BMD == B_GATEUP ? 2 * g.N : g.N) / BN;
   const int tiles_m = (g.M + BM - 1) / BM;
   const int ntiles = tiles_m * tiles_n;
-  const int KT = g.K / BK;
+  const int KT = g.K / BKT;
 
   // this workgroup's tiles: the blocks b with equal x = b % 8 (one XCD, nx
   // of them populated) own tiles [lo_x, hi_x); the nb_x blocks of XCD x
@@ -497,7 +569,7 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
 #pragma unroll
     for (int q = 0; q < A_LD; ++q) {
       const int p = (wave * A_LD + q) * 64 + lane;
-      const int P = p >> 3, gc = (p & 7) ^ swz(P);
+      const int P = p / CH, gc = (p % CH) ^ swzc<CH>(P);
       int m = tm * BM + P;
       m = m < g.M ? m : g.M - 1;
       ga[q] = reinterpret_cast<const char*>(g.A) + (size_t(m) * g.lda + gc * 8) * 2;
@@ -505,7 +577,7 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
 #pragma unroll
     for (int q = 0; q < B_LD; ++q) {
       const int p = (wave * B_LD + q) * 64 + lane;
-      const int P = p >> 3, gc = (p & 7) ^ swz(P);
+      const int P = p / CH, gc = (p % CH) ^ swzc<CH>(P);
       gb[q] = b_row<BMD>(g, tn * BN + P) + gc * 16;
     }
   };
@@ -515,7 +587,7 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
   auto issue_next = [&]() {
     if (is_kt == 0) set_rows(tile_of(is_tile));
     const int st = is_step % NS;
-    const size_t koff = size_t(is_kt) * BK * 2;
+    const size_t koff = size_t(is_kt) * BKT * 2;
 #pragma unroll
     for (int q = 0; q < A_LD; ++q)
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(ga[q] + koff),
@@ -523,7 +595,7 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
 #pragma unroll
     for (int q = 0; q < B_LD; ++q)
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(gb[q] + koff),
-                                       (lds_void*)&lds[st][BM * 8 + (wave * B_LD + q) * 64], 16, 0, 0);
+                                       (lds_void*)&lds[st][BM * CH + (wave * B_LD + q) * 64], 16, 0, 0);
     ++is_step;
     if (++is_kt == KT) {
       is_kt = 0;
@@ -555,26 +627,51 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
     __syncthreads();
     if (is_step < steps) issue_next();
     const u32x4* sa = lds[step % NS];
-    const u32x4* sb = lds[step % NS] + BM * 8;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    const u32x4* sb = lds[step % NS] + BM * CH;
+    // fragments of k-substep ks + 1 are read while the MFMAs of ks run
+    constexpr int KS = BKT / 16;
+    u32x4 fa[2][TM], fb[2][TN];
+    auto read_frags = [&](int ks, u32x4 (&ra)[TM], u32x4 (&rb)[TN]) {
       const int ch = 2 * ks + lhalf;
-      u32x4 fa[TM], fb[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int row = wm * TMW + 32 * i + lrow;
-        fa[i] = sa[row * 8 + (ch ^ swz(row))];
+        ra[i] = sa[row * CH + (ch ^ swzc<CH>(row))];
       }
 #pragma unroll
       for (int jn = 0; jn < TN; ++jn) {
         const int row = wn * TNW + 32 * jn + lrow;
-        fb[jn] = sb[row * 8 + (ch ^ swz(row))];
+        rb[jn] = sb[row * CH + (ch ^ swzc<CH>(row))];
       }
+    };
+    read_frags(0, fa[0], fb[0]);
+    static_for<KS>([&](auto ks_c) {
+      constexpr int ks = decltype(ks_c)::value;
+      if constexpr (ks + 1 < KS) read_frags(ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int jn = 0; jn < TN; ++jn) acc[i][jn] = mfma32x32x16(fa[i], fb[jn], acc[i][jn]);
-    }
+        for (int jn = 0; jn < TN; ++jn) acc[i][jn] = mfma32x32x16(fa[ks & 1][i], fb[ks & 1][jn], acc[i][jn]);
+    });
+#if PV_GEMM_SCHED == 1
+    // issue order: the first fragments, then per k-substep the next
+    // fragments' reads spread between that substep's MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+    static_for<KS>([&](auto ks_c) {
+      constexpr int ks = decltype(ks_c)::value;
+      if constexpr (ks + 1 < KS) {
+        constexpr int NMF = TM * TN, NRD = TM + TN, PAIRS = NMF < NRD ? NMF : NRD;
+        static_for<PAIRS>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        });
+        if constexpr (NMF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
+        if constexpr (NRD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PAIRS, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+      }
+    });
+#endif
     if (++kt == KT) {
       int tm, tn;
       tile_mn(tile_of(ti), tm, tn);
@@ -583,7 +680,7 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
       // uses its own slice of it to stage the output
       __syncthreads();
       float* scratch = reinterpret_cast<float*>(lds[step % NS]) + wave * kScratchFloats;
-      epilogue_lds<EM, TM, TN>(g, acc, tm * BM + wm * TMW, tn * BN + wn * TNW, lane, scratch);
+      epilogue_lds<EM, TM, TN, kEpiRows>(g, acc, tm * BM + wm * TMW, tn * BN + wn * TNW, lane, scratch);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -596,14 +693,18 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
   }
 }
 
-template <int BM, int BN, int WMW, int WNW, int NS, int BMD, int EM>
+template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int BMD, int EM>
 hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
   const int ncols = (BMD == B_GATEUP) ? 2 * g.N : g.N;
-  if (ncols % BN || g.K % BK) return hipErrorInvalidValue;
+  if (ncols % BN || g.K % BKT) return hipErrorInvalidValue;
   const int tiles = ((g.M + BM - 1) / BM) * (ncols / BN);
-  // one resident workgroup per CU (the LDS ring takes most of the 160 KiB)
-  const int grid = tiles < kNumCUs ? tiles : kNumCUs;
-  hipLaunchKernelGGL((gemm_dense_kernel<BM, BN, WMW, WNW, NS, BMD, EM>), dim3(grid), dim3(WMW * WNW * 64), 0, s, g);
+  // as many workgroups as fit on the chip at once: the LDS ring sets how
+  // many a CU holds
+  constexpr int kLdsBytes = NS * (BM + BN) * BKT * 2;
+  constexpr int kPerCU = (160 * 1024) / kLdsBytes < 2 ? 1 : 2;
+  const int grid = tiles < kNumCUs * kPerCU ? tiles : kNumCUs * kPerCU;
+  hipLaunchKernelGGL((gemm_dense_kernel<BM, BN, WMW, WNW, NS, BKT, BMD, EM>), dim3(grid), dim3(WMW * WNW * 64), 0, s,
+                     g);
   return hipGetLastError();
 }
 
@@ -618,20 +719,26 @@ hipError_t launch(const GemmArgs& g, hipStream_t s) {
 
 }  // namespace
 
-// Tile configurations (BM, BN, waves along M, waves along N, LDS stages) of
-// the dense GEMMs: wide-N products and the N = hidden products.
+// Tile configurations (BM, BN, waves along M, waves along N, LDS stages, k
+// depth of a stage) of the dense GEMMs: wide-N products and the N = hidden
+// products.
 #ifndef PV_GEMM_CFG_BIG
-#define PV_GEMM_CFG_BIG 256, 256, 4, 2, 2
+#define PV_GEMM_CFG_BIG 256, 256, 4, 2, 2, 64
 #endif
 #ifndef PV_GEMM_CFG_N1K
-#define PV_GEMM_CFG_N1K 256, 128, 4, 2, 2
+#define PV_GEMM_CFG_N1K 256, 128, 4, 2, 2, 64
+#endif
+// q,k,v: 192-column tiles (16 per row of tiles instead of 12) balance the
+// 1540 x 1540 image's 48 rows of tiles evenly over the 256 CUs
+#ifndef PV_GEMM_CFG_QKV
+#define PV_GEMM_CFG_QKV 256, 192, 4, 2, 2, 64
 #endif
 
 hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
   switch (kind) {
     case GEMM_PATCH:  return launch<128, 128, A_IM2COL, B_ONE, E_STORE_F32>(g, s);
-    case GEMM_QKV:    return launch_dense<PV_GEMM_CFG_BIG, B_QKV, E_QKV_ROPE>(g, s);
+    case GEMM_QKV:    return launch_dense<PV_GEMM_CFG_QKV, B_QKV, E_QKV_ROPE>(g, s);
     case GEMM_OPROJ:  return launch_dense<PV_GEMM_CFG_N1K, B_ONE, E_ADD_F32>(g, s);
     case GEMM_GATEUP: return launch_dense<PV_GEMM_CFG_BIG, B_GATEUP, E_SILU_MUL>(g, s);
     case GEMM_DOWN:   return launch_dense<PV_GEMM_CFG_N1K, B_ONE, E_ADD_F32>(g, s);
