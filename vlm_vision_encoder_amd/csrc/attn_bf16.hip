@@ -90,7 +90,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
   const uint16_t* qkv = reinterpret_cast<const uint16_t*>(a.qkv);
   const int qoff = head * 64, koff = D + head * 64, voff = 2 * D + head * 64;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // uniform wave index (scalar): the LDS destinations of the direct loads
+  // (M0) are then computed on the scalar unit
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int wq0 = it.q0 + 32 * QB * wave;  // first query of this wave
   const bool active = wq0 < n;

@@ -369,9 +369,33 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 // epilogue and >= 32 * 20 floats for bf16 outputs.
 __device__ __forceinline__ int stage_row(int r) { return r ^ ((r >> 2) & 1); }
 
+// Read-back layout of the fp32 epilogue: pass h, iteration it of block
+// (i, j) gives a lane row (lane >> 3) + 8 * it + h * SR, columns 4 * (lane & 7)
+// .. +3.  load_residual fetches the residual values of those positions ahead
+// of time (E_ADD_F32), so the read-modify-write does not wait for them.
+template <int TM, int TN>
+struct Residual {
+  floatx4 v[TM][TN][4];
+};
+template <int TM, int TN>
+__device__ __forceinline__ void load_residual(const GemmArgs& g, Residual<TM, TN>& res, int m_base, int n_base,
+                                              int lane) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int row = m_base + 32 * i + (lane >> 3) + 8 * it, col = n_base + 32 * j + 4 * (lane & 7);
+        const int rr = row < g.M ? row : g.M - 1;  // rows past M are loaded but never stored
+        res.v[i][j][it] =
+            *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(g.C) + size_t(rr) * g.ldc + col);
+      }
+}
+
 template <int EM, int TM, int TN, int SR = 32>
 __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[TM][TN], int m_base, int n_base,
-                                             int lane, float* scratch) {
+                                             int lane, float* scratch, const Residual<TM, TN>* res = nullptr) {
   const int lrow = lane & 31, lhalf = lane >> 5;
   if constexpr (EM == E_ADD_F32 || EM == E_STORE_F32) {
     static_assert(SR == 32 || SR == 16, "staging rows");
@@ -393,8 +417,12 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[
             const int row = m_base + 32 * i + h * SR + r, col = n_base + 32 * j + c4;
             if (row < g.M) {
               floatx4* dst = reinterpret_cast<floatx4*>(reinterpret_cast<float*>(g.C) + size_t(row) * g.ldc + col);
-              if constexpr (EM == E_ADD_F32) *dst = *dst + val;
-              else *dst = val;
+              if constexpr (EM == E_ADD_F32) {
+                static_assert(EM != E_ADD_F32 || SR == 32, "prefetched residual assumes one pass per block");
+                *dst = (res ? res->v[i][j][it] : *dst) + val;
+              } else {
+                *dst = val;
+              }
             }
           }
           __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next pass's writes
@@ -470,8 +498,10 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[
           const int rib = 8 * (v >> 2) + 4 * lhalf + (v & 3);  // row in block
           float x;
           if constexpr (EM == E_SILU_MUL) {
+            // silu(g) * u = g * u / (1 + e^-g); the approximate reciprocal
+            // (1 ulp) is far inside the bf16 rounding that follows
             const float gt = acc[i][2 * jb][v], up = acc[i][2 * jb + 1][v];
-            x = gt / (1.f + __expf(-gt)) * up;
+            x = gt * up * __builtin_amdgcn_rcpf(1.f + __expf(-gt));
             ocol0 = (n_base + 64 * jb) / 2;
           } else {
             x = acc[i][jb][v];
@@ -528,7 +558,9 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
   static_assert(kScratchFloats >= 16 * 32 && kScratchFloats >= 32 * 20 && (EM != E_QKV_ROPE || kScratchFloats >= 32 * 32),
                 "epilogue scratch does not fit a stage");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: keeping it scalar puts the LDS destinations of
+  // the direct loads (M0) on the scalar unit
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WNW, wn = wave % WNW;
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int tiles_n = (BMD == B_GATEUP ? 2 * g.N : g.N) / BN;
@@ -626,6 +658,16 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
     }
     __syncthreads();
     if (is_step < steps) issue_next();
+    // the residual of an accumulating epilogue is fetched while the tile's
+    // last k-step runs
+    Residual<TM, TN> res;
+    if constexpr (EM == E_ADD_F32) {
+      if (kt == KT - 1) {
+        int tm, tn;
+        tile_mn(tile_of(ti), tm, tn);
+        load_residual<TM, TN>(g, res, tm * BM + wm * TMW, tn * BN + wn * TNW, lane);
+      }
+    }
     const u32x4* sa = lds[step % NS];
     const u32x4* sb = lds[step % NS] + BM * CH;
     // fragments of k-substep ks + 1 are read while the MFMAs of ks run
@@ -680,7 +722,8 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
       // uses its own slice of it to stage the output
       __syncthreads();
       float* scratch = reinterpret_cast<float*>(lds[step % NS]) + wave * kScratchFloats;
-      epilogue_lds<EM, TM, TN, kEpiRows>(g, acc, tm * BM + wm * TMW, tn * BN + wn * TNW, lane, scratch);
+      epilogue_lds<EM, TM, TN, kEpiRows>(g, acc, tm * BM + wm * TMW, tn * BN + wn * TNW, lane, scratch,
+                                         EM == E_ADD_F32 ? &res : nullptr);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
