@@ -95,6 +95,7 @@ struct GemmArgs {
   const void* B1;
   const void* B2;
   int32_t ldb;
+  int32_t kb;         // K extent of B when A's K repeats it (hi | lo halves of A), else 0
   void* C;
   int32_t ldc;
   int32_t hidden;     // D (QKV split, merge gather)

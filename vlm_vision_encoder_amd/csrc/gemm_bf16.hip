@@ -567,6 +567,8 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
   const int tiles_m = (g.M + BM - 1) / BM;
   const int ntiles = tiles_m * tiles_n;
   const int KT = g.K / BKT;
+  // k-tiles of B: A's K may run over B's K twice (hi | lo halves of A)
+  const int KTB = g.kb > 0 ? g.kb / BKT : KT;
 
   // this workgroup's tiles: the blocks b with equal x = b % 8 (one XCD, nx
   // of them populated) own tiles [lo_x, hi_x); the nb_x blocks of XCD x
@@ -620,13 +622,14 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
     if (is_kt == 0) set_rows(tile_of(is_tile));
     const int st = is_step % NS;
     const size_t koff = size_t(is_kt) * BKT * 2;
+    const size_t koffb = size_t(is_kt < KTB ? is_kt : is_kt - KTB) * BKT * 2;
 #pragma unroll
     for (int q = 0; q < A_LD; ++q)
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(ga[q] + koff),
                                        (lds_void*)&lds[st][(wave * A_LD + q) * 64], 16, 0, 0);
 #pragma unroll
     for (int q = 0; q < B_LD; ++q)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(gb[q] + koff),
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(gb[q] + koffb),
                                        (lds_void*)&lds[st][BM * CH + (wave * B_LD + q) * 64], 16, 0, 0);
     ++is_step;
     if (++is_kt == KT) {
@@ -739,7 +742,8 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
 template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int BMD, int EM>
 hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
   const int ncols = (BMD == B_GATEUP) ? 2 * g.N : g.N;
-  if (ncols % BN || g.K % BKT) return hipErrorInvalidValue;
+  if (ncols % BN || g.K % BKT || g.kb % BKT) return hipErrorInvalidValue;
+  if (g.kb > 0 && g.K != 2 * g.kb) return hipErrorInvalidValue;
   const int tiles = ((g.M + BM - 1) / BM) * (ncols / BN);
   // as many workgroups as fit on the chip at once: the LDS ring sets how
   // many a CU holds

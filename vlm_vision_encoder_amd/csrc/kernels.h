@@ -30,6 +30,8 @@ hipError_t gemm_f32(GemmKind kind, const GemmArgs& g, hipStream_t s);
 //   rmsnorm_dual: h = norm(x) * g1 written back in place (fp32), y = norm(h) * g2
 hipError_t rmsnorm(const float* x, const float* g, void* y, int rows, int D, float eps,
                    bool y_f32, hipStream_t s);
+// rmsnorm_split: y = norm(x) * g as [N][2D] bf16: hi | lo = bf16(y - hi)
+hipError_t rmsnorm_split(const float* x, const float* g, void* y, int rows, int D, float eps, hipStream_t s);
 hipError_t rmsnorm_dual(float* x, const float* g1, const float* g2, void* y, int rows, int D,
                         float eps, bool y_f32, hipStream_t s);
 

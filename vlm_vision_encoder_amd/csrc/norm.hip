@@ -38,6 +38,42 @@ __device__ __forceinline__ void store_row(void* y, size_t row, int D, int lane, 
   }
 }
 
+// bf16 hi and lo = bf16(v - hi) of a row, stored as [hi (D) | lo (D)]: a
+// product over both halves carries about 16 significant bits of v.
+template <int NC>
+__device__ __forceinline__ void store_row_split(void* y, size_t row, int D, int lane, const floatx4 (&v)[NC]) {
+  uint16_t* yr = reinterpret_cast<uint16_t*>(y) + row * 2 * D;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const size_t o = size_t(i * 64 + lane) * 4;
+    u32x2 hi, lo;
+    hi[0] = pack_bf16x2(v[i][0], v[i][1]);
+    hi[1] = pack_bf16x2(v[i][2], v[i][3]);
+    lo[0] = pack_bf16x2(v[i][0] - lo_bf16(hi[0]), v[i][1] - hi_bf16(hi[0]));
+    lo[1] = pack_bf16x2(v[i][2] - lo_bf16(hi[1]), v[i][3] - hi_bf16(hi[1]));
+    *reinterpret_cast<u32x2*>(yr + o) = hi;
+    *reinterpret_cast<u32x2*>(yr + D + o) = lo;
+  }
+}
+
+template <int NC>
+__global__ __launch_bounds__(256) void rmsnorm_split_kernel(const float* __restrict__ x, const float* __restrict__ g,
+                                                            void* __restrict__ y, int rows, float eps) {
+  constexpr int D = NC * 256;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const floatx4* xr = reinterpret_cast<const floatx4*>(x + size_t(row) * D);
+  const floatx4* gr = reinterpret_cast<const floatx4*>(g);
+  floatx4 v[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) v[i] = xr[i * 64 + lane];
+  const float inv = rsqrtf(sumsq<NC>(v) * (1.f / D) + eps);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) v[i] = v[i] * inv * gr[i * 64 + lane];
+  store_row_split<NC>(y, row, D, lane, v);
+}
+
 template <int NC, bool YF32>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, const float* __restrict__ g,
                                                       void* __restrict__ y, int rows, float eps) {
@@ -103,6 +139,19 @@ hipError_t rmsnorm(const float* x, const float* g, void* y, int rows, int D, flo
     if (y_f32) hipLaunchKernelGGL((rmsnorm_kernel<NC, true>), grid, block, 0, s, x, g, y, rows, eps); \
     else hipLaunchKernelGGL((rmsnorm_kernel<NC, false>), grid, block, 0, s, x, g, y, rows, eps);     \
     return hipGetLastError();                                                                     \
+  }
+  PV_NORM_CASES(PV_CASE)
+#undef PV_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t rmsnorm_split(const float* x, const float* g, void* y, int rows, int D, float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((rows + 3) / 4), block(256);
+#define PV_CASE(NC)                                                                       \
+  if (D == NC * 256) {                                                                    \
+    hipLaunchKernelGGL((rmsnorm_split_kernel<NC>), grid, block, 0, s, x, g, y, rows, eps); \
+    return hipGetLastError();                                                             \
   }
   PV_NORM_CASES(PV_CASE)
 #undef PV_CASE

@@ -92,8 +92,8 @@ int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, P
   const size_t N = size_t(patches), D = size_t(p.hidden);
   L.r = off;
   off = align256(off + N * D * 4);
-  L.y = off;
-  off = align256(off + N * D * p.elem_bytes);
+  L.y = off;  // bf16 tower: [N][2D] (the MLP input's hi | lo halves); fp32: [N][D]
+  off = align256(off + N * D * 4);
   L.big = off;
   off = align256(off + N * std::max(3 * D, size_t(p.mlp)) * p.elem_bytes);
   L.total = off;
