@@ -1,24 +1,19 @@
 // bf16 GEMM family on CDNA4 MFMA (v_mfma_f32_32x32x16_bf16):
 //   C[M][N] = A[M][K] * B[N][K]^T  (fp32 accumulation)
-// with three A-operand loaders and five epilogues, covering every linear map
-// of the tower:
-//   patch embedding   A = im2col(pixels) (fp32 -> bf16 in the load), C fp32
+// covering every linear map of the tower ("Mistral 3" (KerasFormers),
+// Mistral3VisionModel and Mistral3Model table):
+//   patch embedding   A = im2col of the pixels as bf16 hi | lo, C fp32
 //   q,k,v             A = y, B rows from wq|wk|wv, epilogue rotates q and k
 //   out-projection    A = attention output, epilogue adds into the residual
-//   MLP gate/up       B rows interleave gate and up, epilogue silu(g) * u
+//   MLP gate/up       A = y as hi | lo, B rows interleave gate and up,
+//                     epilogue silu(g) * u
 //   MLP down          epilogue adds into the residual
-//   merger            A = 2x2 gather of the residual (fp32 -> bf16 in the load)
-// ("Mistral 3" (KerasFormers), Mistral3VisionModel and Mistral3Model table.)
-//
-// Tiling: BM x BN x 64 block tile, 256 threads = 4 waves in a 2 x 2 grid,
-// each wave owns a (BM/2) x (BN/2) tile of 32x32 MFMA blocks.  A and B tiles
-// are staged through registers into double-buffered LDS (one barrier per
-// k-tile); rows are 128 bytes = 8 chunks of 16 bytes, and chunk c of row r is
-// stored at c ^ ((r >> 1) & 7): the LDS has 64 four-byte banks and serves a
-// 16-byte read for 16 lanes (16 consecutive rows) per pass, which then differ
-// in (row parity, chunk) and hit distinct banks.  Blocks are renumbered so each XCD (blocks b with the same
-// b % 8) works on a contiguous range of output tiles, which keeps the A panel
-// and the weights it shares in that XCD's L2.
+//   merger            A = 2x2 gather of the residual (bf16 hi | lo copy),
+//                     done by the A-operand loads themselves
+// Operands that carry fp32 values (pixels, the MLP input, the final
+// residual) enter as two bf16 halves hi and lo = bf16(x - hi) over a K range
+// twice as long, both against the same B rows (GemmArgs::kb): about 16
+// significant bits of the fp32 operand on bf16 MFMAs.
 #include <type_traits>
 
 #include "common.h"
@@ -30,7 +25,6 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int BK = 64;
 constexpr int kNumCUs = 256;  // MI355X: 8 XCDs x 32 CUs
 // tile rows per group of the persistent dense GEMM's tile order
 #ifndef PV_GEMM_GM
@@ -48,97 +42,17 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
-// The same for rows of CH chunks (CH = 8: 128-byte rows, as swz; CH = 4:
-// 64-byte rows, where four consecutive rows already span the 64 banks, so the
-// 16 rows of a pass must differ in (row % 4, chunk): chunk ^ ((row >> 2) & 3)).
+// 16-byte chunk swizzle of LDS tile rows of CH chunks.  The LDS has 64
+// four-byte banks and serves a 16-byte read for 16 lanes (16 consecutive
+// rows) per pass.  CH = 8 (128-byte rows): chunk ^ ((row >> 1) & 7) makes
+// those rows differ in (row parity, chunk); CH = 4 (64-byte rows): four
+// consecutive rows already span the 64 banks, so they must differ in
+// (row % 4, chunk): chunk ^ ((row >> 2) & 3).
 template <int CH>
 __device__ __forceinline__ int swzc(int row) {
   static_assert(CH == 8 || CH == 4, "row width");
   if constexpr (CH == 8) return (row >> 1) & 7;
   else return (row >> 2) & 3;
-}
-
-__device__ __forceinline__ int xcd_remap(int b, int nblocks) {
-  const int xcd = b & 7, idx = b >> 3;
-  const int per = nblocks >> 3, rem = nblocks & 7;
-  return xcd * per + (xcd < rem ? xcd : rem) + idx;
-}
-
-template <int AM>
-struct ARow {
-  const char* p0 = nullptr;  // A_DENSE: row pointer; A_IM2COL: image pixel base at the patch origin
-  int32_t hw = 0, w = 0;     // A_IM2COL: plane stride, row stride (elements)
-  int32_t src[4] = {0, 0, 0, 0};  // A_MERGE: source patch rows
-};
-
-// fp32 values -> bf16 hi and bf16 lo = bf16(x - hi): hi + lo carries about
-// 16 mantissa bits, so a product over both halves keeps the fp32 operand's
-// precision to within the accumulation error.
-__device__ __forceinline__ void split8(const float* f, u32x4& hi, u32x4& lo) {
-  hi = pack8(f);
-  float r[8];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    r[2 * e] = f[2 * e] - lo_bf16(hi[e]);
-    r[2 * e + 1] = f[2 * e + 1] - hi_bf16(hi[e]);
-  }
-  lo = pack8(r);
-}
-
-// Loads A[row][k0 .. k0+8) for one thread's chunk: bf16 rows are copied; the
-// fp32 operands (pixels, residual) are split into bf16 hi and lo parts.
-template <int AM>
-__device__ __forceinline__ void load_a_chunk(const GemmArgs& g, const ARow<AM>& r, int k0, u32x4& hi, u32x4& lo) {
-  if constexpr (AM == A_DENSE) {
-    hi = *reinterpret_cast<const u32x4*>(r.p0 + size_t(k0) * 2);
-  } else if constexpr (AM == A_IM2COL) {
-    const int p = g.maps.patch, pp = p * p;
-    const float* base = reinterpret_cast<const float*>(r.p0);
-    float f[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int k = k0 + e;
-      float v = 0.f;
-      if (k < g.K) {
-        const int ch = k / pp, rem = k - ch * pp;
-        const int u = rem / p, x = rem - u * p;
-        v = base[size_t(ch) * r.hw + size_t(u) * r.w + x];
-      }
-      f[e] = v;
-    }
-    split8(f, hi, lo);
-  } else {
-    const int D = g.hidden;
-    const int q = k0 / D, ch = k0 - q * D;
-    const float* src = reinterpret_cast<const float*>(g.A) + size_t(r.src[q]) * D + ch;
-    const floatx4 a = *reinterpret_cast<const floatx4*>(src);
-    const floatx4 b = *reinterpret_cast<const floatx4*>(src + 4);
-    float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    split8(f, hi, lo);
-  }
-}
-
-template <int AM>
-__device__ __forceinline__ ARow<AM> a_row(const GemmArgs& g, int m) {
-  ARow<AM> r;
-  m = m < g.M ? m : g.M - 1;  // rows past M are computed but never stored
-  if constexpr (AM == A_DENSE) {
-    r.p0 = reinterpret_cast<const char*>(g.A) + size_t(m) * g.lda * 2;
-  } else if constexpr (AM == A_IM2COL) {
-    const int img = g.maps.rowinfo[2 * m];
-    const int rc = g.maps.rowinfo[2 * m + 1];
-    const ImageMeta mt = g.maps.meta[img];
-    const int p = g.maps.patch;
-    const int pr = rc >> 16, pc = rc & 0xffff;
-    r.hw = mt.H * mt.W;
-    r.w = mt.W;
-    r.p0 = reinterpret_cast<const char*>(g.pixels + pix_offset(mt) + size_t(pr * p) * mt.W + pc * p);
-  } else {
-    const int4 s = reinterpret_cast<const int4*>(g.maps.msrc)[m];
-    r.src[0] = s.x; r.src[1] = s.y; r.src[2] = s.z; r.src[3] = s.w;
-  }
-  return r;
 }
 
 // Row pointer of B-tile row n (global output column n of this GEMM).
@@ -160,194 +74,6 @@ __device__ __forceinline__ const char* b_row(const GemmArgs& g, int n) {
     return reinterpret_cast<const char*>(b) + size_t(j) * g.ldb * 2;
   }
 }
-
-// Epilogue of one wave's TM x TN grid of 32x32 accumulator blocks whose
-// top-left output element is (m_base, n_base).  C layout of a 32x32 block:
-// lane holds column (lane & 31) and rows 8*(v/4) + 4*(lane/32) + (v%4).
-template <int EM, int TM, int TN>
-__device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[TM][TN], int m_base, int n_base,
-                                         int lrow, int lhalf) {
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = m_base + 32 * i + 8 * (v >> 2) + 4 * lhalf + (v & 3);
-      const bool ok = row < g.M;
-      if constexpr (EM == E_SILU_MUL) {
-#pragma unroll
-        for (int jj = 0; jj < TN / 2; ++jj) {
-          const float gt = acc[i][2 * jj][v], up = acc[i][2 * jj + 1][v];
-          const float sv = gt / (1.f + __expf(-gt)) * up;
-          const int col = (n_base + 64 * jj) / 2 + lrow;
-          if (ok) reinterpret_cast<bf16*>(g.C)[size_t(row) * g.ldc + col] = (bf16)sv;
-        }
-      } else if constexpr (EM == E_QKV_ROPE) {
-        int rc = 0;
-        if (ok) rc = g.maps.rowinfo[2 * row + 1];
-        const int pr = rc >> 16, pc = rc & 0xffff;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = n_base + 32 * j + lrow;
-          float x = acc[i][j][v];
-          const float xp = swap_adjacent(x);
-          if (col < 2 * g.hidden) {
-            const int d = col & 63, pair = d >> 1;
-            const int axis = pair >> 4, m = pair & 15;
-            const int pos = axis ? pc : pr;
-            const float2 cs = reinterpret_cast<const float2*>(g.maps.rope)[(axis * g.maps.rope_maxpos + pos) * 16 + m];
-            // even lane: x0 cos - x1 sin ; odd lane: x0 sin + x1 cos
-            x = (d & 1) ? (xp * cs.y + x * cs.x) : (x * cs.x - xp * cs.y);
-            // q leaves in exp2 units of the attention softmax: times
-            // log2(e)/sqrt(64), before its single rounding to bf16
-            if (col < g.hidden) x *= 0.18033688011112042f;
-          }
-          if (ok) reinterpret_cast<bf16*>(g.C)[size_t(row) * g.ldc + col] = (bf16)x;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = n_base + 32 * j + lrow;
-          if (!ok || col >= g.N) continue;
-          const size_t o = size_t(row) * g.ldc + col;
-          if constexpr (EM == E_STORE) {
-            reinterpret_cast<bf16*>(g.C)[o] = (bf16)acc[i][j][v];
-          } else if constexpr (EM == E_STORE_F32) {
-            reinterpret_cast<float*>(g.C)[o] = acc[i][j][v];
-          } else {
-            reinterpret_cast<float*>(g.C)[o] += acc[i][j][v];
-          }
-        }
-      }
-    }
-  }
-}
-
-template <int BM, int BN, int AM, int BMD, int EM>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int AC = BM * 8 / 256;  // 16-byte A chunks per thread per k-tile
-  constexpr int BC = BN * 8 / 256;
-  static_assert(AC >= 1 && BC >= 1, "tile too small");
-  static_assert(EM != E_SILU_MUL || (TN % 2) == 0, "silu-mul needs gate/up block pairs in a wave");
-  // fp32 A operands (pixels, residual) run as two bf16 products, hi and lo
-  constexpr bool SPLIT = AM != A_DENSE;
-  constexpr int AROWS = SPLIT ? 2 * BM : BM;  // LDS rows of the A tile(s)
-
-  __shared__ u32x4 lds[2][(AROWS + BN) * 8];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_n = (BMD == B_GATEUP ? 2 * g.N : g.N) / BN;
-  const int tiles_m = (g.M + BM - 1) / BM;
-  const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-  const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  // Per-thread global row descriptors (fixed across k-tiles).
-  ARow<AM> arow[AC];
-  const char* brow[BC];
-#pragma unroll
-  for (int i = 0; i < AC; ++i) arow[i] = a_row<AM>(g, m0 + ((tid + 256 * i) >> 3));
-#pragma unroll
-  for (int i = 0; i < BC; ++i) brow[i] = b_row<BMD>(g, n0 + ((tid + 256 * i) >> 3));
-  const int cchunk = tid & 7;
-
-  u32x4 ra[AC], ral[SPLIT ? AC : 1], rb[BC];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK + cchunk * 8;
-#pragma unroll
-    for (int i = 0; i < AC; ++i) load_a_chunk<AM>(g, arow[i], k0, ra[i], ral[SPLIT ? i : 0]);
-#pragma unroll
-    for (int i = 0; i < BC; ++i) {
-      if constexpr (AM == A_IM2COL) {
-        // patch kernel rows have 3 p^2 elements: ragged K and rows that are
-        // only 2-byte aligned, so load element by element
-        const uint16_t* src = reinterpret_cast<const uint16_t*>(brow[i]) + k0;
-        uint16_t h[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = (k0 + e < g.K) ? src[e] : uint16_t(0);
-        u32x4 z;
-        z[0] = h[0] | (uint32_t(h[1]) << 16);
-        z[1] = h[2] | (uint32_t(h[3]) << 16);
-        z[2] = h[4] | (uint32_t(h[5]) << 16);
-        z[3] = h[6] | (uint32_t(h[7]) << 16);
-        rb[i] = z;
-      } else {
-        rb[i] = *reinterpret_cast<const u32x4*>(brow[i] + size_t(k0) * 2);
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < AC; ++i) {
-      const int row = (tid + 256 * i) >> 3;
-      lds[buf][row * 8 + (cchunk ^ swz(row))] = ra[i];
-      if constexpr (SPLIT) lds[buf][(BM + row) * 8 + (cchunk ^ swz(row))] = ral[i];
-    }
-#pragma unroll
-    for (int i = 0; i < BC; ++i) {
-      const int row = (tid + 256 * i) >> 3;
-      lds[buf][(AROWS + row) * 8 + (cchunk ^ swz(row))] = rb[i];
-    }
-  };
-
-  floatx16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  const int KT = (g.K + BK - 1) / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  const int lrow = lane & 31, lhalf = lane >> 5;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    const u32x4* sa = lds[buf];
-    const u32x4* sb = lds[buf] + AROWS * 8;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int ch = 2 * ks + lhalf;
-      u32x4 fa[TM], fb[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * WM + 32 * i + lrow;
-        fa[i] = sa[row * 8 + (ch ^ swz(row))];
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int row = wn * WN + 32 * j + lrow;
-        fb[j] = sb[row * 8 + (ch ^ swz(row))];
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
-      if constexpr (SPLIT) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int row = BM + wm * WM + 32 * i + lrow;
-          fa[i] = sa[row * 8 + (ch ^ swz(row))];
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
-      }
-    }
-    if (kt + 1 < KT) sstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  epilogue<EM, TM, TN>(g, acc, m0 + wm * WM, n0 + wn * WN, lrow, lhalf);
-}
-
 
 // Epilogue through LDS: each 32x32 accumulator block is written to a per-wave
 // LDS scratch in row-major order and read back so that every lane owns 8
@@ -529,7 +255,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[
 // lgkmcnt left at their maxima).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// Dense-A GEMM (q,k,v, out-projection, gate/up, down), persistent: each
+// Persistent GEMM (every linear map of the bf16 tower): each
 // workgroup walks a fixed list of output tiles, and the global -> LDS load
 // ring (global_load_lds_dwordx4, NS stages, no VGPR staging) runs over the
 // flattened sequence of (tile, k-tile) steps, so the next tile's first
@@ -540,8 +266,13 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 // workgroups of one XCD (blocks b with equal b % 8) share a contiguous range
 // of tiles, grouped GM tile rows at a time, keeping the A and B panels they
 // share in that XCD's L2.
-template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int BMD, int EM>
+// A operand (AMD): A_DENSE, rows of A; A_MERGE, output row t of the merger
+// is the concatenation of four residual rows msrc[t][0..3] (2x2 patch
+// gather): the loads fetch straight from the [rows][2D] hi | lo copy of the
+// residual, K = 8D = (hi: 4 gathered rows) | (lo: the same 4 rows).
+template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int AMD, int BMD, int EM>
 __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) {
+  static_assert(AMD == A_DENSE || AMD == A_MERGE, "A operand mode");
   constexpr int NW = WMW * WNW, NT = NW * 64;
   constexpr int CH = BKT / 8;                    // 16-byte chunks per tile row
   constexpr int TMW = BM / WMW, TNW = BN / WNW;  // wave tile
@@ -597,6 +328,8 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
   // [(wave * X_LD + q) * 64, +64) of the A (B) tile; lane l takes slot p.
   const char* ga[A_LD];
   const char* gb[B_LD];
+  int4 msrc4[AMD == A_MERGE ? A_LD : 1];  // A_MERGE: source rows of each load slot's row
+  int a_gc[AMD == A_MERGE ? A_LD : 1];    // A_MERGE: chunk each load slot fetches
   auto set_rows = [&](int t) {
     int tm, tn;
     tile_mn(t, tm, tn);
@@ -605,8 +338,13 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
       const int p = (wave * A_LD + q) * 64 + lane;
       const int P = p / CH, gc = (p % CH) ^ swzc<CH>(P);
       int m = tm * BM + P;
-      m = m < g.M ? m : g.M - 1;
-      ga[q] = reinterpret_cast<const char*>(g.A) + (size_t(m) * g.lda + gc * 8) * 2;
+      m = m < g.M ? m : g.M - 1;  // rows past M are computed but never stored
+      if constexpr (AMD == A_DENSE) {
+        ga[q] = reinterpret_cast<const char*>(g.A) + (size_t(m) * g.lda + gc * 8) * 2;
+      } else {
+        msrc4[q] = reinterpret_cast<const int4*>(g.maps.msrc)[m];
+        a_gc[q] = gc;
+      }
     }
 #pragma unroll
     for (int q = 0; q < B_LD; ++q) {
@@ -618,10 +356,27 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
   // (the global source is passed as a uint16_t pointer: with a char pointer
   // the host pass drops the kernel's launch stub without a diagnostic)
   int is_step = 0, is_kt = 0, is_tile = 0;  // next step to issue
+  // A_MERGE: k-tiles per gathered row segment (D / BKT); segment s of K
+  // takes part s / 4 (hi, lo) of source row msrc[t][s % 4]
+  const int KTQ = AMD == A_MERGE ? g.hidden / BKT : 1;
   auto issue_next = [&]() {
     if (is_kt == 0) set_rows(tile_of(is_tile));
     const int st = is_step % NS;
-    const size_t koff = size_t(is_kt) * BKT * 2;
+    size_t koff = size_t(is_kt) * BKT * 2;
+    if constexpr (AMD == A_MERGE) {
+      const int seg = is_kt / KTQ, kin = is_kt - seg * KTQ;
+      if (kin == 0) {
+        const int part = seg >> 2, qi = seg & 3;
+#pragma unroll
+        for (int q = 0; q < A_LD; ++q) {
+          const int4 m4 = msrc4[q];
+          const int src = qi == 0 ? m4.x : (qi == 1 ? m4.y : (qi == 2 ? m4.z : m4.w));
+          ga[q] = reinterpret_cast<const char*>(g.A) +
+                  (size_t(src) * g.lda + size_t(part) * g.hidden + a_gc[q] * 8) * 2;
+        }
+      }
+      koff = size_t(kin) * BKT * 2;
+    }
     const size_t koffb = size_t(is_kt < KTB ? is_kt : is_kt - KTB) * BKT * 2;
 #pragma unroll
     for (int q = 0; q < A_LD; ++q)
@@ -739,28 +494,20 @@ __global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) 
   }
 }
 
-template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int BMD, int EM>
+template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int AMD, int BMD, int EM>
 hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
   const int ncols = (BMD == B_GATEUP) ? 2 * g.N : g.N;
   if (ncols % BN || g.K % BKT || g.kb % BKT) return hipErrorInvalidValue;
   if (g.kb > 0 && g.K != 2 * g.kb) return hipErrorInvalidValue;
+  if (AMD == A_MERGE && (g.hidden % BKT || g.K != 8 * g.hidden || g.kb != 4 * g.hidden)) return hipErrorInvalidValue;
   const int tiles = ((g.M + BM - 1) / BM) * (ncols / BN);
   // as many workgroups as fit on the chip at once: the LDS ring sets how
   // many a CU holds
   constexpr int kLdsBytes = NS * (BM + BN) * BKT * 2;
   constexpr int kPerCU = (160 * 1024) / kLdsBytes < 2 ? 1 : 2;
   const int grid = tiles < kNumCUs * kPerCU ? tiles : kNumCUs * kPerCU;
-  hipLaunchKernelGGL((gemm_dense_kernel<BM, BN, WMW, WNW, NS, BKT, BMD, EM>), dim3(grid), dim3(WMW * WNW * 64), 0, s,
-                     g);
-  return hipGetLastError();
-}
-
-template <int BM, int BN, int AM, int BMD, int EM>
-hipError_t launch(const GemmArgs& g, hipStream_t s) {
-  const int ncols = (BMD == B_GATEUP) ? 2 * g.N : g.N;
-  if (ncols % BN) return hipErrorInvalidValue;
-  const int tiles = ((g.M + BM - 1) / BM) * (ncols / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AM, BMD, EM>), dim3(tiles), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((gemm_dense_kernel<BM, BN, WMW, WNW, NS, BKT, AMD, BMD, EM>), dim3(grid), dim3(WMW * WNW * 64), 0,
+                     s, g);
   return hipGetLastError();
 }
 
@@ -784,14 +531,14 @@ hipError_t launch(const GemmArgs& g, hipStream_t s) {
 hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
   switch (kind) {
-    case GEMM_PATCH:  return launch<128, 128, A_IM2COL, B_ONE, E_STORE_F32>(g, s);
-    case GEMM_QKV:    return launch_dense<PV_GEMM_CFG_QKV, B_QKV, E_QKV_ROPE>(g, s);
-    case GEMM_OPROJ:  return launch_dense<PV_GEMM_CFG_N1K, B_ONE, E_ADD_F32>(g, s);
-    case GEMM_GATEUP: return launch_dense<PV_GEMM_CFG_BIG, B_GATEUP, E_SILU_MUL>(g, s);
-    case GEMM_DOWN:   return launch_dense<PV_GEMM_CFG_N1K, B_ONE, E_ADD_F32>(g, s);
-    case GEMM_MERGE:  return launch<128, 128, A_MERGE, B_ONE, E_STORE>(g, s);
-    case GEMM_PLAIN:  return launch_dense<PV_GEMM_CFG_N1K, B_ONE, E_STORE>(g, s);
-    case GEMM_MERGE_F32: return launch<128, 128, A_MERGE, B_ONE, E_STORE_F32>(g, s);
+    case GEMM_PATCH:  return launch_dense<PV_GEMM_CFG_N1K, A_DENSE, B_ONE, E_STORE_F32>(g, s);
+    case GEMM_QKV:    return launch_dense<PV_GEMM_CFG_QKV, A_DENSE, B_QKV, E_QKV_ROPE>(g, s);
+    case GEMM_OPROJ:  return launch_dense<PV_GEMM_CFG_N1K, A_DENSE, B_ONE, E_ADD_F32>(g, s);
+    case GEMM_GATEUP: return launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL>(g, s);
+    case GEMM_DOWN:   return launch_dense<PV_GEMM_CFG_N1K, A_DENSE, B_ONE, E_ADD_F32>(g, s);
+    case GEMM_MERGE:  return launch_dense<PV_GEMM_CFG_N1K, A_MERGE, B_ONE, E_STORE>(g, s);
+    case GEMM_PLAIN:  return launch_dense<PV_GEMM_CFG_N1K, A_DENSE, B_ONE, E_STORE>(g, s);
+    case GEMM_MERGE_F32: return launch_dense<PV_GEMM_CFG_N1K, A_MERGE, B_ONE, E_STORE_F32>(g, s);
   }
   return hipErrorInvalidValue;
 }

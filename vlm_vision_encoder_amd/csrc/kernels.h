@@ -69,5 +69,13 @@ hipError_t export_maps(const ImageMeta* meta, const int32_t* rowinfo, int n_imag
 
 // fp32 -> bf16 copy (no-merge output of the bf16 path).
 hipError_t f32_to_bf16(const float* x, void* y, size_t n, hipStream_t s);
+// Operand preparation (bf16 hi | lo halves of fp32 A operands):
+//   im2col_split: out [N][2 Kp] = im2col(pixels) as hi | lo, k >= K zero
+//   split_rows:   out [rows][2 D] = x as hi | lo
+//   pad_rows:     out [rows][Kp] = w [rows][K] zero-padded (bf16)
+hipError_t im2col_split(const float* pixels, const DevMaps& maps, void* out, int n_patches, int K, int Kp,
+                        hipStream_t s);
+hipError_t split_rows(const float* x, void* out, int rows, int D, hipStream_t s);
+hipError_t pad_rows(const void* w, void* out, int rows, int K, int Kp, hipStream_t s);
 
 }  // namespace pv

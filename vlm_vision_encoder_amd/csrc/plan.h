@@ -43,10 +43,14 @@ struct PlanParams {
   int32_t rope_pairs = 16;  // rotation pairs per axis (head_dim / 4)
 };
 
+// K of the patch embedding's bf16 GEMM: 3 p^2 zero-padded to a multiple of 64.
+inline int32_t patch_kp(int32_t patch) { return (3 * patch * patch + 63) / 64 * 64; }
+
 // Byte offsets into the device workspace (all 256-byte aligned).
 struct Layout {
   size_t meta = 0, items = 0, rope = 0, rowinfo = 0, msrc = 0;
   size_t r = 0, y = 0, big = 0;
+  size_t wpad = 0;          // bf16 tower: patch weights zero-padded to [D][Kp]
   size_t upload_bytes = 0;  // [0, upload_bytes) is filled by one host->device copy
   size_t total = 0;
 };

@@ -1,0 +1,118 @@
+// Operand preparation for the bf16 GEMMs whose A operand carries fp32
+// values: each such value x goes to the MFMAs as two bf16 numbers, hi =
+// bf16(x) and lo = bf16(x - hi), placed in two halves of the K range (row =
+// [hi | lo]) that meet the same weights.  HBM-bound passes: 4 bytes read and
+// 4 bytes written per value.
+//   im2col_split: the patch embedding's A ("Mistral 3" (KerasFormers),
+//                 Mistral3VisionModel: the convolution with stride = kernel =
+//                 patch size, i.e. one GEMM row per patch), K order
+//                 (channel, row, column) of the conv weight, zero-padded to Kp.
+//   split_rows:   the final residual, which the merger's A-operand loads then
+//                 gather 2x2 straight from this copy.
+//   pad_rows:     copy of a bf16 matrix with its rows zero-padded (patch
+//                 weights [D][3p^2] -> [D][Kp]).
+#include "common.h"
+#include "kernels.h"
+
+namespace pv {
+
+namespace {
+
+__device__ __forceinline__ void split8(const float (&f)[8], u32x4& hi, u32x4& lo) {
+  float r[8];
+  hi = pack8(f);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[2 * e] = f[2 * e] - lo_bf16(hi[e]);
+    r[2 * e + 1] = f[2 * e + 1] - hi_bf16(hi[e]);
+  }
+  lo = pack8(r);
+}
+
+// One thread per (patch g, 8 consecutive k).
+__global__ __launch_bounds__(256) void im2col_split_kernel(const float* __restrict__ pixels, DevMaps maps,
+                                                           uint16_t* __restrict__ out, int n_patches, int K, int Kp) {
+  const int chunks = Kp / 8;
+  const long long idx = blockIdx.x * 256ll + threadIdx.x;
+  if (idx >= (long long)n_patches * chunks) return;
+  const int g = int(idx / chunks), k0 = int(idx - (long long)g * chunks) * 8;
+  const int img = maps.rowinfo[2 * g], rc = maps.rowinfo[2 * g + 1];
+  const ImageMeta mt = maps.meta[img];
+  const int p = maps.patch, pp = p * p;
+  const int pr = rc >> 16, pc = rc & 0xffff;
+  const float* base = pixels + pix_offset(mt) + size_t(pr * p) * mt.W + pc * p;
+  const size_t plane = size_t(mt.H) * mt.W;
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int k = k0 + e;
+    float v = 0.f;
+    if (k < K) {
+      const int ch = k / pp, rem = k - ch * pp;
+      const int u = rem / p, x = rem - u * p;
+      v = base[size_t(ch) * plane + size_t(u) * mt.W + x];
+    }
+    f[e] = v;
+  }
+  u32x4 hi, lo;
+  split8(f, hi, lo);
+  uint16_t* row = out + size_t(g) * 2 * Kp;
+  *reinterpret_cast<u32x4*>(row + k0) = hi;
+  *reinterpret_cast<u32x4*>(row + Kp + k0) = lo;
+}
+
+// One thread per 8 consecutive values of a row.
+__global__ __launch_bounds__(256) void split_rows_kernel(const float* __restrict__ x, uint16_t* __restrict__ out,
+                                                         int rows, int D) {
+  const int chunks = D / 8;
+  const long long idx = blockIdx.x * 256ll + threadIdx.x;
+  if (idx >= (long long)rows * chunks) return;
+  const int r = int(idx / chunks), c0 = int(idx - (long long)r * chunks) * 8;
+  const floatx4* src = reinterpret_cast<const floatx4*>(x + size_t(r) * D + c0);
+  const floatx4 a = src[0], b = src[1];
+  const float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  u32x4 hi, lo;
+  split8(f, hi, lo);
+  uint16_t* row = out + size_t(r) * 2 * D;
+  *reinterpret_cast<u32x4*>(row + c0) = hi;
+  *reinterpret_cast<u32x4*>(row + D + c0) = lo;
+}
+
+__global__ __launch_bounds__(256) void pad_rows_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ out,
+                                                       int rows, int K, int Kp) {
+  const long long idx = blockIdx.x * 256ll + threadIdx.x;
+  if (idx >= (long long)rows * Kp) return;
+  const int r = int(idx / Kp), k = int(idx - (long long)r * Kp);
+  out[idx] = k < K ? w[size_t(r) * K + k] : uint16_t(0);
+}
+
+inline dim3 grid_for(long long threads) { return dim3(unsigned((threads + 255) / 256)); }
+
+}  // namespace
+
+hipError_t im2col_split(const float* pixels, const DevMaps& maps, void* out, int n_patches, int K, int Kp,
+                        hipStream_t s) {
+  if (n_patches <= 0) return hipSuccess;
+  if (Kp % 8 || K > Kp) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(im2col_split_kernel, grid_for((long long)n_patches * (Kp / 8)), dim3(256), 0, s, pixels, maps,
+                     static_cast<uint16_t*>(out), n_patches, K, Kp);
+  return hipGetLastError();
+}
+
+hipError_t split_rows(const float* x, void* out, int rows, int D, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (D % 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(split_rows_kernel, grid_for((long long)rows * (D / 8)), dim3(256), 0, s, x,
+                     static_cast<uint16_t*>(out), rows, D);
+  return hipGetLastError();
+}
+
+hipError_t pad_rows(const void* w, void* out, int rows, int K, int Kp, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (K > Kp) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pad_rows_kernel, grid_for((long long)rows * Kp), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(w), static_cast<uint16_t*>(out), rows, K, Kp);
+  return hipGetLastError();
+}
+
+}  // namespace pv

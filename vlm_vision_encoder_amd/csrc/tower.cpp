@@ -187,7 +187,19 @@ pv_status run_tower(pv_tower* t, const float* pixels, const pv::Plan& plan, void
   g.heads = c.heads;
 
   // ---- patch embedding: X = im2col(pixels) W^T, fp32 into the residual buffer
-  {
+  if (bf) {
+    // pixels as bf16 hi | lo rows of im2col, against weights padded to Kp
+    const int Kpatch = 3 * c.patch * c.patch, Kp = pv::patch_kp(c.patch);
+    void* wpad = ws + L.wpad;
+    PV_LAUNCH(PV_K_PATCH, pv::pad_rows(t->w.patch_w, wpad, D, Kpatch, Kp, s));
+    PV_LAUNCH(PV_K_PATCH, pv::im2col_split(pixels, g.maps, big, N, Kpatch, Kp, s));
+    pv::GemmArgs a = g;
+    a.M = N; a.N = D; a.K = 2 * Kp; a.kb = Kp;
+    a.A = big; a.lda = 2 * Kp;
+    a.B0 = wpad; a.ldb = Kp;
+    a.C = r; a.ldc = D;
+    PV_LAUNCH(PV_K_PATCH, gemm(pv::GEMM_PATCH, a));
+  } else {
     pv::GemmArgs a = g;
     a.M = N; a.N = D; a.K = 3 * c.patch * c.patch;
     a.pixels = pixels;
@@ -267,13 +279,23 @@ pv_status run_tower(pv_tower* t, const float* pixels, const pv::Plan& plan, void
   if (st.stage >= 0) return fail(PV_ERR_ARG, "stage/layer not reached");
 
   const bool out_bf16 = bf && c.out_dtype == PV_BF16;
-  if (c.merge == 2) {
+  if (c.merge == 2 && bf) {
+    // the final residual as bf16 hi | lo rows; the merger's A loads gather
+    // the 2x2 groups from that copy
+    PV_LAUNCH(PV_K_MERGE, pv::split_rows(r, big, N, D, s));
+    pv::GemmArgs a = g;
+    a.M = int(plan.out_rows); a.N = c.out_dim; a.K = 8 * D; a.kb = 4 * D;
+    a.A = big; a.lda = 2 * D;
+    a.B0 = t->w.merge_w; a.ldb = 4 * D;
+    a.C = out; a.ldc = c.out_dim;
+    PV_LAUNCH(PV_K_MERGE, gemm(out_bf16 ? pv::GEMM_MERGE : pv::GEMM_MERGE_F32, a));
+  } else if (c.merge == 2) {
     pv::GemmArgs a = g;
     a.M = int(plan.out_rows); a.N = c.out_dim; a.K = 4 * D;
     a.A = r; a.lda = D;
     a.B0 = t->w.merge_w; a.ldb = 4 * D;
     a.C = out; a.ldc = c.out_dim;
-    PV_LAUNCH(PV_K_MERGE, gemm(out_bf16 ? pv::GEMM_MERGE : pv::GEMM_MERGE_F32, a));
+    PV_LAUNCH(PV_K_MERGE, gemm(pv::GEMM_MERGE_F32, a));
   } else if (out_bf16) {
     PV_LAUNCH(PV_K_MERGE, pv::f32_to_bf16(r, out, size_t(N) * D, s));
   } else {
