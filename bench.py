@@ -101,6 +101,81 @@ def cpu_baseline(wl, weights, pixels):
     }
 
 
+def copy_probe(mib):
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 5}), flush=True)
+
+
+KERNEL_MATCH = {"attn": ("attn_bf16_kernel", "attn_bf16.hip")}
+
+
+def pmc_summary(args):
+    """Writes profiles/traffic_<class>_<workload>.json from rocprofv3 --pmc CSV
+    outputs (FETCH_SIZE and WRITE_SIZE, KiB per dispatch) of the tower kernel
+    and of the copy probe: bytes = counter KiB * 1024 * (known copy bytes /
+    the copy probe's counter bytes)."""
+    import csv
+    import statistics
+
+    def per_dispatch(path, needle):
+        with open(path) as f:
+            vals = [float(r["Counter_Value"]) for r in csv.DictReader(f) if needle in r["Kernel_Name"]]
+        if not vals:
+            raise SystemExit(f"no dispatch of {needle} in {path}")
+        return statistics.mean(vals), len(vals)
+
+    kcls, wname = args.pmc_summary
+    needle, src = KERNEL_MATCH[kcls]
+    copy_bytes = args.copy_probe_mib * (1 << 20)
+    f_kib, nf = per_dispatch(args.pmc_fetch, needle)
+    w_kib, nw = per_dispatch(args.pmc_write, needle)
+    cf_kib, _ = per_dispatch(args.pmc_copy_fetch, "MulFunctor")
+    cw_kib, _ = per_dispatch(args.pmc_copy_write, "MulFunctor")
+    f_scale, w_scale = copy_bytes / (cf_kib * 1024), copy_bytes / (cw_kib * 1024)
+    fetch_b, write_b = f_kib * 1024 * f_scale, w_kib * 1024 * w_scale
+    out = {"kernel": needle, "workload": wname, "source": src,
+           "source_sha256": source_sha256(os.path.join(ROOT, "vlm_vision_encoder_amd", "csrc", src)),
+           "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
+           "copy_probe_bytes": copy_bytes, "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "hbm_fetch_bytes_per_dispatch": fetch_b, "hbm_write_bytes_per_dispatch": write_b,
+           "hbm_bytes_per_dispatch": fetch_b + write_b}
+    path = os.path.join(ROOT, "profiles", f"traffic_{kcls}_{wname}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
+def source_sha256(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel_class, wl, launches_per_step):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by what
+    the same counter reads for a copy kernel of known size), or None when no
+    summary exists for this kernel and workload or the kernel's source has
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_class}_{wl.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    src = os.path.join(ROOT, "vlm_vision_encoder_amd", "csrc", t["source"])
+    if source_sha256(src) != t["source_sha256"]:
+        return None
+    return float(t["hbm_bytes_per_dispatch"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,7 +184,23 @@ def main():
     ap.add_argument("--workload", default="ms31_1540")
     ap.add_argument("--profile-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain fp32 copy kernel (y = x * 1) over MIB MiB, 5 times, and exit: the "
+                         "reference for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("CLASS", "WORKLOAD"),
+                    help="write profiles/traffic_CLASS_WORKLOAD.json from the four CSVs below and exit")
+    ap.add_argument("--pmc-fetch")
+    ap.add_argument("--pmc-write")
+    ap.add_argument("--pmc-copy-fetch")
+    ap.add_argument("--pmc-copy-write")
+    ap.add_argument("--copy-probe-mib", type=int, default=512)
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the tower runs on a single MI355X here "
               f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
@@ -189,7 +280,8 @@ def main():
         dom_flops_launch = fl[dom] / kernels[dom]["launches_per_step"]
         achieved = dom_flops_launch / (dom_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                    "traffic": measured_traffic(dom, wl, kernels[dom]["launches_per_step"]),
                     "flops_per_launch": dom_flops_launch, "avg_launch_ms": dom_ms}
 
     patches_s = wl.n_patches / (ms_step * 1e-3)
