@@ -215,6 +215,18 @@ def test_bf16_no_merge_patch16_single_patch_image():
     check("out", to_np(out), ref["out"], TOL["bf16"], stored_bf16=True)
 
 
+def test_bf16_merger_width_not_multiple_of_256():
+    """Merger output width 384 (a multiple of 128 only): the merger GEMM takes
+    its 256 x 128 tiles instead of 256 x 256."""
+    wl = _bf16_small([(224, 224), (56, 112)], 1, out_dim=384)
+    say(f"bf16 merger width 384 {wl.image_hw}")
+    c = Case(wl)
+    ref = c.ref()
+    out = c.run()
+    assert tuple(out.shape) == (wl.out_rows, 384)
+    check("out", to_np(out), ref["out"], TOL["bf16"], stored_bf16=True)
+
+
 def test_bf16_sharp_logits():
     """Logit std ~4 instead of ~0.4.  bf16 storage of q and k moves every
     logit s by up to about 2^-8 |s| (two half-ulp roundings), which moves the

@@ -271,7 +271,8 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 // gather): the loads fetch straight from the [rows][2D] hi | lo copy of the
 // residual, K = 8D = (hi: 4 gathered rows) | (lo: the same 4 rows).
 template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int AMD, int BMD, int EM>
-__global__ __launch_bounds__(WMW * WNW * 64) void gemm_dense_kernel(GemmArgs g) {
+__global__ __launch_bounds__(WMW * WNW * 64) __attribute__((amdgpu_waves_per_eu(WMW * WNW >= 8 ? 2 : 8 / (WMW * WNW))))
+void gemm_dense_kernel(GemmArgs g) {
   static_assert(AMD == A_DENSE || AMD == A_MERGE, "A operand mode");
   constexpr int NW = WMW * WNW, NT = NW * 64;
   constexpr int CH = BKT / 8;                    // 16-byte chunks per tile row
@@ -522,6 +523,18 @@ hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
 #ifndef PV_GEMM_CFG_N1K
 #define PV_GEMM_CFG_N1K 256, 128, 4, 2, 2, 64
 #endif
+// N = hidden products with an fp32 output (out-projection, down, patch
+// embedding): 128 x 128 tiles, 4 waves, two workgroups per CU -- at 1540^2
+// the 760 tiles spread over 512 slots instead of 384 over 256 (measured
+// 11% faster on down than 256 x 128)
+#ifndef PV_GEMM_CFG_RES
+#define PV_GEMM_CFG_RES 128, 128, 2, 2, 2, 64
+#endif
+// merger (a few thousand rows, N = 5120): 256 x 256 tiles, one round of
+// 240 tiles at 1540^2; 256 x 128 when N is not a multiple of 256
+#ifndef PV_GEMM_CFG_MERGE
+#define PV_GEMM_CFG_MERGE PV_GEMM_CFG_BIG
+#endif
 // q,k,v: 192-column tiles (16 per row of tiles instead of 12) balance the
 // 1540 x 1540 image's 48 rows of tiles evenly over the 256 CUs
 #ifndef PV_GEMM_CFG_QKV
@@ -531,14 +544,18 @@ hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
 hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
   switch (kind) {
-    case GEMM_PATCH:  return launch_dense<PV_GEMM_CFG_N1K, A_DENSE, B_ONE, E_STORE_F32>(g, s);
+    case GEMM_PATCH:  return launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_STORE_F32>(g, s);
     case GEMM_QKV:    return launch_dense<PV_GEMM_CFG_QKV, A_DENSE, B_QKV, E_QKV_ROPE>(g, s);
-    case GEMM_OPROJ:  return launch_dense<PV_GEMM_CFG_N1K, A_DENSE, B_ONE, E_ADD_F32>(g, s);
+    case GEMM_OPROJ:  return launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_ADD_F32>(g, s);
     case GEMM_GATEUP: return launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL>(g, s);
-    case GEMM_DOWN:   return launch_dense<PV_GEMM_CFG_N1K, A_DENSE, B_ONE, E_ADD_F32>(g, s);
-    case GEMM_MERGE:  return launch_dense<PV_GEMM_CFG_N1K, A_MERGE, B_ONE, E_STORE>(g, s);
+    case GEMM_DOWN:   return launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_ADD_F32>(g, s);
+    case GEMM_MERGE:
+      return g.N % 256 == 0 ? launch_dense<PV_GEMM_CFG_MERGE, A_MERGE, B_ONE, E_STORE>(g, s)
+                            : launch_dense<PV_GEMM_CFG_N1K, A_MERGE, B_ONE, E_STORE>(g, s);
     case GEMM_PLAIN:  return launch_dense<PV_GEMM_CFG_N1K, A_DENSE, B_ONE, E_STORE>(g, s);
-    case GEMM_MERGE_F32: return launch_dense<PV_GEMM_CFG_N1K, A_MERGE, B_ONE, E_STORE_F32>(g, s);
+    case GEMM_MERGE_F32:
+      return g.N % 256 == 0 ? launch_dense<PV_GEMM_CFG_MERGE, A_MERGE, B_ONE, E_STORE_F32>(g, s)
+                            : launch_dense<PV_GEMM_CFG_N1K, A_MERGE, B_ONE, E_STORE_F32>(g, s);
   }
   return hipErrorInvalidValue;
 }
