@@ -96,6 +96,15 @@ struct GemmArgs {
   const void* B2;
   int32_t ldb;
   int32_t kb;         // K extent of B when A's K repeats it (hi | lo halves of A), else 0
+  // fp8 low-part correction (gate/up): after the bf16 K range, k8 more k of
+  // A8 [M][k8] x B8 [N][k8] (fp8 e4m3 with one power-of-two scale per 32 k,
+  // scale bytes in step-major blocks As [k8/128][as_rows][4], Bs
+  // [k8/128][bs_rows][4]); k8 = 0: none
+  const void* A8;
+  const void* B8;
+  const void* As;
+  const void* Bs;
+  int32_t k8, as_rows, bs_rows;
   void* C;
   int32_t ldc;
   int32_t hidden;     // D (QKV split, merge gather)

@@ -34,6 +34,13 @@ constexpr int kNumCUs = 256;  // MI355X: 8 XCDs x 32 CUs
 #define PV_GEMM_SCHED 1
 #endif
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// two 16-byte LDS chunks -> the 32-byte fp8 operand of a 32x32x64 MFMA
+__device__ __forceinline__ i32x8 join8(const u32x4& x, const u32x4& y) {
+  return i32x8{int(x[0]), int(x[1]), int(x[2]), int(x[3]), int(y[0]), int(y[1]), int(y[2]), int(y[3])};
+}
+
 template <int N, typename F, int I = 0>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
@@ -270,7 +277,15 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 // is the concatenation of four residual rows msrc[t][0..3] (2x2 patch
 // gather): the loads fetch straight from the [rows][2D] hi | lo copy of the
 // residual, K = 8D = (hi: 4 gathered rows) | (lo: the same 4 rows).
-template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int AMD, int BMD, int EM>
+// LO8: after the bf16 k-steps, k8 / 128 more steps multiply the fp8 low part
+// of A with an fp8 copy of B (v_mfma_scale_f32_32x32x64_f8f6f4, one scale
+// byte per 32 k on each side) into the same accumulators.  A step then moves
+// 128 fp8 k: the same 128-byte tile rows and chunk swizzle as a bf16 step,
+// plus 1 KB of A and 1 KB of B scale bytes behind the tiles.  In the MFMA
+// operand, lane l (half h = l / 32) holds row l % 32, k [16h, 16h + 16) and
+// [32 + 16h, 32 + 16h + 16) of the 64, and supplies the scale of its row's
+// 32-k block h (byte 0 of its scale operand).
+template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int AMD, int BMD, int EM, bool LO8 = false>
 __global__ __launch_bounds__(WMW * WNW * 64) __attribute__((amdgpu_waves_per_eu(WMW * WNW >= 8 ? 2 : 8 / (WMW * WNW))))
 void gemm_dense_kernel(GemmArgs g) {
   static_assert(AMD == A_DENSE || AMD == A_MERGE, "A operand mode");
@@ -282,9 +297,13 @@ void gemm_dense_kernel(GemmArgs g) {
   constexpr int LDT = A_LD + B_LD;
   static_assert(A_LD >= 1 && B_LD >= 1 && (BM * CH) % NT == 0 && (BN * CH) % NT == 0, "tile/thread mismatch");
   static_assert(EM != E_SILU_MUL || (TN % 2) == 0, "silu-mul needs gate/up block pairs in a wave");
-  static_assert((NS - 2) * LDT <= 63, "vmcnt range");
+  static_assert((NS - 2) * (LDT + 1) <= 63, "vmcnt range");
+  static_assert(!LO8 || (BM == 256 && BN == 256 && BKT == 64 && NS == 2 && AMD == A_DENSE && NW >= 2),
+                "fp8 low part: 256 x 256 tiles, 64-k bf16 steps");
 
-  __shared__ u32x4 lds[NS][(BM + BN) * CH];
+  // LO8: 2 KB of scale bytes behind each stage's tiles
+  constexpr int kStageU4 = (BM + BN) * CH + (LO8 ? 128 : 0);
+  __shared__ u32x4 lds[NS][kStageU4];
   constexpr int kScratchFloats = (BM + BN) * CH * 4 / NW;  // per-wave slice of one stage
   constexpr int kEpiRows = kScratchFloats >= 32 * 32 ? 32 : 16;
   static_assert(kScratchFloats >= 16 * 32 && kScratchFloats >= 32 * 20 && (EM != E_QKV_ROPE || kScratchFloats >= 32 * 32),
@@ -298,9 +317,10 @@ void gemm_dense_kernel(GemmArgs g) {
   const int tiles_n = (BMD == B_GATEUP ? 2 * g.N : g.N) / BN;
   const int tiles_m = (g.M + BM - 1) / BM;
   const int ntiles = tiles_m * tiles_n;
-  const int KT = g.K / BKT;
+  const int KT16 = g.K / BKT;                  // bf16 k-steps per tile
+  const int KT = KT16 + (LO8 ? g.k8 / 128 : 0);  // all k-steps per tile
   // k-tiles of B: A's K may run over B's K twice (hi | lo halves of A)
-  const int KTB = g.kb > 0 ? g.kb / BKT : KT;
+  const int KTB = g.kb > 0 ? g.kb / BKT : KT16;
 
   // this workgroup's tiles: the blocks b with equal x = b % 8 (one XCD, nx
   // of them populated) own tiles [lo_x, hi_x); the nb_x blocks of XCD x
@@ -331,9 +351,12 @@ void gemm_dense_kernel(GemmArgs g) {
   const char* gb[B_LD];
   int4 msrc4[AMD == A_MERGE ? A_LD : 1];  // A_MERGE: source rows of each load slot's row
   int a_gc[AMD == A_MERGE ? A_LD : 1];    // A_MERGE: chunk each load slot fetches
+  int is_tm = 0, is_tn = 0;               // tile of the steps being issued
   auto set_rows = [&](int t) {
     int tm, tn;
     tile_mn(t, tm, tn);
+    is_tm = tm;
+    is_tn = tn;
 #pragma unroll
     for (int q = 0; q < A_LD; ++q) {
       const int p = (wave * A_LD + q) * 64 + lane;
@@ -354,6 +377,23 @@ void gemm_dense_kernel(GemmArgs g) {
       gb[q] = b_row<BMD>(g, tn * BN + P) + gc * 16;
     }
   };
+  // LO8: row pointers of the fp8 operands (128-byte rows of k8 bytes)
+  auto set_rows8 = [&]() {
+#pragma unroll
+    for (int q = 0; q < A_LD; ++q) {
+      const int p = (wave * A_LD + q) * 64 + lane;
+      const int P = p / CH, gc = (p % CH) ^ swzc<CH>(P);
+      int m = is_tm * BM + P;
+      m = m < g.M ? m : g.M - 1;
+      ga[q] = reinterpret_cast<const char*>(g.A8) + size_t(m) * g.k8 + gc * 16;
+    }
+#pragma unroll
+    for (int q = 0; q < B_LD; ++q) {
+      const int p = (wave * B_LD + q) * 64 + lane;
+      const int P = p / CH, gc = (p % CH) ^ swzc<CH>(P);
+      gb[q] = reinterpret_cast<const char*>(g.B8) + size_t(is_tn * BN + P) * g.k8 + gc * 16;
+    }
+  };
   // (the global source is passed as a uint16_t pointer: with a char pointer
   // the host pass drops the kernel's launch stub without a diagnostic)
   int is_step = 0, is_kt = 0, is_tile = 0;  // next step to issue
@@ -363,6 +403,36 @@ void gemm_dense_kernel(GemmArgs g) {
   auto issue_next = [&]() {
     if (is_kt == 0) set_rows(tile_of(is_tile));
     const int st = is_step % NS;
+    if constexpr (LO8) {
+      if (is_kt >= KT16) {
+        const int s8 = is_kt - KT16;
+        if (s8 == 0) set_rows8();
+        const size_t koff8 = size_t(s8) * 128;
+#pragma unroll
+        for (int q = 0; q < A_LD; ++q)
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(ga[q] + koff8),
+                                           (lds_void*)&lds[st][(wave * A_LD + q) * 64], 16, 0, 0);
+#pragma unroll
+        for (int q = 0; q < B_LD; ++q)
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(gb[q] + koff8),
+                                           (lds_void*)&lds[st][BM * CH + (wave * B_LD + q) * 64], 16, 0, 0);
+        // scale bytes of the tile's 256 rows for this step: 1 KB each, A by
+        // wave 0 and B by wave 1 (rows past M read padding rows)
+        if (wave < 2) {
+          const char* src = wave == 0
+              ? reinterpret_cast<const char*>(g.As) + (size_t(s8) * g.as_rows + is_tm * BM) * 4 + lane * 16
+              : reinterpret_cast<const char*>(g.Bs) + (size_t(s8) * g.bs_rows + is_tn * BN) * 4 + lane * 16;
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(src),
+                                           (lds_void*)&lds[st][(BM + BN) * CH + wave * 64], 16, 0, 0);
+        }
+        ++is_step;
+        if (++is_kt == KT) {
+          is_kt = 0;
+          ++is_tile;
+        }
+        return;
+      }
+    }
     size_t koff = size_t(is_kt) * BKT * 2;
     if constexpr (AMD == A_MERGE) {
       const int seg = is_kt / KTQ, kin = is_kt - seg * KTQ;
@@ -405,31 +475,23 @@ void gemm_dense_kernel(GemmArgs g) {
   for (int st = 0; st < NS - 1; ++st)
     if (is_step < steps) issue_next();
 
-  int kt = 0, ti = 0;
-  for (int step = 0; step < steps; ++step) {
-    // step has landed once at most (steps issued after it) x LDT loads of
-    // this thread are outstanding; the barrier makes every thread's part
-    // visible and frees the stage read in the previous step
+  // step has landed once at most (steps issued after it) x (loads per step)
+  // of this thread are outstanding; the barrier makes every thread's part
+  // visible and frees the stage read in the previous step
+  auto begin_step = [&](int step) {
     if (step + NS - 2 < steps) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LDT));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * (LO8 ? LDT + 1 : LDT)));
     } else {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
     __syncthreads();
     if (is_step < steps) issue_next();
-    // the residual of an accumulating epilogue is fetched while the tile's
-    // last k-step runs
-    Residual<TM, TN> res;
-    if constexpr (EM == E_ADD_F32) {
-      if (kt == KT - 1) {
-        int tm, tn;
-        tile_mn(tile_of(ti), tm, tn);
-        load_residual<TM, TN>(g, res, tm * BM + wm * TMW, tn * BN + wn * TNW, lane);
-      }
-    }
-    const u32x4* sa = lds[step % NS];
-    const u32x4* sb = lds[step % NS] + BM * CH;
-    // fragments of k-substep ks + 1 are read while the MFMAs of ks run
+  };
+  // one bf16 k-step: fragments of k-substep ks + 1 are read while the MFMAs
+  // of ks run
+  auto compute_bf16 = [&](int stage) {
+    const u32x4* sa = lds[stage];
+    const u32x4* sb = lds[stage] + BM * CH;
     constexpr int KS = BKT / 16;
     u32x4 fa[2][TM], fb[2][TN];
     auto read_frags = [&](int ks, u32x4 (&ra)[TM], u32x4 (&rb)[TN]) {
@@ -473,42 +535,92 @@ void gemm_dense_kernel(GemmArgs g) {
       }
     });
 #endif
-    if (++kt == KT) {
-      int tm, tn;
-      tile_mn(tile_of(ti), tm, tn);
-      // the stage just consumed is free until the next step's loads (issued
-      // after the next barrier): once every wave is done with it, each wave
-      // uses its own slice of it to stage the output
-      __syncthreads();
-      float* scratch = reinterpret_cast<float*>(lds[step % NS]) + wave * kScratchFloats;
-      epilogue_lds<EM, TM, TN, kEpiRows>(g, acc, tm * BM + wm * TMW, tn * BN + wn * TNW, lane, scratch,
-                                         EM == E_ADD_F32 ? &res : nullptr);
+  };
+  // one fp8 k-step (LO8): two 64-k scaled MFMAs; scale words: one dword per
+  // tile row, byte b = 32-k block b of the step
+  auto compute_fp8 = [&](int stage) {
+    const u32x4* sa = lds[stage];
+    const u32x4* sb = lds[stage] + BM * CH;
+    const uint32_t* scl = reinterpret_cast<const uint32_t*>(lds[stage] + (BM + BN) * CH);
+    uint32_t sa_w[TM], sb_w[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i) sa_w[i] = scl[wm * TMW + 32 * i + lrow];
 #pragma unroll
-        for (int jn = 0; jn < TN; ++jn)
+    for (int jn = 0; jn < TN; ++jn) sb_w[jn] = scl[BM + wn * TNW + 32 * jn + lrow];
+    static_for<2>([&](auto ks_c) {
+      constexpr int ks = decltype(ks_c)::value;
+      const int c0 = 4 * ks + lhalf, c1 = c0 + 2;
+      // all A fragments held, B fragments streamed one at a time
+      i32x8 fa8[TM];
 #pragma unroll
-          for (int v = 0; v < 16; ++v) acc[i][jn][v] = 0.f;
-      kt = 0;
-      ++ti;
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * TMW + 32 * i + lrow;
+        fa8[i] = join8(sa[row * CH + (c0 ^ swzc<CH>(row))], sa[row * CH + (c1 ^ swzc<CH>(row))]);
+      }
+      const int sh = 8 * (2 * ks + lhalf);
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn) {
+        const int row = wn * TNW + 32 * jn + lrow;
+        const i32x8 fb8 = join8(sb[row * CH + (c0 ^ swzc<CH>(row))], sb[row * CH + (c1 ^ swzc<CH>(row))]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          acc[i][jn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa8[i], fb8, acc[i][jn], 0, 0, 0,
+                                                                       int(sa_w[i] >> sh), 0, int(sb_w[jn] >> sh));
+      }
+    });
+  };
+
+  int step = 0;
+  for (int ti = 0; ti < my_tiles; ++ti) {
+    int tm, tn;
+    tile_mn(tile_of(ti), tm, tn);
+    Residual<TM, TN> res;
+    for (int kt = 0; kt < KT16; ++kt, ++step) {
+      begin_step(step);
+      // the residual of an accumulating epilogue is fetched while the
+      // tile's last k-step runs
+      if constexpr (EM == E_ADD_F32) {
+        if (kt == KT16 - 1) load_residual<TM, TN>(g, res, tm * BM + wm * TMW, tn * BN + wn * TNW, lane);
+      }
+      compute_bf16(step % NS);
     }
+    if constexpr (LO8) {
+      for (int kt = KT16; kt < KT; ++kt, ++step) {
+        begin_step(step);
+        compute_fp8(step % NS);
+      }
+    }
+    // the stage just consumed is free until the next step's loads (issued
+    // after the next barrier): once every wave is done with it, each wave
+    // uses its own slice of it to stage the output
+    __syncthreads();
+    float* scratch = reinterpret_cast<float*>(lds[(step - 1) % NS]) + wave * kScratchFloats;
+    epilogue_lds<EM, TM, TN, kEpiRows>(g, acc, tm * BM + wm * TMW, tn * BN + wn * TNW, lane, scratch,
+                                       EM == E_ADD_F32 ? &res : nullptr);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][jn][v] = 0.f;
   }
 }
 
-template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int AMD, int BMD, int EM>
+template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int AMD, int BMD, int EM, bool LO8 = false>
 hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
   const int ncols = (BMD == B_GATEUP) ? 2 * g.N : g.N;
   if (ncols % BN || g.K % BKT || g.kb % BKT) return hipErrorInvalidValue;
   if (g.kb > 0 && g.K != 2 * g.kb) return hipErrorInvalidValue;
   if (AMD == A_MERGE && (g.hidden % BKT || g.K != 8 * g.hidden || g.kb != 4 * g.hidden)) return hipErrorInvalidValue;
+  if (LO8 && (g.k8 <= 0 || g.k8 % 128 || g.kb != 0 || g.as_rows < ((g.M + BM - 1) / BM) * BM)) return hipErrorInvalidValue;
   const int tiles = ((g.M + BM - 1) / BM) * (ncols / BN);
   // as many workgroups as fit on the chip at once: the LDS ring sets how
   // many a CU holds
-  constexpr int kLdsBytes = NS * (BM + BN) * BKT * 2;
+  constexpr int kLdsBytes = NS * ((BM + BN) * BKT * 2 + (LO8 ? 2048 : 0));
   constexpr int kPerCU = (160 * 1024) / kLdsBytes < 2 ? 1 : 2;
   const int grid = tiles < kNumCUs * kPerCU ? tiles : kNumCUs * kPerCU;
-  hipLaunchKernelGGL((gemm_dense_kernel<BM, BN, WMW, WNW, NS, BKT, AMD, BMD, EM>), dim3(grid), dim3(WMW * WNW * 64), 0,
-                     s, g);
+  hipLaunchKernelGGL((gemm_dense_kernel<BM, BN, WMW, WNW, NS, BKT, AMD, BMD, EM, LO8>), dim3(grid),
+                     dim3(WMW * WNW * 64), 0, s, g);
   return hipGetLastError();
 }
 
@@ -547,7 +659,9 @@ hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
     case GEMM_PATCH:  return launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_STORE_F32>(g, s);
     case GEMM_QKV:    return launch_dense<PV_GEMM_CFG_QKV, A_DENSE, B_QKV, E_QKV_ROPE>(g, s);
     case GEMM_OPROJ:  return launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_ADD_F32>(g, s);
-    case GEMM_GATEUP: return launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL>(g, s);
+    case GEMM_GATEUP:
+      return g.k8 > 0 ? launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL, true>(g, s)
+                      : launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL>(g, s);
     case GEMM_DOWN:   return launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_ADD_F32>(g, s);
     case GEMM_MERGE:
       return g.N % 256 == 0 ? launch_dense<PV_GEMM_CFG_MERGE, A_MERGE, B_ONE, E_STORE>(g, s)

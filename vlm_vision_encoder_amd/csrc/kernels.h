@@ -30,8 +30,11 @@ hipError_t gemm_f32(GemmKind kind, const GemmArgs& g, hipStream_t s);
 //   rmsnorm_dual: h = norm(x) * g1 written back in place (fp32), y = norm(h) * g2
 hipError_t rmsnorm(const float* x, const float* g, void* y, int rows, int D, float eps,
                    bool y_f32, hipStream_t s);
-// rmsnorm_split: y = norm(x) * g as [N][2D] bf16: hi | lo = bf16(y - hi)
-hipError_t rmsnorm_split(const float* x, const float* g, void* y, int rows, int D, float eps, hipStream_t s);
+// rmsnorm_hi_lo8: y = norm(x) * g as bf16 hi [N][D] plus the low part y - hi
+// as fp8 e4m3 [N][D] with a power-of-two scale byte per 32 columns, scale
+// bytes step-major: ys[(col / 128) * srows + row][(col / 32) % 4]
+hipError_t rmsnorm_hi_lo8(const float* x, const float* g, void* yh, void* y8, void* ys, int rows, int srows, int D,
+                          float eps, hipStream_t s);
 hipError_t rmsnorm_dual(float* x, const float* g1, const float* g2, void* y, int rows, int D,
                         float eps, bool y_f32, hipStream_t s);
 
@@ -77,5 +80,8 @@ hipError_t im2col_split(const float* pixels, const DevMaps& maps, void* out, int
                         hipStream_t s);
 hipError_t split_rows(const float* x, void* out, int rows, int D, hipStream_t s);
 hipError_t pad_rows(const void* w, void* out, int rows, int K, int Kp, hipStream_t s);
+//   gateup_fp8:   b8 [2F][D] fp8 e4m3 = the gate/up weights in the GEMM's
+//                 interleaved row order, bs [D/128][2F][4] scale bytes
+hipError_t gateup_fp8(const void* w_gate, const void* w_up, void* b8, void* bs, int F, int D, hipStream_t s);
 
 }  // namespace pv

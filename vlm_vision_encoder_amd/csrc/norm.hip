@@ -38,27 +38,32 @@ __device__ __forceinline__ void store_row(void* y, size_t row, int D, int lane, 
   }
 }
 
-// bf16 hi and lo = bf16(v - hi) of a row, stored as [hi (D) | lo (D)]: a
-// product over both halves carries about 16 significant bits of v.
-template <int NC>
-__device__ __forceinline__ void store_row_split(void* y, size_t row, int D, int lane, const floatx4 (&v)[NC]) {
-  uint16_t* yr = reinterpret_cast<uint16_t*>(y) + row * 2 * D;
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const size_t o = size_t(i * 64 + lane) * 4;
-    u32x2 hi, lo;
-    hi[0] = pack_bf16x2(v[i][0], v[i][1]);
-    hi[1] = pack_bf16x2(v[i][2], v[i][3]);
-    lo[0] = pack_bf16x2(v[i][0] - lo_bf16(hi[0]), v[i][1] - hi_bf16(hi[0]));
-    lo[1] = pack_bf16x2(v[i][2] - lo_bf16(hi[1]), v[i][3] - hi_bf16(hi[1]));
-    *reinterpret_cast<u32x2*>(yr + o) = hi;
-    *reinterpret_cast<u32x2*>(yr + D + o) = lo;
-  }
+// Power-of-two scale of a block of 32 values for fp8 e4m3 (max normal 448):
+// the exponent X = floor(log2(max|x|)) - 7 puts the block maximum in
+// [128, 256), clear of the top of the range.  Returns the E8M0 byte X + 127
+// and sets mul = 2^-X.
+__device__ __forceinline__ uint32_t mx_scale(float amax, float& mul) {
+  const int e = int((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xff);  // biased exponent of the max
+  int x = e - 127 - 7;
+  x = x < -120 ? -120 : (x > 120 ? 120 : x);
+  mul = __builtin_bit_cast(float, uint32_t(127 - x) << 23);
+  return uint32_t(x + 127);
 }
 
+// Four fp32 values -> four fp8 e4m3 bytes (round to nearest even).
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return uint32_t(r);
+}
+
+// The MLP input: y = norm(x) * g as bf16 hi [N][D], and its low part y - hi
+// as fp8 [N][D] with one scale byte per 32 values (blocks of 32 columns;
+// scale bytes step-major: ys[(col / 128) * srows + row][(col / 32) % 4]).
 template <int NC>
-__global__ __launch_bounds__(256) void rmsnorm_split_kernel(const float* __restrict__ x, const float* __restrict__ g,
-                                                            void* __restrict__ y, int rows, float eps) {
+__global__ __launch_bounds__(256) void rmsnorm_hi_lo8_kernel(const float* __restrict__ x, const float* __restrict__ g,
+                                                             uint16_t* __restrict__ yh, uint8_t* __restrict__ y8,
+                                                             uint8_t* __restrict__ ys, int rows, int srows, float eps) {
   constexpr int D = NC * 256;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -70,8 +75,28 @@ __global__ __launch_bounds__(256) void rmsnorm_split_kernel(const float* __restr
   for (int i = 0; i < NC; ++i) v[i] = xr[i * 64 + lane];
   const float inv = rsqrtf(sumsq<NC>(v) * (1.f / D) + eps);
 #pragma unroll
-  for (int i = 0; i < NC; ++i) v[i] = v[i] * inv * gr[i * 64 + lane];
-  store_row_split<NC>(y, row, D, lane, v);
+  for (int i = 0; i < NC; ++i) {
+    v[i] = v[i] * inv * gr[i * 64 + lane];
+    const int col = (i * 64 + lane) * 4;
+    u32x2 hi;
+    hi[0] = pack_bf16x2(v[i][0], v[i][1]);
+    hi[1] = pack_bf16x2(v[i][2], v[i][3]);
+    *reinterpret_cast<u32x2*>(yh + size_t(row) * D + col) = hi;
+    const float l0 = v[i][0] - lo_bf16(hi[0]), l1 = v[i][1] - hi_bf16(hi[0]);
+    const float l2 = v[i][2] - lo_bf16(hi[1]), l3 = v[i][3] - hi_bf16(hi[1]);
+    // block of 32 columns = 8 consecutive lanes
+    float amax = fmaxf(fmaxf(fabsf(l0), fabsf(l1)), fmaxf(fabsf(l2), fabsf(l3)));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+    float mul;
+    const uint32_t sbyte = mx_scale(amax, mul);
+    *reinterpret_cast<uint32_t*>(y8 + size_t(row) * D + col) = pack_fp8x4(l0 * mul, l1 * mul, l2 * mul, l3 * mul);
+    if ((lane & 7) == 0) {
+      const int blk = col / 32;
+      ys[(size_t(blk / 4) * srows + row) * 4 + (blk & 3)] = uint8_t(sbyte);
+    }
+  }
 }
 
 template <int NC, bool YF32>
@@ -145,13 +170,16 @@ hipError_t rmsnorm(const float* x, const float* g, void* y, int rows, int D, flo
   return hipErrorInvalidValue;
 }
 
-hipError_t rmsnorm_split(const float* x, const float* g, void* y, int rows, int D, float eps, hipStream_t s) {
+hipError_t rmsnorm_hi_lo8(const float* x, const float* g, void* yh, void* y8, void* ys, int rows, int srows, int D,
+                         float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (D % 128 || srows < rows) return hipErrorInvalidValue;
   const dim3 grid((rows + 3) / 4), block(256);
-#define PV_CASE(NC)                                                                       \
-  if (D == NC * 256) {                                                                    \
-    hipLaunchKernelGGL((rmsnorm_split_kernel<NC>), grid, block, 0, s, x, g, y, rows, eps); \
-    return hipGetLastError();                                                             \
+#define PV_CASE(NC)                                                                                    \
+  if (D == NC * 256) {                                                                                 \
+    hipLaunchKernelGGL((rmsnorm_hi_lo8_kernel<NC>), grid, block, 0, s, x, g, static_cast<uint16_t*>(yh), \
+                       static_cast<uint8_t*>(y8), static_cast<uint8_t*>(ys), rows, srows, eps);           \
+    return hipGetLastError();                                                                          \
   }
   PV_NORM_CASES(PV_CASE)
 #undef PV_CASE

@@ -92,14 +92,25 @@ int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, P
   const size_t N = size_t(patches), D = size_t(p.hidden);
   L.r = off;
   off = align256(off + N * D * 4);
-  L.y = off;  // bf16 tower: [N][2D] (the MLP input's hi | lo halves); fp32: [N][D]
-  off = align256(off + N * D * 4);
+  L.y = off;
+  off = align256(off + N * D * p.elem_bytes);
   L.big = off;  // also: im2col hi | lo [N][2 Kp] and the final residual's hi | lo [N][2D] (bf16 tower)
   size_t big_row = std::max(3 * D, size_t(p.mlp)) * p.elem_bytes;
   if (p.elem_bytes == 2) big_row = std::max(big_row, std::max(size_t(4) * patch_kp(p.patch), 4 * D));
   off = align256(off + N * big_row);
   L.wpad = off;
   off = align256(off + (p.elem_bytes == 2 ? D * size_t(patch_kp(p.patch)) * 2 : 0));
+  if (p.elem_bytes == 2) {
+    const size_t F2 = 2 * size_t(p.mlp);
+    L.a8 = off;
+    off = align256(off + N * D);
+    L.as = off;
+    off = align256(off + (D / 128) * size_t(a8_scale_rows(int64_t(N))) * 4);
+    L.b8 = off;
+    off = align256(off + F2 * D);
+    L.bs = off;
+    off = align256(off + (D / 128) * F2 * 4);
+  }
   L.total = off;
   return 0;
 }

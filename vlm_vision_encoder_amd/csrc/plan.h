@@ -43,6 +43,10 @@ struct PlanParams {
   int32_t rope_pairs = 16;  // rotation pairs per axis (head_dim / 4)
 };
 
+// Rows of the MLP input's fp8 scale blocks: the patches plus one tile of
+// padding (a GEMM tile reads the scale bytes of 256 consecutive rows).
+inline int64_t a8_scale_rows(int64_t patches) { return patches + 256; }
+
 // K of the patch embedding's bf16 GEMM: 3 p^2 zero-padded to a multiple of 64.
 inline int32_t patch_kp(int32_t patch) { return (3 * patch * patch + 63) / 64 * 64; }
 
@@ -51,6 +55,8 @@ struct Layout {
   size_t meta = 0, items = 0, rope = 0, rowinfo = 0, msrc = 0;
   size_t r = 0, y = 0, big = 0;
   size_t wpad = 0;          // bf16 tower: patch weights zero-padded to [D][Kp]
+  // bf16 tower, MLP input's fp8 low part and the gate/up weights in fp8:
+  size_t a8 = 0, as = 0, b8 = 0, bs = 0;
   size_t upload_bytes = 0;  // [0, upload_bytes) is filled by one host->device copy
   size_t total = 0;
 };

@@ -11,6 +11,9 @@
 //                 gather 2x2 straight from this copy.
 //   pad_rows:     copy of a bf16 matrix with its rows zero-padded (patch
 //                 weights [D][3p^2] -> [D][Kp]).
+//   gateup_fp8:   fp8 e4m3 copy of the gate/up weights in the GEMM's
+//                 interleaved row order, one power-of-two scale per 32 k, for
+//                 the fp8 product with the MLP input's low part.
 #include "common.h"
 #include "kernels.h"
 
@@ -86,6 +89,49 @@ __global__ __launch_bounds__(256) void pad_rows_kernel(const uint16_t* __restric
   out[idx] = k < K ? w[size_t(r) * K + k] : uint16_t(0);
 }
 
+// One thread per (row n of the interleaved gate/up matrix, block of 32 k).
+// Row n: 32-row blocks alternate gate and up (rows [64j, 64j+32) -> gate
+// rows [32j, +32), rows [64j+32, 64j+64) -> up rows [32j, +32)).
+__global__ __launch_bounds__(256) void gateup_fp8_kernel(const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
+                                                         uint8_t* __restrict__ b8, uint8_t* __restrict__ bs, int F,
+                                                         int D) {
+  const int blocks = D / 32;
+  const long long idx = blockIdx.x * 256ll + threadIdx.x;
+  if (idx >= 2ll * F * blocks) return;
+  const int n = int(idx / blocks), blk = int(idx - (long long)n * blocks);
+  const int src_row = (n >> 6) * 32 + (n & 31);
+  const uint16_t* src = ((n & 32) ? wu : wg) + size_t(src_row) * D + blk * 32;
+  float f[32];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const u32x4 w = reinterpret_cast<const u32x4*>(src)[c];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[8 * c + 2 * e] = lo_bf16(w[e]);
+      f[8 * c + 2 * e + 1] = hi_bf16(w[e]);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(f[e]));
+  // X = floor(log2(amax)) - 7: the block maximum lands in [128, 256) of e4m3
+  const int ex = int((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xff);
+  int x = ex - 127 - 7;
+  x = x < -120 ? -120 : (x > 120 ? 120 : x);
+  const float mul = __builtin_bit_cast(float, uint32_t(127 - x) << 23);
+  u32x4 o[2];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * q] * mul, f[4 * q + 1] * mul, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * q + 2] * mul, f[4 * q + 3] * mul, r, true);
+    o[q / 4][q % 4] = uint32_t(r);
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(b8 + size_t(n) * D + blk * 32);
+  dst[0] = o[0];
+  dst[1] = o[1];
+  bs[(size_t(blk / 4) * (2 * F) + n) * 4 + (blk & 3)] = uint8_t(x + 127);
+}
+
 inline dim3 grid_for(long long threads) { return dim3(unsigned((threads + 255) / 256)); }
 
 }  // namespace
@@ -104,6 +150,15 @@ hipError_t split_rows(const float* x, void* out, int rows, int D, hipStream_t s)
   if (D % 8) return hipErrorInvalidValue;
   hipLaunchKernelGGL(split_rows_kernel, grid_for((long long)rows * (D / 8)), dim3(256), 0, s, x,
                      static_cast<uint16_t*>(out), rows, D);
+  return hipGetLastError();
+}
+
+hipError_t gateup_fp8(const void* w_gate, const void* w_up, void* b8, void* bs, int F, int D, hipStream_t s) {
+  if (F <= 0) return hipSuccess;
+  if (D % 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gateup_fp8_kernel, grid_for(2ll * F * (D / 32)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
+                     static_cast<uint8_t*>(b8), static_cast<uint8_t*>(bs), F, D);
   return hipGetLastError();
 }
 

@@ -250,16 +250,24 @@ pv_status run_tower(pv_tower* t, const float* pixels, const pv::Plan& plan, void
       PV_LAUNCH(PV_K_OPROJ, gemm(pv::GEMM_OPROJ, a));
     }
     if (stop_here && st.stage == PV_STAGE_ATTN_RESID) return copy_stage(st, r, size_t(N) * D * 4, s);
-    // the MLP input of the bf16 tower goes in as bf16 hi and lo halves
-    // (about 16 significant bits): its rounding would otherwise be the
-    // largest error of the tower output
-    if (bf) PV_LAUNCH(PV_K_NORM, pv::rmsnorm_split(r, lw.ffn_norm, y, N, D, eps, s));
-    else PV_LAUNCH(PV_K_NORM, pv::rmsnorm(r, lw.ffn_norm, y, N, D, eps, true, s));
+    // the MLP input of the bf16 tower goes in as bf16 plus its low part in
+    // fp8 (times fp8 copies of the weights, 32-k scale blocks): its plain
+    // bf16 rounding would otherwise be the largest error of the tower output
+    const int srows = int(pv::a8_scale_rows(N));
+    if (bf) {
+      PV_LAUNCH(PV_K_GATEUP, pv::gateup_fp8(lw.w_gate, lw.w_up, ws + L.b8, ws + L.bs, F, D, s));
+      PV_LAUNCH(PV_K_NORM, pv::rmsnorm_hi_lo8(r, lw.ffn_norm, y, ws + L.a8, ws + L.as, N, srows, D, eps, s));
+    } else {
+      PV_LAUNCH(PV_K_NORM, pv::rmsnorm(r, lw.ffn_norm, y, N, D, eps, true, s));
+    }
     {  // gate/up with silu(gate) * up in the epilogue
       pv::GemmArgs a = g;
-      a.M = N; a.N = F; a.K = bf ? 2 * D : D;
-      a.A = y; a.lda = a.K;
-      a.kb = bf ? D : 0;
+      a.M = N; a.N = F; a.K = D;
+      a.A = y; a.lda = D;
+      if (bf) {
+        a.A8 = ws + L.a8; a.B8 = ws + L.b8; a.As = ws + L.as; a.Bs = ws + L.bs;
+        a.k8 = D; a.as_rows = srows; a.bs_rows = 2 * F;
+      }
       a.B0 = lw.w_gate; a.B1 = lw.w_up; a.ldb = D;
       a.C = big; a.ldc = F;
       PV_LAUNCH(PV_K_GATEUP, gemm(pv::GEMM_GATEUP, a));
