@@ -47,10 +47,23 @@ def flops_by_class(wl):
 
 
 def norm_bytes(wl):
-    """Algorithmic HBM bytes of the RMSNorm passes of one forward (bf16 path):
-    dual pass 4 read + 4 write + 2 write, single pass 4 read + 2 write."""
+    """Algorithmic HBM bytes per element of the RMSNorm passes of one forward
+    (bf16 path): the dual first pass reads 4 and writes 4 + 2; an attention
+    norm reads 4 and writes 2; an MLP norm reads 4 and writes 2 (bf16) + 1
+    (fp8 low part) + 1/32 (scale bytes)."""
     N, D, L = wl.n_patches, wl.hidden, wl.layers
-    return N * D * (10 + (2 * L - 1) * 6) if L > 0 else N * D * 8
+    return N * D * (10 + (L - 1) * 6 + L * (7 + 1 / 32)) if L > 0 else N * D * 8
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(wl, weights, pixels):
@@ -98,6 +111,7 @@ def cpu_baseline(wl, weights, pixels):
                    f"extrapolated as embed + {wl.layers} x block + merge = {fwd_s:.1f} s"),
         "merged_tokens_per_s": wl.out_rows / fwd_s,
         "host_cpus": os.cpu_count(),
+        "cpu_model": cpu_model(),
     }
 
 
@@ -272,6 +286,7 @@ def main():
                 d["tflops"] = round(fl[k] / (ms / args.profile_steps) / 1e9, 1)
             if k == "norm":
                 d["gbs"] = round(norm_bytes(wl) / (ms / args.profile_steps) / 1e6, 1)
+                d["hbm_frac"] = round(d["gbs"] / HBM_PEAK_GBS, 4)
             kernels[k] = d
             log(f"  {k:7s} {per_launch_ms:9.4f} ms x {launches_per_fwd:5.1f}/step  {d.get('tflops', '')} TFLOP/s "
                 f"{d.get('gbs', '')}")
