@@ -167,6 +167,35 @@ def pmc_summary(args):
     print(json.dumps(out))
 
 
+def time_scatter(out, wl, stream, reps=20):
+    """The masked scatter of the merged rows into a text sequence of the
+    same tokens plus 1,024 text tokens (HIP events around `reps` calls on the
+    launch stream).  Algorithmic bytes: each image row read and written once,
+    each token id read once."""
+    import numpy as np
+    import torch
+
+    from vlm_vision_encoder_amd import tower as T
+    rng = np.random.default_rng(9)
+    S = out.shape[0] + 1024
+    ids = rng.integers(11, 131072, size=S).astype(np.int32)
+    ids[rng.choice(S, size=out.shape[0], replace=False)] = 10
+    d_ids = torch.from_numpy(ids).cuda()
+    txt = torch.zeros((S, out.shape[1]), dtype=out.dtype, device="cuda")
+    T.scatter_image_embeddings(d_ids, out, txt, 10)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        st = T.scatter_image_embeddings(d_ids, out, txt, 10)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = 2 * out.numel() * out.element_size() + S * 4
+    return {"seq_len": S, "image_rows": int(out.shape[0]), "ms": round(ms, 5), "status": int(st.item()),
+            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def source_sha256(path):
     import hashlib
     with open(path, "rb") as f:
@@ -299,6 +328,8 @@ def main():
                     "traffic": measured_traffic(dom, wl, kernels[dom]["launches_per_step"]),
                     "flops_per_launch": dom_flops_launch, "avg_launch_ms": dom_ms}
 
+    scatter = time_scatter(out, wl, stream) if wl.merge == 2 else None
+
     patches_s = wl.n_patches / (ms_step * 1e-3)
     tokens_s = wl.out_rows / (ms_step * 1e-3)
     res = {
@@ -322,6 +353,7 @@ def main():
         "forward_mfma_frac": round(total_flops / (ms_step * 1e-3) / 1e12 / peak, 4),
         "roofline": roofline,
         "kernels": kernels,
+        "scatter": scatter,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")

@@ -198,19 +198,49 @@ pv_status pv_tower_index_maps(pv_tower* t, const int32_t* image_hw, int32_t n_im
  * per launch; leave it off for throughput runs.
  * Errors: PV_ERR_ARG (null), PV_ERR_HIP. */
 enum {
-  PV_K_MAPS = 0,     /* per-row index maps                     */
-  PV_K_PATCH = 1,    /* patch-embedding GEMM                   */
-  PV_K_NORM = 2,     /* RMSNorm passes                         */
-  PV_K_QKV = 3,      /* q,k,v GEMM with the rotary epilogue    */
-  PV_K_ATTN = 4,     /* block-diagonal attention               */
-  PV_K_OPROJ = 5,    /* out-projection GEMM (+ residual)       */
-  PV_K_GATEUP = 6,   /* MLP gate/up GEMM (silu * up)           */
-  PV_K_DOWN = 7,     /* MLP down GEMM (+ residual)             */
-  PV_K_MERGE = 8,    /* 2x2 merge + projection GEMM, or copy   */
+  PV_K_MAPS = 0,     /* per-row index maps                                    */
+  PV_K_PATCH = 1,    /* patch embedding: weight padding, im2col, GEMM         */
+  PV_K_NORM = 2,     /* RMSNorm passes                                        */
+  PV_K_QKV = 3,      /* q,k,v GEMM with the rotary epilogue                   */
+  PV_K_ATTN = 4,     /* block-diagonal attention                              */
+  PV_K_OPROJ = 5,    /* out-projection GEMM (+ residual)                      */
+  PV_K_GATEUP = 6,   /* MLP gate/up: fp8 weight copy + GEMM (silu * up)       */
+  PV_K_DOWN = 7,     /* MLP down GEMM (+ residual)                            */
+  PV_K_MERGE = 8,    /* residual copy + 2x2 merge GEMM, or output copy        */
   PV_K_COUNT = 9
 };
 pv_status pv_tower_set_profiling(pv_tower* t, int32_t enable);
 pv_status pv_tower_read_profile(pv_tower* t, double* ms, int64_t* launches, int32_t reset);
+
+/* Merge of the tower output into a text-embedding sequence ("Mistral 3"
+ * (KerasFormers) model page: Mistral3Model argument table, image_token_id --
+ * the placeholder token the processor expands to each image's own number of
+ * merged tokens -- and "Several images in one conversation"; the
+ * inference-research record's masked-scatter merge of projected image
+ * features into the decoder's input embeddings).
+ * Position p of the sequence (0 <= p < seq_len) with token_ids[p] ==
+ * image_token_id is the k-th such position (k counted from 0 in sequence
+ * order); row p of text_emb is replaced by row k of image_emb when
+ * k < n_image_rows.  Other rows are left unchanged.
+ *   token_ids   device int32 [seq_len]
+ *   image_emb   device [n_image_rows][dim], elements of elem_bytes bytes
+ *               (2 = bf16, 4 = fp32; the tower output as written)
+ *   text_emb    device [seq_len][dim], same element size; updated in place
+ *   status      device int32 [1], written: 0 if the number of placeholder
+ *               positions equals n_image_rows, else 1 (the copy then covers
+ *               min(count, n_image_rows) rows)
+ *   workspace   device, >= pv_scatter_workspace_bytes(seq_len) bytes,
+ *               256-byte aligned
+ * Rows must be 16-byte multiples (dim * elem_bytes % 16 == 0) and all
+ * pointers 16-byte aligned.  Enqueued on stream; no synchronisation.
+ * Errors: PV_ERR_ARG (null pointer, seq_len < 0, n_image_rows < 0, dim < 1,
+ * elem_bytes not 2 or 4, misalignment), PV_ERR_CAPACITY (workspace),
+ * PV_ERR_HIP. */
+size_t pv_scatter_workspace_bytes(int64_t seq_len);
+pv_status pv_scatter_image_embeddings(const int32_t* token_ids, int64_t seq_len, int32_t image_token_id,
+                                      const void* image_emb, int64_t n_image_rows, void* text_emb,
+                                      int32_t dim, int32_t elem_bytes, int32_t* status, void* workspace,
+                                      size_t ws_bytes, void* stream);
 
 /* Thread-local message of the last failure in this thread ("" if none). */
 const char* pv_last_error(void);

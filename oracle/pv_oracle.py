@@ -49,7 +49,7 @@ parity unpinned: neither weights nor another implementation exist here.
 from __future__ import annotations
 
 from dataclasses import dataclass
-from typing import Dict, List, Optional, Sequence
+from typing import Tuple, Dict, List, Optional, Sequence
 
 import numpy as np
 
@@ -260,6 +260,31 @@ def merge_project(h: np.ndarray, merge_src: np.ndarray, w_merge: np.ndarray) -> 
     src = np.asarray(merge_src, dtype=np.int64)
     z = np.concatenate([h[src[:, 0]], h[src[:, 1]], h[src[:, 2]], h[src[:, 3]]], axis=1)
     return z @ np.asarray(w_merge, dtype=np.float64).T
+
+
+# --------------------------------------------------------------------------
+# after the tower: masked scatter into the text-embedding sequence
+# --------------------------------------------------------------------------
+def masked_scatter(token_ids: np.ndarray, image_emb: np.ndarray, text_emb: np.ndarray,
+                   image_token_id: int) -> Tuple[np.ndarray, bool]:
+    """The k-th placeholder position of the sequence takes image row k.
+
+    "Mistral 3", Mistral3Model argument table: image_token_id is the
+    placeholder the processor expands per image; "Several images in one
+    conversation": each image's marker expands to that image's own count, so
+    the placeholders of all images, in sequence order, line up with the
+    merged rows of all images in input order.  Returns (new text embeddings,
+    whether the placeholder count equals the number of image rows); on a
+    mismatch the first min(count, rows) placeholders are filled.
+    """
+    ids = np.asarray(token_ids)
+    out = np.array(text_emb, copy=True)
+    positions = [p for p in range(ids.shape[0]) if int(ids[p]) == int(image_token_id)]
+    rows = np.asarray(image_emb)
+    for k, p in enumerate(positions):
+        if k < rows.shape[0]:
+            out[p] = rows[k]
+    return out, len(positions) == rows.shape[0]
 
 
 # --------------------------------------------------------------------------

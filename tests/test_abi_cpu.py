@@ -178,3 +178,37 @@ def test_host_index_maps_equal_oracle(name):
             np.testing.assert_array_equal(ms[:Tn], m["merge_src"])
     finally:
         lib.pv_tower_destroy(h)
+
+
+@pytest.mark.parametrize("args,status", [
+    # (ids, S, image rows, text, dim, elem_bytes, status ptr, ws, ws bytes)
+    ((FAKE, 10, FAKE, 4, FAKE, 5120, 2, FAKE, FAKE, 1 << 20), 0),
+    ((FAKE, 10, FAKE, 4, FAKE, 5120, 3, FAKE, FAKE, 1 << 20), -1),      # element size
+    ((FAKE, 10, FAKE, 4, FAKE, 4, 2, FAKE, FAKE, 1 << 20), -1),         # 8-byte rows
+    ((FAKE, 10, FAKE, 4, FAKE, 0, 2, FAKE, FAKE, 1 << 20), -1),         # dim
+    ((FAKE, -1, FAKE, 4, FAKE, 5120, 2, FAKE, FAKE, 1 << 20), -1),      # seq_len
+    ((FAKE, 10, FAKE, -2, FAKE, 5120, 2, FAKE, FAKE, 1 << 20), -1),     # rows
+    ((None, 10, FAKE, 4, FAKE, 5120, 2, FAKE, FAKE, 1 << 20), -1),      # token ids
+    ((FAKE, 10, None, 4, FAKE, 5120, 2, FAKE, FAKE, 1 << 20), -1),      # image rows
+    ((FAKE, 10, FAKE, 4, FAKE, 5120, 2, None, FAKE, 1 << 20), -1),      # status
+    ((FAKE, 10, FAKE + 8, 4, FAKE, 5120, 2, FAKE, FAKE, 1 << 20), -1),  # alignment
+    ((FAKE, 10, FAKE, 4, FAKE, 5120, 2, FAKE, FAKE + 16, 1 << 20), -1), # workspace alignment
+    ((FAKE, 1000, FAKE, 4, FAKE, 5120, 2, FAKE, FAKE, 64), -3),         # workspace size
+])
+def test_scatter_validation_before_any_device_work(args, status):
+    """Argument checks of the masked scatter; the one valid call is not made
+    (it would touch device memory)."""
+    lib = T.load_library()
+    if status == 0:
+        assert lib.pv_scatter_workspace_bytes(args[1]) <= args[9]
+        return
+    ids, S, img, rows, txt, dim, eb, st, ws, wsb = args
+    got = lib.pv_scatter_image_embeddings(ids, S, 10, img, rows, txt, dim, eb, st, ws, wsb, None)
+    assert got == status, lib.pv_last_error().decode()
+    assert lib.pv_last_error().decode()
+
+
+def test_scatter_workspace_grows_with_the_sequence():
+    lib = T.load_library()
+    a, b = lib.pv_scatter_workspace_bytes(0), lib.pv_scatter_workspace_bytes(100_000)
+    assert a >= 256 and b >= 400_000 + 256 and b % 256 == 0

@@ -427,3 +427,26 @@ def test_tower_no_merge_returns_patch_states():
     res = O.tower_forward(rng.standard_normal(3 * 96), hw, w, cfg)
     assert res["out"].shape == (6, 16)
     np.testing.assert_array_equal(res["out"], res["tower_out"])
+
+
+def test_masked_scatter_hand_example():
+    """Placeholder id 10 ("Mistral 3", Mistral3Model table): the k-th
+    placeholder in sequence order takes image row k; other rows unchanged."""
+    ids = np.array([1, 10, 5, 10, 10, 2])
+    img = np.array([[1.0, 1.5], [2.0, 2.5], [3.0, 3.5]])
+    txt = np.arange(12, dtype=np.float64).reshape(6, 2) + 100
+    out, ok = O.masked_scatter(ids, img, txt, 10)
+    want = txt.copy()
+    want[1], want[3], want[4] = img[0], img[1], img[2]
+    assert ok and np.array_equal(out, want)
+    assert np.array_equal(txt, np.arange(12, dtype=np.float64).reshape(6, 2) + 100)  # input untouched
+
+
+def test_masked_scatter_count_mismatch_fills_what_fits():
+    ids = np.array([10, 3, 10])
+    img = np.array([[7.0], [8.0], [9.0]])
+    txt = np.zeros((3, 1))
+    out, ok = O.masked_scatter(ids, img, txt, 10)
+    assert not ok and out[:, 0].tolist() == [7.0, 0.0, 8.0]
+    out, ok = O.masked_scatter(np.array([10, 10, 10, 10]), img, np.zeros((4, 1)), 10)
+    assert not ok and out[:, 0].tolist() == [7.0, 8.0, 9.0, 0.0]

@@ -83,5 +83,11 @@ hipError_t pad_rows(const void* w, void* out, int rows, int K, int Kp, hipStream
 //   gateup_fp8:   b8 [2F][D] fp8 e4m3 = the gate/up weights in the GEMM's
 //                 interleaved row order, bs [D/128][2F][4] scale bytes
 hipError_t gateup_fp8(const void* w_gate, const void* w_up, void* b8, void* bs, int F, int D, hipStream_t s);
+// Masked scatter: the k-th position p with ids[p] == token takes row k of src
+// (k < rows); status[0] = (placeholder count == rows) ? 0 : 1.  ws: a list of
+// n positions + the count (scatter_workspace_bytes(n) bytes).
+size_t scatter_workspace_bytes(int64_t n);
+hipError_t scatter_rows(const int32_t* ids, int64_t n, int32_t token, const void* src, int64_t rows, void* dst,
+                        int64_t row_bytes, int32_t* status, void* ws, hipStream_t s);
 
 }  // namespace pv

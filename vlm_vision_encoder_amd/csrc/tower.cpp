@@ -494,6 +494,32 @@ pv_status pv_tower_index_maps(pv_tower* t, const int32_t* image_hw, int32_t n_im
   return PV_OK;
 }
 
+size_t pv_scatter_workspace_bytes(int64_t seq_len) { return pv::scatter_workspace_bytes(seq_len); }
+
+pv_status pv_scatter_image_embeddings(const int32_t* token_ids, int64_t seq_len, int32_t image_token_id,
+                                      const void* image_emb, int64_t n_image_rows, void* text_emb, int32_t dim,
+                                      int32_t elem_bytes, int32_t* status, void* workspace, size_t ws_bytes,
+                                      void* stream) {
+  g_last_error.clear();
+  if (!status || !workspace) return fail(PV_ERR_ARG, "status and workspace must not be null");
+  if (seq_len < 0 || n_image_rows < 0) return fail(PV_ERR_ARG, "seq_len and n_image_rows must be >= 0");
+  if (seq_len > INT32_MAX || n_image_rows > INT32_MAX) return fail(PV_ERR_ARG, "seq_len and n_image_rows must fit int32");
+  if (dim < 1) return fail(PV_ERR_ARG, "dim must be >= 1");
+  if (elem_bytes != 2 && elem_bytes != 4) return fail(PV_ERR_ARG, "elem_bytes must be 2 (bf16) or 4 (fp32)");
+  if ((int64_t(dim) * elem_bytes) % 16) return fail(PV_ERR_ARG, "rows must be a multiple of 16 bytes");
+  if (seq_len > 0 && (!token_ids || !text_emb)) return fail(PV_ERR_ARG, "token_ids and text_emb must not be null");
+  if (n_image_rows > 0 && !image_emb) return fail(PV_ERR_ARG, "image_emb must not be null");
+  if (!aligned(image_emb, 16) || !aligned(text_emb, 16) || !aligned(token_ids, 4) || !aligned(status, 4))
+    return fail(PV_ERR_ARG, "image_emb and text_emb must be 16-byte aligned, token_ids and status 4-byte aligned");
+  if (!aligned(workspace, 256)) return fail(PV_ERR_ARG, "workspace must be 256-byte aligned");
+  const size_t need = pv::scatter_workspace_bytes(seq_len);
+  if (ws_bytes < need)
+    return fail(PV_ERR_CAPACITY, "workspace " + std::to_string(ws_bytes) + " < " + std::to_string(need));
+  PV_HIP(pv::scatter_rows(token_ids, seq_len, image_token_id, image_emb, n_image_rows, text_emb,
+                          int64_t(dim) * elem_bytes, status, workspace, static_cast<hipStream_t>(stream)));
+  return PV_OK;
+}
+
 pv_status pv_tower_set_profiling(pv_tower* t, int32_t enable) {
   g_last_error.clear();
   if (!t) return fail(PV_ERR_ARG, "tower is null");

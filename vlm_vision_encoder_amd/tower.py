@@ -21,7 +21,7 @@ STATUS = {0: "PV_OK", -1: "PV_ERR_ARG", -2: "PV_ERR_SHAPE", -3: "PV_ERR_CAPACITY
 
 EXPORTED = ("pv_tower_create", "pv_tower_destroy", "pv_tower_plan", "pv_tower_forward",
             "pv_tower_forward_stage", "pv_tower_index_maps", "pv_tower_set_profiling", "pv_tower_read_profile",
-            "pv_last_error", "pv_status_str")
+            "pv_scatter_workspace_bytes", "pv_scatter_image_embeddings", "pv_last_error", "pv_status_str")
 KERNEL_CLASSES = ("maps", "patch", "norm", "qkv", "attn", "oproj", "gateup", "down", "merge")
 
 
@@ -82,6 +82,10 @@ def load_library(path: str = LIB_PATH):
     lib.pv_tower_set_profiling.restype = i32
     lib.pv_tower_read_profile.argtypes = [vp, C.POINTER(C.c_double), C.POINTER(C.c_int64), i32]
     lib.pv_tower_read_profile.restype = i32
+    lib.pv_scatter_workspace_bytes.argtypes = [i64]
+    lib.pv_scatter_workspace_bytes.restype = sz
+    lib.pv_scatter_image_embeddings.argtypes = [vp, i64, i32, vp, i64, vp, i32, i32, vp, vp, sz, vp]
+    lib.pv_scatter_image_embeddings.restype = i32
     lib.pv_last_error.argtypes = []
     lib.pv_last_error.restype = C.c_char_p
     lib.pv_status_str.argtypes = [i32]
@@ -244,6 +248,28 @@ class Tower:
                                             torch.cuda.current_stream().cuda_stream))
         torch.cuda.synchronize()
         return cu.cpu().numpy(), rc[:info.n_patches].cpu().numpy(), ms[:T].cpu().numpy()
+
+
+def scatter_image_embeddings(token_ids, image_emb, text_emb, image_token_id: int = 10):
+    """In place: the k-th position of token_ids (int32, [S], CUDA) equal to
+    image_token_id takes row k of image_emb ([T][dim], CUDA) in text_emb
+    ([S][dim], CUDA, same dtype).  Returns the device int32 status (0: the
+    placeholder count equals T).  Enqueued on the current stream."""
+    import torch
+    lib = load_library()
+    assert token_ids.dtype == torch.int32 and token_ids.is_contiguous()
+    assert image_emb.dtype == text_emb.dtype and image_emb.is_contiguous() and text_emb.is_contiguous()
+    S, T = token_ids.numel(), image_emb.shape[0]
+    dim = text_emb.shape[1] if text_emb.dim() == 2 else image_emb.shape[1]
+    status = torch.empty(1, dtype=torch.int32, device=text_emb.device)
+    wsb = lib.pv_scatter_workspace_bytes(S)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=text_emb.device)
+    _check(lib.pv_scatter_image_embeddings(token_ids.data_ptr() if S else None, S, int(image_token_id),
+                                           image_emb.data_ptr() if T else None, T,
+                                           text_emb.data_ptr() if S else None, dim, image_emb.element_size(),
+                                           status.data_ptr(), ws.data_ptr(), wsb,
+                                           torch.cuda.current_stream().cuda_stream))
+    return status
 
 
 # ---------------------------------------------------------------- helpers
