@@ -39,15 +39,30 @@ notes of the repository):
    fastest; merged tokens row-major per image, images in input order.
 7. The projector is a single bias-free linear map 4*D -> out_dim.
 8. RMSNorm: x / sqrt(mean(x^2) + eps) * g with eps = 1e-5.
+9. Resize target (the processor's description on the "Mistral 3" page): an
+   image whose longest side exceeds ``longest_edge`` is first shrunk by the
+   factor longest_edge / max(H, W), each side rounded down to whole pixels;
+   smaller images are not enlarged.  Each side is then rounded up to the
+   grid the projector consumes (patch * merge pixels), and never past the
+   largest multiple of that grid within ``longest_edge``.
+10. Resampling: bilinear with pixel centres at half-integers (source
+    coordinate (t + 0.5) * in / out - 0.5, clamped at the first pixel, the
+    upper neighbour clamped at the last), no antialiasing, on the uint8
+    values taken as reals (no re-quantisation after the resize).
+11. Normalisation: x / 255 then (x - mean_c) / std_c with the processor
+    table's constants; uint8 pixels come in as H x W x 3 (RGB).
 
 Pinning: every function here is pinned in ``tests/test_oracle_pins.py`` by a
 check that does not reuse this code path (closed-form counts printed on the
 pages, direct convolution loops, textbook dense masked softmax, rotation
-identities, identity/zero weights).  The full tower against a trained model is
+identities, identity/zero weights; for the preprocessing, torch's bilinear
+interpolate in float64, 2x2 block means, ramps, and a search-based statement
+of the target-size rule).  The full tower against a trained model is
 parity unpinned: neither weights nor another implementation exist here.
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
 from typing import Tuple, Dict, List, Optional, Sequence
 
@@ -285,6 +300,105 @@ def masked_scatter(token_ids: np.ndarray, image_emb: np.ndarray, text_emb: np.nd
         if k < rows.shape[0]:
             out[p] = rows[k]
     return out, len(positions) == rows.shape[0]
+
+
+# --------------------------------------------------------------------------
+# before the tower: resize onto the patch grid and normalise (uint8 input)
+# --------------------------------------------------------------------------
+# "Mistral 3", Mistral3ImageProcessor table: per-channel mean and std
+PROCESSOR_MEAN = (0.48145466, 0.4578275, 0.40821073)
+PROCESSOR_STD = (0.26862954, 0.26130258, 0.27577711)
+
+
+def resize_target(h: int, w: int, longest_edge: int, grid: int) -> Tuple[int, int]:
+    """(H, W) of the resized image, in exact integer arithmetic.
+
+    "Mistral 3" page, model description: images are resized so that the
+    longest edge fits ``longest_edge`` and the sides stay on the patch grid.
+    Step 1 (fit): if max(H, W) > longest_edge, each side becomes
+    floor(side * longest_edge / max(H, W)) (at least 1).  Step 2 (grid): each
+    side is rounded up to a multiple of ``grid``, capped at the largest
+    multiple of ``grid`` that is <= longest_edge.
+    """
+    h, w, L, g = int(h), int(w), int(longest_edge), int(grid)
+    if h <= 0 or w <= 0 or g <= 0 or L < g:
+        raise ValueError("sides and grid must be positive and longest_edge >= grid")
+    m = max(h, w)
+    if m > L:
+        h = max(1, (h * L) // m)
+        w = max(1, (w * L) // m)
+    cap = (L // g) * g
+    return min(-(-h // g) * g, cap), min(-(-w // g) * g, cap)
+
+
+def bilinear_taps(n_in: int, n_out: int, t: int) -> Tuple[int, int, float]:
+    """Source taps (i0, i1) and weight f of i1 for output index t.
+
+    Pixel centres at half-integers: s = (t + 0.5) * n_in / n_out - 0.5,
+    clamped below at 0; i0 = floor(s), i1 = min(i0 + 1, n_in - 1), f = s - i0.
+    """
+    s = (t + 0.5) * n_in / n_out - 0.5
+    if s < 0.0:
+        s = 0.0
+    i0 = int(math.floor(s))
+    i1 = min(i0 + 1, n_in - 1)
+    return i0, i1, s - i0
+
+
+def interp_matrix(n_in: int, n_out: int) -> np.ndarray:
+    """[n_out][n_in] matrix of the 1-D bilinear resampling (rows of taps)."""
+    m = np.zeros((n_out, n_in), dtype=np.float64)
+    for t in range(n_out):
+        i0, i1, f = bilinear_taps(n_in, n_out, t)
+        m[t, i0] += 1.0 - f
+        m[t, i1] += f
+    return m
+
+
+def preprocess_image(img_u8: np.ndarray, th: int, tw: int,
+                     mean: Sequence[float] = PROCESSOR_MEAN,
+                     std: Sequence[float] = PROCESSOR_STD) -> np.ndarray:
+    """uint8 H x W x 3 image -> float64 3 x th x tw planes, resized and
+    normalised.
+
+    The bilinear resize is separable: out_c = R_h img_c R_w^T with the two
+    1-D interpolation matrices; then x / 255 and (x - mean_c) / std_c
+    ("Mistral 3", Mistral3ImageProcessor table).
+    """
+    img = np.asarray(img_u8)
+    if img.ndim != 3 or img.shape[2] != 3:
+        raise ValueError("image must be H x W x 3")
+    h, w = img.shape[:2]
+    rh, rw = interp_matrix(h, th), interp_matrix(w, tw)
+    out = np.empty((3, th, tw), dtype=np.float64)
+    for c in range(3):
+        plane = rh @ img[:, :, c].astype(np.float64) @ rw.T
+        out[c] = (plane / 255.0 - mean[c]) / std[c]
+    return out
+
+
+def preprocess_pixel(img_u8: np.ndarray, th: int, tw: int, c: int, y: int, x: int,
+                     mean: Sequence[float] = PROCESSOR_MEAN,
+                     std: Sequence[float] = PROCESSOR_STD) -> float:
+    """One value of ``preprocess_image`` (channel c, row y, column x) from its
+    four taps, for spot checks of large images."""
+    img = np.asarray(img_u8)
+    h, w = img.shape[:2]
+    y0, y1, fy = bilinear_taps(h, th, y)
+    x0, x1, fx = bilinear_taps(w, tw, x)
+    v = ((1 - fy) * ((1 - fx) * float(img[y0, x0, c]) + fx * float(img[y0, x1, c]))
+         + fy * ((1 - fx) * float(img[y1, x0, c]) + fx * float(img[y1, x1, c])))
+    return (v / 255.0 - mean[c]) / std[c]
+
+
+def preprocess_batch(images: Sequence[np.ndarray], longest_edge: int, grid: int,
+                     mean: Sequence[float] = PROCESSOR_MEAN,
+                     std: Sequence[float] = PROCESSOR_STD):
+    """uint8 images -> (flat float64 pixels, target sizes) in the tower's input
+    layout: each image's 3 x H x W planes after the previous image's."""
+    hw = [resize_target(im.shape[0], im.shape[1], longest_edge, grid) for im in images]
+    parts = [preprocess_image(im, th, tw, mean, std).reshape(-1) for im, (th, tw) in zip(images, hw)]
+    return np.concatenate(parts), hw
 
 
 # --------------------------------------------------------------------------

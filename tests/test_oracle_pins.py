@@ -450,3 +450,128 @@ def test_masked_scatter_count_mismatch_fills_what_fits():
     assert not ok and out[:, 0].tolist() == [7.0, 0.0, 8.0]
     out, ok = O.masked_scatter(np.array([10, 10, 10, 10]), img, np.zeros((4, 1)), 10)
     assert not ok and out[:, 0].tolist() == [7.0, 8.0, 9.0, 0.0]
+
+
+# ------------------------------------------------------- preprocessing (uint8)
+def test_resize_target_page_sizes():
+    """"Mistral 3" processor table: longest_edge 1540, patch 14 (merge 2 ->
+    28-pixel grid); a 4096x4096 photo becomes 1540x1540 = 110x110 patches.
+    "Pixtral-12B-2409": a 1024x1024 tile with patch 16 stays 1024x1024."""
+    assert O.resize_target(4096, 4096, 1540, 28) == (1540, 1540)
+    assert O.resize_target(1024, 1024, 1024, 16) == (1024, 1024)
+    # already on the grid and within the edge: unchanged, never enlarged
+    for h, w in [(28, 28), (224, 1540), (1540, 56), (812, 644)]:
+        assert O.resize_target(h, w, 1540, 28) == (h, w)
+    # a small off-grid image is only rounded up to the grid
+    assert O.resize_target(300, 200, 1540, 28) == (308, 224)
+    # wide photo: 1000 x 4000 -> fit 385 x 1540 -> grid 392 x 1540
+    assert O.resize_target(1000, 4000, 1540, 28) == (392, 1540)
+
+
+def test_resize_target_brute_force():
+    """Search-based restatement: the fitted side is the largest integer s >= 1
+    with s * max(H, W) <= side * L (if max(H, W) > L, else the side itself),
+    then the smallest grid multiple >= s, capped at the largest grid multiple
+    <= L."""
+    rng = np.random.default_rng(21)
+    for _ in range(400):
+        grid = int(rng.integers(1, 40))
+        L = int(rng.integers(grid, 300))
+        h, w = (int(v) for v in rng.integers(1, 700, size=2))
+        m = max(h, w)
+        want = []
+        for side in (h, w):
+            s = side
+            if m > L:
+                s = 1
+                while (s + 1) * m <= side * L:
+                    s += 1
+            t = grid
+            while t < s:
+                t += grid
+            cap = grid
+            while cap + grid <= L:
+                cap += grid
+            want.append(min(t, cap))
+        got = O.resize_target(h, w, L, grid)
+        assert got == tuple(want), (h, w, L, grid)
+        assert max(got) <= L and got[0] % grid == 0 and got[1] % grid == 0
+
+
+@pytest.mark.parametrize("src,dst", [
+    ((7, 5), (7, 5)), ((8, 12), (4, 6)), ((9, 13), (28, 28)), ((40, 31), (14, 28)),
+    ((1, 6), (5, 3)), ((6, 1), (2, 9)), ((33, 47), (1, 1)), ((4096 // 64, 4096 // 64), (1540 // 64, 1540 // 64)),
+])
+def test_bilinear_matches_library_interpolate(src, dst):
+    """Half-pixel-centre bilinear without antialiasing is torch's
+    interpolate(mode='bilinear', align_corners=False) in float64."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(22)
+    img = rng.integers(0, 256, size=src + (3,), dtype=np.uint8)
+    got = O.preprocess_image(img, dst[0], dst[1], mean=(0, 0, 0), std=(1 / 255, 1 / 255, 1 / 255))
+    t = torch.from_numpy(img.astype(np.float64)).permute(2, 0, 1)[None]
+    want = torch.nn.functional.interpolate(t, size=dst, mode="bilinear", align_corners=False,
+                                           antialias=False)[0].numpy()
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-9)
+
+
+def test_bilinear_closed_forms():
+    rng = np.random.default_rng(23)
+    unit = dict(mean=(0, 0, 0), std=(1 / 255, 1 / 255, 1 / 255))  # raw values out
+    img = rng.integers(0, 256, size=(10, 14, 3), dtype=np.uint8)
+    # same size: an exact copy
+    np.testing.assert_array_equal(O.preprocess_image(img, 10, 14, **unit),
+                                  img.transpose(2, 0, 1).astype(np.float64))
+    # halving each side: every output is the mean of its 2x2 source block
+    half = O.preprocess_image(img, 5, 7, **unit)
+    blocks = img.astype(np.float64).reshape(5, 2, 7, 2, 3).mean(axis=(1, 3)).transpose(2, 0, 1)
+    np.testing.assert_allclose(half, blocks, rtol=0, atol=1e-12)
+    # a constant image stays constant at any size
+    flat = np.full((9, 6, 3), 77, dtype=np.uint8)
+    np.testing.assert_allclose(O.preprocess_image(flat, 13, 4, **unit), 77.0, rtol=0, atol=1e-12)
+    # doubling a linear ramp v = 3y + 2x: output t sits at source t/2 - 1/4,
+    # so interior outputs are 3(ty/2 - 1/4) + 2(tx/2 - 1/4); the clamped
+    # border rows/columns take the edge pixel's coordinate
+    ramp = np.zeros((6, 8, 3), dtype=np.uint8)
+    yy, xx = np.mgrid[0:6, 0:8]
+    ramp[..., 0] = 3 * yy + 2 * xx
+    up = O.preprocess_image(ramp, 12, 16, **unit)[0]
+    for ty in range(12):
+        for tx in range(16):
+            sy = min(max(ty / 2 - 0.25, 0.0), 5.0)
+            sx = min(max(tx / 2 - 0.25, 0.0), 7.0)
+            assert abs(up[ty, tx] - (3 * sy + 2 * sx)) < 1e-12
+
+
+def test_normalisation_constants_and_channel_order():
+    """x/255 then (x - mean_c)/std_c with the processor table's values;
+    channel 0 of the output is the image's first (R) component."""
+    mean = (0.48145466, 0.4578275, 0.40821073)
+    std = (0.26862954, 0.26130258, 0.27577711)
+    img = np.zeros((4, 4, 3), dtype=np.uint8)
+    img[..., 0] = 255
+    img[..., 2] = 51
+    out = O.preprocess_image(img, 4, 4)
+    np.testing.assert_allclose(out[0], (1.0 - mean[0]) / std[0], rtol=1e-15)
+    np.testing.assert_allclose(out[1], -mean[1] / std[1], rtol=1e-15)
+    np.testing.assert_allclose(out[2], (0.2 - mean[2]) / std[2], rtol=1e-14)
+
+
+def test_preprocess_pixel_spot_values_agree_with_planes():
+    rng = np.random.default_rng(24)
+    img = rng.integers(0, 256, size=(37, 23, 3), dtype=np.uint8)
+    full = O.preprocess_image(img, 56, 28)
+    for c, y, x in [(0, 0, 0), (1, 55, 27), (2, 17, 9), (0, 31, 20), (1, 1, 26)]:
+        assert abs(O.preprocess_pixel(img, 56, 28, c, y, x) - full[c, y, x]) < 1e-12
+
+
+def test_preprocess_batch_layout():
+    rng = np.random.default_rng(25)
+    ims = [rng.integers(0, 256, size=(50, 90, 3), dtype=np.uint8),
+           rng.integers(0, 256, size=(30, 20, 3), dtype=np.uint8)]
+    flat, hw = O.preprocess_batch(ims, 56, 28)
+    # 50x90 fits as 31x56, then both sides round up to 56; 30x20 is within
+    # the edge and rounds up to 56x28
+    assert hw == [(56, 56), (56, 28)]
+    assert flat.shape == (3 * 56 * 56 + 3 * 56 * 28,)
+    np.testing.assert_array_equal(flat[3 * 56 * 56:].reshape(3, 56, 28), O.preprocess_image(ims[1], 56, 28))

@@ -165,6 +165,13 @@ def make_pixels(wl: Workload, seed: int = SEED_PIXELS) -> np.ndarray:
     return np.concatenate(parts)
 
 
+def make_u8_images(hw, seed: int = SEED_PIXELS) -> List[np.ndarray]:
+    """Uniform uint8 H x W x 3 (RGB, channel fastest) images of the given
+    source sizes, drawn in input order."""
+    rng = np.random.default_rng(seed)
+    return [rng.integers(0, 256, size=(int(h), int(w), 3), dtype=np.uint8) for h, w in hw]
+
+
 def oracle_weights(w: Dict) -> Dict:
     """The same weights as float64 arrays (what the oracle consumes)."""
     out = {"patch_w": w["patch_w"].astype(np.float64), "ln_pre": w["ln_pre"].astype(np.float64),
