@@ -242,6 +242,67 @@ pv_status pv_scatter_image_embeddings(const int32_t* token_ids, int64_t seq_len,
                                       int32_t dim, int32_t elem_bytes, int32_t* status, void* workspace,
                                       size_t ws_bytes, void* stream);
 
+/* ---- uint8 input: resize onto the patch grid + normalisation ----
+ * Sources: "Mistral 3" (KerasFormers) model page, description (images are
+ * resized so that the longest edge fits longest_edge and the sides stay on
+ * the patch grid) and Mistral3ImageProcessor table (longest_edge 1540, patch
+ * 14, per-channel mean and std).  Readings where the page is silent:
+ *  - target size: if max(H, W) > longest_edge, each side becomes
+ *    floor(side * longest_edge / max(H, W)) (at least 1; images are never
+ *    enlarged); then each side is rounded up to a multiple of grid, capped at
+ *    the largest multiple of grid within longest_edge.  For a tower, grid =
+ *    patch * merge (the merge needs whole 2x2 patch windows) and
+ *    longest_edge = max_side.
+ *  - resampling: bilinear, pixel centres at half-integers (source coordinate
+ *    (t + 0.5) * in / out - 0.5, clamped at the first pixel; the upper tap
+ *    clamped at the last), no antialiasing, computed in fp32 on the uint8
+ *    values (no re-quantisation).
+ *  - normalisation: (x / 255 - mean_c) / std_c.
+ * Image layout: uint8 H x W x 3 (row, column, channel; RGB, channel fastest);
+ * image i follows image i-1 with no padding.  Every source side must be in
+ * [1, 32768].  mean_std: host float [6] = mean R, G, B then std R, G, B, or
+ * NULL for the processor table's values (0.48145466, 0.4578275,
+ * 0.40821073; 0.26862954, 0.26130258, 0.27577711). */
+
+/* Host-only, pure: target sizes (dst_hw, host [n_images][2]) of source sizes
+ * (src_hw, host [n_images][2]) under the rule above.
+ * Errors: PV_ERR_ARG (null, n_images < 1, grid < 1, longest_edge < grid),
+ * PV_ERR_SHAPE (a source side outside [1, 32768]). */
+pv_status pv_resize_target(const int32_t* src_hw, int32_t n_images, int32_t longest_edge,
+                           int32_t grid, int32_t* dst_hw);
+
+/* Host-only, pure: as pv_tower_plan for uint8 sources of sizes src_hw, with
+ * the tower's own longest_edge (max_side) and grid (patch * merge); writes
+ * the target sizes to dst_hw (host [n_images][2], may be NULL).  The
+ * workspace size is the same as for pv_tower_plan of the target sizes.
+ * Errors: PV_ERR_ARG, PV_ERR_SHAPE. */
+pv_status pv_tower_plan_u8(const pv_tower* t, const int32_t* src_hw, int32_t n_images,
+                           int32_t* dst_hw, pv_plan_info* info);
+
+/* Runs the whole tower from uint8 images: the resize and the normalisation
+ * happen inside the patch embedding's operand load (bf16 tower: no
+ * intermediate image; fp32 tower: the normalised planes go through the
+ * workspace).  Output, out_rows_cap, workspace, stream: as pv_tower_forward,
+ * for the target sizes pv_tower_plan_u8 reports.
+ *  images  device uint8, the layout above; src_hw host [n_images][2].
+ * Errors: PV_ERR_ARG (null, misaligned output/workspace, bad mean_std),
+ * PV_ERR_SHAPE, PV_ERR_CAPACITY, PV_ERR_HIP. */
+pv_status pv_tower_forward_u8(pv_tower* t, const uint8_t* images, const int32_t* src_hw,
+                              int32_t n_images, const float* mean_std, void* out,
+                              int64_t out_rows_cap, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+/* The preprocessing alone, to any target size: image i (src_hw[i], uint8,
+ * layout above) is resampled to dst_hw[i] and normalised into out (device
+ * fp32, 4-byte aligned): image i's 3 x tH x tW planes (channel, row, column)
+ * after image i-1's -- the pixel layout pv_tower_forward takes.  src_hw and
+ * dst_hw are host [n_images][2]; every side in [1, 32768].  No workspace;
+ * one launch per image on stream.
+ * Errors: PV_ERR_ARG (null, n_images < 1, misaligned out, bad mean_std),
+ * PV_ERR_SHAPE, PV_ERR_HIP. */
+pv_status pv_preprocess_u8(const uint8_t* images, const int32_t* src_hw, const int32_t* dst_hw,
+                           int32_t n_images, const float* mean_std, float* out, void* stream);
+
 /* Thread-local message of the last failure in this thread ("" if none). */
 const char* pv_last_error(void);
 

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(T.LIB_PATH), reason="libpv_to
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pv_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pv_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_expected_entry_points():
@@ -212,3 +212,82 @@ def test_scatter_workspace_grows_with_the_sequence():
     lib = T.load_library()
     a, b = lib.pv_scatter_workspace_bytes(0), lib.pv_scatter_workspace_bytes(100_000)
     assert a >= 256 and b >= 400_000 + 256 and b % 256 == 0
+
+
+# ------------------------------------------------------------ uint8 input
+def test_resize_target_equals_oracle():
+    """The library's target-size rule is integer work: bit-exact against the
+    oracle over random sizes, edges and grids."""
+    rng = np.random.default_rng(31)
+    hw = [(int(a), int(b)) for a, b in rng.integers(1, 9000, size=(300, 2))]
+    hw += [(4096, 4096), (1540, 1540), (1, 1), (1, 32768), (32768, 17), (300, 200), (1000, 4000)]
+    for L, g in [(1540, 28), (1024, 16), (1540, 14), (97, 5), (28, 28)]:
+        got = T.resize_target(hw, L, g)
+        want = [O.resize_target(h, w, L, g) for h, w in hw]
+        assert got == want, (L, g)
+
+
+def test_resize_target_errors():
+    lib = T.load_library()
+    dst = (C.c_int32 * 4)()
+    for hw, L, g, status in [([(0, 5)], 1540, 28, -2), ([(5, 32769)], 1540, 28, -2), ([(5, 5)], 20, 28, -1),
+                             ([(5, 5)], 1540, 0, -1)]:
+        arr, n = T._hw_array(hw)
+        assert lib.pv_resize_target(arr, n, L, g, dst) == status
+        assert lib.pv_last_error()
+    arr, n = T._hw_array([(5, 5)])
+    assert lib.pv_resize_target(arr, 0, 1540, 28, dst) == -1
+    assert lib.pv_resize_target(None, 1, 1540, 28, dst) == -1
+    assert lib.pv_resize_target(arr, 1, 1540, 28, None) == -1
+
+
+def test_plan_u8_targets_and_workspace(tower_handle):
+    lib, h, cfg = tower_handle
+    src = [(4096, 4096), (300, 200), (1000, 4000), (1, 1)]
+    arr, n = T._hw_array(src)
+    dst = (C.c_int32 * (2 * n))()
+    info = T.PvPlanInfo()
+    assert lib.pv_tower_plan_u8(h, arr, n, dst, C.byref(info)) == 0
+    tgt = [(dst[2 * i], dst[2 * i + 1]) for i in range(n)]
+    assert tgt == [O.resize_target(a, b, 1540, 28) for a, b in src]
+    st, ref = _plan(lib, h, tgt)
+    assert st == 0
+    for f in ("n_patches", "out_rows", "out_cols", "workspace_bytes", "max_patches"):
+        assert getattr(info, f) == getattr(ref, f), f
+    assert lib.pv_tower_plan_u8(h, arr, n, None, C.byref(info)) == 0
+    bad, nb = T._hw_array([(40000, 10)])
+    assert lib.pv_tower_plan_u8(h, bad, nb, None, C.byref(info)) == -2
+
+
+def test_forward_u8_and_preprocess_validation_before_device_work(tower_handle):
+    lib, h, cfg = tower_handle
+    src = [(100, 150)]
+    arr, n = T._hw_array(src)
+    info = T.PvPlanInfo()
+    assert lib.pv_tower_plan_u8(h, arr, n, None, C.byref(info)) == 0
+    big = 1 << 40
+    ws = FAKE * 256
+    ok_ms = (C.c_float * 6)(0.5, 0.5, 0.5, 0.25, 0.25, 0.25)
+    bad_ms = (C.c_float * 6)(0.5, 0.5, 0.5, 0.25, 0.0, 0.25)
+    f = lib.pv_tower_forward_u8
+    assert f(None, FAKE, arr, n, None, FAKE, 99, ws, big, None) == -1
+    assert f(h, None, arr, n, None, FAKE, 99, ws, big, None) == -1
+    assert f(h, FAKE, None, n, None, FAKE, 99, ws, big, None) == -1
+    assert f(h, FAKE, arr, 0, None, FAKE, 99, ws, big, None) == -1
+    assert f(h, FAKE, arr, n, bad_ms, FAKE, 99, ws, big, None) == -1
+    assert f(h, FAKE, arr, n, ok_ms, FAKE + 8, 99, ws, big, None) == -1       # output alignment
+    assert f(h, FAKE, arr, n, None, FAKE, 99, ws + 16, big, None) == -1        # workspace alignment
+    assert f(h, FAKE, arr, n, None, FAKE, info.out_rows - 1, ws, big, None) == -3
+    assert f(h, FAKE, arr, n, None, FAKE, info.out_rows, ws, info.workspace_bytes - 1, None) == -3
+    zero, nz = T._hw_array([(0, 10)])
+    assert f(h, FAKE, zero, nz, None, FAKE, 99, ws, big, None) == -2
+    p = lib.pv_preprocess_u8
+    d, _ = T._hw_array([(28, 28)])
+    assert p(None, arr, d, 1, None, FAKE, None) == -1
+    assert p(FAKE, arr, None, 1, None, FAKE, None) == -1
+    assert p(FAKE, arr, d, 0, None, FAKE, None) == -1
+    assert p(FAKE, arr, d, 1, bad_ms, FAKE, None) == -1
+    assert p(FAKE, arr, d, 1, None, FAKE + 2, None) == -1
+    d0, _ = T._hw_array([(28, 0)])
+    assert p(FAKE, arr, d0, 1, None, FAKE, None) == -2
+    assert p(FAKE, zero, d, 1, None, FAKE, None) == -2

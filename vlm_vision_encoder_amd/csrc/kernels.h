@@ -79,6 +79,18 @@ hipError_t f32_to_bf16(const float* x, void* y, size_t n, hipStream_t s);
 hipError_t im2col_split(const float* pixels, const DevMaps& maps, void* out, int n_patches, int K, int Kp,
                         hipStream_t s);
 hipError_t split_rows(const float* x, void* out, int rows, int D, hipStream_t s);
+// Resize + normalisation of uint8 H x W x 3 images: value = raw * mul[c] +
+// add[c] after a half-pixel-centre bilinear resample to the plan's size.
+struct NormAff {
+  float mul[3], add[3];
+};
+//   im2col_u8_split: as im2col_split, with the pixels sampled from the uint8
+//                    source images src[] (device) of the plan's images
+//   resize_norm_u8:  one image -> fp32 planes [3][tH][tW]
+hipError_t im2col_u8_split(const uint8_t* images, const SrcImage* src, const DevMaps& maps, const NormAff& aff,
+                           void* out, int n_patches, int K, int Kp, hipStream_t s);
+hipError_t resize_norm_u8(const uint8_t* image, int sH, int sW, int tH, int tW, const NormAff& aff, float* out,
+                          hipStream_t s);
 hipError_t pad_rows(const void* w, void* out, int rows, int K, int Kp, hipStream_t s);
 //   gateup_fp8:   b8 [2F][D] fp8 e4m3 = the gate/up weights in the GEMM's
 //                 interleaved row order, bs [D/128][2F][4] scale bytes

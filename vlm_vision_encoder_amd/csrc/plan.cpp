@@ -84,6 +84,8 @@ int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, P
   off = align256(off + sizeof(AttnItem) * pl.items.size());
   L.rope = off;
   off = align256(off + sizeof(float) * 2 * 2 * size_t(pl.rope_maxpos) * p.rope_pairs);
+  L.src = off;
+  off = align256(off + sizeof(SrcImage) * n_images);
   L.upload_bytes = off;
   L.rowinfo = off;
   off = align256(off + sizeof(int32_t) * 2 * size_t(patches));
@@ -97,6 +99,8 @@ int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, P
   L.big = off;  // also: im2col hi | lo [N][2 Kp] and the final residual's hi | lo [N][2D] (bf16 tower)
   size_t big_row = std::max(3 * D, size_t(p.mlp)) * p.elem_bytes;
   if (p.elem_bytes == 2) big_row = std::max(big_row, std::max(size_t(4) * patch_kp(p.patch), 4 * D));
+  // fp32 tower from uint8 input: the resized, normalised planes (3 p^2 fp32 per patch)
+  if (p.elem_bytes == 4) big_row = std::max(big_row, size_t(12) * p.patch * p.patch);
   off = align256(off + N * big_row);
   L.wpad = off;
   off = align256(off + (p.elem_bytes == 2 ? D * size_t(patch_kp(p.patch)) * 2 : 0));
@@ -112,6 +116,29 @@ int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, P
     off = align256(off + (D / 128) * F2 * 4);
   }
   L.total = off;
+  return 0;
+}
+
+int resize_target(int32_t h, int32_t w, int32_t longest_edge, int32_t grid, int32_t* th, int32_t* tw,
+                  std::string* err) {
+  if (grid < 1 || longest_edge < grid) {
+    *err = "grid must be >= 1 and longest_edge >= grid";
+    return -1;
+  }
+  if (h < 1 || w < 1 || h > kMaxSrcSide || w > kMaxSrcSide) {
+    *err = "source image " + std::to_string(h) + "x" + std::to_string(w) + ": each side must be in [1, " +
+           std::to_string(kMaxSrcSide) + "]";
+    return -2;
+  }
+  const int64_t L = longest_edge, g = grid, m = std::max(h, w);
+  int64_t a = h, b = w;
+  if (m > L) {  // fit: shrink so the longest side is longest_edge
+    a = std::max<int64_t>(1, a * L / m);
+    b = std::max<int64_t>(1, b * L / m);
+  }
+  const int64_t cap = L / g * g;  // then onto the grid
+  *th = int32_t(std::min((a + g - 1) / g * g, cap));
+  *tw = int32_t(std::min((b + g - 1) / g * g, cap));
   return 0;
 }
 

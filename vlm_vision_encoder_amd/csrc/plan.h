@@ -25,6 +25,17 @@ struct ImageMeta {
 };
 static_assert(sizeof(ImageMeta) == 32, "ImageMeta layout");
 
+// Source of one uint8 image (H x W x 3, channel fastest) for the resize in
+// the patch embedding's A load; uploaded after the rotary table (16 bytes).
+struct SrcImage {
+  int32_t H, W;             // source pixels
+  uint32_t off_lo, off_hi;  // 64-bit byte offset of the image in the uint8 buffer
+};
+static_assert(sizeof(SrcImage) == 16, "SrcImage layout");
+
+// Largest source side the resize accepts (its tap arithmetic is 32-bit).
+constexpr int32_t kMaxSrcSide = 32768;
+
 // One attention work item: q-tile starting at local query q0 of an image.
 struct AttnItem {
   int32_t image;
@@ -52,7 +63,7 @@ inline int32_t patch_kp(int32_t patch) { return (3 * patch * patch + 63) / 64 * 
 
 // Byte offsets into the device workspace (all 256-byte aligned).
 struct Layout {
-  size_t meta = 0, items = 0, rope = 0, rowinfo = 0, msrc = 0;
+  size_t meta = 0, items = 0, rope = 0, src = 0, rowinfo = 0, msrc = 0;
   size_t r = 0, y = 0, big = 0;
   size_t wpad = 0;          // bf16 tower: patch weights zero-padded to [D][Kp]
   // bf16 tower, MLP input's fp8 low part and the gate/up weights in fp8:
@@ -70,8 +81,18 @@ struct Plan {
   std::vector<ImageMeta> meta;
   std::vector<int32_t> cu;  // n_images + 1
   std::vector<AttnItem> items;
+  std::vector<SrcImage> src;  // uint8 input only (else empty; the region is zeroed)
   Layout ws;
 };
+
+// Target size of the resize onto the patch grid: if max(h, w) > longest_edge
+// each side becomes floor(side * longest_edge / max(h, w)) (at least 1;
+// images are never enlarged), then is rounded up to a multiple of `grid`,
+// capped at the largest multiple of `grid` within longest_edge.  Exact
+// integer arithmetic.  Returns 0, -1 (grid < 1 or longest_edge < grid) or -2
+// (a side outside [1, kMaxSrcSide]) with *err set.
+int resize_target(int32_t h, int32_t w, int32_t longest_edge, int32_t grid, int32_t* th, int32_t* tw,
+                  std::string* err);
 
 // Returns 0 on success, -1 (argument) or -2 (shape) with *err set.
 int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, Plan* out,

@@ -11,6 +11,14 @@
 //                 gather 2x2 straight from this copy.
 //   pad_rows:     copy of a bf16 matrix with its rows zero-padded (patch
 //                 weights [D][3p^2] -> [D][Kp]).
+//   im2col_u8_split: the same A operand straight from uint8 H x W x 3 images:
+//                 each pixel of the resized image is a bilinear sample of the
+//                 source ("Mistral 3" page: images are resized so the longest
+//                 edge fits and the sides stay on the patch grid; pixel
+//                 centres at half-integers, no antialiasing), then x / 255 and
+//                 (x - mean_c) / std_c (Mistral3ImageProcessor table), folded
+//                 into one multiply-add per channel.
+//   resize_norm_u8: the same samples written out as fp32 planes.
 //   gateup_fp8:   fp8 e4m3 copy of the gate/up weights in the GEMM's
 //                 interleaved row order, one power-of-two scale per 32 k, for
 //                 the fp8 product with the MLP input's low part.
@@ -30,6 +38,38 @@ __device__ __forceinline__ void split8(const float (&f)[8], u32x4& hi, u32x4& lo
     r[2 * e + 1] = f[2 * e + 1] - hi_bf16(hi[e]);
   }
   lo = pack8(r);
+}
+
+// Taps of output index t when n_in source pixels are resampled to n_out:
+// the source coordinate is ((2t + 1) n_in - n_out) / (2 n_out), clamped below
+// at 0; taps i0 = floor, i1 = min(i0 + 1, n_in - 1), weight f of i1.  The
+// integer form picks the taps exactly (sides <= 32768 keep it in 32 bits).
+__device__ __forceinline__ void bilinear_taps(uint32_t t, uint32_t n_in, uint32_t n_out, uint32_t& i0,
+                                              uint32_t& i1, float& f) {
+  const uint32_t num = (2u * t + 1u) * n_in, den = 2u * n_out;
+  if (num <= n_out) {
+    i0 = 0;
+    f = 0.f;
+  } else {
+    const uint32_t e = num - n_out;
+    i0 = e / den;
+    f = float(e - i0 * den) / float(den);
+  }
+  i1 = i0 + 1 < n_in ? i0 + 1 : n_in - 1;
+}
+
+// Normalised value of channel c at resized pixel (ty, tx).
+__device__ __forceinline__ float sample_u8(const uint8_t* __restrict__ img, uint32_t sH, uint32_t sW, uint32_t tH,
+                                           uint32_t tW, uint32_t ty, uint32_t tx, int c, float mul, float add) {
+  uint32_t y0, y1, x0, x1;
+  float fy, fx;
+  bilinear_taps(ty, sH, tH, y0, y1, fy);
+  bilinear_taps(tx, sW, tW, x0, x1, fx);
+  const uint8_t* r0 = img + size_t(y0) * sW * 3 + c;
+  const uint8_t* r1 = img + size_t(y1) * sW * 3 + c;
+  const float a = r0[x0 * 3], b = r0[x1 * 3], cc = r1[x0 * 3], d = r1[x1 * 3];
+  const float top = a + fx * (b - a), bot = cc + fx * (d - cc);
+  return (top + fy * (bot - top)) * mul + add;
 }
 
 // One thread per (patch g, 8 consecutive k).
@@ -62,6 +102,53 @@ __global__ __launch_bounds__(256) void im2col_split_kernel(const float* __restri
   uint16_t* row = out + size_t(g) * 2 * Kp;
   *reinterpret_cast<u32x4*>(row + k0) = hi;
   *reinterpret_cast<u32x4*>(row + Kp + k0) = lo;
+}
+
+// One thread per (patch g, 8 consecutive k); the image is sampled from its
+// uint8 source.
+__global__ __launch_bounds__(256) void im2col_u8_split_kernel(const uint8_t* __restrict__ images,
+                                                              const SrcImage* __restrict__ srcs, DevMaps maps,
+                                                              NormAff aff, uint16_t* __restrict__ out,
+                                                              int n_patches, int K, int Kp) {
+  const int chunks = Kp / 8;
+  const long long idx = blockIdx.x * 256ll + threadIdx.x;
+  if (idx >= (long long)n_patches * chunks) return;
+  const int g = int(idx / chunks), k0 = int(idx - (long long)g * chunks) * 8;
+  const int img = maps.rowinfo[2 * g], rc = maps.rowinfo[2 * g + 1];
+  const ImageMeta mt = maps.meta[img];
+  const SrcImage sm = srcs[img];
+  const uint8_t* src = images + ((uint64_t(sm.off_hi) << 32) | sm.off_lo);
+  const int p = maps.patch, pp = p * p;
+  const int pr = rc >> 16, pc = rc & 0xffff;
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int k = k0 + e;
+    float v = 0.f;
+    if (k < K) {
+      const int ch = k / pp, rem = k - ch * pp;
+      const int u = rem / p, x = rem - u * p;
+      v = sample_u8(src, sm.H, sm.W, mt.H, mt.W, pr * p + u, pc * p + x, ch, aff.mul[ch], aff.add[ch]);
+    }
+    f[e] = v;
+  }
+  u32x4 hi, lo;
+  split8(f, hi, lo);
+  uint16_t* row = out + size_t(g) * 2 * Kp;
+  *reinterpret_cast<u32x4*>(row + k0) = hi;
+  *reinterpret_cast<u32x4*>(row + Kp + k0) = lo;
+}
+
+// One thread per resized pixel (all three channels).
+__global__ __launch_bounds__(256) void resize_norm_u8_kernel(const uint8_t* __restrict__ img, int sH, int sW,
+                                                             int tH, int tW, NormAff aff, float* __restrict__ out) {
+  const long long idx = blockIdx.x * 256ll + threadIdx.x;
+  const long long plane = (long long)tH * tW;
+  if (idx >= plane) return;
+  const int ty = int(idx / tW), tx = int(idx - (long long)ty * tW);
+#pragma unroll
+  for (int c = 0; c < 3; ++c)
+    out[c * plane + idx] = sample_u8(img, sH, sW, tH, tW, ty, tx, c, aff.mul[c], aff.add[c]);
 }
 
 // One thread per 8 consecutive values of a row.
@@ -142,6 +229,25 @@ hipError_t im2col_split(const float* pixels, const DevMaps& maps, void* out, int
   if (Kp % 8 || K > Kp) return hipErrorInvalidValue;
   hipLaunchKernelGGL(im2col_split_kernel, grid_for((long long)n_patches * (Kp / 8)), dim3(256), 0, s, pixels, maps,
                      static_cast<uint16_t*>(out), n_patches, K, Kp);
+  return hipGetLastError();
+}
+
+hipError_t im2col_u8_split(const uint8_t* images, const SrcImage* src, const DevMaps& maps, const NormAff& aff,
+                           void* out, int n_patches, int K, int Kp, hipStream_t s) {
+  if (n_patches <= 0) return hipSuccess;
+  if (Kp % 8 || K > Kp || K != 3 * maps.patch * maps.patch) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(im2col_u8_split_kernel, grid_for((long long)n_patches * (Kp / 8)), dim3(256), 0, s, images,
+                     src, maps, aff, static_cast<uint16_t*>(out), n_patches, K, Kp);
+  return hipGetLastError();
+}
+
+hipError_t resize_norm_u8(const uint8_t* image, int sH, int sW, int tH, int tW, const NormAff& aff, float* out,
+                          hipStream_t s) {
+  if (sH < 1 || sW < 1 || tH < 1 || tW < 1 || sH > kMaxSrcSide || sW > kMaxSrcSide || tH > kMaxSrcSide ||
+      tW > kMaxSrcSide)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(resize_norm_u8_kernel, grid_for((long long)tH * tW), dim3(256), 0, s, image, sH, sW, tH, tW,
+                     aff, out);
   return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -47,6 +48,33 @@ pv_status fail(pv_status s, const std::string& msg) {
   } while (0)
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Per-channel (R, G, B) normalisation of the Mistral 3 image processor
+// ("Mistral 3" (KerasFormers), Mistral3ImageProcessor table): on x / 255.
+constexpr float kProcessorMean[3] = {0.48145466f, 0.4578275f, 0.40821073f};
+constexpr float kProcessorStd[3] = {0.26862954f, 0.26130258f, 0.27577711f};
+
+// mean_std: host [6] = mean (R, G, B), std (R, G, B), or null for the
+// processor's values.  Folded as raw * mul + add (mul = 1 / (255 std),
+// add = -mean / std), computed in double and rounded once.
+bool norm_affine(const float* mean_std, pv::NormAff* a) {
+  for (int c = 0; c < 3; ++c) {
+    const double m = mean_std ? mean_std[c] : kProcessorMean[c];
+    const double sd = mean_std ? mean_std[3 + c] : kProcessorStd[c];
+    if (!(sd > 0.0) || !std::isfinite(m) || !std::isfinite(sd)) return false;
+    a->mul[c] = float(1.0 / (255.0 * sd));
+    a->add[c] = float(-m / sd);
+  }
+  return true;
+}
+
+// Where the patch embedding takes its pixels from: normalised fp32 planes, or
+// uint8 H x W x 3 source images resized in the A-operand load.
+struct PixelSource {
+  const float* f32 = nullptr;
+  const uint8_t* u8 = nullptr;
+  pv::NormAff aff{};
+};
 
 }  // namespace
 
@@ -139,6 +167,7 @@ pv_status upload_and_maps(pv_tower* t, const pv::Plan& plan, char* ws, hipStream
   std::memcpy(h + L.meta, plan.meta.data(), sizeof(pv::ImageMeta) * plan.meta.size());
   std::memcpy(h + L.items, plan.items.data(), sizeof(pv::AttnItem) * plan.items.size());
   std::memcpy(h + L.rope, t->rope.data(), sizeof(float) * t->rope.size());
+  if (!plan.src.empty()) std::memcpy(h + L.src, plan.src.data(), sizeof(pv::SrcImage) * plan.src.size());
   PV_HIP(hipMemcpyAsync(ws, h, L.upload_bytes, hipMemcpyHostToDevice, s));
   PV_HIP(hipEventRecord(t->upload_done, s));
   t->upload_pending = true;
@@ -163,7 +192,7 @@ pv_status copy_stage(const StageStop& st, const void* src, size_t bytes, hipStre
   return PV_OK;
 }
 
-pv_status run_tower(pv_tower* t, const float* pixels, const pv::Plan& plan, void* out, char* ws,
+pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, void* out, char* ws,
                     const StageStop& st, hipStream_t s) {
   const pv_config& c = t->cfg;
   const bool bf = c.dtype == PV_BF16;
@@ -192,7 +221,11 @@ pv_status run_tower(pv_tower* t, const float* pixels, const pv::Plan& plan, void
     const int Kpatch = 3 * c.patch * c.patch, Kp = pv::patch_kp(c.patch);
     void* wpad = ws + L.wpad;
     PV_LAUNCH(PV_K_PATCH, pv::pad_rows(t->w.patch_w, wpad, D, Kpatch, Kp, s));
-    PV_LAUNCH(PV_K_PATCH, pv::im2col_split(pixels, g.maps, big, N, Kpatch, Kp, s));
+    if (px.u8)
+      PV_LAUNCH(PV_K_PATCH, pv::im2col_u8_split(px.u8, reinterpret_cast<const pv::SrcImage*>(ws + L.src), g.maps,
+                                                 px.aff, big, N, Kpatch, Kp, s));
+    else
+      PV_LAUNCH(PV_K_PATCH, pv::im2col_split(px.f32, g.maps, big, N, Kpatch, Kp, s));
     pv::GemmArgs a = g;
     a.M = N; a.N = D; a.K = 2 * Kp; a.kb = Kp;
     a.A = big; a.lda = 2 * Kp;
@@ -200,6 +233,18 @@ pv_status run_tower(pv_tower* t, const float* pixels, const pv::Plan& plan, void
     a.C = r; a.ldc = D;
     PV_LAUNCH(PV_K_PATCH, gemm(pv::GEMM_PATCH, a));
   } else {
+    const float* pixels = px.f32;
+    if (px.u8) {  // resized, normalised planes of every image into the big buffer first
+      float* planes = reinterpret_cast<float*>(big);
+      for (int i = 0; i < plan.n_images; ++i) {
+        const pv::ImageMeta& m = plan.meta[i];
+        const pv::SrcImage& sm = plan.src[i];
+        const size_t off = (size_t(m.pix_hi) << 32) | m.pix_lo;
+        const size_t soff = (size_t(sm.off_hi) << 32) | sm.off_lo;
+        PV_LAUNCH(PV_K_PATCH, pv::resize_norm_u8(px.u8 + soff, sm.H, sm.W, m.H, m.W, px.aff, planes + off, s));
+      }
+      pixels = planes;
+    }
     pv::GemmArgs a = g;
     a.M = N; a.N = D; a.K = 3 * c.patch * c.patch;
     a.pixels = pixels;
@@ -312,6 +357,44 @@ pv_status run_tower(pv_tower* t, const float* pixels, const pv::Plan& plan, void
   return PV_OK;
 }
 
+// Target sizes of uint8 source images for this tower (longest edge = max_side,
+// grid = patch * merge), the plan of those sizes, and the source offsets.
+pv_status make_plan_u8(const pv_tower* t, const int32_t* src_hw, int32_t n, pv::Plan* plan,
+                       std::vector<int32_t>* dst_hw) {
+  if (!src_hw) return fail(PV_ERR_ARG, "src_hw must not be null");
+  if (n < 1) return fail(PV_ERR_ARG, "n_images must be >= 1 (the tower runs only on image input)");
+  dst_hw->assign(size_t(2) * n, 0);
+  std::string err;
+  for (int32_t i = 0; i < n; ++i) {
+    const int rc = pv::resize_target(src_hw[2 * i], src_hw[2 * i + 1], t->cfg.max_side, t->cfg.patch * t->cfg.merge,
+                                     &(*dst_hw)[2 * i], &(*dst_hw)[2 * i + 1], &err);
+    if (rc == -1) return fail(PV_ERR_ARG, err);
+    if (rc == -2) return fail(PV_ERR_SHAPE, "image " + std::to_string(i) + ": " + err);
+  }
+  pv_status st = make_plan(t, dst_hw->data(), n, plan);
+  if (st != PV_OK) return st;
+  plan->src.resize(n);
+  uint64_t off = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    pv::SrcImage& sm = plan->src[i];
+    sm.H = src_hw[2 * i];
+    sm.W = src_hw[2 * i + 1];
+    sm.off_lo = uint32_t(off & 0xffffffffu);
+    sm.off_hi = uint32_t(off >> 32);
+    off += uint64_t(3) * uint64_t(sm.H) * uint64_t(sm.W);
+  }
+  return PV_OK;
+}
+
+void fill_info(const pv_tower* t, const pv::Plan& plan, pv_plan_info* info) {
+  info->n_patches = plan.n_patches;
+  info->out_rows = plan.out_rows;
+  info->out_cols = t->cfg.merge == 2 ? t->cfg.out_dim : t->cfg.hidden;
+  info->workspace_bytes = int64_t(plan.ws.total);
+  info->n_images = plan.n_images;
+  info->max_patches = plan.max_patches;
+}
+
 pv_status check_call(const pv_tower* t, const float* pixels, const int32_t* image_hw, int32_t n, const void* dst,
                      const void* ws) {
   if (!t) return fail(PV_ERR_ARG, "tower is null");
@@ -410,12 +493,88 @@ pv_status pv_tower_plan(const pv_tower* t, const int32_t* image_hw, int32_t n_im
   pv::Plan plan;
   pv_status st = make_plan(t, image_hw, n_images, &plan);
   if (st != PV_OK) return st;
-  info->n_patches = plan.n_patches;
-  info->out_rows = plan.out_rows;
-  info->out_cols = t->cfg.merge == 2 ? t->cfg.out_dim : t->cfg.hidden;
-  info->workspace_bytes = int64_t(plan.ws.total);
-  info->n_images = plan.n_images;
-  info->max_patches = plan.max_patches;
+  fill_info(t, plan, info);
+  return PV_OK;
+}
+
+pv_status pv_resize_target(const int32_t* src_hw, int32_t n_images, int32_t longest_edge, int32_t grid,
+                           int32_t* dst_hw) {
+  g_last_error.clear();
+  if (!src_hw || !dst_hw) return fail(PV_ERR_ARG, "src_hw and dst_hw must not be null");
+  if (n_images < 1) return fail(PV_ERR_ARG, "n_images must be >= 1");
+  std::string err;
+  for (int32_t i = 0; i < n_images; ++i) {
+    int32_t th = 0, tw = 0;
+    const int rc = pv::resize_target(src_hw[2 * i], src_hw[2 * i + 1], longest_edge, grid, &th, &tw, &err);
+    if (rc == -1) return fail(PV_ERR_ARG, err);
+    if (rc == -2) return fail(PV_ERR_SHAPE, "image " + std::to_string(i) + ": " + err);
+    dst_hw[2 * i] = th;
+    dst_hw[2 * i + 1] = tw;
+  }
+  return PV_OK;
+}
+
+pv_status pv_tower_plan_u8(const pv_tower* t, const int32_t* src_hw, int32_t n_images, int32_t* dst_hw,
+                           pv_plan_info* info) {
+  g_last_error.clear();
+  if (!t || !info) return fail(PV_ERR_ARG, "tower and info must not be null");
+  pv::Plan plan;
+  std::vector<int32_t> hw;
+  pv_status st = make_plan_u8(t, src_hw, n_images, &plan, &hw);
+  if (st != PV_OK) return st;
+  if (dst_hw) std::memcpy(dst_hw, hw.data(), sizeof(int32_t) * hw.size());
+  fill_info(t, plan, info);
+  return PV_OK;
+}
+
+pv_status pv_tower_forward_u8(pv_tower* t, const uint8_t* images, const int32_t* src_hw, int32_t n_images,
+                              const float* mean_std, void* out, int64_t out_rows_cap, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!t) return fail(PV_ERR_ARG, "tower is null");
+  if (!images || !out || !workspace) return fail(PV_ERR_ARG, "images, output and workspace must not be null");
+  if (!aligned(out, 16)) return fail(PV_ERR_ARG, "output must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(PV_ERR_ARG, "workspace must be 256-byte aligned");
+  PixelSource px;
+  px.u8 = images;
+  if (!norm_affine(mean_std, &px.aff)) return fail(PV_ERR_ARG, "mean_std must be finite with std > 0");
+  pv::Plan plan;
+  std::vector<int32_t> hw;
+  pv_status st = make_plan_u8(t, src_hw, n_images, &plan, &hw);
+  if (st != PV_OK) return st;
+  if (out_rows_cap < plan.out_rows)
+    return fail(PV_ERR_CAPACITY, "out_rows_cap " + std::to_string(out_rows_cap) + " < " + std::to_string(plan.out_rows));
+  if (ws_bytes < plan.ws.total)
+    return fail(PV_ERR_CAPACITY, "workspace " + std::to_string(ws_bytes) + " < " + std::to_string(plan.ws.total));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if ((st = upload_and_maps(t, plan, ws, s)) != PV_OK) return st;
+  return run_tower(t, px, plan, out, ws, StageStop(), s);
+}
+
+pv_status pv_preprocess_u8(const uint8_t* images, const int32_t* src_hw, const int32_t* dst_hw, int32_t n_images,
+                           const float* mean_std, float* out, void* stream) {
+  g_last_error.clear();
+  if (!images || !src_hw || !dst_hw || !out) return fail(PV_ERR_ARG, "images, src_hw, dst_hw and out must not be null");
+  if (n_images < 1) return fail(PV_ERR_ARG, "n_images must be >= 1");
+  if (!aligned(out, 4)) return fail(PV_ERR_ARG, "out must be 4-byte aligned");
+  pv::NormAff aff;
+  if (!norm_affine(mean_std, &aff)) return fail(PV_ERR_ARG, "mean_std must be finite with std > 0");
+  for (int32_t i = 0; i < n_images; ++i) {
+    const int32_t v[4] = {src_hw[2 * i], src_hw[2 * i + 1], dst_hw[2 * i], dst_hw[2 * i + 1]};
+    for (int32_t x : v)
+      if (x < 1 || x > pv::kMaxSrcSide)
+        return fail(PV_ERR_SHAPE, "image " + std::to_string(i) + ": every side must be in [1, " +
+                                      std::to_string(pv::kMaxSrcSide) + "]");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  size_t soff = 0, doff = 0;
+  for (int32_t i = 0; i < n_images; ++i) {
+    const int32_t sH = src_hw[2 * i], sW = src_hw[2 * i + 1], tH = dst_hw[2 * i], tW = dst_hw[2 * i + 1];
+    PV_HIP(pv::resize_norm_u8(images + soff, sH, sW, tH, tW, aff, out + doff, s));
+    soff += size_t(3) * sH * sW;
+    doff += size_t(3) * tH * tW;
+  }
   return PV_OK;
 }
 
@@ -433,7 +592,9 @@ pv_status pv_tower_forward(pv_tower* t, const float* pixels, const int32_t* imag
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if ((st = upload_and_maps(t, plan, ws, s)) != PV_OK) return st;
-  return run_tower(t, pixels, plan, out, ws, StageStop(), s);
+  PixelSource px;
+  px.f32 = pixels;
+  return run_tower(t, px, plan, out, ws, StageStop(), s);
 }
 
 pv_status pv_tower_forward_stage(pv_tower* t, const float* pixels, const int32_t* image_hw, int32_t n_images,
@@ -464,7 +625,9 @@ pv_status pv_tower_forward_stage(pv_tower* t, const float* pixels, const int32_t
   stop.layer = stage >= PV_STAGE_QKV ? layer : -1;
   stop.dst = dst;
   stop.dst_bytes = dst_bytes;
-  return run_tower(t, pixels, plan, nullptr, ws, stop, s);
+  PixelSource px;
+  px.f32 = pixels;
+  return run_tower(t, px, plan, nullptr, ws, stop, s);
 }
 
 pv_status pv_tower_index_maps(pv_tower* t, const int32_t* image_hw, int32_t n_images, int32_t* cu_seqlens,

@@ -21,7 +21,8 @@ STATUS = {0: "PV_OK", -1: "PV_ERR_ARG", -2: "PV_ERR_SHAPE", -3: "PV_ERR_CAPACITY
 
 EXPORTED = ("pv_tower_create", "pv_tower_destroy", "pv_tower_plan", "pv_tower_forward",
             "pv_tower_forward_stage", "pv_tower_index_maps", "pv_tower_set_profiling", "pv_tower_read_profile",
-            "pv_scatter_workspace_bytes", "pv_scatter_image_embeddings", "pv_last_error", "pv_status_str")
+            "pv_scatter_workspace_bytes", "pv_scatter_image_embeddings", "pv_resize_target", "pv_tower_plan_u8",
+            "pv_tower_forward_u8", "pv_preprocess_u8", "pv_last_error", "pv_status_str")
 KERNEL_CLASSES = ("maps", "patch", "norm", "qkv", "attn", "oproj", "gateup", "down", "merge")
 
 
@@ -86,6 +87,14 @@ def load_library(path: str = LIB_PATH):
     lib.pv_scatter_workspace_bytes.restype = sz
     lib.pv_scatter_image_embeddings.argtypes = [vp, i64, i32, vp, i64, vp, i32, i32, vp, vp, sz, vp]
     lib.pv_scatter_image_embeddings.restype = i32
+    lib.pv_resize_target.argtypes = [vp, i32, i32, i32, vp]
+    lib.pv_resize_target.restype = i32
+    lib.pv_tower_plan_u8.argtypes = [vp, vp, i32, vp, C.POINTER(PvPlanInfo)]
+    lib.pv_tower_plan_u8.restype = i32
+    lib.pv_tower_forward_u8.argtypes = [vp, vp, vp, i32, vp, vp, i64, vp, sz, vp]
+    lib.pv_tower_forward_u8.restype = i32
+    lib.pv_preprocess_u8.argtypes = [vp, vp, vp, i32, vp, vp, vp]
+    lib.pv_preprocess_u8.restype = i32
     lib.pv_last_error.argtypes = []
     lib.pv_last_error.restype = C.c_char_p
     lib.pv_status_str.argtypes = [i32]
@@ -195,6 +204,29 @@ class Tower:
         _check(self.lib.pv_tower_forward(self.handle, pixels_ptr, arr, n, out_ptr, out_rows_cap, ws_ptr,
                                          ws_bytes, stream))
 
+    # ------------------------------------------------------------ uint8 input
+    def plan_u8(self, src_hw) -> Tuple[PvPlanInfo, List[Tuple[int, int]]]:
+        """Plan of uint8 sources: (info, target sizes)."""
+        arr, n = _hw_array(src_hw)
+        dst = (C.c_int32 * (2 * n))()
+        info = PvPlanInfo()
+        _check(self.lib.pv_tower_plan_u8(self.handle, arr, n, dst, C.byref(info)))
+        return info, [(dst[2 * i], dst[2 * i + 1]) for i in range(n)]
+
+    def forward_u8(self, images, src_hw, mean_std=None, out=None, stream=None):
+        """images: flat uint8 CUDA tensor of the H x W x 3 images in order."""
+        import torch
+        arr, n = _hw_array(src_hw)
+        info, _ = self.plan_u8(src_hw)
+        if out is None:
+            out = torch.empty((info.out_rows, info.out_cols), dtype=self._out_dtype(), device="cuda")
+        ws = self.workspace(info.workspace_bytes)
+        s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+        ms = (C.c_float * 6)(*mean_std) if mean_std is not None else None
+        _check(self.lib.pv_tower_forward_u8(self.handle, images.data_ptr(), arr, n, ms, out.data_ptr(),
+                                            out.shape[0], ws.data_ptr(), ws.numel(), s))
+        return out
+
     def set_profiling(self, enable: bool):
         _check(self.lib.pv_tower_set_profiling(self.handle, 1 if enable else 0))
 
@@ -270,6 +302,31 @@ def scatter_image_embeddings(token_ids, image_emb, text_emb, image_token_id: int
                                            status.data_ptr(), ws.data_ptr(), wsb,
                                            torch.cuda.current_stream().cuda_stream))
     return status
+
+
+def resize_target(src_hw, longest_edge: int, grid: int) -> List[Tuple[int, int]]:
+    """Target sizes of the resize onto the patch grid (host only)."""
+    lib = load_library()
+    arr, n = _hw_array(src_hw)
+    dst = (C.c_int32 * (2 * n))()
+    _check(lib.pv_resize_target(arr, n, int(longest_edge), int(grid), dst))
+    return [(dst[2 * i], dst[2 * i + 1]) for i in range(n)]
+
+
+def preprocess_u8(images, src_hw, dst_hw, mean_std=None, out=None):
+    """Resize + normalise uint8 images (flat CUDA tensor, H x W x 3 each) to
+    dst_hw; returns the flat fp32 CUDA tensor of the 3 x tH x tW planes."""
+    import torch
+    lib = load_library()
+    sa, n = _hw_array(src_hw)
+    da, _ = _hw_array(dst_hw)
+    total = sum(3 * int(h) * int(w) for h, w in dst_hw)
+    if out is None:
+        out = torch.empty(max(1, total), dtype=torch.float32, device=images.device)
+    ms = (C.c_float * 6)(*mean_std) if mean_std is not None else None
+    _check(lib.pv_preprocess_u8(images.data_ptr(), sa, da, n, ms, out.data_ptr(),
+                                torch.cuda.current_stream().cuda_stream))
+    return out[:total]
 
 
 # ---------------------------------------------------------------- helpers
