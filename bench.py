@@ -196,6 +196,55 @@ def time_scatter(out, wl, stream, reps=20):
             "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def time_u8_input(tw, wl, out, ws, stream, f32_patch_ms, reps=5):
+    """The uint8 input path on a 4096x4096 photo (resized to the workload's
+    1540x1540): the whole forward from uint8 (HIP events around `reps`
+    calls), its patch-embedding kernel class (fused resize + normalise +
+    hi|lo im2col, weight padding, GEMM) beside the float path's, and the
+    standalone preprocessing into fp32 planes.  Algorithmic bytes of the
+    standalone pass: the source image read once plus the planes written."""
+    import torch
+
+    from vlm_vision_encoder_amd import synth
+    from vlm_vision_encoder_amd import tower as T
+    src = [(4096, 4096)]
+    info, tgt = tw.plan_u8(src)
+    if tgt != list(wl.image_hw):
+        return None
+    img = torch.from_numpy(synth.make_u8_images(src, seed=3)[0].reshape(-1)).cuda()
+    sptr = stream.cuda_stream
+    tw.forward_u8(img, src, out=out, stream=sptr)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        tw.forward_u8(img, src, out=out, stream=sptr)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = e0.elapsed_time(e1) / reps
+    tw.set_profiling(True)
+    tw.forward_u8(img, src, out=out, stream=sptr)
+    torch.cuda.synchronize()
+    prof = tw.read_profile(reset=True)
+    tw.set_profiling(False)
+    planes = torch.empty(3 * tgt[0][0] * tgt[0][1], dtype=torch.float32, device="cuda")
+    T.preprocess_u8(img, src, tgt, out=planes)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        T.preprocess_u8(img, src, tgt, out=planes)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pre_ms = e0.elapsed_time(e1) / reps
+    nbytes = img.numel() + planes.numel() * 4
+    return {"source": "4096x4096 uint8 RGB", "target": list(tgt[0]), "forward_ms": round(fwd_ms, 4),
+            "patches_per_s": round(info.n_patches / (fwd_ms * 1e-3), 1),
+            "patch_class_ms": round(prof["patch"][0], 5), "patch_class_ms_float_input": f32_patch_ms,
+            "preprocess_planes_ms": round(pre_ms, 5),
+            "preprocess_planes_gbs": round(nbytes / (pre_ms * 1e-3) / 1e9, 1),
+            "preprocess_planes_hbm_frac": round(nbytes / (pre_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def source_sha256(path):
     import hashlib
     with open(path, "rb") as f:
@@ -329,6 +378,9 @@ def main():
                     "flops_per_launch": dom_flops_launch, "avg_launch_ms": dom_ms}
 
     scatter = time_scatter(out, wl, stream) if wl.merge == 2 else None
+    u8_input = None
+    if len(wl.image_hw) == 1 and "patch" in kernels:
+        u8_input = time_u8_input(tw, wl, out, ws, stream, kernels["patch"]["ms_per_step"])
 
     patches_s = wl.n_patches / (ms_step * 1e-3)
     tokens_s = wl.out_rows / (ms_step * 1e-3)
@@ -354,6 +406,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "scatter": scatter,
+        "u8_input": u8_input,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
