@@ -51,6 +51,12 @@ notes of the repository):
     values taken as reals (no re-quantisation after the resize).
 11. Normalisation: x / 255 then (x - mean_c) / std_c with the processor
     table's constants; uint8 pixels come in as H x W x 3 (RGB).
+12. Tiles ("Pixtral-12B-2409", VISION TOKENS: large images are split into
+    1024x1024 tiles, the tile count capped by ``max_num_tiles``): the image
+    is scaled by the largest s <= 1 whose tile grid ceil(sH/T) x ceil(sW/T)
+    has at most max_num_tiles tiles; each side becomes floor(s * side)
+    (at least 1), rounded up to the patch grid; tiles are cut row-major,
+    full T x T except the last row/column, which keep the remainder.
 
 Pinning: every function here is pinned in ``tests/test_oracle_pins.py`` by a
 check that does not reuse this code path (closed-form counts printed on the
@@ -399,6 +405,61 @@ def preprocess_batch(images: Sequence[np.ndarray], longest_edge: int, grid: int,
     hw = [resize_target(im.shape[0], im.shape[1], longest_edge, grid) for im in images]
     parts = [preprocess_image(im, th, tw, mean, std).reshape(-1) for im, (th, tw) in zip(images, hw)]
     return np.concatenate(parts), hw
+
+
+def tile_layout(h: int, w: int, tile: int, grid: int, max_num_tiles: int) -> Tuple[int, int, int, int]:
+    """(resized H, resized W, tile rows, tile columns) of one image.
+
+    "Pixtral-12B-2409", VISION TOKENS: tiles of ``tile`` x ``tile`` pixels
+    (a 4096x4096 image is a 4x4 grid); the processor caps the tile count with
+    ``max_num_tiles``.  Scale s = min(1, max over grids r x c with r*c <=
+    max_num_tiles of min(r*tile/H, c*tile/W)), exact fractions; each side
+    becomes max(1, floor(s * side)) rounded up to a multiple of ``grid``.
+    """
+    from fractions import Fraction
+    h, w, T, g, M = int(h), int(w), int(tile), int(grid), int(max_num_tiles)
+    if h <= 0 or w <= 0 or g <= 0 or T < g or T % g or M < 1:
+        raise ValueError("bad tile layout arguments")
+    best = Fraction(0)
+    for r in range(1, M + 1):
+        for c in range(1, M // r + 1):
+            best = max(best, min(Fraction(r * T, h), Fraction(c * T, w)))
+    s = min(Fraction(1), best)
+    rh = max(1, math.floor(s * h))
+    rw = max(1, math.floor(s * w))
+    rh = -(-rh // g) * g
+    rw = -(-rw // g) * g
+    return rh, rw, -(-rh // T), -(-rw // T)
+
+
+def tile_image(img_u8: np.ndarray, tile: int, grid: int, max_num_tiles: int,
+               mean: Sequence[float] = PROCESSOR_MEAN, std: Sequence[float] = PROCESSOR_STD):
+    """uint8 H x W x 3 image -> (list of float64 3 x th x tw tiles, their
+    sizes), row-major over the tile grid: the image resized to the
+    ``tile_layout`` size and normalised, then cut."""
+    img = np.asarray(img_u8)
+    rh, rw, rows, cols = tile_layout(img.shape[0], img.shape[1], tile, grid, max_num_tiles)
+    full = preprocess_image(img, rh, rw, mean, std)
+    tiles, hw = [], []
+    for a in range(rows):
+        for b in range(cols):
+            t = full[:, a * tile: min((a + 1) * tile, rh), b * tile: min((b + 1) * tile, rw)]
+            tiles.append(t)
+            hw.append((t.shape[1], t.shape[2]))
+    return tiles, hw
+
+
+def tile_batch(images: Sequence[np.ndarray], tile: int, grid: int, max_num_tiles: int,
+               mean: Sequence[float] = PROCESSOR_MEAN, std: Sequence[float] = PROCESSOR_STD):
+    """Tiles of every image, images in order, in the tower's input layout:
+    (flat float64 pixels, tile sizes, tiles per image)."""
+    parts, hw, counts = [], [], []
+    for im in images:
+        tiles, thw = tile_image(im, tile, grid, max_num_tiles, mean, std)
+        parts += [t.reshape(-1) for t in tiles]
+        hw += thw
+        counts.append(len(tiles))
+    return np.concatenate(parts), hw, counts
 
 
 # --------------------------------------------------------------------------

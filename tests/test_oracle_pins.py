@@ -575,3 +575,69 @@ def test_preprocess_batch_layout():
     assert hw == [(56, 56), (56, 28)]
     assert flat.shape == (3 * 56 * 56 + 3 * 56 * 28,)
     np.testing.assert_array_equal(flat[3 * 56 * 56:].reshape(3, 56, 28), O.preprocess_image(ims[1], 56, 28))
+
+
+# ------------------------------------------------------------- Pixtral tiles
+def test_tile_layout_page_example():
+    """"Pixtral-12B-2409", VISION TOKENS: a 4096x4096 image is a 4x4 grid of
+    1024x1024 tiles = 16 tiles = 65,536 patches of 16x16."""
+    rh, rw, rows, cols = O.tile_layout(4096, 4096, 1024, 16, 16)
+    assert (rh, rw, rows, cols) == (4096, 4096, 4, 4)
+    assert rows * cols * (1024 // 16) ** 2 == 65536
+    # a lower cap scales the image down: 4 tiles -> 2048^2, 1 tile -> 1024^2
+    assert O.tile_layout(4096, 4096, 1024, 16, 4) == (2048, 2048, 2, 2)
+    assert O.tile_layout(4096, 4096, 1024, 16, 1) == (1024, 1024, 1, 1)
+    # no scaling when the grid fits; the sides round up to the patch grid
+    assert O.tile_layout(1000, 3000, 1024, 16, 16) == (1008, 3008, 1, 3)
+    assert O.tile_layout(300, 200, 1024, 16, 16) == (304, 208, 1, 1)
+    # 3 tiles allowed for a 4096^2 image: the best grid is 1x3 / 3x1 / 1x1...
+    # -> min(1024/4096, 3072/4096) = 1/4 for 1x3, so 1024^2, one tile
+    assert O.tile_layout(4096, 4096, 1024, 16, 3) == (1024, 1024, 1, 1)
+    # a wide image with 3 tiles: 1x3 grid, s = 3072/6000
+    rh, rw, rows, cols = O.tile_layout(1500, 6000, 1024, 16, 3)
+    assert (rows, cols) == (1, 3) and rw == 3072 and rh == 768
+
+
+def test_tile_layout_brute_force():
+    """s* = the largest s in {1} u {k T / H} u {k T / W} (the points where a
+    grid side changes) with ceil(sH/T) * ceil(sW/T) <= M and s <= 1."""
+    from fractions import Fraction
+    rng = np.random.default_rng(26)
+    for _ in range(300):
+        g = int(rng.choice([1, 2, 4, 8]))
+        T = g * int(rng.integers(1, 6))
+        M = int(rng.integers(1, 10))
+        h, w = (int(v) for v in rng.integers(1, 120, size=2))
+        cands = {Fraction(1)} | {Fraction(k * T, h) for k in range(1, 40)} | {Fraction(k * T, w) for k in range(1, 40)}
+        ok = [s for s in cands if s <= 1 and math.ceil(s * h / T) * math.ceil(s * w / T) <= M]
+        s = max(ok)
+        rh = -(-max(1, math.floor(s * h)) // g) * g
+        rw = -(-max(1, math.floor(s * w)) // g) * g
+        got = O.tile_layout(h, w, T, g, M)
+        assert got == (rh, rw, -(-rh // T), -(-rw // T)), (h, w, T, g, M)
+        assert got[2] * got[3] <= M
+
+
+def test_tiles_reassemble_the_resized_image():
+    rng = np.random.default_rng(27)
+    img = rng.integers(0, 256, size=(70, 45, 3), dtype=np.uint8)
+    tiles, hw = O.tile_image(img, 32, 8, 6)
+    rh, rw, rows, cols = O.tile_layout(70, 45, 32, 8, 6)
+    assert len(tiles) == rows * cols and all(0 < a <= 32 and 0 < b <= 32 and a % 8 == 0 and b % 8 == 0
+                                             for a, b in hw)
+    full = O.preprocess_image(img, rh, rw)
+    rebuilt = np.concatenate([np.concatenate(tiles[r * cols:(r + 1) * cols], axis=2) for r in range(rows)], axis=1)
+    np.testing.assert_array_equal(rebuilt, full)
+
+
+def test_tiles_without_scaling_are_normalised_source_crops():
+    """When the source already sits on the tile grid no resampling happens:
+    each tile is the normalised crop of the source."""
+    rng = np.random.default_rng(28)
+    img = rng.integers(0, 256, size=(64, 96, 3), dtype=np.uint8)
+    tiles, hw = O.tile_image(img, 32, 16, 6)
+    assert hw == [(32, 32)] * 6
+    mean = np.asarray(O.PROCESSOR_MEAN)[:, None, None]
+    std = np.asarray(O.PROCESSOR_STD)[:, None, None]
+    crop = img[32:64, 64:96].transpose(2, 0, 1).astype(np.float64)
+    np.testing.assert_allclose(tiles[5], (crop / 255.0 - mean) / std, rtol=0, atol=1e-12)
