@@ -198,7 +198,8 @@ def time_scatter(out, wl, stream, reps=20):
 
 def time_u8_input(tw, wl, out, ws, stream, f32_patch_ms, reps=5):
     """The uint8 input path on a 4096x4096 photo (resized to the workload's
-    1540x1540): the whole forward from uint8 (HIP events around `reps`
+    1540x1540, or cut into the Pixtral workload's 16 tiles of 1024x1024):
+    the whole forward from uint8 (HIP events around `reps`
     calls), its patch-embedding kernel class (fused resize + normalise +
     hi|lo im2col, weight padding, GEMM) beside the float path's, and the
     standalone preprocessing into fp32 planes.  Algorithmic bytes of the
@@ -208,22 +209,33 @@ def time_u8_input(tw, wl, out, ws, stream, f32_patch_ms, reps=5):
     from vlm_vision_encoder_amd import synth
     from vlm_vision_encoder_amd import tower as T
     src = [(4096, 4096)]
-    info, tgt = tw.plan_u8(src)
-    if tgt != list(wl.image_hw):
-        return None
+    if wl.tiles_from is not None:  # Pixtral: the photo cut into tiles, capped at the workload's tile count
+        cap = len(wl.image_hw)
+        info, layout = tw.plan_tiles_u8(src, cap)
+        tiles = [(min(1024, layout[0][0] - a * 1024), min(1024, layout[0][1] - b * 1024))
+                 for a in range(layout[0][2]) for b in range(layout[0][3])]
+        if tiles != list(wl.image_hw):
+            return None
+        tgt = [(layout[0][0], layout[0][1])]
+        fwd = lambda: tw.forward_tiles_u8(img, src, cap, out=out, stream=sptr)  # noqa: E731
+    else:
+        info, tgt = tw.plan_u8(src)
+        if tgt != list(wl.image_hw):
+            return None
+        fwd = lambda: tw.forward_u8(img, src, out=out, stream=sptr)  # noqa: E731
     img = torch.from_numpy(synth.make_u8_images(src, seed=3)[0].reshape(-1)).cuda()
     sptr = stream.cuda_stream
-    tw.forward_u8(img, src, out=out, stream=sptr)
+    fwd()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
-        tw.forward_u8(img, src, out=out, stream=sptr)
+        fwd()
     e1.record(stream)
     torch.cuda.synchronize()
     fwd_ms = e0.elapsed_time(e1) / reps
     tw.set_profiling(True)
-    tw.forward_u8(img, src, out=out, stream=sptr)
+    fwd()
     torch.cuda.synchronize()
     prof = tw.read_profile(reset=True)
     tw.set_profiling(False)
@@ -237,7 +249,8 @@ def time_u8_input(tw, wl, out, ws, stream, f32_patch_ms, reps=5):
     torch.cuda.synchronize()
     pre_ms = e0.elapsed_time(e1) / reps
     nbytes = img.numel() + planes.numel() * 4
-    return {"source": "4096x4096 uint8 RGB", "target": list(tgt[0]), "forward_ms": round(fwd_ms, 4),
+    return {"source": "4096x4096 uint8 RGB", "target": list(tgt[0]),
+            "tiles": len(wl.image_hw) if wl.tiles_from is not None else None, "forward_ms": round(fwd_ms, 4),
             "patches_per_s": round(info.n_patches / (fwd_ms * 1e-3), 1),
             "patch_class_ms": round(prof["patch"][0], 5), "patch_class_ms_float_input": f32_patch_ms,
             "preprocess_planes_ms": round(pre_ms, 5),
@@ -379,7 +392,7 @@ def main():
 
     scatter = time_scatter(out, wl, stream) if wl.merge == 2 else None
     u8_input = None
-    if len(wl.image_hw) == 1 and "patch" in kernels:
+    if (len(wl.image_hw) == 1 or wl.tiles_from is not None) and "patch" in kernels:
         u8_input = time_u8_input(tw, wl, out, ws, stream, kernels["patch"]["ms_per_step"])
 
     patches_s = wl.n_patches / (ms_step * 1e-3)

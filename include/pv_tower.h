@@ -303,6 +303,59 @@ pv_status pv_tower_forward_u8(pv_tower* t, const uint8_t* images, const int32_t*
 pv_status pv_preprocess_u8(const uint8_t* images, const int32_t* src_hw, const int32_t* dst_hw,
                            int32_t n_images, const float* mean_std, float* out, void* stream);
 
+/* ---- tiles ("Pixtral-12B-2409" inference-research record, VISION TOKENS:
+ * large images are split into 1024x1024 tiles -- a 4096x4096 image is a 4x4
+ * grid of 16 tiles, 65,536 patches -- and the processor caps the tile count
+ * with max_num_tiles).  Readings: the image is scaled by the largest
+ * s <= 1 whose tile grid ceil(s*H/tile) x ceil(s*W/tile) has at most
+ * max_num_tiles tiles (exact fractions; s = 1 when the unscaled grid fits),
+ * each side becoming max(1, floor(s*side)) rounded up to a multiple of grid;
+ * the resized image is cut row-major into tile x tile tiles, the last row
+ * and column keeping the remainder (multiples of grid).  Each tile is one
+ * image of the tower (its own attention block, positions from 0).  Pixels
+ * are resampled and normalised as for pv_tower_forward_u8. */
+
+/* Host-only, pure: layout (host [n_images][4]) = resized H, resized W, tile
+ * rows, tile columns of each source size (src_hw, host [n_images][2]).
+ * Errors: PV_ERR_ARG (null, n_images < 1, grid < 1, tile not a positive
+ * multiple of grid or > 32768, max_num_tiles outside [1, 65536]),
+ * PV_ERR_SHAPE (a source side outside [1, 32768]). */
+pv_status pv_tile_layout(const int32_t* src_hw, int32_t n_images, int32_t tile, int32_t grid,
+                         int32_t max_num_tiles, int32_t* layout);
+
+/* Host-only, pure: plan of the tiles of uint8 sources with tile = the
+ * tower's max_side and grid = patch * merge; layout as pv_tile_layout (may
+ * be NULL).  info counts every tile as an image.
+ * Errors: PV_ERR_ARG, PV_ERR_SHAPE, PV_ERR_UNSUPPORTED (max_side not a
+ * multiple of patch * merge). */
+pv_status pv_tower_plan_tiles_u8(const pv_tower* t, const int32_t* src_hw, int32_t n_images,
+                                 int32_t max_num_tiles, int32_t* layout, pv_plan_info* info);
+
+/* Runs the tower over the tiles of uint8 images (layout as for
+ * pv_tower_forward_u8); the resampling happens per tile inside the patch
+ * embedding's operand load.  Output rows: tiles row-major within an image,
+ * images in order; per tile its merged tokens (merge 2) or patches (merge 1),
+ * row-major.  Errors: as pv_tower_forward_u8, PV_ERR_ARG for
+ * max_num_tiles < 1, PV_ERR_UNSUPPORTED as pv_tower_plan_tiles_u8. */
+pv_status pv_tower_forward_tiles_u8(pv_tower* t, const uint8_t* images, const int32_t* src_hw,
+                                    int32_t n_images, int32_t max_num_tiles, const float* mean_std,
+                                    void* out, int64_t out_rows_cap, void* workspace,
+                                    size_t ws_bytes, void* stream);
+
+/* Configurations of the two towers the pages describe, filled into *cfg
+ * (dtype and out_dtype = dtype, flags 0):
+ *   PV_PRESET_MISTRAL3    "Mistral 3", Mistral3Model argument table and
+ *                         Mistral3ImageProcessor: patch 14, width 1024, MLP
+ *                         4096, 24 layers, 16 heads, rotary base 1e4, 2x2
+ *                         merge to 5120, longest edge 1540.
+ *   PV_PRESET_PIXTRAL12B  "Pixtral-12B-2409", part (1) Vision: patch 16,
+ *                         width 1024, MLP 4096, 24 layers, 16 heads, rotary
+ *                         base 1e4, no merge, image size (tile) 1024.
+ * rms_eps 1e-5 in both.  Errors: PV_ERR_ARG (null, unknown preset or
+ * dtype). */
+enum { PV_PRESET_MISTRAL3 = 0, PV_PRESET_PIXTRAL12B = 1 };
+pv_status pv_config_preset(int32_t preset, int32_t dtype, pv_config* cfg);
+
 /* Thread-local message of the last failure in this thread ("" if none). */
 const char* pv_last_error(void);
 

@@ -291,3 +291,76 @@ def test_forward_u8_and_preprocess_validation_before_device_work(tower_handle):
     d0, _ = T._hw_array([(28, 0)])
     assert p(FAKE, arr, d0, 1, None, FAKE, None) == -2
     assert p(FAKE, zero, d, 1, None, FAKE, None) == -2
+
+
+# ------------------------------------------------------------- tiles, presets
+def test_tile_layout_equals_oracle():
+    rng = np.random.default_rng(32)
+    hw = [(int(a), int(b)) for a, b in rng.integers(1, 9000, size=(150, 2))]
+    hw += [(4096, 4096), (1024, 1024), (1000, 3000), (1500, 6000), (1, 1), (32768, 32768)]
+    for T_, g, M in [(1024, 16, 16), (1024, 16, 4), (1024, 16, 1), (1024, 16, 3), (1540, 28, 7), (64, 8, 100)]:
+        got = T.tile_layout(hw, T_, g, M)
+        want = [O.tile_layout(h, w, T_, g, M) for h, w in hw]
+        assert got == want, (T_, g, M)
+
+
+def test_tile_layout_errors():
+    lib = T.load_library()
+    lay = (C.c_int32 * 4)()
+    arr, n = T._hw_array([(100, 100)])
+    for tile, grid, M, status in [(1024, 0, 4, -1), (1000, 16, 4, -1), (1024, 16, 0, -1), (1024, 16, 65537, -1),
+                                  (65536, 16, 4, -1)]:
+        assert lib.pv_tile_layout(arr, n, tile, grid, M, lay) == status
+    bad, nb = T._hw_array([(0, 100)])
+    assert lib.pv_tile_layout(bad, nb, 1024, 16, 4, lay) == -2
+    assert lib.pv_tile_layout(None, 1, 1024, 16, 4, lay) == -1
+    assert lib.pv_tile_layout(arr, 0, 1024, 16, 4, lay) == -1
+
+
+def test_presets_match_the_pages():
+    m = T.preset("mistral3")
+    assert (m.patch, m.hidden, m.heads, m.mlp, m.layers, m.merge, m.out_dim, m.max_side) == \
+        (14, 1024, 16, 4096, 24, 2, 5120, 1540)
+    p = T.preset("pixtral12b", "f32")
+    assert (p.patch, p.hidden, p.heads, p.mlp, p.layers, p.merge, p.max_side) == (16, 1024, 16, 4096, 24, 1, 1024)
+    assert p.dtype == T.PV_F32 and p.out_dtype == T.PV_F32 and m.dtype == T.PV_BF16
+    assert m.rope_theta == p.rope_theta == 1.0e4
+    lib = T.load_library()
+    assert lib.pv_config_preset(7, 0, C.byref(T.PvConfig())) == -1
+    assert lib.pv_config_preset(0, 5, C.byref(T.PvConfig())) == -1
+    assert lib.pv_config_preset(0, 0, None) == -1
+    # both presets create towers (weights are only borrowed, never touched here)
+    for cfg in (m, p):
+        st, h, _ = create(cfg)
+        assert st == 0
+        lib.pv_tower_destroy(h)
+
+
+def test_plan_tiles_u8_counts():
+    """Pixtral preset: a 4096x4096 photo with max_num_tiles 16 is 16 tiles of
+    1024^2 = 65,536 output rows; the cap 4 gives 4 tiles (16,384 rows)."""
+    cfg = T.preset("pixtral12b")
+    st, h, _ = create(cfg)
+    assert st == 0
+    lib = T.load_library()
+    try:
+        arr, n = T._hw_array([(4096, 4096), (1000, 3000)])
+        lay = (C.c_int32 * 8)()
+        info = T.PvPlanInfo()
+        assert lib.pv_tower_plan_tiles_u8(h, arr, n, 16, lay, C.byref(info)) == 0
+        assert list(lay) == [4096, 4096, 4, 4, 1008, 3008, 1, 3]
+        assert info.n_images == 19 and info.out_cols == 1024
+        assert info.n_patches == 16 * 4096 + 63 * (64 + 64 + 60)
+        tiles = [(1024, 1024)] * 16 + [(1008, 1024), (1008, 1024), (1008, 960)]
+        st, ref = _plan(lib, h, tiles)
+        assert st == 0 and ref.workspace_bytes == info.workspace_bytes and ref.out_rows == info.out_rows
+        assert lib.pv_tower_plan_tiles_u8(h, arr, 1, 4, None, C.byref(info)) == 0
+        assert info.n_patches == 4 * 4096 and info.n_images == 4
+        assert lib.pv_tower_plan_tiles_u8(h, arr, 1, 0, None, C.byref(info)) == -1
+        f = lib.pv_tower_forward_tiles_u8
+        ws = FAKE * 256
+        assert f(h, FAKE, arr, 1, 0, None, FAKE, 1 << 30, ws, 1 << 40, None) == -1
+        assert f(h, FAKE, arr, 1, 4, None, FAKE, 4 * 4096 - 1, ws, 1 << 40, None) == -3
+        assert f(h, None, arr, 1, 4, None, FAKE, 1 << 30, ws, 1 << 40, None) == -1
+    finally:
+        lib.pv_tower_destroy(h)

@@ -7,7 +7,11 @@ within the tower's own bars (2e-2 * RMS bf16, 1e-4 * RMS fp32) of the oracle
 run on the oracle's preprocessed pixels.  At the 1540x1540 size (a 4096x4096
 photo) the planes are checked on sampled pixels the oracle computes one by
 one, and the fused path must equal the two-pass path (preprocess, then the
-float forward) bit for bit: both take the same fp32 samples.
+float forward) bit for bit: both take the same fp32 samples.  The Pixtral
+tile path (tiles of max_side, capped by max_num_tiles) is held to the same
+bars: tile layouts bit-exact, the tower over the tiles vs the oracle on its
+own tiles, and at 4096x4096 (16 tiles; 4 tiles under a cap of 4) sampled
+pixels plus bit-equality with preprocess + cut + float forward.
 Inputs: seeded uniform uint8 images (vlm_vision_encoder_amd.synth).
 """
 import numpy as np
@@ -166,6 +170,107 @@ def test_fullsize_4096_photo_to_1540():
     assert e <= TOL_PLANES
     a = tower.forward_u8(images, src).clone()
     b = tower.forward(torch.from_numpy(planes.reshape(-1)).cuda(), tgt)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    tower.close()
+
+
+# ------------------------------------------------------------------- tiles
+def tiles_from_planes(planes, layout, tile):
+    """Cut the resized planes of each image into its tiles (row-major), as a
+    flat fp32 tensor in the tower's input layout, plus the tile sizes."""
+    torch = _torch()
+    parts, hw, off = [], [], 0
+    for rh, rw, rows, cols in layout:
+        img = planes[off: off + 3 * rh * rw].view(3, rh, rw)
+        off += 3 * rh * rw
+        for a in range(rows):
+            for b in range(cols):
+                t = img[:, a * tile: min((a + 1) * tile, rh), b * tile: min((b + 1) * tile, rw)]
+                parts.append(t.contiguous().view(-1))
+                hw.append((t.shape[1], t.shape[2]))
+    return torch.cat(parts), hw
+
+
+TILE_CASES = [
+    # dtype, patch, merge, tile, max_num_tiles, sources
+    ("bf16", 16, 1, 64, 4, [(150, 100), (64, 64), (40, 200), (300, 300)]),
+    ("f32", 16, 1, 64, 4, [(150, 100), (64, 64), (40, 200), (300, 300)]),
+    ("bf16", 14, 2, 56, 3, [(200, 90), (56, 112), (13, 29)]),
+    ("f32", 14, 2, 56, 3, [(200, 90), (56, 112), (13, 29)]),
+]
+
+
+@pytest.mark.parametrize("dtype,patch,merge,tile,cap,src", TILE_CASES)
+def test_forward_tiles_u8_matches_oracle(dtype, patch, merge, tile, cap, src):
+    torch = _torch()
+    say(f"forward_tiles_u8 {dtype} patch={patch} merge={merge} tile={tile} max_num_tiles={cap} src={src}")
+    wl = small_workload(dtype, merge, patch)
+    w = synth.make_weights(wl)
+    tower = T.Tower(T.config_for(wl, max_side=tile), T.weights_to_device(w, dtype))
+    images = synth.make_u8_images(src, seed=47)
+    info, layout = tower.plan_tiles_u8(src, cap)
+    grid = patch * merge
+    assert layout == [O.tile_layout(h, w_, tile, grid, cap) for h, w_ in src]
+    out = to_np(tower.forward_tiles_u8(upload_u8(images), src, cap))
+    torch.cuda.synchronize()
+    px, hw, counts = O.tile_batch(images, tile, grid, cap)
+    assert sum(counts) == info.n_images
+    cfg = O.TowerConfig(patch=patch, hidden=wl.hidden, heads=wl.heads, mlp=wl.mlp, layers=wl.layers, merge=merge,
+                        out_dim=wl.out_dim, rope_theta=wl.rope_theta, rms_eps=wl.rms_eps)
+    want = O.tower_forward(px, hw, synth.oracle_weights(w), cfg)["out"]
+    assert out.shape == want.shape
+    e = err_over_rms(out, want)
+    say(f"  out: max-abs-err/RMS = {e:.3e} (tol {TOL[dtype]}), {info.n_images} tiles")
+    assert e <= TOL[dtype]
+    tower.close()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_forward_tiles_u8_equals_two_pass(dtype):
+    torch = _torch()
+    say(f"forward_tiles_u8 vs two-pass {dtype}")
+    wl = small_workload(dtype, merge=1, patch=16)
+    tower = T.Tower(T.config_for(wl, max_side=64), T.weights_to_device(synth.make_weights(wl), dtype))
+    src = [(500, 333), (100, 224), (17, 260)]
+    images = upload_u8(synth.make_u8_images(src, seed=48))
+    info, layout = tower.plan_tiles_u8(src, 6)
+    a = tower.forward_tiles_u8(images, src, 6).clone()
+    planes = T.preprocess_u8(images, src, [(l[0], l[1]) for l in layout])
+    px, hw = tiles_from_planes(planes, layout, 64)
+    b = tower.forward(px, hw)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    tower.close()
+
+
+@pytest.mark.parametrize("cap,n_tiles", [(16, 16), (4, 4)])
+def test_fullsize_pixtral_4096_photo_tiles(cap, n_tiles):
+    """Pixtral-12B preset: a 4096x4096 photo as 1024^2 tiles (16 tiles =
+    65,536 rows with max_num_tiles 16; 4 tiles of the 2048^2 resize with 4):
+    sampled tile pixels vs the oracle's per-pixel values, and the fused path
+    bit-equal to preprocess + cut + float forward."""
+    torch = _torch()
+    say(f"full size: Pixtral 4096x4096 uint8, max_num_tiles={cap}")
+    wl = synth.workload("pixtral_tiles16")
+    tower = T.Tower(T.preset("pixtral12b"), T.weights_to_device(synth.make_weights(wl), "bf16"))
+    src = [(4096, 4096)]
+    host = synth.make_u8_images(src, seed=49)
+    images = upload_u8(host)
+    info, layout = tower.plan_tiles_u8(src, cap)
+    rh, rw, rows, cols = layout[0]
+    assert rows * cols == n_tiles == info.n_images and info.out_rows == n_tiles * 4096
+    planes = T.preprocess_u8(images, src, [(rh, rw)])
+    px, hw = tiles_from_planes(planes, layout, 1024)
+    cpu = planes.cpu().numpy().reshape(3, rh, rw)
+    rng = np.random.default_rng(50)
+    picks = [(int(c), int(y), int(x)) for c, y, x in zip(rng.integers(0, 3, 300), rng.integers(0, rh, 300),
+                                                          rng.integers(0, rw, 300))]
+    got = np.array([cpu[c, y, x] for c, y, x in picks])
+    want = np.array([O.preprocess_pixel(host[0], rh, rw, c, y, x) for c, y, x in picks])
+    assert err_over_rms(got, want) <= TOL_PLANES
+    a = tower.forward_tiles_u8(images, src, cap).clone()
+    b = tower.forward(px, hw)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     tower.close()

@@ -85,11 +85,12 @@ struct NormAff {
   float mul[3], add[3];
 };
 //   im2col_u8_split: as im2col_split, with the pixels sampled from the uint8
-//                    source images src[] (device) of the plan's images
-//   resize_norm_u8:  one image -> fp32 planes [3][tH][tW]
+//                    sources src[] (device, one per plan image)
+//   resize_norm_u8:  the tH x tW window at (sm.y0, sm.x0) of the source
+//                    `image` resized to sm.RH x sm.RW -> fp32 planes [3][tH][tW]
 hipError_t im2col_u8_split(const uint8_t* images, const SrcImage* src, const DevMaps& maps, const NormAff& aff,
                            void* out, int n_patches, int K, int Kp, hipStream_t s);
-hipError_t resize_norm_u8(const uint8_t* image, int sH, int sW, int tH, int tW, const NormAff& aff, float* out,
+hipError_t resize_norm_u8(const uint8_t* image, const SrcImage& sm, int tH, int tW, const NormAff& aff, float* out,
                           hipStream_t s);
 hipError_t pad_rows(const void* w, void* out, int rows, int K, int Kp, hipStream_t s);
 //   gateup_fp8:   b8 [2F][D] fp8 e4m3 = the gate/up weights in the GEMM's

@@ -142,6 +142,48 @@ int resize_target(int32_t h, int32_t w, int32_t longest_edge, int32_t grid, int3
   return 0;
 }
 
+int tile_layout(int32_t h, int32_t w, int32_t tile, int32_t grid, int32_t max_num_tiles, int32_t* rh,
+                int32_t* rw, int32_t* rows, int32_t* cols, std::string* err) {
+  if (grid < 1 || tile < grid || tile % grid || tile > kMaxSrcSide || max_num_tiles < 1 ||
+      max_num_tiles > kMaxTiles) {
+    *err = "tile must be a multiple of grid (>= 1, <= " + std::to_string(kMaxSrcSide) +
+           ") and max_num_tiles in [1, " + std::to_string(kMaxTiles) + "]";
+    return -1;
+  }
+  if (h < 1 || w < 1 || h > kMaxSrcSide || w > kMaxSrcSide) {
+    *err = "source image " + std::to_string(h) + "x" + std::to_string(w) + ": each side must be in [1, " +
+           std::to_string(kMaxSrcSide) + "]";
+    return -2;
+  }
+  // best scale as a fraction num / den: for each row count r the widest
+  // grid r x floor(M / r) is the best one with r rows
+  int64_t num = 0, den = 1;
+  for (int64_t r = 1; r <= max_num_tiles; ++r) {
+    const int64_t c = max_num_tiles / r;
+    int64_t n = r * tile, d = h;                       // r * tile / h
+    if (c * tile * int64_t(h) < n * int64_t(w)) {      // c * tile / w is smaller
+      n = c * tile;
+      d = w;
+    }
+    if (n * den > num * d) {
+      num = n;
+      den = d;
+    }
+  }
+  if (num >= den) {  // never enlarged
+    num = 1;
+    den = 1;
+  }
+  const int64_t g = grid;
+  const int64_t a = std::max<int64_t>(1, int64_t(h) * num / den);
+  const int64_t b = std::max<int64_t>(1, int64_t(w) * num / den);
+  *rh = int32_t((a + g - 1) / g * g);
+  *rw = int32_t((b + g - 1) / g * g);
+  *rows = (*rh + tile - 1) / tile;
+  *cols = (*rw + tile - 1) / tile;
+  return 0;
+}
+
 void host_index_maps(const Plan& pl, int merge, int32_t* cu, int32_t* rc, int32_t* msrc) {
   for (int32_t i = 0; i <= pl.n_images; ++i) cu[i] = pl.cu[i];
   for (int32_t i = 0; i < pl.n_images; ++i) {

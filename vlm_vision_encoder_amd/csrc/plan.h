@@ -25,16 +25,21 @@ struct ImageMeta {
 };
 static_assert(sizeof(ImageMeta) == 32, "ImageMeta layout");
 
-// Source of one uint8 image (H x W x 3, channel fastest) for the resize in
-// the patch embedding's A load; uploaded after the rotary table (16 bytes).
+// Source of one plan image (a whole resized image, or one tile of it) in the
+// uint8 input (H x W x 3, channel fastest), for the resize in the patch
+// embedding's A load; uploaded after the rotary table (32 bytes).
 struct SrcImage {
   int32_t H, W;             // source pixels
-  uint32_t off_lo, off_hi;  // 64-bit byte offset of the image in the uint8 buffer
+  int32_t RH, RW;           // size of the resized image the plan image is cut from
+  int32_t y0, x0;           // origin of the plan image in the resized image
+  uint32_t off_lo, off_hi;  // 64-bit byte offset of the source in the uint8 buffer
 };
-static_assert(sizeof(SrcImage) == 16, "SrcImage layout");
+static_assert(sizeof(SrcImage) == 32, "SrcImage layout");
 
-// Largest source side the resize accepts (its tap arithmetic is 32-bit).
+// Largest source or resized side the resize accepts (its tap arithmetic is
+// 32-bit), and the largest tile cap.
 constexpr int32_t kMaxSrcSide = 32768;
+constexpr int32_t kMaxTiles = 65536;
 
 // One attention work item: q-tile starting at local query q0 of an image.
 struct AttnItem {
@@ -93,6 +98,16 @@ struct Plan {
 // (a side outside [1, kMaxSrcSide]) with *err set.
 int resize_target(int32_t h, int32_t w, int32_t longest_edge, int32_t grid, int32_t* th, int32_t* tw,
                   std::string* err);
+
+// Tile layout of one image: the image is scaled by s = min(1, max over tile
+// grids r x c with r * c <= max_num_tiles of min(r*tile/h, c*tile/w)) (exact
+// fractions), each side becoming max(1, floor(s * side)) rounded up to a
+// multiple of `grid`; the tiles are tile x tile, row-major, the last row and
+// column keeping the remainder.  Writes the resized size and the grid.
+// Returns 0, -1 (grid < 1, tile not a multiple of grid, max_num_tiles outside
+// [1, kMaxTiles]) or -2 (a side outside [1, kMaxSrcSide]) with *err set.
+int tile_layout(int32_t h, int32_t w, int32_t tile, int32_t grid, int32_t max_num_tiles, int32_t* rh,
+                int32_t* rw, int32_t* rows, int32_t* cols, std::string* err);
 
 // Returns 0 on success, -1 (argument) or -2 (shape) with *err set.
 int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, Plan* out,

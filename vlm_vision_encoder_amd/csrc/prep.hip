@@ -58,13 +58,14 @@ __device__ __forceinline__ void bilinear_taps(uint32_t t, uint32_t n_in, uint32_
   i1 = i0 + 1 < n_in ? i0 + 1 : n_in - 1;
 }
 
-// Normalised value of channel c at resized pixel (ty, tx).
-__device__ __forceinline__ float sample_u8(const uint8_t* __restrict__ img, uint32_t sH, uint32_t sW, uint32_t tH,
-                                           uint32_t tW, uint32_t ty, uint32_t tx, int c, float mul, float add) {
+// Normalised value of channel c at pixel (ty, tx) of the sH x sW source
+// resized to RH x RW.
+__device__ __forceinline__ float sample_u8(const uint8_t* __restrict__ img, uint32_t sH, uint32_t sW, uint32_t RH,
+                                           uint32_t RW, uint32_t ty, uint32_t tx, int c, float mul, float add) {
   uint32_t y0, y1, x0, x1;
   float fy, fx;
-  bilinear_taps(ty, sH, tH, y0, y1, fy);
-  bilinear_taps(tx, sW, tW, x0, x1, fx);
+  bilinear_taps(ty, sH, RH, y0, y1, fy);
+  bilinear_taps(tx, sW, RW, x0, x1, fx);
   const uint8_t* r0 = img + size_t(y0) * sW * 3 + c;
   const uint8_t* r1 = img + size_t(y1) * sW * 3 + c;
   const float a = r0[x0 * 3], b = r0[x1 * 3], cc = r1[x0 * 3], d = r1[x1 * 3];
@@ -104,8 +105,8 @@ __global__ __launch_bounds__(256) void im2col_split_kernel(const float* __restri
   *reinterpret_cast<u32x4*>(row + Kp + k0) = lo;
 }
 
-// One thread per (patch g, 8 consecutive k); the image is sampled from its
-// uint8 source.
+// One thread per (patch g, 8 consecutive k); the plan image (a resized image
+// or a tile of one) is sampled from its uint8 source.
 __global__ __launch_bounds__(256) void im2col_u8_split_kernel(const uint8_t* __restrict__ images,
                                                               const SrcImage* __restrict__ srcs, DevMaps maps,
                                                               NormAff aff, uint16_t* __restrict__ out,
@@ -115,7 +116,6 @@ __global__ __launch_bounds__(256) void im2col_u8_split_kernel(const uint8_t* __r
   if (idx >= (long long)n_patches * chunks) return;
   const int g = int(idx / chunks), k0 = int(idx - (long long)g * chunks) * 8;
   const int img = maps.rowinfo[2 * g], rc = maps.rowinfo[2 * g + 1];
-  const ImageMeta mt = maps.meta[img];
   const SrcImage sm = srcs[img];
   const uint8_t* src = images + ((uint64_t(sm.off_hi) << 32) | sm.off_lo);
   const int p = maps.patch, pp = p * p;
@@ -128,7 +128,8 @@ __global__ __launch_bounds__(256) void im2col_u8_split_kernel(const uint8_t* __r
     if (k < K) {
       const int ch = k / pp, rem = k - ch * pp;
       const int u = rem / p, x = rem - u * p;
-      v = sample_u8(src, sm.H, sm.W, mt.H, mt.W, pr * p + u, pc * p + x, ch, aff.mul[ch], aff.add[ch]);
+      v = sample_u8(src, sm.H, sm.W, sm.RH, sm.RW, sm.y0 + pr * p + u, sm.x0 + pc * p + x, ch, aff.mul[ch],
+                    aff.add[ch]);
     }
     f[e] = v;
   }
@@ -139,16 +140,18 @@ __global__ __launch_bounds__(256) void im2col_u8_split_kernel(const uint8_t* __r
   *reinterpret_cast<u32x4*>(row + Kp + k0) = lo;
 }
 
-// One thread per resized pixel (all three channels).
-__global__ __launch_bounds__(256) void resize_norm_u8_kernel(const uint8_t* __restrict__ img, int sH, int sW,
-                                                             int tH, int tW, NormAff aff, float* __restrict__ out) {
+// One thread per output pixel (all three channels) of the tH x tW window at
+// (y0, x0) of the resized RH x RW image.
+__global__ __launch_bounds__(256) void resize_norm_u8_kernel(const uint8_t* __restrict__ img, SrcImage sm, int tH,
+                                                             int tW, NormAff aff, float* __restrict__ out) {
   const long long idx = blockIdx.x * 256ll + threadIdx.x;
   const long long plane = (long long)tH * tW;
   if (idx >= plane) return;
   const int ty = int(idx / tW), tx = int(idx - (long long)ty * tW);
 #pragma unroll
   for (int c = 0; c < 3; ++c)
-    out[c * plane + idx] = sample_u8(img, sH, sW, tH, tW, ty, tx, c, aff.mul[c], aff.add[c]);
+    out[c * plane + idx] =
+        sample_u8(img, sm.H, sm.W, sm.RH, sm.RW, sm.y0 + ty, sm.x0 + tx, c, aff.mul[c], aff.add[c]);
 }
 
 // One thread per 8 consecutive values of a row.
@@ -241,13 +244,13 @@ hipError_t im2col_u8_split(const uint8_t* images, const SrcImage* src, const Dev
   return hipGetLastError();
 }
 
-hipError_t resize_norm_u8(const uint8_t* image, int sH, int sW, int tH, int tW, const NormAff& aff, float* out,
+hipError_t resize_norm_u8(const uint8_t* image, const SrcImage& sm, int tH, int tW, const NormAff& aff, float* out,
                           hipStream_t s) {
-  if (sH < 1 || sW < 1 || tH < 1 || tW < 1 || sH > kMaxSrcSide || sW > kMaxSrcSide || tH > kMaxSrcSide ||
-      tW > kMaxSrcSide)
+  if (sm.H < 1 || sm.W < 1 || sm.H > kMaxSrcSide || sm.W > kMaxSrcSide || tH < 1 || tW < 1 || sm.y0 < 0 ||
+      sm.x0 < 0 || sm.y0 + tH > sm.RH || sm.x0 + tW > sm.RW || sm.RH > 2 * kMaxSrcSide || sm.RW > 2 * kMaxSrcSide)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(resize_norm_u8_kernel, grid_for((long long)tH * tW), dim3(256), 0, s, image, sH, sW, tH, tW,
-                     aff, out);
+  hipLaunchKernelGGL(resize_norm_u8_kernel, grid_for((long long)tH * tW), dim3(256), 0, s, image, sm, tH, tW, aff,
+                     out);
   return hipGetLastError();
 }
 

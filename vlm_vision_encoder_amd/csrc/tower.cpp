@@ -241,7 +241,7 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
         const pv::SrcImage& sm = plan.src[i];
         const size_t off = (size_t(m.pix_hi) << 32) | m.pix_lo;
         const size_t soff = (size_t(sm.off_hi) << 32) | sm.off_lo;
-        PV_LAUNCH(PV_K_PATCH, pv::resize_norm_u8(px.u8 + soff, sm.H, sm.W, m.H, m.W, px.aff, planes + off, s));
+        PV_LAUNCH(PV_K_PATCH, pv::resize_norm_u8(px.u8 + soff, sm, m.H, m.W, px.aff, planes + off, s));
       }
       pixels = planes;
     }
@@ -379,10 +379,57 @@ pv_status make_plan_u8(const pv_tower* t, const int32_t* src_hw, int32_t n, pv::
     pv::SrcImage& sm = plan->src[i];
     sm.H = src_hw[2 * i];
     sm.W = src_hw[2 * i + 1];
+    sm.RH = (*dst_hw)[2 * i];
+    sm.RW = (*dst_hw)[2 * i + 1];
+    sm.y0 = sm.x0 = 0;
     sm.off_lo = uint32_t(off & 0xffffffffu);
     sm.off_hi = uint32_t(off >> 32);
     off += uint64_t(3) * uint64_t(sm.H) * uint64_t(sm.W);
   }
+  return PV_OK;
+}
+
+// Tiles of uint8 source images for this tower (tile = max_side, grid =
+// patch * merge): layout [n][4] = (resized H, W, tile rows, tile columns),
+// then the plan over all tiles (row-major per image, images in order).
+pv_status make_plan_tiles_u8(const pv_tower* t, const int32_t* src_hw, int32_t n, int32_t max_num_tiles,
+                             pv::Plan* plan, std::vector<int32_t>* layout) {
+  if (!src_hw) return fail(PV_ERR_ARG, "src_hw must not be null");
+  if (n < 1) return fail(PV_ERR_ARG, "n_images must be >= 1 (the tower runs only on image input)");
+  const int32_t tile = t->cfg.max_side, grid = t->cfg.patch * t->cfg.merge;
+  if (tile % grid) return fail(PV_ERR_UNSUPPORTED, "the tile edge (max_side) must be a multiple of patch * merge");
+  layout->assign(size_t(4) * n, 0);
+  std::vector<int32_t> tile_hw;
+  std::vector<pv::SrcImage> src;
+  std::string err;
+  uint64_t off = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t* L = &(*layout)[4 * i];
+    const int rc = pv::tile_layout(src_hw[2 * i], src_hw[2 * i + 1], tile, grid, max_num_tiles, &L[0], &L[1], &L[2],
+                                   &L[3], &err);
+    if (rc == -1) return fail(PV_ERR_ARG, err);
+    if (rc == -2) return fail(PV_ERR_SHAPE, "image " + std::to_string(i) + ": " + err);
+    for (int32_t a = 0; a < L[2]; ++a)
+      for (int32_t b = 0; b < L[3]; ++b) {
+        pv::SrcImage sm;
+        sm.H = src_hw[2 * i];
+        sm.W = src_hw[2 * i + 1];
+        sm.RH = L[0];
+        sm.RW = L[1];
+        sm.y0 = a * tile;
+        sm.x0 = b * tile;
+        sm.off_lo = uint32_t(off & 0xffffffffu);
+        sm.off_hi = uint32_t(off >> 32);
+        src.push_back(sm);
+        tile_hw.push_back(std::min(tile, L[0] - sm.y0));
+        tile_hw.push_back(std::min(tile, L[1] - sm.x0));
+        if (src.size() > size_t(INT32_MAX / 2)) return fail(PV_ERR_SHAPE, "too many tiles");
+      }
+    off += uint64_t(3) * uint64_t(src_hw[2 * i]) * uint64_t(src_hw[2 * i + 1]);
+  }
+  pv_status st = make_plan(t, tile_hw.data(), int32_t(src.size()), plan);
+  if (st != PV_OK) return st;
+  plan->src = std::move(src);
   return PV_OK;
 }
 
@@ -404,6 +451,34 @@ pv_status check_call(const pv_tower* t, const float* pixels, const int32_t* imag
   if (!aligned(dst, 16)) return fail(PV_ERR_ARG, "output must be 16-byte aligned");
   if (!aligned(ws, 256)) return fail(PV_ERR_ARG, "workspace must be 256-byte aligned");
   return PV_OK;
+}
+
+// uint8 forward: max_num_tiles == 0 resizes each image whole (the longest
+// edge rule), else cuts it into tiles of max_side.
+pv_status forward_u8_common(pv_tower* t, const uint8_t* images, const int32_t* src_hw, int32_t n_images,
+                            int32_t max_num_tiles, const float* mean_std, void* out, int64_t out_rows_cap,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!t) return fail(PV_ERR_ARG, "tower is null");
+  if (!images || !out || !workspace) return fail(PV_ERR_ARG, "images, output and workspace must not be null");
+  if (!aligned(out, 16)) return fail(PV_ERR_ARG, "output must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(PV_ERR_ARG, "workspace must be 256-byte aligned");
+  PixelSource px;
+  px.u8 = images;
+  if (!norm_affine(mean_std, &px.aff)) return fail(PV_ERR_ARG, "mean_std must be finite with std > 0");
+  pv::Plan plan;
+  std::vector<int32_t> hw;
+  pv_status st = max_num_tiles > 0 ? make_plan_tiles_u8(t, src_hw, n_images, max_num_tiles, &plan, &hw)
+                                   : make_plan_u8(t, src_hw, n_images, &plan, &hw);
+  if (st != PV_OK) return st;
+  if (out_rows_cap < plan.out_rows)
+    return fail(PV_ERR_CAPACITY, "out_rows_cap " + std::to_string(out_rows_cap) + " < " + std::to_string(plan.out_rows));
+  if (ws_bytes < plan.ws.total)
+    return fail(PV_ERR_CAPACITY, "workspace " + std::to_string(ws_bytes) + " < " + std::to_string(plan.ws.total));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if ((st = upload_and_maps(t, plan, ws, s)) != PV_OK) return st;
+  return run_tower(t, px, plan, out, ws, StageStop(), s);
 }
 
 }  // namespace
@@ -530,26 +605,78 @@ pv_status pv_tower_plan_u8(const pv_tower* t, const int32_t* src_hw, int32_t n_i
 pv_status pv_tower_forward_u8(pv_tower* t, const uint8_t* images, const int32_t* src_hw, int32_t n_images,
                               const float* mean_std, void* out, int64_t out_rows_cap, void* workspace,
                               size_t ws_bytes, void* stream) {
+  return forward_u8_common(t, images, src_hw, n_images, 0, mean_std, out, out_rows_cap, workspace, ws_bytes, stream);
+}
+
+pv_status pv_tower_forward_tiles_u8(pv_tower* t, const uint8_t* images, const int32_t* src_hw, int32_t n_images,
+                                    int32_t max_num_tiles, const float* mean_std, void* out, int64_t out_rows_cap,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  if (max_num_tiles < 1) {
+    g_last_error = "max_num_tiles must be >= 1";
+    return PV_ERR_ARG;
+  }
+  return forward_u8_common(t, images, src_hw, n_images, max_num_tiles, mean_std, out, out_rows_cap, workspace,
+                           ws_bytes, stream);
+}
+
+pv_status pv_tile_layout(const int32_t* src_hw, int32_t n_images, int32_t tile, int32_t grid, int32_t max_num_tiles,
+                         int32_t* layout) {
   g_last_error.clear();
-  if (!t) return fail(PV_ERR_ARG, "tower is null");
-  if (!images || !out || !workspace) return fail(PV_ERR_ARG, "images, output and workspace must not be null");
-  if (!aligned(out, 16)) return fail(PV_ERR_ARG, "output must be 16-byte aligned");
-  if (!aligned(workspace, 256)) return fail(PV_ERR_ARG, "workspace must be 256-byte aligned");
-  PixelSource px;
-  px.u8 = images;
-  if (!norm_affine(mean_std, &px.aff)) return fail(PV_ERR_ARG, "mean_std must be finite with std > 0");
+  if (!src_hw || !layout) return fail(PV_ERR_ARG, "src_hw and layout must not be null");
+  if (n_images < 1) return fail(PV_ERR_ARG, "n_images must be >= 1");
+  std::string err;
+  for (int32_t i = 0; i < n_images; ++i) {
+    int32_t* L = layout + 4 * i;
+    const int rc = pv::tile_layout(src_hw[2 * i], src_hw[2 * i + 1], tile, grid, max_num_tiles, &L[0], &L[1], &L[2],
+                                   &L[3], &err);
+    if (rc == -1) return fail(PV_ERR_ARG, err);
+    if (rc == -2) return fail(PV_ERR_SHAPE, "image " + std::to_string(i) + ": " + err);
+  }
+  return PV_OK;
+}
+
+pv_status pv_tower_plan_tiles_u8(const pv_tower* t, const int32_t* src_hw, int32_t n_images, int32_t max_num_tiles,
+                                 int32_t* layout, pv_plan_info* info) {
+  g_last_error.clear();
+  if (!t || !info) return fail(PV_ERR_ARG, "tower and info must not be null");
   pv::Plan plan;
-  std::vector<int32_t> hw;
-  pv_status st = make_plan_u8(t, src_hw, n_images, &plan, &hw);
+  std::vector<int32_t> lay;
+  pv_status st = make_plan_tiles_u8(t, src_hw, n_images, max_num_tiles, &plan, &lay);
   if (st != PV_OK) return st;
-  if (out_rows_cap < plan.out_rows)
-    return fail(PV_ERR_CAPACITY, "out_rows_cap " + std::to_string(out_rows_cap) + " < " + std::to_string(plan.out_rows));
-  if (ws_bytes < plan.ws.total)
-    return fail(PV_ERR_CAPACITY, "workspace " + std::to_string(ws_bytes) + " < " + std::to_string(plan.ws.total));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  if ((st = upload_and_maps(t, plan, ws, s)) != PV_OK) return st;
-  return run_tower(t, px, plan, out, ws, StageStop(), s);
+  if (layout) std::memcpy(layout, lay.data(), sizeof(int32_t) * lay.size());
+  fill_info(t, plan, info);
+  return PV_OK;
+}
+
+pv_status pv_config_preset(int32_t preset, int32_t dtype, pv_config* cfg) {
+  g_last_error.clear();
+  if (!cfg) return fail(PV_ERR_ARG, "cfg must not be null");
+  if (dtype != PV_BF16 && dtype != PV_F32) return fail(PV_ERR_ARG, "dtype must be PV_BF16 or PV_F32");
+  pv_config c{};
+  c.hidden = 1024;
+  c.heads = 16;
+  c.mlp = 4096;
+  c.layers = 24;
+  c.rope_theta = 1.0e4;
+  c.rms_eps = 1.0e-5;
+  c.dtype = dtype;
+  c.out_dtype = dtype;
+  c.flags = 0;
+  if (preset == PV_PRESET_MISTRAL3) {
+    c.patch = 14;
+    c.merge = 2;
+    c.out_dim = 5120;
+    c.max_side = 1540;
+  } else if (preset == PV_PRESET_PIXTRAL12B) {
+    c.patch = 16;
+    c.merge = 1;
+    c.out_dim = 0;
+    c.max_side = 1024;
+  } else {
+    return fail(PV_ERR_ARG, "unknown preset");
+  }
+  *cfg = c;
+  return PV_OK;
 }
 
 pv_status pv_preprocess_u8(const uint8_t* images, const int32_t* src_hw, const int32_t* dst_hw, int32_t n_images,
@@ -571,7 +698,12 @@ pv_status pv_preprocess_u8(const uint8_t* images, const int32_t* src_hw, const i
   size_t soff = 0, doff = 0;
   for (int32_t i = 0; i < n_images; ++i) {
     const int32_t sH = src_hw[2 * i], sW = src_hw[2 * i + 1], tH = dst_hw[2 * i], tW = dst_hw[2 * i + 1];
-    PV_HIP(pv::resize_norm_u8(images + soff, sH, sW, tH, tW, aff, out + doff, s));
+    pv::SrcImage sm{};
+    sm.H = sH;
+    sm.W = sW;
+    sm.RH = tH;
+    sm.RW = tW;
+    PV_HIP(pv::resize_norm_u8(images + soff, sm, tH, tW, aff, out + doff, s));
     soff += size_t(3) * sH * sW;
     doff += size_t(3) * tH * tW;
   }

@@ -22,7 +22,9 @@ STATUS = {0: "PV_OK", -1: "PV_ERR_ARG", -2: "PV_ERR_SHAPE", -3: "PV_ERR_CAPACITY
 EXPORTED = ("pv_tower_create", "pv_tower_destroy", "pv_tower_plan", "pv_tower_forward",
             "pv_tower_forward_stage", "pv_tower_index_maps", "pv_tower_set_profiling", "pv_tower_read_profile",
             "pv_scatter_workspace_bytes", "pv_scatter_image_embeddings", "pv_resize_target", "pv_tower_plan_u8",
-            "pv_tower_forward_u8", "pv_preprocess_u8", "pv_last_error", "pv_status_str")
+            "pv_tower_forward_u8", "pv_preprocess_u8", "pv_tile_layout", "pv_tower_plan_tiles_u8",
+            "pv_tower_forward_tiles_u8", "pv_config_preset", "pv_last_error", "pv_status_str")
+PRESETS = {"mistral3": 0, "pixtral12b": 1}
 KERNEL_CLASSES = ("maps", "patch", "norm", "qkv", "attn", "oproj", "gateup", "down", "merge")
 
 
@@ -95,6 +97,14 @@ def load_library(path: str = LIB_PATH):
     lib.pv_tower_forward_u8.restype = i32
     lib.pv_preprocess_u8.argtypes = [vp, vp, vp, i32, vp, vp, vp]
     lib.pv_preprocess_u8.restype = i32
+    lib.pv_tile_layout.argtypes = [vp, i32, i32, i32, i32, vp]
+    lib.pv_tile_layout.restype = i32
+    lib.pv_tower_plan_tiles_u8.argtypes = [vp, vp, i32, i32, vp, C.POINTER(PvPlanInfo)]
+    lib.pv_tower_plan_tiles_u8.restype = i32
+    lib.pv_tower_forward_tiles_u8.argtypes = [vp, vp, vp, i32, i32, vp, vp, i64, vp, sz, vp]
+    lib.pv_tower_forward_tiles_u8.restype = i32
+    lib.pv_config_preset.argtypes = [i32, i32, C.POINTER(PvConfig)]
+    lib.pv_config_preset.restype = i32
     lib.pv_last_error.argtypes = []
     lib.pv_last_error.restype = C.c_char_p
     lib.pv_status_str.argtypes = [i32]
@@ -227,6 +237,29 @@ class Tower:
                                             out.shape[0], ws.data_ptr(), ws.numel(), s))
         return out
 
+    def plan_tiles_u8(self, src_hw, max_num_tiles: int):
+        """Plan of the tiles of uint8 sources: (info, per-image (resized H,
+        resized W, tile rows, tile columns))."""
+        arr, n = _hw_array(src_hw)
+        lay = (C.c_int32 * (4 * n))()
+        info = PvPlanInfo()
+        _check(self.lib.pv_tower_plan_tiles_u8(self.handle, arr, n, int(max_num_tiles), lay, C.byref(info)))
+        return info, [tuple(lay[4 * i: 4 * i + 4]) for i in range(n)]
+
+    def forward_tiles_u8(self, images, src_hw, max_num_tiles: int, mean_std=None, out=None, stream=None):
+        """The tower over the tiles of uint8 images (flat CUDA tensor)."""
+        import torch
+        arr, n = _hw_array(src_hw)
+        info, _ = self.plan_tiles_u8(src_hw, max_num_tiles)
+        if out is None:
+            out = torch.empty((info.out_rows, info.out_cols), dtype=self._out_dtype(), device="cuda")
+        ws = self.workspace(info.workspace_bytes)
+        s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+        ms = (C.c_float * 6)(*mean_std) if mean_std is not None else None
+        _check(self.lib.pv_tower_forward_tiles_u8(self.handle, images.data_ptr(), arr, n, int(max_num_tiles), ms,
+                                                  out.data_ptr(), out.shape[0], ws.data_ptr(), ws.numel(), s))
+        return out
+
     def set_profiling(self, enable: bool):
         _check(self.lib.pv_tower_set_profiling(self.handle, 1 if enable else 0))
 
@@ -311,6 +344,23 @@ def resize_target(src_hw, longest_edge: int, grid: int) -> List[Tuple[int, int]]
     dst = (C.c_int32 * (2 * n))()
     _check(lib.pv_resize_target(arr, n, int(longest_edge), int(grid), dst))
     return [(dst[2 * i], dst[2 * i + 1]) for i in range(n)]
+
+
+def tile_layout(src_hw, tile: int, grid: int, max_num_tiles: int) -> List[Tuple[int, int, int, int]]:
+    """Per image (resized H, resized W, tile rows, tile columns) (host only)."""
+    lib = load_library()
+    arr, n = _hw_array(src_hw)
+    lay = (C.c_int32 * (4 * n))()
+    _check(lib.pv_tile_layout(arr, n, int(tile), int(grid), int(max_num_tiles), lay))
+    return [tuple(lay[4 * i: 4 * i + 4]) for i in range(n)]
+
+
+def preset(name: str, dtype: str = "bf16") -> PvConfig:
+    """PvConfig of a named tower ("mistral3" or "pixtral12b")."""
+    lib = load_library()
+    cfg = PvConfig()
+    _check(lib.pv_config_preset(PRESETS[name], PV_BF16 if dtype == "bf16" else PV_F32, C.byref(cfg)))
+    return cfg
 
 
 def preprocess_u8(images, src_hw, dst_hw, mean_std=None, out=None):
