@@ -463,6 +463,42 @@ def tile_batch(images: Sequence[np.ndarray], tile: int, grid: int, max_num_tiles
 
 
 # --------------------------------------------------------------------------
+# content key of a uint8 image (embeddings cache)
+# --------------------------------------------------------------------------
+_M64 = (1 << 64) - 1
+KEY_G = (0x9E3779B97F4A7C15, 0xD1B54A32D192ED03)
+
+
+def splitmix64_mix(z: int) -> int:
+    """Output function of the SplitMix64 generator (Steele, Lea and Flood,
+    2014; Vigna's constants), on Python integers mod 2^64."""
+    z &= _M64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+    return z ^ (z >> 31)
+
+
+def image_key(img_u8: np.ndarray) -> Tuple[int, int]:
+    """Two 64-bit lanes over an H x W x 3 uint8 image, for the multimodal
+    embeddings cache (the inference-research record's per-model cache):
+    words w_i = the bytes as little-endian 64-bit integers, zero-padded;
+    acc_s = sum_i mix(w_i + (i + 1) G_s) mod 2^64;
+    key_s = mix(acc_s + mix(((H << 32) | W) ^ G_s)).  Written as a loop over
+    Python integers (small images only)."""
+    img = np.asarray(img_u8, dtype=np.uint8)
+    h, w = img.shape[:2]
+    data = img.tobytes()
+    keys = []
+    for g in KEY_G:
+        acc = 0
+        for i in range(0, len(data), 8):
+            word = int.from_bytes(data[i:i + 8].ljust(8, b"\0"), "little")
+            acc = (acc + splitmix64_mix(word + (i // 8 + 1) * g)) & _M64
+        keys.append(splitmix64_mix(acc + splitmix64_mix(((h << 32) | w) ^ g)))
+    return keys[0], keys[1]
+
+
+# --------------------------------------------------------------------------
 # whole tower
 # --------------------------------------------------------------------------
 def tower_forward(

@@ -641,3 +641,37 @@ def test_tiles_without_scaling_are_normalised_source_crops():
     std = np.asarray(O.PROCESSOR_STD)[:, None, None]
     crop = img[32:64, 64:96].transpose(2, 0, 1).astype(np.float64)
     np.testing.assert_allclose(tiles[5], (crop / 255.0 - mean) / std, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------- embeddings cache key
+def test_splitmix64_published_outputs():
+    """SplitMix64 from state 0: state advances by 0x9E3779B97F4A7C15 and each
+    output is mix(state); the generator's first three outputs are the
+    published 0xe220a8397b1dcdaf, 0x6e789e6aa1b965f4, 0x06c45d188009454f."""
+    g = 0x9E3779B97F4A7C15
+    want = [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+    got = [O.splitmix64_mix((k + 1) * g & ((1 << 64) - 1)) for k in range(3)]
+    assert got == want
+
+
+def test_image_key_properties():
+    rng = np.random.default_rng(29)
+    img = rng.integers(0, 256, size=(5, 7, 3), dtype=np.uint8)
+    k = O.image_key(img)
+    assert k == O.image_key(img.copy()) and k[0] != k[1]
+    # one changed byte, two swapped words, or the same bytes as another shape
+    # give other keys
+    b = img.copy()
+    b[4, 6, 2] ^= 1
+    assert O.image_key(b) != k
+    flat = img.reshape(-1).copy()
+    flat[0:8], flat[8:16] = img.reshape(-1)[8:16], img.reshape(-1)[0:8]
+    if not np.array_equal(flat, img.reshape(-1)):
+        assert O.image_key(flat.reshape(5, 7, 3)) != k
+    assert O.image_key(img.reshape(7, 5, 3)) != k
+    # the zero padding of the last word: 1 x 1 image = one word of 3 bytes
+    one = np.array([[[1, 2, 3]]], dtype=np.uint8)
+    word = 1 | (2 << 8) | (3 << 16)
+    want0 = O.splitmix64_mix((O.splitmix64_mix(word + O.KEY_G[0]) + O.splitmix64_mix((1 << 32 | 1) ^ O.KEY_G[0]))
+                             & ((1 << 64) - 1))
+    assert O.image_key(one)[0] == want0
