@@ -356,6 +356,68 @@ pv_status pv_tower_forward_tiles_u8(pv_tower* t, const uint8_t* images, const in
 enum { PV_PRESET_MISTRAL3 = 0, PV_PRESET_PIXTRAL12B = 1 };
 pv_status pv_config_preset(int32_t preset, int32_t dtype, pv_config* cfg);
 
+/* ---- multimodal embeddings cache (the inference-research record: an engine
+ * keeps a per-model cache of multimodal embeddings next to an encoder side
+ * stream).  The cache maps an image's content key to its output rows, kept
+ * in caller-owned device memory; a hit skips the tower.  The side stream
+ * needs no entry point: every call runs on the stream it is given, so the
+ * encoder can be enqueued on its own stream and the consumer can wait on an
+ * event recorded after it. */
+
+/* Content keys of uint8 images (layout as for pv_tower_forward_u8; images
+ * 4-byte aligned): keys (device uint64 [n_images][2]) = two 64-bit lanes per
+ * image over its bytes and size.  Definition (exact, so a caller can compute
+ * the same key on the host): mix(z) is SplitMix64's output function
+ * (z ^= z >> 30; z *= 0xBF58476D1CE4E5B9; z ^= z >> 27;
+ * z *= 0x94D049BB133111EB; z ^= z >> 31); w_i are the image's 3HW bytes as
+ * little-endian 64-bit words, the last one zero-padded;
+ * acc_s = sum_i mix(w_i + (i + 1) * G_s) mod 2^64;
+ * key_s = mix(acc_s + mix(((H << 32) | W) ^ G_s)), G_0 = 0x9E3779B97F4A7C15,
+ * G_1 = 0xD1B54A32D192ED03.  Not cryptographic.  workspace: device,
+ * >= pv_image_keys_workspace_bytes(n_images), 256-byte aligned.
+ * Errors: PV_ERR_ARG, PV_ERR_SHAPE, PV_ERR_CAPACITY, PV_ERR_HIP. */
+size_t pv_image_keys_workspace_bytes(int32_t n_images);
+pv_status pv_image_keys_u8(const uint8_t* images, const int32_t* src_hw, int32_t n_images,
+                           uint64_t* keys, void* workspace, size_t ws_bytes, void* stream);
+
+typedef struct pv_embcache pv_embcache;
+
+/* Creates a cache over cache_mem (device, cache_bytes, 16-byte aligned,
+ * owned by the caller) for tower t (borrowed; it must outlive the cache).
+ * It holds cache_bytes / row_bytes output rows (row_bytes = out_cols times
+ * the output element size).  mean_std (host [6] or NULL, copied) is the
+ * normalisation every cached forward uses.  Errors: PV_ERR_ARG,
+ * PV_ERR_CAPACITY (not one row). */
+pv_status pv_embcache_create(pv_tower* t, const float* mean_std, void* cache_mem,
+                             int64_t cache_bytes, pv_embcache** out);
+void pv_embcache_destroy(pv_embcache* c);
+/* Forgets every entry (the memory is kept). */
+pv_status pv_embcache_clear(pv_embcache* c);
+/* stats (host int64 [5]): entries, rows in use, capacity in rows, images
+ * served from the cache, images computed. */
+pv_status pv_embcache_stats(const pv_embcache* c, int64_t* stats);
+/* Workspace (bytes) of a cached forward of these uint8 sources. */
+pv_status pv_embcache_workspace_bytes(const pv_embcache* c, const int32_t* src_hw,
+                                      int32_t n_images, int64_t* bytes);
+
+/* pv_tower_forward_u8 through the cache.  keys: host uint64 [n_images][2]
+ * chosen by the caller (one key per distinct image content and size), or
+ * NULL: then the keys are computed on the device (pv_image_keys_u8) and read
+ * back, which synchronises the stream.  Images whose key is cached are
+ * copied from the cache; the others (each distinct key once) run through
+ * one tower forward into a contiguous run of cache rows at the ring head,
+ * evicting the entries that run overlaps (oldest insertions first), and are
+ * copied out.  out/out_rows_cap: as pv_tower_forward_u8.  hit: host int32
+ * [n_images] or NULL; 1 where the image was served from the cache (also a
+ * repeat of an image computed earlier in the same call), 0 where the tower
+ * ran for it.  Use one stream per cache.
+ * Errors: PV_ERR_ARG, PV_ERR_SHAPE, PV_ERR_CAPACITY (workspace, output, or
+ * the missed images need more rows than the cache holds), PV_ERR_HIP. */
+pv_status pv_tower_forward_cached_u8(pv_embcache* c, const uint8_t* images, const int32_t* src_hw,
+                                     int32_t n_images, const uint64_t* keys, void* out,
+                                     int64_t out_rows_cap, void* workspace, size_t ws_bytes,
+                                     void* stream, int32_t* hit);
+
 /* Thread-local message of the last failure in this thread ("" if none). */
 const char* pv_last_error(void);
 

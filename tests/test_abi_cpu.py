@@ -364,3 +364,46 @@ def test_plan_tiles_u8_counts():
         assert f(h, None, arr, 1, 4, None, FAKE, 1 << 30, ws, 1 << 40, None) == -1
     finally:
         lib.pv_tower_destroy(h)
+
+
+# ------------------------------------------------------------ embeddings cache
+def test_embcache_host_side_without_device_work():
+    cfg = T.make_config(layers=2, max_side=1540)
+    st, h, _ = create(cfg)
+    assert st == 0
+    lib = T.load_library()
+    c = C.c_void_p()
+    try:
+        row = 5120 * 2
+        assert lib.pv_embcache_create(None, None, FAKE, 10 * row, C.byref(c)) == -1
+        assert lib.pv_embcache_create(h, None, FAKE + 8, 10 * row, C.byref(c)) == -1
+        assert lib.pv_embcache_create(h, None, FAKE, row - 1, C.byref(c)) == -3
+        bad = (C.c_float * 6)(0.5, 0.5, 0.5, 0.2, -1.0, 0.2)
+        assert lib.pv_embcache_create(h, bad, FAKE, 10 * row, C.byref(c)) == -1
+        assert lib.pv_embcache_create(h, None, FAKE, 3025 * row + 7, C.byref(c)) == 0
+        st5 = (C.c_int64 * 5)()
+        assert lib.pv_embcache_stats(c, st5) == 0 and list(st5) == [0, 0, 3025, 0, 0]
+        arr, n = T._hw_array([(4096, 4096), (100, 150)])
+        b = C.c_int64()
+        assert lib.pv_embcache_workspace_bytes(c, arr, n, C.byref(b)) == 0
+        info = T.PvPlanInfo()
+        assert lib.pv_tower_plan_u8(h, arr, n, None, C.byref(info)) == 0
+        assert b.value >= info.workspace_bytes + 2 * 16
+        f = lib.pv_tower_forward_cached_u8
+        ws = FAKE * 256
+        assert f(None, FAKE, arr, n, None, FAKE, 1 << 20, ws, 1 << 40, None, None) == -1
+        assert f(c, FAKE, arr, 0, None, FAKE, 1 << 20, ws, 1 << 40, None, None) == -1
+        assert f(c, FAKE + 1, arr, n, None, FAKE, 1 << 20, ws, 1 << 40, None, None) == -1   # hashing needs 4-byte alignment
+        assert f(c, FAKE, arr, n, None, FAKE, 1 << 20, ws, b.value - 1, None, None) == -3
+        assert f(c, FAKE, arr, n, None, FAKE, info.out_rows - 1, ws, 1 << 40, None, None) == -3
+        big, nb = T._hw_array([(0, 5)])
+        assert f(c, FAKE, big, nb, None, FAKE, 1 << 20, ws, 1 << 40, None, None) == -2
+        assert lib.pv_embcache_clear(c) == 0
+        kw = lib.pv_image_keys_workspace_bytes(3)
+        assert kw >= 48 and kw % 256 == 0 and lib.pv_image_keys_workspace_bytes(0) == 0
+        assert lib.pv_image_keys_u8(FAKE, arr, n, FAKE, ws, 16, None) == -3
+        assert lib.pv_image_keys_u8(FAKE + 2, arr, n, FAKE, ws, 1 << 20, None) == -1
+        assert lib.pv_image_keys_u8(FAKE, big, nb, FAKE, ws, 1 << 20, None) == -2
+    finally:
+        lib.pv_embcache_destroy(c)
+        lib.pv_tower_destroy(h)

@@ -18,8 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpv_tower.so")
 
-SOURCES = ["plan.cpp", "tower.cpp", "maps.hip", "norm.hip", "prep.hip", "gemm_bf16.hip", "attn_bf16.hip", "f32_path.hip",
-           "scatter.hip"]
+SOURCES = ["plan.cpp", "tower.cpp", "embcache.cpp", "maps.hip", "norm.hip", "prep.hip", "gemm_bf16.hip",
+           "attn_bf16.hip", "f32_path.hip", "scatter.hip", "hash.hip"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -96,6 +96,13 @@ hipError_t pad_rows(const void* w, void* out, int rows, int K, int Kp, hipStream
 //   gateup_fp8:   b8 [2F][D] fp8 e4m3 = the gate/up weights in the GEMM's
 //                 interleaved row order, bs [D/128][2F][4] scale bytes
 hipError_t gateup_fp8(const void* w_gate, const void* w_up, void* b8, void* bs, int F, int D, hipStream_t s);
+// Content keys of uint8 images (two 64-bit lanes per image, keys [n][2]
+// device); offsets[i] (host) is image i's byte offset from `images`, which
+// must be 4-byte aligned; src_hw host; ws: image_keys_workspace_bytes(n)
+// bytes (the accumulators).
+size_t image_keys_workspace_bytes(int n);
+hipError_t image_keys(const uint8_t* images, const int32_t* src_hw, const uint64_t* offsets, int n, uint64_t* keys,
+                      void* ws, hipStream_t s);
 // Masked scatter: the k-th position p with ids[p] == token takes row k of src
 // (k < rows); status[0] = (placeholder count == rows) ? 0 : 1.  ws: a list of
 // n positions + the count (scatter_workspace_bytes(n) bytes).

@@ -20,24 +20,18 @@
 #include <vector>
 
 #include "../../include/pv_tower.h"
+#include "api.h"
 #include "kernels.h"
 #include "plan.h"
 
-namespace {
-
-thread_local std::string g_last_error;
-
-pv_status fail(pv_status s, const std::string& msg) {
-  g_last_error = msg;
-  return s;
+std::string& pv::last_error() {
+  thread_local std::string msg;
+  return msg;
 }
 
-#define PV_HIP(call)                                                                        \
-  do {                                                                                      \
-    hipError_t e_ = (call);                                                                 \
-    if (e_ != hipSuccess)                                                                   \
-      return fail(PV_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_));           \
-  } while (0)
+namespace {
+
+using pv::fail;
 
 // A timed launch: event before/after when the tower is profiling.
 #define PV_LAUNCH(kind, call)              \
@@ -360,7 +354,7 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
 // Target sizes of uint8 source images for this tower (longest edge = max_side,
 // grid = patch * merge), the plan of those sizes, and the source offsets.
 pv_status make_plan_u8(const pv_tower* t, const int32_t* src_hw, int32_t n, pv::Plan* plan,
-                       std::vector<int32_t>* dst_hw) {
+                       std::vector<int32_t>* dst_hw, const uint64_t* offsets = nullptr) {
   if (!src_hw) return fail(PV_ERR_ARG, "src_hw must not be null");
   if (n < 1) return fail(PV_ERR_ARG, "n_images must be >= 1 (the tower runs only on image input)");
   dst_hw->assign(size_t(2) * n, 0);
@@ -382,8 +376,9 @@ pv_status make_plan_u8(const pv_tower* t, const int32_t* src_hw, int32_t n, pv::
     sm.RH = (*dst_hw)[2 * i];
     sm.RW = (*dst_hw)[2 * i + 1];
     sm.y0 = sm.x0 = 0;
-    sm.off_lo = uint32_t(off & 0xffffffffu);
-    sm.off_hi = uint32_t(off >> 32);
+    const uint64_t o = offsets ? offsets[i] : off;
+    sm.off_lo = uint32_t(o & 0xffffffffu);
+    sm.off_hi = uint32_t(o >> 32);
     off += uint64_t(3) * uint64_t(sm.H) * uint64_t(sm.W);
   }
   return PV_OK;
@@ -457,8 +452,8 @@ pv_status check_call(const pv_tower* t, const float* pixels, const int32_t* imag
 // edge rule), else cuts it into tiles of max_side.
 pv_status forward_u8_common(pv_tower* t, const uint8_t* images, const int32_t* src_hw, int32_t n_images,
                             int32_t max_num_tiles, const float* mean_std, void* out, int64_t out_rows_cap,
-                            void* workspace, size_t ws_bytes, void* stream) {
-  g_last_error.clear();
+                            void* workspace, size_t ws_bytes, void* stream, const uint64_t* offsets = nullptr) {
+  pv::last_error().clear();
   if (!t) return fail(PV_ERR_ARG, "tower is null");
   if (!images || !out || !workspace) return fail(PV_ERR_ARG, "images, output and workspace must not be null");
   if (!aligned(out, 16)) return fail(PV_ERR_ARG, "output must be 16-byte aligned");
@@ -469,7 +464,7 @@ pv_status forward_u8_common(pv_tower* t, const uint8_t* images, const int32_t* s
   pv::Plan plan;
   std::vector<int32_t> hw;
   pv_status st = max_num_tiles > 0 ? make_plan_tiles_u8(t, src_hw, n_images, max_num_tiles, &plan, &hw)
-                                   : make_plan_u8(t, src_hw, n_images, &plan, &hw);
+                                   : make_plan_u8(t, src_hw, n_images, &plan, &hw, offsets);
   if (st != PV_OK) return st;
   if (out_rows_cap < plan.out_rows)
     return fail(PV_ERR_CAPACITY, "out_rows_cap " + std::to_string(out_rows_cap) + " < " + std::to_string(plan.out_rows));
@@ -483,9 +478,31 @@ pv_status forward_u8_common(pv_tower* t, const uint8_t* images, const int32_t* s
 
 }  // namespace
 
+pv_status pv::u8_out_rows(const pv_tower* t, const int32_t* src_hw, int32_t n, std::vector<int64_t>* rows,
+                          int64_t* row_bytes, int64_t* ws_bytes) {
+  pv::Plan plan;
+  std::vector<int32_t> hw;
+  pv_status st = make_plan_u8(t, src_hw, n, &plan, &hw);
+  if (st != PV_OK) return st;
+  rows->resize(n);
+  for (int32_t i = 0; i < n; ++i)
+    (*rows)[i] = (i + 1 < n ? plan.meta[i + 1].tok_base : plan.out_rows) - plan.meta[i].tok_base;
+  const int64_t cols = t->cfg.merge == 2 ? t->cfg.out_dim : t->cfg.hidden;
+  const int64_t es = (t->cfg.dtype == PV_BF16 && t->cfg.out_dtype == PV_BF16) ? 2 : 4;
+  *row_bytes = cols * es;
+  *ws_bytes = int64_t(plan.ws.total);
+  return PV_OK;
+}
+
+pv_status pv::forward_u8_at(pv_tower* t, const uint8_t* images, const int32_t* src_hw, const uint64_t* offsets,
+                            int32_t n, const float* mean_std, void* out, int64_t out_rows_cap, void* workspace,
+                            size_t ws_bytes, hipStream_t s) {
+  return forward_u8_common(t, images, src_hw, n, 0, mean_std, out, out_rows_cap, workspace, ws_bytes, s, offsets);
+}
+
 extern "C" {
 
-const char* pv_last_error(void) { return g_last_error.c_str(); }
+const char* pv_last_error(void) { return pv::last_error().c_str(); }
 
 const char* pv_status_str(pv_status s) {
   switch (s) {
@@ -500,7 +517,7 @@ const char* pv_status_str(pv_status s) {
 }
 
 pv_status pv_tower_create(const pv_config* cfg, const pv_weights* w, pv_tower** out) {
-  g_last_error.clear();
+  pv::last_error().clear();
   if (!cfg || !w || !out) return fail(PV_ERR_ARG, "cfg, weights and out must not be null");
   *out = nullptr;
   const pv_config& c = *cfg;
@@ -563,7 +580,7 @@ void pv_tower_destroy(pv_tower* t) {
 }
 
 pv_status pv_tower_plan(const pv_tower* t, const int32_t* image_hw, int32_t n_images, pv_plan_info* info) {
-  g_last_error.clear();
+  pv::last_error().clear();
   if (!t || !info) return fail(PV_ERR_ARG, "tower and info must not be null");
   pv::Plan plan;
   pv_status st = make_plan(t, image_hw, n_images, &plan);
@@ -574,7 +591,7 @@ pv_status pv_tower_plan(const pv_tower* t, const int32_t* image_hw, int32_t n_im
 
 pv_status pv_resize_target(const int32_t* src_hw, int32_t n_images, int32_t longest_edge, int32_t grid,
                            int32_t* dst_hw) {
-  g_last_error.clear();
+  pv::last_error().clear();
   if (!src_hw || !dst_hw) return fail(PV_ERR_ARG, "src_hw and dst_hw must not be null");
   if (n_images < 1) return fail(PV_ERR_ARG, "n_images must be >= 1");
   std::string err;
@@ -591,7 +608,7 @@ pv_status pv_resize_target(const int32_t* src_hw, int32_t n_images, int32_t long
 
 pv_status pv_tower_plan_u8(const pv_tower* t, const int32_t* src_hw, int32_t n_images, int32_t* dst_hw,
                            pv_plan_info* info) {
-  g_last_error.clear();
+  pv::last_error().clear();
   if (!t || !info) return fail(PV_ERR_ARG, "tower and info must not be null");
   pv::Plan plan;
   std::vector<int32_t> hw;
@@ -612,7 +629,7 @@ pv_status pv_tower_forward_tiles_u8(pv_tower* t, const uint8_t* images, const in
                                     int32_t max_num_tiles, const float* mean_std, void* out, int64_t out_rows_cap,
                                     void* workspace, size_t ws_bytes, void* stream) {
   if (max_num_tiles < 1) {
-    g_last_error = "max_num_tiles must be >= 1";
+    pv::last_error() = "max_num_tiles must be >= 1";
     return PV_ERR_ARG;
   }
   return forward_u8_common(t, images, src_hw, n_images, max_num_tiles, mean_std, out, out_rows_cap, workspace,
@@ -621,7 +638,7 @@ pv_status pv_tower_forward_tiles_u8(pv_tower* t, const uint8_t* images, const in
 
 pv_status pv_tile_layout(const int32_t* src_hw, int32_t n_images, int32_t tile, int32_t grid, int32_t max_num_tiles,
                          int32_t* layout) {
-  g_last_error.clear();
+  pv::last_error().clear();
   if (!src_hw || !layout) return fail(PV_ERR_ARG, "src_hw and layout must not be null");
   if (n_images < 1) return fail(PV_ERR_ARG, "n_images must be >= 1");
   std::string err;
@@ -637,7 +654,7 @@ pv_status pv_tile_layout(const int32_t* src_hw, int32_t n_images, int32_t tile, 
 
 pv_status pv_tower_plan_tiles_u8(const pv_tower* t, const int32_t* src_hw, int32_t n_images, int32_t max_num_tiles,
                                  int32_t* layout, pv_plan_info* info) {
-  g_last_error.clear();
+  pv::last_error().clear();
   if (!t || !info) return fail(PV_ERR_ARG, "tower and info must not be null");
   pv::Plan plan;
   std::vector<int32_t> lay;
@@ -649,7 +666,7 @@ pv_status pv_tower_plan_tiles_u8(const pv_tower* t, const int32_t* src_hw, int32
 }
 
 pv_status pv_config_preset(int32_t preset, int32_t dtype, pv_config* cfg) {
-  g_last_error.clear();
+  pv::last_error().clear();
   if (!cfg) return fail(PV_ERR_ARG, "cfg must not be null");
   if (dtype != PV_BF16 && dtype != PV_F32) return fail(PV_ERR_ARG, "dtype must be PV_BF16 or PV_F32");
   pv_config c{};
@@ -681,7 +698,7 @@ pv_status pv_config_preset(int32_t preset, int32_t dtype, pv_config* cfg) {
 
 pv_status pv_preprocess_u8(const uint8_t* images, const int32_t* src_hw, const int32_t* dst_hw, int32_t n_images,
                            const float* mean_std, float* out, void* stream) {
-  g_last_error.clear();
+  pv::last_error().clear();
   if (!images || !src_hw || !dst_hw || !out) return fail(PV_ERR_ARG, "images, src_hw, dst_hw and out must not be null");
   if (n_images < 1) return fail(PV_ERR_ARG, "n_images must be >= 1");
   if (!aligned(out, 4)) return fail(PV_ERR_ARG, "out must be 4-byte aligned");
@@ -712,7 +729,7 @@ pv_status pv_preprocess_u8(const uint8_t* images, const int32_t* src_hw, const i
 
 pv_status pv_tower_forward(pv_tower* t, const float* pixels, const int32_t* image_hw, int32_t n_images, void* out,
                            int64_t out_rows_cap, void* workspace, size_t ws_bytes, void* stream) {
-  g_last_error.clear();
+  pv::last_error().clear();
   pv_status st = check_call(t, pixels, image_hw, n_images, out, workspace);
   if (st != PV_OK) return st;
   pv::Plan plan;
@@ -732,7 +749,7 @@ pv_status pv_tower_forward(pv_tower* t, const float* pixels, const int32_t* imag
 pv_status pv_tower_forward_stage(pv_tower* t, const float* pixels, const int32_t* image_hw, int32_t n_images,
                                  int32_t stage, int32_t layer, void* dst, int64_t dst_bytes, void* workspace,
                                  size_t ws_bytes, void* stream) {
-  g_last_error.clear();
+  pv::last_error().clear();
   pv_status st = check_call(t, pixels, image_hw, n_images, dst, workspace);
   if (st != PV_OK) return st;
   if (stage < PV_STAGE_PATCH_EMBED || stage > PV_STAGE_BLOCK_OUT) return fail(PV_ERR_ARG, "unknown stage");
@@ -765,7 +782,7 @@ pv_status pv_tower_forward_stage(pv_tower* t, const float* pixels, const int32_t
 pv_status pv_tower_index_maps(pv_tower* t, const int32_t* image_hw, int32_t n_images, int32_t* cu_seqlens,
                               int32_t* patch_rc, int32_t* merge_src, int32_t on_device, void* workspace,
                               size_t ws_bytes, void* stream) {
-  g_last_error.clear();
+  pv::last_error().clear();
   if (!t || !cu_seqlens || !patch_rc) return fail(PV_ERR_ARG, "tower, cu_seqlens and patch_rc must not be null");
   pv::Plan plan;
   pv_status st = make_plan(t, image_hw, n_images, &plan);
@@ -795,7 +812,7 @@ pv_status pv_scatter_image_embeddings(const int32_t* token_ids, int64_t seq_len,
                                       const void* image_emb, int64_t n_image_rows, void* text_emb, int32_t dim,
                                       int32_t elem_bytes, int32_t* status, void* workspace, size_t ws_bytes,
                                       void* stream) {
-  g_last_error.clear();
+  pv::last_error().clear();
   if (!status || !workspace) return fail(PV_ERR_ARG, "status and workspace must not be null");
   if (seq_len < 0 || n_image_rows < 0) return fail(PV_ERR_ARG, "seq_len and n_image_rows must be >= 0");
   if (seq_len > INT32_MAX || n_image_rows > INT32_MAX) return fail(PV_ERR_ARG, "seq_len and n_image_rows must fit int32");
@@ -816,7 +833,7 @@ pv_status pv_scatter_image_embeddings(const int32_t* token_ids, int64_t seq_len,
 }
 
 pv_status pv_tower_set_profiling(pv_tower* t, int32_t enable) {
-  g_last_error.clear();
+  pv::last_error().clear();
   if (!t) return fail(PV_ERR_ARG, "tower is null");
   if (enable) {
     for (auto& r : t->recs) {
@@ -831,7 +848,7 @@ pv_status pv_tower_set_profiling(pv_tower* t, int32_t enable) {
 }
 
 pv_status pv_tower_read_profile(pv_tower* t, double* ms, int64_t* launches, int32_t reset) {
-  g_last_error.clear();
+  pv::last_error().clear();
   if (!t || !ms || !launches) return fail(PV_ERR_ARG, "tower, ms and launches must not be null");
   for (int k = 0; k < PV_K_COUNT; ++k) {
     ms[k] = 0.0;

@@ -23,7 +23,9 @@ EXPORTED = ("pv_tower_create", "pv_tower_destroy", "pv_tower_plan", "pv_tower_fo
             "pv_tower_forward_stage", "pv_tower_index_maps", "pv_tower_set_profiling", "pv_tower_read_profile",
             "pv_scatter_workspace_bytes", "pv_scatter_image_embeddings", "pv_resize_target", "pv_tower_plan_u8",
             "pv_tower_forward_u8", "pv_preprocess_u8", "pv_tile_layout", "pv_tower_plan_tiles_u8",
-            "pv_tower_forward_tiles_u8", "pv_config_preset", "pv_last_error", "pv_status_str")
+            "pv_tower_forward_tiles_u8", "pv_config_preset", "pv_image_keys_workspace_bytes", "pv_image_keys_u8",
+            "pv_embcache_create", "pv_embcache_destroy", "pv_embcache_clear", "pv_embcache_stats",
+            "pv_embcache_workspace_bytes", "pv_tower_forward_cached_u8", "pv_last_error", "pv_status_str")
 PRESETS = {"mistral3": 0, "pixtral12b": 1}
 KERNEL_CLASSES = ("maps", "patch", "norm", "qkv", "attn", "oproj", "gateup", "down", "merge")
 
@@ -105,6 +107,22 @@ def load_library(path: str = LIB_PATH):
     lib.pv_tower_forward_tiles_u8.restype = i32
     lib.pv_config_preset.argtypes = [i32, i32, C.POINTER(PvConfig)]
     lib.pv_config_preset.restype = i32
+    lib.pv_image_keys_workspace_bytes.argtypes = [i32]
+    lib.pv_image_keys_workspace_bytes.restype = sz
+    lib.pv_image_keys_u8.argtypes = [vp, vp, i32, vp, vp, sz, vp]
+    lib.pv_image_keys_u8.restype = i32
+    lib.pv_embcache_create.argtypes = [vp, vp, vp, i64, C.POINTER(vp)]
+    lib.pv_embcache_create.restype = i32
+    lib.pv_embcache_destroy.argtypes = [vp]
+    lib.pv_embcache_destroy.restype = None
+    lib.pv_embcache_clear.argtypes = [vp]
+    lib.pv_embcache_clear.restype = i32
+    lib.pv_embcache_stats.argtypes = [vp, vp]
+    lib.pv_embcache_stats.restype = i32
+    lib.pv_embcache_workspace_bytes.argtypes = [vp, vp, i32, C.POINTER(C.c_int64)]
+    lib.pv_embcache_workspace_bytes.restype = i32
+    lib.pv_tower_forward_cached_u8.argtypes = [vp, vp, vp, i32, vp, vp, i64, vp, sz, vp, vp]
+    lib.pv_tower_forward_cached_u8.restype = i32
     lib.pv_last_error.argtypes = []
     lib.pv_last_error.restype = C.c_char_p
     lib.pv_status_str.argtypes = [i32]
@@ -353,6 +371,86 @@ def tile_layout(src_hw, tile: int, grid: int, max_num_tiles: int) -> List[Tuple[
     lay = (C.c_int32 * (4 * n))()
     _check(lib.pv_tile_layout(arr, n, int(tile), int(grid), int(max_num_tiles), lay))
     return [tuple(lay[4 * i: 4 * i + 4]) for i in range(n)]
+
+
+def image_keys_u8(images, src_hw):
+    """Content keys of uint8 images (flat CUDA tensor): int64 CUDA tensor
+    [n][2] holding the two uint64 lanes' bits."""
+    import torch
+    lib = load_library()
+    arr, n = _hw_array(src_hw)
+    keys = torch.empty((n, 2), dtype=torch.int64, device=images.device)
+    wsb = lib.pv_image_keys_workspace_bytes(n)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=images.device)
+    _check(lib.pv_image_keys_u8(images.data_ptr(), arr, n, keys.data_ptr(), ws.data_ptr(), ws.numel(),
+                                torch.cuda.current_stream().cuda_stream))
+    return keys
+
+
+class EmbCache:
+    """Embeddings cache over a device buffer of `capacity_rows` output rows of
+    `tower`; forward() runs pv_tower_forward_cached_u8."""
+
+    def __init__(self, tower: "Tower", capacity_rows: int, mean_std=None):
+        import torch
+        self.lib = load_library()
+        self.tower = tower
+        cols_dtype = tower._out_dtype()
+        cols = tower.cfg.out_dim if tower.cfg.merge == 2 else tower.cfg.hidden
+        self.mem = torch.empty((capacity_rows, cols), dtype=cols_dtype, device="cuda")
+        self._ms = (C.c_float * 6)(*mean_std) if mean_std is not None else None
+        h = C.c_void_p()
+        _check(self.lib.pv_embcache_create(tower.handle, self._ms, self.mem.data_ptr(),
+                                           self.mem.numel() * self.mem.element_size(), C.byref(h)))
+        self.handle = h
+        self._ws = None
+
+    def workspace_bytes(self, src_hw) -> int:
+        arr, n = _hw_array(src_hw)
+        b = C.c_int64()
+        _check(self.lib.pv_embcache_workspace_bytes(self.handle, arr, n, C.byref(b)))
+        return b.value
+
+    def forward(self, images, src_hw, keys=None, out=None, stream=None):
+        """Returns (out, hits): hits[i] = 1 where image i came from the cache.
+        keys: None (hashed on the device; synchronises) or a host sequence of
+        n pairs of uint64."""
+        import torch
+        arr, n = _hw_array(src_hw)
+        info, _ = self.tower.plan_u8(src_hw)
+        if out is None:
+            out = torch.empty((info.out_rows, info.out_cols), dtype=self.tower._out_dtype(), device="cuda")
+        need = self.workspace_bytes(src_hw)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        k = None
+        if keys is not None:
+            flat = [int(v) & 0xFFFFFFFFFFFFFFFF for pair in keys for v in pair]
+            k = (C.c_uint64 * (2 * n))(*flat)
+        hits = (C.c_int32 * n)()
+        s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+        _check(self.lib.pv_tower_forward_cached_u8(self.handle, images.data_ptr(), arr, n, k, out.data_ptr(),
+                                                   out.shape[0], self._ws.data_ptr(), self._ws.numel(), s, hits))
+        return out, list(hits)
+
+    def stats(self) -> Dict[str, int]:
+        st = (C.c_int64 * 5)()
+        _check(self.lib.pv_embcache_stats(self.handle, st))
+        return dict(zip(("entries", "rows_used", "capacity_rows", "hits", "misses"), list(st)))
+
+    def clear(self):
+        _check(self.lib.pv_embcache_clear(self.handle))
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.pv_embcache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def preset(name: str, dtype: str = "bf16") -> PvConfig:
