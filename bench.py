@@ -258,6 +258,56 @@ def time_u8_input(tw, wl, out, ws, stream, f32_patch_ms, reps=5):
             "preprocess_planes_hbm_frac": round(nbytes / (pre_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def time_embcache(tw, wl, stream, reps=5):
+    """The embeddings cache on the 4096x4096 photo: a miss (keys hashed on
+    the GPU and read back, tower forward into the cache, copy out) and a hit
+    (keys, copy out), each timed on the host around the synchronising call;
+    and the key kernel alone (HIP events), whose algorithmic bytes are the
+    photo's bytes read once."""
+    import torch
+
+    from vlm_vision_encoder_amd import synth
+    from vlm_vision_encoder_amd import tower as T
+    if wl.tiles_from is not None or len(wl.image_hw) != 1:
+        return None
+    src = [(4096, 4096)]
+    info, tgt = tw.plan_u8(src)
+    if tgt != list(wl.image_hw):
+        return None
+    img = torch.from_numpy(synth.make_u8_images(src, seed=3)[0].reshape(-1)).cuda()
+    cache = T.EmbCache(tw, capacity_rows=info.out_rows)
+    sptr = stream.cuda_stream
+    out, _ = cache.forward(img, src, stream=sptr)
+    miss_ms, hit_ms = [], []
+    for _ in range(reps):
+        cache.clear()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        _, h = cache.forward(img, src, out=out, stream=sptr)
+        torch.cuda.synchronize()
+        miss_ms.append((time.perf_counter() - t0) * 1e3)
+        assert h == [0]
+        t0 = time.perf_counter()
+        _, h = cache.forward(img, src, out=out, stream=sptr)
+        torch.cuda.synchronize()
+        hit_ms.append((time.perf_counter() - t0) * 1e3)
+        assert h == [1]
+    T.image_keys_u8(img, src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        T.image_keys_u8(img, src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    keys_ms = e0.elapsed_time(e1) / reps
+    cache.close()
+    return {"source": "4096x4096 uint8 RGB", "rows": int(info.out_rows), "miss_ms": round(min(miss_ms), 4),
+            "hit_ms": round(min(hit_ms), 4), "keys_ms": round(keys_ms, 5),
+            "keys_gbs": round(img.numel() / (keys_ms * 1e-3) / 1e9, 1),
+            "keys_hbm_frac": round(img.numel() / (keys_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def source_sha256(path):
     import hashlib
     with open(path, "rb") as f:
@@ -394,6 +444,7 @@ def main():
     u8_input = None
     if (len(wl.image_hw) == 1 or wl.tiles_from is not None) and "patch" in kernels:
         u8_input = time_u8_input(tw, wl, out, ws, stream, kernels["patch"]["ms_per_step"])
+    embcache = time_embcache(tw, wl, stream)
 
     patches_s = wl.n_patches / (ms_step * 1e-3)
     tokens_s = wl.out_rows / (ms_step * 1e-3)
@@ -420,6 +471,7 @@ def main():
         "kernels": kernels,
         "scatter": scatter,
         "u8_input": u8_input,
+        "embcache": embcache,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
