@@ -258,13 +258,17 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens, heads: in
 # --------------------------------------------------------------------------
 # a7/a8: vision MLP (reading 1: gated SiLU)
 # --------------------------------------------------------------------------
-def swiglu_mlp(y: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+def swiglu_mlp(y: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray,
+               hidden_map=None) -> np.ndarray:
     """down(silu(y gate^T) * (y up^T)), silu(x) = x / (1 + exp(-x))
-    ("Mistral 3", Mistral3Model table, vision_mlp_dim 4096)."""
+    ("Mistral 3", Mistral3Model table, vision_mlp_dim 4096).  ``hidden_map``
+    (optional) is applied to silu * up before the down projection."""
     y = np.asarray(y, dtype=np.float64)
     g = y @ np.asarray(w_gate, dtype=np.float64).T
     u = y @ np.asarray(w_up, dtype=np.float64).T
     hmid = g / (1.0 + np.exp(-g)) * u
+    if hidden_map is not None:
+        hmid = hidden_map(hmid)
     return hmid @ np.asarray(w_down, dtype=np.float64).T
 
 
@@ -499,6 +503,44 @@ def image_key(img_u8: np.ndarray) -> Tuple[int, int]:
 
 
 # --------------------------------------------------------------------------
+# fp8 (e4m3) GEMM variant: block-scaled quantisation of GEMM operands
+# --------------------------------------------------------------------------
+def e4m3_round(v: np.ndarray) -> np.ndarray:
+    """Nearest OCP e4m3 value (1 sign, 4 exponent bits with bias 7, 3
+    mantissa bits; normal range 2^-6 .. 448, subnormal step 2^-9), ties to
+    the even mantissa, as float64.  Inputs must lie within +-464 (no
+    saturation is needed by the block scaling below)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    if np.any(a >= 464.0):
+        raise ValueError("value outside the e4m3 range")
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)          # below 2^-6 the step stays 2^-9
+    step = np.exp2(e - 3.0)
+    q = np.round(a / step) * step    # numpy rounds halves to even
+    return np.sign(v) * q
+
+
+def mx_e4m3(x: np.ndarray) -> np.ndarray:
+    """Block-scaled e4m3 copy of x along its last axis (blocks of 32
+    consecutive elements), dequantised to float64: per block
+    X = floor(log2(max |x|)) - 7 clamped to [-120, 120], values
+    e4m3(x * 2^-X) * 2^X -- the block maximum lands in [128, 256).
+    The scale is a power of two, as in the MX formats' shared exponent
+    (E8M0), one per 32 values."""
+    x = np.asarray(x, dtype=np.float64)
+    k = x.shape[-1]
+    if k % 32:
+        raise ValueError("the quantised axis must be a multiple of 32")
+    blocks = x.reshape(x.shape[:-1] + (k // 32, 32))
+    amax = np.max(np.abs(blocks), axis=-1, keepdims=True)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    X = np.where(amax > 0, ex - 1 - 7, -120).clip(-120, 120).astype(np.float64)
+    q = e4m3_round(blocks * np.exp2(-X)) * np.exp2(X)
+    return q.reshape(x.shape)
+
+
+# --------------------------------------------------------------------------
 # whole tower
 # --------------------------------------------------------------------------
 def tower_forward(
@@ -508,6 +550,7 @@ def tower_forward(
     cfg: TowerConfig,
     layers: Optional[int] = None,
     collect: bool = False,
+    fp8: bool = False,
 ) -> Dict[str, np.ndarray]:
     """Pixels + image sizes -> merged embeddings (or per-patch states when
     merge == 1).
@@ -521,8 +564,12 @@ def tower_forward(
     with ``attn_norm``, ``wq``, ``wk``, ``wv``, ``wo``, ``ffn_norm``,
     ``w_gate``, ``w_up``, ``w_down``), ``merge_w`` [out_dim, 4D].
     ``layers`` limits the depth (default cfg.layers).  With ``collect`` the
-    per-stage tensors are returned too.
+    per-stage tensors are returned too.  With ``fp8`` the four linear maps of
+    every block (q/k/v, out-projection, gate/up, down) take both operands
+    through ``mx_e4m3`` along their contraction axis first (the fp8 GEMM
+    variant); the patch embedding, attention and the merger stay exact.
     """
+    qz = mx_e4m3 if fp8 else (lambda a: a)
     n_layers = cfg.layers if layers is None else layers
     maps = plan_maps(image_hw, cfg.patch, cfg.merge)
     res: Dict[str, np.ndarray] = {"maps": maps}
@@ -538,16 +585,17 @@ def tower_forward(
     rc = maps["patch_rc"]
     for li in range(n_layers):
         lw = weights["layers"][li]
-        y = rms_norm(h, lw["attn_norm"], cfg.rms_eps)
-        q = rope_2d(y @ np.asarray(lw["wq"], np.float64).T, rc, cfg.heads, cfg.rope_theta)
-        k = rope_2d(y @ np.asarray(lw["wk"], np.float64).T, rc, cfg.heads, cfg.rope_theta)
-        v = y @ np.asarray(lw["wv"], np.float64).T
+        W = {k_: qz(np.asarray(lw[k_], np.float64)) for k_ in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")}
+        y = qz(rms_norm(h, lw["attn_norm"], cfg.rms_eps))
+        q = rope_2d(y @ W["wq"].T, rc, cfg.heads, cfg.rope_theta)
+        k = rope_2d(y @ W["wk"].T, rc, cfg.heads, cfg.rope_theta)
+        v = y @ W["wv"].T
         a = attention(q, k, v, cu, cfg.heads)
-        h = h + a @ np.asarray(lw["wo"], np.float64).T
+        h = h + qz(a) @ W["wo"].T
         if collect:
             res["attn_out"].append(h.copy())
-        y = rms_norm(h, lw["ffn_norm"], cfg.rms_eps)
-        h = h + swiglu_mlp(y, lw["w_gate"], lw["w_up"], lw["w_down"])
+        y = qz(rms_norm(h, lw["ffn_norm"], cfg.rms_eps))
+        h = h + swiglu_mlp(y, W["w_gate"], W["w_up"], W["w_down"], hidden_map=qz if fp8 else None)
         if collect:
             res["block_out"].append(h.copy())
     res["tower_out"] = h

@@ -675,3 +675,68 @@ def test_image_key_properties():
     want0 = O.splitmix64_mix((O.splitmix64_mix(word + O.KEY_G[0]) + O.splitmix64_mix((1 << 32 | 1) ^ O.KEY_G[0]))
                              & ((1 << 64) - 1))
     assert O.image_key(one)[0] == want0
+
+
+# -------------------------------------------------------------- fp8 variant
+def test_e4m3_round_table_and_ties():
+    """OCP e4m3: 448 is the largest normal, 2^-6 the smallest normal, 2^-9
+    the subnormal step; halfway cases go to the even mantissa."""
+    cases = {1.0: 1.0, 1.0625: 1.0, 1.1875: 1.25, 448.0: 448.0, 300.0: 288.0, 2.0 ** -6: 2.0 ** -6,
+             2.0 ** -10: 0.0, 1.5 * 2.0 ** -10: 2.0 ** -9, 3 * 2.0 ** -10: 2.0 ** -8, -17.0: -16.0,
+             240.0: 240.0, 250.0: 256.0, 0.0: 0.0}
+    for v, want in cases.items():
+        assert float(O.e4m3_round(np.array([v]))[0]) == want, v
+
+
+def test_e4m3_round_matches_library_cast():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(30)
+    v = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 0.1, 1.0, 30.0, 120.0)])
+    v = v[np.abs(v) < 448].astype(np.float32).astype(np.float64)
+    want = torch.from_numpy(v).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.e4m3_round(v), want)
+
+
+def test_mx_e4m3_block_scale_rule():
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((5, 96)) * np.exp2(rng.integers(-20, 20, size=(5, 1)))
+    q = O.mx_e4m3(x)
+    for r in range(5):
+        for b in range(3):
+            blk, qb = x[r, 32 * b:32 * b + 32], q[r, 32 * b:32 * b + 32]
+            X = math.floor(math.log2(np.max(np.abs(blk)))) - 7
+            scaled = np.max(np.abs(blk)) * 2.0 ** -X
+            assert 128 <= scaled < 256
+            # every value is an e4m3 value times 2^X, within half a step
+            np.testing.assert_array_equal(qb, O.e4m3_round(blk * 2.0 ** -X) * 2.0 ** X)
+            assert np.all(np.abs(qb - blk) <= np.maximum(2.0 ** (np.floor(np.log2(np.abs(blk) + 1e-300)) - 4),
+                                                          2.0 ** (X - 10)) + 1e-300)
+    # an all-zero block stays zero; a block of powers of two is exact
+    z = np.zeros((1, 32))
+    assert np.array_equal(O.mx_e4m3(z), z)
+    p2 = np.exp2(np.arange(-8, 24, dtype=np.float64))[None, :] * -1.0
+    np.testing.assert_array_equal(O.mx_e4m3(p2)[0, 23:], p2[0, 23:])
+
+
+def test_fp8_tower_reduces_to_exact_tower_on_e4m3_values():
+    """When every operand of the four linear maps is already an e4m3 value
+    times its block scale, the fp8 variant changes nothing: weights and
+    activations that quantise to themselves (zero blocks make every block
+    trivially exact)."""
+    rng = np.random.default_rng(32)
+    cfg = O.TowerConfig(patch=4, hidden=32, heads=2, mlp=64, layers=1, merge=1)
+    hw = [(8, 8)]
+    w = _tiny_weights(rng, 32, 64, 4, 1, 10)
+    for k in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"):
+        w["layers"][0][k] = np.zeros_like(w["layers"][0][k])
+    px = rng.standard_normal(3 * 64)
+    a = O.tower_forward(px, hw, w, cfg)["out"]
+    b = O.tower_forward(px, hw, w, cfg, fp8=True)["out"]
+    np.testing.assert_array_equal(a, b)
+    # with real weights the variant differs (a few e4m3 steps at the worst
+    # element of this small tower)
+    w2 = _tiny_weights(rng, 32, 64, 4, 1, 10)
+    a = O.tower_forward(px, hw, w2, cfg)["out"]
+    b = O.tower_forward(px, hw, w2, cfg, fp8=True)["out"]
+    rel = np.max(np.abs(a - b)) / np.sqrt(np.mean(a * a))
+    assert 1e-4 < rel < 0.5
