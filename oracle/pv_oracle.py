@@ -57,6 +57,10 @@ notes of the repository):
     has at most max_num_tiles tiles; each side becomes floor(s * side)
     (at least 1), rounded up to the patch grid; tiles are cut row-major,
     full T x T except the last row/column, which keep the remainder.
+13. fp8 variant (the NeMo Automodel page's FP8-native Mistral 3 VLM
+    registration): OCP e4m3 with one power-of-two scale per 32 values along
+    the contraction axis, X = floor(log2(block max)) - 7, ties to even; the
+    four linear maps of every block quantise both operands.
 
 Pinning: every function here is pinned in ``tests/test_oracle_pins.py`` by a
 check that does not reuse this code path (closed-form counts printed on the

@@ -8,6 +8,9 @@ output.  Usage:
     python tests/golden/make_golden.py [workload ...]
 
 Output: tests/golden/<workload>.npz.  Several minutes per workload.
+With ``--fp8`` the oracle runs its fp8 emulation of the four per-block
+linear maps (``tower_forward(..., fp8=True)``) and writes
+tests/golden/<workload>_fp8.npz (same sampled rows).
 """
 import os
 import sys
@@ -35,14 +38,14 @@ def sample_rows(out_rows: int, image_rows) -> np.ndarray:
     return np.unique(np.array(fixed + list(rest), dtype=np.int64))
 
 
-def make(name: str) -> str:
+def make(name: str, fp8: bool = False) -> str:
     wl = synth.workload(name)
     t0 = time.time()
     w = synth.oracle_weights(synth.make_weights(wl))
     px = synth.make_pixels(wl).astype(np.float64)
     cfg = O.TowerConfig(patch=wl.patch, hidden=wl.hidden, heads=wl.heads, mlp=wl.mlp, layers=wl.layers,
                         merge=wl.merge, out_dim=wl.out_dim, rope_theta=wl.rope_theta, rms_eps=wl.rms_eps)
-    res = O.tower_forward(px, wl.image_hw, w, cfg)
+    res = O.tower_forward(px, wl.image_hw, w, cfg, fp8=fp8)
     out = res["out"]
     maps = res["maps"]
     if wl.merge == 2:
@@ -50,7 +53,7 @@ def make(name: str) -> str:
     else:
         starts = maps["cu_seqlens"][:-1]
     rows = sample_rows(out.shape[0], list(starts))
-    path = os.path.join(HERE, f"{name}.npz")
+    path = os.path.join(HERE, f"{name}_fp8.npz" if fp8 else f"{name}.npz")
     np.savez_compressed(path, rows=rows, values=out[rows].astype(np.float32),
                         rms=np.float64(np.sqrt(np.mean(out * out))), shape=np.array(out.shape, np.int64),
                         image_hw=np.array(wl.image_hw, np.int64))
@@ -60,6 +63,7 @@ def make(name: str) -> str:
 
 
 if __name__ == "__main__":
-    names = sys.argv[1:] or ["ms31_1540", "packed8", "sweep64", "pixtral_tiles16"]
+    args = [a for a in sys.argv[1:] if a != "--fp8"]
+    names = args or ["ms31_1540", "packed8", "sweep64", "pixtral_tiles16"]
     for n in names:
-        make(n)
+        make(n, fp8="--fp8" in sys.argv[1:])
