@@ -308,6 +308,39 @@ def time_embcache(tw, wl, stream, reps=5):
             "keys_hbm_frac": round(img.numel() / (keys_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def time_fp8_variant(wl, dev_w, pix, stream, reps=5):
+    """The fp8 variant (PV_FLAG_FP8) of the same tower on the same input:
+    forward time (HIP events around `reps` calls) and per-class times.  A
+    different precision: reported beside the bf16 figure, never as it."""
+    import torch
+
+    from vlm_vision_encoder_amd import tower as T
+    if wl.dtype != "bf16":
+        return None
+    tw8 = T.Tower(T.config_for(wl, flags=T.PV_FLAG_FP8), dev_w)
+    info = tw8.plan(wl.image_hw)
+    out = torch.empty((info.out_rows, info.out_cols), dtype=torch.bfloat16, device="cuda")
+    sptr = stream.cuda_stream
+    tw8.forward(pix, wl.image_hw, out=out, stream=sptr)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        tw8.forward(pix, wl.image_hw, out=out, stream=sptr)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tw8.set_profiling(True)
+    tw8.forward(pix, wl.image_hw, out=out, stream=sptr)
+    torch.cuda.synchronize()
+    prof = tw8.read_profile(reset=True)
+    tw8.set_profiling(False)
+    tw8.close()
+    return {"dtype": "fp8 e4m3 (per-block linear maps), bf16 elsewhere", "ms_per_step": round(ms, 4),
+            "patches_per_s": round(wl.n_patches / (ms * 1e-3), 1),
+            "class_ms": {k: round(v[0], 4) for k, v in prof.items() if v[1]}}
+
+
 def source_sha256(path):
     import hashlib
     with open(path, "rb") as f:
@@ -445,6 +478,7 @@ def main():
     if (len(wl.image_hw) == 1 or wl.tiles_from is not None) and "patch" in kernels:
         u8_input = time_u8_input(tw, wl, out, ws, stream, kernels["patch"]["ms_per_step"])
     embcache = time_embcache(tw, wl, stream)
+    fp8_variant = time_fp8_variant(wl, dev_w, pix, stream)
 
     patches_s = wl.n_patches / (ms_step * 1e-3)
     tokens_s = wl.out_rows / (ms_step * 1e-3)
@@ -472,6 +506,7 @@ def main():
         "scatter": scatter,
         "u8_input": u8_input,
         "embcache": embcache,
+        "fp8_variant": fp8_variant,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")

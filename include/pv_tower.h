@@ -81,6 +81,18 @@ typedef struct pv_config {
  * with a running max only if the sums overflow or underflow; this bit makes it
  * always take the online form (testing and diagnosis). */
 #define PV_FLAG_ATTN_ONLINE_MAX 1
+/* pv_config.flags, bf16 tower only: the four linear maps of every block
+ * (q/k/v, out-projection, gate/up, down) run as fp8 e4m3 products with one
+ * power-of-two (E8M0) scale per 32 k on both operands
+ * (v_mfma_scale_f32_32x32x64_f8f6f4, fp32 accumulation): the weights are
+ * quantised per layer into the workspace, the activations by the norm
+ * kernels and by quantisation passes over the attention output and
+ * silu(gate) * up.  Scale X = floor(log2(block max)) - 7, values rounded to
+ * nearest even.  The patch embedding, attention, the residual stream and the
+ * merger keep their bf16/fp32 arithmetic.  An fp8 variant of the tower
+ * (the NeMo Automodel page registers FP8-native Mistral 3 VLM checkpoints);
+ * its accuracy is that of e4m3, not the bf16 tower's. */
+#define PV_FLAG_FP8 2
 
 /* Per-block weights: borrowed device pointers, row-major, "out x in" like a
  * linear layer (y = x W^T).  Gains are always fp32; matrices use cfg.dtype. */
@@ -417,6 +429,18 @@ pv_status pv_tower_forward_cached_u8(pv_embcache* c, const uint8_t* images, cons
                                      int32_t n_images, const uint64_t* keys, void* out,
                                      int64_t out_rows_cap, void* workspace, size_t ws_bytes,
                                      void* stream, int32_t* hit);
+
+/* The block-scaled fp8 quantisation the PV_FLAG_FP8 tower applies to its
+ * weights, as a standalone pass (e.g. to inspect or store fp8 weights):
+ *  src     device bf16 [rows][K], K a multiple of 128, 16-byte aligned
+ *  codes   device uint8 [rows][K]: e4m3 bytes (OCP E4M3FN) of src / 2^X,
+ *          rounded to nearest even, 16-byte aligned
+ *  scales  device uint8: for row r and 32-column block b, the E8M0 byte
+ *          X + 127 at scales[((b / 4) * rows + r) * 4 + b % 4], where
+ *          X = floor(log2(max |block|)) - 7 clamped to [-120, 120]
+ * Errors: PV_ERR_ARG, PV_ERR_HIP. */
+pv_status pv_quantize_fp8(const void* src, int64_t rows, int32_t K, void* codes, void* scales,
+                          void* stream);
 
 /* Thread-local message of the last failure in this thread ("" if none). */
 const char* pv_last_error(void);

@@ -64,7 +64,8 @@ def create(cfg, layers_present=True):
     (dict(dtype=7), -1),
     (dict(dtype=1), 0),
     (dict(max_side=10), -1),
-    (dict(flags=2), -1),
+    (dict(flags=4), -1),
+    (dict(flags=2), 0),
     (dict(flags=1), 0),
     (dict(rope_theta=0.0), -1),
 ])
@@ -407,3 +408,30 @@ def test_embcache_host_side_without_device_work():
     finally:
         lib.pv_embcache_destroy(c)
         lib.pv_tower_destroy(h)
+
+
+# ------------------------------------------------------------ fp8 variant
+def test_fp8_flag_validation_and_workspace():
+    lib = T.load_library()
+    st, h, _ = create(T.make_config(layers=2, dtype="f32", flags=T.PV_FLAG_FP8))
+    assert st == -5
+    st, h, _ = create(T.make_config(layers=2, flags=8))
+    assert st == -1
+    st, h8, _ = create(T.make_config(layers=2, flags=T.PV_FLAG_FP8))
+    st2, hb, _ = create(T.make_config(layers=2))
+    assert st == 0 and st2 == 0
+    try:
+        s8, i8 = _plan(lib, h8, [(1540, 1540)])
+        sb, ib = _plan(lib, hb, [(1540, 1540)])
+        assert s8 == 0 and sb == 0
+        # + the fp8 A operand at its widest (F = 4096 columns, 3 more bytes a
+        # row than D), scales, and the fp8 q|k|v, out-projection, down weights
+        extra = i8.workspace_bytes - ib.workspace_bytes
+        assert extra >= 12100 * 3 * 1024 + (3 + 1 + 4) * 1024 * 1024
+        assert lib.pv_quantize_fp8(None, 4, 128, FAKE, FAKE, None) == -1
+        assert lib.pv_quantize_fp8(FAKE, 4, 96, FAKE, FAKE, None) == -1
+        assert lib.pv_quantize_fp8(FAKE, 0, 128, FAKE, FAKE, None) == -1
+        assert lib.pv_quantize_fp8(FAKE + 8, 4, 128, FAKE, FAKE, None) == -1
+    finally:
+        lib.pv_tower_destroy(h8)
+        lib.pv_tower_destroy(hb)

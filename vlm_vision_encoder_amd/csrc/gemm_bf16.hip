@@ -298,8 +298,8 @@ void gemm_dense_kernel(GemmArgs g) {
   static_assert(A_LD >= 1 && B_LD >= 1 && (BM * CH) % NT == 0 && (BN * CH) % NT == 0, "tile/thread mismatch");
   static_assert(EM != E_SILU_MUL || (TN % 2) == 0, "silu-mul needs gate/up block pairs in a wave");
   static_assert((NS - 2) * (LDT + 1) <= 63, "vmcnt range");
-  static_assert(!LO8 || (BM == 256 && BN == 256 && BKT == 64 && NS == 2 && AMD == A_DENSE && NW >= 2),
-                "fp8 low part: 256 x 256 tiles, 64-k bf16 steps");
+  static_assert(!LO8 || (BM <= 256 && BN <= 256 && BKT == 64 && NS == 2 && AMD == A_DENSE && NW >= 2),
+                "fp8 steps: tiles of at most 256 x 256, 64-k bf16 steps (128-byte rows)");
 
   // LO8: 2 KB of scale bytes behind each stage's tiles
   constexpr int kStageU4 = (BM + BN) * CH + (LO8 ? 128 : 0);
@@ -416,14 +416,15 @@ void gemm_dense_kernel(GemmArgs g) {
         for (int q = 0; q < B_LD; ++q)
           __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(gb[q] + koff8),
                                            (lds_void*)&lds[st][BM * CH + (wave * B_LD + q) * 64], 16, 0, 0);
-        // scale bytes of the tile's 256 rows for this step: 1 KB each, A by
-        // wave 0 and B by wave 1 (rows past M read padding rows)
-        if (wave < 2) {
+        // scale bytes of the tile's rows for this step (4 per row): A's BM
+        // rows by wave 0, B's BN rows by wave 1, placed as dwords [0, BM)
+        // and [BM, BM + BN) behind the tiles (rows past M read padding rows)
+        if (wave < 2 && lane < (wave == 0 ? BM : BN) / 4) {
           const char* src = wave == 0
               ? reinterpret_cast<const char*>(g.As) + (size_t(s8) * g.as_rows + is_tm * BM) * 4 + lane * 16
               : reinterpret_cast<const char*>(g.Bs) + (size_t(s8) * g.bs_rows + is_tn * BN) * 4 + lane * 16;
           __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(src),
-                                           (lds_void*)&lds[st][(BM + BN) * CH + wave * 64], 16, 0, 0);
+                                           (lds_void*)&lds[st][(BM + BN) * CH + (wave == 0 ? 0 : BM / 4)], 16, 0, 0);
         }
         ++is_step;
         if (++is_kt == KT) {
@@ -587,6 +588,10 @@ void gemm_dense_kernel(GemmArgs g) {
     if constexpr (LO8) {
       for (int kt = KT16; kt < KT; ++kt, ++step) {
         begin_step(step);
+        // fp8-only products (no bf16 steps) fetch the residual here
+        if constexpr (EM == E_ADD_F32) {
+          if (KT16 == 0 && kt == KT - 1) load_residual<TM, TN>(g, res, tm * BM + wm * TMW, tn * BN + wn * TNW, lane);
+        }
         compute_fp8(step % NS);
       }
     }
@@ -612,7 +617,8 @@ hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
   if (ncols % BN || g.K % BKT || g.kb % BKT) return hipErrorInvalidValue;
   if (g.kb > 0 && g.K != 2 * g.kb) return hipErrorInvalidValue;
   if (AMD == A_MERGE && (g.hidden % BKT || g.K != 8 * g.hidden || g.kb != 4 * g.hidden)) return hipErrorInvalidValue;
-  if (LO8 && (g.k8 <= 0 || g.k8 % 128 || g.kb != 0 || g.as_rows < ((g.M + BM - 1) / BM) * BM)) return hipErrorInvalidValue;
+  if (LO8 && (g.k8 <= 0 || g.k8 % 128 || g.kb != 0 || g.as_rows < ((g.M + BM - 1) / BM) * BM || g.bs_rows < ncols))
+    return hipErrorInvalidValue;
   const int tiles = ((g.M + BM - 1) / BM) * (ncols / BN);
   // as many workgroups as fit on the chip at once: the LDS ring sets how
   // many a CU holds
@@ -657,12 +663,16 @@ hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
   switch (kind) {
     case GEMM_PATCH:  return launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_STORE_F32>(g, s);
-    case GEMM_QKV:    return launch_dense<PV_GEMM_CFG_QKV, A_DENSE, B_QKV, E_QKV_ROPE>(g, s);
-    case GEMM_OPROJ:  return launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_ADD_F32>(g, s);
+    case GEMM_QKV:
+      return g.k8 > 0 ? launch_dense<PV_GEMM_CFG_QKV, A_DENSE, B_QKV, E_QKV_ROPE, true>(g, s)
+                      : launch_dense<PV_GEMM_CFG_QKV, A_DENSE, B_QKV, E_QKV_ROPE>(g, s);
+    case GEMM_OPROJ:
+    case GEMM_DOWN:
+      return g.k8 > 0 ? launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_ADD_F32, true>(g, s)
+                      : launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_ADD_F32>(g, s);
     case GEMM_GATEUP:
       return g.k8 > 0 ? launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL, true>(g, s)
                       : launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL>(g, s);
-    case GEMM_DOWN:   return launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_ADD_F32>(g, s);
     case GEMM_MERGE:
       return g.N % 256 == 0 ? launch_dense<PV_GEMM_CFG_MERGE, A_MERGE, B_ONE, E_STORE>(g, s)
                             : launch_dense<PV_GEMM_CFG_N1K, A_MERGE, B_ONE, E_STORE>(g, s);

@@ -35,6 +35,9 @@ hipError_t rmsnorm(const float* x, const float* g, void* y, int rows, int D, flo
 // bytes step-major: ys[(col / 128) * srows + row][(col / 32) % 4]
 hipError_t rmsnorm_hi_lo8(const float* x, const float* g, void* yh, void* y8, void* ys, int rows, int srows, int D,
                           float eps, hipStream_t s);
+// rmsnorm_fp8: y = norm(x) * g as fp8 e4m3 [N][D] with the same scale bytes
+hipError_t rmsnorm_fp8(const float* x, const float* g, void* y8, void* ys, int rows, int srows, int D, float eps,
+                       hipStream_t s);
 hipError_t rmsnorm_dual(float* x, const float* g1, const float* g2, void* y, int rows, int D,
                         float eps, bool y_f32, hipStream_t s);
 
@@ -93,6 +96,11 @@ hipError_t im2col_u8_split(const uint8_t* images, const SrcImage* src, const Dev
 hipError_t resize_norm_u8(const uint8_t* image, const SrcImage& sm, int tH, int tW, const NormAff& aff, float* out,
                           hipStream_t s);
 hipError_t pad_rows(const void* w, void* out, int rows, int K, int Kp, hipStream_t s);
+//   quant_rows_fp8: rows [row0, row0 + rows) of dst8 [.][K] = the bf16 src
+//                 [rows][K] in fp8 e4m3, scales[(k/128)*srows + row][(k/32)%4]
+//                 one E8M0 byte per 32 k (K a multiple of 128)
+hipError_t quant_rows_fp8(const void* src, int rows, int K, void* dst8, void* scales, int srows, int row0,
+                          hipStream_t s);
 //   gateup_fp8:   b8 [2F][D] fp8 e4m3 = the gate/up weights in the GEMM's
 //                 interleaved row order, bs [D/128][2F][4] scale bytes
 hipError_t gateup_fp8(const void* w_gate, const void* w_up, void* b8, void* bs, int F, int D, hipStream_t s);

@@ -99,6 +99,41 @@ __global__ __launch_bounds__(256) void rmsnorm_hi_lo8_kernel(const float* __rest
   }
 }
 
+// The input of an fp8 linear map: y = norm(x) * g as fp8 e4m3 [N][D] with
+// one scale byte per 32 columns (same scale layout as above).
+template <int NC>
+__global__ __launch_bounds__(256) void rmsnorm_fp8_kernel(const float* __restrict__ x, const float* __restrict__ g,
+                                                          uint8_t* __restrict__ y8, uint8_t* __restrict__ ys, int rows,
+                                                          int srows, float eps) {
+  constexpr int D = NC * 256;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const floatx4* xr = reinterpret_cast<const floatx4*>(x + size_t(row) * D);
+  const floatx4* gr = reinterpret_cast<const floatx4*>(g);
+  floatx4 v[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) v[i] = xr[i * 64 + lane];
+  const float inv = rsqrtf(sumsq<NC>(v) * (1.f / D) + eps);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    v[i] = v[i] * inv * gr[i * 64 + lane];
+    const int col = (i * 64 + lane) * 4;
+    float amax = fmaxf(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])), fmaxf(fabsf(v[i][2]), fabsf(v[i][3])));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+    float mul;
+    const uint32_t sbyte = mx_scale(amax, mul);
+    *reinterpret_cast<uint32_t*>(y8 + size_t(row) * D + col) =
+        pack_fp8x4(v[i][0] * mul, v[i][1] * mul, v[i][2] * mul, v[i][3] * mul);
+    if ((lane & 7) == 0) {
+      const int blk = col / 32;
+      ys[(size_t(blk / 4) * srows + row) * 4 + (blk & 3)] = uint8_t(sbyte);
+    }
+  }
+}
+
 template <int NC, bool YF32>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, const float* __restrict__ g,
                                                       void* __restrict__ y, int rows, float eps) {
@@ -180,6 +215,22 @@ hipError_t rmsnorm_hi_lo8(const float* x, const float* g, void* yh, void* y8, vo
     hipLaunchKernelGGL((rmsnorm_hi_lo8_kernel<NC>), grid, block, 0, s, x, g, static_cast<uint16_t*>(yh), \
                        static_cast<uint8_t*>(y8), static_cast<uint8_t*>(ys), rows, srows, eps);           \
     return hipGetLastError();                                                                          \
+  }
+  PV_NORM_CASES(PV_CASE)
+#undef PV_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t rmsnorm_fp8(const float* x, const float* g, void* y8, void* ys, int rows, int srows, int D, float eps,
+                       hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (D % 128 || srows < rows) return hipErrorInvalidValue;
+  const dim3 grid((rows + 3) / 4), block(256);
+#define PV_CASE(NC)                                                                                   \
+  if (D == NC * 256) {                                                                                \
+    hipLaunchKernelGGL((rmsnorm_fp8_kernel<NC>), grid, block, 0, s, x, g, static_cast<uint8_t*>(y8),    \
+                       static_cast<uint8_t*>(ys), rows, srows, eps);                                  \
+    return hipGetLastError();                                                                         \
   }
   PV_NORM_CASES(PV_CASE)
 #undef PV_CASE

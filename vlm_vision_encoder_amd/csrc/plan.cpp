@@ -105,15 +105,30 @@ int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, P
   L.wpad = off;
   off = align256(off + (p.elem_bytes == 2 ? D * size_t(patch_kp(p.patch)) * 2 : 0));
   if (p.elem_bytes == 2) {
-    const size_t F2 = 2 * size_t(p.mlp);
+    const size_t F = size_t(p.mlp), F2 = 2 * F;
+    const size_t KA = p.fp8 ? std::max(D, F) : D;  // widest fp8 A operand
     L.a8 = off;
-    off = align256(off + N * D);
+    off = align256(off + N * KA);
     L.as = off;
-    off = align256(off + (D / 128) * size_t(a8_scale_rows(int64_t(N))) * 4);
+    off = align256(off + (KA / 128) * size_t(a8_scale_rows(int64_t(N))) * 4);
     L.b8 = off;
     off = align256(off + F2 * D);
     L.bs = off;
     off = align256(off + (D / 128) * F2 * 4);
+    if (p.fp8) {
+      L.wq8 = off;
+      off = align256(off + 3 * D * D);
+      L.wqs = off;
+      off = align256(off + (D / 128) * 3 * D * 4);
+      L.wo8 = off;
+      off = align256(off + D * D);
+      L.wos = off;
+      off = align256(off + (D / 128) * D * 4);
+      L.wd8 = off;
+      off = align256(off + D * F);
+      L.wds = off;
+      off = align256(off + (F / 128) * D * 4);
+    }
   }
   L.total = off;
   return 0;

@@ -57,6 +57,7 @@ struct PlanParams {
   int32_t elem_bytes = 2;   // 2 = bf16 activations, 4 = fp32
   int32_t q_tile = 256;     // queries per attention work item
   int32_t rope_pairs = 16;  // rotation pairs per axis (head_dim / 4)
+  bool fp8 = false;         // bf16 tower whose per-block linear maps run in fp8
 };
 
 // Rows of the MLP input's fp8 scale blocks: the patches plus one tile of
@@ -71,8 +72,11 @@ struct Layout {
   size_t meta = 0, items = 0, rope = 0, src = 0, rowinfo = 0, msrc = 0;
   size_t r = 0, y = 0, big = 0;
   size_t wpad = 0;          // bf16 tower: patch weights zero-padded to [D][Kp]
-  // bf16 tower, MLP input's fp8 low part and the gate/up weights in fp8:
+  // bf16 tower, MLP input's fp8 low part and the gate/up weights in fp8
+  // (fp8 variant: a8/as hold every fp8 GEMM input, up to [N][max(D, F)]):
   size_t a8 = 0, as = 0, b8 = 0, bs = 0;
+  // fp8 variant: this layer's q|k|v, out-projection and down weights in fp8
+  size_t wq8 = 0, wqs = 0, wo8 = 0, wos = 0, wd8 = 0, wds = 0;
   size_t upload_bytes = 0;  // [0, upload_bytes) is filled by one host->device copy
   size_t total = 0;
 };

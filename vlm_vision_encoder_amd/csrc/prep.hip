@@ -179,18 +179,10 @@ __global__ __launch_bounds__(256) void pad_rows_kernel(const uint16_t* __restric
   out[idx] = k < K ? w[size_t(r) * K + k] : uint16_t(0);
 }
 
-// One thread per (row n of the interleaved gate/up matrix, block of 32 k).
-// Row n: 32-row blocks alternate gate and up (rows [64j, 64j+32) -> gate
-// rows [32j, +32), rows [64j+32, 64j+64) -> up rows [32j, +32)).
-__global__ __launch_bounds__(256) void gateup_fp8_kernel(const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
-                                                         uint8_t* __restrict__ b8, uint8_t* __restrict__ bs, int F,
-                                                         int D) {
-  const int blocks = D / 32;
-  const long long idx = blockIdx.x * 256ll + threadIdx.x;
-  if (idx >= 2ll * F * blocks) return;
-  const int n = int(idx / blocks), blk = int(idx - (long long)n * blocks);
-  const int src_row = (n >> 6) * 32 + (n & 31);
-  const uint16_t* src = ((n & 32) ? wu : wg) + size_t(src_row) * D + blk * 32;
+// 32 consecutive bf16 values -> 32 fp8 e4m3 bytes at dst and the block's
+// E8M0 scale byte (returned): X = floor(log2(max |x|)) - 7 puts the block
+// maximum in [128, 256) of e4m3.
+__device__ __forceinline__ uint8_t quant_block32(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst) {
   float f[32];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -216,10 +208,40 @@ __global__ __launch_bounds__(256) void gateup_fp8_kernel(const uint16_t* __restr
     r = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * q + 2] * mul, f[4 * q + 3] * mul, r, true);
     o[q / 4][q % 4] = uint32_t(r);
   }
-  u32x4* dst = reinterpret_cast<u32x4*>(b8 + size_t(n) * D + blk * 32);
-  dst[0] = o[0];
-  dst[1] = o[1];
-  bs[(size_t(blk / 4) * (2 * F) + n) * 4 + (blk & 3)] = uint8_t(x + 127);
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+  d[0] = o[0];
+  d[1] = o[1];
+  return uint8_t(x + 127);
+}
+
+// One thread per (row n of the interleaved gate/up matrix, block of 32 k).
+// Row n: 32-row blocks alternate gate and up (rows [64j, 64j+32) -> gate
+// rows [32j, +32), rows [64j+32, 64j+64) -> up rows [32j, +32)).
+__global__ __launch_bounds__(256) void gateup_fp8_kernel(const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
+                                                         uint8_t* __restrict__ b8, uint8_t* __restrict__ bs, int F,
+                                                         int D) {
+  const int blocks = D / 32;
+  const long long idx = blockIdx.x * 256ll + threadIdx.x;
+  if (idx >= 2ll * F * blocks) return;
+  const int n = int(idx / blocks), blk = int(idx - (long long)n * blocks);
+  const int src_row = (n >> 6) * 32 + (n & 31);
+  const uint16_t* src = ((n & 32) ? wu : wg) + size_t(src_row) * D + blk * 32;
+  bs[(size_t(blk / 4) * (2 * F) + n) * 4 + (blk & 3)] = quant_block32(src, b8 + size_t(n) * D + blk * 32);
+}
+
+// One thread per (row r, block of 32 columns) of a bf16 [rows][K] matrix;
+// output row row0 + r of dst8 [.][K] and of the scale bytes
+// scales[(col / 128) * srows + row][(col / 32) % 4].
+__global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint16_t* __restrict__ src, int rows, int K,
+                                                             uint8_t* __restrict__ dst8, uint8_t* __restrict__ scales,
+                                                             int srows, int row0) {
+  const int blocks = K / 32;
+  const long long idx = blockIdx.x * 256ll + threadIdx.x;
+  if (idx >= (long long)rows * blocks) return;
+  const int r = int(idx / blocks), blk = int(idx - (long long)r * blocks);
+  const size_t row = size_t(row0) + r;
+  scales[(size_t(blk / 4) * srows + row) * 4 + (blk & 3)] =
+      quant_block32(src + size_t(r) * K + blk * 32, dst8 + row * K + blk * 32);
 }
 
 inline dim3 grid_for(long long threads) { return dim3(unsigned((threads + 255) / 256)); }
@@ -268,6 +290,16 @@ hipError_t gateup_fp8(const void* w_gate, const void* w_up, void* b8, void* bs, 
   hipLaunchKernelGGL(gateup_fp8_kernel, grid_for(2ll * F * (D / 32)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
                      static_cast<uint8_t*>(b8), static_cast<uint8_t*>(bs), F, D);
+  return hipGetLastError();
+}
+
+hipError_t quant_rows_fp8(const void* src, int rows, int K, void* dst8, void* scales, int srows, int row0,
+                          hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (K % 128 || row0 < 0 || row0 + rows > srows) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_rows_fp8_kernel, grid_for((long long)rows * (K / 32)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(src), rows, K, static_cast<uint8_t*>(dst8),
+                     static_cast<uint8_t*>(scales), srows, row0);
   return hipGetLastError();
 }
 

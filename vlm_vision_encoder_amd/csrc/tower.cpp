@@ -105,6 +105,7 @@ pv::PlanParams plan_params(const pv_tower* t) {
   p.elem_bytes = t->cfg.dtype == PV_BF16 ? 2 : 4;
   p.q_tile = t->cfg.dtype == PV_BF16 ? pv::kAttnQTileBf16 : pv::kAttnQTileF32;
   p.rope_pairs = 16;
+  p.fp8 = (t->cfg.flags & PV_FLAG_FP8) != 0;
   return p;
 }
 
@@ -190,6 +191,7 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
                     const StageStop& st, hipStream_t s) {
   const pv_config& c = t->cfg;
   const bool bf = c.dtype == PV_BF16;
+  const bool f8 = bf && (c.flags & PV_FLAG_FP8);  // per-block linear maps in fp8
   const size_t es = bf ? 2 : 4;
   const pv::Layout& L = plan.ws;
   const int N = int(plan.n_patches), D = c.hidden, F = c.mlp;
@@ -248,9 +250,14 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
   }
   if (st.stage == PV_STAGE_PATCH_EMBED) return copy_stage(st, r, size_t(N) * D * 4, s);
   const float eps = float(c.rms_eps);
-  if (c.layers == 0) {
+  const int srows = int(pv::a8_scale_rows(N));
+  char* a8 = ws + L.a8;  // fp8 variant: the input of every fp8 linear map
+  char* as = ws + L.as;
+  if (c.layers == 0 || f8) {
     PV_LAUNCH(PV_K_NORM, pv::rmsnorm(r, t->w.ln_pre, r, N, D, eps, true, s));  // in place, fp32 out
     if (st.stage == PV_STAGE_LN_PRE) return copy_stage(st, r, size_t(N) * D * 4, s);
+    if (f8 && c.layers > 0)
+      PV_LAUNCH(PV_K_NORM, pv::rmsnorm_fp8(r, t->layers[0].attn_norm, a8, as, N, srows, D, eps, s));
   } else {
     PV_LAUNCH(PV_K_NORM, pv::rmsnorm_dual(r, t->w.ln_pre, t->layers[0].attn_norm, y, N, D, eps, !bf, s));
     if (st.stage == PV_STAGE_LN_PRE) return copy_stage(st, r, size_t(N) * D * 4, s);
@@ -269,12 +276,27 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
   for (int l = 0; l < c.layers; ++l) {
     const pv_layer_weights& lw = t->layers[l];
     const bool stop_here = st.layer == l;
+    // fp8 variant: operand in fp8 with one power-of-two scale per 32 k
+    auto use_fp8 = [&](pv::GemmArgs& a, int k, const void* b8, const void* bsc, int brows) {
+      a.K = 0; a.kb = 0;
+      a.A = a8; a.A8 = a8; a.As = as; a.as_rows = srows; a.k8 = k;
+      a.B8 = b8; a.Bs = bsc; a.bs_rows = brows;
+    };
+    if (f8) {  // this layer's weights in fp8
+      PV_LAUNCH(PV_K_QKV, pv::quant_rows_fp8(lw.wq, D, D, ws + L.wq8, ws + L.wqs, 3 * D, 0, s));
+      PV_LAUNCH(PV_K_QKV, pv::quant_rows_fp8(lw.wk, D, D, ws + L.wq8, ws + L.wqs, 3 * D, D, s));
+      PV_LAUNCH(PV_K_QKV, pv::quant_rows_fp8(lw.wv, D, D, ws + L.wq8, ws + L.wqs, 3 * D, 2 * D, s));
+      PV_LAUNCH(PV_K_OPROJ, pv::quant_rows_fp8(lw.wo, D, D, ws + L.wo8, ws + L.wos, D, 0, s));
+      PV_LAUNCH(PV_K_GATEUP, pv::gateup_fp8(lw.w_gate, lw.w_up, ws + L.b8, ws + L.bs, F, D, s));
+      PV_LAUNCH(PV_K_DOWN, pv::quant_rows_fp8(lw.w_down, D, F, ws + L.wd8, ws + L.wds, D, 0, s));
+    }
     {  // q,k,v with the 2-D rotary in the epilogue
       pv::GemmArgs a = g;
       a.M = N; a.N = 3 * D; a.K = D;
       a.A = y; a.lda = D;
       a.B0 = lw.wq; a.B1 = lw.wk; a.B2 = lw.wv; a.ldb = D;
       a.C = big; a.ldc = 3 * D;
+      if (f8) use_fp8(a, D, ws + L.wq8, ws + L.wqs, 3 * D);
       PV_LAUNCH(PV_K_QKV, gemm(pv::GEMM_QKV, a));
     }
     if (stop_here && st.stage == PV_STAGE_QKV) return copy_stage(st, big, size_t(N) * 3 * D * es, s);
@@ -286,14 +308,19 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
       a.A = y; a.lda = D;
       a.B0 = lw.wo; a.ldb = D;
       a.C = r; a.ldc = D;
+      if (f8) {
+        PV_LAUNCH(PV_K_OPROJ, pv::quant_rows_fp8(y, N, D, a8, as, srows, 0, s));
+        use_fp8(a, D, ws + L.wo8, ws + L.wos, D);
+      }
       PV_LAUNCH(PV_K_OPROJ, gemm(pv::GEMM_OPROJ, a));
     }
     if (stop_here && st.stage == PV_STAGE_ATTN_RESID) return copy_stage(st, r, size_t(N) * D * 4, s);
     // the MLP input of the bf16 tower goes in as bf16 plus its low part in
     // fp8 (times fp8 copies of the weights, 32-k scale blocks): its plain
     // bf16 rounding would otherwise be the largest error of the tower output
-    const int srows = int(pv::a8_scale_rows(N));
-    if (bf) {
+    if (f8) {
+      PV_LAUNCH(PV_K_NORM, pv::rmsnorm_fp8(r, lw.ffn_norm, a8, as, N, srows, D, eps, s));
+    } else if (bf) {
       PV_LAUNCH(PV_K_GATEUP, pv::gateup_fp8(lw.w_gate, lw.w_up, ws + L.b8, ws + L.bs, F, D, s));
       PV_LAUNCH(PV_K_NORM, pv::rmsnorm_hi_lo8(r, lw.ffn_norm, y, ws + L.a8, ws + L.as, N, srows, D, eps, s));
     } else {
@@ -309,6 +336,7 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
       }
       a.B0 = lw.w_gate; a.B1 = lw.w_up; a.ldb = D;
       a.C = big; a.ldc = F;
+      if (f8) use_fp8(a, D, ws + L.b8, ws + L.bs, 2 * F);
       PV_LAUNCH(PV_K_GATEUP, gemm(pv::GEMM_GATEUP, a));
     }
     if (stop_here && st.stage == PV_STAGE_MLP_HIDDEN) return copy_stage(st, big, size_t(N) * F * es, s);
@@ -318,10 +346,17 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
       a.A = big; a.lda = F;
       a.B0 = lw.w_down; a.ldb = F;
       a.C = r; a.ldc = D;
+      if (f8) {
+        PV_LAUNCH(PV_K_DOWN, pv::quant_rows_fp8(big, N, F, a8, as, srows, 0, s));
+        use_fp8(a, F, ws + L.wd8, ws + L.wds, D);
+      }
       PV_LAUNCH(PV_K_DOWN, gemm(pv::GEMM_DOWN, a));
     }
     if (stop_here && st.stage == PV_STAGE_BLOCK_OUT) return copy_stage(st, r, size_t(N) * D * 4, s);
-    if (l + 1 < c.layers) PV_LAUNCH(PV_K_NORM, pv::rmsnorm(r, t->layers[l + 1].attn_norm, y, N, D, eps, !bf, s));
+    if (l + 1 < c.layers) {
+      if (f8) PV_LAUNCH(PV_K_NORM, pv::rmsnorm_fp8(r, t->layers[l + 1].attn_norm, a8, as, N, srows, D, eps, s));
+      else PV_LAUNCH(PV_K_NORM, pv::rmsnorm(r, t->layers[l + 1].attn_norm, y, N, D, eps, !bf, s));
+    }
   }
   if (st.stage >= 0) return fail(PV_ERR_ARG, "stage/layer not reached");
 
@@ -523,7 +558,8 @@ pv_status pv_tower_create(const pv_config* cfg, const pv_weights* w, pv_tower** 
   const pv_config& c = *cfg;
   if (c.dtype != PV_BF16 && c.dtype != PV_F32) return fail(PV_ERR_ARG, "dtype must be PV_BF16 or PV_F32");
   if (c.out_dtype != PV_BF16 && c.out_dtype != PV_F32) return fail(PV_ERR_ARG, "out_dtype must be PV_BF16 or PV_F32");
-  if (c.flags & ~PV_FLAG_ATTN_ONLINE_MAX) return fail(PV_ERR_ARG, "unknown bits in flags");
+  if (c.flags & ~(PV_FLAG_ATTN_ONLINE_MAX | PV_FLAG_FP8)) return fail(PV_ERR_ARG, "unknown bits in flags");
+  if ((c.flags & PV_FLAG_FP8) && c.dtype != PV_BF16) return fail(PV_ERR_UNSUPPORTED, "PV_FLAG_FP8 needs the bf16 tower");
   if (c.patch < 1 || c.patch > 64) return fail(PV_ERR_ARG, "patch must be in [1, 64]");
   if (c.merge != 1 && c.merge != 2) return fail(PV_ERR_ARG, "merge must be 1 or 2");
   if (c.layers < 0) return fail(PV_ERR_ARG, "layers must be >= 0");
@@ -662,6 +698,16 @@ pv_status pv_tower_plan_tiles_u8(const pv_tower* t, const int32_t* src_hw, int32
   if (st != PV_OK) return st;
   if (layout) std::memcpy(layout, lay.data(), sizeof(int32_t) * lay.size());
   fill_info(t, plan, info);
+  return PV_OK;
+}
+
+pv_status pv_quantize_fp8(const void* src, int64_t rows, int32_t K, void* codes, void* scales, void* stream) {
+  pv::last_error().clear();
+  if (!src || !codes || !scales) return fail(PV_ERR_ARG, "src, codes and scales must not be null");
+  if (rows < 1 || rows > INT32_MAX || K < 128 || K % 128) return fail(PV_ERR_ARG, "rows must be >= 1 and K a positive multiple of 128");
+  if (int64_t(rows) * K > (int64_t(1) << 40)) return fail(PV_ERR_ARG, "matrix too large");
+  if (!aligned(src, 16) || !aligned(codes, 16)) return fail(PV_ERR_ARG, "src and codes must be 16-byte aligned");
+  PV_HIP(pv::quant_rows_fp8(src, int(rows), K, codes, scales, int(rows), 0, static_cast<hipStream_t>(stream)));
   return PV_OK;
 }
 

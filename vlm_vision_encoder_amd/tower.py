@@ -15,6 +15,7 @@ LIB_PATH = os.environ.get("PV_TOWER_LIB") or os.path.join(PKG, "libpv_tower.so")
 
 PV_BF16, PV_F32 = 0, 1
 PV_FLAG_ATTN_ONLINE_MAX = 1
+PV_FLAG_FP8 = 2
 STAGES = {"patch_embed": 0, "ln_pre": 1, "qkv": 2, "attn": 3, "attn_resid": 4, "mlp_hidden": 5, "block_out": 6}
 STATUS = {0: "PV_OK", -1: "PV_ERR_ARG", -2: "PV_ERR_SHAPE", -3: "PV_ERR_CAPACITY", -4: "PV_ERR_HIP",
           -5: "PV_ERR_UNSUPPORTED"}
@@ -25,7 +26,7 @@ EXPORTED = ("pv_tower_create", "pv_tower_destroy", "pv_tower_plan", "pv_tower_fo
             "pv_tower_forward_u8", "pv_preprocess_u8", "pv_tile_layout", "pv_tower_plan_tiles_u8",
             "pv_tower_forward_tiles_u8", "pv_config_preset", "pv_image_keys_workspace_bytes", "pv_image_keys_u8",
             "pv_embcache_create", "pv_embcache_destroy", "pv_embcache_clear", "pv_embcache_stats",
-            "pv_embcache_workspace_bytes", "pv_tower_forward_cached_u8", "pv_last_error", "pv_status_str")
+            "pv_embcache_workspace_bytes", "pv_tower_forward_cached_u8", "pv_quantize_fp8", "pv_last_error", "pv_status_str")
 PRESETS = {"mistral3": 0, "pixtral12b": 1}
 KERNEL_CLASSES = ("maps", "patch", "norm", "qkv", "attn", "oproj", "gateup", "down", "merge")
 
@@ -123,6 +124,8 @@ def load_library(path: str = LIB_PATH):
     lib.pv_embcache_workspace_bytes.restype = i32
     lib.pv_tower_forward_cached_u8.argtypes = [vp, vp, vp, i32, vp, vp, i64, vp, sz, vp, vp]
     lib.pv_tower_forward_cached_u8.restype = i32
+    lib.pv_quantize_fp8.argtypes = [vp, i64, i32, vp, vp, vp]
+    lib.pv_quantize_fp8.restype = i32
     lib.pv_last_error.argtypes = []
     lib.pv_last_error.restype = C.c_char_p
     lib.pv_status_str.argtypes = [i32]
@@ -451,6 +454,19 @@ class EmbCache:
             self.close()
         except Exception:
             pass
+
+
+def quantize_fp8(x):
+    """bf16 CUDA matrix [rows][K] -> (uint8 e4m3 codes [rows][K], uint8 scale
+    bytes in the GEMM layout [K/128][rows][4])."""
+    import torch
+    lib = load_library()
+    rows, K = x.shape
+    codes = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((K // 128, rows, 4), dtype=torch.uint8, device=x.device)
+    _check(lib.pv_quantize_fp8(x.data_ptr(), rows, K, codes.data_ptr(), scales.data_ptr(),
+                               torch.cuda.current_stream().cuda_stream))
+    return codes, scales
 
 
 def preset(name: str, dtype: str = "bf16") -> PvConfig:
