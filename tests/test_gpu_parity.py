@@ -227,6 +227,30 @@ def test_bf16_merger_width_not_multiple_of_256():
     check("out", to_np(out), ref["out"], TOL["bf16"], stored_bf16=True)
 
 
+def test_bf16_many_tiny_images():
+    """150 images of 1 to 9 merged tokens each (28..84 pixels a side): every
+    attention work item is a whole small image and row tiles cross many
+    image boundaries."""
+    rng = np.random.default_rng(81)
+    hw = [(28 * int(a), 28 * int(b)) for a, b in rng.integers(1, 4, size=(150, 2))]
+    wl = _bf16_small(hw, 2, hidden=256, heads=4, mlp=512, out_dim=384)
+    say(f"bf16 {len(hw)} tiny images, {wl.n_patches} patches")
+    c = Case(wl)
+    ref = c.ref()
+    check("out", to_np(c.run()), ref["out"], TOL["bf16"], stored_bf16=True)
+
+
+@pytest.mark.parametrize("hidden,heads,mlp", [(512, 8, 1024), (768, 12, 2048), (1536, 24, 3072), (2048, 32, 2048)])
+def test_bf16_other_widths(hidden, heads, mlp):
+    """The other supported widths (norm kernels of 2, 3, 6, 8 row chunks; q,k,v
+    with 3D columns in 192-wide tiles; merger K = 4D)."""
+    wl = _bf16_small([(224, 168), (56, 84)], 2, hidden=hidden, heads=heads, mlp=mlp, out_dim=640)
+    say(f"bf16 width D={hidden} heads={heads} F={mlp}")
+    c = Case(wl)
+    ref = c.ref()
+    check("out", to_np(c.run()), ref["out"], TOL["bf16"], stored_bf16=True)
+
+
 def test_bf16_sharp_logits():
     """Logit std ~4 instead of ~0.4.  bf16 storage of q and k moves every
     logit s by up to about 2^-8 |s| (two half-ulp roundings), which moves the
