@@ -49,10 +49,10 @@ def flops_by_class(wl):
 def norm_bytes(wl):
     """Algorithmic HBM bytes per element of the RMSNorm passes of one forward
     (bf16 path): the dual first pass reads 4 and writes 4 + 2; an attention
-    norm reads 4 and writes 2; an MLP norm reads 4 and writes 2 (bf16) + 1
-    (fp8 low part) + 1/32 (scale bytes)."""
+    norm reads 4 and writes 2; an MLP norm reads 4 and writes 2 (bf16) + 1/2
+    (fp4 low part) + 1/32 (scale bytes)."""
     N, D, L = wl.n_patches, wl.hidden, wl.layers
-    return N * D * (10 + (L - 1) * 6 + L * (7 + 1 / 32)) if L > 0 else N * D * 8
+    return N * D * (10 + (L - 1) * 6 + L * (6.5 + 1 / 32)) if L > 0 else N * D * 8
 
 
 def cpu_model():

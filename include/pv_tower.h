@@ -216,7 +216,7 @@ enum {
   PV_K_QKV = 3,      /* q,k,v GEMM with the rotary epilogue                   */
   PV_K_ATTN = 4,     /* block-diagonal attention                              */
   PV_K_OPROJ = 5,    /* out-projection GEMM (+ residual)                      */
-  PV_K_GATEUP = 6,   /* MLP gate/up: fp8 weight copy + GEMM (silu * up)       */
+  PV_K_GATEUP = 6,   /* MLP gate/up: fp4 (fp8 variant: fp8) weight copy + GEMM (silu * up) */
   PV_K_DOWN = 7,     /* MLP down GEMM (+ residual)                            */
   PV_K_MERGE = 8,    /* residual copy + 2x2 merge GEMM, or output copy        */
   PV_K_COUNT = 9

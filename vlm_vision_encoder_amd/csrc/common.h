@@ -72,6 +72,25 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // ---------------------------------------------------------------------------
 // Device view of the per-call maps (all in the workspace).
+// Power-of-two block scale for fp4 e2m1 (0, 0.5, 1, 1.5, 2, 3, 4, 6):
+// X = floor(log2(max |x|)) - 2 puts the block maximum in [4, 8) (past 6 it
+// saturates); returns the E8M0 byte X + 127 and sets scale = 2^X.  The
+// hardware conversion v_cvt_scalef32_pk_fp4_f32 divides by that scale and
+// rounds to nearest even, two values per instruction.
+__device__ __forceinline__ uint32_t mx_scale4(float amax, float& scale) {
+  const int e = int((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xff);
+  int x = e - 127 - 2;
+  x = x < -120 ? -120 : (x > 120 ? 120 : x);
+  scale = __builtin_bit_cast(float, uint32_t(x + 127) << 23);
+  return uint32_t(x + 127);
+}
+
+// Four values / scale -> four fp4 nibbles (16 bits, first value lowest).
+__device__ __forceinline__ uint32_t pack_fp4x4(float a, float b, float c, float d, float scale) {
+  uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, scale, 0);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, c, d, scale, 1);
+}
+
 struct DevMaps {
   const ImageMeta* meta;
   const int32_t* rowinfo;  // [N][2]: image, (row << 16) | col
@@ -96,15 +115,18 @@ struct GemmArgs {
   const void* B2;
   int32_t ldb;
   int32_t kb;         // K extent of B when A's K repeats it (hi | lo halves of A), else 0
-  // fp8 low-part correction (gate/up): after the bf16 K range, k8 more k of
-  // A8 [M][k8] x B8 [N][k8] (fp8 e4m3 with one power-of-two scale per 32 k,
-  // scale bytes in step-major blocks As [k8/128][as_rows][4], Bs
-  // [k8/128][bs_rows][4]); k8 = 0: none
+  // low-precision k (after the bf16 K range, or alone): k8 more k of
+  // A8 [M][k8] x B8 [N][k8] in fp8 e4m3 (low_fmt 8) or packed fp4 e2m1
+  // (low_fmt 4, two values a byte, low nibble first), one power-of-two scale
+  // per 32 k on both sides, scale bytes in step-major blocks
+  // As [k8/kstep][as_rows][sb], Bs [k8/kstep][bs_rows][sb] with
+  // (kstep, sb) = (128, 4) for fp8 and (256, 8) for fp4; k8 = 0: none
   const void* A8;
   const void* B8;
   const void* As;
   const void* Bs;
   int32_t k8, as_rows, bs_rows;
+  int32_t low_fmt;
   void* C;
   int32_t ldc;
   int32_t hidden;     // D (QKV split, merge gather)

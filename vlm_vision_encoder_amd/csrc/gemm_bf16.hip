@@ -40,6 +40,10 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ i32x8 join8(const u32x4& x, const u32x4& y) {
   return i32x8{int(x[0]), int(x[1]), int(x[2]), int(x[3]), int(y[0]), int(y[1]), int(y[2]), int(y[3])};
 }
+// one 16-byte LDS chunk -> the fp4 operand (its upper 16 bytes unused)
+__device__ __forceinline__ i32x8 widen4(const u32x4& x) {
+  return i32x8{int(x[0]), int(x[1]), int(x[2]), int(x[3]), 0, 0, 0, 0};
+}
 
 template <int N, typename F, int I = 0>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -277,15 +281,17 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 // is the concatenation of four residual rows msrc[t][0..3] (2x2 patch
 // gather): the loads fetch straight from the [rows][2D] hi | lo copy of the
 // residual, K = 8D = (hi: 4 gathered rows) | (lo: the same 4 rows).
-// LO8: after the bf16 k-steps, k8 / 128 more steps multiply the fp8 low part
-// of A with an fp8 copy of B (v_mfma_scale_f32_32x32x64_f8f6f4, one scale
-// byte per 32 k on each side) into the same accumulators.  A step then moves
-// 128 fp8 k: the same 128-byte tile rows and chunk swizzle as a bf16 step,
-// plus 1 KB of A and 1 KB of B scale bytes behind the tiles.  In the MFMA
-// operand, lane l (half h = l / 32) holds row l % 32, k [16h, 16h + 16) and
-// [32 + 16h, 32 + 16h + 16) of the 64, and supplies the scale of its row's
-// 32-k block h (byte 0 of its scale operand).
-template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int AMD, int BMD, int EM, bool LO8 = false>
+// LOW (8 or 4): after the bf16 k-steps, more steps multiply low-precision
+// copies of A and B -- fp8 e4m3 (LOW 8) or fp4 e2m1 (LOW 4), one scale byte
+// per 32 k on each side (v_mfma_scale_f32_32x32x64_f8f6f4) -- into the same
+// accumulators.  A step moves the same 128-byte tile rows and chunk swizzle
+// as a bf16 step (128 fp8 or 256 fp4 k), plus the rows' scale bytes (4 or 8
+// a row) behind the tiles.  MFMA operands: for fp8, lane l (half h = l / 32)
+// holds row l % 32, k [16h, 16h + 16) and [32 + 16h, 32 + 16h + 16) of the
+// 64 and supplies the scale of its row's 32-k block h (byte 0 of its scale
+// operand); for fp4 the lane's 16 operand bytes are one 32-k block (k
+// [32h, 32h + 32) of the 64) and its scale byte scales exactly those values.
+template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int AMD, int BMD, int EM, int LOW = 0>
 __global__ __launch_bounds__(WMW * WNW * 64) __attribute__((amdgpu_waves_per_eu(WMW * WNW >= 8 ? 2 : 8 / (WMW * WNW))))
 void gemm_dense_kernel(GemmArgs g) {
   static_assert(AMD == A_DENSE || AMD == A_MERGE, "A operand mode");
@@ -298,11 +304,17 @@ void gemm_dense_kernel(GemmArgs g) {
   static_assert(A_LD >= 1 && B_LD >= 1 && (BM * CH) % NT == 0 && (BN * CH) % NT == 0, "tile/thread mismatch");
   static_assert(EM != E_SILU_MUL || (TN % 2) == 0, "silu-mul needs gate/up block pairs in a wave");
   static_assert((NS - 2) * (LDT + 1) <= 63, "vmcnt range");
-  static_assert(!LO8 || (BM <= 256 && BN <= 256 && BKT == 64 && NS == 2 && AMD == A_DENSE && NW >= 2),
-                "fp8 steps: tiles of at most 256 x 256, 64-k bf16 steps (128-byte rows)");
+  static_assert(LOW == 0 || LOW == 8 || LOW == 4, "low-precision format");
+  constexpr bool LO8 = LOW != 0;               // has low-precision steps
+  constexpr int SB = LOW == 4 ? 8 : 4;         // scale bytes per row and step
+  constexpr int KSTEP = LOW == 4 ? 256 : 128;  // k per low-precision step
+  constexpr int SCA = BM * SB / 16, SCB = BN * SB / 16;  // 16-byte scale chunks per step
+  constexpr int WSA = (SCA + 63) / 64, WSB = (SCB + 63) / 64;  // waves that load them
+  static_assert(!LO8 || (BM <= 256 && BN <= 256 && BKT == 64 && NS == 2 && AMD == A_DENSE && WSA + WSB <= NW),
+                "low-precision steps: tiles of at most 256 x 256, 64-k bf16 steps (128-byte rows)");
 
-  // LO8: 2 KB of scale bytes behind each stage's tiles
-  constexpr int kStageU4 = (BM + BN) * CH + (LO8 ? 128 : 0);
+  // scale bytes behind each stage's tiles
+  constexpr int kStageU4 = (BM + BN) * CH + (LO8 ? SCA + SCB : 0);
   __shared__ u32x4 lds[NS][kStageU4];
   constexpr int kScratchFloats = (BM + BN) * CH * 4 / NW;  // per-wave slice of one stage
   constexpr int kEpiRows = kScratchFloats >= 32 * 32 ? 32 : 16;
@@ -318,7 +330,7 @@ void gemm_dense_kernel(GemmArgs g) {
   const int tiles_m = (g.M + BM - 1) / BM;
   const int ntiles = tiles_m * tiles_n;
   const int KT16 = g.K / BKT;                  // bf16 k-steps per tile
-  const int KT = KT16 + (LO8 ? g.k8 / 128 : 0);  // all k-steps per tile
+  const int KT = KT16 + (LO8 ? g.k8 / KSTEP : 0);  // all k-steps per tile
   // k-tiles of B: A's K may run over B's K twice (hi | lo halves of A)
   const int KTB = g.kb > 0 ? g.kb / BKT : KT16;
 
@@ -377,7 +389,8 @@ void gemm_dense_kernel(GemmArgs g) {
       gb[q] = b_row<BMD>(g, tn * BN + P) + gc * 16;
     }
   };
-  // LO8: row pointers of the fp8 operands (128-byte rows of k8 bytes)
+  // row pointers of the low-precision operands (rows of k8 * LOW / 8 bytes)
+  const size_t row8 = size_t(g.k8) * LOW / 8;
   auto set_rows8 = [&]() {
 #pragma unroll
     for (int q = 0; q < A_LD; ++q) {
@@ -385,13 +398,13 @@ void gemm_dense_kernel(GemmArgs g) {
       const int P = p / CH, gc = (p % CH) ^ swzc<CH>(P);
       int m = is_tm * BM + P;
       m = m < g.M ? m : g.M - 1;
-      ga[q] = reinterpret_cast<const char*>(g.A8) + size_t(m) * g.k8 + gc * 16;
+      ga[q] = reinterpret_cast<const char*>(g.A8) + size_t(m) * row8 + gc * 16;
     }
 #pragma unroll
     for (int q = 0; q < B_LD; ++q) {
       const int p = (wave * B_LD + q) * 64 + lane;
       const int P = p / CH, gc = (p % CH) ^ swzc<CH>(P);
-      gb[q] = reinterpret_cast<const char*>(g.B8) + size_t(is_tn * BN + P) * g.k8 + gc * 16;
+      gb[q] = reinterpret_cast<const char*>(g.B8) + size_t(is_tn * BN + P) * row8 + gc * 16;
     }
   };
   // (the global source is passed as a uint16_t pointer: with a char pointer
@@ -416,15 +429,21 @@ void gemm_dense_kernel(GemmArgs g) {
         for (int q = 0; q < B_LD; ++q)
           __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(gb[q] + koff8),
                                            (lds_void*)&lds[st][BM * CH + (wave * B_LD + q) * 64], 16, 0, 0);
-        // scale bytes of the tile's rows for this step (4 per row): A's BM
-        // rows by wave 0, B's BN rows by wave 1, placed as dwords [0, BM)
-        // and [BM, BM + BN) behind the tiles (rows past M read padding rows)
-        if (wave < 2 && lane < (wave == 0 ? BM : BN) / 4) {
-          const char* src = wave == 0
-              ? reinterpret_cast<const char*>(g.As) + (size_t(s8) * g.as_rows + is_tm * BM) * 4 + lane * 16
-              : reinterpret_cast<const char*>(g.Bs) + (size_t(s8) * g.bs_rows + is_tn * BN) * 4 + lane * 16;
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(src),
-                                           (lds_void*)&lds[st][(BM + BN) * CH + (wave == 0 ? 0 : BM / 4)], 16, 0, 0);
+        // scale bytes of the tile's rows for this step (SB per row): A's BM
+        // rows by waves [0, WSA), B's BN rows by the next WSB waves, placed
+        // as A's rows then B's rows behind the tiles (rows past M read
+        // padding rows)
+        if (wave < WSA + WSB) {
+          const bool isa = wave < WSA;
+          const int c = (isa ? wave : wave - WSA) * 64 + lane;
+          if (c < (isa ? SCA : SCB)) {
+            const char* src = isa
+                ? reinterpret_cast<const char*>(g.As) + (size_t(s8) * g.as_rows + is_tm * BM) * SB + c * 16
+                : reinterpret_cast<const char*>(g.Bs) + (size_t(s8) * g.bs_rows + is_tn * BN) * SB + c * 16;
+            __builtin_amdgcn_global_load_lds(
+                reinterpret_cast<const uint16_t*>(src),
+                (lds_void*)&lds[st][(BM + BN) * CH + (isa ? wave * 64 : SCA + (wave - WSA) * 64)], 16, 0, 0);
+          }
         }
         ++is_step;
         if (++is_kt == KT) {
@@ -571,6 +590,37 @@ void gemm_dense_kernel(GemmArgs g) {
     });
   };
 
+  // one fp4 k-step (LOW 4): 256 k as four 64-k scaled MFMAs; the MFMA over
+  // k [64m, 64m + 64) takes, for lane half h, 16-byte chunk c = 2m + h of the
+  // row (32 fp4 k, one scale block) and that block's scale byte c of the
+  // row's two scale dwords
+  auto compute_fp4 = [&](int stage) {
+    const u32x4* sa = lds[stage];
+    const u32x4* sb = lds[stage] + BM * CH;
+    const uint32_t* scl = reinterpret_cast<const uint32_t*>(lds[stage] + (BM + BN) * CH);
+    static_for<4>([&](auto m_c) {
+      constexpr int m = decltype(m_c)::value;
+      const int c = 2 * m + lhalf, sh = 8 * (c & 3);
+      i32x8 fa4[TM];
+      int sav[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * TMW + 32 * i + lrow;
+        fa4[i] = widen4(sa[row * CH + (c ^ swzc<CH>(row))]);
+        sav[i] = int(scl[2 * row + (m >> 1)] >> sh);
+      }
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn) {
+        const int row = wn * TNW + 32 * jn + lrow;
+        const i32x8 fb4 = widen4(sb[row * CH + (c ^ swzc<CH>(row))]);
+        const int sbv = int(scl[2 * BM + 2 * row + (m >> 1)] >> sh);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          acc[i][jn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa4[i], fb4, acc[i][jn], 4, 4, 0, sav[i], 0, sbv);
+      }
+    });
+  };
+
   int step = 0;
   for (int ti = 0; ti < my_tiles; ++ti) {
     int tm, tn;
@@ -588,11 +638,12 @@ void gemm_dense_kernel(GemmArgs g) {
     if constexpr (LO8) {
       for (int kt = KT16; kt < KT; ++kt, ++step) {
         begin_step(step);
-        // fp8-only products (no bf16 steps) fetch the residual here
+        // low-precision-only products (no bf16 steps) fetch the residual here
         if constexpr (EM == E_ADD_F32) {
           if (KT16 == 0 && kt == KT - 1) load_residual<TM, TN>(g, res, tm * BM + wm * TMW, tn * BN + wn * TNW, lane);
         }
-        compute_fp8(step % NS);
+        if constexpr (LOW == 8) compute_fp8(step % NS);
+        else compute_fp4(step % NS);
       }
     }
     // the stage just consumed is free until the next step's loads (issued
@@ -611,21 +662,23 @@ void gemm_dense_kernel(GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int AMD, int BMD, int EM, bool LO8 = false>
+template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int AMD, int BMD, int EM, int LOW = 0>
 hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
+  constexpr bool LO8 = LOW != 0;
+  constexpr int KSTEP = LOW == 4 ? 256 : 128, SB = LOW == 4 ? 8 : 4;
   const int ncols = (BMD == B_GATEUP) ? 2 * g.N : g.N;
   if (ncols % BN || g.K % BKT || g.kb % BKT) return hipErrorInvalidValue;
   if (g.kb > 0 && g.K != 2 * g.kb) return hipErrorInvalidValue;
   if (AMD == A_MERGE && (g.hidden % BKT || g.K != 8 * g.hidden || g.kb != 4 * g.hidden)) return hipErrorInvalidValue;
-  if (LO8 && (g.k8 <= 0 || g.k8 % 128 || g.kb != 0 || g.as_rows < ((g.M + BM - 1) / BM) * BM || g.bs_rows < ncols))
+  if (LO8 && (g.k8 <= 0 || g.k8 % KSTEP || g.kb != 0 || g.as_rows < ((g.M + BM - 1) / BM) * BM || g.bs_rows < ncols))
     return hipErrorInvalidValue;
   const int tiles = ((g.M + BM - 1) / BM) * (ncols / BN);
   // as many workgroups as fit on the chip at once: the LDS ring sets how
   // many a CU holds
-  constexpr int kLdsBytes = NS * ((BM + BN) * BKT * 2 + (LO8 ? 2048 : 0));
+  constexpr int kLdsBytes = NS * ((BM + BN) * BKT * 2 + (LO8 ? (BM + BN) * SB : 0));
   constexpr int kPerCU = (160 * 1024) / kLdsBytes < 2 ? 1 : 2;
   const int grid = tiles < kNumCUs * kPerCU ? tiles : kNumCUs * kPerCU;
-  hipLaunchKernelGGL((gemm_dense_kernel<BM, BN, WMW, WNW, NS, BKT, AMD, BMD, EM, LO8>), dim3(grid),
+  hipLaunchKernelGGL((gemm_dense_kernel<BM, BN, WMW, WNW, NS, BKT, AMD, BMD, EM, LOW>), dim3(grid),
                      dim3(WMW * WNW * 64), 0, s, g);
   return hipGetLastError();
 }
@@ -664,15 +717,16 @@ hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
   switch (kind) {
     case GEMM_PATCH:  return launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_STORE_F32>(g, s);
     case GEMM_QKV:
-      return g.k8 > 0 ? launch_dense<PV_GEMM_CFG_QKV, A_DENSE, B_QKV, E_QKV_ROPE, true>(g, s)
+      return g.k8 > 0 ? launch_dense<PV_GEMM_CFG_QKV, A_DENSE, B_QKV, E_QKV_ROPE, 8>(g, s)
                       : launch_dense<PV_GEMM_CFG_QKV, A_DENSE, B_QKV, E_QKV_ROPE>(g, s);
     case GEMM_OPROJ:
     case GEMM_DOWN:
-      return g.k8 > 0 ? launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_ADD_F32, true>(g, s)
+      return g.k8 > 0 ? launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_ADD_F32, 8>(g, s)
                       : launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_ADD_F32>(g, s);
     case GEMM_GATEUP:
-      return g.k8 > 0 ? launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL, true>(g, s)
-                      : launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL>(g, s);
+      if (g.k8 <= 0) return launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL>(g, s);
+      return g.low_fmt == 4 ? launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL, 4>(g, s)
+                            : launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL, 8>(g, s);
     case GEMM_MERGE:
       return g.N % 256 == 0 ? launch_dense<PV_GEMM_CFG_MERGE, A_MERGE, B_ONE, E_STORE>(g, s)
                             : launch_dense<PV_GEMM_CFG_N1K, A_MERGE, B_ONE, E_STORE>(g, s);

@@ -30,12 +30,13 @@ hipError_t gemm_f32(GemmKind kind, const GemmArgs& g, hipStream_t s);
 //   rmsnorm_dual: h = norm(x) * g1 written back in place (fp32), y = norm(h) * g2
 hipError_t rmsnorm(const float* x, const float* g, void* y, int rows, int D, float eps,
                    bool y_f32, hipStream_t s);
-// rmsnorm_hi_lo8: y = norm(x) * g as bf16 hi [N][D] plus the low part y - hi
-// as fp8 e4m3 [N][D] with a power-of-two scale byte per 32 columns, scale
-// bytes step-major: ys[(col / 128) * srows + row][(col / 32) % 4]
-hipError_t rmsnorm_hi_lo8(const float* x, const float* g, void* yh, void* y8, void* ys, int rows, int srows, int D,
+// rmsnorm_hi_lo4: y = norm(x) * g as bf16 hi [N][D] plus the low part y - hi
+// in packed fp4 e2m1 [N][D/2] (low nibble = even column) with a power-of-two
+// scale byte per 32 columns, step-major: ys[(col / 256) * srows + row][(col / 32) % 8]
+hipError_t rmsnorm_hi_lo4(const float* x, const float* g, void* yh, void* y4, void* ys, int rows, int srows, int D,
                           float eps, hipStream_t s);
-// rmsnorm_fp8: y = norm(x) * g as fp8 e4m3 [N][D] with the same scale bytes
+// rmsnorm_fp8: y = norm(x) * g as fp8 e4m3 [N][D] with a power-of-two scale
+// byte per 32 columns, step-major: ys[(col / 128) * srows + row][(col / 32) % 4]
 hipError_t rmsnorm_fp8(const float* x, const float* g, void* y8, void* ys, int rows, int srows, int D, float eps,
                        hipStream_t s);
 hipError_t rmsnorm_dual(float* x, const float* g1, const float* g2, void* y, int rows, int D,
@@ -104,6 +105,9 @@ hipError_t quant_rows_fp8(const void* src, int rows, int K, void* dst8, void* sc
 //   gateup_fp8:   b8 [2F][D] fp8 e4m3 = the gate/up weights in the GEMM's
 //                 interleaved row order, bs [D/128][2F][4] scale bytes
 hipError_t gateup_fp8(const void* w_gate, const void* w_up, void* b8, void* bs, int F, int D, hipStream_t s);
+//   gateup_fp4:   the same rows in packed fp4 e2m1, b4 [2F][D/2],
+//                 bs [D/256][2F][8] scale bytes
+hipError_t gateup_fp4(const void* w_gate, const void* w_up, void* b4, void* bs, int F, int D, hipStream_t s);
 // Content keys of uint8 images (two 64-bit lanes per image, keys [n][2]
 // device); offsets[i] (host) is image i's byte offset from `images`, which
 // must be 4-byte aligned; src_hw host; ws: image_keys_workspace_bytes(n)

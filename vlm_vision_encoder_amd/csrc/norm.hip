@@ -58,11 +58,11 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 }
 
 // The MLP input: y = norm(x) * g as bf16 hi [N][D], and its low part y - hi
-// as fp8 [N][D] with one scale byte per 32 values (blocks of 32 columns;
-// scale bytes step-major: ys[(col / 128) * srows + row][(col / 32) % 4]).
+// as packed fp4 [N][D/2] (low nibble = even column) with one scale byte per
+// 32 columns, scale bytes step-major: ys[(col / 256) * srows + row][(col / 32) % 8].
 template <int NC>
-__global__ __launch_bounds__(256) void rmsnorm_hi_lo8_kernel(const float* __restrict__ x, const float* __restrict__ g,
-                                                             uint16_t* __restrict__ yh, uint8_t* __restrict__ y8,
+__global__ __launch_bounds__(256) void rmsnorm_hi_lo4_kernel(const float* __restrict__ x, const float* __restrict__ g,
+                                                             uint16_t* __restrict__ yh, uint8_t* __restrict__ y4,
                                                              uint8_t* __restrict__ ys, int rows, int srows, float eps) {
   constexpr int D = NC * 256;
   const int lane = threadIdx.x & 63;
@@ -89,12 +89,12 @@ __global__ __launch_bounds__(256) void rmsnorm_hi_lo8_kernel(const float* __rest
     amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
     amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
     amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
-    float mul;
-    const uint32_t sbyte = mx_scale(amax, mul);
-    *reinterpret_cast<uint32_t*>(y8 + size_t(row) * D + col) = pack_fp8x4(l0 * mul, l1 * mul, l2 * mul, l3 * mul);
+    float scale;
+    const uint32_t sbyte = mx_scale4(amax, scale);
+    *reinterpret_cast<uint16_t*>(y4 + size_t(row) * (D / 2) + col / 2) = uint16_t(pack_fp4x4(l0, l1, l2, l3, scale));
     if ((lane & 7) == 0) {
       const int blk = col / 32;
-      ys[(size_t(blk / 4) * srows + row) * 4 + (blk & 3)] = uint8_t(sbyte);
+      ys[(size_t(blk / 8) * srows + row) * 8 + (blk & 7)] = uint8_t(sbyte);
     }
   }
 }
@@ -205,15 +205,15 @@ hipError_t rmsnorm(const float* x, const float* g, void* y, int rows, int D, flo
   return hipErrorInvalidValue;
 }
 
-hipError_t rmsnorm_hi_lo8(const float* x, const float* g, void* yh, void* y8, void* ys, int rows, int srows, int D,
-                         float eps, hipStream_t s) {
+hipError_t rmsnorm_hi_lo4(const float* x, const float* g, void* yh, void* y4, void* ys, int rows, int srows, int D,
+                          float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (D % 128 || srows < rows) return hipErrorInvalidValue;
+  if (D % 256 || srows < rows) return hipErrorInvalidValue;
   const dim3 grid((rows + 3) / 4), block(256);
 #define PV_CASE(NC)                                                                                    \
   if (D == NC * 256) {                                                                                 \
-    hipLaunchKernelGGL((rmsnorm_hi_lo8_kernel<NC>), grid, block, 0, s, x, g, static_cast<uint16_t*>(yh), \
-                       static_cast<uint8_t*>(y8), static_cast<uint8_t*>(ys), rows, srows, eps);           \
+    hipLaunchKernelGGL((rmsnorm_hi_lo4_kernel<NC>), grid, block, 0, s, x, g, static_cast<uint16_t*>(yh), \
+                       static_cast<uint8_t*>(y4), static_cast<uint8_t*>(ys), rows, srows, eps);           \
     return hipGetLastError();                                                                          \
   }
   PV_NORM_CASES(PV_CASE)

@@ -72,8 +72,9 @@ struct Layout {
   size_t meta = 0, items = 0, rope = 0, src = 0, rowinfo = 0, msrc = 0;
   size_t r = 0, y = 0, big = 0;
   size_t wpad = 0;          // bf16 tower: patch weights zero-padded to [D][Kp]
-  // bf16 tower, MLP input's fp8 low part and the gate/up weights in fp8
-  // (fp8 variant: a8/as hold every fp8 GEMM input, up to [N][max(D, F)]):
+  // bf16 tower: the MLP input's fp4 low part and the gate/up weights in fp4
+  // (fp8 variant: a8/as hold every fp8 GEMM input, up to [N][max(D, F)], and
+  // b8/bs this layer's gate/up weights in fp8):
   size_t a8 = 0, as = 0, b8 = 0, bs = 0;
   // fp8 variant: this layer's q|k|v, out-projection and down weights in fp8
   size_t wq8 = 0, wqs = 0, wo8 = 0, wos = 0, wd8 = 0, wds = 0;

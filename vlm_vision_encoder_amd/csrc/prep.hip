@@ -19,9 +19,11 @@
 //                 (x - mean_c) / std_c (Mistral3ImageProcessor table), folded
 //                 into one multiply-add per channel.
 //   resize_norm_u8: the same samples written out as fp32 planes.
-//   gateup_fp8:   fp8 e4m3 copy of the gate/up weights in the GEMM's
+//   gateup_fp4:   fp4 e2m1 copy of the gate/up weights in the GEMM's
 //                 interleaved row order, one power-of-two scale per 32 k, for
-//                 the fp8 product with the MLP input's low part.
+//                 the fp4 product with the MLP input's low part.
+//   gateup_fp8, quant_rows_fp8: fp8 e4m3 copies of weights and activations
+//                 for the fp8 variant of the tower's linear maps.
 #include "common.h"
 #include "kernels.h"
 
@@ -229,6 +231,41 @@ __global__ __launch_bounds__(256) void gateup_fp8_kernel(const uint16_t* __restr
   bs[(size_t(blk / 4) * (2 * F) + n) * 4 + (blk & 3)] = quant_block32(src, b8 + size_t(n) * D + blk * 32);
 }
 
+// The same rows in packed fp4 for the MLP input's fp4 low part: b4
+// [2F][D/2] (low nibble = even k), scales bs[(k/256) * 2F + n][(k/32) % 8].
+__global__ __launch_bounds__(256) void gateup_fp4_kernel(const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
+                                                         uint8_t* __restrict__ b4, uint8_t* __restrict__ bs, int F,
+                                                         int D) {
+  const int blocks = D / 32;
+  const long long idx = blockIdx.x * 256ll + threadIdx.x;
+  if (idx >= 2ll * F * blocks) return;
+  const int n = int(idx / blocks), blk = int(idx - (long long)n * blocks);
+  const int src_row = (n >> 6) * 32 + (n & 31);
+  const uint16_t* src = ((n & 32) ? wu : wg) + size_t(src_row) * D + blk * 32;
+  float f[32];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const u32x4 w = reinterpret_cast<const u32x4*>(src)[c];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[8 * c + 2 * e] = lo_bf16(w[e]);
+      f[8 * c + 2 * e + 1] = hi_bf16(w[e]);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(f[e]));
+  float scale;
+  const uint32_t sbyte = mx_scale4(amax, scale);
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    o[q] = pack_fp4x4(f[8 * q], f[8 * q + 1], f[8 * q + 2], f[8 * q + 3], scale) |
+           (pack_fp4x4(f[8 * q + 4], f[8 * q + 5], f[8 * q + 6], f[8 * q + 7], scale) << 16);
+  *reinterpret_cast<u32x4*>(b4 + size_t(n) * (D / 2) + blk * 16) = o;
+  bs[(size_t(blk / 8) * (2 * F) + n) * 8 + (blk & 7)] = uint8_t(sbyte);
+}
+
 // One thread per (row r, block of 32 columns) of a bf16 [rows][K] matrix;
 // output row row0 + r of dst8 [.][K] and of the scale bytes
 // scales[(col / 128) * srows + row][(col / 32) % 4].
@@ -300,6 +337,15 @@ hipError_t quant_rows_fp8(const void* src, int rows, int K, void* dst8, void* sc
   hipLaunchKernelGGL(quant_rows_fp8_kernel, grid_for((long long)rows * (K / 32)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(src), rows, K, static_cast<uint8_t*>(dst8),
                      static_cast<uint8_t*>(scales), srows, row0);
+  return hipGetLastError();
+}
+
+hipError_t gateup_fp4(const void* w_gate, const void* w_up, void* b4, void* bs, int F, int D, hipStream_t s) {
+  if (F <= 0) return hipSuccess;
+  if (D % 256) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gateup_fp4_kernel, grid_for(2ll * F * (D / 32)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
+                     static_cast<uint8_t*>(b4), static_cast<uint8_t*>(bs), F, D);
   return hipGetLastError();
 }
 

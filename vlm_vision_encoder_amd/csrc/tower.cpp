@@ -280,7 +280,7 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
     auto use_fp8 = [&](pv::GemmArgs& a, int k, const void* b8, const void* bsc, int brows) {
       a.K = 0; a.kb = 0;
       a.A = a8; a.A8 = a8; a.As = as; a.as_rows = srows; a.k8 = k;
-      a.B8 = b8; a.Bs = bsc; a.bs_rows = brows;
+      a.B8 = b8; a.Bs = bsc; a.bs_rows = brows; a.low_fmt = 8;
     };
     if (f8) {  // this layer's weights in fp8
       PV_LAUNCH(PV_K_QKV, pv::quant_rows_fp8(lw.wq, D, D, ws + L.wq8, ws + L.wqs, 3 * D, 0, s));
@@ -316,13 +316,13 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
     }
     if (stop_here && st.stage == PV_STAGE_ATTN_RESID) return copy_stage(st, r, size_t(N) * D * 4, s);
     // the MLP input of the bf16 tower goes in as bf16 plus its low part in
-    // fp8 (times fp8 copies of the weights, 32-k scale blocks): its plain
+    // fp4 (times fp4 copies of the weights, 32-k scale blocks): its plain
     // bf16 rounding would otherwise be the largest error of the tower output
     if (f8) {
       PV_LAUNCH(PV_K_NORM, pv::rmsnorm_fp8(r, lw.ffn_norm, a8, as, N, srows, D, eps, s));
     } else if (bf) {
-      PV_LAUNCH(PV_K_GATEUP, pv::gateup_fp8(lw.w_gate, lw.w_up, ws + L.b8, ws + L.bs, F, D, s));
-      PV_LAUNCH(PV_K_NORM, pv::rmsnorm_hi_lo8(r, lw.ffn_norm, y, ws + L.a8, ws + L.as, N, srows, D, eps, s));
+      PV_LAUNCH(PV_K_GATEUP, pv::gateup_fp4(lw.w_gate, lw.w_up, ws + L.b8, ws + L.bs, F, D, s));
+      PV_LAUNCH(PV_K_NORM, pv::rmsnorm_hi_lo4(r, lw.ffn_norm, y, ws + L.a8, ws + L.as, N, srows, D, eps, s));
     } else {
       PV_LAUNCH(PV_K_NORM, pv::rmsnorm(r, lw.ffn_norm, y, N, D, eps, true, s));
     }
@@ -332,7 +332,7 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
       a.A = y; a.lda = D;
       if (bf) {
         a.A8 = ws + L.a8; a.B8 = ws + L.b8; a.As = ws + L.as; a.Bs = ws + L.bs;
-        a.k8 = D; a.as_rows = srows; a.bs_rows = 2 * F;
+        a.k8 = D; a.as_rows = srows; a.bs_rows = 2 * F; a.low_fmt = 4;
       }
       a.B0 = lw.w_gate; a.B1 = lw.w_up; a.ldb = D;
       a.C = big; a.ldc = F;
