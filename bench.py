@@ -424,16 +424,23 @@ def main():
     torch.cuda.synchronize()
     log("warmup done")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # an event after every step as well (per-step median and spread)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         step()
+        marks[i].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
+    per_step = sorted([ev0.elapsed_time(marks[0])] + [marks[i - 1].elapsed_time(marks[i])
+                                                      for i in range(1, args.steps)])
+    step_stats = {"median_ms": round(per_step[len(per_step) // 2], 4), "min_ms": round(per_step[0], 4),
+                  "max_ms": round(per_step[-1], 4)}
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (wall {t_wall * 1e3 / args.steps:.3f} ms/step)")
     assert torch.isfinite(out.float()).all().item(), "non-finite output"
 
@@ -490,6 +497,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms": step_stats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -240,6 +240,20 @@ def test_bf16_many_tiny_images():
     check("out", to_np(c.run()), ref["out"], TOL["bf16"], stored_bf16=True)
 
 
+def test_bf16_wide_tiles_for_the_hidden_width_products():
+    """9 images of 448^2 (9,216 patches, D 1024): the out-projection, down
+    and patch-embedding products take their 192 x 256 tiles (one round of
+    the chip instead of two partly filled ones) -- checked stage by stage."""
+    wl = _bf16_small([(448, 448)] * 9, 1)
+    say(f"bf16 wide hidden-width tiles: {wl.n_patches} patches")
+    c = Case(wl)
+    ref = c.ref()
+    check("patch_embed", to_np(c.stage("patch_embed")), ref["patch_embed"], TOL["bf16"])
+    check("attn_resid[0]", to_np(c.stage("attn_resid", 0)), ref["attn_out"][0], TOL["bf16"])
+    check("block_out[0]", to_np(c.stage("block_out", 0)), ref["block_out"][0], TOL["bf16"])
+    check("out", to_np(c.run()), ref["out"], TOL["bf16"], stored_bf16=True)
+
+
 @pytest.mark.parametrize("hidden,heads,mlp", [(512, 8, 1024), (768, 12, 2048), (1536, 24, 3072), (2048, 32, 2048)])
 def test_bf16_other_widths(hidden, heads, mlp):
     """The other supported widths (norm kernels of 2, 3, 6, 8 row chunks; q,k,v

@@ -313,6 +313,7 @@ void gemm_dense_kernel(GemmArgs g) {
   static_assert(!LO8 || (BM <= 256 && BN <= 256 && BKT == 64 && NS == 2 && AMD == A_DENSE && WSA + WSB <= NW),
                 "low-precision steps: tiles of at most 256 x 256, 64-k bf16 steps (128-byte rows)");
 
+  constexpr bool kPrefetchRes = TM * TN <= 4;
   // scale bytes behind each stage's tiles
   constexpr int kStageU4 = (BM + BN) * CH + (LO8 ? SCA + SCB : 0);
   __shared__ u32x4 lds[NS][kStageU4];
@@ -629,8 +630,9 @@ void gemm_dense_kernel(GemmArgs g) {
     for (int kt = 0; kt < KT16; ++kt, ++step) {
       begin_step(step);
       // the residual of an accumulating epilogue is fetched while the
-      // tile's last k-step runs
-      if constexpr (EM == E_ADD_F32) {
+      // tile's last k-step runs (when its TM x TN x 16 values fit the
+      // registers; larger wave tiles read it in the epilogue)
+      if constexpr (EM == E_ADD_F32 && kPrefetchRes) {
         if (kt == KT16 - 1) load_residual<TM, TN>(g, res, tm * BM + wm * TMW, tn * BN + wn * TNW, lane);
       }
       compute_bf16(step % NS);
@@ -639,7 +641,7 @@ void gemm_dense_kernel(GemmArgs g) {
       for (int kt = KT16; kt < KT; ++kt, ++step) {
         begin_step(step);
         // low-precision-only products (no bf16 steps) fetch the residual here
-        if constexpr (EM == E_ADD_F32) {
+        if constexpr (EM == E_ADD_F32 && kPrefetchRes) {
           if (KT16 == 0 && kt == KT - 1) load_residual<TM, TN>(g, res, tm * BM + wm * TMW, tn * BN + wn * TNW, lane);
         }
         if constexpr (LOW == 8) compute_fp8(step % NS);
@@ -652,7 +654,7 @@ void gemm_dense_kernel(GemmArgs g) {
     __syncthreads();
     float* scratch = reinterpret_cast<float*>(lds[(step - 1) % NS]) + wave * kScratchFloats;
     epilogue_lds<EM, TM, TN, kEpiRows>(g, acc, tm * BM + wm * TMW, tn * BN + wn * TNW, lane, scratch,
-                                       EM == E_ADD_F32 ? &res : nullptr);
+                                       EM == E_ADD_F32 && kPrefetchRes ? &res : nullptr);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -701,6 +703,11 @@ hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
 #ifndef PV_GEMM_CFG_RES
 #define PV_GEMM_CFG_RES 128, 128, 2, 2, 2, 64
 #endif
+// the same products in 192 x 256 tiles, 8 waves, one workgroup per CU:
+// chosen per call when it needs enough fewer rounds of the chip (below)
+#ifndef PV_GEMM_CFG_RES_WIDE
+#define PV_GEMM_CFG_RES_WIDE 192, 256, 2, 4, 2, 64
+#endif
 // merger (a few thousand rows, N = 5120): 256 x 256 tiles, one round of
 // 240 tiles at 1540^2; 256 x 128 when N is not a multiple of 256
 #ifndef PV_GEMM_CFG_MERGE
@@ -712,15 +719,35 @@ hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
 #define PV_GEMM_CFG_QKV 256, 192, 4, 2, 2, 64
 #endif
 
+// N = hidden products: a 192 x 256 round of the chip (one tile per CU) takes
+// about 5/3 of a 128 x 128 round (two tiles per CU) -- measured at 1540^2
+// with K = 4096 -- so the wide tiles pay only when they save a partly
+// filled last round (1540^2: 256 tiles in one round against 760 tiles in
+// two rounds of 512 slots).
+bool use_res_wide(const GemmArgs& g) {
+  if (g.N % 256) return false;
+  const long long t_res = (long long)((g.M + 127) / 128) * (g.N / 128);
+  const long long t_wide = (long long)((g.M + 191) / 192) * (g.N / 256);
+  const long long r_res = (t_res + 2 * kNumCUs - 1) / (2 * kNumCUs);
+  const long long r_wide = (t_wide + kNumCUs - 1) / kNumCUs;
+  return 5 * r_wide < 3 * r_res;
+}
+
 hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
+  const bool wide = use_res_wide(g);
   switch (kind) {
-    case GEMM_PATCH:  return launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_STORE_F32>(g, s);
+    case GEMM_PATCH:
+      return wide ? launch_dense<PV_GEMM_CFG_RES_WIDE, A_DENSE, B_ONE, E_STORE_F32>(g, s)
+                  : launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_STORE_F32>(g, s);
     case GEMM_QKV:
       return g.k8 > 0 ? launch_dense<PV_GEMM_CFG_QKV, A_DENSE, B_QKV, E_QKV_ROPE, 8>(g, s)
                       : launch_dense<PV_GEMM_CFG_QKV, A_DENSE, B_QKV, E_QKV_ROPE>(g, s);
     case GEMM_OPROJ:
     case GEMM_DOWN:
+      if (wide)
+        return g.k8 > 0 ? launch_dense<PV_GEMM_CFG_RES_WIDE, A_DENSE, B_ONE, E_ADD_F32, 8>(g, s)
+                        : launch_dense<PV_GEMM_CFG_RES_WIDE, A_DENSE, B_ONE, E_ADD_F32>(g, s);
       return g.k8 > 0 ? launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_ADD_F32, 8>(g, s)
                       : launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_ADD_F32>(g, s);
     case GEMM_GATEUP:
