@@ -113,7 +113,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
     kbase[j] = qkv + size_t(base + k_row[j]) * ld + koff + k_chunk[j] * 8;
     vbase[j] = qkv + size_t(base + v_row[j]) * ld + voff + v_chunk[j] * 8;
   }
-  auto issue_loads = [&](int kt, int st) {
+  // LDS stages as compile-time constants: the key loop runs two tiles per
+  // trip (stage 1 then 0, or 0 then 1), so every fragment address is a
+  // loop-invariant register plus an immediate offset
+  const std::integral_constant<int, 0> S0;
+  const std::integral_constant<int, 1> S1;
+  auto issue_loads = [&](int kt, auto st_c) {
+    constexpr int st = decltype(st_c)::value;
     const bool partial = kt * 64 + 64 > n;  // rows past the image are clamped to its last row
     const size_t toff = size_t(kt) * 64 * ld;
 #pragma unroll
@@ -128,8 +134,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
         gk = qkv + size_t(base + uk) * ld + koff + k_chunk[j] * 8;
         gv = qkv + size_t(base + uv) * ld + voff + v_chunk[j] * 8;
       }
-      __builtin_amdgcn_global_load_lds(gk, (lds_void*)&kl[st][(wave * LPT + j) * 64], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(gv, (lds_void*)&vl[st][(wave * LPT + j) * 64], 16, 0, 0);
+      // (the index is below SLOTS anyway; the mask lets the compiler see that
+      // the load stays inside its stage, so reads of the other stage do not
+      // wait for it)
+      __builtin_amdgcn_global_load_lds(gk, (lds_void*)&kl[st][((wave * LPT + j) * 64) & (SLOTS - 1)], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(gv, (lds_void*)&vl[st][((wave * LPT + j) * 64) & (SLOTS - 1)], 16, 0, 0);
     }
   };
 
@@ -164,9 +173,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
   // One key tile.  MODE 0: first tile of the fixed-offset pass (finds m0);
   // MODE 1: later tiles of that pass (offset folded into the MFMA); MODE 2:
   // online softmax with a running max (fallback pass).
-  auto tile = [&](auto mode_c, int kt) {
+  auto tile = [&](auto mode_c, int kt, auto st_c) {
     constexpr int MODE = decltype(mode_c)::value;
-    const int st = kt & 1;
+    constexpr int st = decltype(st_c)::value;  // = kt & 1: LDS addresses are base + immediate
     // ---- S^T = K Q^T (minus the query offset in MODE 1)
     floatx16 s[2][QB];
 #pragma unroll
@@ -289,12 +298,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
       m_sc[tb] = -INFINITY;
       l_run[tb] = 0.f;
     }
-    issue_loads(0, 0);
+    issue_loads(0, S0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  auto next = [&](int kt) {  // loads of tile kt+1 behind tile kt's compute
-    if (kt + 1 < nkt) issue_loads(kt + 1, (kt + 1) & 1);
+  // loads of tile kt+1 (into stage st_next = (kt+1) & 1) behind tile kt's compute
+  auto next = [&](int kt, auto st_next) {
+    if (kt + 1 < nkt) issue_loads(kt + 1, st_next);
   };
   auto done = [&]() {
     __builtin_amdgcn_s_waitcnt(0);
@@ -305,12 +315,21 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
   if (!online) {
     // ---- fixed-offset pass
     reset();
-    next(0);
-    if (active) tile(std::integral_constant<int, 0>(), 0);
+    next(0, S1);
+    if (active) tile(std::integral_constant<int, 0>(), 0, S0);
     done();
-    for (int kt = 1; kt < nkt; ++kt) {
-      next(kt);
-      if (active) tile(std::integral_constant<int, 1>(), kt);
+    int kt = 1;
+    for (; kt + 1 < nkt; kt += 2) {  // two tiles per trip: stages 1, 0
+      next(kt, S0);
+      if (active) tile(std::integral_constant<int, 1>(), kt, S1);
+      done();
+      next(kt + 1, S1);
+      if (active) tile(std::integral_constant<int, 1>(), kt + 1, S0);
+      done();
+    }
+    if (kt < nkt) {
+      next(kt, S0);
+      if (active) tile(std::integral_constant<int, 1>(), kt, S1);
       done();
     }
     // ---- range check: rerun with a running max if any sum or output overflowed
@@ -330,9 +349,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
   }
   if (online) {
     reset();
-    for (int kt = 0; kt < nkt; ++kt) {
-      next(kt);
-      if (active) tile(std::integral_constant<int, 2>(), kt);
+    int kt = 0;
+    for (; kt + 1 < nkt; kt += 2) {
+      next(kt, S1);
+      if (active) tile(std::integral_constant<int, 2>(), kt, S0);
+      done();
+      next(kt + 1, S0);
+      if (active) tile(std::integral_constant<int, 2>(), kt + 1, S1);
+      done();
+    }
+    if (kt < nkt) {
+      next(kt, S1);
+      if (active) tile(std::integral_constant<int, 2>(), kt, S0);
       done();
     }
   }
