@@ -360,8 +360,17 @@ void gemm_dense_kernel(GemmArgs g) {
 
   // load plan: wave instruction q of this wave fills LDS slots
   // [(wave * X_LD + q) * 64, +64) of the A (B) tile; lane l takes slot p.
-  const char* ga[A_LD];
-  const char* gb[B_LD];
+  // Every instruction reads rows of one matrix, so its address is a uniform
+  // base (scalar registers; the k-step moves only that) plus a per-lane
+  // 32-bit byte offset inside the tile: the loads cost no vector ALU work.
+  // The instruction's rows are [P0, P0 + 64 / CH), P0 = (wave * X_LD + q) *
+  // 64 / CH: inside one 32-row gate/up block and one q/k/v matrix.
+  static_assert(64 % CH == 0 && 32 % (64 / CH) == 0, "rows per load instruction");
+  const char* ga_b = nullptr;             // A_DENSE: this tile's first row of A
+  uint32_t ga_o[A_LD];
+  const char* ga[AMD == A_MERGE ? A_LD : 1];  // A_MERGE: per-lane row pointers
+  const char* gb_b[B_LD];
+  uint32_t gb_o[B_LD];
   int4 msrc4[AMD == A_MERGE ? A_LD : 1];  // A_MERGE: source rows of each load slot's row
   int a_gc[AMD == A_MERGE ? A_LD : 1];    // A_MERGE: chunk each load slot fetches
   int is_tm = 0, is_tn = 0;               // tile of the steps being issued
@@ -370,6 +379,7 @@ void gemm_dense_kernel(GemmArgs g) {
     tile_mn(t, tm, tn);
     is_tm = tm;
     is_tn = tn;
+    if constexpr (AMD == A_DENSE) ga_b = reinterpret_cast<const char*>(g.A) + size_t(tm) * BM * g.lda * 2;
 #pragma unroll
     for (int q = 0; q < A_LD; ++q) {
       const int p = (wave * A_LD + q) * 64 + lane;
@@ -377,7 +387,7 @@ void gemm_dense_kernel(GemmArgs g) {
       int m = tm * BM + P;
       m = m < g.M ? m : g.M - 1;  // rows past M are computed but never stored
       if constexpr (AMD == A_DENSE) {
-        ga[q] = reinterpret_cast<const char*>(g.A) + (size_t(m) * g.lda + gc * 8) * 2;
+        ga_o[q] = uint32_t(((m - tm * BM) * g.lda + gc * 8) * 2);
       } else {
         msrc4[q] = reinterpret_cast<const int4*>(g.maps.msrc)[m];
         a_gc[q] = gc;
@@ -387,25 +397,48 @@ void gemm_dense_kernel(GemmArgs g) {
     for (int q = 0; q < B_LD; ++q) {
       const int p = (wave * B_LD + q) * 64 + lane;
       const int P = p / CH, gc = (p % CH) ^ swzc<CH>(P);
-      gb[q] = b_row<BMD>(g, tn * BN + P) + gc * 16;
+      const int P0 = (wave * B_LD + q) * (64 / CH);  // uniform: row of lane 0
+      const int n0 = tn * BN + P0;
+      const char* base;
+      int r;  // row inside the base matrix, relative to the base
+      if constexpr (BMD == B_ONE) {
+        const int n0c = n0 < g.N ? n0 : g.N - 1, n = tn * BN + P;
+        base = reinterpret_cast<const char*>(g.B0) + size_t(n0c) * g.ldb * 2;
+        r = (n < g.N ? n : g.N - 1) - n0c;
+      } else if constexpr (BMD == B_QKV) {
+        const int which = n0 / g.hidden;
+        const void* bm = which == 0 ? g.B0 : (which == 1 ? g.B1 : g.B2);
+        base = reinterpret_cast<const char*>(bm) + size_t(n0 - which * g.hidden) * g.ldb * 2;
+        r = P - P0;
+      } else {
+        // 32-row blocks alternate gate, up: rows [64j, 64j+32) -> gate rows
+        // [32j, 32j+32), rows [64j+32, 64j+64) -> up rows [32j, 32j+32).
+        const void* bm = (n0 & 32) ? g.B1 : g.B0;
+        base = reinterpret_cast<const char*>(bm) + size_t((n0 >> 6) * 32 + (n0 & 31)) * g.ldb * 2;
+        r = P - P0;
+      }
+      gb_b[q] = base;
+      gb_o[q] = uint32_t(r * g.ldb * 2 + gc * 16);
     }
   };
-  // row pointers of the low-precision operands (rows of k8 * LOW / 8 bytes)
+  // the same for the low-precision operands (rows of k8 * LOW / 8 bytes)
   const size_t row8 = size_t(g.k8) * LOW / 8;
   auto set_rows8 = [&]() {
+    ga_b = reinterpret_cast<const char*>(g.A8) + size_t(is_tm) * BM * row8;
 #pragma unroll
     for (int q = 0; q < A_LD; ++q) {
       const int p = (wave * A_LD + q) * 64 + lane;
       const int P = p / CH, gc = (p % CH) ^ swzc<CH>(P);
       int m = is_tm * BM + P;
       m = m < g.M ? m : g.M - 1;
-      ga[q] = reinterpret_cast<const char*>(g.A8) + size_t(m) * row8 + gc * 16;
+      ga_o[q] = uint32_t((m - is_tm * BM) * row8 + gc * 16);
     }
 #pragma unroll
     for (int q = 0; q < B_LD; ++q) {
       const int p = (wave * B_LD + q) * 64 + lane;
       const int P = p / CH, gc = (p % CH) ^ swzc<CH>(P);
-      gb[q] = reinterpret_cast<const char*>(g.B8) + size_t(is_tn * BN + P) * row8 + gc * 16;
+      gb_b[q] = reinterpret_cast<const char*>(g.B8) + size_t(is_tn * BN) * row8;
+      gb_o[q] = uint32_t(P * row8 + gc * 16);
     }
   };
   // (the global source is passed as a uint16_t pointer: with a char pointer
@@ -424,11 +457,11 @@ void gemm_dense_kernel(GemmArgs g) {
         const size_t koff8 = size_t(s8) * 128;
 #pragma unroll
         for (int q = 0; q < A_LD; ++q)
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(ga[q] + koff8),
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(ga_b + koff8 + ga_o[q]),
                                            (lds_void*)&lds[st][(wave * A_LD + q) * 64], 16, 0, 0);
 #pragma unroll
         for (int q = 0; q < B_LD; ++q)
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(gb[q] + koff8),
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(gb_b[q] + koff8 + gb_o[q]),
                                            (lds_void*)&lds[st][BM * CH + (wave * B_LD + q) * 64], 16, 0, 0);
         // scale bytes of the tile's rows for this step (SB per row): A's BM
         // rows by waves [0, WSA), B's BN rows by the next WSB waves, placed
@@ -471,12 +504,16 @@ void gemm_dense_kernel(GemmArgs g) {
     }
     const size_t koffb = size_t(is_kt < KTB ? is_kt : is_kt - KTB) * BKT * 2;
 #pragma unroll
-    for (int q = 0; q < A_LD; ++q)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(ga[q] + koff),
+    for (int q = 0; q < A_LD; ++q) {
+      const char* src;
+      if constexpr (AMD == A_MERGE) src = ga[q] + koff;
+      else src = ga_b + koff + ga_o[q];
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(src),
                                        (lds_void*)&lds[st][(wave * A_LD + q) * 64], 16, 0, 0);
+    }
 #pragma unroll
     for (int q = 0; q < B_LD; ++q)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(gb[q] + koffb),
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(gb_b[q] + koffb + gb_o[q]),
                                        (lds_void*)&lds[st][BM * CH + (wave * B_LD + q) * 64], 16, 0, 0);
     ++is_step;
     if (++is_kt == KT) {
@@ -508,25 +545,30 @@ void gemm_dense_kernel(GemmArgs g) {
     __syncthreads();
     if (is_step < steps) issue_next();
   };
+  // fragment offsets (16-byte units inside a stage).  A row's chunk swizzle
+  // depends only on lrow here (wave tiles and 32-row blocks start at
+  // multiples of 16 rows), so chunk c = 2k + lhalf of A fragment i sits at
+  // fa_off[k] + 32 * i * CH (B: fb_off[k] + 32 * j * CH): one register per k
+  // and an immediate offset per fragment.
+  static_assert(TMW % 16 == 0 && TNW % 16 == 0, "row-independent chunk swizzle");
+  int fa_off[CH / 2], fb_off[CH / 2];
+#pragma unroll
+  for (int k = 0; k < CH / 2; ++k) {
+    const int c = (2 * k + lhalf) ^ swzc<CH>(lrow);
+    fa_off[k] = (wm * TMW + lrow) * CH + c;
+    fb_off[k] = BM * CH + (wn * TNW + lrow) * CH + c;
+  }
   // one bf16 k-step: fragments of k-substep ks + 1 are read while the MFMAs
   // of ks run
   auto compute_bf16 = [&](int stage) {
-    const u32x4* sa = lds[stage];
-    const u32x4* sb = lds[stage] + BM * CH;
+    const u32x4* sl = lds[stage];
     constexpr int KS = BKT / 16;
     u32x4 fa[2][TM], fb[2][TN];
     auto read_frags = [&](int ks, u32x4 (&ra)[TM], u32x4 (&rb)[TN]) {
-      const int ch = 2 * ks + lhalf;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * TMW + 32 * i + lrow;
-        ra[i] = sa[row * CH + (ch ^ swzc<CH>(row))];
-      }
+      for (int i = 0; i < TM; ++i) ra[i] = sl[fa_off[ks] + 32 * i * CH];
 #pragma unroll
-      for (int jn = 0; jn < TN; ++jn) {
-        const int row = wn * TNW + 32 * jn + lrow;
-        rb[jn] = sb[row * CH + (ch ^ swzc<CH>(row))];
-      }
+      for (int jn = 0; jn < TN; ++jn) rb[jn] = sl[fb_off[ks] + 32 * jn * CH];
     };
     read_frags(0, fa[0], fb[0]);
     static_for<KS>([&](auto ks_c) {
@@ -560,8 +602,7 @@ void gemm_dense_kernel(GemmArgs g) {
   // one fp8 k-step (LO8): two 64-k scaled MFMAs; scale words: one dword per
   // tile row, byte b = 32-k block b of the step
   auto compute_fp8 = [&](int stage) {
-    const u32x4* sa = lds[stage];
-    const u32x4* sb = lds[stage] + BM * CH;
+    const u32x4* sl = lds[stage];
     const uint32_t* scl = reinterpret_cast<const uint32_t*>(lds[stage] + (BM + BN) * CH);
     uint32_t sa_w[TM], sb_w[TN];
 #pragma unroll
@@ -570,19 +611,16 @@ void gemm_dense_kernel(GemmArgs g) {
     for (int jn = 0; jn < TN; ++jn) sb_w[jn] = scl[BM + wn * TNW + 32 * jn + lrow];
     static_for<2>([&](auto ks_c) {
       constexpr int ks = decltype(ks_c)::value;
-      const int c0 = 4 * ks + lhalf, c1 = c0 + 2;
-      // all A fragments held, B fragments streamed one at a time
+      // chunks c0 = 4 ks + lhalf and c1 = c0 + 2 of each row; all A
+      // fragments held, B fragments streamed one at a time
       i32x8 fa8[TM];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * TMW + 32 * i + lrow;
-        fa8[i] = join8(sa[row * CH + (c0 ^ swzc<CH>(row))], sa[row * CH + (c1 ^ swzc<CH>(row))]);
-      }
+      for (int i = 0; i < TM; ++i)
+        fa8[i] = join8(sl[fa_off[2 * ks] + 32 * i * CH], sl[fa_off[2 * ks + 1] + 32 * i * CH]);
       const int sh = 8 * (2 * ks + lhalf);
 #pragma unroll
       for (int jn = 0; jn < TN; ++jn) {
-        const int row = wn * TNW + 32 * jn + lrow;
-        const i32x8 fb8 = join8(sb[row * CH + (c0 ^ swzc<CH>(row))], sb[row * CH + (c1 ^ swzc<CH>(row))]);
+        const i32x8 fb8 = join8(sl[fb_off[2 * ks] + 32 * jn * CH], sl[fb_off[2 * ks + 1] + 32 * jn * CH]);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
           acc[i][jn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa8[i], fb8, acc[i][jn], 0, 0, 0,
@@ -596,8 +634,7 @@ void gemm_dense_kernel(GemmArgs g) {
   // row (32 fp4 k, one scale block) and that block's scale byte c of the
   // row's two scale dwords
   auto compute_fp4 = [&](int stage) {
-    const u32x4* sa = lds[stage];
-    const u32x4* sb = lds[stage] + BM * CH;
+    const u32x4* sl = lds[stage];
     const uint32_t* scl = reinterpret_cast<const uint32_t*>(lds[stage] + (BM + BN) * CH);
     static_for<4>([&](auto m_c) {
       constexpr int m = decltype(m_c)::value;
@@ -607,13 +644,13 @@ void gemm_dense_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int row = wm * TMW + 32 * i + lrow;
-        fa4[i] = widen4(sa[row * CH + (c ^ swzc<CH>(row))]);
+        fa4[i] = widen4(sl[fa_off[m] + 32 * i * CH]);
         sav[i] = int(scl[2 * row + (m >> 1)] >> sh);
       }
 #pragma unroll
       for (int jn = 0; jn < TN; ++jn) {
         const int row = wn * TNW + 32 * jn + lrow;
-        const i32x8 fb4 = widen4(sb[row * CH + (c ^ swzc<CH>(row))]);
+        const i32x8 fb4 = widen4(sl[fb_off[m] + 32 * jn * CH]);
         const int sbv = int(scl[2 * BM + 2 * row + (m >> 1)] >> sh);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
