@@ -98,9 +98,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
   const bool active = wq0 < n;
 
   // ---- load plan: wave-instruction j covers slots [(wave*LPT + j) * 64, +64);
-  // lane l fetches slot p = that + l.
-  const uint16_t* kbase[LPT];
-  const uint16_t* vbase[LPT];
+  // lane l fetches slot p = that + l.  A load's address is the key tile's
+  // first row (uniform, scalar registers) plus a 32-bit lane offset.
+  uint32_t k_lo[LPT], v_lo[LPT];
   int k_row[LPT], v_row[LPT], k_chunk[LPT], v_chunk[LPT];
 #pragma unroll
   for (int j = 0; j < LPT; ++j) {
@@ -110,8 +110,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
     k_chunk[j] = pc ^ kswz(P);
     v_row[j] = P;
     v_chunk[j] = pc ^ (2 * (P & 3));
-    kbase[j] = qkv + size_t(base + k_row[j]) * ld + koff + k_chunk[j] * 8;
-    vbase[j] = qkv + size_t(base + v_row[j]) * ld + voff + v_chunk[j] * 8;
+    k_lo[j] = uint32_t((k_row[j] * ld + koff + k_chunk[j] * 8) * 2);
+    v_lo[j] = uint32_t((v_row[j] * ld + voff + v_chunk[j] * 8) * 2);
   }
   // LDS stages as compile-time constants: the key loop runs two tiles per
   // trip (stage 1 then 0, or 0 then 1), so every fragment address is a
@@ -121,19 +121,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
   auto issue_loads = [&](int kt, auto st_c) {
     constexpr int st = decltype(st_c)::value;
     const bool partial = kt * 64 + 64 > n;  // rows past the image are clamped to its last row
-    const size_t toff = size_t(kt) * 64 * ld;
+    const char* tile0 = reinterpret_cast<const char*>(qkv + size_t(base + kt * 64) * ld);
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
-      const uint16_t* gk = kbase[j] + toff;
-      const uint16_t* gv = vbase[j] + toff;
+      uint32_t ok = k_lo[j], ov = v_lo[j];
       if (partial) {
-        int uk = kt * 64 + k_row[j];
-        uk = uk < n ? uk : n - 1;
-        int uv = kt * 64 + v_row[j];
-        uv = uv < n ? uv : n - 1;
-        gk = qkv + size_t(base + uk) * ld + koff + k_chunk[j] * 8;
-        gv = qkv + size_t(base + uv) * ld + voff + v_chunk[j] * 8;
+        const int last = n - 1 - kt * 64;  // >= 0: the tile holds a key
+        const int uk = k_row[j] < last ? k_row[j] : last, uv = v_row[j] < last ? v_row[j] : last;
+        ok = uint32_t((uk * ld + koff + k_chunk[j] * 8) * 2);
+        ov = uint32_t((uv * ld + voff + v_chunk[j] * 8) * 2);
       }
+      const uint16_t* gk = reinterpret_cast<const uint16_t*>(tile0 + ok);
+      const uint16_t* gv = reinterpret_cast<const uint16_t*>(tile0 + ov);
       // (the index is below SLOTS anyway; the mask lets the compiler see that
       // the load stays inside its stage, so reads of the other stage do not
       // wait for it)
