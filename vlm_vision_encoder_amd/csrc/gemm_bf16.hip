@@ -109,30 +109,28 @@ __device__ __forceinline__ int stage_row(int r) { return r ^ ((r >> 2) & 1); }
 // Read-back layout of the fp32 epilogue: pass h, iteration it of block
 // (i, j) gives a lane row (lane >> 3) + 8 * it + h * SR, columns 4 * (lane & 7)
 // .. +3.  load_residual fetches the residual values of those positions ahead
-// of time (E_ADD_F32), so the read-modify-write does not wait for them.
-template <int TM, int TN>
+// of time (E_ADD_F32) for the first NB blocks (b = i * TN + j < NB), so the
+// read-modify-write does not wait for them; the other blocks read theirs in
+// the epilogue.
+template <int NB>
 struct Residual {
-  floatx4 v[TM][TN][4];
+  floatx4 v[NB][4];
 };
-template <int TM, int TN>
-__device__ __forceinline__ void load_residual(const GemmArgs& g, Residual<TM, TN>& res, int m_base, int n_base,
-                                              int lane) {
+template <int TM, int TN, int B, int NB>
+__device__ __forceinline__ void load_residual_block(const GemmArgs& g, Residual<NB>& res, int m_base, int n_base,
+                                                    int lane) {
+  constexpr int i = B / TN, j = B % TN;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int row = m_base + 32 * i + (lane >> 3) + 8 * it, col = n_base + 32 * j + 4 * (lane & 7);
-        const int rr = row < g.M ? row : g.M - 1;  // rows past M are loaded but never stored
-        res.v[i][j][it] =
-            *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(g.C) + size_t(rr) * g.ldc + col);
-      }
+  for (int it = 0; it < 4; ++it) {
+    const int row = m_base + 32 * i + (lane >> 3) + 8 * it, col = n_base + 32 * j + 4 * (lane & 7);
+    const int rr = row < g.M ? row : g.M - 1;  // rows past M are loaded but never stored
+    res.v[B][it] = *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(g.C) + size_t(rr) * g.ldc + col);
+  }
 }
 
-template <int EM, int TM, int TN, int SR = 32>
+template <int EM, int TM, int TN, int SR, int NRB>
 __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[TM][TN], int m_base, int n_base,
-                                             int lane, float* scratch, const Residual<TM, TN>* res = nullptr) {
+                                             int lane, float* scratch, const Residual<NRB>& res) {
   const int lrow = lane & 31, lhalf = lane >> 5;
   if constexpr (EM == E_ADD_F32 || EM == E_STORE_F32) {
     static_assert(SR == 32 || SR == 16, "staging rows");
@@ -156,7 +154,9 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[
               floatx4* dst = reinterpret_cast<floatx4*>(reinterpret_cast<float*>(g.C) + size_t(row) * g.ldc + col);
               if constexpr (EM == E_ADD_F32) {
                 static_assert(EM != E_ADD_F32 || SR == 32, "prefetched residual assumes one pass per block");
-                *dst = (res ? res->v[i][j][it] : *dst) + val;
+                const int b = i * TN + j;
+                if (b < NRB) *dst = res.v[b < NRB ? b : 0][it] + val;
+                else *dst = *dst + val;
               } else {
                 *dst = val;
               }
@@ -313,7 +313,11 @@ void gemm_dense_kernel(GemmArgs g) {
   static_assert(!LO8 || (BM <= 256 && BN <= 256 && BKT == 64 && NS == 2 && AMD == A_DENSE && WSA + WSB <= NW),
                 "low-precision steps: tiles of at most 256 x 256, 64-k bf16 steps (128-byte rows)");
 
-  constexpr bool kPrefetchRes = TM * TN <= 4;
+  // residual-adding epilogues fetch the residual of up to 4 blocks (64
+  // values a lane) during the tile's last k-steps, one block per step, so
+  // the reads overlap those steps' MFMAs (a step waits for all loads issued
+  // in the one before)
+  constexpr int kPreBlocks = TM * TN <= 4 ? TM * TN : 2;
   // scale bytes behind each stage's tiles
   constexpr int kStageU4 = (BM + BN) * CH + (LO8 ? SCA + SCB : 0);
   __shared__ u32x4 lds[NS][kStageU4];
@@ -663,14 +667,21 @@ void gemm_dense_kernel(GemmArgs g) {
   for (int ti = 0; ti < my_tiles; ++ti) {
     int tm, tn;
     tile_mn(tile_of(ti), tm, tn);
-    Residual<TM, TN> res;
+    Residual<kPreBlocks> res;
     for (int kt = 0; kt < KT16; ++kt, ++step) {
       begin_step(step);
-      // the residual of an accumulating epilogue is fetched while the
-      // tile's last k-step runs (when its TM x TN x 16 values fit the
-      // registers; larger wave tiles read it in the epilogue)
-      if constexpr (EM == E_ADD_F32 && kPrefetchRes) {
-        if (kt == KT16 - 1) load_residual<TM, TN>(g, res, tm * BM + wm * TMW, tn * BN + wn * TNW, lane);
+      // an accumulating epilogue's residual: block b of the first
+      // kPreBlocks is fetched in k-step KT16 - kPreBlocks + b (the other
+      // blocks of larger wave tiles are read in the epilogue)
+      if constexpr (EM == E_ADD_F32) {
+        static_for<kPreBlocks>([&](auto b_c) {
+          constexpr int b = decltype(b_c)::value;
+          // products with low-precision steps take all blocks in the last
+          // bf16 step (spreading them spills there)
+          const int at = LO8 ? KT16 - 1 : (KT16 - kPreBlocks + b > 0 ? KT16 - kPreBlocks + b : 0);
+          if (kt == at)
+            load_residual_block<TM, TN, b, kPreBlocks>(g, res, tm * BM + wm * TMW, tn * BN + wn * TNW, lane);
+        });
       }
       compute_bf16(step % NS);
     }
@@ -678,8 +689,14 @@ void gemm_dense_kernel(GemmArgs g) {
       for (int kt = KT16; kt < KT; ++kt, ++step) {
         begin_step(step);
         // low-precision-only products (no bf16 steps) fetch the residual here
-        if constexpr (EM == E_ADD_F32 && kPrefetchRes) {
-          if (KT16 == 0 && kt == KT - 1) load_residual<TM, TN>(g, res, tm * BM + wm * TMW, tn * BN + wn * TNW, lane);
+        if constexpr (EM == E_ADD_F32) {
+          // (all blocks in the last step here: spreading them spills)
+          if (KT16 == 0 && kt == KT - 1) {
+            static_for<kPreBlocks>([&](auto b_c) {
+              load_residual_block<TM, TN, decltype(b_c)::value, kPreBlocks>(g, res, tm * BM + wm * TMW,
+                                                                             tn * BN + wn * TNW, lane);
+            });
+          }
         }
         if constexpr (LOW == 8) compute_fp8(step % NS);
         else compute_fp4(step % NS);
@@ -690,8 +707,8 @@ void gemm_dense_kernel(GemmArgs g) {
     // uses its own slice of it to stage the output
     __syncthreads();
     float* scratch = reinterpret_cast<float*>(lds[(step - 1) % NS]) + wave * kScratchFloats;
-    epilogue_lds<EM, TM, TN, kEpiRows>(g, acc, tm * BM + wm * TMW, tn * BN + wn * TNW, lane, scratch,
-                                       EM == E_ADD_F32 && kPrefetchRes ? &res : nullptr);
+    epilogue_lds<EM, TM, TN, kEpiRows, kPreBlocks>(g, acc, tm * BM + wm * TMW, tn * BN + wn * TNW, lane, scratch,
+                                                   res);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
