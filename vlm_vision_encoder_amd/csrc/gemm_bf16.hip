@@ -104,6 +104,12 @@ __device__ __forceinline__ const char* b_row(const GemmArgs& g, int n) {
 // scratch: LDS private to the wave, >= SR * 32 floats (fp32 outputs go
 // through it SR = 32 or 16 rows at a time), >= 32 * 32 floats for the q,k,v
 // epilogue and >= 32 * 20 floats for bf16 outputs.
+// Orders one wave's LDS staging writes and the read-back of other lanes'
+// values: a compiler barrier only.  A wave's LDS instructions execute in
+// issue order, so a read issued after a write sees it without a counter
+// wait; the compiler waits for a read's data where the data is used.
+__device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
+
 __device__ __forceinline__ int stage_row(int r) { return r ^ ((r >> 2) & 1); }
 
 // Read-back layout of the fp32 epilogue: pass h, iteration it of block
@@ -144,7 +150,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[
 #pragma unroll
           for (int v = 0; v < VP; ++v)
             scratch[stage_row(8 * (v >> 2) + 4 * lhalf + (v & 3)) * 32 + lrow] = acc[i][j][h * VP + v];
-          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+          wave_lds_order();
 #pragma unroll
           for (int it = 0; it < SR / 8; ++it) {
             const int r = (lane >> 3) + 8 * it, c4 = 4 * (lane & 7);
@@ -162,7 +168,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[
               }
             }
           }
-          __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next pass's writes
+          wave_lds_order();
         }
   } else if constexpr (EM == E_QKV_ROPE) {
     const float4* rope = reinterpret_cast<const float4*>(g.maps.rope);
@@ -179,7 +185,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[
 #pragma unroll
         for (int v = 0; v < 16; ++v)
           scratch[stage_row(8 * (v >> 2) + 4 * lhalf + (v & 3)) * 32 + lrow] = acc[i][jb][v];
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        wave_lds_order();
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
           const int r = (lane >> 2) + 16 * it, c8 = 8 * (lane & 3);
@@ -217,7 +223,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[
           if (row < g.M)
             *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.C) + size_t(row) * g.ldc + col0) = pack8(x);
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next block's writes
+        wave_lds_order();
       }
     }
   } else {
@@ -246,7 +252,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[
           }
           sh[rib * LDH + lrow] = __builtin_bit_cast(uint16_t, (bf16)x);
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        wave_lds_order();
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
           const int r = (lane >> 2) + 16 * it, c8 = 8 * (lane & 3);
@@ -255,7 +261,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[
           if (row < g.M)
             *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.C) + size_t(row) * g.ldc + ocol0 + c8) = val;
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);
+        wave_lds_order();
       }
     }
   }
