@@ -544,11 +544,13 @@ void gemm_dense_kernel(GemmArgs g) {
     if (is_step < steps) issue_next();
 
   // step has landed once at most (steps issued after it) x (loads per step)
-  // of this thread are outstanding; the barrier makes every thread's part
-  // visible and frees the stage read in the previous step
+  // of this thread are outstanding (low-precision products run two stages,
+  // so their extra scale loads never enter the count); the barrier makes
+  // every thread's part visible and frees the stage read in the previous step
+  static_assert(!LO8 || NS == 2, "low-precision steps use two stages");
   auto begin_step = [&](int step) {
     if (step + NS - 2 < steps) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * (LO8 ? LDT + 1 : LDT)));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LDT));
     } else {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
