@@ -62,7 +62,7 @@ typedef struct pv_config {
   int32_t patch;      /* patch edge in pixels (14 for Mistral 3, 16 for Pixtral-12B) */
   int32_t hidden;     /* D, a multiple of 256 (1024) */
   int32_t heads;      /* attention heads (16) */
-  int32_t mlp;        /* F, MLP width, a multiple of 256 (4096) */
+  int32_t mlp;        /* F, MLP width, a multiple of 256, at most 2^20 (4096) */
   int32_t layers;     /* number of blocks L >= 0 (24) */
   int32_t merge;      /* 2 = 2x2 patch merge + projection, 1 = no merge */
   int32_t out_dim;    /* projection width when merge == 2 (5120), a multiple of 128 */
@@ -131,7 +131,8 @@ typedef struct pv_plan_info {
  * pointers inside w are borrowed.  Builds the rotary cos/sin table on the host
  * in double precision.  Allocates no device memory.
  * Errors: PV_ERR_ARG (null, bad field), PV_ERR_UNSUPPORTED (head_dim != 64,
- * hidden or mlp not a multiple of 256, out_dim not a multiple of 128). */
+ * hidden or mlp not a multiple of 256, mlp above 2^20, out_dim not a
+ * multiple of 128). */
 pv_status pv_tower_create(const pv_config* cfg, const pv_weights* w, pv_tower** out);
 
 /* Frees the tower's host resources.  Waits for the tower's own pending

@@ -57,6 +57,7 @@ def create(cfg, layers_present=True):
     (dict(heads=8), -5),            # head_dim 128
     (dict(hidden=1000, heads=10), -5),
     (dict(mlp=1000), -5),
+    (dict(mlp=(1 << 20) + 256), -5),
     (dict(out_dim=5000), -5),
     (dict(merge=3), -1),
     (dict(patch=0), -1),

@@ -571,7 +571,9 @@ pv_status pv_tower_create(const pv_config* cfg, const pv_weights* w, pv_tower** 
   const int nc = c.hidden / 256;
   if (c.hidden % 256 || !(nc == 1 || nc == 2 || nc == 3 || nc == 4 || nc == 6 || nc == 8))
     return fail(PV_ERR_UNSUPPORTED, "hidden must be 256, 512, 768, 1024, 1536 or 2048");
-  if (c.mlp % 256) return fail(PV_ERR_UNSUPPORTED, "mlp must be a multiple of 256");
+  // (the GEMMs address a tile's rows of A by a 32-bit byte offset: at most
+  // 384 rows of 2 * mlp bytes)
+  if (c.mlp % 256 || c.mlp > (1 << 20)) return fail(PV_ERR_UNSUPPORTED, "mlp must be a multiple of 256, at most 2^20");
   if (c.merge == 2 && (c.out_dim <= 0 || c.out_dim % 128)) return fail(PV_ERR_UNSUPPORTED, "out_dim must be a positive multiple of 128");
   if (!w->patch_w || !w->ln_pre) return fail(PV_ERR_ARG, "patch_w and ln_pre must not be null");
   if (c.merge == 2 && !w->merge_w) return fail(PV_ERR_ARG, "merge_w must not be null when merge == 2");
