@@ -73,8 +73,11 @@ template <int QB, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4))) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NT = WAVES * 64;
   constexpr int SLOTS = 512;                 // 16-byte chunks per 64 x 64 bf16 tile
-  constexpr int LPT = SLOTS / NT;            // global_load_lds per thread per tile (K and V each)
-  static_assert(LPT >= 1 && SLOTS % NT == 0, "WAVES must divide 8");
+  // global_load_lds per thread per tile (K and V each); with more than 8
+  // waves only the first 8 load
+  constexpr int LPT = SLOTS / NT > 0 ? SLOTS / NT : 1;
+  constexpr int LOAD_WAVES = SLOTS / (64 * LPT);
+  static_assert(SLOTS % (64 * LPT) == 0 && (NT <= SLOTS ? SLOTS % NT == 0 : true), "load plan");
 
   __shared__ u32x4 kl[2][SLOTS];
   __shared__ u32x4 vl[2][SLOTS];
@@ -120,6 +123,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
   const std::integral_constant<int, 1> S1;
   auto issue_loads = [&](int kt, auto st_c) {
     constexpr int st = decltype(st_c)::value;
+    if (WAVES > LOAD_WAVES && wave >= LOAD_WAVES) return;
     const bool partial = kt * 64 + 64 > n;  // rows past the image are clamped to its last row
     const char* tile0 = reinterpret_cast<const char*>(qkv + size_t(base + kt * 64) * ld);
 #pragma unroll
@@ -391,8 +395,15 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.n_items <= 0) return hipSuccess;
   static_assert(kAttnQTileBf16 == 32 * PV_ATTN_QB * PV_ATTN_WAVES, "q tile must match the kernel shape");
-  hipLaunchKernelGGL((attn_bf16_kernel<PV_ATTN_QB, PV_ATTN_WAVES>), dim3(a.n_items * a.heads),
-                     dim3(PV_ATTN_WAVES * 64), 0, s, a);
+  if (a.q_tile == kAttnQTileBf16) {
+    hipLaunchKernelGGL((attn_bf16_kernel<PV_ATTN_QB, PV_ATTN_WAVES>), dim3(a.n_items * a.heads),
+                       dim3(PV_ATTN_WAVES * 64), 0, s, a);
+  } else if (a.q_tile == kAttnQTileBf16Wide) {
+    hipLaunchKernelGGL((attn_bf16_kernel<PV_ATTN_QB, kAttnWavesWide>), dim3(a.n_items * a.heads),
+                       dim3(kAttnWavesWide * 64), 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -25,7 +25,6 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kNumCUs = 256;  // MI355X: 8 XCDs x 32 CUs
 // tile rows per group of the persistent dense GEMM's tile order
 #ifndef PV_GEMM_GM
 #define PV_GEMM_GM 4

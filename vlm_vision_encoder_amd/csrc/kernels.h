@@ -52,6 +52,7 @@ struct AttnArgs {
   int32_t heads;
   int32_t hidden;
   int32_t online_max;  // 1: always use the running-max softmax (bf16 path)
+  int32_t q_tile;      // queries per work item (bf16: kAttnQTileBf16 or kAttnQTileBf16Wide)
 };
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t attention_f32(const AttnArgs& a, hipStream_t s);
@@ -64,6 +65,10 @@ hipError_t attention_f32(const AttnArgs& a, hipStream_t s);
 #define PV_ATTN_WAVES 8
 #endif
 constexpr int kAttnQTileBf16 = 32 * PV_ATTN_QB * PV_ATTN_WAVES;
+constexpr int kNumCUs = 256;  // MI355X: 8 XCDs x 32 CUs
+// the wide work item: 12 waves, one workgroup per CU
+constexpr int kAttnWavesWide = 12;
+constexpr int kAttnQTileBf16Wide = 32 * PV_ATTN_QB * kAttnWavesWide;
 constexpr int kAttnQTileF32 = 64;
 
 // Per-row maps from per-image metadata (maps.hip):

@@ -56,6 +56,13 @@ struct PlanParams {
   int32_t out_dim = 5120;
   int32_t elem_bytes = 2;   // 2 = bf16 activations, 4 = fp32
   int32_t q_tile = 256;     // queries per attention work item
+  // bf16 attention: a wider item (q_tile_wide queries, one workgroup per
+  // CU) is chosen per call when it fills the rounds of the chip better at no
+  // more padding (0: never); heads and slots size the rounds
+  int32_t q_tile_wide = 0;
+  int32_t heads = 16;
+  int32_t slots = 512;       // workgroups of q_tile queries the chip holds at once
+  int32_t slots_wide = 256;  // the same for q_tile_wide
   int32_t rope_pairs = 16;  // rotation pairs per axis (head_dim / 4)
   bool fp8 = false;         // bf16 tower whose per-block linear maps run in fp8
 };
@@ -91,6 +98,7 @@ struct Plan {
   std::vector<ImageMeta> meta;
   std::vector<int32_t> cu;  // n_images + 1
   std::vector<AttnItem> items;
+  int32_t q_tile = 0;  // queries per attention work item chosen for this call
   std::vector<SrcImage> src;  // uint8 input only (else empty; the region is zeroed)
   Layout ws;
 };

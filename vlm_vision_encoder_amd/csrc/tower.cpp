@@ -104,6 +104,10 @@ pv::PlanParams plan_params(const pv_tower* t) {
   p.out_dim = t->cfg.out_dim;
   p.elem_bytes = t->cfg.dtype == PV_BF16 ? 2 : 4;
   p.q_tile = t->cfg.dtype == PV_BF16 ? pv::kAttnQTileBf16 : pv::kAttnQTileF32;
+  p.q_tile_wide = t->cfg.dtype == PV_BF16 ? pv::kAttnQTileBf16Wide : 0;
+  p.heads = t->cfg.heads;
+  p.slots = 2 * pv::kNumCUs;  // two 8-wave items per CU (registers: 4 waves per SIMD)
+  p.slots_wide = pv::kNumCUs;
   p.rope_pairs = 16;
   p.fp8 = (t->cfg.flags & PV_FLAG_FP8) != 0;
   return p;
@@ -272,6 +276,7 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
   at.heads = c.heads;
   at.hidden = D;
   at.online_max = (c.flags & PV_FLAG_ATTN_ONLINE_MAX) ? 1 : 0;
+  at.q_tile = plan.q_tile;
 
   for (int l = 0; l < c.layers; ++l) {
     const pv_layer_weights& lw = t->layers[l];
