@@ -125,6 +125,10 @@ typedef struct pv_plan_info {
   int64_t workspace_bytes; /* device workspace that forward() needs */
   int32_t n_images;
   int32_t max_patches;     /* longest image, in patches */
+  int32_t attn_q_tile;     /* queries per attention work item chosen for the
+                            * call: bf16 256 (8 waves) or 384 (12 waves, when
+                            * those items fill the chip's rounds of
+                            * workgroups better at no more padding); f32 64 */
 } pv_plan_info;
 
 /* Creates a tower.  cfg and w are read (w->layers is copied); the device

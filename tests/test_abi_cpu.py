@@ -119,6 +119,35 @@ def _plan(lib, h, hw):
     return st, info
 
 
+def test_plan_attention_item_size(tower_handle):
+    """bf16: 384-query items (12 waves) only where they fill the chip's
+    rounds of workgroups at least 0.1 better by count (512 slots of
+    256-query items, 256 of 384-query items) at no more query padding."""
+    lib, h, cfg = tower_handle
+
+    def q_tile(hw):
+        st, info = _plan(lib, h, hw)
+        assert st == 0
+        return info.attn_q_tile
+
+    # 1540^2: 768 items fill 0.75 of two rounds of 512; 512 fill two of 256
+    assert q_tile([(1540, 1540)]) == 384
+    # 8,448 patches: 528 items (0.52 of two rounds) against 352 (0.69), same padding
+    assert q_tile([(1344, 1232)]) == 384
+    # two 1540^2 images: both fill their rounds completely
+    assert q_tile([(1540, 1540)] * 2) == 256
+    # few items: neither fills a round
+    assert q_tile([(224, 224)]) == 256
+    # 1,944 patches: fill 0.375 against 0.25, but 2,304 padded queries against 2,048
+    assert q_tile([(252, 1512)]) == 256
+    st, hf, _ = create(T.make_config(layers=1, max_side=1540, dtype="f32"))
+    assert st == 0
+    arr, n = T._hw_array([(1540, 1540)])
+    info = T.PvPlanInfo()
+    assert lib.pv_tower_plan(hf, arr, n, C.byref(info)) == 0 and info.attn_q_tile == 64
+    lib.pv_tower_destroy(hf)
+
+
 def test_plan_counts_and_shape_errors(tower_handle):
     lib, h, cfg = tower_handle
     st, info = _plan(lib, h, [(1540, 1540)])

@@ -317,6 +317,28 @@ def test_bf16_online_max_softmax_path():
         check(f"attn[0] image {i}", att[cu[i]:cu[i + 1]], want[cu[i]:cu[i + 1]], TOL["bf16"], stored_bf16=True)
 
 
+def test_bf16_wide_attention_items():
+    """One 1344x1232 image (8,448 patches) at 16 heads: the planner takes the
+    12-wave work items of 384 queries (352 items fill two rounds of 256
+    workgroups better than 528 items of 256 queries fill two rounds of 512, at
+    the same padding).  Attention of layer 0 against the oracle, with the
+    fixed offset and with the running max forced (the fallback pass)."""
+    import torch
+    wl = _bf16_small([(1344, 1232)], 1, mlp=1024)
+    say(f"bf16 12-wave attention items: {wl.n_patches} patches")
+    c = Case(wl)
+    assert c.tower.plan(wl.image_hw).attn_q_tile == 384
+    ref = c.ref()
+    want = oracle_stage(ref, wl, "attn", 0, c.w)
+    check("attn[0]", to_np(c.stage("attn", 0)), want, TOL["bf16"], stored_bf16=True)
+    tw = T.Tower(T.config_for(wl, flags=T.PV_FLAG_ATTN_ONLINE_MAX), c.dev_w)
+    att = to_np(tw.forward_stage(c.pix, wl.image_hw, "attn", 0))
+    torch.cuda.synchronize()
+    check("attn[0] online max", att, want, TOL["bf16"], stored_bf16=True)
+    check("out", to_np(c.run()), ref["out"], TOL["bf16"], stored_bf16=True)
+    tw.close()
+
+
 def test_bf16_fixed_offset_overflow_falls_back():
     """First key tile of the image all zero (zero pixels -> zero keys, offset
     m0 = 0) and large q/k weights: later scores exceed m0 by far more than

@@ -475,6 +475,7 @@ void fill_info(const pv_tower* t, const pv::Plan& plan, pv_plan_info* info) {
   info->workspace_bytes = int64_t(plan.ws.total);
   info->n_images = plan.n_images;
   info->max_patches = plan.max_patches;
+  info->attn_q_tile = plan.q_tile;
 }
 
 pv_status check_call(const pv_tower* t, const float* pixels, const int32_t* image_hw, int32_t n, const void* dst,

@@ -50,7 +50,8 @@ class PvWeights(C.Structure):
 
 class PvPlanInfo(C.Structure):
     _fields_ = [("n_patches", C.c_int64), ("out_rows", C.c_int64), ("out_cols", C.c_int64),
-                ("workspace_bytes", C.c_int64), ("n_images", C.c_int32), ("max_patches", C.c_int32)]
+                ("workspace_bytes", C.c_int64), ("n_images", C.c_int32), ("max_patches", C.c_int32),
+                ("attn_q_tile", C.c_int32)]
 
 
 class PvError(RuntimeError):
