@@ -140,6 +140,14 @@ def test_plan_attention_item_size(tower_handle):
     assert q_tile([(224, 224)]) == 256
     # 1,944 patches: fill 0.375 against 0.25, but 2,304 padded queries against 2,048
     assert q_tile([(252, 1512)]) == 256
+    # a subset of the images may choose the other size; the workspace of the
+    # subset never exceeds that of the whole set (the embeddings cache
+    # forwards the missed subset inside the whole set's workspace)
+    st, whole = _plan(lib, h, [(28, 28), (1372, 1148)])
+    st2, part = _plan(lib, h, [(1372, 1148)])
+    assert st == 0 and st2 == 0
+    assert (whole.attn_q_tile, part.attn_q_tile) == (384, 256)
+    assert part.workspace_bytes <= whole.workspace_bytes
     st, hf, _ = create(T.make_config(layers=1, max_side=1540, dtype="f32"))
     assert st == 0
     arr, n = T._hw_array([(1540, 1540)])

@@ -107,8 +107,17 @@ int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, P
   size_t off = 0;
   L.meta = off;
   off = align256(off + sizeof(ImageMeta) * n_images);
+  // (sized for the larger of the two item counts, so that the workspace of
+  // a subset of the images never exceeds that of the whole set)
+  size_t items_cap = pl.items.size();
+  for (int32_t q : {p.q_tile, p.q_tile_wide}) {
+    if (q <= 0) continue;
+    size_t k = 0;
+    for (int32_t i = 0; i < n_images; ++i) k += size_t((pl.cu[i + 1] - pl.cu[i] + q - 1) / q);
+    items_cap = std::max(items_cap, k);
+  }
   L.items = off;
-  off = align256(off + sizeof(AttnItem) * pl.items.size());
+  off = align256(off + sizeof(AttnItem) * items_cap);
   L.rope = off;
   off = align256(off + sizeof(float) * 2 * 2 * size_t(pl.rope_maxpos) * p.rope_pairs);
   L.src = off;
