@@ -740,3 +740,144 @@ def test_fp8_tower_reduces_to_exact_tower_on_e4m3_values():
     b = O.tower_forward(px, hw, w2, cfg, fp8=True)["out"]
     rel = np.max(np.abs(a - b)) / np.sqrt(np.mean(a * a))
     assert 1e-4 < rel < 0.5
+
+
+# ---- the fp8 variant's quantisation points, step by step, against an
+# independent quantiser: the nearest of the 254 finite OCP E4M3FN code values
+# (decoded from the bit layout: sign, 4 exponent bits with bias 7, 3 mantissa
+# bits, subnormals at exponent 0, S.1111.111 = NaN), ties to the even code,
+# with the block exponent X found by search (the unique X with
+# 128 <= max|block| * 2^-X < 256).
+def _e4m3_code_values():
+    vals, even = [], []
+    for b in range(256):
+        s, e, m = b >> 7, (b >> 3) & 15, b & 7
+        if e == 15 and m == 7:
+            continue                                   # NaN codes
+        mag = m * 2.0 ** -9 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        vals.append(-mag if s else mag)
+        even.append(m % 2 == 0)
+    return np.array(vals), np.array(even)
+
+
+_E4M3_VALS, _E4M3_EVEN = _e4m3_code_values()
+
+
+def _brute_e4m3_block(blk):
+    amax = float(np.max(np.abs(blk)))
+    if amax == 0.0:
+        return np.zeros_like(blk)
+    X = next(x for x in range(-150, 151) if 128.0 <= amax * 2.0 ** -x < 256.0)
+    X = min(max(X, -120), 120)
+    out = np.empty_like(blk)
+    for i, v in enumerate(blk * 2.0 ** -X):
+        d = np.abs(_E4M3_VALS - v)
+        cand = np.flatnonzero(d == d.min())
+        pick = [c for c in cand if _E4M3_EVEN[c]] or list(cand)
+        out[i] = _E4M3_VALS[pick[0]] * 2.0 ** X
+    return out
+
+
+def _brute_mx(x, axis=-1):
+    """Block-scaled e4m3 copy of x, blocks of 32 along `axis`."""
+    x = np.moveaxis(np.asarray(x, np.float64), axis, -1)
+    out = np.empty_like(x)
+    flat, fo = x.reshape(-1, x.shape[-1]), out.reshape(-1, x.shape[-1])
+    for r in range(flat.shape[0]):
+        for b in range(0, flat.shape[1], 32):
+            fo[r, b:b + 32] = _brute_e4m3_block(flat[r, b:b + 32])
+    return np.moveaxis(out, -1, axis)
+
+
+def test_brute_e4m3_quantiser_agrees_with_library_cast():
+    """The brute-force quantiser itself, on values in one binade of scale:
+    with X = 0 forced (block max in [128, 256)) its values equal torch's
+    float8_e4m3fn cast (round to nearest even)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(33)
+    blk = rng.uniform(-255, 255, size=32)
+    blk[0] = 200.0
+    want = torch.from_numpy(blk).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(_brute_e4m3_block(blk), want)
+
+
+def _fp8_tower_by_steps(px, hw, w, cfg, mistake=None):
+    """The fp8 variant written out step by step: the four linear maps of
+    every block take both operands through the block quantiser along their
+    contraction axis -- (norm output, wq, wk, wv), (attention output, wo),
+    (ffn norm output, w_gate, w_up), (silu(gate) * up, w_down) -- and nothing
+    else is quantised.  Returns the residual after each attention and each
+    block, and the output.  `mistake` plants one error (to show the pin
+    fails)."""
+    def qa(a):                     # an activation [rows][K]
+        return _brute_mx(a, axis=1)
+
+    def qw(m):                     # a weight [out][K]
+        return _brute_mx(m, axis=0 if mistake == "weight_axis" else 1)
+
+    def norm(x, g):
+        return x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + cfg.rms_eps) * g
+
+    maps = O.plan_maps(hw, cfg.patch, cfg.merge)
+    h = norm(O.patch_embed(px, hw, w["patch_w"], cfg.patch), w["ln_pre"])
+    attn_out, block_out = [], []
+    for lw in w["layers"]:
+        y = norm(h, lw["attn_norm"])
+        y = y if mistake == "skip_norm_out" else qa(y)
+        q = O.rope_2d(y @ qw(lw["wq"]).T, maps["patch_rc"], cfg.heads, cfg.rope_theta)
+        k = O.rope_2d(y @ qw(lw["wk"]).T, maps["patch_rc"], cfg.heads, cfg.rope_theta)
+        v = y @ qw(lw["wv"]).T
+        a = O.attention(q, k, v, maps["cu_seqlens"], cfg.heads)
+        a = a if mistake == "skip_attn_out" else qa(a)
+        h = h + a @ qw(lw["wo"]).T
+        attn_out.append(h)
+        y2 = qa(norm(h, lw["ffn_norm"]))
+        g, u = y2 @ qw(lw["w_gate"]).T, y2 @ qw(lw["w_up"]).T
+        hm = g / (1.0 + np.exp(-g)) * u
+        hm = hm if mistake == "skip_hidden" else qa(hm)
+        h = h + hm @ qw(lw["w_down"]).T
+        if mistake == "quantise_residual":
+            h = qa(h)
+        block_out.append(h)
+    out = O.merge_project(h, maps["merge_src"], w["merge_w"]) if cfg.merge == 2 else h
+    return attn_out, block_out, out
+
+
+def _col_err(got, want):
+    """max over columns of max|got - want| / RMS of that column of want."""
+    rms = np.sqrt(np.mean(want * want, axis=0))
+    return float(np.max(np.max(np.abs(got - want), axis=0) / rms))
+
+
+def test_fp8_tower_quantisation_points_step_by_step():
+    """tower_forward(fp8=True) equals the step-by-step fp8 tower with the
+    brute-force quantiser (two blocks, two images, merge 2): the residual
+    after every attention and every block, column by column, and the output.
+    Each planted placement mistake moves some column far beyond that
+    agreement.  The odd features are 2^-16 of the even ones (ln_pre gain and
+    the rows of wo and w_down that write them): a weight block taken along
+    the output axis then spans both magnitudes and flushes the small rows
+    into e4m3's subnormals, which the per-column comparison sees."""
+    rng = np.random.default_rng(34)
+    d, f = 64, 96
+    cfg = O.TowerConfig(patch=4, hidden=d, heads=2, mlp=f, layers=2, merge=2, out_dim=24)
+    hw = [(8, 8), (16, 8)]
+    w = _tiny_weights(rng, d, f, 4, 2, 24)
+    small = np.where(np.arange(d) % 2 == 1, 2.0 ** -16, 1.0)
+    w["ln_pre"] = w["ln_pre"] * small
+    for lw in w["layers"]:
+        lw["wo"] = lw["wo"] * small[:, None]
+        lw["w_down"] = lw["w_down"] * small[:, None]
+    px = rng.standard_normal(sum(3 * a * b for a, b in hw))
+    res = O.tower_forward(px, hw, w, cfg, collect=True, fp8=True)
+    got = res["attn_out"] + res["block_out"] + [res["out"]]
+    a_, b_, o_ = _fp8_tower_by_steps(px, hw, w, cfg)
+    want = a_ + b_ + [o_]
+    for g_, w_ in zip(got, want):
+        assert _col_err(g_, w_) <= 1e-12
+    exact = O.tower_forward(px, hw, w, cfg)["out"]
+    assert _col_err(exact, o_) > 1e-3                    # the quantisation is really there
+    for mistake in ("weight_axis", "skip_norm_out", "skip_attn_out", "skip_hidden", "quantise_residual"):
+        a_, b_, o_ = _fp8_tower_by_steps(px, hw, w, cfg, mistake)
+        worst = max(_col_err(g_, w_) for g_, w_ in zip(got, a_ + b_ + [o_]))
+        assert worst > 1e-3, mistake
