@@ -46,13 +46,27 @@ def flops_by_class(wl):
     return out
 
 
-def norm_bytes(wl):
-    """Algorithmic HBM bytes per element of the RMSNorm passes of one forward
-    (bf16 path): the dual first pass reads 4 and writes 4 + 2; an attention
-    norm reads 4 and writes 2; an MLP norm reads 4 and writes 2 (bf16) + 1/2
-    (fp4 low part) + 1/32 (scale bytes)."""
-    N, D, L = wl.n_patches, wl.hidden, wl.layers
-    return N * D * (10 + (L - 1) * 6 + L * (6.5 + 1 / 32)) if L > 0 else N * D * 8
+def memory_bound_bytes(wl):
+    """Algorithmic HBM bytes of one forward's memory-bound passes, by kernel
+    class (bf16 tower).
+      norm:     the first pass reads X (4 B) and writes h (4 B) and y (2 B);
+                each later attention norm reads h (4 B), writes y (2 B)
+      norm_mlp: each MLP norm reads h (4 B), writes y (2 B) + its fp4 low
+                part (1/2 B) + one scale byte per 32 values
+      operand:  im2col split: the pixels read once (3 p^2 fp32 per patch),
+                2 Kp bf16 written per patch; the final residual split: 4 B
+                read + 4 B written per value (merge), or the fp32 -> bf16
+                output copy: 4 + 2 B (no merge)."""
+    import math
+    N, D, L, p = wl.n_patches, wl.hidden, wl.layers, wl.patch
+    if wl.dtype != "bf16" or L == 0:
+        return {}
+    kp = math.ceil(3 * p * p / 64) * 64
+    return {
+        "norm": N * D * (10 + (L - 1) * 6),
+        "norm_mlp": N * D * L * (6 + 0.5 + 1 / 32),
+        "operand": N * (3 * p * p * 4 + 2 * kp * 2) + N * D * (8 if wl.merge == 2 else 6),
+    }
 
 
 def cpu_model():
@@ -66,49 +80,58 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(wl, weights, pixels):
-    """The float64 oracle on a bounded sample: patch embedding + ln_pre + ONE
-    block + the merge projection of the full workload; the forward time is
-    extrapolated as embed + L x block + merge."""
+def cpu_baseline(wl, weights, pixels, full=False, log=None):
+    """The float64 oracle on the GPU host's cores.  full=True: the whole
+    forward, every block (a progress line per block); else a bounded sample:
+    patch embedding + ln_pre + ONE block + the merge projection of the full
+    batch, the forward time extrapolated as embed + L x block + merge."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import pv_oracle as O
     from vlm_vision_encoder_amd import synth
 
+    n_blocks = wl.layers if full else min(1, wl.layers)
     ow = synth.oracle_weights({"patch_w": weights["patch_w"], "ln_pre": weights["ln_pre"],
-                               "layers": weights["layers"][:1], **({"merge_w": weights["merge_w"]}
-                                                                   if "merge_w" in weights else {})})
-    cfg = O.TowerConfig(patch=wl.patch, hidden=wl.hidden, heads=wl.heads, mlp=wl.mlp, layers=1, merge=wl.merge,
-                        out_dim=wl.out_dim, rope_theta=wl.rope_theta, rms_eps=wl.rms_eps)
+                               "layers": weights["layers"][:n_blocks], **({"merge_w": weights["merge_w"]}
+                                                                          if "merge_w" in weights else {})})
     px = pixels.astype(np.float64)
     t0 = time.perf_counter()
     x = O.patch_embed(px, wl.image_hw, ow["patch_w"], wl.patch)
     h = O.rms_norm(x, ow["ln_pre"], wl.rms_eps)
     t1 = time.perf_counter()
     maps = O.plan_maps(wl.image_hw, wl.patch, wl.merge)
-    lw = ow["layers"][0]
-    y = O.rms_norm(h, lw["attn_norm"], wl.rms_eps)
-    q = O.rope_2d(y @ lw["wq"].T, maps["patch_rc"], wl.heads, wl.rope_theta)
-    k = O.rope_2d(y @ lw["wk"].T, maps["patch_rc"], wl.heads, wl.rope_theta)
-    v = y @ lw["wv"].T
-    h = h + O.attention(q, k, v, maps["cu_seqlens"], wl.heads) @ lw["wo"].T
-    y = O.rms_norm(h, lw["ffn_norm"], wl.rms_eps)
-    h = h + O.swiglu_mlp(y, lw["w_gate"], lw["w_up"], lw["w_down"])
+    for i, lw in enumerate(ow["layers"]):
+        y = O.rms_norm(h, lw["attn_norm"], wl.rms_eps)
+        q = O.rope_2d(y @ lw["wq"].T, maps["patch_rc"], wl.heads, wl.rope_theta)
+        k = O.rope_2d(y @ lw["wk"].T, maps["patch_rc"], wl.heads, wl.rope_theta)
+        v = y @ lw["wv"].T
+        h = h + O.attention(q, k, v, maps["cu_seqlens"], wl.heads) @ lw["wo"].T
+        y = O.rms_norm(h, lw["ffn_norm"], wl.rms_eps)
+        h = h + O.swiglu_mlp(y, lw["w_gate"], lw["w_up"], lw["w_down"])
+        if log:
+            log(f"oracle {wl.name}: block {i + 1}/{len(ow['layers'])} done, {time.perf_counter() - t0:.1f} s")
     t2 = time.perf_counter()
     if wl.merge == 2:
         O.merge_project(h, maps["merge_src"], ow["merge_w"])
     t3 = time.perf_counter()
-    fwd_s = (t1 - t0) + wl.layers * (t2 - t1) + (t3 - t2)
+    if full:
+        fwd_s = t3 - t0
+        sample = (f"float64 numpy oracle: the whole forward of the {wl.name} batch ({wl.n_patches} patches, "
+                  f"{wl.layers} blocks), {fwd_s:.1f} s measured")
+    else:
+        fwd_s = (t1 - t0) + wl.layers * (t2 - t1) / max(1, n_blocks) + (t3 - t2)
+        sample = (f"float64 numpy oracle: patch embedding + ln_pre + 1 of {wl.layers} blocks + merge projection "
+                  f"of the full {wl.name} batch ({wl.n_patches} patches), timed {t3 - t0:.1f} s; forward time "
+                  f"extrapolated as embed + {wl.layers} x block + merge = {fwd_s:.1f} s")
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {
         "value": wl.n_patches / fwd_s,
         "unit": "patches/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"float64 numpy oracle: patch embedding + ln_pre + 1 of {wl.layers} blocks + merge projection "
-                   f"of the full {wl.name} batch ({wl.n_patches} patches), timed {t3 - t0:.1f} s; forward time "
-                   f"extrapolated as embed + {wl.layers} x block + merge = {fwd_s:.1f} s"),
+        "sample": sample,
+        "extrapolated": not full,
         "merged_tokens_per_s": wl.out_rows / fwd_s,
         "host_cpus": os.cpu_count(),
         "cpu_model": cpu_model(),
@@ -153,8 +176,12 @@ def pmc_summary(args):
     cw_kib, _ = per_dispatch(args.pmc_copy_write, "MulFunctor")
     f_scale, w_scale = copy_bytes / (cf_kib * 1024), copy_bytes / (cw_kib * 1024)
     fetch_b, write_b = f_kib * 1024 * f_scale, w_kib * 1024 * w_scale
-    out = {"kernel": needle, "workload": wname, "source": src,
-           "source_sha256": source_sha256(os.path.join(ROOT, "vlm_vision_encoder_amd", "csrc", src)),
+    if args.attn_q_tile is None:
+        raise SystemExit("--attn-q-tile (the work-item size of the measured run) is required")
+    out = {"kernel": needle, "workload": wname, "source": src, "sources_sha256": traffic_sources_sha256(),
+           "attn_q_tile": args.attn_q_tile,
+           "fetch_scale_note": "the copy probe's FETCH_SIZE per byte; assumes the kernel's request-size mix "
+                               "reads like the copy kernel's",
            "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
            "copy_probe_bytes": copy_bytes, "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib,
            "fetch_scale": f_scale, "write_scale": w_scale,
@@ -200,8 +227,9 @@ def time_u8_input(tw, wl, out, ws, stream, f32_patch_ms, reps=5):
     """The uint8 input path on a 4096x4096 photo (resized to the workload's
     1540x1540, or cut into the Pixtral workload's 16 tiles of 1024x1024):
     the whole forward from uint8 (HIP events around `reps`
-    calls), its patch-embedding kernel class (fused resize + normalise +
-    hi|lo im2col, weight padding, GEMM) beside the float path's, and the
+    calls), its patch-embedding and operand kernel classes (fused resize +
+    normalise + hi|lo im2col, GEMM, the final residual's split) beside the
+    float path's, and the
     standalone preprocessing into fp32 planes.  Algorithmic bytes of the
     standalone pass: the source image read once plus the planes written."""
     import torch
@@ -252,7 +280,8 @@ def time_u8_input(tw, wl, out, ws, stream, f32_patch_ms, reps=5):
     return {"source": "4096x4096 uint8 RGB", "target": list(tgt[0]),
             "tiles": len(wl.image_hw) if wl.tiles_from is not None else None, "forward_ms": round(fwd_ms, 4),
             "patches_per_s": round(info.n_patches / (fwd_ms * 1e-3), 1),
-            "patch_class_ms": round(prof["patch"][0], 5), "patch_class_ms_float_input": f32_patch_ms,
+            "patch_and_operand_ms": round(prof["patch"][0] + prof["operand"][0], 5),
+            "patch_and_operand_ms_float_input": round(f32_patch_ms, 5),
             "preprocess_planes_ms": round(pre_ms, 5),
             "preprocess_planes_gbs": round(nbytes / (pre_ms * 1e-3) / 1e9, 1),
             "preprocess_planes_hbm_frac": round(nbytes / (pre_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -347,66 +376,41 @@ def source_sha256(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(kernel_class, wl, launches_per_step):
+# sources whose change makes a stored traffic measurement stale: the kernel,
+# and the planner that chooses its work-item size
+TRAFFIC_SOURCES = ("attn_bf16.hip", "kernels.h", "plan.cpp")
+
+
+def traffic_sources_sha256():
+    return {f: source_sha256(os.path.join(ROOT, "vlm_vision_encoder_amd", "csrc", f)) for f in TRAFFIC_SOURCES}
+
+
+def measured_traffic(kernel_class, wl, attn_q_tile):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     counter summary (FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by what
     the same counter reads for a copy kernel of known size), or None when no
-    summary exists for this kernel and workload or the kernel's source has
-    changed since the counters were taken."""
+    summary exists for this kernel and workload, when the kernel, its launch
+    header or the planner has changed since the counters were taken, or when
+    this run's attention work-item size differs from the measured one."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel_class}_{wl.name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    src = os.path.join(ROOT, "vlm_vision_encoder_amd", "csrc", t["source"])
-    if source_sha256(src) != t["source_sha256"]:
+    if t.get("sources_sha256") != traffic_sources_sha256() or t.get("attn_q_tile") != attn_q_tile:
         return None
     return float(t["hbm_bytes_per_dispatch"])
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="ms31_1540")
-    ap.add_argument("--profile-steps", type=int, default=3)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
-                    help="only run a plain fp32 copy kernel (y = x * 1) over MIB MiB, 5 times, and exit: the "
-                         "reference for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
-    ap.add_argument("--pmc-summary", nargs=2, metavar=("CLASS", "WORKLOAD"),
-                    help="write profiles/traffic_CLASS_WORKLOAD.json from the four CSVs below and exit")
-    ap.add_argument("--pmc-fetch")
-    ap.add_argument("--pmc-write")
-    ap.add_argument("--pmc-copy-fetch")
-    ap.add_argument("--pmc-copy-write")
-    ap.add_argument("--copy-probe-mib", type=int, default=512)
-    args = ap.parse_args()
-    if args.pmc_summary:
-        pmc_summary(args)
-        return
-    if args.copy_probe:
-        copy_probe(args.copy_probe)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: the tower runs on a single MI355X here "
-              f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
+def run_workload(wl, dev_w, weights, pixels, args, log, headline):
+    """Times one workload: `args.steps` forwards after `args.warmup` (HIP
+    events on the launch stream), per-class kernel times over
+    `args.profile_steps` more, the dominant kernel's roofline, the memory-bound
+    passes' HBM fractions; the headline also times the extra legs."""
     import torch
 
-    from vlm_vision_encoder_amd import synth
     from vlm_vision_encoder_amd import tower as T
 
-    wl = synth.workload(args.workload)
-    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)  # noqa: E731
-    log(f"workload {wl.name}: {len(wl.image_hw)} images, {wl.n_patches} patches, {wl.out_rows} out rows, "
-        f"{wl.layers} layers, {wl.dtype}")
-    weights = synth.make_weights(wl)
-    pixels = synth.make_pixels(wl)
-    dev_w = T.weights_to_device(weights, wl.dtype)
     tw = T.Tower(T.config_for(wl), dev_w)
     pix = torch.from_numpy(pixels).cuda()
     info = tw.plan(wl.image_hw)
@@ -419,36 +423,37 @@ def main():
     def step():
         tw.forward_raw(pix.data_ptr(), wl.image_hw, out.data_ptr(), out.shape[0], ws.data_ptr(), ws.numel(), sptr)
 
+    steps = args.steps if headline else args.sub_steps
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log("warmup done")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     # an event after every step as well (per-step median and spread)
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     ev0.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step()
         marks[i].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
+    ms_step = ev0.elapsed_time(ev1) / steps
     per_step = sorted([ev0.elapsed_time(marks[0])] + [marks[i - 1].elapsed_time(marks[i])
-                                                      for i in range(1, args.steps)])
+                                                      for i in range(1, steps)])
     step_stats = {"median_ms": round(per_step[len(per_step) // 2], 4), "min_ms": round(per_step[0], 4),
                   "max_ms": round(per_step[-1], 4)}
-    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (wall {t_wall * 1e3 / args.steps:.3f} ms/step)")
+    log(f"{wl.name}: timed {steps} steps: {ms_step:.3f} ms/step (wall {t_wall * 1e3 / steps:.3f} ms/step)")
     assert torch.isfinite(out.float()).all().item(), "non-finite output"
 
     # per-kernel-class times, HIP events around each launch on the same stream
     fl = flops_by_class(wl)
+    mb = memory_bound_bytes(wl)
     total_flops = sum(fl.values())
-    peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
-    kernels, roofline = {}, None
+    bf = wl.dtype == "bf16"
+    peak = MFMA_BF16_PEAK_TFLOPS if bf else FP32_PEAK_TFLOPS
+    kernels, roofline, memory_bound = {}, None, {}
     if args.profile_steps > 0:
         tw.set_profiling(True)
         for _ in range(args.profile_steps):
@@ -465,64 +470,149 @@ def main():
                  "ms_per_step": round(ms / args.profile_steps, 4)}
             if fl.get(k):
                 d["tflops"] = round(fl[k] / (ms / args.profile_steps) / 1e9, 1)
-            if k == "norm":
-                d["gbs"] = round(norm_bytes(wl) / (ms / args.profile_steps) / 1e6, 1)
+            if mb.get(k):
+                d["gbs"] = round(mb[k] / (ms / args.profile_steps) / 1e6, 1)
                 d["hbm_frac"] = round(d["gbs"] / HBM_PEAK_GBS, 4)
+                memory_bound[k] = {"bytes_per_step": mb[k], "ms_per_step": d["ms_per_step"], "gbs": d["gbs"],
+                                   "hbm_frac": d["hbm_frac"]}
             kernels[k] = d
-            log(f"  {k:7s} {per_launch_ms:9.4f} ms x {launches_per_fwd:5.1f}/step  {d.get('tflops', '')} TFLOP/s "
-                f"{d.get('gbs', '')}")
+            rate = (f"{d['tflops']} TFLOP/s" if "tflops" in d else "") + (f"{d['gbs']} GB/s" if "gbs" in d else "")
+            log(f"  {k:8s} {per_launch_ms:9.4f} ms x {launches_per_fwd:5.1f}/step  {rate}")
         dom = max((k for k in fl if fl[k] > 0 and k in kernels), key=lambda k: kernels[k]["ms_per_step"])
         dom_ms = kernels[dom]["avg_ms"]
         dom_flops_launch = fl[dom] / kernels[dom]["launches_per_step"]
         achieved = dom_flops_launch / (dom_ms * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": peak,
+        roofline = {"bound": "mfma" if bf else "alu", "kernel": dom, "achieved": round(achieved, 1), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                    "traffic": measured_traffic(dom, wl, kernels[dom]["launches_per_step"]),
+                    "traffic": measured_traffic(dom, wl, info.attn_q_tile) if dom == "attn" else None,
                     "flops_per_launch": dom_flops_launch, "avg_launch_ms": dom_ms}
 
-    scatter = time_scatter(out, wl, stream) if wl.merge == 2 else None
-    u8_input = None
-    if (len(wl.image_hw) == 1 or wl.tiles_from is not None) and "patch" in kernels:
-        u8_input = time_u8_input(tw, wl, out, ws, stream, kernels["patch"]["ms_per_step"])
-    embcache = time_embcache(tw, wl, stream)
-    fp8_variant = time_fp8_variant(wl, dev_w, pix, stream)
-
-    patches_s = wl.n_patches / (ms_step * 1e-3)
-    tokens_s = wl.out_rows / (ms_step * 1e-3)
     res = {
+        "workload": wl.name, "ms_per_step": round(ms_step, 4), "step_ms": step_stats,
+        "patches_per_s": round(wl.n_patches / (ms_step * 1e-3), 1),
+        "merged_tokens_per_s": round(wl.out_rows / (ms_step * 1e-3), 1),
+        "forward_tflops": round(total_flops / (ms_step * 1e-3) / 1e12, 1),
+        "forward_mfma_frac": round(total_flops / (ms_step * 1e-3) / 1e12 / peak, 4),
+        "dtype": wl.dtype, "attn_q_tile": info.attn_q_tile,
+        "config": {"workload": wl.name, "images": [list(hw) for hw in wl.image_hw][:8],
+                   "n_images": len(wl.image_hw), "patch": wl.patch, "layers": wl.layers, "merge": wl.merge,
+                   "n_patches": wl.n_patches, "out_rows": wl.out_rows, "out_cols": wl.out_cols},
+        "roofline": roofline, "memory_bound": memory_bound, "kernels": kernels,
+    }
+    if headline:
+        res["scatter"] = time_scatter(out, wl, stream) if wl.merge == 2 else None
+        res["u8_input"] = None
+        if (len(wl.image_hw) == 1 or wl.tiles_from is not None) and "operand" in kernels:
+            res["u8_input"] = time_u8_input(tw, wl, out, ws, stream,
+                                            kernels["patch"]["ms_per_step"] + kernels["operand"]["ms_per_step"])
+        res["embcache"] = time_embcache(tw, wl, stream)
+        res["fp8_variant"] = time_fp8_variant(wl, dev_w, pix, stream)
+    tw.close()
+    del ws, out, pix
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ms31_1540", help="the headline workload")
+    ap.add_argument("--profile-steps", type=int, default=3)
+    ap.add_argument("--sub-steps", type=int, default=10, help="timed steps of each other workload")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="time only the headline workload (no per-workload records)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-quick", action="store_true",
+                    help="headline oracle timing from one block, extrapolated (default: the whole forward)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain fp32 copy kernel (y = x * 1) over MIB MiB, 5 times, and exit: the "
+                         "reference for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("CLASS", "WORKLOAD"),
+                    help="write profiles/traffic_CLASS_WORKLOAD.json from the four CSVs below and exit")
+    ap.add_argument("--pmc-fetch")
+    ap.add_argument("--pmc-write")
+    ap.add_argument("--pmc-copy-fetch")
+    ap.add_argument("--pmc-copy-write")
+    ap.add_argument("--copy-probe-mib", type=int, default=512)
+    ap.add_argument("--attn-q-tile", type=int, default=None,
+                    help="with --pmc-summary: the attention work-item size of the measured run")
+    args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the tower runs on a single MI355X here "
+              f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from vlm_vision_encoder_amd import synth
+    from vlm_vision_encoder_amd import tower as T
+
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)  # noqa: E731
+    names = [args.workload] + ([] if args.no_other_workloads else
+                               [n for n in synth.WORKLOADS if n != args.workload])
+    cache = {}  # weights shared by workloads of the same architecture (same seed, same draws)
+    results = {}
+    for name in names:
+        wl = synth.workload(name)
+        key = (wl.patch, wl.merge, wl.layers, wl.dtype)
+        log(f"workload {wl.name}: {len(wl.image_hw)} images, {wl.n_patches} patches, {wl.out_rows} out rows, "
+            f"{wl.layers} layers, {wl.dtype}")
+        if key not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            weights = synth.make_weights(wl)
+            cache[key] = (weights, T.weights_to_device(weights, wl.dtype))
+        weights, dev_w = cache[key]
+        pixels = synth.make_pixels(wl)
+        res = run_workload(wl, dev_w, weights, pixels, args, log, headline=(name == args.workload))
+        if not args.no_cpu_baseline:
+            full = name == args.workload and not args.cpu_quick
+            log(f"timing the CPU oracle on {name} ({'the whole forward' if full else 'one block'})")
+            res["cpu_baseline"] = cpu_baseline(wl, weights, pixels, full=full, log=log if full else None)
+        else:
+            res["cpu_baseline"] = None
+        results[name] = res
+        torch.cuda.empty_cache()
+
+    h = results[args.workload]
+    line = {
         "metric": "vision patches/s + merged tokens/s at 1540x1540; % bf16 MFMA peak",
-        "value": round(patches_s, 1),
+        "value": h["patches_per_s"],
         "unit": "patches/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "step_ms": step_stats,
+        "ms_per_step": h["ms_per_step"],
+        "step_ms": h["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": h["dtype"],
         "data": "synthetic",
-        "config": {"workload": wl.name, "images": [list(hw) for hw in wl.image_hw][:8],
-                   "n_images": len(wl.image_hw), "patch": wl.patch, "layers": wl.layers, "merge": wl.merge,
-                   "n_patches": wl.n_patches, "out_rows": wl.out_rows, "out_cols": wl.out_cols},
-        "merged_tokens_per_s": round(tokens_s, 1),
-        "forward_tflops": round(total_flops / (ms_step * 1e-3) / 1e12, 1),
-        "forward_mfma_frac": round(total_flops / (ms_step * 1e-3) / 1e12 / peak, 4),
-        "roofline": roofline,
-        "kernels": kernels,
-        "scatter": scatter,
-        "u8_input": u8_input,
-        "embcache": embcache,
-        "fp8_variant": fp8_variant,
+        "config": h["config"],
+        "merged_tokens_per_s": h["merged_tokens_per_s"],
+        "forward_tflops": h["forward_tflops"],
+        "forward_mfma_frac": h["forward_mfma_frac"],
+        "attn_q_tile": h["attn_q_tile"],
+        "roofline": h["roofline"],
+        "memory_bound": h["memory_bound"],
+        "kernels": h["kernels"],
+        "scatter": h.get("scatter"),
+        "u8_input": h.get("u8_input"),
+        "embcache": h.get("embcache"),
+        "fp8_variant": h.get("fp8_variant"),
+        "cpu_baseline": h["cpu_baseline"],
+        "workloads": {n: {k: v for k, v in r.items() if k not in ("config",)} | {"config": r["config"]}
+                      for n, r in results.items() if n != args.workload},
     }
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        res["cpu_baseline"] = cpu_baseline(wl, weights, pixels)
-    else:
-        res["cpu_baseline"] = None
-    tw.close()
-    print(json.dumps(res), flush=True)
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

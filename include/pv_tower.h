@@ -32,6 +32,13 @@
  *    the null stream) and the call returns without synchronising.  Device
  *    faults surface at the caller's next synchronisation.  One tower object
  *    must not be used by two streams (or threads) at once.
+ *  - A forward call uploads its per-call plan (image metadata, attention work
+ *    list, rotary table) from a ring of up to 8 pinned host staging buffers
+ *    owned by the tower.  A call whose upload equals the bytes a slot already
+ *    holds copies from that slot without rewriting it; otherwise it takes a
+ *    slot whose last copy has completed (or adds one).  The host therefore
+ *    never waits for the GPU, except when 8 distinct uploads are still in
+ *    flight: then it waits for the oldest copy (not for kernels).
  */
 #ifndef PV_TOWER_H
 #define PV_TOWER_H
@@ -85,7 +92,8 @@ typedef struct pv_config {
  * (q/k/v, out-projection, gate/up, down) run as fp8 e4m3 products with one
  * power-of-two (E8M0) scale per 32 k on both operands
  * (v_mfma_scale_f32_32x32x64_f8f6f4, fp32 accumulation): the weights are
- * quantised per layer into the workspace, the activations by the norm
+ * quantised once by pv_tower_prepare (else per layer into the workspace of
+ * every call), the activations by the norm
  * kernels and by quantisation passes over the attention output and
  * silu(gate) * up.  Scale X = floor(log2(block max)) - 7, values rounded to
  * nearest even.  The patch embedding, attention, the residual stream and the
@@ -142,6 +150,27 @@ pv_status pv_tower_create(const pv_config* cfg, const pv_weights* w, pv_tower** 
 /* Frees the tower's host resources.  Waits for the tower's own pending
  * host-to-device uploads first.  NULL is ignored. */
 void pv_tower_destroy(pv_tower* t);
+
+/* Derived weight copies, made once instead of in every forward call: the
+ * bf16 tower's patch weights zero-padded to the GEMM's K, and per block the
+ * fp4 (e2m1, 32-k scale blocks) copy of the gate/up weights that multiplies
+ * the MLP input's low part -- or, with PV_FLAG_FP8, the block-scaled e4m3
+ * copies of all seven block matrices.
+ * pv_tower_prepared_bytes: device bytes those copies need (0 for the fp32
+ *   tower, which uses its weights as given).  Host-only.
+ * pv_tower_prepare: writes the copies into mem (device, caller-owned,
+ *   256-byte aligned, at least pv_tower_prepared_bytes) on stream and makes
+ *   every later forward of this tower read them there (its workspace then
+ *   shrinks by the regions they used to take).  Allocates nothing.  mem is
+ *   borrowed: keep it allocated and unmodified while the tower is used, and
+ *   prepare again after changing the weights.  Work on another stream must be
+ *   ordered after this stream's copies by the caller.  mem == NULL detaches:
+ *   forward calls derive the copies per call again.  A failed preparation
+ *   leaves the tower detached.
+ * Errors: PV_ERR_ARG (null tower or bytes, misaligned mem), PV_ERR_CAPACITY
+ * (mem_bytes too small), PV_ERR_HIP. */
+pv_status pv_tower_prepared_bytes(const pv_tower* t, int64_t* bytes);
+pv_status pv_tower_prepare(pv_tower* t, void* mem, int64_t mem_bytes, void* stream);
 
 /* Host-only, pure: validates image_hw (host, [n_images][2] = (H, W) pixels)
  * and fills *info.  Errors: PV_ERR_ARG, PV_ERR_SHAPE. */
@@ -216,15 +245,21 @@ pv_status pv_tower_index_maps(pv_tower* t, const int32_t* image_hw, int32_t n_im
  * Errors: PV_ERR_ARG (null), PV_ERR_HIP. */
 enum {
   PV_K_MAPS = 0,     /* per-row index maps                                    */
-  PV_K_PATCH = 1,    /* patch embedding: weight padding, im2col, GEMM         */
-  PV_K_NORM = 2,     /* RMSNorm passes                                        */
-  PV_K_QKV = 3,      /* q,k,v GEMM with the rotary epilogue                   */
+  PV_K_PATCH = 1,    /* patch embedding GEMM (+ weight padding when unprepared) */
+  PV_K_NORM = 2,     /* RMSNorm passes before attention (ln_pre + first one fused) */
+  PV_K_QKV = 3,      /* q,k,v GEMM with the rotary epilogue (+ the fp8 variant's
+                        weight copies when unprepared)                        */
   PV_K_ATTN = 4,     /* block-diagonal attention                              */
   PV_K_OPROJ = 5,    /* out-projection GEMM (+ residual)                      */
-  PV_K_GATEUP = 6,   /* MLP gate/up: fp4 (fp8 variant: fp8) weight copy + GEMM (silu * up) */
+  PV_K_GATEUP = 6,   /* MLP gate/up GEMM (silu * up) (+ the fp4 weight copy
+                        when unprepared)                                      */
   PV_K_DOWN = 7,     /* MLP down GEMM (+ residual)                            */
-  PV_K_MERGE = 8,    /* residual copy + 2x2 merge GEMM, or output copy        */
-  PV_K_COUNT = 9
+  PV_K_MERGE = 8,    /* 2x2 merge GEMM                                        */
+  PV_K_NORM_MLP = 9, /* RMSNorm passes before the MLP (bf16 + fp4 low part)   */
+  PV_K_OPERAND = 10, /* operand passes: im2col hi | lo split (or the uint8
+                        resize into it), final residual hi | lo split or
+                        output copy                                           */
+  PV_K_COUNT = 11
 };
 pv_status pv_tower_set_profiling(pv_tower* t, int32_t enable);
 pv_status pv_tower_read_profile(pv_tower* t, double* ms, int64_t* launches, int32_t reset);

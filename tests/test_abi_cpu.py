@@ -473,3 +473,40 @@ def test_fp8_flag_validation_and_workspace():
     finally:
         lib.pv_tower_destroy(h8)
         lib.pv_tower_destroy(hb)
+
+
+def test_prepared_bytes_and_prepare_validation():
+    """pv_tower_prepared_bytes: the padded patch weights plus, per block, the
+    fp4 gate/up copy (bf16 tower) or the seven fp8 matrices (fp8 variant);
+    nothing for the fp32 tower.  pv_tower_prepare's argument checks return
+    before any device work."""
+    lib = T.load_library()
+    D, F, L, Kp = 1024, 4096, 24, 640   # patch 14: 3 * 14^2 = 588 -> 640
+
+    def rnd(x):
+        return (x + 255) // 256 * 256
+
+    def prepared(cfg):
+        st, h, _ = create(cfg)
+        assert st == 0
+        b = C.c_int64(-1)
+        assert lib.pv_tower_prepared_bytes(h, C.byref(b)) == 0
+        return h, b.value
+
+    h, b = prepared(T.make_config(layers=L))
+    per_layer = rnd(2 * F * D // 2) + rnd(D // 256 * 2 * F * 8)
+    assert b == rnd(D * Kp * 2) + L * per_layer
+    assert lib.pv_tower_prepare(None, FAKE * 256, b, None) == -1
+    assert lib.pv_tower_prepare(h, FAKE * 256 + 16, b, None) == -1    # misaligned
+    assert lib.pv_tower_prepare(h, FAKE * 256, b - 1, None) == -3     # too small
+    assert lib.pv_tower_prepare(h, None, 0, None) == 0                # detach: nothing to do
+    assert lib.pv_tower_prepared_bytes(h, None) == -1
+    lib.pv_tower_destroy(h)
+    h, b8 = prepared(T.make_config(layers=L, flags=T.PV_FLAG_FP8))
+    per8 = (rnd(3 * D * D) + rnd(D // 128 * 3 * D * 4) + rnd(D * D) + rnd(D // 128 * D * 4) + rnd(2 * F * D)
+            + rnd(D // 128 * 2 * F * 4) + rnd(D * F) + rnd(F // 128 * D * 4))
+    assert b8 == rnd(D * Kp * 2) + L * per8
+    lib.pv_tower_destroy(h)
+    h, bf = prepared(T.make_config(layers=L, dtype="f32"))
+    assert bf == 0
+    lib.pv_tower_destroy(h)

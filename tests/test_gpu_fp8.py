@@ -20,6 +20,7 @@ Inputs: the seeded synthetic ones of vlm_vision_encoder_amd.synth.
 import numpy as np
 import pytest
 
+from fp8_twin import fp8_chain, _rms
 from oracle import pv_oracle as O
 from vlm_vision_encoder_amd import synth
 from vlm_vision_encoder_amd import tower as T
@@ -107,6 +108,7 @@ def test_fp8_tower_matches_oracle_emulation(case):
     emu = O.tower_forward(px.astype(np.float64), wl.image_hw, ow, ocfg, fp8=True)["out"]
     exact = O.tower_forward(px.astype(np.float64), wl.image_hw, ow, ocfg)["out"]
     check_fp8_bars(out, emu, exact)
+    check_against_twin("output", out, emu, fp8_chain(px, wl, w, twin=True)["out"])
     tower.close()
 
 
@@ -138,3 +140,155 @@ def test_fp8_tower_fullsize_against_stored_emulation():
     emu, exact = ge["values"].astype(np.float64), gx["values"].astype(np.float64)
     check_fp8_bars(got, emu, exact)
     tower.close()
+
+
+# ------------------------------------------------------------------ stages
+# The fp8 tower's layer-0 stages against the oracle's fp8 emulation of the
+# same stage.  The q,k,v product takes the norm output quantised to e4m3;
+# the GPU computes it in fp32 from pixels that enter the patch product as
+# bf16 hi + lo pairs (about 16 significant bits), the emulation in float64,
+# so the two quantisers see inputs up to about 2^-17 of the row's scale
+# apart and may round a value that lies on an e4m3 rounding boundary (within
+# that distance) to different neighbours.  Such ties are found in the
+# emulation (a scaled value within TIE_REL * 256 of a midpoint between e4m3
+# values -- the block maximum scales to below 256 -- or a block maximum
+# within a relative TIE_REL of a power of two, which moves the block's
+# scale) and each adds
+# |weight| times the step between the two candidates to the allowance of the
+# outputs it feeds (both elements of a rotation pair).  The bar is then
+# max(|gpu - emu| - allowance) <= 2e-2 RMS, with the bf16 storage rounding
+# of q, k, v allowed as in every bf16 stage check.
+TIE_REL = 2.0 ** -15          # pixels enter the patch product as bf16 hi + lo (about 2^-17)
+BF16_ULP = 2.0 ** -8
+
+
+def _e4m3_mid_distance(s):
+    """For scaled values s (|s| < 256): distance to the nearest rounding
+    midpoint between two e4m3 values, and the step there (scaled units)."""
+    a = np.abs(s)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)
+    step = np.exp2(e - 3.0)
+    frac = a / step - np.floor(a / step)           # position within a step
+    return np.abs(frac - 0.5) * step, step
+
+
+def _tie_allowance(y, weights, heads, rotate_cols):
+    """Allowance per output element of y_q @ w^T for the quantised-operand
+    ties of y (rows x K) described above; w: list of [out][K] weights
+    concatenated along the output.  rotate_cols: number of leading output
+    columns that are rotated in adjacent pairs (q and k)."""
+    rows, K = y.shape
+    blocks = y.reshape(rows, K // 32, 32)
+    amax = np.abs(blocks).max(axis=2, keepdims=True)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    X = (ex - 1 - 7).astype(np.float64)
+    s = blocks * np.exp2(-X)
+    dist, step = _e4m3_mid_distance(s)
+    amb = (dist <= TIE_REL * 256.0)                 # the block maximum is below 256
+    # a block maximum near a power of two may take the next scale: every value
+    # of the block may then move by up to one step at that scale
+    m = amax * np.exp2(-X)
+    scale_amb = (np.abs(m - 128.0) <= TIE_REL * 128.0) | (np.abs(m - 256.0) <= TIE_REL * 256.0)
+    dy = np.where(amb, step, 0.0) * np.exp2(X)
+    dy = np.where(scale_amb, np.maximum(dy, 2.0 * step * np.exp2(X)), dy).reshape(rows, K)
+    W = np.concatenate([np.abs(np.asarray(w_, np.float64)) for w_ in weights], axis=0)
+    allow = dy @ W.T
+    if rotate_cols:
+        r = allow[:, :rotate_cols].reshape(rows, -1, 2)
+        allow[:, :rotate_cols] = np.repeat(r.sum(axis=2), 2, axis=1)
+    n_amb = int(amb.sum() + 32 * scale_amb.sum())
+    return allow, n_amb
+
+
+def _fp8_qkv_emulation(px, wl, w):
+    """Layer-0 q|k|v of the fp8 emulation, q in the bf16 tower's exp2 units,
+    and the quantised operand's tie allowance."""
+    ow = synth.oracle_weights(w)
+    lw = ow["layers"][0]
+    maps = O.plan_maps(wl.image_hw, wl.patch, wl.merge)
+    h0 = O.rms_norm(O.patch_embed(px.astype(np.float64), wl.image_hw, ow["patch_w"], wl.patch), ow["ln_pre"],
+                    wl.rms_eps)
+    y = O.rms_norm(h0, lw["attn_norm"], wl.rms_eps)
+    yq = O.mx_e4m3(y)
+    wq, wk, wv = (O.mx_e4m3(lw[k_]) for k_ in ("wq", "wk", "wv"))
+    q = O.rope_2d(yq @ wq.T, maps["patch_rc"], wl.heads, wl.rope_theta) * (np.log2(np.e) / 8.0)
+    k = O.rope_2d(yq @ wk.T, maps["patch_rc"], wl.heads, wl.rope_theta)
+    v = yq @ wv.T
+    allow, n_amb = _tie_allowance(y, [wq * (np.log2(np.e) / 8.0), wk, wv], wl.heads, 2 * wl.hidden)
+    return np.concatenate([q, k, v], axis=1), allow, n_amb
+
+
+@pytest.mark.parametrize("case", ["full-width", "ms31_1540"])
+def test_fp8_layer0_qkv_stage(case):
+    torch = _torch()
+    if case == "ms31_1540":
+        wl = synth.workload("ms31_1540").with_(layers=1)
+    else:
+        kw = {k_: v for k_, v in CASES["full-width"].items()}
+        wl = synth.Workload("fp8-full-width", dtype="bf16", **kw).with_(layers=1)
+    say(f"fp8 tower layer-0 q,k,v stage: {case}, {wl.n_patches} patches")
+    w = synth.make_weights(wl)
+    px = synth.make_pixels(wl)
+    tower = T.Tower(T.config_for(wl, flags=T.PV_FLAG_FP8), T.weights_to_device(w, "bf16"))
+    got = tower.forward_stage(torch.from_numpy(px).cuda(), wl.image_hw, "qkv", 0)
+    torch.cuda.synchronize()
+    got = got.float().cpu().numpy().astype(np.float64)
+    tower.close()
+    want, allow, n_amb = _fp8_qkv_emulation(px, wl, w)
+    rms = float(np.sqrt(np.mean(want * want)))
+    diff = np.abs(got - want) - BF16_ULP * np.abs(want)
+    plain = float(np.max(np.maximum(diff, 0)) / rms)
+    err = float(np.max(np.maximum(diff - allow, 0)) / rms)
+    say(f"  qkv: max-abs-err/RMS {plain:.3e} (storage allowance only), {err:.3e} with the tie allowance "
+        f"({n_amb} tied operand values; max allowance {allow.max() / rms:.2e} RMS); tol {TOL_FLOOR}")
+    assert err <= TOL_FLOOR
+
+
+# A correct fp8 tower sits at the twin's distance from the emulation (the GPU
+# also rounds the softmax probabilities to bf16 and accumulates in fp32, which
+# the twin leaves out): bars on the largest and on the RMS difference.
+TWIN_RATIO = 1.5
+
+
+def check_against_twin(name, got, emu, twin):
+    r = _rms(emu)
+    d_max, t_max = float(np.abs(got - emu).max()) / r, float(np.abs(twin - emu).max()) / r
+    d_rms, t_rms = _rms(got - emu) / r, _rms(twin - emu) / r
+    bar_max, bar_rms = max(TOL_FLOOR, TWIN_RATIO * t_max), TWIN_RATIO * t_rms + 1e-3
+    say(f"  {name}: gpu vs emulation max {d_max:.3e} (bar {bar_max:.3e}), rms {d_rms:.3e} (bar {bar_rms:.3e}); "
+        f"bf16 twin vs emulation max {t_max:.3e}, rms {t_rms:.3e}")
+    assert np.isfinite(got).all()
+    assert d_max <= bar_max, name
+    assert d_rms <= bar_rms, name
+
+
+def test_fp8_layer0_stages_full_width():
+    """Layer-0 attention output (plain bar), residual after attention (plain
+    bar), silu(gate) * up and the block output (twin bars) of the fp8 tower
+    (full widths, one 448x448 image) against the emulation of the same
+    stages."""
+    torch = _torch()
+    kw = {k_: v for k_, v in CASES["full-width"].items()}
+    wl = synth.Workload("fp8-full-width", dtype="bf16", **kw).with_(layers=1)
+    say(f"fp8 tower layer-0 stages, full width, {wl.n_patches} patches")
+    w = synth.make_weights(wl)
+    px = synth.make_pixels(wl)
+    tower = T.Tower(T.config_for(wl, flags=T.PV_FLAG_FP8), T.weights_to_device(w, "bf16"))
+    pix = torch.from_numpy(px).cuda()
+    g = {}
+    for st in ("attn", "attn_resid", "mlp_hidden", "block_out"):
+        g[st] = tower.forward_stage(pix, wl.image_hw, st, 0).float().cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    tower.close()
+    emu, twin = fp8_chain(px, wl, w), fp8_chain(px, wl, w, twin=True)
+    for st in ("attn", "attn_resid"):
+        want = emu[st][0]
+        diff = np.abs(g[st] - want)
+        if st == "attn":
+            diff = np.maximum(diff - BF16_ULP * np.abs(want), 0.0)
+        e = float(diff.max() / _rms(want))
+        say(f"  {st}: max-abs-err/RMS {e:.3e} (tol {TOL_FLOOR})")
+        assert e <= TOL_FLOOR, st
+    for st in ("mlp_hidden", "block_out"):
+        check_against_twin(st, g[st], emu[st][0], twin[st][0])

@@ -143,10 +143,13 @@ def test_device_index_maps_exact(name):
     say(f"device index maps {name}")
     dev_w = {"patch_w": None}
     import torch
-    # weights are not read by the map kernel; any aligned buffers do
+    # weights are not read by the map kernel; any aligned buffers do, as long
+    # as the tower makes no weight copies (prepare=False: preparing would read
+    # every matrix at its full size)
     z = torch.zeros(16, dtype=torch.float32, device="cuda")
     lw = {k: z for k in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")}
-    tw = T.Tower(T.config_for(wl), {"patch_w": z, "ln_pre": z, "layers": [lw] * wl.layers, "merge_w": z})
+    tw = T.Tower(T.config_for(wl), {"patch_w": z, "ln_pre": z, "layers": [lw] * wl.layers, "merge_w": z},
+                 prepare=False)
     cu, rc, ms = tw.index_maps(wl.image_hw, on_device=True)
     m = O.plan_maps(wl.image_hw, wl.patch, wl.merge)
     np.testing.assert_array_equal(cu, m["cu_seqlens"])

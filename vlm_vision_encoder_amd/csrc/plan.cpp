@@ -139,14 +139,17 @@ int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, P
   if (p.elem_bytes == 4) big_row = std::max(big_row, size_t(12) * p.patch * p.patch);
   off = align256(off + N * big_row);
   L.wpad = off;
-  off = align256(off + (p.elem_bytes == 2 ? D * size_t(patch_kp(p.patch)) * 2 : 0));
+  off = align256(off + (p.elem_bytes == 2 && !p.prepared ? D * size_t(patch_kp(p.patch)) * 2 : 0));
   if (p.elem_bytes == 2) {
-    const size_t F = size_t(p.mlp), F2 = 2 * F;
+    const size_t F = size_t(p.mlp);
     const size_t KA = p.fp8 ? std::max(D, F) : D;  // widest fp8 A operand
     L.a8 = off;
     off = align256(off + N * KA);
     L.as = off;
     off = align256(off + (KA / 128) * size_t(a8_scale_rows(int64_t(N))) * 4);
+  }
+  if (p.elem_bytes == 2 && !p.prepared) {
+    const size_t F = size_t(p.mlp), F2 = 2 * F;
     L.b8 = off;
     off = align256(off + F2 * D);
     L.bs = off;
@@ -168,6 +171,42 @@ int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, P
   }
   L.total = off;
   return 0;
+}
+
+PrepLayout prep_layout(int32_t patch, int32_t hidden, int32_t mlp, int32_t layers, bool fp8) {
+  PrepLayout P;
+  const size_t D = size_t(hidden), F = size_t(mlp), F2 = 2 * F;
+  size_t off = 0;
+  P.wpad = off;
+  off = align256(off + D * size_t(patch_kp(patch)) * 2);
+  P.layer0 = off;
+  size_t lo = 0;
+  if (fp8) {
+    P.wq8 = lo;
+    lo = align256(lo + 3 * D * D);
+    P.wqs = lo;
+    lo = align256(lo + (D / 128) * 3 * D * 4);
+    P.wo8 = lo;
+    lo = align256(lo + D * D);
+    P.wos = lo;
+    lo = align256(lo + (D / 128) * D * 4);
+    P.b8 = lo;
+    lo = align256(lo + F2 * D);
+    P.bs = lo;
+    lo = align256(lo + (D / 128) * F2 * 4);
+    P.wd8 = lo;
+    lo = align256(lo + D * F);
+    P.wds = lo;
+    lo = align256(lo + (F / 128) * D * 4);
+  } else {
+    P.b8 = lo;
+    lo = align256(lo + F2 * D / 2);
+    P.bs = lo;
+    lo = align256(lo + (D / 256) * F2 * 8);
+  }
+  P.layer_stride = lo;
+  P.total = off + size_t(layers > 0 ? layers : 0) * lo;
+  return P;
 }
 
 int resize_target(int32_t h, int32_t w, int32_t longest_edge, int32_t grid, int32_t* th, int32_t* tw,

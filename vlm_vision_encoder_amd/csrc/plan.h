@@ -65,7 +65,29 @@ struct PlanParams {
   int32_t slots_wide = 256;  // the same for q_tile_wide
   int32_t rope_pairs = 16;  // rotation pairs per axis (head_dim / 4)
   bool fp8 = false;         // bf16 tower whose per-block linear maps run in fp8
+  // the tower's derived weight copies (padded patch weights, fp4 / fp8 copies
+  // of the block matrices) live in caller memory written once: the workspace
+  // then holds no region for them
+  bool prepared = false;
 };
+
+// Byte offsets of a tower's derived weight copies in the memory that one
+// preparation fills (bf16 tower; every region 256-byte aligned):
+//   wpad  [D][Kp] bf16, the patch weights zero-padded to Kp
+//   per layer l, at layer0 + l * layer_stride:
+//     fp4 copies (bf16 tower): b4 [2F][D/2] gate/up in the GEMM's interleaved
+//       row order, bs4 [D/256][2F][8] scale bytes
+//     fp8 copies (fp8 variant): wq8 [3D][D] + wqs [D/128][3D][4], wo8 [D][D] +
+//       wos [D/128][D][4], b8 [2F][D] + bs8 [D/128][2F][4], wd8 [D][F] + wds
+//       [F/128][D][4]
+struct PrepLayout {
+  size_t wpad = 0;
+  size_t layer0 = 0, layer_stride = 0;
+  // offsets within a layer's region
+  size_t b8 = 0, bs = 0, wq8 = 0, wqs = 0, wo8 = 0, wos = 0, wd8 = 0, wds = 0;
+  size_t total = 0;
+};
+PrepLayout prep_layout(int32_t patch, int32_t hidden, int32_t mlp, int32_t layers, bool fp8);
 
 // Rows of the MLP input's fp8 scale blocks: the patches plus one tile of
 // padding (a GEMM tile reads the scale bytes of 256 consecutive rows).

@@ -78,10 +78,26 @@ struct pv_tower {
   std::vector<pv_layer_weights> layers;
   std::vector<float> rope;  // host rotary table
   int32_t rope_maxpos = 0;
-  void* pinned = nullptr;   // staging of the per-call upload
-  size_t pinned_bytes = 0;
-  hipEvent_t upload_done = nullptr;
-  bool upload_pending = false;
+  // Staging of the per-call upload: a ring of pinned host buffers, each with
+  // the event of its last copy and the bytes it holds.  A call whose upload
+  // equals a slot's bytes copies from that slot as it is (no host write, so no
+  // wait even while an earlier copy from it is in flight); otherwise it fills
+  // the least recently used slot whose copy has completed, adds a slot while
+  // fewer than kStagingSlots exist, and only then waits for the oldest copy.
+  struct Staging {
+    void* host = nullptr;
+    size_t cap = 0, used = 0;
+    hipEvent_t done = nullptr;
+    bool pending = false;
+    uint64_t last_use = 0;
+  };
+  static constexpr int kStagingSlots = 8;
+  std::vector<Staging> staging;
+  uint64_t uploads = 0;
+  std::vector<char> upload_buf;  // the next upload, assembled in plain host memory
+  // derived weight copies written by pv_tower_prepare (borrowed caller memory)
+  char* prep = nullptr;
+  pv::PrepLayout prep_layout;
   // profiling: (class, start, end) per recorded launch; events are pooled
   bool profiling = false;
   struct Rec {
@@ -110,6 +126,7 @@ pv::PlanParams plan_params(const pv_tower* t) {
   p.slots_wide = pv::kNumCUs;
   p.rope_pairs = 16;
   p.fp8 = (t->cfg.flags & PV_FLAG_FP8) != 0;
+  p.prepared = t->prep != nullptr;
   return p;
 }
 
@@ -146,35 +163,107 @@ hipError_t prof_end(pv_tower* t, hipStream_t s) {
   return hipEventRecord(t->recs.back().b, s);
 }
 
-// Host -> device upload of [meta | items | rope] and expansion of the row maps.
+// A staging slot for an upload of `bytes` bytes whose content is t->upload_buf.
+pv_status staging_slot(pv_tower* t, size_t bytes, pv_tower::Staging** out, bool* fill) {
+  auto done = [&](pv_tower::Staging& st) -> pv_status {
+    if (!st.pending) return PV_OK;
+    const hipError_t q = hipEventQuery(st.done);
+    if (q == hipSuccess) {
+      st.pending = false;
+    } else if (q != hipErrorNotReady) {
+      PV_HIP(q);
+    }
+    return PV_OK;
+  };
+  // 1. a slot that already holds these bytes: copy from it as it is
+  for (auto& st : t->staging)
+    if (st.used == bytes && std::memcmp(st.host, t->upload_buf.data(), bytes) == 0) {
+      *out = &st;
+      *fill = false;
+      return PV_OK;
+    }
+  // 2. the least recently used slot whose last copy has completed
+  pv_tower::Staging* best = nullptr;
+  for (auto& st : t->staging) {
+    pv_status e = done(st);
+    if (e != PV_OK) return e;
+    if (!st.pending && (!best || st.last_use < best->last_use)) best = &st;
+  }
+  // 3. a new slot; 4. else wait for the oldest copy
+  if (!best && int(t->staging.size()) < pv_tower::kStagingSlots) {
+    t->staging.emplace_back();
+    best = &t->staging.back();
+    PV_HIP(hipEventCreateWithFlags(&best->done, hipEventDisableTiming));
+  }
+  if (!best) {
+    for (auto& st : t->staging)
+      if (!best || st.last_use < best->last_use) best = &st;
+    PV_HIP(hipEventSynchronize(best->done));
+    best->pending = false;
+  }
+  if (best->cap < bytes) {
+    if (best->host) PV_HIP(hipHostFree(best->host));
+    best->host = nullptr;
+    best->cap = 0;
+    best->used = 0;
+    PV_HIP(hipHostMalloc(&best->host, bytes, hipHostMallocDefault));
+    best->cap = bytes;
+  }
+  *out = best;
+  *fill = true;
+  return PV_OK;
+}
+
+// Host -> device upload of [meta | items | rope | src] and expansion of the row maps.
 pv_status upload_and_maps(pv_tower* t, const pv::Plan& plan, char* ws, hipStream_t s) {
   const pv::Layout& L = plan.ws;
-  if (t->upload_pending) {
-    PV_HIP(hipEventSynchronize(t->upload_done));
-    t->upload_pending = false;
+  std::vector<char>& h = t->upload_buf;
+  h.assign(L.upload_bytes, 0);
+  std::memcpy(h.data() + L.meta, plan.meta.data(), sizeof(pv::ImageMeta) * plan.meta.size());
+  std::memcpy(h.data() + L.items, plan.items.data(), sizeof(pv::AttnItem) * plan.items.size());
+  std::memcpy(h.data() + L.rope, t->rope.data(), sizeof(float) * t->rope.size());
+  if (!plan.src.empty()) std::memcpy(h.data() + L.src, plan.src.data(), sizeof(pv::SrcImage) * plan.src.size());
+  pv_tower::Staging* st = nullptr;
+  bool fill = false;
+  pv_status e = staging_slot(t, L.upload_bytes, &st, &fill);
+  if (e != PV_OK) return e;
+  if (fill) {
+    std::memcpy(st->host, h.data(), L.upload_bytes);
+    st->used = L.upload_bytes;
   }
-  if (t->pinned_bytes < L.upload_bytes) {
-    if (t->pinned) PV_HIP(hipHostFree(t->pinned));
-    t->pinned = nullptr;
-    t->pinned_bytes = 0;
-    PV_HIP(hipHostMalloc(&t->pinned, L.upload_bytes, hipHostMallocDefault));
-    t->pinned_bytes = L.upload_bytes;
-  }
-  if (!t->upload_done) PV_HIP(hipEventCreateWithFlags(&t->upload_done, hipEventDisableTiming));
-  char* h = static_cast<char*>(t->pinned);
-  std::memset(h, 0, L.upload_bytes);
-  std::memcpy(h + L.meta, plan.meta.data(), sizeof(pv::ImageMeta) * plan.meta.size());
-  std::memcpy(h + L.items, plan.items.data(), sizeof(pv::AttnItem) * plan.items.size());
-  std::memcpy(h + L.rope, t->rope.data(), sizeof(float) * t->rope.size());
-  if (!plan.src.empty()) std::memcpy(h + L.src, plan.src.data(), sizeof(pv::SrcImage) * plan.src.size());
-  PV_HIP(hipMemcpyAsync(ws, h, L.upload_bytes, hipMemcpyHostToDevice, s));
-  PV_HIP(hipEventRecord(t->upload_done, s));
-  t->upload_pending = true;
+  PV_HIP(hipMemcpyAsync(ws, st->host, L.upload_bytes, hipMemcpyHostToDevice, s));
+  PV_HIP(hipEventRecord(st->done, s));
+  st->pending = true;
+  st->last_use = ++t->uploads;
   PV_LAUNCH(PV_K_MAPS, pv::build_maps(reinterpret_cast<const pv::ImageMeta*>(ws + L.meta), plan.n_images,
                                        int(plan.n_patches), int(plan.out_rows), t->cfg.merge,
                                        reinterpret_cast<int32_t*>(ws + L.rowinfo),
                                        reinterpret_cast<int32_t*>(ws + L.msrc), s));
   return PV_OK;
+}
+
+// Where a layer's derived weight copies are (fp4 gate/up of the bf16
+// tower; every fp8 copy of the fp8 variant).
+struct WeightCopies {
+  void *wq8, *wqs, *wo8, *wos, *b8, *bs, *wd8, *wds;
+};
+
+WeightCopies prepared_copies(const pv_tower* t, int l) {
+  const pv::PrepLayout& P = t->prep_layout;
+  char* b = t->prep + P.layer0 + size_t(l) * P.layer_stride;
+  return {b + P.wq8, b + P.wqs, b + P.wo8, b + P.wos, b + P.b8, b + P.bs, b + P.wd8, b + P.wds};
+}
+
+// The fp8 copies of one layer's matrices: q|k|v stacked, out-projection,
+// gate/up interleaved, down.
+hipError_t make_fp8_copies(const pv_layer_weights& lw, const WeightCopies& wc, int D, int F, hipStream_t s) {
+  hipError_t e = pv::quant_rows_fp8(lw.wq, D, D, wc.wq8, wc.wqs, 3 * D, 0, s);
+  if (e == hipSuccess) e = pv::quant_rows_fp8(lw.wk, D, D, wc.wq8, wc.wqs, 3 * D, D, s);
+  if (e == hipSuccess) e = pv::quant_rows_fp8(lw.wv, D, D, wc.wq8, wc.wqs, 3 * D, 2 * D, s);
+  if (e == hipSuccess) e = pv::quant_rows_fp8(lw.wo, D, D, wc.wo8, wc.wos, D, 0, s);
+  if (e == hipSuccess) e = pv::gateup_fp8(lw.w_gate, lw.w_up, wc.b8, wc.bs, F, D, s);
+  if (e == hipSuccess) e = pv::quant_rows_fp8(lw.w_down, D, F, wc.wd8, wc.wds, D, 0, s);
+  return e;
 }
 
 struct StageStop {
@@ -219,13 +308,13 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
   if (bf) {
     // pixels as bf16 hi | lo rows of im2col, against weights padded to Kp
     const int Kpatch = 3 * c.patch * c.patch, Kp = pv::patch_kp(c.patch);
-    void* wpad = ws + L.wpad;
-    PV_LAUNCH(PV_K_PATCH, pv::pad_rows(t->w.patch_w, wpad, D, Kpatch, Kp, s));
+    void* wpad = t->prep ? static_cast<void*>(t->prep + t->prep_layout.wpad) : static_cast<void*>(ws + L.wpad);
+    if (!t->prep) PV_LAUNCH(PV_K_PATCH, pv::pad_rows(t->w.patch_w, wpad, D, Kpatch, Kp, s));
     if (px.u8)
-      PV_LAUNCH(PV_K_PATCH, pv::im2col_u8_split(px.u8, reinterpret_cast<const pv::SrcImage*>(ws + L.src), g.maps,
+      PV_LAUNCH(PV_K_OPERAND, pv::im2col_u8_split(px.u8, reinterpret_cast<const pv::SrcImage*>(ws + L.src), g.maps,
                                                  px.aff, big, N, Kpatch, Kp, s));
     else
-      PV_LAUNCH(PV_K_PATCH, pv::im2col_split(px.f32, g.maps, big, N, Kpatch, Kp, s));
+      PV_LAUNCH(PV_K_OPERAND, pv::im2col_split(px.f32, g.maps, big, N, Kpatch, Kp, s));
     pv::GemmArgs a = g;
     a.M = N; a.N = D; a.K = 2 * Kp; a.kb = Kp;
     a.A = big; a.lda = 2 * Kp;
@@ -241,7 +330,7 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
         const pv::SrcImage& sm = plan.src[i];
         const size_t off = (size_t(m.pix_hi) << 32) | m.pix_lo;
         const size_t soff = (size_t(sm.off_hi) << 32) | sm.off_lo;
-        PV_LAUNCH(PV_K_PATCH, pv::resize_norm_u8(px.u8 + soff, sm, m.H, m.W, px.aff, planes + off, s));
+        PV_LAUNCH(PV_K_OPERAND, pv::resize_norm_u8(px.u8 + soff, sm, m.H, m.W, px.aff, planes + off, s));
       }
       pixels = planes;
     }
@@ -287,13 +376,12 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
       a.A = a8; a.A8 = a8; a.As = as; a.as_rows = srows; a.k8 = k;
       a.B8 = b8; a.Bs = bsc; a.bs_rows = brows; a.low_fmt = 8;
     };
-    if (f8) {  // this layer's weights in fp8
-      PV_LAUNCH(PV_K_QKV, pv::quant_rows_fp8(lw.wq, D, D, ws + L.wq8, ws + L.wqs, 3 * D, 0, s));
-      PV_LAUNCH(PV_K_QKV, pv::quant_rows_fp8(lw.wk, D, D, ws + L.wq8, ws + L.wqs, 3 * D, D, s));
-      PV_LAUNCH(PV_K_QKV, pv::quant_rows_fp8(lw.wv, D, D, ws + L.wq8, ws + L.wqs, 3 * D, 2 * D, s));
-      PV_LAUNCH(PV_K_OPROJ, pv::quant_rows_fp8(lw.wo, D, D, ws + L.wo8, ws + L.wos, D, 0, s));
-      PV_LAUNCH(PV_K_GATEUP, pv::gateup_fp8(lw.w_gate, lw.w_up, ws + L.b8, ws + L.bs, F, D, s));
-      PV_LAUNCH(PV_K_DOWN, pv::quant_rows_fp8(lw.w_down, D, F, ws + L.wd8, ws + L.wds, D, 0, s));
+    // this layer's derived weight copies: prepared once, or made here per call
+    const WeightCopies wc = t->prep ? prepared_copies(t, l)
+                                    : WeightCopies{ws + L.wq8, ws + L.wqs, ws + L.wo8, ws + L.wos,
+                                                   ws + L.b8,  ws + L.bs,  ws + L.wd8, ws + L.wds};
+    if (f8 && !t->prep) {  // this layer's weights in fp8
+      PV_LAUNCH(PV_K_QKV, make_fp8_copies(lw, wc, D, F, s));
     }
     {  // q,k,v with the 2-D rotary in the epilogue
       pv::GemmArgs a = g;
@@ -301,7 +389,7 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
       a.A = y; a.lda = D;
       a.B0 = lw.wq; a.B1 = lw.wk; a.B2 = lw.wv; a.ldb = D;
       a.C = big; a.ldc = 3 * D;
-      if (f8) use_fp8(a, D, ws + L.wq8, ws + L.wqs, 3 * D);
+      if (f8) use_fp8(a, D, wc.wq8, wc.wqs, 3 * D);
       PV_LAUNCH(PV_K_QKV, gemm(pv::GEMM_QKV, a));
     }
     if (stop_here && st.stage == PV_STAGE_QKV) return copy_stage(st, big, size_t(N) * 3 * D * es, s);
@@ -315,7 +403,7 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
       a.C = r; a.ldc = D;
       if (f8) {
         PV_LAUNCH(PV_K_OPROJ, pv::quant_rows_fp8(y, N, D, a8, as, srows, 0, s));
-        use_fp8(a, D, ws + L.wo8, ws + L.wos, D);
+        use_fp8(a, D, wc.wo8, wc.wos, D);
       }
       PV_LAUNCH(PV_K_OPROJ, gemm(pv::GEMM_OPROJ, a));
     }
@@ -324,24 +412,24 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
     // fp4 (times fp4 copies of the weights, 32-k scale blocks): its plain
     // bf16 rounding would otherwise be the largest error of the tower output
     if (f8) {
-      PV_LAUNCH(PV_K_NORM, pv::rmsnorm_fp8(r, lw.ffn_norm, a8, as, N, srows, D, eps, s));
+      PV_LAUNCH(PV_K_NORM_MLP, pv::rmsnorm_fp8(r, lw.ffn_norm, a8, as, N, srows, D, eps, s));
     } else if (bf) {
-      PV_LAUNCH(PV_K_GATEUP, pv::gateup_fp4(lw.w_gate, lw.w_up, ws + L.b8, ws + L.bs, F, D, s));
-      PV_LAUNCH(PV_K_NORM, pv::rmsnorm_hi_lo4(r, lw.ffn_norm, y, ws + L.a8, ws + L.as, N, srows, D, eps, s));
+      if (!t->prep) PV_LAUNCH(PV_K_GATEUP, pv::gateup_fp4(lw.w_gate, lw.w_up, wc.b8, wc.bs, F, D, s));
+      PV_LAUNCH(PV_K_NORM_MLP, pv::rmsnorm_hi_lo4(r, lw.ffn_norm, y, ws + L.a8, ws + L.as, N, srows, D, eps, s));
     } else {
-      PV_LAUNCH(PV_K_NORM, pv::rmsnorm(r, lw.ffn_norm, y, N, D, eps, true, s));
+      PV_LAUNCH(PV_K_NORM_MLP, pv::rmsnorm(r, lw.ffn_norm, y, N, D, eps, true, s));
     }
     {  // gate/up with silu(gate) * up in the epilogue
       pv::GemmArgs a = g;
       a.M = N; a.N = F; a.K = D;
       a.A = y; a.lda = D;
       if (bf) {
-        a.A8 = ws + L.a8; a.B8 = ws + L.b8; a.As = ws + L.as; a.Bs = ws + L.bs;
+        a.A8 = ws + L.a8; a.B8 = wc.b8; a.As = ws + L.as; a.Bs = wc.bs;
         a.k8 = D; a.as_rows = srows; a.bs_rows = 2 * F; a.low_fmt = 4;
       }
       a.B0 = lw.w_gate; a.B1 = lw.w_up; a.ldb = D;
       a.C = big; a.ldc = F;
-      if (f8) use_fp8(a, D, ws + L.b8, ws + L.bs, 2 * F);
+      if (f8) use_fp8(a, D, wc.b8, wc.bs, 2 * F);
       PV_LAUNCH(PV_K_GATEUP, gemm(pv::GEMM_GATEUP, a));
     }
     if (stop_here && st.stage == PV_STAGE_MLP_HIDDEN) return copy_stage(st, big, size_t(N) * F * es, s);
@@ -353,7 +441,7 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
       a.C = r; a.ldc = D;
       if (f8) {
         PV_LAUNCH(PV_K_DOWN, pv::quant_rows_fp8(big, N, F, a8, as, srows, 0, s));
-        use_fp8(a, F, ws + L.wd8, ws + L.wds, D);
+        use_fp8(a, F, wc.wd8, wc.wds, D);
       }
       PV_LAUNCH(PV_K_DOWN, gemm(pv::GEMM_DOWN, a));
     }
@@ -369,7 +457,7 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
   if (c.merge == 2 && bf) {
     // the final residual as bf16 hi | lo rows; the merger's A loads gather
     // the 2x2 groups from that copy
-    PV_LAUNCH(PV_K_MERGE, pv::split_rows(r, big, N, D, s));
+    PV_LAUNCH(PV_K_OPERAND, pv::split_rows(r, big, N, D, s));
     pv::GemmArgs a = g;
     a.M = int(plan.out_rows); a.N = c.out_dim; a.K = 8 * D; a.kb = 4 * D;
     a.A = big; a.lda = 2 * D;
@@ -384,7 +472,7 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
     a.C = out; a.ldc = c.out_dim;
     PV_LAUNCH(PV_K_MERGE, gemm(pv::GEMM_MERGE_F32, a));
   } else if (out_bf16) {
-    PV_LAUNCH(PV_K_MERGE, pv::f32_to_bf16(r, out, size_t(N) * D, s));
+    PV_LAUNCH(PV_K_OPERAND, pv::f32_to_bf16(r, out, size_t(N) * D, s));
   } else {
     PV_HIP(hipMemcpyAsync(out, r, size_t(N) * D * 4, hipMemcpyDeviceToDevice, s));
   }
@@ -609,11 +697,13 @@ pv_status pv_tower_create(const pv_config* cfg, const pv_weights* w, pv_tower** 
 
 void pv_tower_destroy(pv_tower* t) {
   if (!t) return;
-  if (t->upload_done) {
-    (void)hipEventSynchronize(t->upload_done);
-    (void)hipEventDestroy(t->upload_done);
+  for (auto& st : t->staging) {
+    if (st.done) {
+      (void)hipEventSynchronize(st.done);
+      (void)hipEventDestroy(st.done);
+    }
+    if (st.host) (void)hipHostFree(st.host);
   }
-  if (t->pinned) (void)hipHostFree(t->pinned);
   for (auto& r : t->recs) {
     (void)hipEventSynchronize(r.b);
     (void)hipEventDestroy(r.a);
@@ -630,6 +720,49 @@ pv_status pv_tower_plan(const pv_tower* t, const int32_t* image_hw, int32_t n_im
   pv_status st = make_plan(t, image_hw, n_images, &plan);
   if (st != PV_OK) return st;
   fill_info(t, plan, info);
+  return PV_OK;
+}
+
+pv_status pv_tower_prepared_bytes(const pv_tower* t, int64_t* bytes) {
+  pv::last_error().clear();
+  if (!t || !bytes) return fail(PV_ERR_ARG, "tower and bytes must not be null");
+  const pv_config& c = t->cfg;
+  *bytes = c.dtype == PV_BF16
+               ? int64_t(pv::prep_layout(c.patch, c.hidden, c.mlp, c.layers, (c.flags & PV_FLAG_FP8) != 0).total)
+               : 0;
+  return PV_OK;
+}
+
+pv_status pv_tower_prepare(pv_tower* t, void* mem, int64_t mem_bytes, void* stream) {
+  pv::last_error().clear();
+  if (!t) return fail(PV_ERR_ARG, "tower is null");
+  const pv_config& c = t->cfg;
+  if (!mem) {  // detach: derive the copies per call again
+    t->prep = nullptr;
+    return PV_OK;
+  }
+  if (c.dtype != PV_BF16) return PV_OK;  // the fp32 tower uses its weights as given
+  if (!aligned(mem, 256)) return fail(PV_ERR_ARG, "mem must be 256-byte aligned");
+  const bool f8 = (c.flags & PV_FLAG_FP8) != 0;
+  const pv::PrepLayout P = pv::prep_layout(c.patch, c.hidden, c.mlp, c.layers, f8);
+  if (mem_bytes < int64_t(P.total))
+    return fail(PV_ERR_CAPACITY, "mem_bytes " + std::to_string(mem_bytes) + " < " + std::to_string(P.total));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* m = static_cast<char*>(mem);
+  const int D = c.hidden, F = c.mlp;
+  t->prep = nullptr;  // a failed preparation leaves the tower deriving per call
+  PV_HIP(pv::pad_rows(t->w.patch_w, m + P.wpad, D, 3 * c.patch * c.patch, pv::patch_kp(c.patch), s));
+  for (int l = 0; l < c.layers; ++l) {
+    const pv_layer_weights& lw = t->layers[l];
+    char* b = m + P.layer0 + size_t(l) * P.layer_stride;
+    const WeightCopies wc{b + P.wq8, b + P.wqs, b + P.wo8, b + P.wos, b + P.b8, b + P.bs, b + P.wd8, b + P.wds};
+    if (f8)
+      PV_HIP(make_fp8_copies(lw, wc, D, F, s));
+    else
+      PV_HIP(pv::gateup_fp4(lw.w_gate, lw.w_up, wc.b8, wc.bs, F, D, s));
+  }
+  t->prep = m;
+  t->prep_layout = P;
   return PV_OK;
 }
 

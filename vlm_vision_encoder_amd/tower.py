@@ -26,9 +26,10 @@ EXPORTED = ("pv_tower_create", "pv_tower_destroy", "pv_tower_plan", "pv_tower_fo
             "pv_tower_forward_u8", "pv_preprocess_u8", "pv_tile_layout", "pv_tower_plan_tiles_u8",
             "pv_tower_forward_tiles_u8", "pv_config_preset", "pv_image_keys_workspace_bytes", "pv_image_keys_u8",
             "pv_embcache_create", "pv_embcache_destroy", "pv_embcache_clear", "pv_embcache_stats",
-            "pv_embcache_workspace_bytes", "pv_tower_forward_cached_u8", "pv_quantize_fp8", "pv_last_error", "pv_status_str")
+            "pv_embcache_workspace_bytes", "pv_tower_forward_cached_u8", "pv_quantize_fp8", "pv_last_error", "pv_status_str",
+            "pv_tower_prepared_bytes", "pv_tower_prepare")
 PRESETS = {"mistral3": 0, "pixtral12b": 1}
-KERNEL_CLASSES = ("maps", "patch", "norm", "qkv", "attn", "oproj", "gateup", "down", "merge")
+KERNEL_CLASSES = ("maps", "patch", "norm", "qkv", "attn", "oproj", "gateup", "down", "merge", "norm_mlp", "operand")
 
 
 class PvConfig(C.Structure):
@@ -127,6 +128,10 @@ def load_library(path: str = LIB_PATH):
     lib.pv_tower_forward_cached_u8.restype = i32
     lib.pv_quantize_fp8.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.pv_quantize_fp8.restype = i32
+    lib.pv_tower_prepared_bytes.argtypes = [vp, C.POINTER(C.c_int64)]
+    lib.pv_tower_prepared_bytes.restype = i32
+    lib.pv_tower_prepare.argtypes = [vp, vp, i64, vp]
+    lib.pv_tower_prepare.restype = i32
     lib.pv_last_error.argtypes = []
     lib.pv_last_error.restype = C.c_char_p
     lib.pv_status_str.argtypes = [i32]
@@ -152,6 +157,28 @@ def make_config(patch=14, hidden=1024, heads=16, mlp=4096, layers=24, merge=2, o
                     int(flags))
 
 
+def _stream_pair(stream):
+    """(torch stream object, raw hipStream_t) of a stream argument: None (the
+    current stream), a torch.cuda.Stream, or a raw hipStream_t given as an
+    int.  The raw handle goes to the library exactly as given; the torch
+    object only places and records allocations (the current stream itself
+    whenever the handle is the current stream's)."""
+    import torch
+    cur = torch.cuda.current_stream()
+    if stream is None:
+        return cur, cur.cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream, stream.cuda_stream
+    ptr = int(stream)
+    if ptr == cur.cuda_stream:
+        return cur, ptr
+    return torch.cuda.ExternalStream(ptr), ptr
+
+
+def _torch_stream(stream):
+    return _stream_pair(stream)[0]
+
+
 def _hw_array(image_hw: Sequence[Sequence[int]]):
     flat = [int(v) for hw in image_hw for v in hw]
     return (C.c_int32 * max(1, len(flat)))(*flat), len(image_hw)
@@ -165,9 +192,18 @@ class Tower:
     ``wk``, ``wv``, ``wo``, ``ffn_norm``, ``w_gate``, ``w_up``, ``w_down``),
     ``merge_w`` [out_dim, 4D] (merge 2).  Matrices in the tower dtype; the
     tensors are kept referenced for the tower's lifetime.
+
+    With ``prepare`` (the default) the tower's derived weight copies (padded
+    patch weights, fp4 / fp8 copies of the block matrices) are written once
+    into device memory the object owns (``pv_tower_prepare``); without it
+    every forward derives them in its workspace.
+
+    ``stream`` arguments take a ``torch.cuda.Stream`` or a raw ``hipStream_t``
+    (int); outputs and the workspace are allocated for, and recorded on, the
+    stream the call runs on.
     """
 
-    def __init__(self, cfg: PvConfig, weights: Dict):
+    def __init__(self, cfg: PvConfig, weights: Dict, prepare: bool = True):
         self.lib = load_library()
         self.cfg = cfg
         self._keep = weights
@@ -182,6 +218,28 @@ class Tower:
         _check(self.lib.pv_tower_create(C.byref(cfg), C.byref(self._w), C.byref(h)))
         self.handle = h
         self._ws = None
+        self._prep = None
+        if prepare:
+            self.prepare()
+
+    def prepare(self):
+        """Writes the derived weight copies once (pv_tower_prepare) on the
+        current stream and waits for them."""
+        import torch
+        nb = C.c_int64()
+        _check(self.lib.pv_tower_prepared_bytes(self.handle, C.byref(nb)))
+        if nb.value == 0:
+            return
+        mem = torch.empty(nb.value, dtype=torch.uint8, device="cuda")
+        st = torch.cuda.current_stream()
+        _check(self.lib.pv_tower_prepare(self.handle, mem.data_ptr(), nb.value, st.cuda_stream))
+        st.synchronize()
+        self._prep = mem
+
+    def unprepare(self):
+        """Forward calls derive the weight copies per call again."""
+        _check(self.lib.pv_tower_prepare(self.handle, None, 0, None))
+        self._prep = None
 
     def close(self):
         if getattr(self, "handle", None):
@@ -202,11 +260,25 @@ class Tower:
         return info
 
     # ------------------------------------------------------------ device
-    def workspace(self, nbytes: int):
+    def workspace(self, nbytes: int, stream=None):
+        """The cached workspace, grown to nbytes on `stream` and recorded on
+        it (so the caching allocator never hands its memory to another stream
+        while this stream's work is pending)."""
         import torch
+        st = _torch_stream(stream)
         if self._ws is None or self._ws.numel() < nbytes:
-            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+            if self._ws is not None:
+                self._ws.record_stream(st)
+            with torch.cuda.stream(st):
+                self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        elif st != torch.cuda.current_stream():
+            self._ws.record_stream(st)
         return self._ws
+
+    def _new_out(self, info, stream):
+        import torch
+        with torch.cuda.stream(_torch_stream(stream)):
+            return torch.empty((info.out_rows, info.out_cols), dtype=self._out_dtype(), device="cuda")
 
     def _act_dtype(self):
         import torch
@@ -223,9 +295,9 @@ class Tower:
         arr, n = _hw_array(image_hw)
         info = self.plan(image_hw)
         if out is None:
-            out = torch.empty((info.out_rows, info.out_cols), dtype=self._out_dtype(), device="cuda")
-        ws = self.workspace(info.workspace_bytes)
-        s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+            out = self._new_out(info, stream)
+        ws = self.workspace(info.workspace_bytes, stream)
+        s = _stream_pair(stream)[1]
         _check(self.lib.pv_tower_forward(self.handle, pixels.data_ptr(), arr, n, out.data_ptr(), out.shape[0],
                                          ws.data_ptr(), ws.numel(), s))
         return out
@@ -251,9 +323,9 @@ class Tower:
         arr, n = _hw_array(src_hw)
         info, _ = self.plan_u8(src_hw)
         if out is None:
-            out = torch.empty((info.out_rows, info.out_cols), dtype=self._out_dtype(), device="cuda")
-        ws = self.workspace(info.workspace_bytes)
-        s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+            out = self._new_out(info, stream)
+        ws = self.workspace(info.workspace_bytes, stream)
+        s = _stream_pair(stream)[1]
         ms = (C.c_float * 6)(*mean_std) if mean_std is not None else None
         _check(self.lib.pv_tower_forward_u8(self.handle, images.data_ptr(), arr, n, ms, out.data_ptr(),
                                             out.shape[0], ws.data_ptr(), ws.numel(), s))
@@ -274,9 +346,9 @@ class Tower:
         arr, n = _hw_array(src_hw)
         info, _ = self.plan_tiles_u8(src_hw, max_num_tiles)
         if out is None:
-            out = torch.empty((info.out_rows, info.out_cols), dtype=self._out_dtype(), device="cuda")
-        ws = self.workspace(info.workspace_bytes)
-        s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+            out = self._new_out(info, stream)
+        ws = self.workspace(info.workspace_bytes, stream)
+        s = _stream_pair(stream)[1]
         ms = (C.c_float * 6)(*mean_std) if mean_std is not None else None
         _check(self.lib.pv_tower_forward_tiles_u8(self.handle, images.data_ptr(), arr, n, int(max_num_tiles), ms,
                                                   out.data_ptr(), out.shape[0], ws.data_ptr(), ws.numel(), s))
@@ -422,17 +494,23 @@ class EmbCache:
         import torch
         arr, n = _hw_array(src_hw)
         info, _ = self.tower.plan_u8(src_hw)
+        st, sptr = _stream_pair(stream)
         if out is None:
-            out = torch.empty((info.out_rows, info.out_cols), dtype=self.tower._out_dtype(), device="cuda")
+            out = self.tower._new_out(info, st)
         need = self.workspace_bytes(src_hw)
         if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+            if self._ws is not None:
+                self._ws.record_stream(st)
+            with torch.cuda.stream(st):
+                self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        elif st != torch.cuda.current_stream():
+            self._ws.record_stream(st)
         k = None
         if keys is not None:
             flat = [int(v) & 0xFFFFFFFFFFFFFFFF for pair in keys for v in pair]
             k = (C.c_uint64 * (2 * n))(*flat)
         hits = (C.c_int32 * n)()
-        s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+        s = sptr
         _check(self.lib.pv_tower_forward_cached_u8(self.handle, images.data_ptr(), arr, n, k, out.data_ptr(),
                                                    out.shape[0], self._ws.data_ptr(), self._ws.numel(), s, hits))
         return out, list(hits)
