@@ -27,14 +27,28 @@ from vlm_vision_encoder_amd import synth  # noqa: E402
 
 N_SAMPLE_ROWS = 32
 SAMPLE_SEED = 1234
+# at least one sampled row in every band of this many consecutive output rows
+# of an image: 128 patch rows, or 64 merged rows (a merged row gathers four
+# patches, so 64 of them span about 256 patch rows)
+BAND_PATCH_ROWS = 128
+BAND_MERGED_ROWS = 64
 
 
-def sample_rows(out_rows: int, image_rows) -> np.ndarray:
-    """First and last row of the batch, the first row of every image (up to
-    8), and seeded random rows, sorted and unique."""
+def sample_rows(out_rows: int, image_starts, band: int = BAND_PATCH_ROWS) -> np.ndarray:
+    """Per image: its first and last output row and one seeded row in every
+    band of `band` consecutive rows; then seeded rows over the whole batch.
+    Sorted and unique."""
     rng = np.random.default_rng(SAMPLE_SEED)
-    fixed = [0, out_rows - 1] + list(image_rows[:8])
-    rest = rng.choice(out_rows, size=N_SAMPLE_ROWS, replace=False)
+    bounds = list(image_starts) + [out_rows]
+    fixed = []
+    for s, e in zip(bounds[:-1], bounds[1:]):
+        if e <= s:
+            continue
+        fixed += [s, e - 1]
+        for b0 in range(s, e, band):
+            b1 = min(b0 + band, e)
+            fixed.append(int(rng.integers(b0, b1)))
+    rest = rng.choice(out_rows, size=min(N_SAMPLE_ROWS, out_rows), replace=False)
     return np.unique(np.array(fixed + list(rest), dtype=np.int64))
 
 
@@ -52,7 +66,8 @@ def make(name: str, fp8: bool = False) -> str:
         starts = np.cumsum([0] + [(h // wl.patch // 2) * (ww // wl.patch // 2) for h, ww in wl.image_hw])[:-1]
     else:
         starts = maps["cu_seqlens"][:-1]
-    rows = sample_rows(out.shape[0], list(starts))
+    rows = sample_rows(out.shape[0], [int(x) for x in starts],
+                       BAND_MERGED_ROWS if wl.merge == 2 else BAND_PATCH_ROWS)
     path = os.path.join(HERE, f"{name}_fp8.npz" if fp8 else f"{name}.npz")
     np.savez_compressed(path, rows=rows, values=out[rows].astype(np.float32),
                         rms=np.float64(np.sqrt(np.mean(out * out))), shape=np.array(out.shape, np.int64),
