@@ -72,6 +72,11 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run __graft_entry__.build() "
                            "(python -m vlm_vision_encoder_amd.build_lib)")
+    # torch first: its HIP runtime (a copy under torch/lib with the same
+    # soname) is then the one the library binds to.  Loaded the other way
+    # round, the process would hold two HIP runtimes, one for torch's memory
+    # and streams and one for the library's kernels.
+    import torch  # noqa: F401
     lib = C.CDLL(path)
     vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
     lib.pv_tower_create.argtypes = [C.POINTER(PvConfig), C.POINTER(PvWeights), C.POINTER(vp)]
