@@ -294,6 +294,23 @@ pv_status pv_scatter_image_embeddings(const int32_t* token_ids, int64_t seq_len,
                                       int32_t dim, int32_t elem_bytes, int32_t* status, void* workspace,
                                       size_t ws_bytes, void* stream);
 
+/* pv_scatter_image_embeddings for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same operation and arguments without the workspace.  Its
+ * scratch (the list of placeholder positions and their count) is a fixed
+ * 4 MB array in the library's device memory, one per GPU, held until the
+ * process ends; nothing is allocated by the call.  seq_len is at most
+ * 1,048,576 (2^20) positions.  The array of the current device is used (the
+ * stream must belong to it); every call on one GPU shares it, so calls that
+ * overlap on one GPU (different streams, or host threads) race -- serialise
+ * them, e.g. on one stream.  Nothing in it needs clearing: each call writes
+ * the count and the list before reading them.
+ * Errors: as pv_scatter_image_embeddings, and PV_ERR_CAPACITY when seq_len
+ * exceeds 2^20. */
+pv_status pv_scatter_image_embeddings_noalloc(const int32_t* token_ids, int64_t seq_len, int32_t image_token_id,
+                                              const void* image_emb, int64_t n_image_rows, void* text_emb,
+                                              int32_t dim, int32_t elem_bytes, int32_t* status, void* stream);
+
 /* ---- uint8 input: resize onto the patch grid + normalisation ----
  * Sources: "Mistral 3" (KerasFormers) model page, description (images are
  * resized so that the longest edge fits longest_edge and the sides stay on

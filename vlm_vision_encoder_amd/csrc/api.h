@@ -39,4 +39,9 @@ pv_status forward_u8_at(pv_tower* t, const uint8_t* images, const int32_t* src_h
                         int32_t n, const float* mean_std, void* out, int64_t out_rows_cap, void* workspace,
                         size_t ws_bytes, hipStream_t s);
 
+// Argument checks of the masked scatter shared by its entry points (null,
+// range, element size, row size, alignment): PV_OK or PV_ERR_ARG.
+pv_status scatter_check(const int32_t* token_ids, int64_t seq_len, const void* image_emb, int64_t n_image_rows,
+                        const void* text_emb, int32_t dim, int32_t elem_bytes, const int32_t* status);
+
 }  // namespace pv

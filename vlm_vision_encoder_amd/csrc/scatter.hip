@@ -6,6 +6,10 @@
 //   scan: one workgroup compacts the placeholder positions (in sequence
 //         order) into a list and counts them;
 //   copy: one workgroup per image row moves the row (16-byte accesses).
+#include <mutex>
+#include <string>
+
+#include "api.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -73,4 +77,56 @@ hipError_t scatter_rows(const int32_t* ids, int64_t n, int32_t token, const void
   return hipGetLastError();
 }
 
+// ---- allocation-free variant: the scratch (position list + count) lives in
+// a file-scope device array of a fixed size instead of a caller workspace.
+namespace {
+
+// longest token sequence the allocation-free scatter takes
+constexpr int64_t kScratchMaxSeq = int64_t(1) << 20;
+// scatter_workspace_bytes(kScratchMaxSeq) bytes: the list of up to
+// kScratchMaxSeq positions, then 256 bytes holding the count
+constexpr size_t kScratchBytes = (size_t(kScratchMaxSeq) * 4 + 255) / 256 * 256 + 256;
+static __device__ __align__(256) int32_t scratch[kScratchBytes / 4];
+
+// Device address of `scratch` per device: the host-side name is only a
+// stand-in, so it is looked up once per device (with that device current)
+// and the address is passed to the kernels.
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+pv_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  PV_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PV_ERR_HIP, "device index " + std::to_string(dev) + " out of range");
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    PV_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(PV_ERR_HIP, "no device address for the scatter scratch");
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return PV_OK;
+}
+
+}  // namespace
+
 }  // namespace pv
+
+extern "C" pv_status pv_scatter_image_embeddings_noalloc(const int32_t* token_ids, int64_t seq_len,
+                                                         int32_t image_token_id, const void* image_emb,
+                                                         int64_t n_image_rows, void* text_emb, int32_t dim,
+                                                         int32_t elem_bytes, int32_t* status, void* stream) {
+  pv::last_error().clear();
+  pv_status st = pv::scatter_check(token_ids, seq_len, image_emb, n_image_rows, text_emb, dim, elem_bytes, status);
+  if (st != PV_OK) return st;
+  if (seq_len > pv::kScratchMaxSeq)
+    return pv::fail(PV_ERR_CAPACITY, "seq_len " + std::to_string(seq_len) + " exceeds the allocation-free scatter's "
+                                     "maximum of " + std::to_string(pv::kScratchMaxSeq) + " positions");
+  void* ws = nullptr;
+  if ((st = pv::scratch_of_current_device(&ws)) != PV_OK) return st;
+  PV_HIP(pv::scatter_rows(token_ids, seq_len, image_token_id, image_emb, n_image_rows, text_emb,
+                          int64_t(dim) * elem_bytes, status, ws, static_cast<hipStream_t>(stream)));
+  return PV_OK;
+}

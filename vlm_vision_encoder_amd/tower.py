@@ -27,7 +27,7 @@ EXPORTED = ("pv_tower_create", "pv_tower_destroy", "pv_tower_plan", "pv_tower_fo
             "pv_tower_forward_tiles_u8", "pv_config_preset", "pv_image_keys_workspace_bytes", "pv_image_keys_u8",
             "pv_embcache_create", "pv_embcache_destroy", "pv_embcache_clear", "pv_embcache_stats",
             "pv_embcache_workspace_bytes", "pv_tower_forward_cached_u8", "pv_quantize_fp8", "pv_last_error", "pv_status_str",
-            "pv_tower_prepared_bytes", "pv_tower_prepare")
+            "pv_tower_prepared_bytes", "pv_tower_prepare", "pv_scatter_image_embeddings_noalloc")
 PRESETS = {"mistral3": 0, "pixtral12b": 1}
 KERNEL_CLASSES = ("maps", "patch", "norm", "qkv", "attn", "oproj", "gateup", "down", "merge", "norm_mlp", "operand")
 
@@ -133,6 +133,8 @@ def load_library(path: str = LIB_PATH):
     lib.pv_tower_forward_cached_u8.restype = i32
     lib.pv_quantize_fp8.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.pv_quantize_fp8.restype = i32
+    lib.pv_scatter_image_embeddings_noalloc.argtypes = [vp, i64, i32, vp, i64, vp, i32, i32, vp, vp]
+    lib.pv_scatter_image_embeddings_noalloc.restype = i32
     lib.pv_tower_prepared_bytes.argtypes = [vp, C.POINTER(C.c_int64)]
     lib.pv_tower_prepared_bytes.restype = i32
     lib.pv_tower_prepare.argtypes = [vp, vp, i64, vp]
@@ -433,6 +435,24 @@ def scatter_image_embeddings(token_ids, image_emb, text_emb, image_token_id: int
                                            text_emb.data_ptr() if S else None, dim, image_emb.element_size(),
                                            status.data_ptr(), ws.data_ptr(), wsb,
                                            torch.cuda.current_stream().cuda_stream))
+    return status
+
+
+def scatter_image_embeddings_noalloc(token_ids, image_emb, text_emb, image_token_id: int = 10):
+    """As scatter_image_embeddings, through the allocation-free entry point
+    (the library's fixed device scratch; at most 2^20 tokens).  Allocates
+    only the returned status word."""
+    import torch
+    lib = load_library()
+    assert token_ids.dtype == torch.int32 and token_ids.is_contiguous()
+    assert image_emb.dtype == text_emb.dtype and image_emb.is_contiguous() and text_emb.is_contiguous()
+    S, T = token_ids.numel(), image_emb.shape[0]
+    dim = text_emb.shape[1] if text_emb.dim() == 2 else image_emb.shape[1]
+    status = torch.empty(1, dtype=torch.int32, device=text_emb.device)
+    _check(lib.pv_scatter_image_embeddings_noalloc(token_ids.data_ptr() if S else None, S, int(image_token_id),
+                                                   image_emb.data_ptr() if T else None, T,
+                                                   text_emb.data_ptr() if S else None, dim, image_emb.element_size(),
+                                                   status.data_ptr(), torch.cuda.current_stream().cuda_stream))
     return status
 
 
