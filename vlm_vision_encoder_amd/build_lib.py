@@ -51,6 +51,23 @@ def _compile(src: str, build_dir: str = BUILD, defines=()) -> str:
     return obj
 
 
+PROBE_SRC = "probe_issue.hip"
+PROBE = os.path.join(PKG, "probe_issue")
+
+
+def build_probe(verbose: bool = True) -> str:
+    """Builds the MFMA / VALU overlap microbenchmark (an executable, not part
+    of the library)."""
+    cmd = [hipcc()] + COMMON + DEVICE + [os.path.join(CSRC, PROBE_SRC), "-o", PROBE + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(PROBE + ".tmp", PROBE)
+    if verbose:
+        print(f"built {PROBE}")
+    return PROBE
+
+
 def build(verbose: bool = True, jobs: int = 8, out: str = LIB, build_dir: str = BUILD, defines=()) -> str:
     """Compiles all sources (optionally with extra -D defines) and links `out`."""
     os.makedirs(build_dir, exist_ok=True)
