@@ -82,8 +82,22 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
   __shared__ u32x4 kl[2][SLOTS];
   __shared__ u32x4 vl[2][SLOTS];
 
+  // Workgroups reach the 8 XCDs round robin (block b on XCD b % 8).  With a
+  // head count divisible by 8, XCD x takes heads x, x + 8, ... and walks
+  // them item-major, so the query tiles running together on one XCD share
+  // its L2 for their heads' K and V, and every XCD still starts its longest
+  // items (the work list is longest-first) first.  Otherwise item-major over
+  // all heads.
   const int heads = a.heads;
-  const int item = blockIdx.x / heads, head = blockIdx.x - item * heads;
+  int item, head;
+  if ((heads & 7) == 0) {
+    const int hpx = heads >> 3, jx = blockIdx.x >> 3;
+    item = jx / hpx;
+    head = (blockIdx.x & 7) + 8 * (jx - item * hpx);
+  } else {
+    item = blockIdx.x / heads;
+    head = blockIdx.x - item * heads;
+  }
   const AttnItem it = a.items[item];
   const ImageMeta mt = a.meta[it.image];
   const int n = mt.Hp * mt.Wp;
