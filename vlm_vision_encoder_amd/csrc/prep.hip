@@ -75,6 +75,105 @@ __device__ __forceinline__ float sample_u8(const uint8_t* __restrict__ img, uint
   return (top + fy * (bot - top)) * mul + add;
 }
 
+// Staged im2col: one workgroup per kStagePatches consecutive patches of the
+// packed sequence.  Phase 1 reads, for every channel c and pixel row u of a
+// patch, the p pixels of each of the workgroup's patches -- consecutive
+// patches of one patch row sit side by side in the image, so a wave reads one
+// contiguous run -- into LDS (element k = c p^2 + u p + x of patch q at
+// stage[q * stride + k]).  Phase 2 writes every (patch, 8 k) chunk as
+// bf16 hi | lo with 16-byte stores, k >= K zero.  Phase 1 takes one thread per
+// pixel column of the workgroup's patches (16 p <= 256), so patches of up to
+// 16 pixels use it (K <= 768 fits the stride); larger ones take the
+// per-thread kernel below.
+constexpr int kStagePatches = 16;
+constexpr int kStageStride = 1040;  // floats, any patch up to 16 pixels; consecutive patches 16 banks apart
+constexpr int kStageThreads = 256;
+// per-patch LDS stride for a compile-time patch edge: K rounded up to 8, plus
+// an offset that moves consecutive patches to other banks (P = 14: 600 floats,
+// 24 banks apart; P = 16: 776, 8 apart), so that 4 (P = 14) or 3 (P = 16)
+// workgroups fit a CU's LDS
+template <int P>
+constexpr int stage_stride() {
+  return P == 14 ? 600 : P == 16 ? 776 : kStageStride;
+}
+
+// P: the patch edge as a compile-time constant (its 3 P loads of a thread are
+// all issued before the LDS stores), or 0 (maps.patch, a loop).
+template <int P>
+__global__ __launch_bounds__(kStageThreads) void im2col_staged_kernel(const float* __restrict__ pixels, DevMaps maps,
+                                                                      uint16_t* __restrict__ out, int n_patches,
+                                                                      int K, int Kp) {
+  constexpr int SS = stage_stride<P>();
+  static_assert(P == 0 || SS >= 3 * P * P, "stage stride below K");
+  __shared__ __attribute__((aligned(16))) float stage[kStagePatches * SS];
+  __shared__ long long q_base[kStagePatches];  // element offset of the patch's first pixel (channel 0)
+  __shared__ long long q_plane[kStagePatches];  // H * W of its image
+  __shared__ int q_w[kStagePatches];            // W of its image
+  const int g0 = blockIdx.x * kStagePatches;
+  const int np = n_patches - g0 < kStagePatches ? n_patches - g0 : kStagePatches;
+  const int p = P > 0 ? P : maps.patch, pp = p * p;
+  const int t = threadIdx.x;
+  if (t < np) {
+    const int g = g0 + t;
+    const int img = maps.rowinfo[2 * g], rc = maps.rowinfo[2 * g + 1];
+    const ImageMeta mt = maps.meta[img];
+    q_base[t] = pix_offset(mt) + (long long)((rc >> 16) * p) * mt.W + (rc & 0xffff) * p;
+    q_plane[t] = (long long)mt.H * mt.W;
+    q_w[t] = mt.W;
+  }
+  __syncthreads();
+  // phase 1: thread t owns pixel x of patch q in every (c, u) row
+  if (t < np * p) {
+    const int q = t / p, x = t - q * p;
+    const float* src = pixels + q_base[q] + x;
+    const long long plane = q_plane[q];
+    const int w = q_w[q];
+    float* dst = stage + q * SS + x;
+    if constexpr (P > 0) {
+      float v[3 * P];
+#pragma unroll
+      for (int c = 0; c < 3; ++c)
+#pragma unroll
+        for (int u = 0; u < P; ++u) v[c * P + u] = src[c * plane + (long long)u * w];
+#pragma unroll
+      for (int c = 0; c < 3; ++c)
+#pragma unroll
+        for (int u = 0; u < P; ++u) dst[c * P * P + u * P] = v[c * P + u];
+    } else {
+      for (int c = 0; c < 3; ++c) {
+        const float* sc = src + c * plane;
+        float* dc = dst + c * pp;
+#pragma unroll 7
+        for (int u = 0; u < p; ++u) dc[u * p] = sc[(long long)u * w];
+      }
+    }
+  }
+  __syncthreads();
+  // phase 2: (patch, 8 k) chunks
+  const int chunks = Kp / 8;
+  for (int f = t; f < np * chunks; f += kStageThreads) {
+    const int q = f / chunks, k0 = (f - q * chunks) * 8;
+    float v[8];
+    if (k0 + 8 <= K) {
+      const floatx4 a = *reinterpret_cast<const floatx4*>(stage + q * SS + k0);
+      const floatx4 b = *reinterpret_cast<const floatx4*>(stage + q * SS + k0 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = a[e];
+        v[4 + e] = b[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = k0 + e < K ? stage[q * SS + k0 + e] : 0.f;
+    }
+    u32x4 hi, lo;
+    split8(v, hi, lo);
+    uint16_t* row = out + size_t(g0 + q) * 2 * Kp;
+    *reinterpret_cast<u32x4*>(row + k0) = hi;
+    *reinterpret_cast<u32x4*>(row + Kp + k0) = lo;
+  }
+}
+
 // One thread per (patch g, 8 consecutive k).
 __global__ __launch_bounds__(256) void im2col_split_kernel(const float* __restrict__ pixels, DevMaps maps,
                                                            uint16_t* __restrict__ out, int n_patches, int K, int Kp) {
@@ -289,6 +388,17 @@ hipError_t im2col_split(const float* pixels, const DevMaps& maps, void* out, int
                         hipStream_t s) {
   if (n_patches <= 0) return hipSuccess;
   if (Kp % 8 || K > Kp) return hipErrorInvalidValue;
+  if (K <= kStageStride && K == 3 * maps.patch * maps.patch && kStagePatches * maps.patch <= kStageThreads) {
+    const dim3 grid((n_patches + kStagePatches - 1) / kStagePatches), block(kStageThreads);
+    uint16_t* o = static_cast<uint16_t*>(out);
+    if (maps.patch == 14)
+      hipLaunchKernelGGL(im2col_staged_kernel<14>, grid, block, 0, s, pixels, maps, o, n_patches, K, Kp);
+    else if (maps.patch == 16)
+      hipLaunchKernelGGL(im2col_staged_kernel<16>, grid, block, 0, s, pixels, maps, o, n_patches, K, Kp);
+    else
+      hipLaunchKernelGGL(im2col_staged_kernel<0>, grid, block, 0, s, pixels, maps, o, n_patches, K, Kp);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(im2col_split_kernel, grid_for((long long)n_patches * (Kp / 8)), dim3(256), 0, s, pixels, maps,
                      static_cast<uint16_t*>(out), n_patches, K, Kp);
   return hipGetLastError();
