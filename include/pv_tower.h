@@ -101,6 +101,18 @@ typedef struct pv_config {
  * (the NeMo Automodel page registers FP8-native Mistral 3 VLM checkpoints);
  * its accuracy is that of e4m3, not the bf16 tower's. */
 #define PV_FLAG_FP8 2
+/* pv_config.flags, bf16 tower with merge == 2 only: a deeper projector in
+ * place of the single bias-free merge projection (the pages name only "a
+ * 2x2 patch-merging projector" without bias; this variant is a reading of a
+ * deeper adapter, off by default):
+ *   y   = RMSNorm(h_L) * proj->norm         per patch, eps = cfg.rms_eps
+ *   z   = 2x2 gather of y (as the plain merge: (dy,dx) order, channel fastest)
+ *   m   = z merge_w^T                       merge_w [D][4D] (4D -> D)
+ *   a   = GELU(m w1^T)                      w1 [out_dim][D], GELU(x) = x Phi(x)
+ *   out = a w2^T                            w2 [out_dim][out_dim]
+ * all without bias.  The weights come from pv_weights.merge_w and
+ * pv_weights.proj. */
+#define PV_FLAG_DEEP_PROJECTOR 4
 
 /* Per-block weights: borrowed device pointers, row-major, "out x in" like a
  * linear layer (y = x W^T).  Gains are always fp32; matrices use cfg.dtype. */
@@ -116,12 +128,23 @@ typedef struct pv_layer_weights {
   const void* w_down;     /* [D][F] */
 } pv_layer_weights;
 
+/* Weights of the deeper projector (PV_FLAG_DEEP_PROJECTOR): borrowed device
+ * pointers, matrices in cfg.dtype. */
+typedef struct pv_projector_weights {
+  const float* norm;  /* [D] fp32 gain of the RMSNorm before the merge */
+  const void* w1;     /* [out_dim][D]       */
+  const void* w2;     /* [out_dim][out_dim] */
+} pv_projector_weights;
+
 typedef struct pv_weights {
   const void* patch_w;             /* [D][3][p][p] device, cfg.dtype (conv kernel, no bias) */
   const float* ln_pre;             /* [D] device fp32 */
   const pv_layer_weights* layers;  /* HOST array of cfg.layers entries; copied at create */
   const void* merge_w;             /* [out_dim][4D] device, cfg.dtype; K order (dy,dx,channel)
-                                      with channel fastest; NULL when merge == 1 */
+                                      with channel fastest; NULL when merge == 1.  With
+                                      PV_FLAG_DEEP_PROJECTOR: [D][4D] (4D -> D) */
+  const pv_projector_weights* proj; /* HOST pointer, read at create; NULL unless
+                                       PV_FLAG_DEEP_PROJECTOR */
 } pv_weights;
 
 typedef struct pv_tower pv_tower;
@@ -142,9 +165,10 @@ typedef struct pv_plan_info {
 /* Creates a tower.  cfg and w are read (w->layers is copied); the device
  * pointers inside w are borrowed.  Builds the rotary cos/sin table on the host
  * in double precision.  Allocates no device memory.
- * Errors: PV_ERR_ARG (null, bad field), PV_ERR_UNSUPPORTED (head_dim != 64,
- * hidden or mlp not a multiple of 256, mlp above 2^20, out_dim not a
- * multiple of 128). */
+ * Errors: PV_ERR_ARG (null, bad field, PV_FLAG_DEEP_PROJECTOR without
+ * proj weights), PV_ERR_UNSUPPORTED (head_dim != 64, hidden or mlp not a
+ * multiple of 256, mlp above 2^20, out_dim not a multiple of 128, the deeper
+ * projector with the fp32 tower or without merge). */
 pv_status pv_tower_create(const pv_config* cfg, const pv_weights* w, pv_tower** out);
 
 /* Frees the tower's host resources.  Waits for the tower's own pending

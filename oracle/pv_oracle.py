@@ -61,6 +61,10 @@ notes of the repository):
     registration): OCP e4m3 with one power-of-two scale per 32 values along
     the contraction axis, X = floor(log2(block max)) - 7, ties to even; the
     four linear maps of every block quantise both operands.
+14. Deeper projector (off by default; the "Mistral 3" page names only a
+    bias-free 2x2 patch-merging projector): RMSNorm of each patch (own
+    gain), the 2x2 gather with a bias-free 4D -> D linear, then D -> out_dim,
+    GELU (x Phi(x), the erf form), out_dim -> out_dim, without biases.
 
 Pinning: every function here is pinned in ``tests/test_oracle_pins.py`` by a
 check that does not reuse this code path (closed-form counts printed on the
@@ -93,6 +97,7 @@ class TowerConfig:
     out_dim: int = 5120
     rope_theta: float = 1.0e4
     rms_eps: float = 1.0e-5
+    deep_projector: bool = False  # reading 14: the deeper projector variant
 
     @property
     def head_dim(self) -> int:
@@ -289,6 +294,25 @@ def merge_project(h: np.ndarray, merge_src: np.ndarray, w_merge: np.ndarray) -> 
     src = np.asarray(merge_src, dtype=np.int64)
     z = np.concatenate([h[src[:, 0]], h[src[:, 1]], h[src[:, 2]], h[src[:, 3]]], axis=1)
     return z @ np.asarray(w_merge, dtype=np.float64).T
+
+
+def gelu(x: np.ndarray) -> np.ndarray:
+    """GELU(x) = x Phi(x), Phi the standard normal distribution function,
+    Phi(x) = (1 + erf(x / sqrt 2)) / 2."""
+    from scipy.special import erf
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+
+
+def deep_project(h: np.ndarray, merge_src: np.ndarray, w_merge: np.ndarray, proj: dict, eps: float) -> np.ndarray:
+    """The deeper projector variant (reading 14; the pages name only a 2x2
+    patch-merging projector without bias): RMSNorm of every patch with its own
+    gain, the 2x2 gather and a bias-free 4D -> D linear, then D -> out_dim,
+    GELU, out_dim -> out_dim, all bias-free."""
+    y = rms_norm(h, proj["norm"], eps)
+    m = merge_project(y, merge_src, w_merge)
+    a = gelu(m @ np.asarray(proj["w1"], dtype=np.float64).T)
+    return a @ np.asarray(proj["w2"], dtype=np.float64).T
 
 
 # --------------------------------------------------------------------------
@@ -603,7 +627,9 @@ def tower_forward(
         if collect:
             res["block_out"].append(h.copy())
     res["tower_out"] = h
-    if cfg.merge == 2:
+    if cfg.merge == 2 and cfg.deep_projector:
+        res["out"] = deep_project(h, maps["merge_src"], weights["merge_w"], weights["proj"], cfg.rms_eps)
+    elif cfg.merge == 2:
         res["out"] = merge_project(h, maps["merge_src"], weights["merge_w"])
     else:
         res["out"] = h

@@ -510,3 +510,36 @@ def test_prepared_bytes_and_prepare_validation():
     h, bf = prepared(T.make_config(layers=L, dtype="f32"))
     assert bf == 0
     lib.pv_tower_destroy(h)
+
+
+def test_deep_projector_flag_validation():
+    """PV_FLAG_DEEP_PROJECTOR: bf16 tower with merge only, projector weights
+    required; the planner sizes the big region for the out_dim-wide GELU
+    output."""
+    lib = T.load_library()
+    flag = T.PV_FLAG_DEEP_PROJECTOR
+    st, h, _ = create(T.make_config(layers=2, flags=flag))
+    assert st == -1 and b"proj" in lib.pv_last_error()
+    st, h, _ = create(T.make_config(layers=2, dtype="f32", flags=flag))
+    assert st == -5
+    st, h, _ = create(T.make_config(layers=2, merge=1, flags=flag))
+    assert st == -5
+    w, arr = fake_weights(2, True)
+    pj = T.PvProjectorWeights(FAKE, FAKE, FAKE)
+    w.proj = C.pointer(pj)
+    handles = []
+    for out_dim, flags in ((5120, flag), (5120, 0), (32768, flag)):
+        cfg = T.make_config(layers=2, out_dim=out_dim, flags=flags)
+        hd = C.c_void_p()
+        assert lib.pv_tower_create(C.byref(cfg), C.byref(w), C.byref(hd)) == 0
+        handles.append(hd)
+    st_d, deep = _plan(lib, handles[0], [(448, 448)])
+    st_p, plain = _plan(lib, handles[1], [(448, 448)])
+    st_w, wide = _plan(lib, handles[2], [(448, 448)])
+    assert st_d == st_p == st_w == 0
+    # 448^2: 1,024 patches, 256 merged tokens; the big region holds 1,024 rows
+    # of 4,096 bf16 (8 MiB): 256 x 5,120 bf16 fit, 256 x 32,768 (16 MiB) grow it
+    assert deep.workspace_bytes == plain.workspace_bytes
+    assert wide.workspace_bytes - plain.workspace_bytes == 256 * 32768 * 2 - 1024 * 4096 * 2
+    for hd in handles:
+        lib.pv_tower_destroy(hd)

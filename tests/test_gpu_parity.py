@@ -398,3 +398,32 @@ def test_zero_layer_tower_and_capacity_errors():
     c = Case(wl)
     ref = c.ref()
     check("out", to_np(c.run()), ref["out"], TOL["bf16"], stored_bf16=True)
+
+
+@pytest.mark.parametrize("case", ["narrow-3-images", "full-width"])
+def test_bf16_deep_projector(case):
+    """The deeper projector variant (PV_FLAG_DEEP_PROJECTOR: RMSNorm -> 2x2
+    merge 4D -> D -> D -> out_dim -> GELU -> out_dim -> out_dim) against the
+    oracle's deep_project: output at the bf16 bar with an fp32 and with a
+    bf16 output buffer."""
+    torch = _torch()
+    if case == "full-width":
+        wl = synth.Workload("deep", patch=14, layers=1, merge=2, image_hw=((448, 448),), deep_projector=True)
+    else:
+        wl = synth.Workload("deep", patch=14, layers=2, merge=2, image_hw=((448, 392), (224, 280), (84, 140)),
+                            hidden=256, heads=4, mlp=512, out_dim=384, deep_projector=True)
+    say(f"bf16 deeper projector {case}: {wl.n_patches} patches, out_dim {wl.out_dim}")
+    w = synth.make_weights(wl)
+    px = synth.make_pixels(wl)
+    dev_w = T.weights_to_device(w, "bf16")
+    cfg = O.TowerConfig(patch=wl.patch, hidden=wl.hidden, heads=wl.heads, mlp=wl.mlp, layers=wl.layers, merge=2,
+                        out_dim=wl.out_dim, rope_theta=wl.rope_theta, rms_eps=wl.rms_eps, deep_projector=True)
+    ref = O.tower_forward(px.astype(np.float64), wl.image_hw, synth.oracle_weights(w), cfg)["out"]
+    pix = torch.from_numpy(px).cuda()
+    for out_dtype in ("f32", "bf16"):
+        tw = T.Tower(T.config_for(wl, out_dtype=out_dtype, flags=T.PV_FLAG_DEEP_PROJECTOR), dev_w)
+        out = tw.forward(pix, wl.image_hw)
+        torch.cuda.synchronize()
+        assert tuple(out.shape) == ref.shape
+        check(f"deep projector out ({out_dtype} buffer)", to_np(out), ref, TOL["bf16"], stored_bf16=out_dtype == "bf16")
+        tw.close()

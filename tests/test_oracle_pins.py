@@ -881,3 +881,80 @@ def test_fp8_tower_quantisation_points_step_by_step():
         a_, b_, o_ = _fp8_tower_by_steps(px, hw, w, cfg, mistake)
         worst = max(_col_err(g_, w_) for g_, w_ in zip(got, a_ + b_ + [o_]))
         assert worst > 1e-3, mistake
+
+
+# ------------------------------------------------------ deeper projector
+def test_gelu_values():
+    """GELU(x) = x Phi(x): Phi(1) = 0.8413447460685429 and Phi(-1) =
+    0.15865525393145705 (standard normal table values), GELU(0) = 0, and
+    GELU(x) -> x, -> 0 far out on either side."""
+    x = np.array([0.0, 1.0, -1.0, 40.0, -40.0])
+    want = np.array([0.0, 0.8413447460685429, -0.15865525393145705, 40.0, 0.0])
+    np.testing.assert_allclose(O.gelu(x), want, rtol=0, atol=1e-15)
+
+
+def _deep_case(rng, d=16, sel=0, scale=1e6):
+    """A tiny merged tower output h over two images, and projector weights
+    that make the projector the ReLU of the normed patch at window offset
+    `sel` (merge_w picks it, w1 = scale I, w2 = I / scale): GELU(scale m) /
+    scale -> relu(m) as scale grows."""
+    hw = [(16, 8), (8, 8)]
+    maps = O.plan_maps(hw, 4, 2)
+    h = rng.standard_normal((maps["n_patches"], d)) * 3.0
+    merge_w = np.zeros((d, 4 * d))
+    merge_w[:, sel * d:(sel + 1) * d] = np.eye(d)
+    proj = {"norm": 1.0 + 0.1 * rng.standard_normal(d), "w1": scale * np.eye(d), "w2": np.eye(d) / scale}
+    return h, maps, merge_w, proj
+
+
+def test_deep_projector_reduces_to_relu_of_one_window_patch():
+    rng = np.random.default_rng(40)
+    for sel in range(4):
+        h, maps, merge_w, proj = _deep_case(rng, sel=sel)
+        out = O.deep_project(h, maps["merge_src"], merge_w, proj, 1e-5)
+        # independent statement: the normed patch at window offset sel of
+        # every merged token, then max(., 0)
+        src = maps["merge_src"][:, sel]
+        xs = h[src]
+        y = xs / np.sqrt(np.mean(xs * xs, axis=1, keepdims=True) + 1e-5) * proj["norm"]
+        np.testing.assert_allclose(out, np.maximum(y, 0.0), rtol=0, atol=1e-6)
+
+
+def test_deep_projector_zero_weights_and_order():
+    """w2 = 0 or w1 = 0 gives a zero output; GELU applied after w2 instead of
+    between w1 and w2, or the norm left out, both move the output."""
+    rng = np.random.default_rng(41)
+    h, maps, merge_w, proj = _deep_case(rng, scale=1.0)
+    proj["w1"] = rng.standard_normal(proj["w1"].shape)
+    proj["w2"] = rng.standard_normal(proj["w2"].shape)
+    for k in ("w1", "w2"):
+        p0 = dict(proj)
+        p0[k] = np.zeros_like(proj[k])
+        assert np.array_equal(O.deep_project(h, maps["merge_src"], merge_w, p0, 1e-5), np.zeros((len(maps["merge_src"]), 16)))
+    good = O.deep_project(h, maps["merge_src"], merge_w, proj, 1e-5)
+    m = O.merge_project(O.rms_norm(h, proj["norm"], 1e-5), maps["merge_src"], merge_w)
+    act_after = O.gelu(m @ proj["w1"].T @ proj["w2"].T)
+    no_norm = O.gelu(O.merge_project(h, maps["merge_src"], merge_w) @ proj["w1"].T) @ proj["w2"].T
+    for bad in (act_after, no_norm):
+        assert np.max(np.abs(bad - good)) > 1e-2 * np.max(np.abs(good))
+
+
+def test_tower_with_deep_projector_zero_blocks():
+    """Zero Wo and Wd: the tower output is the deeper projector of
+    ln_pre(patch embedding), with the weights as drawn."""
+    from vlm_vision_encoder_amd import synth
+    wl = synth.Workload("deep", patch=4, layers=1, merge=2, image_hw=((16, 8), (8, 8)), dtype="f32", hidden=16,
+                        heads=1, mlp=32, out_dim=24, deep_projector=True)
+    w = synth.oracle_weights(synth.make_weights(wl))
+    w["layers"][0]["wo"] = np.zeros_like(w["layers"][0]["wo"])
+    w["layers"][0]["w_down"] = np.zeros_like(w["layers"][0]["w_down"])
+    px = np.random.default_rng(42).standard_normal(sum(3 * a * b for a, b in wl.image_hw))
+    cfg = O.TowerConfig(patch=4, hidden=16, heads=1, mlp=32, layers=1, merge=2, out_dim=24, deep_projector=True)
+    got = O.tower_forward(px, wl.image_hw, w, cfg)["out"]
+    maps = O.plan_maps(wl.image_hw, 4, 2)
+    x = np.concatenate([_direct_conv(px[:3 * 128].reshape(3, 16, 8), w["patch_w"], 4),
+                        _direct_conv(px[3 * 128:].reshape(3, 8, 8), w["patch_w"], 4)])
+    h0 = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + 1e-5) * w["ln_pre"]
+    want = O.deep_project(h0, maps["merge_src"], w["merge_w"], w["proj"], 1e-5)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    assert got.shape == (maps["out_rows"], 24)

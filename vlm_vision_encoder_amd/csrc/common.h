@@ -103,7 +103,7 @@ struct DevMaps {
 
 enum AMode { A_DENSE = 0, A_IM2COL = 1, A_MERGE = 2 };
 enum BMode { B_ONE = 0, B_QKV = 1, B_GATEUP = 2 };
-enum EMode { E_STORE = 0, E_STORE_F32 = 1, E_QKV_ROPE = 2, E_SILU_MUL = 3, E_ADD_F32 = 4 };
+enum EMode { E_STORE = 0, E_STORE_F32 = 1, E_QKV_ROPE = 2, E_SILU_MUL = 3, E_ADD_F32 = 4, E_GELU = 5 };
 
 struct GemmArgs {
   int32_t M, N, K;

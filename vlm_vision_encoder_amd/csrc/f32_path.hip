@@ -201,6 +201,8 @@ hipError_t gemm_f32(GemmKind kind, const GemmArgs& g, hipStream_t s) {
     case GEMM_MERGE:  return launch<A_MERGE, B_ONE, E_STORE>(g, s);
     case GEMM_PLAIN:  return launch<A_DENSE, B_ONE, E_STORE>(g, s);
     case GEMM_MERGE_F32: return launch<A_MERGE, B_ONE, E_STORE>(g, s);
+    case GEMM_GELU:
+    case GEMM_PLAIN_F32: return hipErrorInvalidValue;  // the deeper projector is bf16 only
   }
   return hipErrorInvalidValue;
 }

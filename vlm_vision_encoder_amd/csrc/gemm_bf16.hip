@@ -245,6 +245,11 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[
             const float gt = acc[i][2 * jb][v], up = acc[i][2 * jb + 1][v];
             x = gt * up * __builtin_amdgcn_rcpf(1.f + __expf(-gt));
             ocol0 = (n_base + 64 * jb) / 2;
+          } else if constexpr (EM == E_GELU) {
+            // GELU(x) = x Phi(x) = x (1 + erf(x / sqrt 2)) / 2
+            const float a = acc[i][jb][v];
+            x = 0.5f * a * (1.f + erff(a * 0.70710678118654752f));
+            ocol0 = n_base + 32 * jb;
           } else {
             x = acc[i][jb][v];
             ocol0 = n_base + 32 * jb;
@@ -827,6 +832,10 @@ hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
     case GEMM_MERGE_F32:
       return g.N % 256 == 0 ? launch_dense<PV_GEMM_CFG_MERGE, A_MERGE, B_ONE, E_STORE_F32>(g, s)
                             : launch_dense<PV_GEMM_CFG_N1K, A_MERGE, B_ONE, E_STORE_F32>(g, s);
+    case GEMM_GELU:
+      return launch_dense<PV_GEMM_CFG_N1K, A_DENSE, B_ONE, E_GELU>(g, s);
+    case GEMM_PLAIN_F32:
+      return launch_dense<PV_GEMM_CFG_N1K, A_DENSE, B_ONE, E_STORE_F32>(g, s);
   }
   return hipErrorInvalidValue;
 }

@@ -16,7 +16,9 @@ enum GemmKind {
   GEMM_DOWN = 4,    // hm x w_down^T added into the fp32 residual
   GEMM_MERGE = 5,   // gather2x2(residual) x merge_w^T -> bf16 out
   GEMM_PLAIN = 6,   // dense A x B^T -> bf16 (tests and measurement)
-  GEMM_MERGE_F32 = 7  // as GEMM_MERGE with an fp32 output
+  GEMM_MERGE_F32 = 7,  // as GEMM_MERGE with an fp32 output
+  GEMM_GELU = 8,       // dense A x B^T -> bf16 GELU(.) (deeper projector)
+  GEMM_PLAIN_F32 = 9   // dense A x B^T -> fp32
 };
 
 // bf16 MFMA GEMM family (gemm_bf16.hip).

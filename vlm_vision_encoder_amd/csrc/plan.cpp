@@ -137,7 +137,9 @@ int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, P
   if (p.elem_bytes == 2) big_row = std::max(big_row, std::max(size_t(4) * patch_kp(p.patch), 4 * D));
   // fp32 tower from uint8 input: the resized, normalised planes (3 p^2 fp32 per patch)
   if (p.elem_bytes == 4) big_row = std::max(big_row, size_t(12) * p.patch * p.patch);
-  off = align256(off + N * big_row);
+  size_t big_bytes = N * big_row;
+  if (p.deep_out > 0) big_bytes = std::max(big_bytes, size_t(toks) * size_t(p.deep_out) * 2);
+  off = align256(off + big_bytes);
   L.wpad = off;
   off = align256(off + (p.elem_bytes == 2 && !p.prepared ? D * size_t(patch_kp(p.patch)) * 2 : 0));
   if (p.elem_bytes == 2) {

@@ -69,6 +69,9 @@ struct PlanParams {
   // of the block matrices) live in caller memory written once: the workspace
   // then holds no region for them
   bool prepared = false;
+  // deeper projector: its out_dim-wide GELU output ([out_rows][out_dim] bf16)
+  // goes through the big region (0: plain merge)
+  int32_t deep_out = 0;
 };
 
 // Byte offsets of a tower's derived weight copies in the memory that one

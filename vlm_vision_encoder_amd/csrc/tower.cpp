@@ -76,6 +76,7 @@ struct pv_tower {
   pv_config cfg;
   pv_weights w;
   std::vector<pv_layer_weights> layers;
+  pv_projector_weights proj{};  // deeper projector (PV_FLAG_DEEP_PROJECTOR)
   std::vector<float> rope;  // host rotary table
   int32_t rope_maxpos = 0;
   // Staging of the per-call upload: a ring of pinned host buffers, each with
@@ -127,6 +128,7 @@ pv::PlanParams plan_params(const pv_tower* t) {
   p.rope_pairs = 16;
   p.fp8 = (t->cfg.flags & PV_FLAG_FP8) != 0;
   p.prepared = t->prep != nullptr;
+  p.deep_out = (t->cfg.flags & PV_FLAG_DEEP_PROJECTOR) ? t->cfg.out_dim : 0;
   return p;
 }
 
@@ -454,7 +456,32 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
   if (st.stage >= 0) return fail(PV_ERR_ARG, "stage/layer not reached");
 
   const bool out_bf16 = bf && c.out_dtype == PV_BF16;
-  if (c.merge == 2 && bf) {
+  if (c.merge == 2 && bf && (c.flags & PV_FLAG_DEEP_PROJECTOR)) {
+    // deeper projector: RMSNorm (in place, fp32) -> hi | lo copy -> 2x2
+    // gather and 4D -> D (bf16 m in y) -> D -> out_dim with GELU (bf16 a in
+    // big) -> out_dim -> out_dim into out
+    PV_LAUNCH(PV_K_NORM, pv::rmsnorm(r, t->proj.norm, r, N, D, eps, true, s));
+    PV_LAUNCH(PV_K_OPERAND, pv::split_rows(r, big, N, D, s));
+    const int T = int(plan.out_rows), O = c.out_dim;
+    pv::GemmArgs a = g;
+    a.M = T; a.N = D; a.K = 8 * D; a.kb = 4 * D;
+    a.A = big; a.lda = 2 * D;
+    a.B0 = t->w.merge_w; a.ldb = 4 * D;
+    a.C = y; a.ldc = D;
+    PV_LAUNCH(PV_K_MERGE, gemm(pv::GEMM_MERGE, a));
+    pv::GemmArgs b = g;
+    b.M = T; b.N = O; b.K = D;
+    b.A = y; b.lda = D;
+    b.B0 = t->proj.w1; b.ldb = D;
+    b.C = big; b.ldc = O;
+    PV_LAUNCH(PV_K_MERGE, gemm(pv::GEMM_GELU, b));
+    pv::GemmArgs o = g;
+    o.M = T; o.N = O; o.K = O;
+    o.A = big; o.lda = O;
+    o.B0 = t->proj.w2; o.ldb = O;
+    o.C = out; o.ldc = O;
+    PV_LAUNCH(PV_K_MERGE, gemm(out_bf16 ? pv::GEMM_PLAIN : pv::GEMM_PLAIN_F32, o));
+  } else if (c.merge == 2 && bf) {
     // the final residual as bf16 hi | lo rows; the merger's A loads gather
     // the 2x2 groups from that copy
     PV_LAUNCH(PV_K_OPERAND, pv::split_rows(r, big, N, D, s));
@@ -652,8 +679,12 @@ pv_status pv_tower_create(const pv_config* cfg, const pv_weights* w, pv_tower** 
   const pv_config& c = *cfg;
   if (c.dtype != PV_BF16 && c.dtype != PV_F32) return fail(PV_ERR_ARG, "dtype must be PV_BF16 or PV_F32");
   if (c.out_dtype != PV_BF16 && c.out_dtype != PV_F32) return fail(PV_ERR_ARG, "out_dtype must be PV_BF16 or PV_F32");
-  if (c.flags & ~(PV_FLAG_ATTN_ONLINE_MAX | PV_FLAG_FP8)) return fail(PV_ERR_ARG, "unknown bits in flags");
+  if (c.flags & ~(PV_FLAG_ATTN_ONLINE_MAX | PV_FLAG_FP8 | PV_FLAG_DEEP_PROJECTOR))
+    return fail(PV_ERR_ARG, "unknown bits in flags");
   if ((c.flags & PV_FLAG_FP8) && c.dtype != PV_BF16) return fail(PV_ERR_UNSUPPORTED, "PV_FLAG_FP8 needs the bf16 tower");
+  const bool deep = (c.flags & PV_FLAG_DEEP_PROJECTOR) != 0;
+  if (deep && (c.dtype != PV_BF16 || c.merge != 2))
+    return fail(PV_ERR_UNSUPPORTED, "PV_FLAG_DEEP_PROJECTOR needs the bf16 tower with merge == 2");
   if (c.patch < 1 || c.patch > 64) return fail(PV_ERR_ARG, "patch must be in [1, 64]");
   if (c.merge != 1 && c.merge != 2) return fail(PV_ERR_ARG, "merge must be 1 or 2");
   if (c.layers < 0) return fail(PV_ERR_ARG, "layers must be >= 0");
@@ -682,6 +713,12 @@ pv_status pv_tower_create(const pv_config* cfg, const pv_weights* w, pv_tower** 
   }
   if (!aligned(w->ln_pre, 16) || (w->merge_w && !aligned(w->merge_w, 16)) || !aligned(w->patch_w, 4))
     return fail(PV_ERR_ARG, "weights must be 16-byte aligned (patch_w 4-byte)");
+  if (deep) {
+    if (!w->proj || !w->proj->norm || !w->proj->w1 || !w->proj->w2)
+      return fail(PV_ERR_ARG, "PV_FLAG_DEEP_PROJECTOR needs proj weights (norm, w1, w2)");
+    if (!aligned(w->proj->norm, 16) || !aligned(w->proj->w1, 16) || !aligned(w->proj->w2, 16))
+      return fail(PV_ERR_ARG, "projector weights must be 16-byte aligned");
+  }
 
   pv_tower* t = new (std::nothrow) pv_tower();
   if (!t) return fail(PV_ERR_ARG, "out of host memory");
@@ -689,6 +726,8 @@ pv_status pv_tower_create(const pv_config* cfg, const pv_weights* w, pv_tower** 
   t->w = *w;
   if (c.layers > 0) t->layers.assign(w->layers, w->layers + c.layers);
   t->w.layers = t->layers.empty() ? nullptr : t->layers.data();
+  if (deep) t->proj = *w->proj;
+  t->w.proj = deep ? &t->proj : nullptr;
   t->rope_maxpos = std::max(1, c.max_side / c.patch);
   pv::build_rope_table(c.rope_theta, 16, t->rope_maxpos, &t->rope);
   *out = t;

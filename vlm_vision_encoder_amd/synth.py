@@ -39,6 +39,7 @@ class Workload:
     rms_eps: float = 1.0e-5
     tiles_from: Optional[Tuple[int, int]] = None  # (H, W) of the image the tiles are cut from
     note: str = ""
+    deep_projector: bool = False  # the deeper projector variant (merge 2)
 
     @property
     def n_patches(self) -> int:
@@ -108,7 +109,9 @@ def make_weights(wl: Workload, seed: int = SEED_WEIGHTS, layers: Optional[int] =
     their matrices rounded to bf16 (gains stay float32).
 
     Draw order: patch_w, ln_pre, per layer (attn_norm, wq, wk, wv, wo,
-    ffn_norm, w_gate, w_up, w_down), merge_w.
+    ffn_norm, w_gate, w_up, w_down), merge_w; with the deeper projector
+    merge_w is [D][4D] and proj (norm gain, w1 [out_dim][D], w2
+    [out_dim][out_dim]) follows.
     """
     n_layers = wl.layers if layers is None else layers
     rng = np.random.default_rng(seed)
@@ -129,7 +132,10 @@ def make_weights(wl: Workload, seed: int = SEED_WEIGHTS, layers: Optional[int] =
             "ffn_norm": gain(),
             "w_gate": mat(f, d), "w_up": mat(f, d), "w_down": mat(d, f),
         })
-    if wl.merge == 2:
+    if wl.merge == 2 and wl.deep_projector:
+        w["merge_w"] = mat(d, 4 * d)
+        w["proj"] = {"norm": gain(), "w1": mat(wl.out_dim, d), "w2": mat(wl.out_dim, wl.out_dim)}
+    elif wl.merge == 2:
         w["merge_w"] = mat(wl.out_dim, 4 * d)
     return w
 
@@ -178,4 +184,6 @@ def oracle_weights(w: Dict) -> Dict:
            "layers": [{k: v.astype(np.float64) for k, v in lw.items()} for lw in w["layers"]]}
     if "merge_w" in w:
         out["merge_w"] = w["merge_w"].astype(np.float64)
+    if "proj" in w:
+        out["proj"] = {k: v.astype(np.float64) for k, v in w["proj"].items()}
     return out

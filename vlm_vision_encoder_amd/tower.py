@@ -16,6 +16,7 @@ LIB_PATH = os.environ.get("PV_TOWER_LIB") or os.path.join(PKG, "libpv_tower.so")
 PV_BF16, PV_F32 = 0, 1
 PV_FLAG_ATTN_ONLINE_MAX = 1
 PV_FLAG_FP8 = 2
+PV_FLAG_DEEP_PROJECTOR = 4
 STAGES = {"patch_embed": 0, "ln_pre": 1, "qkv": 2, "attn": 3, "attn_resid": 4, "mlp_hidden": 5, "block_out": 6}
 STATUS = {0: "PV_OK", -1: "PV_ERR_ARG", -2: "PV_ERR_SHAPE", -3: "PV_ERR_CAPACITY", -4: "PV_ERR_HIP",
           -5: "PV_ERR_UNSUPPORTED"}
@@ -44,9 +45,13 @@ class PvLayerWeights(C.Structure):
                                           "w_down")]
 
 
+class PvProjectorWeights(C.Structure):
+    _fields_ = [("norm", C.c_void_p), ("w1", C.c_void_p), ("w2", C.c_void_p)]
+
+
 class PvWeights(C.Structure):
     _fields_ = [("patch_w", C.c_void_p), ("ln_pre", C.c_void_p), ("layers", C.POINTER(PvLayerWeights)),
-                ("merge_w", C.c_void_p)]
+                ("merge_w", C.c_void_p), ("proj", C.POINTER(PvProjectorWeights))]
 
 
 class PvPlanInfo(C.Structure):
@@ -218,9 +223,12 @@ class Tower:
               for i in range(cfg.layers)]
         self._layers = (PvLayerWeights * max(1, len(lw)))(*lw)
         mw = weights.get("merge_w")
+        pj = weights.get("proj")
+        self._proj = PvProjectorWeights(pj["norm"].data_ptr(), pj["w1"].data_ptr(), pj["w2"].data_ptr()) if pj else None
         self._w = PvWeights(weights["patch_w"].data_ptr(), weights["ln_pre"].data_ptr(),
                             C.cast(self._layers, C.POINTER(PvLayerWeights)) if lw else None,
-                            mw.data_ptr() if mw is not None else None)
+                            mw.data_ptr() if mw is not None else None,
+                            C.pointer(self._proj) if pj else None)
         h = C.c_void_p()
         _check(self.lib.pv_tower_create(C.byref(cfg), C.byref(self._w), C.byref(h)))
         self.handle = h
@@ -622,4 +630,6 @@ def weights_to_device(w: Dict, dtype: str) -> Dict:
         out["layers"].append({k: (vec(v) if k.endswith("norm") else mat(v)) for k, v in lw.items()})
     if "merge_w" in w:
         out["merge_w"] = mat(w["merge_w"])
+    if "proj" in w:
+        out["proj"] = {"norm": vec(w["proj"]["norm"]), "w1": mat(w["proj"]["w1"]), "w2": mat(w["proj"]["w2"])}
     return out
