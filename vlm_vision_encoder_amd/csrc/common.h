@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "plan.h"
 
@@ -70,8 +71,20 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// ---------------------------------------------------------------------------
-// Device view of the per-call maps (all in the workspace).
+// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
+template <int N, typename F, int I = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>());
+    static_for<N, F, I + 1>(static_cast<F&&>(f));
+  }
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // Power-of-two block scale for fp4 e2m1 (0, 0.5, 1, 1.5, 2, 3, 4, 6):
 // X = floor(log2(max |x|)) - 2 puts the block maximum in [4, 8) (past 6 it
 // saturates); returns the E8M0 byte X + 127 and sets scale = 2^X.  The
@@ -91,6 +104,8 @@ __device__ __forceinline__ uint32_t pack_fp4x4(float a, float b, float c, float 
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, c, d, scale, 1);
 }
 
+// ---------------------------------------------------------------------------
+// Device view of the per-call maps (all in the workspace).
 struct DevMaps {
   const ImageMeta* meta;
   const int32_t* rowinfo;  // [N][2]: image, (row << 16) | col

@@ -44,14 +44,6 @@ __device__ __forceinline__ i32x8 widen4(const u32x4& x) {
   return i32x8{int(x[0]), int(x[1]), int(x[2]), int(x[3]), 0, 0, 0, 0};
 }
 
-template <int N, typename F, int I = 0>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>());
-    static_for<N, F, I + 1>(static_cast<F&&>(f));
-  }
-}
-
 // 16-byte chunk swizzle of LDS tile rows of CH chunks.  The LDS has 64
 // four-byte banks and serves a 16-byte read for 16 lanes (16 consecutive
 // rows) per pass.  CH = 8 (128-byte rows): chunk ^ ((row >> 1) & 7) makes
@@ -270,11 +262,6 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[
     }
   }
 }
-
-// s_waitcnt immediate that waits until at most n vector-memory operations
-// are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
-// lgkmcnt left at their maxima).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // Persistent GEMM (every linear map of the bf16 tower): each
 // workgroup walks a fixed list of output tiles, and the global -> LDS load
