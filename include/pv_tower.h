@@ -113,6 +113,17 @@ typedef struct pv_config {
  * all without bias.  The weights come from pv_weights.merge_w and
  * pv_weights.proj. */
 #define PV_FLAG_DEEP_PROJECTOR 4
+/* pv_config.flags, both dtypes: the other split of the 2-D rotary
+ * frequencies between the axes.  By default both the row pairs (0..15 of a
+ * head) and the column pairs (16..31) turn at omega_m = theta^(-2m/32),
+ * m = 0..15.  With this bit the two axes share one ladder theta^(-j/32),
+ * j = 0..31: rows take the even steps (omega_m = theta^(-2m/32), as by
+ * default) and columns the odd ones (omega_m = theta^(-(2m+1)/32)).  The
+ * pages fix the rotary base ("Mistral 3", Mistral3Model table,
+ * vision_rope_theta) and the row/column split of the pairs, not which
+ * ladder steps each axis takes; only the host-built rotation table
+ * changes. */
+#define PV_FLAG_ROPE_INTERLEAVED 8
 
 /* Per-block weights: borrowed device pointers, row-major, "out x in" like a
  * linear layer (y = x W^T).  Gains are always fp32; matrices use cfg.dtype. */

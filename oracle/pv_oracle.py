@@ -98,6 +98,7 @@ class TowerConfig:
     rope_theta: float = 1.0e4
     rms_eps: float = 1.0e-5
     deep_projector: bool = False  # reading 14: the deeper projector variant
+    rope_interleaved: bool = False  # reading 3: columns on the odd ladder steps
 
     @property
     def head_dim(self) -> int:
@@ -207,9 +208,21 @@ def rope_omega(head_dim: int, theta: float) -> np.ndarray:
     return np.power(float(theta), -2.0 * m / (head_dim / 2.0))
 
 
-def rope_2d(x: np.ndarray, patch_rc: np.ndarray, heads: int, theta: float) -> np.ndarray:
+def rope_axis_omegas(head_dim: int, theta: float, interleaved: bool = False):
+    """(row, column) frequency ladders.  Default (reading 3): both axes
+    omega_m = theta^(-2m/(head_dim/2)).  interleaved: the axes share one
+    ladder theta^(-j/(head_dim/2)), j = 0..head_dim/2-1, rows on the even
+    steps j = 2m and columns on the odd steps j = 2m + 1."""
+    rows = rope_omega(head_dim, theta)
+    if not interleaved:
+        return rows, rows.copy()
+    m = np.arange(head_dim // 4, dtype=np.float64)
+    return rows, np.power(float(theta), -(2.0 * m + 1.0) / (head_dim / 2.0))
+
+
+def rope_2d(x: np.ndarray, patch_rc: np.ndarray, heads: int, theta: float, interleaved: bool = False) -> np.ndarray:
     """Rotate every head's adjacent pairs (2j, 2j+1) by the patch's row (first
-    half of the pairs) or column (second half) times omega.
+    half of the pairs) or column (second half) times that axis's omega.
 
     "Mistral 3", Mistral3VisionModel (2-D rotary blocks).
     (x0, x1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a).
@@ -217,9 +230,9 @@ def rope_2d(x: np.ndarray, patch_rc: np.ndarray, heads: int, theta: float) -> np
     x = np.asarray(x, dtype=np.float64)
     n, width = x.shape
     dh = width // heads
-    om = rope_omega(dh, theta)
+    om_r, om_c = rope_axis_omegas(dh, theta, interleaved)
     rc = np.asarray(patch_rc, dtype=np.float64)
-    ang = np.concatenate([rc[:, 0:1] * om[None, :], rc[:, 1:2] * om[None, :]], axis=1)  # [n, dh/2]
+    ang = np.concatenate([rc[:, 0:1] * om_r[None, :], rc[:, 1:2] * om_c[None, :]], axis=1)  # [n, dh/2]
     cos = np.cos(ang)[:, None, :]
     sin = np.sin(ang)[:, None, :]
     xp = x.reshape(n, heads, dh // 2, 2)
@@ -615,8 +628,8 @@ def tower_forward(
         lw = weights["layers"][li]
         W = {k_: qz(np.asarray(lw[k_], np.float64)) for k_ in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")}
         y = qz(rms_norm(h, lw["attn_norm"], cfg.rms_eps))
-        q = rope_2d(y @ W["wq"].T, rc, cfg.heads, cfg.rope_theta)
-        k = rope_2d(y @ W["wk"].T, rc, cfg.heads, cfg.rope_theta)
+        q = rope_2d(y @ W["wq"].T, rc, cfg.heads, cfg.rope_theta, cfg.rope_interleaved)
+        k = rope_2d(y @ W["wk"].T, rc, cfg.heads, cfg.rope_theta, cfg.rope_interleaved)
         v = y @ W["wv"].T
         a = attention(q, k, v, cu, cfg.heads)
         h = h + qz(a) @ W["wo"].T

@@ -68,6 +68,9 @@ def create(cfg, layers_present=True):
     (dict(flags=4), -1),
     (dict(flags=2), 0),
     (dict(flags=1), 0),
+    (dict(flags=8), 0),               # PV_FLAG_ROPE_INTERLEAVED
+    (dict(flags=8, dtype=1), 0),
+    (dict(flags=16), -1),             # unknown bit
     (dict(rope_theta=0.0), -1),
 ])
 def test_create_validation(kw, status):
@@ -453,7 +456,7 @@ def test_fp8_flag_validation_and_workspace():
     lib = T.load_library()
     st, h, _ = create(T.make_config(layers=2, dtype="f32", flags=T.PV_FLAG_FP8))
     assert st == -5
-    st, h, _ = create(T.make_config(layers=2, flags=8))
+    st, h, _ = create(T.make_config(layers=2, flags=16))
     assert st == -1
     st, h8, _ = create(T.make_config(layers=2, flags=T.PV_FLAG_FP8))
     st2, hb, _ = create(T.make_config(layers=2))

@@ -33,7 +33,7 @@ def say(msg):
 def oracle_cfg(wl, layers=None):
     return O.TowerConfig(patch=wl.patch, hidden=wl.hidden, heads=wl.heads, mlp=wl.mlp,
                          layers=wl.layers if layers is None else layers, merge=wl.merge, out_dim=wl.out_dim,
-                         rope_theta=wl.rope_theta, rms_eps=wl.rms_eps)
+                         rope_theta=wl.rope_theta, rms_eps=wl.rms_eps, rope_interleaved=wl.rope_interleaved)
 
 
 def rel_err(got, want):
@@ -129,8 +129,8 @@ def oracle_stage(ref, wl, name, layer, w):
     maps = ref["maps"]
     if name in ("qkv", "attn"):
         y = O.rms_norm(h, lw["attn_norm"], wl.rms_eps)
-        q = O.rope_2d(y @ lw["wq"].T, maps["patch_rc"], wl.heads, wl.rope_theta)
-        k = O.rope_2d(y @ lw["wk"].T, maps["patch_rc"], wl.heads, wl.rope_theta)
+        q = O.rope_2d(y @ lw["wq"].T, maps["patch_rc"], wl.heads, wl.rope_theta, wl.rope_interleaved)
+        k = O.rope_2d(y @ lw["wk"].T, maps["patch_rc"], wl.heads, wl.rope_theta, wl.rope_interleaved)
         v = y @ lw["wv"].T
         if name == "qkv":
             # the bf16 tower stores q in its softmax's exp2 units
@@ -361,6 +361,35 @@ def test_bf16_wide_attention_items(image_hw):
     torch.cuda.synchronize()
     check_per_image("attn[0] online max", att, want, cu, TOL["bf16"], stored_bf16=True)
     check("out", to_np(c.run()), ref["out"], TOL["bf16"], stored_bf16=True)
+    tw.close()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rope_interleaved_flag(dtype):
+    """PV_FLAG_ROPE_INTERLEAVED: the column rotary pairs on the odd steps of
+    one ladder shared with the rows.  q,k,v of layer 0 and the output of a
+    one-block tower against the oracle with the same split, on a non-square
+    image beside a small one; the default tower's q,k,v differ from it."""
+    import torch
+    base = synth.workload("tiny") if dtype == "f32" else synth.workload("ms31_1540")
+    wl = base.with_(name="rope-interleaved", image_hw=((224, 336), (112, 56)), layers=1, mlp=1024,
+                    rope_interleaved=True)
+    say(f"{dtype} interleaved rotary ladder {wl.image_hw}")
+    c = Case(wl)  # its own tower keeps the default split
+    tw = T.Tower(T.config_for(wl, flags=T.PV_FLAG_ROPE_INTERLEAVED), c.dev_w)
+    ref = c.ref()
+    stored = dtype == "bf16"
+    want = oracle_stage(ref, wl, "qkv", 0, c.w)
+    got = to_np(tw.forward_stage(c.pix, wl.image_hw, "qkv", 0))
+    torch.cuda.synchronize()
+    check("qkv[0]", got, want, TOL[dtype], stored_bf16=stored)
+    out = to_np(tw.forward(c.pix, wl.image_hw))
+    torch.cuda.synchronize()
+    check("out", out, ref["out"], TOL[dtype], stored_bf16=stored)
+    dflt = to_np(c.stage("qkv", 0))
+    moved = float(np.max(np.abs(dflt - got)) / np.sqrt(np.mean(want * want)))
+    say(f"  default split moves qkv by {moved:.3e} of RMS")
+    assert moved > 0.1
     tw.close()
 
 

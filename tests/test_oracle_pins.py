@@ -208,6 +208,82 @@ def test_rope_relative_offset_invariance_and_composition():
     np.testing.assert_allclose(two, one, rtol=1e-12, atol=1e-12)
 
 
+# The interleaved split (PV_FLAG_ROPE_INTERLEAVED): one ladder shared by the
+# two axes, rows on its even steps and columns on its odd steps.
+def _rope_complex_one_ladder(x, r, c, heads, theta):
+    """Complex form of the interleaved split.  The ladder of dh/2 steps
+    theta^(-j/(dh/2)) is built by repeated multiplication; row pair m of a
+    head takes step 2m, column pair m step 2m + 1."""
+    dh = x.shape[0] // heads
+    per_axis = dh // 4
+    step = theta ** (-1.0 / (dh / 2))
+    ladder = [1.0]
+    for _ in range(dh // 2 - 1):
+        ladder.append(ladder[-1] * step)
+    out = np.empty_like(x)
+    for h in range(heads):
+        for j in range(dh // 2):
+            if j < per_axis:
+                omega, pos = ladder[2 * j], r
+            else:
+                omega, pos = ladder[2 * (j - per_axis) + 1], c
+            z = complex(x[h * dh + 2 * j], x[h * dh + 2 * j + 1]) * complex(math.cos(pos * omega), math.sin(pos * omega))
+            out[h * dh + 2 * j] = z.real
+            out[h * dh + 2 * j + 1] = z.imag
+    return out
+
+
+def test_rope_interleaved_matches_one_ladder_complex_form():
+    rng = np.random.default_rng(15)
+    heads = 2
+    x = rng.standard_normal((4, heads * 64))
+    rc = np.array([[0, 0], [3, 7], [109, 1], [12, 109]])
+    got = O.rope_2d(x, rc, heads, 1e4, interleaved=True)
+    for i in range(4):
+        np.testing.assert_allclose(got[i], _rope_complex_one_ladder(x[i], rc[i, 0], rc[i, 1], heads, 1e4),
+                                   rtol=1e-11, atol=1e-11)
+    # and it is not the default split (the columns differ)
+    assert np.max(np.abs(got - O.rope_2d(x, rc, heads, 1e4))) > 0.1
+
+
+def test_rope_interleaved_rows_as_default_columns_at_scaled_positions():
+    """Rows turn exactly as in the default split; a column position c turns
+    like the default split's column position c * theta^(-1/32) (each column
+    frequency is one ladder step below the default's); together the two axes
+    cover the whole ladder once."""
+    rng = np.random.default_rng(16)
+    x = rng.standard_normal((3, 128))
+    rows = np.array([[5, 0], [77, 0], [1, 0]])
+    np.testing.assert_array_equal(O.rope_2d(x, rows, 2, 1e4, interleaved=True), O.rope_2d(x, rows, 2, 1e4))
+    cols = np.array([[0, 5], [0, 77], [0, 1]], dtype=np.float64)
+    scaled = cols * np.array([1.0, 1e4 ** (-1.0 / 32.0)])
+    np.testing.assert_allclose(O.rope_2d(x, cols, 2, 1e4, interleaved=True), O.rope_2d(x, scaled, 2, 1e4),
+                               rtol=1e-12, atol=1e-12)
+    om_r, om_c = O.rope_axis_omegas(64, 1e4, interleaved=True)
+    both = np.sort(np.concatenate([om_r, om_c]))[::-1]
+    np.testing.assert_allclose(both[1:] / both[:-1], 1e4 ** (-1.0 / 32.0), rtol=1e-12)
+    assert both[0] == 1.0
+
+
+def test_rope_interleaved_relative_offset_invariance_per_axis():
+    rng = np.random.default_rng(17)
+    q = rng.standard_normal((1, 64))
+    k = rng.standard_normal((1, 64))
+
+    def dot(p1, p2):
+        return np.dot(O.rope_2d(q, np.array([p1]), 1, 1e4, interleaved=True)[0],
+                      O.rope_2d(k, np.array([p2]), 1, 1e4, interleaved=True)[0])
+
+    for axis in (0, 1):
+        for (p1, p2, d) in [((3, 5), (10, 2), 4), ((0, 0), (7, 7), 50)]:
+            s1, s2 = list(p1), list(p2)
+            s1[axis] += d
+            s2[axis] += d
+            np.testing.assert_allclose(dot(p1, p2), dot(tuple(s1), tuple(s2)), rtol=1e-10)
+    two = O.rope_2d(O.rope_2d(q, np.array([[2, 3]]), 1, 1e4, True), np.array([[5, 11]]), 1, 1e4, True)
+    np.testing.assert_allclose(two, O.rope_2d(q, np.array([[7, 14]]), 1, 1e4, True), rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------- attention
 def _dense_masked_attention(q, k, v, cu, heads):
     """Textbook softmax over the whole packed sequence with -inf outside each

@@ -298,12 +298,15 @@ void host_index_maps(const Plan& pl, int merge, int32_t* cu, int32_t* rc, int32_
   }
 }
 
-void build_rope_table(double theta, int32_t pairs, int32_t maxpos, std::vector<float>* out) {
+void build_rope_table(double theta, int32_t pairs, int32_t maxpos, bool interleaved, std::vector<float>* out) {
   out->assign(size_t(2) * 2 * maxpos * pairs, 0.f);
   for (int axis = 0; axis < 2; ++axis)
     for (int32_t pos = 0; pos < maxpos; ++pos)
       for (int32_t m = 0; m < pairs; ++m) {
-        const double omega = std::pow(theta, -2.0 * m / (2.0 * pairs));
+        // step j of the ladder theta^(-j / (2 pairs)): 2m on both axes, or 2m
+        // on rows and 2m + 1 on columns (interleaved)
+        const int j = 2 * m + (interleaved && axis == 1 ? 1 : 0);
+        const double omega = std::pow(theta, -double(j) / (2.0 * pairs));
         const double a = double(pos) * omega;
         const size_t idx = ((size_t(axis) * maxpos + pos) * pairs + m) * 2;
         (*out)[idx] = float(std::cos(a));

@@ -158,7 +158,8 @@ void host_index_maps(const Plan& plan, int merge, int32_t* cu_seqlens, int32_t* 
 
 // Rotary cos/sin table, built in double and rounded to float:
 // table[((axis * maxpos) + pos) * pairs + m] = (cos, sin)(pos * omega_m),
-// omega_m = theta^(-2m / (2 * pairs)), axis 0 = patch row, 1 = patch column.
-void build_rope_table(double theta, int32_t pairs, int32_t maxpos, std::vector<float>* out);
+// omega_m = theta^(-2m / (2 * pairs)), axis 0 = patch row, 1 = patch column;
+// interleaved: columns take omega_m = theta^(-(2m + 1) / (2 * pairs)).
+void build_rope_table(double theta, int32_t pairs, int32_t maxpos, bool interleaved, std::vector<float>* out);
 
 }  // namespace pv

@@ -679,7 +679,7 @@ pv_status pv_tower_create(const pv_config* cfg, const pv_weights* w, pv_tower** 
   const pv_config& c = *cfg;
   if (c.dtype != PV_BF16 && c.dtype != PV_F32) return fail(PV_ERR_ARG, "dtype must be PV_BF16 or PV_F32");
   if (c.out_dtype != PV_BF16 && c.out_dtype != PV_F32) return fail(PV_ERR_ARG, "out_dtype must be PV_BF16 or PV_F32");
-  if (c.flags & ~(PV_FLAG_ATTN_ONLINE_MAX | PV_FLAG_FP8 | PV_FLAG_DEEP_PROJECTOR))
+  if (c.flags & ~(PV_FLAG_ATTN_ONLINE_MAX | PV_FLAG_FP8 | PV_FLAG_DEEP_PROJECTOR | PV_FLAG_ROPE_INTERLEAVED))
     return fail(PV_ERR_ARG, "unknown bits in flags");
   if ((c.flags & PV_FLAG_FP8) && c.dtype != PV_BF16) return fail(PV_ERR_UNSUPPORTED, "PV_FLAG_FP8 needs the bf16 tower");
   const bool deep = (c.flags & PV_FLAG_DEEP_PROJECTOR) != 0;
@@ -729,7 +729,7 @@ pv_status pv_tower_create(const pv_config* cfg, const pv_weights* w, pv_tower** 
   if (deep) t->proj = *w->proj;
   t->w.proj = deep ? &t->proj : nullptr;
   t->rope_maxpos = std::max(1, c.max_side / c.patch);
-  pv::build_rope_table(c.rope_theta, 16, t->rope_maxpos, &t->rope);
+  pv::build_rope_table(c.rope_theta, 16, t->rope_maxpos, (c.flags & PV_FLAG_ROPE_INTERLEAVED) != 0, &t->rope);
   *out = t;
   return PV_OK;
 }

@@ -40,6 +40,7 @@ class Workload:
     tiles_from: Optional[Tuple[int, int]] = None  # (H, W) of the image the tiles are cut from
     note: str = ""
     deep_projector: bool = False  # the deeper projector variant (merge 2)
+    rope_interleaved: bool = False  # rotary columns on the odd steps of one ladder
 
     @property
     def n_patches(self) -> int:

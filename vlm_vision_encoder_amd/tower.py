@@ -17,6 +17,7 @@ PV_BF16, PV_F32 = 0, 1
 PV_FLAG_ATTN_ONLINE_MAX = 1
 PV_FLAG_FP8 = 2
 PV_FLAG_DEEP_PROJECTOR = 4
+PV_FLAG_ROPE_INTERLEAVED = 8
 STAGES = {"patch_embed": 0, "ln_pre": 1, "qkv": 2, "attn": 3, "attn_resid": 4, "mlp_hidden": 5, "block_out": 6}
 STATUS = {0: "PV_OK", -1: "PV_ERR_ARG", -2: "PV_ERR_SHAPE", -3: "PV_ERR_CAPACITY", -4: "PV_ERR_HIP",
           -5: "PV_ERR_UNSUPPORTED"}
