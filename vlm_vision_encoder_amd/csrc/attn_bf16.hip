@@ -170,12 +170,22 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[tb][ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
   }
-  // offset operands of the 65th score dimension: dimension 64 of every key
-  // is 1 and dimension 64 of query t is -m0(t) (lane half 0, element 0)
+  // The fixed offset -m0 enters the scores of later tiles in one of two
+  // ways.  8-wave items (128 registers): as a 65th score dimension, one more
+  // MFMA per tile -- dimension 64 of every key is 1 and dimension 64 of
+  // query t is -m0(t) (lane half 0, element 0).  12-wave items (168
+  // registers): as the initial accumulator of the score MFMAs -- a lane's 16
+  // scores all belong to its one query column, so -m0 replicated in 16
+  // registers, set once after the first tile, serves every later tile (the
+  // MFMAs see the same operands, so the scores are the same bits).
+  constexpr bool kAccOffset = WAVES > 8;
   const u32x4 a_off = {lhalf == 0 ? 0x3F80u : 0u, 0u, 0u, 0u};
   u32x4 q_off[QB];
+  floatx16 c_off[kAccOffset ? QB : 1];
 #pragma unroll
   for (int tb = 0; tb < QB; ++tb) q_off[tb] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int tb = 0; tb < (kAccOffset ? QB : 1); ++tb) c_off[tb] = floatx16{};
 
   // transposed-read addresses for the V^T fragments: 16-lane group g gets
   // dims D0 + (lane % 16), keys U..U+3 (and U+4..U+7 from the second read)
@@ -200,7 +210,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
       for (int tb = 0; tb < QB; ++tb) {
         const floatx16 z = {};
-        if constexpr (MODE == 1) s[ub][tb] = mfma32x32x16(a_off, q_off[tb], z);
+        if constexpr (MODE == 1 && kAccOffset) s[ub][tb] = c_off[kAccOffset ? tb : 0];
+        else if constexpr (MODE == 1) s[ub][tb] = mfma32x32x16(a_off, q_off[tb], z);
         else s[ub][tb] = z;
       }
 #pragma unroll
@@ -244,6 +255,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
           const uint32_t mb = pack_bf16x2(-mx, 0.f) & 0xffffu;
           q_off[tb] = u32x4{lhalf == 0 ? mb : 0u, 0u, 0u, 0u};
           sub = lo_bf16(mb);
+          if constexpr (kAccOffset) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) c_off[tb][v] = sub;
+          }
         } else {
           if (__any(mx > m_sc[tb] + kRescaleSlack)) {
             const float m_new = fmaxf(m_sc[tb], mx);
