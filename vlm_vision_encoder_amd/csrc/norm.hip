@@ -14,12 +14,25 @@ namespace pv {
 
 namespace {
 
+// Sum over the 64 lanes, in every lane: DPP moves inside each 16-lane row
+// (quad permutes [1,0,3,2] and [2,3,0,1], half-row mirror, row mirror: no
+// LDS traffic, a few cycles each), then two lane exchanges across rows.
+__device__ __forceinline__ float row_sum64(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
 template <int NC>
 __device__ __forceinline__ float sumsq(const floatx4 (&v)[NC]) {
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < NC; ++i) s += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
-  return wave_sum(s);
+  return row_sum64(s);
 }
 
 template <int NC, bool YF32>
@@ -60,6 +73,26 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 // The MLP input: y = norm(x) * g as bf16 hi [N][D], and its low part y - hi
 // as packed fp4 [N][D/2] (low nibble = even column) with one scale byte per
 // 32 columns, scale bytes step-major: ys[(col / 256) * srows + row][(col / 32) % 8].
+// Maximum over the 8 lanes of v's aligned 8-lane group, by DPP moves (no
+// LDS traffic): quad permutes [1,0,3,2] and [2,3,0,1], then the half-row
+// mirror (lane i of 8 takes lane 7 - i, pairing the two quads).
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true)));
+  return v;
+}
+
+// Four consecutive 32-column scale bytes (lanes 8b..8b+7 hold block b's
+// byte) combined into one little-endian word, valid in lanes 0 and 32 (and
+// every lane of their 32-lane half).
+__device__ __forceinline__ uint32_t scale_word(uint32_t sbyte, int lane) {
+  uint32_t w = (sbyte & 0xffu) << (8 * ((lane >> 3) & 3));
+  w |= uint32_t(__builtin_amdgcn_mov_dpp(int(w), 0x128, 0xF, 0xF, true));  // row_ror:8 (lane ^ 8 in a 16-lane row)
+  w |= uint32_t(__shfl_xor(int(w), 16, 64));
+  return w;
+}
+
 template <int NC>
 __global__ __launch_bounds__(256) void rmsnorm_hi_lo4_kernel(const float* __restrict__ x, const float* __restrict__ g,
                                                              uint16_t* __restrict__ yh, uint8_t* __restrict__ y4,
@@ -85,17 +118,14 @@ __global__ __launch_bounds__(256) void rmsnorm_hi_lo4_kernel(const float* __rest
     const float l0 = v[i][0] - lo_bf16(hi[0]), l1 = v[i][1] - hi_bf16(hi[0]);
     const float l2 = v[i][2] - lo_bf16(hi[1]), l3 = v[i][3] - hi_bf16(hi[1]);
     // block of 32 columns = 8 consecutive lanes
-    float amax = fmaxf(fmaxf(fabsf(l0), fabsf(l1)), fmaxf(fabsf(l2), fabsf(l3)));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+    const float amax = max8(fmaxf(fmaxf(fabsf(l0), fabsf(l1)), fmaxf(fabsf(l2), fabsf(l3))));
     float scale;
     const uint32_t sbyte = mx_scale4(amax, scale);
     *reinterpret_cast<uint16_t*>(y4 + size_t(row) * (D / 2) + col / 2) = uint16_t(pack_fp4x4(l0, l1, l2, l3, scale));
-    if ((lane & 7) == 0) {
-      const int blk = col / 32;
-      ys[(size_t(blk / 8) * srows + row) * 8 + (blk & 7)] = uint8_t(sbyte);
-    }
+    // the 8 scale bytes of this 256-column step (block b = lanes 8b..8b+7)
+    // as two 4-byte words, written by lanes 0 and 32
+    const uint32_t w = scale_word(sbyte, lane);
+    if ((lane & 31) == 0) *reinterpret_cast<uint32_t*>(ys + (size_t(i) * srows + row) * 8 + (lane >> 3)) = w;
   }
 }
 
@@ -119,18 +149,15 @@ __global__ __launch_bounds__(256) void rmsnorm_fp8_kernel(const float* __restric
   for (int i = 0; i < NC; ++i) {
     v[i] = v[i] * inv * gr[i * 64 + lane];
     const int col = (i * 64 + lane) * 4;
-    float amax = fmaxf(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])), fmaxf(fabsf(v[i][2]), fabsf(v[i][3])));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+    const float amax = max8(fmaxf(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])), fmaxf(fabsf(v[i][2]), fabsf(v[i][3]))));
     float mul;
     const uint32_t sbyte = mx_scale(amax, mul);
     *reinterpret_cast<uint32_t*>(y8 + size_t(row) * D + col) =
         pack_fp8x4(v[i][0] * mul, v[i][1] * mul, v[i][2] * mul, v[i][3] * mul);
-    if ((lane & 7) == 0) {
-      const int blk = col / 32;
-      ys[(size_t(blk / 4) * srows + row) * 4 + (blk & 3)] = uint8_t(sbyte);
-    }
+    // the 4 scale bytes of each 128-column step as one word: lanes 0-31
+    // hold step 2i, lanes 32-63 step 2i + 1
+    const uint32_t w = scale_word(sbyte, lane);
+    if ((lane & 31) == 0) *reinterpret_cast<uint32_t*>(ys + (size_t(2 * i + (lane >> 5)) * srows + row) * 4) = w;
   }
 }
 

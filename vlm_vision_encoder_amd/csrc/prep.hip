@@ -85,9 +85,18 @@ __device__ __forceinline__ float sample_u8(const uint8_t* __restrict__ img, uint
 // pixel column of the workgroup's patches (16 p <= 256), so patches of up to
 // 16 pixels use it (K <= 768 fits the stride); larger ones take the
 // per-thread kernel below.
-constexpr int kStagePatches = 16;
+#ifndef PV_STAGE_PATCHES
+#define PV_STAGE_PATCHES 16
+#endif
+#ifndef PV_STAGE_THREADS
+#define PV_STAGE_THREADS 256
+#endif
+#ifndef PV_STAGE_WG_PER_CU
+#define PV_STAGE_WG_PER_CU 2
+#endif
+constexpr int kStagePatches = PV_STAGE_PATCHES;
 constexpr int kStageStride = 1040;  // floats, any patch up to 16 pixels; consecutive patches 16 banks apart
-constexpr int kStageThreads = 256;
+constexpr int kStageThreads = PV_STAGE_THREADS;
 // per-patch LDS stride for a compile-time patch edge: K rounded up to 8, plus
 // an offset that moves consecutive patches to other banks (P = 14: 600 floats,
 // 24 banks apart; P = 16: 776, 8 apart), so that 4 (P = 14) or 3 (P = 16)
@@ -99,78 +108,103 @@ constexpr int stage_stride() {
 
 // P: the patch edge as a compile-time constant (its 3 P loads of a thread are
 // all issued before the LDS stores), or 0 (maps.patch, a loop).
+//
+// Persistent over chunks of kStagePatches patches (workgroup b takes chunks
+// b, b + gridDim.x, ...): the pixels of a workgroup's next chunk are loaded
+// into registers while it writes the current chunk's rows, so the reads of
+// one chunk overlap the stores of the one before (a launch with one
+// workgroup per chunk does all its reads, then all its writes).
 template <int P>
 __global__ __launch_bounds__(kStageThreads) void im2col_staged_kernel(const float* __restrict__ pixels, DevMaps maps,
                                                                       uint16_t* __restrict__ out, int n_patches,
                                                                       int K, int Kp) {
   constexpr int SS = stage_stride<P>();
+  constexpr int NV = P > 0 ? 3 * P : 1;  // pixels a thread holds for the next chunk (P > 0)
   static_assert(P == 0 || SS >= 3 * P * P, "stage stride below K");
   __shared__ __attribute__((aligned(16))) float stage[kStagePatches * SS];
-  __shared__ long long q_base[kStagePatches];  // element offset of the patch's first pixel (channel 0)
-  __shared__ long long q_plane[kStagePatches];  // H * W of its image
-  __shared__ int q_w[kStagePatches];            // W of its image
-  const int g0 = blockIdx.x * kStagePatches;
-  const int np = n_patches - g0 < kStagePatches ? n_patches - g0 : kStagePatches;
   const int p = P > 0 ? P : maps.patch, pp = p * p;
   const int t = threadIdx.x;
-  if (t < np) {
-    const int g = g0 + t;
+  const int n_chunks = (n_patches + kStagePatches - 1) / kStagePatches;
+  // thread t owns pixel x of patch q in every (c, u) row of a chunk
+  const int q = t / p, x = t - q * p;
+  // pointer to pixel x of row 0, channel 0 of patch q of chunk c, its
+  // image's plane size and width; false if the chunk has no such patch
+  auto locate = [&](int c, const float*& src, long long& plane, int& w) {
+    const int g = c * kStagePatches + q;
+    if (q >= kStagePatches || g >= n_patches) return false;
     const int img = maps.rowinfo[2 * g], rc = maps.rowinfo[2 * g + 1];
     const ImageMeta mt = maps.meta[img];
-    q_base[t] = pix_offset(mt) + (long long)((rc >> 16) * p) * mt.W + (rc & 0xffff) * p;
-    q_plane[t] = (long long)mt.H * mt.W;
-    q_w[t] = mt.W;
+    src = pixels + pix_offset(mt) + (long long)((rc >> 16) * p) * mt.W + (rc & 0xffff) * p + x;
+    plane = (long long)mt.H * mt.W;
+    w = mt.W;
+    return true;
+  };
+  float v[NV];
+  auto load = [&](int c) {  // P > 0: the chunk's pixels of this thread into v
+    const float* src;
+    long long plane;
+    int w;
+    if (!locate(c, src, plane, w)) return;
+#pragma unroll
+    for (int cc = 0; cc < 3; ++cc)
+#pragma unroll
+      for (int u = 0; u < P; ++u) v[cc * P + u] = src[cc * plane + (long long)u * w];
+  };
+  int c = blockIdx.x;
+  if constexpr (P > 0) {
+    if (c < n_chunks) load(c);
   }
-  __syncthreads();
-  // phase 1: thread t owns pixel x of patch q in every (c, u) row
-  if (t < np * p) {
-    const int q = t / p, x = t - q * p;
-    const float* src = pixels + q_base[q] + x;
-    const long long plane = q_plane[q];
-    const int w = q_w[q];
-    float* dst = stage + q * SS + x;
-    if constexpr (P > 0) {
-      float v[3 * P];
+  for (; c < n_chunks; c += gridDim.x) {
+    const int g0 = c * kStagePatches;
+    const int np = n_patches - g0 < kStagePatches ? n_patches - g0 : kStagePatches;
+    __syncthreads();  // the previous chunk's rows are read out of the stage
+    if (q < np) {
+      float* dst = stage + q * SS + x;
+      if constexpr (P > 0) {
 #pragma unroll
-      for (int c = 0; c < 3; ++c)
+        for (int cc = 0; cc < 3; ++cc)
 #pragma unroll
-        for (int u = 0; u < P; ++u) v[c * P + u] = src[c * plane + (long long)u * w];
-#pragma unroll
-      for (int c = 0; c < 3; ++c)
-#pragma unroll
-        for (int u = 0; u < P; ++u) dst[c * P * P + u * P] = v[c * P + u];
-    } else {
-      for (int c = 0; c < 3; ++c) {
-        const float* sc = src + c * plane;
-        float* dc = dst + c * pp;
+          for (int u = 0; u < P; ++u) dst[cc * P * P + u * P] = v[cc * P + u];
+      } else {
+        const float* src;
+        long long plane;
+        int w;
+        locate(c, src, plane, w);
+        for (int cc = 0; cc < 3; ++cc) {
+          const float* sc = src + cc * plane;
+          float* dc = dst + cc * pp;
 #pragma unroll 7
-        for (int u = 0; u < p; ++u) dc[u * p] = sc[(long long)u * w];
+          for (int u = 0; u < p; ++u) dc[u * p] = sc[(long long)u * w];
+        }
       }
     }
-  }
-  __syncthreads();
-  // phase 2: (patch, 8 k) chunks
-  const int chunks = Kp / 8;
-  for (int f = t; f < np * chunks; f += kStageThreads) {
-    const int q = f / chunks, k0 = (f - q * chunks) * 8;
-    float v[8];
-    if (k0 + 8 <= K) {
-      const floatx4 a = *reinterpret_cast<const floatx4*>(stage + q * SS + k0);
-      const floatx4 b = *reinterpret_cast<const floatx4*>(stage + q * SS + k0 + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = a[e];
-        v[4 + e] = b[e];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = k0 + e < K ? stage[q * SS + k0 + e] : 0.f;
+    __syncthreads();
+    if constexpr (P > 0) {
+      if (c + gridDim.x < n_chunks) load(c + gridDim.x);  // in flight during the writes below
     }
-    u32x4 hi, lo;
-    split8(v, hi, lo);
-    uint16_t* row = out + size_t(g0 + q) * 2 * Kp;
-    *reinterpret_cast<u32x4*>(row + k0) = hi;
-    *reinterpret_cast<u32x4*>(row + Kp + k0) = lo;
+    // (patch, 8 k) chunks of the rows
+    const int chunks = Kp / 8;
+    for (int f = t; f < np * chunks; f += kStageThreads) {
+      const int qq = f / chunks, k0 = (f - qq * chunks) * 8;
+      float e8[8];
+      if (k0 + 8 <= K) {
+        const floatx4 a = *reinterpret_cast<const floatx4*>(stage + qq * SS + k0);
+        const floatx4 b = *reinterpret_cast<const floatx4*>(stage + qq * SS + k0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          e8[e] = a[e];
+          e8[4 + e] = b[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) e8[e] = k0 + e < K ? stage[qq * SS + k0 + e] : 0.f;
+      }
+      u32x4 hi, lo;
+      split8(e8, hi, lo);
+      uint16_t* row = out + size_t(g0 + qq) * 2 * Kp;
+      *reinterpret_cast<u32x4*>(row + k0) = hi;
+      *reinterpret_cast<u32x4*>(row + Kp + k0) = lo;
+    }
   }
 }
 
@@ -389,7 +423,11 @@ hipError_t im2col_split(const float* pixels, const DevMaps& maps, void* out, int
   if (n_patches <= 0) return hipSuccess;
   if (Kp % 8 || K > Kp) return hipErrorInvalidValue;
   if (K <= kStageStride && K == 3 * maps.patch * maps.patch && kStagePatches * maps.patch <= kStageThreads) {
-    const dim3 grid((n_patches + kStagePatches - 1) / kStagePatches), block(kStageThreads);
+    // PV_STAGE_WG_PER_CU workgroups per CU (each then takes several chunks),
+    // or one per chunk (0)
+    const int n_chunks = (n_patches + kStagePatches - 1) / kStagePatches;
+    const int cap = PV_STAGE_WG_PER_CU > 0 ? PV_STAGE_WG_PER_CU * kNumCUs : n_chunks;
+    const dim3 grid(n_chunks < cap ? n_chunks : cap), block(kStageThreads);
     uint16_t* o = static_cast<uint16_t*>(out);
     if (maps.patch == 14)
       hipLaunchKernelGGL(im2col_staged_kernel<14>, grid, block, 0, s, pixels, maps, o, n_patches, K, Kp);
