@@ -54,9 +54,10 @@ def memory_bound_bytes(wl):
       norm_mlp: each MLP norm reads h (4 B), writes y (2 B) + its fp4 low
                 part (1/2 B) + one scale byte per 32 values
       operand:  im2col split: the pixels read once (3 p^2 fp32 per patch),
-                2 Kp bf16 written per patch; the final residual split: 4 B
-                read + 4 B written per value (merge), or the fp32 -> bf16
-                output copy: 4 + 2 B (no merge)."""
+                2 Kp bf16 written per patch; the merger's input split: 4 B
+                read, 2 B (bf16) + 1/2 B (fp4 low part) + one scale byte per
+                32 values written (merge), or the fp32 -> bf16 output copy:
+                4 + 2 B (no merge)."""
     import math
     N, D, L, p = wl.n_patches, wl.hidden, wl.layers, wl.patch
     if wl.dtype != "bf16" or L == 0:
@@ -65,7 +66,7 @@ def memory_bound_bytes(wl):
     return {
         "norm": N * D * (10 + (L - 1) * 6),
         "norm_mlp": N * D * L * (6 + 0.5 + 1 / 32),
-        "operand": N * (3 * p * p * 4 + 2 * kp * 2) + N * D * (8 if wl.merge == 2 else 6),
+        "operand": N * (3 * p * p * 4 + 2 * kp * 2) + N * D * ((6 + 0.5 + 1 / 32) if wl.merge == 2 else 6),
     }
 
 

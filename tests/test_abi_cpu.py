@@ -480,11 +480,12 @@ def test_fp8_flag_validation_and_workspace():
 
 def test_prepared_bytes_and_prepare_validation():
     """pv_tower_prepared_bytes: the padded patch weights plus, per block, the
-    fp4 gate/up copy (bf16 tower) or the seven fp8 matrices (fp8 variant);
-    nothing for the fp32 tower.  pv_tower_prepare's argument checks return
-    before any device work."""
+    fp4 gate/up copy (bf16 tower) or the seven fp8 matrices (fp8 variant),
+    plus the fp4 copy of the merge weights [O][4D] and its scale bytes (merge
+    2); nothing for the fp32 tower.  pv_tower_prepare's argument checks
+    return before any device work."""
     lib = T.load_library()
-    D, F, L, Kp = 1024, 4096, 24, 640   # patch 14: 3 * 14^2 = 588 -> 640
+    D, F, L, Kp, O = 1024, 4096, 24, 640, 5120   # patch 14: 3 * 14^2 = 588 -> 640
 
     def rnd(x):
         return (x + 255) // 256 * 256
@@ -498,7 +499,8 @@ def test_prepared_bytes_and_prepare_validation():
 
     h, b = prepared(T.make_config(layers=L))
     per_layer = rnd(2 * F * D // 2) + rnd(D // 256 * 2 * F * 8)
-    assert b == rnd(D * Kp * 2) + L * per_layer
+    merge = rnd(O * 4 * D // 2) + rnd(4 * D // 256 * O * 8)
+    assert b == rnd(D * Kp * 2) + L * per_layer + merge
     assert lib.pv_tower_prepare(None, FAKE * 256, b, None) == -1
     assert lib.pv_tower_prepare(h, FAKE * 256 + 16, b, None) == -1    # misaligned
     assert lib.pv_tower_prepare(h, FAKE * 256, b - 1, None) == -3     # too small
@@ -508,7 +510,10 @@ def test_prepared_bytes_and_prepare_validation():
     h, b8 = prepared(T.make_config(layers=L, flags=T.PV_FLAG_FP8))
     per8 = (rnd(3 * D * D) + rnd(D // 128 * 3 * D * 4) + rnd(D * D) + rnd(D // 128 * D * 4) + rnd(2 * F * D)
             + rnd(D // 128 * 2 * F * 4) + rnd(D * F) + rnd(F // 128 * D * 4))
-    assert b8 == rnd(D * Kp * 2) + L * per8
+    assert b8 == rnd(D * Kp * 2) + L * per8 + merge
+    lib.pv_tower_destroy(h)
+    h, bn = prepared(T.make_config(layers=L, merge=1))   # no merger: no merge copy
+    assert bn == rnd(D * Kp * 2) + L * per_layer
     lib.pv_tower_destroy(h)
     h, bf = prepared(T.make_config(layers=L, dtype="f32"))
     assert bf == 0
@@ -541,8 +546,16 @@ def test_deep_projector_flag_validation():
     st_w, wide = _plan(lib, handles[2], [(448, 448)])
     assert st_d == st_p == st_w == 0
     # 448^2: 1,024 patches, 256 merged tokens; the big region holds 1,024 rows
-    # of 4,096 bf16 (8 MiB): 256 x 5,120 bf16 fit, 256 x 32,768 (16 MiB) grow it
-    assert deep.workspace_bytes == plain.workspace_bytes
-    assert wide.workspace_bytes - plain.workspace_bytes == 256 * 32768 * 2 - 1024 * 4096 * 2
+    # of 4,096 bf16 (8 MiB): 256 x 5,120 bf16 fit, 256 x 32,768 (16 MiB) grow
+    # it.  Unprepared, the workspace also holds the fp4 copy of merge_w (its
+    # rows x 2D bytes + 4D/256 x rows x 8 scale bytes): 5,120 rows for the
+    # plain merge, D = 1,024 rows for the deeper projector's first matrix.
+    D = 1024
+
+    def merge_copy(rows):
+        return rows * 2 * D + (4 * D // 256) * rows * 8
+
+    assert plain.workspace_bytes - deep.workspace_bytes == merge_copy(5120) - merge_copy(1024)
+    assert wide.workspace_bytes - deep.workspace_bytes == 256 * 32768 * 2 - 1024 * 4096 * 2
     for hd in handles:
         lib.pv_tower_destroy(hd)

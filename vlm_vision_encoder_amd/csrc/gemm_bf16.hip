@@ -5,15 +5,19 @@
 //   patch embedding   A = im2col of the pixels as bf16 hi | lo, C fp32
 //   q,k,v             A = y, B rows from wq|wk|wv, epilogue rotates q and k
 //   out-projection    A = attention output, epilogue adds into the residual
-//   MLP gate/up       A = y as hi | lo, B rows interleave gate and up,
+//   MLP gate/up       A = y (bf16), B rows interleave gate and up, then
+//                     the fp4 low part of y against fp4 gate/up weights;
 //                     epilogue silu(g) * u
 //   MLP down          epilogue adds into the residual
-//   merger            A = 2x2 gather of the residual (bf16 hi | lo copy),
-//                     done by the A-operand loads themselves
-// Operands that carry fp32 values (pixels, the MLP input, the final
-// residual) enter as two bf16 halves hi and lo = bf16(x - hi) over a K range
-// twice as long, both against the same B rows (GemmArgs::kb): about 16
-// significant bits of the fp32 operand on bf16 MFMAs.
+//   merger            A = 2x2 gather of the final residual's bf16 rows, done
+//                     by the A-operand loads themselves, then its fp4 low
+//                     part (gathered when it was written) against fp4 merge
+//                     weights
+// The pixels enter as two bf16 halves hi and lo = bf16(x - hi) over a K
+// range twice as long, both against the same B rows (GemmArgs::kb): about
+// 16 significant bits on bf16 MFMAs.  The MLP input and the final residual
+// enter as bf16 plus their low part x - bf16(x) in fp4 (the LOW steps
+// below): about 11 bits.
 #include <type_traits>
 
 #include "common.h"
@@ -307,7 +311,9 @@ void gemm_dense_kernel(GemmArgs g) {
   constexpr int KSTEP = LOW == 4 ? 256 : 128;  // k per low-precision step
   constexpr int SCA = BM * SB / 16, SCB = BN * SB / 16;  // 16-byte scale chunks per step
   constexpr int WSA = (SCA + 63) / 64, WSB = (SCB + 63) / 64;  // waves that load them
-  static_assert(!LO8 || (BM <= 256 && BN <= 256 && BKT == 64 && NS == 2 && AMD == A_DENSE && WSA + WSB <= NW),
+  // (with A_MERGE the bf16 steps gather A and the low-precision steps read a
+  // dense operand already in the merged rows' order)
+  static_assert(!LO8 || (BM <= 256 && BN <= 256 && BKT == 64 && NS == 2 && WSA + WSB <= NW),
                 "low-precision steps: tiles of at most 256 x 256, 64-k bf16 steps (128-byte rows)");
 
   // residual-adding epilogues fetch the residual of up to 4 blocks (64
@@ -724,7 +730,11 @@ hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
   const int ncols = (BMD == B_GATEUP) ? 2 * g.N : g.N;
   if (ncols % BN || g.K % BKT || g.kb % BKT) return hipErrorInvalidValue;
   if (g.kb > 0 && g.K != 2 * g.kb) return hipErrorInvalidValue;
-  if (AMD == A_MERGE && (g.hidden % BKT || g.K != 8 * g.hidden || g.kb != 4 * g.hidden)) return hipErrorInvalidValue;
+  // A_MERGE: K = 8D over a hi | lo copy [rows][2D] (kb = 4D), or K = 4D over a
+  // bf16 copy [rows][D] (kb = 0, low-precision steps may follow)
+  if (AMD == A_MERGE && (g.hidden % BKT || !((g.K == 8 * g.hidden && g.kb == 4 * g.hidden) ||
+                                              (g.K == 4 * g.hidden && g.kb == 0))))
+    return hipErrorInvalidValue;
   if (LO8 && (g.k8 <= 0 || g.k8 % KSTEP || g.kb != 0 || g.as_rows < ((g.M + BM - 1) / BM) * BM || g.bs_rows < ncols))
     return hipErrorInvalidValue;
   const int tiles = ((g.M + BM - 1) / BM) * (ncols / BN);
@@ -813,10 +823,16 @@ hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
       return g.low_fmt == 4 ? launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL, 4>(g, s)
                             : launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL, 8>(g, s);
     case GEMM_MERGE:
+      if (g.k8 > 0)
+        return g.N % 256 == 0 ? launch_dense<PV_GEMM_CFG_MERGE, A_MERGE, B_ONE, E_STORE, 4>(g, s)
+                              : launch_dense<PV_GEMM_CFG_N1K, A_MERGE, B_ONE, E_STORE, 4>(g, s);
       return g.N % 256 == 0 ? launch_dense<PV_GEMM_CFG_MERGE, A_MERGE, B_ONE, E_STORE>(g, s)
                             : launch_dense<PV_GEMM_CFG_N1K, A_MERGE, B_ONE, E_STORE>(g, s);
     case GEMM_PLAIN:  return launch_dense<PV_GEMM_CFG_N1K, A_DENSE, B_ONE, E_STORE>(g, s);
     case GEMM_MERGE_F32:
+      if (g.k8 > 0)
+        return g.N % 256 == 0 ? launch_dense<PV_GEMM_CFG_MERGE, A_MERGE, B_ONE, E_STORE_F32, 4>(g, s)
+                              : launch_dense<PV_GEMM_CFG_N1K, A_MERGE, B_ONE, E_STORE_F32, 4>(g, s);
       return g.N % 256 == 0 ? launch_dense<PV_GEMM_CFG_MERGE, A_MERGE, B_ONE, E_STORE_F32>(g, s)
                             : launch_dense<PV_GEMM_CFG_N1K, A_MERGE, B_ONE, E_STORE_F32>(g, s);
     case GEMM_GELU:

@@ -41,6 +41,12 @@ hipError_t rmsnorm_hi_lo4(const float* x, const float* g, void* yh, void* y4, vo
 // byte per 32 columns, step-major: ys[(col / 128) * srows + row][(col / 32) % 4]
 hipError_t rmsnorm_fp8(const float* x, const float* g, void* y8, void* ys, int rows, int srows, int D, float eps,
                        hipStream_t s);
+// merge_hi_lo4: the merger's input x [N][D] as bf16 hi rows yh [N][D] plus
+// the fp4 low part gathered in merged-token order: y4 [T][4D/2] (row t =
+// the low parts of source rows msrc[t][0..3]), scale bytes
+// ys[(k / 256) * srows + t][(k / 32) % 8], k = j D + col
+hipError_t merge_hi_lo4(const float* x, const int32_t* msrc, void* yh, void* y4, void* ys, int tokens, int srows,
+                        int D, hipStream_t s);
 hipError_t rmsnorm_dual(float* x, const float* g1, const float* g2, void* y, int rows, int D,
                         float eps, bool y_f32, hipStream_t s);
 
@@ -85,11 +91,9 @@ hipError_t export_maps(const ImageMeta* meta, const int32_t* rowinfo, int n_imag
 hipError_t f32_to_bf16(const float* x, void* y, size_t n, hipStream_t s);
 // Operand preparation (bf16 hi | lo halves of fp32 A operands):
 //   im2col_split: out [N][2 Kp] = im2col(pixels) as hi | lo, k >= K zero
-//   split_rows:   out [rows][2 D] = x as hi | lo
 //   pad_rows:     out [rows][Kp] = w [rows][K] zero-padded (bf16)
 hipError_t im2col_split(const float* pixels, const DevMaps& maps, void* out, int n_patches, int K, int Kp,
                         hipStream_t s);
-hipError_t split_rows(const float* x, void* out, int rows, int D, hipStream_t s);
 // Resize + normalisation of uint8 H x W x 3 images: value = raw * mul[c] +
 // add[c] after a half-pixel-centre bilinear resample to the plan's size.
 struct NormAff {
@@ -112,7 +116,10 @@ hipError_t quant_rows_fp8(const void* src, int rows, int K, void* dst8, void* sc
 //   gateup_fp8:   b8 [2F][D] fp8 e4m3 = the gate/up weights in the GEMM's
 //                 interleaved row order, bs [D/128][2F][4] scale bytes
 hipError_t gateup_fp8(const void* w_gate, const void* w_up, void* b8, void* bs, int F, int D, hipStream_t s);
-//   gateup_fp4:   the same rows in packed fp4 e2m1, b4 [2F][D/2],
+//   rows_fp4:     a bf16 [rows][K] matrix in packed fp4 e2m1, b4 [rows][K/2],
+//                 bs [K/256][rows][8] scale bytes (K a multiple of 256)
+hipError_t rows_fp4(const void* w, int rows, int K, void* b4, void* bs, hipStream_t s);
+//   gateup_fp4:   the gate/up rows of gateup_fp8 in packed fp4 e2m1, b4 [2F][D/2],
 //                 bs [D/256][2F][8] scale bytes
 hipError_t gateup_fp4(const void* w_gate, const void* w_up, void* b4, void* bs, int F, int D, hipStream_t s);
 // Content keys of uint8 images (two 64-bit lanes per image, keys [n][2]

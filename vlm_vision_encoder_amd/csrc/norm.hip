@@ -129,6 +129,46 @@ __global__ __launch_bounds__(256) void rmsnorm_hi_lo4_kernel(const float* __rest
   }
 }
 
+// The merger's input (the final residual, fp32 [N][D]) as bf16 hi rows plus
+// the low part x - hi in fp4 e2m1, the low part already in the merged
+// tokens' order: workgroup t (one merged token), wave j (window slot j)
+// takes source row src = msrc[t][j] and writes
+//   yh [src][D]                     bf16 hi (row-major per patch: the GEMM's
+//                                   2x2 gather reads it)
+//   y4 [t][4D/2], k = j D + col     fp4 low part, low nibble = even k
+//   ys [(4D/256)][srows][8]         one E8M0 byte per 32 k, step-major
+// so that the low-part operand of the merge GEMM is dense [T][4D].
+template <int NC>
+__global__ __launch_bounds__(256) void merge_hi_lo4_kernel(const float* __restrict__ x, const int32_t* __restrict__ msrc,
+                                                           uint16_t* __restrict__ yh, uint8_t* __restrict__ y4,
+                                                           uint8_t* __restrict__ ys, int tokens, int srows) {
+  constexpr int D = NC * 256;
+  const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
+  const int t = blockIdx.x;
+  if (t >= tokens) return;
+  const int src = msrc[4 * t + j];
+  const floatx4* xr = reinterpret_cast<const floatx4*>(x + size_t(src) * D);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const floatx4 v = xr[i * 64 + lane];
+    const int col = (i * 64 + lane) * 4;
+    u32x2 hi;
+    hi[0] = pack_bf16x2(v[0], v[1]);
+    hi[1] = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<u32x2*>(yh + size_t(src) * D + col) = hi;
+    const float l0 = v[0] - lo_bf16(hi[0]), l1 = v[1] - hi_bf16(hi[0]);
+    const float l2 = v[2] - lo_bf16(hi[1]), l3 = v[3] - hi_bf16(hi[1]);
+    const float amax = max8(fmaxf(fmaxf(fabsf(l0), fabsf(l1)), fmaxf(fabsf(l2), fabsf(l3))));
+    float scale;
+    const uint32_t sbyte = mx_scale4(amax, scale);
+    *reinterpret_cast<uint16_t*>(y4 + size_t(t) * (2 * D) + (j * D + col) / 2) =
+        uint16_t(pack_fp4x4(l0, l1, l2, l3, scale));
+    const uint32_t w = scale_word(sbyte, lane);
+    if ((lane & 31) == 0)
+      *reinterpret_cast<uint32_t*>(ys + (size_t(j * NC + i) * srows + t) * 8 + (lane >> 3)) = w;
+  }
+}
+
 // The input of an fp8 linear map: y = norm(x) * g as fp8 e4m3 [N][D] with
 // one scale byte per 32 columns (same scale layout as above).
 template <int NC>
@@ -242,6 +282,22 @@ hipError_t rmsnorm_hi_lo4(const float* x, const float* g, void* yh, void* y4, vo
     hipLaunchKernelGGL((rmsnorm_hi_lo4_kernel<NC>), grid, block, 0, s, x, g, static_cast<uint16_t*>(yh), \
                        static_cast<uint8_t*>(y4), static_cast<uint8_t*>(ys), rows, srows, eps);           \
     return hipGetLastError();                                                                          \
+  }
+  PV_NORM_CASES(PV_CASE)
+#undef PV_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t merge_hi_lo4(const float* x, const int32_t* msrc, void* yh, void* y4, void* ys, int tokens, int srows,
+                        int D, hipStream_t s) {
+  if (tokens <= 0) return hipSuccess;
+  if (D % 256 || srows < tokens) return hipErrorInvalidValue;
+#define PV_CASE(NC)                                                                                     \
+  if (D == NC * 256) {                                                                                  \
+    hipLaunchKernelGGL((merge_hi_lo4_kernel<NC>), dim3(tokens), dim3(256), 0, s, x, msrc,               \
+                       static_cast<uint16_t*>(yh), static_cast<uint8_t*>(y4), static_cast<uint8_t*>(ys), \
+                       tokens, srows);                                                                  \
+    return hipGetLastError();                                                                           \
   }
   PV_NORM_CASES(PV_CASE)
 #undef PV_CASE

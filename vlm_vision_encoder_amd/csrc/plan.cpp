@@ -146,9 +146,17 @@ int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, P
     const size_t F = size_t(p.mlp);
     const size_t KA = p.fp8 ? std::max(D, F) : D;  // widest fp8 A operand
     L.a8 = off;
-    off = align256(off + N * KA);
+    off = align256(off + N * KA);  // (>= the merger's [T][2D] low part: T <= N / 4)
     L.as = off;
-    off = align256(off + (KA / 128) * size_t(a8_scale_rows(int64_t(N))) * 4);
+    size_t as_bytes = (KA / 128) * size_t(a8_scale_rows(int64_t(N))) * 4;
+    if (p.merge_rows > 0) as_bytes = std::max(as_bytes, (D / 64) * size_t(a8_scale_rows(int64_t(toks))) * 8);
+    off = align256(off + as_bytes);
+  }
+  if (p.elem_bytes == 2 && !p.prepared && p.merge_rows > 0) {
+    L.mw4 = off;
+    off = align256(off + merge_fp4_bytes(p.merge_rows, p.hidden));
+    L.mws = off;
+    off = align256(off + merge_fp4_scale_bytes(p.merge_rows, p.hidden));
   }
   if (p.elem_bytes == 2 && !p.prepared) {
     const size_t F = size_t(p.mlp), F2 = 2 * F;
@@ -175,7 +183,7 @@ int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, P
   return 0;
 }
 
-PrepLayout prep_layout(int32_t patch, int32_t hidden, int32_t mlp, int32_t layers, bool fp8) {
+PrepLayout prep_layout(int32_t patch, int32_t hidden, int32_t mlp, int32_t layers, bool fp8, int32_t merge_rows) {
   PrepLayout P;
   const size_t D = size_t(hidden), F = size_t(mlp), F2 = 2 * F;
   size_t off = 0;
@@ -207,7 +215,14 @@ PrepLayout prep_layout(int32_t patch, int32_t hidden, int32_t mlp, int32_t layer
     lo = align256(lo + (D / 256) * F2 * 8);
   }
   P.layer_stride = lo;
-  P.total = off + size_t(layers > 0 ? layers : 0) * lo;
+  off += size_t(layers > 0 ? layers : 0) * lo;
+  if (merge_rows > 0) {
+    P.mw4 = off;
+    off = align256(off + merge_fp4_bytes(merge_rows, hidden));
+    P.mws = off;
+    off = align256(off + merge_fp4_scale_bytes(merge_rows, hidden));
+  }
+  P.total = off;
   return P;
 }
 

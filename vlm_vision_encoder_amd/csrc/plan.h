@@ -72,6 +72,10 @@ struct PlanParams {
   // deeper projector: its out_dim-wide GELU output ([out_rows][out_dim] bf16)
   // goes through the big region (0: plain merge)
   int32_t deep_out = 0;
+  // bf16 tower with merge == 2: rows of merge_w (out_dim, or D for the deeper
+  // projector), whose fp4 copy the merger multiplies with its input's low
+  // part; 0 otherwise
+  int32_t merge_rows = 0;
 };
 
 // Byte offsets of a tower's derived weight copies in the memory that one
@@ -83,14 +87,23 @@ struct PlanParams {
 //     fp8 copies (fp8 variant): wq8 [3D][D] + wqs [D/128][3D][4], wo8 [D][D] +
 //       wos [D/128][D][4], b8 [2F][D] + bs8 [D/128][2F][4], wd8 [D][F] + wds
 //       [F/128][D][4]
+//   after the layers (merge_rows > 0): mw4 [merge_rows][2D] the merge weights
+//     in fp4, mws [4D/256][merge_rows][8] scale bytes
 struct PrepLayout {
   size_t wpad = 0;
   size_t layer0 = 0, layer_stride = 0;
   // offsets within a layer's region
   size_t b8 = 0, bs = 0, wq8 = 0, wqs = 0, wo8 = 0, wos = 0, wd8 = 0, wds = 0;
+  size_t mw4 = 0, mws = 0;
   size_t total = 0;
 };
-PrepLayout prep_layout(int32_t patch, int32_t hidden, int32_t mlp, int32_t layers, bool fp8);
+PrepLayout prep_layout(int32_t patch, int32_t hidden, int32_t mlp, int32_t layers, bool fp8, int32_t merge_rows);
+
+// Bytes of the merge weights' fp4 copy and of its scale bytes (K = 4D).
+inline size_t merge_fp4_bytes(int32_t merge_rows, int32_t hidden) { return size_t(merge_rows) * 2 * size_t(hidden); }
+inline size_t merge_fp4_scale_bytes(int32_t merge_rows, int32_t hidden) {
+  return size_t(hidden) / 64 * size_t(merge_rows) * 8;
+}
 
 // Rows of the MLP input's fp8 scale blocks: the patches plus one tile of
 // padding (a GEMM tile reads the scale bytes of 256 consecutive rows).
@@ -108,6 +121,10 @@ struct Layout {
   // (fp8 variant: a8/as hold every fp8 GEMM input, up to [N][max(D, F)], and
   // b8/bs this layer's gate/up weights in fp8):
   size_t a8 = 0, as = 0, b8 = 0, bs = 0;
+  // bf16 tower with merge == 2: the merger input's low part goes through
+  // a8 / as ([T][2D] fp4 in merged-token order, [4D/256][T + 256][8] scale
+  // bytes); unprepared, mw4 / mws hold the merge weights' fp4 copy
+  size_t mw4 = 0, mws = 0;
   // fp8 variant: this layer's q|k|v, out-projection and down weights in fp8
   size_t wq8 = 0, wqs = 0, wo8 = 0, wos = 0, wd8 = 0, wds = 0;
   size_t upload_bytes = 0;  // [0, upload_bytes) is filled by one host->device copy

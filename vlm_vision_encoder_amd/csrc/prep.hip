@@ -7,8 +7,6 @@
 //                 Mistral3VisionModel: the convolution with stride = kernel =
 //                 patch size, i.e. one GEMM row per patch), K order
 //                 (channel, row, column) of the conv weight, zero-padded to Kp.
-//   split_rows:   the final residual, which the merger's A-operand loads then
-//                 gather 2x2 straight from this copy.
 //   pad_rows:     copy of a bf16 matrix with its rows zero-padded (patch
 //                 weights [D][3p^2] -> [D][Kp]).
 //   im2col_u8_split: the same A operand straight from uint8 H x W x 3 images:
@@ -22,6 +20,8 @@
 //   gateup_fp4:   fp4 e2m1 copy of the gate/up weights in the GEMM's
 //                 interleaved row order, one power-of-two scale per 32 k, for
 //                 the fp4 product with the MLP input's low part.
+//   rows_fp4:     the same for a plain matrix (the merge weights, against the
+//                 merger input's low part).
 //   gateup_fp8, quant_rows_fp8: fp8 e4m3 copies of weights and activations
 //                 for the fp8 variant of the tower's linear maps.
 #include "common.h"
@@ -289,23 +289,6 @@ __global__ __launch_bounds__(256) void resize_norm_u8_kernel(const uint8_t* __re
         sample_u8(img, sm.H, sm.W, sm.RH, sm.RW, sm.y0 + ty, sm.x0 + tx, c, aff.mul[c], aff.add[c]);
 }
 
-// One thread per 8 consecutive values of a row.
-__global__ __launch_bounds__(256) void split_rows_kernel(const float* __restrict__ x, uint16_t* __restrict__ out,
-                                                         int rows, int D) {
-  const int chunks = D / 8;
-  const long long idx = blockIdx.x * 256ll + threadIdx.x;
-  if (idx >= (long long)rows * chunks) return;
-  const int r = int(idx / chunks), c0 = int(idx - (long long)r * chunks) * 8;
-  const floatx4* src = reinterpret_cast<const floatx4*>(x + size_t(r) * D + c0);
-  const floatx4 a = src[0], b = src[1];
-  const float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  u32x4 hi, lo;
-  split8(f, hi, lo);
-  uint16_t* row = out + size_t(r) * 2 * D;
-  *reinterpret_cast<u32x4*>(row + c0) = hi;
-  *reinterpret_cast<u32x4*>(row + D + c0) = lo;
-}
-
 __global__ __launch_bounds__(256) void pad_rows_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ out,
                                                        int rows, int K, int Kp) {
   const long long idx = blockIdx.x * 256ll + threadIdx.x;
@@ -366,15 +349,9 @@ __global__ __launch_bounds__(256) void gateup_fp8_kernel(const uint16_t* __restr
 
 // The same rows in packed fp4 for the MLP input's fp4 low part: b4
 // [2F][D/2] (low nibble = even k), scales bs[(k/256) * 2F + n][(k/32) % 8].
-__global__ __launch_bounds__(256) void gateup_fp4_kernel(const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
-                                                         uint8_t* __restrict__ b4, uint8_t* __restrict__ bs, int F,
-                                                         int D) {
-  const int blocks = D / 32;
-  const long long idx = blockIdx.x * 256ll + threadIdx.x;
-  if (idx >= 2ll * F * blocks) return;
-  const int n = int(idx / blocks), blk = int(idx - (long long)n * blocks);
-  const int src_row = (n >> 6) * 32 + (n & 31);
-  const uint16_t* src = ((n & 32) ? wu : wg) + size_t(src_row) * D + blk * 32;
+// One 32-value block of bf16 weights -> 16 bytes of fp4 e2m1 (low nibble =
+// even k) and its E8M0 scale byte.
+__device__ __forceinline__ uint32_t fp4_block32(const uint16_t* __restrict__ src, u32x4& o) {
   float f[32];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -390,11 +367,38 @@ __global__ __launch_bounds__(256) void gateup_fp4_kernel(const uint16_t* __restr
   for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(f[e]));
   float scale;
   const uint32_t sbyte = mx_scale4(amax, scale);
-  u32x4 o;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     o[q] = pack_fp4x4(f[8 * q], f[8 * q + 1], f[8 * q + 2], f[8 * q + 3], scale) |
            (pack_fp4x4(f[8 * q + 4], f[8 * q + 5], f[8 * q + 6], f[8 * q + 7], scale) << 16);
+  return sbyte;
+}
+
+// One thread per (row n, block of 32 columns) of a bf16 [rows][K] matrix:
+// b4 [rows][K/2] fp4, bs [K/256][rows][8] scale bytes.
+__global__ __launch_bounds__(256) void rows_fp4_kernel(const uint16_t* __restrict__ w, int rows, int K,
+                                                       uint8_t* __restrict__ b4, uint8_t* __restrict__ bs) {
+  const int blocks = K / 32;
+  const long long idx = blockIdx.x * 256ll + threadIdx.x;
+  if (idx >= (long long)rows * blocks) return;
+  const int n = int(idx / blocks), blk = int(idx - (long long)n * blocks);
+  u32x4 o;
+  const uint32_t sbyte = fp4_block32(w + size_t(n) * K + blk * 32, o);
+  *reinterpret_cast<u32x4*>(b4 + size_t(n) * (K / 2) + blk * 16) = o;
+  bs[(size_t(blk / 8) * rows + n) * 8 + (blk & 7)] = uint8_t(sbyte);
+}
+
+__global__ __launch_bounds__(256) void gateup_fp4_kernel(const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
+                                                         uint8_t* __restrict__ b4, uint8_t* __restrict__ bs, int F,
+                                                         int D) {
+  const int blocks = D / 32;
+  const long long idx = blockIdx.x * 256ll + threadIdx.x;
+  if (idx >= 2ll * F * blocks) return;
+  const int n = int(idx / blocks), blk = int(idx - (long long)n * blocks);
+  const int src_row = (n >> 6) * 32 + (n & 31);
+  const uint16_t* src = ((n & 32) ? wu : wg) + size_t(src_row) * D + blk * 32;
+  u32x4 o;
+  const uint32_t sbyte = fp4_block32(src, o);
   *reinterpret_cast<u32x4*>(b4 + size_t(n) * (D / 2) + blk * 16) = o;
   bs[(size_t(blk / 8) * (2 * F) + n) * 8 + (blk & 7)] = uint8_t(sbyte);
 }
@@ -461,13 +465,6 @@ hipError_t resize_norm_u8(const uint8_t* image, const SrcImage& sm, int tH, int 
   return hipGetLastError();
 }
 
-hipError_t split_rows(const float* x, void* out, int rows, int D, hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  if (D % 8) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(split_rows_kernel, grid_for((long long)rows * (D / 8)), dim3(256), 0, s, x,
-                     static_cast<uint16_t*>(out), rows, D);
-  return hipGetLastError();
-}
 
 hipError_t gateup_fp8(const void* w_gate, const void* w_up, void* b8, void* bs, int F, int D, hipStream_t s) {
   if (F <= 0) return hipSuccess;
@@ -494,6 +491,14 @@ hipError_t gateup_fp4(const void* w_gate, const void* w_up, void* b4, void* bs, 
   hipLaunchKernelGGL(gateup_fp4_kernel, grid_for(2ll * F * (D / 32)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
                      static_cast<uint8_t*>(b4), static_cast<uint8_t*>(bs), F, D);
+  return hipGetLastError();
+}
+
+hipError_t rows_fp4(const void* w, int rows, int K, void* b4, void* bs, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (K % 256) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rows_fp4_kernel, grid_for((long long)rows * (K / 32)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(w), rows, K, static_cast<uint8_t*>(b4), static_cast<uint8_t*>(bs));
   return hipGetLastError();
 }
 

@@ -111,6 +111,12 @@ struct pv_tower {
 
 namespace {
 
+// Rows of merge_w whose fp4 copy the bf16 merger uses (0: no such copy).
+int32_t merge_rows_of(const pv_config& c) {
+  if (c.dtype != PV_BF16 || c.merge != 2) return 0;
+  return (c.flags & PV_FLAG_DEEP_PROJECTOR) ? c.hidden : c.out_dim;
+}
+
 pv::PlanParams plan_params(const pv_tower* t) {
   pv::PlanParams p;
   p.patch = t->cfg.patch;
@@ -129,6 +135,7 @@ pv::PlanParams plan_params(const pv_tower* t) {
   p.fp8 = (t->cfg.flags & PV_FLAG_FP8) != 0;
   p.prepared = t->prep != nullptr;
   p.deep_out = (t->cfg.flags & PV_FLAG_DEEP_PROJECTOR) ? t->cfg.out_dim : 0;
+  p.merge_rows = merge_rows_of(t->cfg);
   return p;
 }
 
@@ -456,17 +463,33 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
   if (st.stage >= 0) return fail(PV_ERR_ARG, "stage/layer not reached");
 
   const bool out_bf16 = bf && c.out_dtype == PV_BF16;
+  // bf16 merger: the final residual (or its norm) as bf16 rows in big,
+  // which the A loads gather 2x2 (K = 4D), plus its low part in fp4, already
+  // gathered in merged-token order (a8 / as), against the fp4 copy of
+  // merge_w (prepared, else made here)
+  auto merge_args = [&](pv::GemmArgs& a, const float* x, int rows_w) -> pv_status {
+    const int T = int(plan.out_rows), srows = int(pv::a8_scale_rows(T));
+    void* mw4 = t->prep ? static_cast<void*>(t->prep + t->prep_layout.mw4) : static_cast<void*>(ws + L.mw4);
+    void* mws = t->prep ? static_cast<void*>(t->prep + t->prep_layout.mws) : static_cast<void*>(ws + L.mws);
+    if (!t->prep) PV_LAUNCH(PV_K_MERGE, pv::rows_fp4(t->w.merge_w, rows_w, 4 * D, mw4, mws, s));
+    PV_LAUNCH(PV_K_OPERAND, pv::merge_hi_lo4(x, g.maps.msrc, big, ws + L.a8, ws + L.as, T, srows, D, s));
+    a.M = T; a.K = 4 * D; a.kb = 0;
+    a.A = big; a.lda = D;
+    a.B0 = t->w.merge_w; a.ldb = 4 * D;
+    a.A8 = ws + L.a8; a.B8 = mw4; a.As = ws + L.as; a.Bs = mws;
+    a.k8 = 4 * D; a.as_rows = srows; a.bs_rows = rows_w; a.low_fmt = 4;
+    return PV_OK;
+  };
   if (c.merge == 2 && bf && (c.flags & PV_FLAG_DEEP_PROJECTOR)) {
-    // deeper projector: RMSNorm (in place, fp32) -> hi | lo copy -> 2x2
-    // gather and 4D -> D (bf16 m in y) -> D -> out_dim with GELU (bf16 a in
-    // big) -> out_dim -> out_dim into out
+    // deeper projector: RMSNorm (in place, fp32) -> 2x2 gather and 4D -> D
+    // (bf16 m in y) -> D -> out_dim with GELU (bf16 a in big) -> out_dim ->
+    // out_dim into out
     PV_LAUNCH(PV_K_NORM, pv::rmsnorm(r, t->proj.norm, r, N, D, eps, true, s));
-    PV_LAUNCH(PV_K_OPERAND, pv::split_rows(r, big, N, D, s));
     const int T = int(plan.out_rows), O = c.out_dim;
     pv::GemmArgs a = g;
-    a.M = T; a.N = D; a.K = 8 * D; a.kb = 4 * D;
-    a.A = big; a.lda = 2 * D;
-    a.B0 = t->w.merge_w; a.ldb = 4 * D;
+    const pv_status ms = merge_args(a, r, D);
+    if (ms != PV_OK) return ms;
+    a.N = D;
     a.C = y; a.ldc = D;
     PV_LAUNCH(PV_K_MERGE, gemm(pv::GEMM_MERGE, a));
     pv::GemmArgs b = g;
@@ -482,13 +505,10 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
     o.C = out; o.ldc = O;
     PV_LAUNCH(PV_K_MERGE, gemm(out_bf16 ? pv::GEMM_PLAIN : pv::GEMM_PLAIN_F32, o));
   } else if (c.merge == 2 && bf) {
-    // the final residual as bf16 hi | lo rows; the merger's A loads gather
-    // the 2x2 groups from that copy
-    PV_LAUNCH(PV_K_OPERAND, pv::split_rows(r, big, N, D, s));
     pv::GemmArgs a = g;
-    a.M = int(plan.out_rows); a.N = c.out_dim; a.K = 8 * D; a.kb = 4 * D;
-    a.A = big; a.lda = 2 * D;
-    a.B0 = t->w.merge_w; a.ldb = 4 * D;
+    const pv_status ms = merge_args(a, r, c.out_dim);
+    if (ms != PV_OK) return ms;
+    a.N = c.out_dim;
     a.C = out; a.ldc = c.out_dim;
     PV_LAUNCH(PV_K_MERGE, gemm(out_bf16 ? pv::GEMM_MERGE : pv::GEMM_MERGE_F32, a));
   } else if (c.merge == 2) {
@@ -766,9 +786,10 @@ pv_status pv_tower_prepared_bytes(const pv_tower* t, int64_t* bytes) {
   pv::last_error().clear();
   if (!t || !bytes) return fail(PV_ERR_ARG, "tower and bytes must not be null");
   const pv_config& c = t->cfg;
-  *bytes = c.dtype == PV_BF16
-               ? int64_t(pv::prep_layout(c.patch, c.hidden, c.mlp, c.layers, (c.flags & PV_FLAG_FP8) != 0).total)
-               : 0;
+  *bytes = c.dtype == PV_BF16 ? int64_t(pv::prep_layout(c.patch, c.hidden, c.mlp, c.layers,
+                                                        (c.flags & PV_FLAG_FP8) != 0, merge_rows_of(c))
+                                           .total)
+                               : 0;
   return PV_OK;
 }
 
@@ -783,7 +804,7 @@ pv_status pv_tower_prepare(pv_tower* t, void* mem, int64_t mem_bytes, void* stre
   if (c.dtype != PV_BF16) return PV_OK;  // the fp32 tower uses its weights as given
   if (!aligned(mem, 256)) return fail(PV_ERR_ARG, "mem must be 256-byte aligned");
   const bool f8 = (c.flags & PV_FLAG_FP8) != 0;
-  const pv::PrepLayout P = pv::prep_layout(c.patch, c.hidden, c.mlp, c.layers, f8);
+  const pv::PrepLayout P = pv::prep_layout(c.patch, c.hidden, c.mlp, c.layers, f8, merge_rows_of(c));
   if (mem_bytes < int64_t(P.total))
     return fail(PV_ERR_CAPACITY, "mem_bytes " + std::to_string(mem_bytes) + " < " + std::to_string(P.total));
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -800,6 +821,7 @@ pv_status pv_tower_prepare(pv_tower* t, void* mem, int64_t mem_bytes, void* stre
     else
       PV_HIP(pv::gateup_fp4(lw.w_gate, lw.w_up, wc.b8, wc.bs, F, D, s));
   }
+  if (P.mw4 || P.mws) PV_HIP(pv::rows_fp4(t->w.merge_w, merge_rows_of(c), 4 * D, m + P.mw4, m + P.mws, s));
   t->prep = m;
   t->prep_layout = P;
   return PV_OK;
