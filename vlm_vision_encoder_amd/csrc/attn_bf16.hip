@@ -22,16 +22,21 @@
 //   row-major and its V^T A-operand fragments come from two ds_read_b64_tr_b16
 //   transpose reads (each 16-lane group receives a 4-key x 16-dim block
 //   transposed), with chunks XOR-swizzled by 2*(row & 3).
-// * Softmax.  At head_dim 64 the kernel is bound by vector-ALU issue (one
-//   exp per score costs about three FMAs and shares their issue slots), so
-//   the per-score work is cut to exp + convert + half a dot2:
+// * Softmax.  At head_dim 64 a score costs 128 MACs of MFMA work and one
+//   exp (a transcendental, two issue cycles); the waves of a work item run
+//   their score MFMAs, softmax and P.V MFMAs in step, and the chip holds a
+//   lower clock the more of the SIMD's cycles are busy (power), so the
+//   per-score vector work is kept to exp + half a convert + one add:
 //   - q arrives multiplied by log2(e)/8 (by the q,k,v projection's epilogue,
 //     before its one rounding to bf16), so scores come out in exp2 units;
 //   - softmax is unchanged by a per-query offset, so each query takes the
 //     max of its first key tile as offset m0 and the offset is folded into
 //     the score MFMA as a 65th dimension (keys carry 1, the query carries
 //     -m0): no per-score subtraction and no running max;
-//   - row sums use v_dot2 on the bf16 probabilities that feed the PV MFMA.
+//   - row sums are fp32 adds of the probabilities (a tree per 8).  A
+//     v_dot2 on the packed bf16 pairs would take half the instructions, but
+//     it does not issue beside the MFMAs of the SIMD's other waves, while
+//     adds, converts and exps largely do (measured by the probe).
 //   The only risk of a fixed offset is range (a later score more than ~127
 //   above m0 overflows, or every score far below it underflows).  Each work
 //   item checks its sums and outputs for that and, if any is not finite,
@@ -48,7 +53,6 @@ namespace {
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -62,10 +66,6 @@ __device__ __forceinline__ int sigma_row(int r) {  // swap bits 2 and 3
 // (row parity, chunk): chunk ^ ((row >> 1) & 7) does that.
 __device__ __forceinline__ int kswz(int row) { return (row >> 1) & 7; }
 
-__device__ __forceinline__ float dot2_sum(uint32_t packed, float acc) {
-  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed), one, acc, false);
-}
 
 // Four waves per SIMD (two work items per CU) is worth more than the few
 // values the register cap moves to scratch outside the key loop (measured).
@@ -111,6 +111,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
   // (M0) are then computed on the scalar unit
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 31, lhalf = lane >> 5;
+  // Waves w, w + 4 and w + 8 share a SIMD; a fixed priority per wave of a
+  // SIMD lets the first one run ahead, so the SIMD's waves drift apart in
+  // phase and one's exps meet another's MFMAs (1-2% per launch)
+  if (wave >= 8) __builtin_amdgcn_s_setprio(2);
+  else if (wave >= 4) __builtin_amdgcn_s_setprio(1);
   const int wq0 = it.q0 + 32 * QB * wave;  // first query of this wave
   const bool active = wq0 < n;
 
@@ -287,10 +292,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
           }
           const u32x4 pk = pack8(p);
           pf[ub][tb][sp] = pk;
-          l_run[tb] = dot2_sum(pk[0], l_run[tb]);
-          l_run[tb] = dot2_sum(pk[1], l_run[tb]);
-          l_run[tb] = dot2_sum(pk[2], l_run[tb]);
-          l_run[tb] = dot2_sum(pk[3], l_run[tb]);
+          l_run[tb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         }
       }
     }

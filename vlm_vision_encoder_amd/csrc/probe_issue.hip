@@ -14,13 +14,20 @@
 // each SIMD holds one wave of each).  If MFMA and VALU did not overlap, a
 // mixed kernel would take the sum of its parts.
 //
-// Two more measurements:
+// More measurements:
 //   LDS read throughput: every lane of 4, 8 or 12 waves per CU reads
 //     conflict-free 16-byte (ds_read_b128) or 8-byte transposing
 //     (ds_read_b64_tr_b16) chunks from a 64 KB LDS buffer, 16 reads in
 //     flight per wave; reported as bytes per ns per CU
 //   wave placement: the SIMD (HW_ID bits 5:4) of every wave of a 12-wave and
 //     an 8-wave workgroup
+//   softmax instruction mix: 12-wave workgroups (3 waves per SIMD), one per
+//     CU, each wave running the vector work of one P.V step of the attention
+//     kernel's key tile (32 scores per lane: exp2, bf16 packing, row sums by
+//     v_dot2 or by fp32 adds, or one kind of instruction alone) with and
+//     without the step's 8 MFMAs beside it, and the whole key tile (8 score
+//     MFMAs, the softmax, 8 P.V MFMAs) serial or with the next tile's score
+//     MFMAs interleaved into the softmax; operands live in registers
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -111,6 +118,173 @@ __global__ __launch_bounds__(THREADS) void lds_probe(uint32_t* sink) {
   sink[blockIdx.x * THREADS + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kMixIters = 10000;
+
+__device__ __forceinline__ floatx16 mfma_u(u32x4 a, u32x4 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                  0, 0);
+}
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float dot2_acc(uint32_t packed, float acc) {
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed), one, acc, false);
+}
+
+// Vector work of one P.V step, 32 scores per lane in 4 groups of 8.  K:
+// exp2 + pack + v_dot2 row sums, exp2 + pack + fp32 adds, or one kind of
+// instruction alone (the values not exponentiated are the scores
+// themselves; what is not packed is xor-folded).  MF adds the step's 8
+// MFMAs (2 accumulators, B operand = the packed group).
+enum MixKind { MIX_EXP_PACK_DOT2 = 0, MIX_EXP_PACK_ADD, MIX_EXP, MIX_PACK, MIX_DOT2, MIX_FMA };
+
+template <int K, bool MF>
+__global__ __launch_bounds__(768) void mix_probe(float* sink) {
+  const int t = threadIdx.x;
+  u32x4 vf[4][2];
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 2; ++j)
+      vf[i][j] = u32x4{pack2(0.5f, 0.25f * j), pack2(0.1f * i, 0.f), pack2(1.f, -1.f), pack2(0.f, 0.5f)};
+  floatx16 o0 = {}, o1 = {};
+  floatx16 s[2];
+  for (int u = 0; u < 2; ++u)
+    for (int v = 0; v < 16; ++v) s[u][v] = -0.01f * float((t + v + u) & 31);
+  float l = 0.f;
+  for (int it = 0; it < kMixIters; ++it) {
+    for (int ub = 0; ub < 2; ++ub) asm volatile("" : "+v"(s[ub]));  // fresh scores every step
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ub = q >> 1, sp = q & 1;
+      float p[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const float x = s[ub][8 * sp + v];
+        if constexpr (K == MIX_FMA) p[v] = __builtin_fmaf(x, 0.999f, 0.001f);
+        else if constexpr (K == MIX_PACK || K == MIX_DOT2) p[v] = x;
+        else p[v] = __builtin_amdgcn_exp2f(x);
+      }
+      u32x4 pk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (K == MIX_EXP_PACK_DOT2 || K == MIX_EXP_PACK_ADD || K == MIX_PACK)
+          pk[i] = pack2(p[2 * i], p[2 * i + 1]);
+        else
+          pk[i] = __builtin_bit_cast(uint32_t, p[2 * i]) ^ __builtin_bit_cast(uint32_t, p[2 * i + 1]);
+      }
+      if constexpr (K == MIX_EXP_PACK_DOT2 || K == MIX_DOT2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l = dot2_acc(pk[i], l);
+      } else if constexpr (K == MIX_EXP_PACK_ADD) {
+        l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      }
+      if constexpr (MF) {
+        o0 = mfma_u(vf[q][0], pk, o0);
+        o1 = mfma_u(vf[q][1], pk, o1);
+      } else {
+        o0[q] += __builtin_bit_cast(float, pk[0] ^ pk[1] ^ pk[2] ^ pk[3]);
+      }
+    }
+  }
+  float r = l;
+  for (int v = 0; v < 16; ++v) r += o0[v] + o1[v] + s[0][v] + s[1][v];
+  sink[blockIdx.x * 768 + t] = r;
+}
+
+// The step's 8 MFMAs alone.
+__global__ __launch_bounds__(768) void mix_mfma_only(float* sink) {
+  u32x4 vf[4][2], b = {0x3f003f00u, 0x3f003f00u, 0x3f003f00u, 0x3f003f00u};
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 2; ++j) vf[i][j] = u32x4{0x3f80u + i, 0x3f00u * j, 0x3e00u, 0x3c00u};
+  floatx16 o0 = {}, o1 = {};
+  for (int it = 0; it < kMixIters; ++it) {
+    asm volatile("" : "+v"(b));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o0 = mfma_u(vf[q][0], b, o0);
+      o1 = mfma_u(vf[q][1], b, o1);
+    }
+  }
+  float r = 0.f;
+  for (int v = 0; v < 16; ++v) r += o0[v] + o1[v];
+  sink[blockIdx.x * 768 + threadIdx.x] = r;
+}
+
+// A whole key tile per step: 8 score MFMAs, the softmax (exp2, pack, row
+// sums by v_dot2 (SUM 0) or fp32 adds (SUM 1)), 8 P.V MFMAs.  PIPE 0 runs
+// them in that order; PIPE 1 computes the next tile's scores while the
+// current tile's softmax and P.V run, the interleave pinned per group of 8
+// scores (one MFMA, five vector instructions, four times).  Two steps per
+// trip, so the score buffers swap roles without copies.
+template <int PIPE, int SUM>
+__global__ __launch_bounds__(768) void tile_probe(float* sink) {
+  const int t = threadIdx.x;
+  u32x4 vf[2][2], kf[2][2], qf[4];
+  for (int i = 0; i < 4; ++i)
+    qf[i] = u32x4{pack2(0.01f * (t & 7), 0.02f), pack2(0.01f, -0.01f), pack2(0.f, 0.01f), pack2(0.03f, 0.f)};
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j) {
+      vf[i][j] = u32x4{pack2(0.5f, 0.25f * j), pack2(0.1f * i, 0.f), pack2(1.f, -1.f), pack2(0.f, 0.5f)};
+      kf[i][j] = u32x4{pack2(0.1f, -0.2f * j), pack2(0.1f * i, 0.3f), pack2(-0.1f, 0.1f), pack2(0.2f, 0.5f)};
+    }
+  floatx16 o0 = {}, o1 = {};
+  floatx16 sa[2], sb[2];
+  for (int u = 0; u < 2; ++u)
+    for (int v = 0; v < 16; ++v) sa[u][v] = -0.01f * float((t + v + u) & 31);
+  float l0 = 0.f, l1 = 0.f;
+  auto step = [&](floatx16(&cur)[2], floatx16(&nxt)[2]) __attribute__((always_inline)) {
+    for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(kf[i][j]), "+v"(vf[i][j]));
+    const floatx16 z = {};
+    nxt[0] = z;
+    nxt[1] = z;
+    if constexpr (PIPE == 0) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int ub = 0; ub < 2; ++ub) nxt[ub] = mfma_u(kf[ks & 1][ub], qf[ks], nxt[ub]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ub = q >> 1, sp = q & 1;
+      if constexpr (PIPE != 0) {
+        nxt[0] = mfma_u(kf[q & 1][0], qf[q], nxt[0]);
+        nxt[1] = mfma_u(kf[q & 1][1], qf[q], nxt[1]);
+      }
+      float p[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) p[v] = __builtin_amdgcn_exp2f((PIPE == 0 ? nxt : cur)[ub][8 * sp + v]);
+      const u32x4 pk = {pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7])};
+      if constexpr (SUM == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l0 = dot2_acc(pk[i], l0);
+      } else {
+        l0 += (p[0] + p[1]) + (p[2] + p[3]);
+        l1 += (p[4] + p[5]) + (p[6] + p[7]);
+      }
+      o0 = mfma_u(vf[q & 1][0], pk, o0);
+      o1 = mfma_u(vf[q & 1][1], pk, o1);
+      if constexpr (PIPE != 0) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, 5, 0);  // five vector / transcendental
+        }
+      }
+    }
+  };
+  for (int it = 0; it < kMixIters; it += 2) {
+    step(sa, sb);
+    step(sb, sa);
+  }
+  float r = l0 + l1;
+  for (int v = 0; v < 16; ++v) r += o0[v] + o1[v] + sa[0][v] + sa[1][v];
+  sink[blockIdx.x * 768 + t] = r;
+}
+
 // SIMD of each wave: HW_ID (hardware register 4) bits 5:4
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void simd_of_wave(int* out) {
@@ -163,6 +337,40 @@ float lds_ms(uint32_t* sink) {
   return ms;
 }
 
+// ns per step of a 768-thread kernel on kCUs workgroups (second of two launches)
+template <typename F>
+float step_ns(F launch) {
+  hipEvent_t e0, e1;
+  check(hipEventCreate(&e0), "event");
+  check(hipEventCreate(&e1), "event");
+  float ms = 0.f;
+  for (int rep = 0; rep < 2; ++rep) {
+    check(hipEventRecord(e0, nullptr), "record");
+    launch();
+    check(hipGetLastError(), "launch");
+    check(hipEventRecord(e1, nullptr), "record");
+    check(hipEventSynchronize(e1), "sync");
+    check(hipEventElapsedTime(&ms, e0, e1), "elapsed");
+  }
+  check(hipEventDestroy(e0), "event");
+  check(hipEventDestroy(e1), "event");
+  return ms * 1e6f / kMixIters;
+}
+
+template <int K>
+void mix_row(const char* name, float* sink, float mfma_ns) {
+  const float a = step_ns([&] { hipLaunchKernelGGL((mix_probe<K, false>), dim3(kCUs), dim3(768), 0, nullptr, sink); });
+  const float b = step_ns([&] { hipLaunchKernelGGL((mix_probe<K, true>), dim3(kCUs), dim3(768), 0, nullptr, sink); });
+  const float hidden = 100.f * (a + mfma_ns - b) / (a < mfma_ns ? a : mfma_ns);
+  std::printf("  %-22s %7.1f ns alone %7.1f ns with the MFMAs  (%5.1f%% of the smaller hidden)\n", name, a, b, hidden);
+}
+
+template <int PIPE, int SUM>
+void tile_row(const char* name, float* sink) {
+  const float a = step_ns([&] { hipLaunchKernelGGL((tile_probe<PIPE, SUM>), dim3(kCUs), dim3(768), 0, nullptr, sink); });
+  std::printf("  %-44s %7.1f ns per key tile\n", name, a);
+}
+
 template <int THREADS>
 void print_waves(int* dev) {
   constexpr int W = THREADS / 64, B = 4;
@@ -213,6 +421,25 @@ int main() {
   lrow("ds_read_b64_tr_b16", 8, 8, lds_ms<1, 512>(lsink));
   lrow("ds_read_b64_tr_b16", 12, 8, lds_ms<1, 768>(lsink));
   check(hipFree(lsink), "hipFree");
+
+  // softmax instruction mix beside MFMAs, 3 waves per SIMD
+  float* msink = nullptr;
+  check(hipMalloc(&msink, size_t(kCUs) * 768 * sizeof(float)), "hipMalloc");
+  const float mf = step_ns([&] { hipLaunchKernelGGL(mix_mfma_only, dim3(kCUs), dim3(768), 0, nullptr, msink); });
+  std::printf("softmax vector work of one P.V step (per SIMD: 3 waves x 32 scores per lane) beside its 8 MFMAs\n");
+  std::printf("  %-22s %7.1f ns\n", "8 MFMAs alone", mf);
+  mix_row<MIX_EXP_PACK_DOT2>("exp2 + pack + v_dot2", msink, mf);
+  mix_row<MIX_EXP_PACK_ADD>("exp2 + pack + fp32 add", msink, mf);
+  mix_row<MIX_EXP>("exp2", msink, mf);
+  mix_row<MIX_PACK>("pack (cvt_pk_bf16)", msink, mf);
+  mix_row<MIX_DOT2>("v_dot2", msink, mf);
+  mix_row<MIX_FMA>("fma", msink, mf);
+  std::printf("whole key tile (16 MFMAs + softmax) per SIMD, 3 waves\n");
+  tile_row<0, 0>("serial, v_dot2 row sums", msink);
+  tile_row<0, 1>("serial, fp32-add row sums", msink);
+  tile_row<1, 0>("next scores interleaved, v_dot2 row sums", msink);
+  tile_row<1, 1>("next scores interleaved, fp32-add row sums", msink);
+  check(hipFree(msink), "hipFree");
 
   // wave placement
   int* wsink = nullptr;
