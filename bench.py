@@ -150,6 +150,40 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 5}), flush=True)
 
 
+def mfma_ceiling(sizes=(8192, 16384)):
+    """The vendor library's bf16 GEMM (torch.matmul -> hipBLASLt) on square
+    products, operands drawn from N(0, 1) and, with the same instructions,
+    all zeros and all ones: what fraction of the 2.5 PF figure the chip
+    sustains on bf16 MFMA work with and without data switching in its
+    operands (HIP events around the timed calls)."""
+    import torch
+    out = []
+    for n in sizes:
+        g = torch.Generator(device="cuda").manual_seed(0)
+        a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+        b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+        for name, (x, y) in (("randn", (a, b)), ("zeros", (torch.zeros_like(a), torch.zeros_like(b))),
+                             ("ones", (torch.ones_like(a), torch.ones_like(b)))):
+            reps = 20 if n > 8192 else 50
+            for _ in range(5):
+                torch.matmul(x, y)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                torch.matmul(x, y)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            tf = 2.0 * n ** 3 / ms / 1e9
+            rec = {"n": n, "operands": name, "ms": round(ms, 4), "tflops": round(tf, 1),
+                   "frac_of_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+            out.append(rec)
+            print(json.dumps(rec), flush=True)
+        del a, b
+    return out
+
+
 KERNEL_MATCH = {"attn": ("attn_bf16_kernel", "attn_bf16.hip")}
 
 
@@ -529,6 +563,9 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain fp32 copy kernel (y = x * 1) over MIB MiB, 5 times, and exit: the "
                          "reference for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only time the vendor bf16 GEMM (hipBLASLt) at 8192^3 and 16384^3 on random, zero and "
+                         "one operands, and exit: the bf16 MFMA rate this chip sustains with real data")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("CLASS", "WORKLOAD"),
                     help="write profiles/traffic_CLASS_WORKLOAD.json from the four CSVs below and exit")
     ap.add_argument("--pmc-fetch")
@@ -544,6 +581,9 @@ def main():
         return
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.mfma_ceiling:
+        mfma_ceiling()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the tower runs on a single MI355X here "
