@@ -51,8 +51,7 @@ def memory_bound_bytes(wl):
     class (bf16 tower).
       norm:     the first pass reads X (4 B) and writes h (4 B) and y (2 B);
                 each later attention norm reads h (4 B), writes y (2 B)
-      norm_mlp: each MLP norm reads h (4 B), writes y (2 B) + its fp4 low
-                part (1/2 B) + one scale byte per 32 values
+      norm_mlp: each MLP norm reads h (4 B), writes y in fp16 (2 B)
       operand:  im2col split: the pixels read once (3 p^2 fp32 per patch),
                 2 Kp bf16 written per patch; the merger's input split: 4 B
                 read, 2 B (bf16) + 1/2 B (fp4 low part) + one scale byte per
@@ -65,7 +64,7 @@ def memory_bound_bytes(wl):
     kp = math.ceil(3 * p * p / 64) * 64
     return {
         "norm": N * D * (10 + (L - 1) * 6),
-        "norm_mlp": N * D * L * (6 + 0.5 + 1 / 32),
+        "norm_mlp": N * D * L * 6,
         "operand": N * (3 * p * p * 4 + 2 * kp * 2) + N * D * ((6 + 0.5 + 1 / 32) if wl.merge == 2 else 6),
     }
 

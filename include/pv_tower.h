@@ -187,10 +187,12 @@ pv_status pv_tower_create(const pv_config* cfg, const pv_weights* w, pv_tower** 
 void pv_tower_destroy(pv_tower* t);
 
 /* Derived weight copies, made once instead of in every forward call: the
- * bf16 tower's patch weights zero-padded to the GEMM's K, and per block the
- * fp4 (e2m1, 32-k scale blocks) copy of the gate/up weights that multiplies
- * the MLP input's low part -- or, with PV_FLAG_FP8, the block-scaled e4m3
- * copies of all seven block matrices.
+ * bf16 tower's patch weights zero-padded to the GEMM's K, per block the fp16
+ * copy of the gate/up weights that multiplies the fp16 MLP input (round to
+ * nearest even, saturated to +-65504) -- or, with PV_FLAG_FP8, the
+ * block-scaled e4m3 copies of all seven block matrices -- and with merge 2
+ * the fp4 (e2m1, 32-k scale blocks) copy of the merge weights that
+ * multiplies the merger input's low part.
  * pv_tower_prepared_bytes: device bytes those copies need (0 for the fp32
  *   tower, which uses its weights as given).  Host-only.
  * pv_tower_prepare: writes the copies into mem (device, caller-owned,
@@ -286,11 +288,11 @@ enum {
                         weight copies when unprepared)                        */
   PV_K_ATTN = 4,     /* block-diagonal attention                              */
   PV_K_OPROJ = 5,    /* out-projection GEMM (+ residual)                      */
-  PV_K_GATEUP = 6,   /* MLP gate/up GEMM (silu * up) (+ the fp4 weight copy
+  PV_K_GATEUP = 6,   /* MLP gate/up GEMM (silu * up) (+ the fp16 weight copy
                         when unprepared)                                      */
   PV_K_DOWN = 7,     /* MLP down GEMM (+ residual)                            */
   PV_K_MERGE = 8,    /* 2x2 merge GEMM                                        */
-  PV_K_NORM_MLP = 9, /* RMSNorm passes before the MLP (bf16 + fp4 low part)   */
+  PV_K_NORM_MLP = 9, /* RMSNorm passes before the MLP (fp16 output)          */
   PV_K_OPERAND = 10, /* operand passes: im2col hi | lo split (or the uint8
                         resize into it), final residual hi | lo split or
                         output copy                                           */

@@ -48,7 +48,7 @@ def test_prepared_equals_per_call_copies(flags):
     torch.cuda.synchronize()
     assert torch.equal(oa, ob)
     # launches per class: the prepared tower skips the patch-weight padding
-    # and, per block, the fp4 gate/up copy (fp8: the seven fp8 copies)
+    # and, per block, the fp16 gate/up copy (fp8: the seven fp8 copies)
     counts = []
     for tw in (a, b):
         tw.set_profiling(True)

@@ -1,6 +1,6 @@
-// Device-side helpers shared by the gfx950 kernels: vector types, bf16
-// conversion, MFMA wrappers, wavefront reductions and the kernel-argument
-// structs.  CDNA4 only (wave64, MFMA 32x32x16 bf16).
+// Device-side helpers shared by the gfx950 kernels: vector types, bf16 and
+// fp16 conversion, MFMA wrappers, wavefront reductions and the
+// kernel-argument structs.  CDNA4 only (wave64, MFMA 32x32x16 bf16 / fp16).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,6 +16,8 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -40,6 +42,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Largest finite fp16 value.
+constexpr float kF16Max = 65504.f;
+
+// Two floats -> packed fp16 pair, round to nearest even, saturated to the
+// finite range (a value past +-65504 becomes +-65504, not infinity).
+__device__ __forceinline__ uint32_t pack_f16x2_sat(float a, float b) {
+  halfx2 v;
+  v[0] = (_Float16)__builtin_amdgcn_fmed3f(a, -kF16Max, kF16Max);
+  v[1] = (_Float16)__builtin_amdgcn_fmed3f(b, -kF16Max, kF16Max);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ u32x4 pack8(const float* f) {
   u32x4 r;
   r[0] = pack_bf16x2(f[0], f[1]);
@@ -52,6 +66,11 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
 __device__ __forceinline__ floatx16 mfma32x32x16(const u32x4& a, const u32x4& b, const floatx16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// The same product on fp16 operands (8 fp16 values per lane and operand).
+__device__ __forceinline__ floatx16 mfma32x32x16_f16(const u32x4& a, const u32x4& b, const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a),
+                                                 __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
 }
 
 // Value of the neighbouring lane (lane ^ 1) via DPP quad permute [1,0,3,2].
@@ -142,6 +161,7 @@ struct GemmArgs {
   const void* Bs;
   int32_t k8, as_rows, bs_rows;
   int32_t low_fmt;
+  int32_t f16;        // 1: A and B are fp16 (fp16 MFMAs for the 16-bit k range), else bf16
   void* C;
   int32_t ldc;
   int32_t hidden;     // D (QKV split, merge gather)

@@ -1,13 +1,13 @@
-// bf16 GEMM family on CDNA4 MFMA (v_mfma_f32_32x32x16_bf16):
+// bf16 GEMM family on CDNA4 MFMA (v_mfma_f32_32x32x16_bf16, and _f16 for
+// the MLP gate/up product):
 //   C[M][N] = A[M][K] * B[N][K]^T  (fp32 accumulation)
 // covering every linear map of the tower ("Mistral 3" (KerasFormers),
 // Mistral3VisionModel and Mistral3Model table):
 //   patch embedding   A = im2col of the pixels as bf16 hi | lo, C fp32
 //   q,k,v             A = y, B rows from wq|wk|wv, epilogue rotates q and k
 //   out-projection    A = attention output, epilogue adds into the residual
-//   MLP gate/up       A = y (bf16), B rows interleave gate and up, then
-//                     the fp4 low part of y against fp4 gate/up weights;
-//                     epilogue silu(g) * u
+//   MLP gate/up       A = y (fp16), B rows interleave fp16 copies of gate
+//                     and up; epilogue silu(g) * u
 //   MLP down          epilogue adds into the residual
 //   merger            A = 2x2 gather of the final residual's bf16 rows, done
 //                     by the A-operand loads themselves, then its fp4 low
@@ -15,9 +15,11 @@
 //                     weights
 // The pixels enter as two bf16 halves hi and lo = bf16(x - hi) over a K
 // range twice as long, both against the same B rows (GemmArgs::kb): about
-// 16 significant bits on bf16 MFMAs.  The MLP input and the final residual
-// enter as bf16 plus their low part x - bf16(x) in fp4 (the LOW steps
-// below): about 11 bits.
+// 16 significant bits on bf16 MFMAs.  The final residual enters the merger
+// as bf16 plus its low part x - bf16(x) in fp4 (the LOW steps below), and
+// the MLP input enters gate/up in fp16 (its RMS-normalised values and the
+// weights sit well inside fp16's range): about 11 significant bits either
+// way, at the bf16 MFMA rate.
 #include <type_traits>
 
 #include "common.h"
@@ -292,7 +294,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[
 // 64 and supplies the scale of its row's 32-k block h (byte 0 of its scale
 // operand); for fp4 the lane's 16 operand bytes are one 32-k block (k
 // [32h, 32h + 32) of the 64) and its scale byte scales exactly those values.
-template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int AMD, int BMD, int EM, int LOW = 0>
+template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int AMD, int BMD, int EM, int LOW = 0, bool F16 = false>
 __global__ __launch_bounds__(WMW * WNW * 64) __attribute__((amdgpu_waves_per_eu(WMW * WNW >= 8 ? 2 : 8 / (WMW * WNW))))
 void gemm_dense_kernel(GemmArgs g) {
   static_assert(AMD == A_DENSE || AMD == A_MERGE, "A operand mode");
@@ -586,7 +588,10 @@ void gemm_dense_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int jn = 0; jn < TN; ++jn) acc[i][jn] = mfma32x32x16(fa[ks & 1][i], fb[ks & 1][jn], acc[i][jn]);
+        for (int jn = 0; jn < TN; ++jn) {
+          if constexpr (F16) acc[i][jn] = mfma32x32x16_f16(fa[ks & 1][i], fb[ks & 1][jn], acc[i][jn]);
+          else acc[i][jn] = mfma32x32x16(fa[ks & 1][i], fb[ks & 1][jn], acc[i][jn]);
+        }
     });
 #if PV_GEMM_SCHED == 1
     // issue order: the first fragments, then per k-substep the next
@@ -723,7 +728,7 @@ void gemm_dense_kernel(GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int AMD, int BMD, int EM, int LOW = 0>
+template <int BM, int BN, int WMW, int WNW, int NS, int BKT, int AMD, int BMD, int EM, int LOW = 0, bool F16 = false>
 hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
   constexpr bool LO8 = LOW != 0;
   constexpr int KSTEP = LOW == 4 ? 256 : 128, SB = LOW == 4 ? 8 : 4;
@@ -743,7 +748,7 @@ hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
   constexpr int kLdsBytes = NS * ((BM + BN) * BKT * 2 + (LO8 ? (BM + BN) * SB : 0));
   constexpr int kPerCU = (160 * 1024) / kLdsBytes < 2 ? 1 : 2;
   const int grid = tiles < kNumCUs * kPerCU ? tiles : kNumCUs * kPerCU;
-  hipLaunchKernelGGL((gemm_dense_kernel<BM, BN, WMW, WNW, NS, BKT, AMD, BMD, EM, LOW>), dim3(grid),
+  hipLaunchKernelGGL((gemm_dense_kernel<BM, BN, WMW, WNW, NS, BKT, AMD, BMD, EM, LOW, F16>), dim3(grid),
                      dim3(WMW * WNW * 64), 0, s, g);
   return hipGetLastError();
 }
@@ -819,9 +824,13 @@ hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
       return g.k8 > 0 ? launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_ADD_F32, 8>(g, s)
                       : launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_ADD_F32>(g, s);
     case GEMM_GATEUP:
+      if (g.f16) {
+        if (g.k8 > 0) return hipErrorInvalidValue;
+        return launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL, 0, true>(g, s);
+      }
       if (g.k8 <= 0) return launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL>(g, s);
-      return g.low_fmt == 4 ? launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL, 4>(g, s)
-                            : launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL, 8>(g, s);
+      if (g.low_fmt != 8) return hipErrorInvalidValue;
+      return launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_GATEUP, E_SILU_MUL, 8>(g, s);
     case GEMM_MERGE:
       if (g.k8 > 0)
         return g.N % 256 == 0 ? launch_dense<PV_GEMM_CFG_MERGE, A_MERGE, B_ONE, E_STORE, 4>(g, s)

@@ -32,11 +32,9 @@ hipError_t gemm_f32(GemmKind kind, const GemmArgs& g, hipStream_t s);
 //   rmsnorm_dual: h = norm(x) * g1 written back in place (fp32), y = norm(h) * g2
 hipError_t rmsnorm(const float* x, const float* g, void* y, int rows, int D, float eps,
                    bool y_f32, hipStream_t s);
-// rmsnorm_hi_lo4: y = norm(x) * g as bf16 hi [N][D] plus the low part y - hi
-// in packed fp4 e2m1 [N][D/2] (low nibble = even column) with a power-of-two
-// scale byte per 32 columns, step-major: ys[(col / 256) * srows + row][(col / 32) % 8]
-hipError_t rmsnorm_hi_lo4(const float* x, const float* g, void* yh, void* y4, void* ys, int rows, int srows, int D,
-                          float eps, hipStream_t s);
+// rmsnorm_f16: y = norm(x) * g as fp16 [N][D] (round to nearest even,
+// saturated to +-65504)
+hipError_t rmsnorm_f16(const float* x, const float* g, void* y, int rows, int D, float eps, hipStream_t s);
 // rmsnorm_fp8: y = norm(x) * g as fp8 e4m3 [N][D] with a power-of-two scale
 // byte per 32 columns, step-major: ys[(col / 128) * srows + row][(col / 32) % 4]
 hipError_t rmsnorm_fp8(const float* x, const float* g, void* y8, void* ys, int rows, int srows, int D, float eps,
@@ -119,9 +117,10 @@ hipError_t gateup_fp8(const void* w_gate, const void* w_up, void* b8, void* bs, 
 //   rows_fp4:     a bf16 [rows][K] matrix in packed fp4 e2m1, b4 [rows][K/2],
 //                 bs [K/256][rows][8] scale bytes (K a multiple of 256)
 hipError_t rows_fp4(const void* w, int rows, int K, void* b4, void* bs, hipStream_t s);
-//   gateup_fp4:   the gate/up rows of gateup_fp8 in packed fp4 e2m1, b4 [2F][D/2],
-//                 bs [D/256][2F][8] scale bytes
-hipError_t gateup_fp4(const void* w_gate, const void* w_up, void* b4, void* bs, int F, int D, hipStream_t s);
+//   gateup_f16:   fp16 copies of the bf16 gate and up weights, h16 [2F][D] =
+//                 gate rows then up rows (round to nearest even, saturated to
+//                 +-65504; D * F a multiple of 8, 16-byte aligned rows)
+hipError_t gateup_f16(const void* w_gate, const void* w_up, void* h16, int F, int D, hipStream_t s);
 // Content keys of uint8 images (two 64-bit lanes per image, keys [n][2]
 // device); offsets[i] (host) is image i's byte offset from `images`, which
 // must be 4-byte aligned; src_hw host; ws: image_keys_workspace_bytes(n)

@@ -4,9 +4,9 @@
 //
 // One wavefront per row; each lane holds D/64 values as float4 chunks laid
 // out so one load instruction covers 1 KiB of contiguous row.  The residual
-// stream x is fp32; y is bf16 (or fp32 for the fp32 tower).  These passes are
-// HBM-bound: 4 bytes read + 2 (4) bytes written per element, 8 + 2 (4) for the
-// dual pass.
+// stream x is fp32; y is bf16 (fp16 for the MLP input of the bf16 tower,
+// fp32 for the fp32 tower).  These passes are HBM-bound: 4 bytes read + 2 (4)
+// bytes written per element, 8 + 2 (4) for the dual pass.
 #include "common.h"
 #include "kernels.h"
 
@@ -35,13 +35,21 @@ __device__ __forceinline__ float sumsq(const floatx4 (&v)[NC]) {
   return row_sum64(s);
 }
 
-template <int NC, bool YF32>
+// Output element types of the norm passes.
+enum NormOut { OUT_BF16 = 0, OUT_F32 = 1, OUT_F16 = 2 };
+
+template <int NC, int YT>
 __device__ __forceinline__ void store_row(void* y, size_t row, int D, int lane, const floatx4 (&v)[NC]) {
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
     const size_t o = row * D + size_t(i * 64 + lane) * 4;
-    if constexpr (YF32) {
+    if constexpr (YT == OUT_F32) {
       *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(y) + o) = v[i];
+    } else if constexpr (YT == OUT_F16) {
+      u32x2 p;
+      p[0] = pack_f16x2_sat(v[i][0], v[i][1]);
+      p[1] = pack_f16x2_sat(v[i][2], v[i][3]);
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(y) + o) = p;
     } else {
       u32x2 p;
       p[0] = pack_bf16x2(v[i][0], v[i][1]);
@@ -70,9 +78,6 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
   return uint32_t(r);
 }
 
-// The MLP input: y = norm(x) * g as bf16 hi [N][D], and its low part y - hi
-// as packed fp4 [N][D/2] (low nibble = even column) with one scale byte per
-// 32 columns, scale bytes step-major: ys[(col / 256) * srows + row][(col / 32) % 8].
 // Maximum over the 8 lanes of v's aligned 8-lane group, by DPP moves (no
 // LDS traffic): quad permutes [1,0,3,2] and [2,3,0,1], then the half-row
 // mirror (lane i of 8 takes lane 7 - i, pairing the two quads).
@@ -91,42 +96,6 @@ __device__ __forceinline__ uint32_t scale_word(uint32_t sbyte, int lane) {
   w |= uint32_t(__builtin_amdgcn_mov_dpp(int(w), 0x128, 0xF, 0xF, true));  // row_ror:8 (lane ^ 8 in a 16-lane row)
   w |= uint32_t(__shfl_xor(int(w), 16, 64));
   return w;
-}
-
-template <int NC>
-__global__ __launch_bounds__(256) void rmsnorm_hi_lo4_kernel(const float* __restrict__ x, const float* __restrict__ g,
-                                                             uint16_t* __restrict__ yh, uint8_t* __restrict__ y4,
-                                                             uint8_t* __restrict__ ys, int rows, int srows, float eps) {
-  constexpr int D = NC * 256;
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const floatx4* xr = reinterpret_cast<const floatx4*>(x + size_t(row) * D);
-  const floatx4* gr = reinterpret_cast<const floatx4*>(g);
-  floatx4 v[NC];
-#pragma unroll
-  for (int i = 0; i < NC; ++i) v[i] = xr[i * 64 + lane];
-  const float inv = rsqrtf(sumsq<NC>(v) * (1.f / D) + eps);
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    v[i] = v[i] * inv * gr[i * 64 + lane];
-    const int col = (i * 64 + lane) * 4;
-    u32x2 hi;
-    hi[0] = pack_bf16x2(v[i][0], v[i][1]);
-    hi[1] = pack_bf16x2(v[i][2], v[i][3]);
-    *reinterpret_cast<u32x2*>(yh + size_t(row) * D + col) = hi;
-    const float l0 = v[i][0] - lo_bf16(hi[0]), l1 = v[i][1] - hi_bf16(hi[0]);
-    const float l2 = v[i][2] - lo_bf16(hi[1]), l3 = v[i][3] - hi_bf16(hi[1]);
-    // block of 32 columns = 8 consecutive lanes
-    const float amax = max8(fmaxf(fmaxf(fabsf(l0), fabsf(l1)), fmaxf(fabsf(l2), fabsf(l3))));
-    float scale;
-    const uint32_t sbyte = mx_scale4(amax, scale);
-    *reinterpret_cast<uint16_t*>(y4 + size_t(row) * (D / 2) + col / 2) = uint16_t(pack_fp4x4(l0, l1, l2, l3, scale));
-    // the 8 scale bytes of this 256-column step (block b = lanes 8b..8b+7)
-    // as two 4-byte words, written by lanes 0 and 32
-    const uint32_t w = scale_word(sbyte, lane);
-    if ((lane & 31) == 0) *reinterpret_cast<uint32_t*>(ys + (size_t(i) * srows + row) * 8 + (lane >> 3)) = w;
-  }
 }
 
 // The merger's input (the final residual, fp32 [N][D]) as bf16 hi rows plus
@@ -201,9 +170,10 @@ __global__ __launch_bounds__(256) void rmsnorm_fp8_kernel(const float* __restric
   }
 }
 
-template <int NC, bool YF32>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, const float* __restrict__ g,
-                                                      void* __restrict__ y, int rows, float eps) {
+// One row per wave; YT: NormOut.
+template <int NC, int YT>
+__device__ __forceinline__ void rmsnorm_rows(const float* __restrict__ x, const float* __restrict__ g,
+                                             void* __restrict__ y, int rows, float eps) {
   constexpr int D = NC * 256;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -216,7 +186,21 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   const float inv = rsqrtf(sumsq<NC>(v) * (1.f / D) + eps);
 #pragma unroll
   for (int i = 0; i < NC; ++i) v[i] = v[i] * inv * gr[i * 64 + lane];
-  store_row<NC, YF32>(y, row, D, lane, v);
+  store_row<NC, YT>(y, row, D, lane, v);
+}
+
+template <int NC, bool YF32>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, const float* __restrict__ g,
+                                                      void* __restrict__ y, int rows, float eps) {
+  rmsnorm_rows<NC, YF32 ? OUT_F32 : OUT_BF16>(x, g, y, rows, eps);
+}
+
+// The MLP input of the bf16 tower in fp16 (saturated to +-65504: |y| is at
+// most sqrt(D) max|g|, since no value of a row exceeds sqrt(D) times its RMS).
+template <int NC>
+__global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const float* __restrict__ x, const float* __restrict__ g,
+                                                          void* __restrict__ y, int rows, float eps) {
+  rmsnorm_rows<NC, OUT_F16>(x, g, y, rows, eps);
 }
 
 template <int NC, bool YF32>
@@ -242,7 +226,7 @@ __global__ __launch_bounds__(256) void rmsnorm_dual_kernel(float* __restrict__ x
   const float inv2 = rsqrtf(sumsq<NC>(v) * (1.f / D) + eps);
 #pragma unroll
   for (int i = 0; i < NC; ++i) v[i] = v[i] * inv2 * g2r[i * 64 + lane];
-  store_row<NC, YF32>(y, row, D, lane, v);
+  store_row<NC, YF32 ? OUT_F32 : OUT_BF16>(y, row, D, lane, v);
 }
 
 __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ x, uint32_t* __restrict__ y,
@@ -272,16 +256,13 @@ hipError_t rmsnorm(const float* x, const float* g, void* y, int rows, int D, flo
   return hipErrorInvalidValue;
 }
 
-hipError_t rmsnorm_hi_lo4(const float* x, const float* g, void* yh, void* y4, void* ys, int rows, int srows, int D,
-                          float eps, hipStream_t s) {
+hipError_t rmsnorm_f16(const float* x, const float* g, void* y, int rows, int D, float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (D % 256 || srows < rows) return hipErrorInvalidValue;
   const dim3 grid((rows + 3) / 4), block(256);
-#define PV_CASE(NC)                                                                                    \
-  if (D == NC * 256) {                                                                                 \
-    hipLaunchKernelGGL((rmsnorm_hi_lo4_kernel<NC>), grid, block, 0, s, x, g, static_cast<uint16_t*>(yh), \
-                       static_cast<uint8_t*>(y4), static_cast<uint8_t*>(ys), rows, srows, eps);           \
-    return hipGetLastError();                                                                          \
+#define PV_CASE(NC)                                                                        \
+  if (D == NC * 256) {                                                                     \
+    hipLaunchKernelGGL((rmsnorm_f16_kernel<NC>), grid, block, 0, s, x, g, y, rows, eps); \
+    return hipGetLastError();                                                              \
   }
   PV_NORM_CASES(PV_CASE)
 #undef PV_CASE

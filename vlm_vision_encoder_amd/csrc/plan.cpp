@@ -143,13 +143,22 @@ int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, P
   L.wpad = off;
   off = align256(off + (p.elem_bytes == 2 && !p.prepared ? D * size_t(patch_kp(p.patch)) * 2 : 0));
   if (p.elem_bytes == 2) {
-    const size_t F = size_t(p.mlp);
-    const size_t KA = p.fp8 ? std::max(D, F) : D;  // widest fp8 A operand
+    // fp8 variant: every fp8 GEMM input (up to [N][max(D, F)]) and its scale
+    // bytes; merge == 2: the merger input's fp4 low part [T][2D] and its scale
+    // bytes
+    size_t a8_bytes = 0, as_bytes = 0;
+    if (p.fp8) {
+      const size_t KA = std::max(D, size_t(p.mlp));
+      a8_bytes = N * KA;
+      as_bytes = (KA / 128) * size_t(a8_scale_rows(int64_t(N))) * 4;
+    }
+    if (p.merge_rows > 0) {
+      a8_bytes = std::max(a8_bytes, size_t(toks) * 2 * D);
+      as_bytes = std::max(as_bytes, (D / 64) * size_t(a8_scale_rows(int64_t(toks))) * 8);
+    }
     L.a8 = off;
-    off = align256(off + N * KA);  // (>= the merger's [T][2D] low part: T <= N / 4)
+    off = align256(off + a8_bytes);
     L.as = off;
-    size_t as_bytes = (KA / 128) * size_t(a8_scale_rows(int64_t(N))) * 4;
-    if (p.merge_rows > 0) as_bytes = std::max(as_bytes, (D / 64) * size_t(a8_scale_rows(int64_t(toks))) * 8);
     off = align256(off + as_bytes);
   }
   if (p.elem_bytes == 2 && !p.prepared && p.merge_rows > 0) {
@@ -159,11 +168,13 @@ int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, P
     off = align256(off + merge_fp4_scale_bytes(p.merge_rows, p.hidden));
   }
   if (p.elem_bytes == 2 && !p.prepared) {
+    // this layer's gate/up weights: fp16 [2F][D] (bf16 tower), or fp8 [2F][D]
+    // and its scale bytes (fp8 variant)
     const size_t F = size_t(p.mlp), F2 = 2 * F;
     L.b8 = off;
-    off = align256(off + F2 * D);
+    off = align256(off + F2 * D * (p.fp8 ? 1 : 2));
     L.bs = off;
-    off = align256(off + (D / 128) * F2 * 4);
+    off = align256(off + (p.fp8 ? (D / 128) * F2 * 4 : 0));
     if (p.fp8) {
       L.wq8 = off;
       off = align256(off + 3 * D * D);
@@ -208,11 +219,10 @@ PrepLayout prep_layout(int32_t patch, int32_t hidden, int32_t mlp, int32_t layer
     lo = align256(lo + D * F);
     P.wds = lo;
     lo = align256(lo + (F / 128) * D * 4);
-  } else {
+  } else {  // fp16 gate rows, then up rows
     P.b8 = lo;
-    lo = align256(lo + F2 * D / 2);
+    lo = align256(lo + F2 * D * 2);
     P.bs = lo;
-    lo = align256(lo + (D / 256) * F2 * 8);
   }
   P.layer_stride = lo;
   off += size_t(layers > 0 ? layers : 0) * lo;

@@ -82,8 +82,8 @@ struct PlanParams {
 // preparation fills (bf16 tower; every region 256-byte aligned):
 //   wpad  [D][Kp] bf16, the patch weights zero-padded to Kp
 //   per layer l, at layer0 + l * layer_stride:
-//     fp4 copies (bf16 tower): b4 [2F][D/2] gate/up in the GEMM's interleaved
-//       row order, bs4 [D/256][2F][8] scale bytes
+//     fp16 copy (bf16 tower): b8 [2F][D] fp16, the gate rows then the up
+//       rows (bs empty)
 //     fp8 copies (fp8 variant): wq8 [3D][D] + wqs [D/128][3D][4], wo8 [D][D] +
 //       wos [D/128][D][4], b8 [2F][D] + bs8 [D/128][2F][4], wd8 [D][F] + wds
 //       [F/128][D][4]
@@ -117,9 +117,9 @@ struct Layout {
   size_t meta = 0, items = 0, rope = 0, src = 0, rowinfo = 0, msrc = 0;
   size_t r = 0, y = 0, big = 0;
   size_t wpad = 0;          // bf16 tower: patch weights zero-padded to [D][Kp]
-  // bf16 tower: the MLP input's fp4 low part and the gate/up weights in fp4
-  // (fp8 variant: a8/as hold every fp8 GEMM input, up to [N][max(D, F)], and
-  // b8/bs this layer's gate/up weights in fp8):
+  // bf16 tower, unprepared: b8 holds this layer's gate/up weights in fp16
+  // [2F][D] (bs empty); fp8 variant: a8/as hold every fp8 GEMM input, up to
+  // [N][max(D, F)], and b8/bs this layer's gate/up weights in fp8
   size_t a8 = 0, as = 0, b8 = 0, bs = 0;
   // bf16 tower with merge == 2: the merger input's low part goes through
   // a8 / as ([T][2D] fp4 in merged-token order, [4D/256][T + 256][8] scale

@@ -17,11 +17,11 @@
 //                 (x - mean_c) / std_c (Mistral3ImageProcessor table), folded
 //                 into one multiply-add per channel.
 //   resize_norm_u8: the same samples written out as fp32 planes.
-//   gateup_fp4:   fp4 e2m1 copy of the gate/up weights in the GEMM's
-//                 interleaved row order, one power-of-two scale per 32 k, for
-//                 the fp4 product with the MLP input's low part.
-//   rows_fp4:     the same for a plain matrix (the merge weights, against the
-//                 merger input's low part).
+//   gateup_f16:   fp16 copies of the gate and up weights for the fp16
+//                 gate/up product (bf16 values convert exactly inside fp16's
+//                 normal range).
+//   rows_fp4:     fp4 e2m1 copy of a matrix, one power-of-two scale per 32 k
+//                 (the merge weights, against the merger input's low part).
 //   gateup_fp8, quant_rows_fp8: fp8 e4m3 copies of weights and activations
 //                 for the fp8 variant of the tower's linear maps.
 #include "common.h"
@@ -388,19 +388,17 @@ __global__ __launch_bounds__(256) void rows_fp4_kernel(const uint16_t* __restric
   bs[(size_t(blk / 8) * rows + n) * 8 + (blk & 7)] = uint8_t(sbyte);
 }
 
-__global__ __launch_bounds__(256) void gateup_fp4_kernel(const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
-                                                         uint8_t* __restrict__ b4, uint8_t* __restrict__ bs, int F,
-                                                         int D) {
-  const int blocks = D / 32;
-  const long long idx = blockIdx.x * 256ll + threadIdx.x;
-  if (idx >= 2ll * F * blocks) return;
-  const int n = int(idx / blocks), blk = int(idx - (long long)n * blocks);
-  const int src_row = (n >> 6) * 32 + (n & 31);
-  const uint16_t* src = ((n & 32) ? wu : wg) + size_t(src_row) * D + blk * 32;
+// Eight values a thread: the gate matrix then the up matrix (n8 16-byte
+// chunks each) as fp16.
+__global__ __launch_bounds__(256) void gateup_f16_kernel(const u32x4* __restrict__ wg, const u32x4* __restrict__ wu,
+                                                         u32x4* __restrict__ h16, long long n8) {
+  const long long i = blockIdx.x * 256ll + threadIdx.x;
+  if (i >= 2 * n8) return;
+  const u32x4 v = i < n8 ? wg[i] : wu[i - n8];
   u32x4 o;
-  const uint32_t sbyte = fp4_block32(src, o);
-  *reinterpret_cast<u32x4*>(b4 + size_t(n) * (D / 2) + blk * 16) = o;
-  bs[(size_t(blk / 8) * (2 * F) + n) * 8 + (blk & 7)] = uint8_t(sbyte);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = pack_f16x2_sat(lo_bf16(v[j]), hi_bf16(v[j]));
+  h16[i] = o;
 }
 
 // One thread per (row r, block of 32 columns) of a bf16 [rows][K] matrix;
@@ -485,12 +483,12 @@ hipError_t quant_rows_fp8(const void* src, int rows, int K, void* dst8, void* sc
   return hipGetLastError();
 }
 
-hipError_t gateup_fp4(const void* w_gate, const void* w_up, void* b4, void* bs, int F, int D, hipStream_t s) {
+hipError_t gateup_f16(const void* w_gate, const void* w_up, void* h16, int F, int D, hipStream_t s) {
   if (F <= 0) return hipSuccess;
-  if (D % 256) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gateup_fp4_kernel, grid_for(2ll * F * (D / 32)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
-                     static_cast<uint8_t*>(b4), static_cast<uint8_t*>(bs), F, D);
+  const long long n = (long long)F * D;
+  if (D <= 0 || n % 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gateup_f16_kernel, grid_for(2 * (n / 8)), dim3(256), 0, s, static_cast<const u32x4*>(w_gate),
+                     static_cast<const u32x4*>(w_up), static_cast<u32x4*>(h16), n / 8);
   return hipGetLastError();
 }
 

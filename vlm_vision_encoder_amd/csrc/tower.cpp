@@ -417,14 +417,14 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
       PV_LAUNCH(PV_K_OPROJ, gemm(pv::GEMM_OPROJ, a));
     }
     if (stop_here && st.stage == PV_STAGE_ATTN_RESID) return copy_stage(st, r, size_t(N) * D * 4, s);
-    // the MLP input of the bf16 tower goes in as bf16 plus its low part in
-    // fp4 (times fp4 copies of the weights, 32-k scale blocks): its plain
-    // bf16 rounding would otherwise be the largest error of the tower output
+    // the MLP input of the bf16 tower goes in as fp16 (times fp16 copies of
+    // the gate/up weights): its bf16 rounding would otherwise be the largest
+    // error of the tower output
     if (f8) {
       PV_LAUNCH(PV_K_NORM_MLP, pv::rmsnorm_fp8(r, lw.ffn_norm, a8, as, N, srows, D, eps, s));
     } else if (bf) {
-      if (!t->prep) PV_LAUNCH(PV_K_GATEUP, pv::gateup_fp4(lw.w_gate, lw.w_up, wc.b8, wc.bs, F, D, s));
-      PV_LAUNCH(PV_K_NORM_MLP, pv::rmsnorm_hi_lo4(r, lw.ffn_norm, y, ws + L.a8, ws + L.as, N, srows, D, eps, s));
+      if (!t->prep) PV_LAUNCH(PV_K_GATEUP, pv::gateup_f16(lw.w_gate, lw.w_up, wc.b8, F, D, s));
+      PV_LAUNCH(PV_K_NORM_MLP, pv::rmsnorm_f16(r, lw.ffn_norm, y, N, D, eps, s));
     } else {
       PV_LAUNCH(PV_K_NORM_MLP, pv::rmsnorm(r, lw.ffn_norm, y, N, D, eps, true, s));
     }
@@ -432,11 +432,11 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
       pv::GemmArgs a = g;
       a.M = N; a.N = F; a.K = D;
       a.A = y; a.lda = D;
-      if (bf) {
-        a.A8 = ws + L.a8; a.B8 = wc.b8; a.As = ws + L.as; a.Bs = wc.bs;
-        a.k8 = D; a.as_rows = srows; a.bs_rows = 2 * F; a.low_fmt = 4;
-      }
       a.B0 = lw.w_gate; a.B1 = lw.w_up; a.ldb = D;
+      if (bf && !f8) {  // fp16 y against the fp16 copies (gate rows, then up rows)
+        a.B0 = wc.b8; a.B1 = static_cast<char*>(wc.b8) + size_t(F) * D * 2;
+        a.f16 = 1;
+      }
       a.C = big; a.ldc = F;
       if (f8) use_fp8(a, D, wc.b8, wc.bs, 2 * F);
       PV_LAUNCH(PV_K_GATEUP, gemm(pv::GEMM_GATEUP, a));
@@ -819,7 +819,7 @@ pv_status pv_tower_prepare(pv_tower* t, void* mem, int64_t mem_bytes, void* stre
     if (f8)
       PV_HIP(make_fp8_copies(lw, wc, D, F, s));
     else
-      PV_HIP(pv::gateup_fp4(lw.w_gate, lw.w_up, wc.b8, wc.bs, F, D, s));
+      PV_HIP(pv::gateup_f16(lw.w_gate, lw.w_up, wc.b8, F, D, s));
   }
   if (P.mw4 || P.mws) PV_HIP(pv::rows_fp4(t->w.merge_w, merge_rows_of(c), 4 * D, m + P.mw4, m + P.mws, s));
   t->prep = m;
