@@ -188,8 +188,8 @@ void pv_tower_destroy(pv_tower* t);
 
 /* Derived weight copies, made once instead of in every forward call: the
  * bf16 tower's patch weights zero-padded to the GEMM's K, per block the fp16
- * copy of the gate/up weights that multiplies the fp16 MLP input (round to
- * nearest even, saturated to +-65504) -- or, with PV_FLAG_FP8, the
+ * copies of the gate, up and down weights for the MLP's fp16 products (round
+ * to nearest even, saturated to +-65504) -- or, with PV_FLAG_FP8, the
  * block-scaled e4m3 copies of all seven block matrices -- and with merge 2
  * the fp4 (e2m1, 32-k scale blocks) copy of the merge weights that
  * multiplies the merger input's low part.
@@ -238,7 +238,8 @@ pv_status pv_tower_forward(pv_tower* t, const float* pixels, const int32_t* imag
  *                         the units of its softmax)
  *   PV_STAGE_ATTN         layer l: attention output      [N][D] cfg.dtype
  *   PV_STAGE_ATTN_RESID   layer l: h after attention     [N][D] fp32
- *   PV_STAGE_MLP_HIDDEN   layer l: silu(gate)*up         [N][F] cfg.dtype
+ *   PV_STAGE_MLP_HIDDEN   layer l: silu(gate)*up         [N][F] fp16 (bf16
+ *                         tower; bf16 with PV_FLAG_FP8), fp32 (fp32 tower)
  *   PV_STAGE_BLOCK_OUT    layer l: h after the block     [N][D] fp32
  * Errors: as pv_tower_forward, PV_ERR_ARG for a bad stage or layer. */
 enum {
@@ -288,9 +289,10 @@ enum {
                         weight copies when unprepared)                        */
   PV_K_ATTN = 4,     /* block-diagonal attention                              */
   PV_K_OPROJ = 5,    /* out-projection GEMM (+ residual)                      */
-  PV_K_GATEUP = 6,   /* MLP gate/up GEMM (silu * up) (+ the fp16 weight copy
+  PV_K_GATEUP = 6,   /* MLP gate/up GEMM (silu * up) (+ the fp16 weight
+                        copies when unprepared)                               */
+  PV_K_DOWN = 7,     /* MLP down GEMM (+ residual) (+ the fp16 weight copy
                         when unprepared)                                      */
-  PV_K_DOWN = 7,     /* MLP down GEMM (+ residual)                            */
   PV_K_MERGE = 8,    /* 2x2 merge GEMM                                        */
   PV_K_NORM_MLP = 9, /* RMSNorm passes before the MLP (fp16 output)          */
   PV_K_OPERAND = 10, /* operand passes: im2col hi | lo split (or the uint8

@@ -467,15 +467,15 @@ def test_fp8_flag_validation_and_workspace():
         assert s8 == 0 and sb == 0
         # The fp8 variant adds its A operand at its widest ([N][F] fp8 and
         # 32-k scale bytes, in place of the merger's [T][2D] fp4 low part) and
-        # the fp8 q|k|v, out-projection and down weights; its gate/up copy is
-        # fp8 [2F][D] + scales where the bf16 tower holds fp16 [2F][D].
+        # the fp8 q|k|v, out-projection and down weights; its gate/up and down
+        # copies are fp8 + scales where the bf16 tower holds fp16 ones.
         rnd = lambda x: (x + 255) // 256 * 256  # noqa: E731
         N, Tk, D, F = 12100, 3025, 1024, 4096
         s8, sT = N + 256, Tk + 256
         a8 = rnd(N * F) + rnd(max(F // 128 * s8 * 4, D // 64 * sT * 8)) - rnd(Tk * 2 * D) - rnd(D // 64 * sT * 8)
         gateup = rnd(2 * F * D) + rnd(D // 128 * 2 * F * 4) - rnd(2 * F * D * 2)
         w8 = (rnd(3 * D * D) + rnd(D // 128 * 3 * D * 4) + rnd(D * D) + rnd(D // 128 * D * 4) + rnd(D * F)
-              + rnd(F // 128 * D * 4))
+              + rnd(F // 128 * D * 4) - rnd(D * F * 2))
         assert i8.workspace_bytes - ib.workspace_bytes == a8 + gateup + w8
         assert lib.pv_quantize_fp8(None, 4, 128, FAKE, FAKE, None) == -1
         assert lib.pv_quantize_fp8(FAKE, 4, 96, FAKE, FAKE, None) == -1
@@ -488,7 +488,7 @@ def test_fp8_flag_validation_and_workspace():
 
 def test_prepared_bytes_and_prepare_validation():
     """pv_tower_prepared_bytes: the padded patch weights plus, per block, the
-    fp16 gate/up copy (bf16 tower) or the seven fp8 matrices (fp8 variant),
+    fp16 gate, up and down copies (bf16 tower) or the seven fp8 matrices (fp8 variant),
     plus the fp4 copy of the merge weights [O][4D] and its scale bytes (merge
     2); nothing for the fp32 tower.  pv_tower_prepare's argument checks
     return before any device work."""
@@ -506,7 +506,7 @@ def test_prepared_bytes_and_prepare_validation():
         return h, b.value
 
     h, b = prepared(T.make_config(layers=L))
-    per_layer = rnd(2 * F * D * 2)  # the fp16 gate rows, then up rows
+    per_layer = rnd(2 * F * D * 2) + rnd(D * F * 2)  # fp16: gate rows then up rows; the down weights
     merge = rnd(O * 4 * D // 2) + rnd(4 * D // 256 * O * 8)
     assert b == rnd(D * Kp * 2) + L * per_layer + merge
     assert lib.pv_tower_prepare(None, FAKE * 256, b, None) == -1

@@ -80,21 +80,30 @@ class Case:
 
 
 # bf16 keeps 8 significant bits, so rounding a value x to bf16 moves it by
-# at most half an ulp <= 2^-8 |x|
+# at most half an ulp <= 2^-8 |x|; fp16 keeps 11: at most 2^-11 |x|
 BF16_ULP = 2.0 ** -8
+F16_ULP = 2.0 ** -11
 
 
-def check(name, got, want, tol, stored_bf16=False):
+def storage_ulp(t):
+    """Largest relative storage rounding of a 16-bit stage tensor."""
+    torch = _torch()
+    return F16_ULP if t.dtype == torch.float16 else BF16_ULP
+
+
+def check(name, got, want, tol, stored_bf16=False, ulp=BF16_ULP):
     """max|got - want| <= tol * RMS(want).  A tensor that the bf16 path stores
-    in bf16 is also allowed its own storage rounding (at most 2^-8 |want|)."""
+    in 16 bits is also allowed its own storage rounding (at most ulp |want|:
+    2^-8 for bf16, 2^-11 for fp16)."""
     want = np.asarray(want, np.float64)
     got = np.asarray(got, np.float64)
     rms = float(np.sqrt(np.mean(want * want)))
     diff = np.abs(got - want)
     if stored_bf16:
-        diff = np.maximum(diff - BF16_ULP * np.abs(want), 0.0)
+        diff = np.maximum(diff - ulp * np.abs(want), 0.0)
+    kind = ", bf16-stored" if ulp == BF16_ULP else ", fp16-stored"
     e = float(np.max(diff) / rms)
-    say(f"  {name}: max-abs-err/RMS = {e:.3e} (RMS {rms:.3e}, tol {tol}{', bf16-stored' if stored_bf16 else ''})")
+    say(f"  {name}: max-abs-err/RMS = {e:.3e} (RMS {rms:.3e}, tol {tol}{kind if stored_bf16 else ''})")
     assert np.isfinite(e) and e <= tol, f"{name}: {e} > {tol}"
 
 
@@ -195,8 +204,9 @@ def test_bf16_stages_single_image():
     ref = c.ref()
     for layer in range(2):
         for st in ALL_STAGES[2:]:
-            check(f"{st}[{layer}]", to_np(c.stage(st, layer)), oracle_stage(ref, wl, st, layer, c.w),
-                  TOL["bf16"], stored_bf16=st in BF16_STORED)
+            t = c.stage(st, layer)
+            check(f"{st}[{layer}]", to_np(t), oracle_stage(ref, wl, st, layer, c.w),
+                  TOL["bf16"], stored_bf16=st in BF16_STORED, ulp=storage_ulp(t))
     check("patch_embed", to_np(c.stage("patch_embed")), ref["patch_embed"], TOL["bf16"])
     check("ln_pre", to_np(c.stage("ln_pre")), ref["ln_pre"], TOL["bf16"])
     check("out", to_np(c.run()), ref["out"], TOL["bf16"], stored_bf16=True)

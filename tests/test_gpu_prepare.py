@@ -48,7 +48,8 @@ def test_prepared_equals_per_call_copies(flags):
     torch.cuda.synchronize()
     assert torch.equal(oa, ob)
     # launches per class: the prepared tower skips the patch-weight padding
-    # and, per block, the fp16 gate/up copy (fp8: the seven fp8 copies)
+    # and, per block, the fp16 gate, up and down copies (fp8: the seven fp8
+    # copies)
     counts = []
     for tw in (a, b):
         tw.set_profiling(True)
@@ -61,7 +62,8 @@ def test_prepared_equals_per_call_copies(flags):
     if flags:
         assert counts[0]["qkv"] == counts[1]["qkv"] - wl.layers
     else:
-        assert counts[0]["gateup"] == counts[1]["gateup"] - wl.layers
+        assert counts[0]["gateup"] == counts[1]["gateup"] - 2 * wl.layers
+        assert counts[0]["down"] == counts[1]["down"] - wl.layers
     # detaching returns to the per-call copies, with the same result
     a.unprepare()
     oc = a.forward(pix, wl.image_hw)

@@ -7,8 +7,9 @@
 //   q,k,v             A = y, B rows from wq|wk|wv, epilogue rotates q and k
 //   out-projection    A = attention output, epilogue adds into the residual
 //   MLP gate/up       A = y (fp16), B rows interleave fp16 copies of gate
-//                     and up; epilogue silu(g) * u
-//   MLP down          epilogue adds into the residual
+//                     and up; epilogue silu(g) * u, written in fp16
+//   MLP down          A = silu(g) * u (fp16) against an fp16 copy of the
+//                     weights; epilogue adds into the residual
 //   merger            A = 2x2 gather of the final residual's bf16 rows, done
 //                     by the A-operand loads themselves, then its fp4 low
 //                     part (gathered when it was written) against fp4 merge
@@ -17,9 +18,9 @@
 // range twice as long, both against the same B rows (GemmArgs::kb): about
 // 16 significant bits on bf16 MFMAs.  The final residual enters the merger
 // as bf16 plus its low part x - bf16(x) in fp4 (the LOW steps below), and
-// the MLP input enters gate/up in fp16 (its RMS-normalised values and the
-// weights sit well inside fp16's range): about 11 significant bits either
-// way, at the bf16 MFMA rate.
+// the MLP's two products take fp16 operands (the RMS-normalised input, the
+// silu * up values and the weights sit well inside fp16's range): about 11
+// significant bits either way, at the bf16 MFMA rate.
 #include <type_traits>
 
 #include "common.h"
@@ -131,7 +132,8 @@ __device__ __forceinline__ void load_residual_block(const GemmArgs& g, Residual<
   }
 }
 
-template <int EM, int TM, int TN, int SR, int NRB>
+// F16O: 16-bit outputs in fp16 (saturated to +-65504) instead of bf16
+template <int EM, int TM, int TN, int SR, int NRB, bool F16O>
 __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[TM][TN], int m_base, int n_base,
                                              int lane, float* scratch, const Residual<NRB>& res) {
   const int lrow = lane & 31, lhalf = lane >> 5;
@@ -252,7 +254,10 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, floatx16 (&acc)[
             x = acc[i][jb][v];
             ocol0 = n_base + 32 * jb;
           }
-          sh[rib * LDH + lrow] = __builtin_bit_cast(uint16_t, (bf16)x);
+          if constexpr (F16O)
+            sh[rib * LDH + lrow] = __builtin_bit_cast(uint16_t, (_Float16)__builtin_amdgcn_fmed3f(x, -kF16Max, kF16Max));
+          else
+            sh[rib * LDH + lrow] = __builtin_bit_cast(uint16_t, (bf16)x);
         }
         wave_lds_order();
 #pragma unroll
@@ -717,7 +722,7 @@ void gemm_dense_kernel(GemmArgs g) {
     // uses its own slice of it to stage the output
     __syncthreads();
     float* scratch = reinterpret_cast<float*>(lds[(step - 1) % NS]) + wave * kScratchFloats;
-    epilogue_lds<EM, TM, TN, kEpiRows, kPreBlocks>(g, acc, tm * BM + wm * TMW, tn * BN + wn * TNW, lane, scratch,
+    epilogue_lds<EM, TM, TN, kEpiRows, kPreBlocks, F16>(g, acc, tm * BM + wm * TMW, tn * BN + wn * TNW, lane, scratch,
                                                    res);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -818,6 +823,11 @@ hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
                       : launch_dense<PV_GEMM_CFG_QKV, A_DENSE, B_QKV, E_QKV_ROPE>(g, s);
     case GEMM_OPROJ:
     case GEMM_DOWN:
+      if (g.f16) {
+        if (g.k8 > 0) return hipErrorInvalidValue;
+        return wide ? launch_dense<PV_GEMM_CFG_RES_WIDE, A_DENSE, B_ONE, E_ADD_F32, 0, true>(g, s)
+                    : launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_ADD_F32, 0, true>(g, s);
+      }
       if (wide)
         return g.k8 > 0 ? launch_dense<PV_GEMM_CFG_RES_WIDE, A_DENSE, B_ONE, E_ADD_F32, 8>(g, s)
                         : launch_dense<PV_GEMM_CFG_RES_WIDE, A_DENSE, B_ONE, E_ADD_F32>(g, s);

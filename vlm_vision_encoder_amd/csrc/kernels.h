@@ -117,10 +117,9 @@ hipError_t gateup_fp8(const void* w_gate, const void* w_up, void* b8, void* bs, 
 //   rows_fp4:     a bf16 [rows][K] matrix in packed fp4 e2m1, b4 [rows][K/2],
 //                 bs [K/256][rows][8] scale bytes (K a multiple of 256)
 hipError_t rows_fp4(const void* w, int rows, int K, void* b4, void* bs, hipStream_t s);
-//   gateup_f16:   fp16 copies of the bf16 gate and up weights, h16 [2F][D] =
-//                 gate rows then up rows (round to nearest even, saturated to
-//                 +-65504; D * F a multiple of 8, 16-byte aligned rows)
-hipError_t gateup_f16(const void* w_gate, const void* w_up, void* h16, int F, int D, hipStream_t s);
+//   copy_f16:     n bf16 values -> fp16 (round to nearest even, saturated to
+//                 +-65504); n a multiple of 8, both pointers 16-byte aligned
+hipError_t copy_f16(const void* src, long long n, void* h16, hipStream_t s);
 // Content keys of uint8 images (two 64-bit lanes per image, keys [n][2]
 // device); offsets[i] (host) is image i's byte offset from `images`, which
 // must be 4-byte aligned; src_hw host; ws: image_keys_workspace_bytes(n)

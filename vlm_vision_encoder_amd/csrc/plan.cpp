@@ -169,12 +169,18 @@ int build_plan(const PlanParams& p, const int32_t* image_hw, int32_t n_images, P
   }
   if (p.elem_bytes == 2 && !p.prepared) {
     // this layer's gate/up weights: fp16 [2F][D] (bf16 tower), or fp8 [2F][D]
-    // and its scale bytes (fp8 variant)
+    // and its scale bytes (fp8 variant); bf16 tower: the down weights in
+    // fp16 [D][F]
     const size_t F = size_t(p.mlp), F2 = 2 * F;
     L.b8 = off;
     off = align256(off + F2 * D * (p.fp8 ? 1 : 2));
     L.bs = off;
     off = align256(off + (p.fp8 ? (D / 128) * F2 * 4 : 0));
+    if (!p.fp8) {
+      L.wd8 = off;
+      off = align256(off + D * F * 2);
+      L.wds = off;
+    }
     if (p.fp8) {
       L.wq8 = off;
       off = align256(off + 3 * D * D);
@@ -219,10 +225,13 @@ PrepLayout prep_layout(int32_t patch, int32_t hidden, int32_t mlp, int32_t layer
     lo = align256(lo + D * F);
     P.wds = lo;
     lo = align256(lo + (F / 128) * D * 4);
-  } else {  // fp16 gate rows, then up rows
+  } else {  // fp16: gate rows, then up rows; the down weights
     P.b8 = lo;
     lo = align256(lo + F2 * D * 2);
     P.bs = lo;
+    P.wd8 = lo;
+    lo = align256(lo + D * F * 2);
+    P.wds = lo;
   }
   P.layer_stride = lo;
   off += size_t(layers > 0 ? layers : 0) * lo;

@@ -82,8 +82,8 @@ struct PlanParams {
 // preparation fills (bf16 tower; every region 256-byte aligned):
 //   wpad  [D][Kp] bf16, the patch weights zero-padded to Kp
 //   per layer l, at layer0 + l * layer_stride:
-//     fp16 copy (bf16 tower): b8 [2F][D] fp16, the gate rows then the up
-//       rows (bs empty)
+//     fp16 copies (bf16 tower): b8 [2F][D] fp16, the gate rows then the up
+//       rows (bs empty), wd8 [D][F] fp16, the down weights (wds empty)
 //     fp8 copies (fp8 variant): wq8 [3D][D] + wqs [D/128][3D][4], wo8 [D][D] +
 //       wos [D/128][D][4], b8 [2F][D] + bs8 [D/128][2F][4], wd8 [D][F] + wds
 //       [F/128][D][4]
@@ -118,14 +118,16 @@ struct Layout {
   size_t r = 0, y = 0, big = 0;
   size_t wpad = 0;          // bf16 tower: patch weights zero-padded to [D][Kp]
   // bf16 tower, unprepared: b8 holds this layer's gate/up weights in fp16
-  // [2F][D] (bs empty); fp8 variant: a8/as hold every fp8 GEMM input, up to
-  // [N][max(D, F)], and b8/bs this layer's gate/up weights in fp8
+  // [2F][D] (bs empty) and wd8 its down weights in fp16 [D][F]; fp8
+  // variant: a8/as hold every fp8 GEMM input, up to [N][max(D, F)], and
+  // b8/bs this layer's gate/up weights in fp8
   size_t a8 = 0, as = 0, b8 = 0, bs = 0;
   // bf16 tower with merge == 2: the merger input's low part goes through
   // a8 / as ([T][2D] fp4 in merged-token order, [4D/256][T + 256][8] scale
   // bytes); unprepared, mw4 / mws hold the merge weights' fp4 copy
   size_t mw4 = 0, mws = 0;
   // fp8 variant: this layer's q|k|v, out-projection and down weights in fp8
+  // (wd8 / wds; the bf16 tower's fp16 down weights above use wd8 alone)
   size_t wq8 = 0, wqs = 0, wo8 = 0, wos = 0, wd8 = 0, wds = 0;
   size_t upload_bytes = 0;  // [0, upload_bytes) is filled by one host->device copy
   size_t total = 0;

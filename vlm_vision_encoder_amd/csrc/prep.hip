@@ -17,9 +17,9 @@
 //                 (x - mean_c) / std_c (Mistral3ImageProcessor table), folded
 //                 into one multiply-add per channel.
 //   resize_norm_u8: the same samples written out as fp32 planes.
-//   gateup_f16:   fp16 copies of the gate and up weights for the fp16
-//                 gate/up product (bf16 values convert exactly inside fp16's
-//                 normal range).
+//   copy_f16:     fp16 copy of a bf16 array (the gate, up and down weights
+//                 of the MLP's fp16 products; bf16 values convert exactly
+//                 inside fp16's normal range).
 //   rows_fp4:     fp4 e2m1 copy of a matrix, one power-of-two scale per 32 k
 //                 (the merge weights, against the merger input's low part).
 //   gateup_fp8, quant_rows_fp8: fp8 e4m3 copies of weights and activations
@@ -388,13 +388,12 @@ __global__ __launch_bounds__(256) void rows_fp4_kernel(const uint16_t* __restric
   bs[(size_t(blk / 8) * rows + n) * 8 + (blk & 7)] = uint8_t(sbyte);
 }
 
-// Eight values a thread: the gate matrix then the up matrix (n8 16-byte
-// chunks each) as fp16.
-__global__ __launch_bounds__(256) void gateup_f16_kernel(const u32x4* __restrict__ wg, const u32x4* __restrict__ wu,
-                                                         u32x4* __restrict__ h16, long long n8) {
+// Eight values a thread (n8 16-byte chunks of bf16) to fp16.
+__global__ __launch_bounds__(256) void copy_f16_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ h16,
+                                                       long long n8) {
   const long long i = blockIdx.x * 256ll + threadIdx.x;
-  if (i >= 2 * n8) return;
-  const u32x4 v = i < n8 ? wg[i] : wu[i - n8];
+  if (i >= n8) return;
+  const u32x4 v = src[i];
   u32x4 o;
 #pragma unroll
   for (int j = 0; j < 4; ++j) o[j] = pack_f16x2_sat(lo_bf16(v[j]), hi_bf16(v[j]));
@@ -483,12 +482,12 @@ hipError_t quant_rows_fp8(const void* src, int rows, int K, void* dst8, void* sc
   return hipGetLastError();
 }
 
-hipError_t gateup_f16(const void* w_gate, const void* w_up, void* h16, int F, int D, hipStream_t s) {
-  if (F <= 0) return hipSuccess;
-  const long long n = (long long)F * D;
-  if (D <= 0 || n % 8) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gateup_f16_kernel, grid_for(2 * (n / 8)), dim3(256), 0, s, static_cast<const u32x4*>(w_gate),
-                     static_cast<const u32x4*>(w_up), static_cast<u32x4*>(h16), n / 8);
+hipError_t copy_f16(const void* src, long long n, void* h16, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n % 8 || (reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(h16)) % 16)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_f16_kernel, grid_for(n / 8), dim3(256), 0, s, static_cast<const u32x4*>(src),
+                     static_cast<u32x4*>(h16), n / 8);
   return hipGetLastError();
 }
 

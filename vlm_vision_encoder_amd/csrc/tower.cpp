@@ -417,13 +417,16 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
       PV_LAUNCH(PV_K_OPROJ, gemm(pv::GEMM_OPROJ, a));
     }
     if (stop_here && st.stage == PV_STAGE_ATTN_RESID) return copy_stage(st, r, size_t(N) * D * 4, s);
-    // the MLP input of the bf16 tower goes in as fp16 (times fp16 copies of
-    // the gate/up weights): its bf16 rounding would otherwise be the largest
-    // error of the tower output
+    // the MLP of the bf16 tower runs its two products on fp16 operands (the
+    // input y, silu(gate) * up and fp16 copies of the weights): their bf16
+    // rounding would otherwise be the two largest errors of the tower output
     if (f8) {
       PV_LAUNCH(PV_K_NORM_MLP, pv::rmsnorm_fp8(r, lw.ffn_norm, a8, as, N, srows, D, eps, s));
     } else if (bf) {
-      if (!t->prep) PV_LAUNCH(PV_K_GATEUP, pv::gateup_f16(lw.w_gate, lw.w_up, wc.b8, F, D, s));
+      if (!t->prep) {  // this layer's gate rows, then up rows, in fp16
+        PV_LAUNCH(PV_K_GATEUP, pv::copy_f16(lw.w_gate, (long long)F * D, wc.b8, s));
+        PV_LAUNCH(PV_K_GATEUP, pv::copy_f16(lw.w_up, (long long)F * D, static_cast<char*>(wc.b8) + size_t(F) * D * 2, s));
+      }
       PV_LAUNCH(PV_K_NORM_MLP, pv::rmsnorm_f16(r, lw.ffn_norm, y, N, D, eps, s));
     } else {
       PV_LAUNCH(PV_K_NORM_MLP, pv::rmsnorm(r, lw.ffn_norm, y, N, D, eps, true, s));
@@ -448,6 +451,11 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
       a.A = big; a.lda = F;
       a.B0 = lw.w_down; a.ldb = F;
       a.C = r; a.ldc = D;
+      if (bf && !f8) {  // fp16 silu * up against the fp16 copy of w_down
+        if (!t->prep) PV_LAUNCH(PV_K_DOWN, pv::copy_f16(lw.w_down, (long long)D * F, wc.wd8, s));
+        a.B0 = wc.wd8;
+        a.f16 = 1;
+      }
       if (f8) {
         PV_LAUNCH(PV_K_DOWN, pv::quant_rows_fp8(big, N, F, a8, as, srows, 0, s));
         use_fp8(a, F, wc.wd8, wc.wds, D);
@@ -819,7 +827,11 @@ pv_status pv_tower_prepare(pv_tower* t, void* mem, int64_t mem_bytes, void* stre
     if (f8)
       PV_HIP(make_fp8_copies(lw, wc, D, F, s));
     else
-      PV_HIP(pv::gateup_f16(lw.w_gate, lw.w_up, wc.b8, F, D, s));
+    {
+      PV_HIP(pv::copy_f16(lw.w_gate, (long long)F * D, wc.b8, s));
+      PV_HIP(pv::copy_f16(lw.w_up, (long long)F * D, static_cast<char*>(wc.b8) + size_t(F) * D * 2, s));
+      PV_HIP(pv::copy_f16(lw.w_down, (long long)D * F, wc.wd8, s));
+    }
   }
   if (P.mw4 || P.mws) PV_HIP(pv::rows_fp4(t->w.merge_w, merge_rows_of(c), 4 * D, m + P.mw4, m + P.mws, s));
   t->prep = m;

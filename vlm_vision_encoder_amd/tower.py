@@ -387,9 +387,11 @@ class Tower:
         info = self.plan(image_hw)
         N, D, F = info.n_patches, self.cfg.hidden, self.cfg.mlp
         act = self._act_dtype()
+        # the bf16 tower's MLP hidden activation is fp16 (the down product's operand)
+        mlp = torch.float16 if act == torch.bfloat16 and not (self.cfg.flags & PV_FLAG_FP8) else act
         shapes = {"patch_embed": ((N, D), torch.float32), "ln_pre": ((N, D), torch.float32),
                   "qkv": ((N, 3 * D), act), "attn": ((N, D), act), "attn_resid": ((N, D), torch.float32),
-                  "mlp_hidden": ((N, F), act), "block_out": ((N, D), torch.float32)}
+                  "mlp_hidden": ((N, F), mlp), "block_out": ((N, D), torch.float32)}
         shape, dt = shapes[stage]
         dst = torch.empty(shape, dtype=dt, device="cuda")
         ws = self.workspace(info.workspace_bytes)
