@@ -209,7 +209,7 @@ def test_bf16_stages_single_image():
                   TOL["bf16"], stored_bf16=st in BF16_STORED, ulp=storage_ulp(t))
     check("patch_embed", to_np(c.stage("patch_embed")), ref["patch_embed"], TOL["bf16"])
     check("ln_pre", to_np(c.stage("ln_pre")), ref["ln_pre"], TOL["bf16"])
-    check("out", to_np(c.run()), ref["out"], TOL["bf16"], stored_bf16=True)
+    check("out", to_np(c.run()), ref["out"], TOL["bf16"])
 
 
 def test_bf16_packed_ragged_batch():
@@ -218,7 +218,7 @@ def test_bf16_packed_ragged_batch():
     say(f"bf16 packed ragged {wl.image_hw}, 3 layers")
     c = Case(wl)
     ref = c.ref()
-    check("out", to_np(c.run()), ref["out"], TOL["bf16"], stored_bf16=True)
+    check("out", to_np(c.run()), ref["out"], TOL["bf16"])
     check("block_out[2]", to_np(c.stage("block_out", 2)), ref["block_out"][2], TOL["bf16"])
     # the same tower writing an fp32 output buffer: no storage rounding
     import torch
@@ -237,7 +237,7 @@ def test_bf16_no_merge_patch16_single_patch_image():
     ref = c.ref()
     out = c.run()
     assert tuple(out.shape) == (wl.n_patches, 1024)
-    check("out", to_np(out), ref["out"], TOL["bf16"], stored_bf16=True)
+    check("out", to_np(out), ref["out"], TOL["bf16"])
 
 
 def test_bf16_merger_width_not_multiple_of_256():
@@ -249,7 +249,7 @@ def test_bf16_merger_width_not_multiple_of_256():
     ref = c.ref()
     out = c.run()
     assert tuple(out.shape) == (wl.out_rows, 384)
-    check("out", to_np(out), ref["out"], TOL["bf16"], stored_bf16=True)
+    check("out", to_np(out), ref["out"], TOL["bf16"])
 
 
 def test_bf16_many_tiny_images():
@@ -262,7 +262,7 @@ def test_bf16_many_tiny_images():
     say(f"bf16 {len(hw)} tiny images, {wl.n_patches} patches")
     c = Case(wl)
     ref = c.ref()
-    check("out", to_np(c.run()), ref["out"], TOL["bf16"], stored_bf16=True)
+    check("out", to_np(c.run()), ref["out"], TOL["bf16"])
 
 
 def test_bf16_wide_tiles_for_the_hidden_width_products():
@@ -276,7 +276,7 @@ def test_bf16_wide_tiles_for_the_hidden_width_products():
     check("patch_embed", to_np(c.stage("patch_embed")), ref["patch_embed"], TOL["bf16"])
     check("attn_resid[0]", to_np(c.stage("attn_resid", 0)), ref["attn_out"][0], TOL["bf16"])
     check("block_out[0]", to_np(c.stage("block_out", 0)), ref["block_out"][0], TOL["bf16"])
-    check("out", to_np(c.run()), ref["out"], TOL["bf16"], stored_bf16=True)
+    check("out", to_np(c.run()), ref["out"], TOL["bf16"])
 
 
 @pytest.mark.parametrize("hidden,heads,mlp", [(512, 8, 1024), (768, 12, 2048), (1536, 24, 3072), (2048, 32, 2048)])
@@ -287,14 +287,15 @@ def test_bf16_other_widths(hidden, heads, mlp):
     say(f"bf16 width D={hidden} heads={heads} F={mlp}")
     c = Case(wl)
     ref = c.ref()
-    check("out", to_np(c.run()), ref["out"], TOL["bf16"], stored_bf16=True)
+    check("out", to_np(c.run()), ref["out"], TOL["bf16"])
 
 
 def test_bf16_sharp_logits():
     """Logit std ~4 instead of ~0.4.  bf16 storage of q and k moves every
     logit s by up to about 2^-8 |s| (two half-ulp roundings), which moves the
-    softmax weights by that relative amount, so the bound is
-    2e-2 + 2^-8 * max|s| (max|s| from the oracle's own q, k)."""
+    softmax weights by that relative amount, so the bound of the attention
+    stage is 2e-2 + 2^-8 * max|s| (max|s| from the oracle's own q, k); the
+    tower output is held to the plain 2e-2."""
     wl = _bf16_small([(308, 196), (84, 56)], 1)
     w = synth.make_weights(wl)
     rng = np.random.default_rng(77)
@@ -317,7 +318,9 @@ def test_bf16_sharp_logits():
     say(f"  max |logit| {smax:.2f} -> tol {tol:.3f}")
     assert smax > 10.0  # the case is really sharp
     check("attn[0]", to_np(c.stage("attn", 0)), oracle_stage(ref, wl, "attn", 0, w), tol, stored_bf16=True)
-    check("out", to_np(c.run()), ref["out"], tol, stored_bf16=True)
+    # the one-block tower's output (after the out-projection, the MLP and the
+    # merger) stays within the plain bar
+    check("out", to_np(c.run()), ref["out"], TOL["bf16"])
 
 
 def test_bf16_online_max_softmax_path():
@@ -331,7 +334,7 @@ def test_bf16_online_max_softmax_path():
     tw = T.Tower(T.config_for(wl, flags=T.PV_FLAG_ATTN_ONLINE_MAX), c.dev_w)
     out = tw.forward(c.pix, wl.image_hw)
     torch.cuda.synchronize()
-    check("out", to_np(out), ref["out"], TOL["bf16"], stored_bf16=True)
+    check("out", to_np(out), ref["out"], TOL["bf16"])
     att = to_np(tw.forward_stage(c.pix, wl.image_hw, "attn", 0))
     torch.cuda.synchronize()
     want = oracle_stage(ref, wl, "attn", 0, c.w)
@@ -370,7 +373,7 @@ def test_bf16_wide_attention_items(image_hw):
     att = to_np(tw.forward_stage(c.pix, wl.image_hw, "attn", 0))
     torch.cuda.synchronize()
     check_per_image("attn[0] online max", att, want, cu, TOL["bf16"], stored_bf16=True)
-    check("out", to_np(c.run()), ref["out"], TOL["bf16"], stored_bf16=True)
+    check("out", to_np(c.run()), ref["out"], TOL["bf16"])
     tw.close()
 
 
@@ -395,7 +398,7 @@ def test_rope_interleaved_flag(dtype):
     check("qkv[0]", got, want, TOL[dtype], stored_bf16=stored)
     out = to_np(tw.forward(c.pix, wl.image_hw))
     torch.cuda.synchronize()
-    check("out", out, ref["out"], TOL[dtype], stored_bf16=stored)
+    check("out", out, ref["out"], TOL[dtype])
     dflt = to_np(c.stage("qkv", 0))
     moved = float(np.max(np.abs(dflt - got)) / np.sqrt(np.mean(want * want)))
     say(f"  default split moves qkv by {moved:.3e} of RMS")
@@ -458,7 +461,7 @@ def test_zero_layer_tower_and_capacity_errors():
     say("bf16 zero-layer tower")
     c = Case(wl)
     ref = c.ref()
-    check("out", to_np(c.run()), ref["out"], TOL["bf16"], stored_bf16=True)
+    check("out", to_np(c.run()), ref["out"], TOL["bf16"])
 
 
 @pytest.mark.parametrize("case", ["narrow-3-images", "full-width"])
