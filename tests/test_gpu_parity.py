@@ -240,6 +240,28 @@ def test_bf16_no_merge_patch16_single_patch_image():
     check("out", to_np(out), ref["out"], TOL["bf16"])
 
 
+def test_bf16_mlp_fp16_range_saturates():
+    """The MLP's fp16 operands saturate at +-65504 instead of overflowing: a
+    norm weight of 4096 puts the MLP input of layer 0 at up to about
+    sqrt(1024) * 4096 = 131072 (past fp16's range), and the silu * up values
+    past it too.  The stage and the tower output stay finite (the oracle,
+    which does not saturate, is not the bar here)."""
+    torch = _torch()
+    wl = _bf16_small([(112, 84)], 1)
+    w = synth.make_weights(wl)
+    w["layers"][0]["ffn_norm"] = np.full_like(w["layers"][0]["ffn_norm"], 4096.0)
+    say("bf16 MLP input past fp16 range (ffn_norm = 4096)")
+    c = Case(wl, weights=w)
+    hid = c.stage("mlp_hidden", 0)
+    assert hid.dtype == torch.float16
+    hv = hid.float()
+    say(f"  mlp_hidden max |value| {hv.abs().max().item():.1f}")
+    assert torch.isfinite(hv).all().item()
+    assert hv.abs().max().item() == 65504.0  # some values really saturated
+    out = c.run()
+    assert torch.isfinite(out.float()).all().item()
+
+
 def test_bf16_merger_width_not_multiple_of_256():
     """Merger output width 384 (a multiple of 128 only): the merger GEMM takes
     its 256 x 128 tiles instead of 256 x 256."""
