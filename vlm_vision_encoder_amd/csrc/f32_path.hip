@@ -51,20 +51,25 @@ __device__ __forceinline__ float b_elem(const GemmArgs& g, int n, int k) {
   return b[size_t(r) * g.ldb + k];
 }
 
-// 64x64 output tile, 256 threads, 4x4 outputs per thread, k-tiles of 16.
-template <int AM, int BMD, int EM>
+// T x T output tile (T = 64 or 32), 256 threads, (T/16)^2 outputs per
+// thread, k-tiles of 16.  The 32 x 32 tiles give small products (few rows)
+// four times as many workgroups.
+template <int AM, int BMD, int EM, int T>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
-  __shared__ float as[16][68];
-  __shared__ float bs[16][68];
-  __shared__ float cs[64][65];
+  static_assert(T == 64 || T == 32, "tile");
+  static_assert(EM != E_SILU_MUL || T == 64, "silu-mul pairs the 32-column halves of a 64-column tile");
+  constexpr int R = T / 16;  // outputs per thread along each side
+  __shared__ float as[16][T + 4];
+  __shared__ float bs[16][T + 4];
+  __shared__ float cs[EM == E_SILU_MUL ? T : 1][T + 1];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const int tiles_n = (BMD == B_GATEUP ? 2 * g.N : g.N) / 64;
+  const int tiles_n = (BMD == B_GATEUP ? 2 * g.N : g.N) / T;
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
-  const int m0 = tm * 64, n0 = tn * 64;
-  float acc[4][4] = {};
+  const int m0 = tm * T, n0 = tn * T;
+  float acc[R][R] = {};
   for (int k0 = 0; k0 < g.K; k0 += 16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < T * 16 / 256; ++i) {
       const int e = tid + 256 * i, r = e >> 4, kk = e & 15;
       as[kk][r] = a_elem<AM>(g, m0 + r, k0 + kk);
       bs[kk][r] = b_elem<BMD>(g, n0 + r, k0 + kk);
@@ -72,24 +77,24 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
-      float av[4], bv[4];
+      float av[R], bv[R];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = as[kk][ty * 4 + i];
+      for (int i = 0; i < R; ++i) av[i] = as[kk][ty * R + i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = bs[kk][tx * 4 + j];
+      for (int j = 0; j < R; ++j) bv[j] = bs[kk][tx * R + j];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < R; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+        for (int j = 0; j < R; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
     }
     __syncthreads();
   }
   if constexpr (EM == E_SILU_MUL) {
     // tile columns [0,32) are gate units, [32,64) the matching up units
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < R; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) cs[ty * 4 + i][tx * 4 + j] = acc[i][j];
+      for (int j = 0; j < R; ++j) cs[ty * R + i][tx * R + j] = acc[i][j];
     __syncthreads();
     for (int e = tid; e < 64 * 32; e += 256) {
       const int r = e >> 5, cc = e & 31, row = m0 + r;
@@ -100,8 +105,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = m0 + ty * 4 + i;
+  for (int i = 0; i < R; ++i) {
+    const int row = m0 + ty * R + i;
     if (row >= g.M) continue;
     int pr = 0, pc = 0;
     if constexpr (EM == E_QKV_ROPE) {
@@ -110,8 +115,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       pc = rc & 0xffff;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + tx * 4 + j;
+    for (int j = 0; j < R; ++j) {
+      const int col = n0 + tx * R + j;
       float x = acc[i][j];
       if constexpr (EM == E_QKV_ROPE) {
         if (col < 2 * g.hidden) {
@@ -129,18 +134,36 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   }
 }
 
+// 64 x 64 tiles, or 32 x 32 where 64 x 64 tiles would not give every CU two
+// workgroups (not for silu-mul, whose tiles pair gate and up columns)
 template <int AM, int BMD, int EM>
 hipError_t launch(const GemmArgs& g, hipStream_t s) {
   const int ncols = (BMD == B_GATEUP) ? 2 * g.N : g.N;
   if (ncols % 64) return hipErrorInvalidValue;
   const int tiles = ((g.M + 63) / 64) * (ncols / 64);
-  hipLaunchKernelGGL((gemm_f32_kernel<AM, BMD, EM>), dim3(tiles), dim3(256), 0, s, g);
+  if (EM != E_SILU_MUL && tiles < 2 * kNumCUs) {
+    const int tiles32 = ((g.M + 31) / 32) * (ncols / 32);
+    hipLaunchKernelGGL((gemm_f32_kernel<AM, BMD, EM, (EM == E_SILU_MUL ? 64 : 32)>), dim3(tiles32), dim3(256), 0, s,
+                       g);
+  } else {
+    hipLaunchKernelGGL((gemm_f32_kernel<AM, BMD, EM, 64>), dim3(tiles), dim3(256), 0, s, g);
+  }
   return hipGetLastError();
 }
 
-// One wave per (64 queries, head): each lane owns one query, keys staged
-// through LDS 64 at a time, online softmax in fp32.
-__global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
+// One workgroup per (64 queries, head), four lanes per query: lane 4 q + j
+// holds dims [16 j, 16 j + 16) of query q and of its output.  A key's score
+// is the sum of the four lanes' partial dot products, formed by two DPP quad
+// permutes (lane ^ 1, then lane ^ 2; the four lanes add the same two pairs,
+// so they hold the same bits).  Keys staged through LDS 64 at a time, online
+// softmax in fp32.
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+  return v;
+}
+
+__global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   __shared__ float ks[64][65];
   __shared__ float vs[64][65];
   const int heads = a.heads;
@@ -150,19 +173,19 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   const int n = mt.Hp * mt.Wp, base = mt.patch_base, D = a.hidden;
   const size_t ld = size_t(3) * D;
   const float* qkv = reinterpret_cast<const float*>(a.qkv);
-  const int lane = threadIdx.x;
-  int t = it.q0 + lane;
+  const int tid = threadIdx.x, d0 = 16 * (tid & 3);
+  int t = it.q0 + (tid >> 2);
   const bool valid = t < n;
   t = valid ? t : n - 1;
-  float q[64], o[64];
-  for (int d = 0; d < 64; ++d) {
-    q[d] = qkv[size_t(base + t) * ld + head * 64 + d] * 0.125f;
+  float q[16], o[16];
+  for (int d = 0; d < 16; ++d) {
+    q[d] = qkv[size_t(base + t) * ld + head * 64 + d0 + d] * 0.125f;
     o[d] = 0.f;
   }
   float m_run = -INFINITY, l_run = 0.f;
   for (int k0 = 0; k0 < n; k0 += 64) {
     __syncthreads();
-    for (int e = lane; e < 64 * 64; e += 64) {
+    for (int e = tid; e < 64 * 64; e += 256) {
       const int r = e >> 6, d = e & 63;
       int u = k0 + r;
       u = u < n ? u : n - 1;
@@ -172,20 +195,23 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
     __syncthreads();
     const int cnt = (n - k0) < 64 ? (n - k0) : 64;
     for (int r = 0; r < cnt; ++r) {
-      float sc = 0.f;
-      for (int d = 0; d < 64; ++d) sc = __builtin_fmaf(q[d], ks[r][d], sc);
+      float part = 0.f;
+#pragma unroll
+      for (int d = 0; d < 16; ++d) part = __builtin_fmaf(q[d], ks[r][d0 + d], part);
+      const float sc = quad_sum(part);
       const float m_new = fmaxf(m_run, sc);
       const float alpha = expf(m_run - m_new);
       const float p = expf(sc - m_new);
       l_run = l_run * alpha + p;
-      for (int d = 0; d < 64; ++d) o[d] = o[d] * alpha + p * vs[r][d];
+#pragma unroll
+      for (int d = 0; d < 16; ++d) o[d] = o[d] * alpha + p * vs[r][d0 + d];
       m_run = m_new;
     }
   }
   if (!valid) return;
-  float* out = reinterpret_cast<float*>(a.out) + size_t(base + t) * D + head * 64;
+  float* out = reinterpret_cast<float*>(a.out) + size_t(base + t) * D + head * 64 + d0;
   const float inv = 1.f / l_run;
-  for (int d = 0; d < 64; ++d) out[d] = o[d] * inv;
+  for (int d = 0; d < 16; ++d) out[d] = o[d] * inv;
 }
 
 }  // namespace
@@ -209,7 +235,7 @@ hipError_t gemm_f32(GemmKind kind, const GemmArgs& g, hipStream_t s) {
 
 hipError_t attention_f32(const AttnArgs& a, hipStream_t s) {
   if (a.n_items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_f32_kernel, dim3(a.n_items * a.heads), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(attn_f32_kernel, dim3(a.n_items * a.heads), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
