@@ -117,9 +117,14 @@ __global__ __launch_bounds__(256) void merge_hi_lo4_kernel(const float* __restri
   if (t >= tokens) return;
   const int src = msrc[4 * t + j];
   const floatx4* xr = reinterpret_cast<const floatx4*>(x + size_t(src) * D);
+  // all of the row's loads first: one memory round trip per wave instead of
+  // one per 256 columns
+  floatx4 vr[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) vr[i] = xr[i * 64 + lane];
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
-    const floatx4 v = xr[i * 64 + lane];
+    const floatx4 v = vr[i];
     const int col = (i * 64 + lane) * 4;
     u32x2 hi;
     hi[0] = pack_bf16x2(v[0], v[1]);
@@ -150,13 +155,15 @@ __global__ __launch_bounds__(256) void rmsnorm_fp8_kernel(const float* __restric
   if (row >= rows) return;
   const floatx4* xr = reinterpret_cast<const floatx4*>(x + size_t(row) * D);
   const floatx4* gr = reinterpret_cast<const floatx4*>(g);
-  floatx4 v[NC];
+  floatx4 v[NC], gv[NC];
 #pragma unroll
   for (int i = 0; i < NC; ++i) v[i] = xr[i * 64 + lane];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) gv[i] = gr[i * 64 + lane];
   const float inv = rsqrtf(sumsq<NC>(v) * (1.f / D) + eps);
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
-    v[i] = v[i] * inv * gr[i * 64 + lane];
+    v[i] = v[i] * inv * gv[i];
     const int col = (i * 64 + lane) * 4;
     const float amax = max8(fmaxf(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])), fmaxf(fabsf(v[i][2]), fabsf(v[i][3]))));
     float mul;
