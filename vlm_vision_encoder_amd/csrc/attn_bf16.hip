@@ -30,9 +30,8 @@
 //   - q arrives multiplied by log2(e)/8 (by the q,k,v projection's epilogue,
 //     before its one rounding to bf16), so scores come out in exp2 units;
 //   - softmax is unchanged by a per-query offset, so each query takes the
-//     max of its first key tile as offset m0 and the offset is folded into
-//     the score MFMA as a 65th dimension (keys carry 1, the query carries
-//     -m0): no per-score subtraction and no running max;
+//     max of its first key tile as offset m0 and the score MFMAs start from
+//     -m0 instead of zero: no per-score subtraction and no running max;
 //   - row sums are fp32 adds of the probabilities (a tree per 8).  A
 //     v_dot2 on the packed bf16 pairs would take half the instructions, but
 //     it does not issue beside the MFMAs of the SIMD's other waves, while
@@ -175,22 +174,14 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[tb][ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
   }
-  // The fixed offset -m0 enters the scores of later tiles in one of two
-  // ways.  8-wave items (128 registers): as a 65th score dimension, one more
-  // MFMA per tile -- dimension 64 of every key is 1 and dimension 64 of
-  // query t is -m0(t) (lane half 0, element 0).  12-wave items (168
-  // registers): as the initial accumulator of the score MFMAs -- a lane's 16
-  // scores all belong to its one query column, so -m0 replicated in 16
-  // registers, set once after the first tile, serves every later tile (the
-  // MFMAs see the same operands, so the scores are the same bits).
-  constexpr bool kAccOffset = WAVES > 8;
-  const u32x4 a_off = {lhalf == 0 ? 0x3F80u : 0u, 0u, 0u, 0u};
-  u32x4 q_off[QB];
-  floatx16 c_off[kAccOffset ? QB : 1];
+  // The fixed offset -m0 enters the scores of later tiles as the initial
+  // accumulator of the score MFMAs: a lane's 16 scores all belong to its one
+  // query column, so -m0 replicated in 16 registers, set once after the
+  // first tile, serves every later tile at no instruction cost (an earlier
+  // form, a 65th score dimension, took one more MFMA per 32 keys).
+  floatx16 c_off[QB];
 #pragma unroll
-  for (int tb = 0; tb < QB; ++tb) q_off[tb] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int tb = 0; tb < (kAccOffset ? QB : 1); ++tb) c_off[tb] = floatx16{};
+  for (int tb = 0; tb < QB; ++tb) c_off[tb] = floatx16{};
 
   // transposed-read addresses for the V^T fragments: 16-lane group g gets
   // dims D0 + (lane % 16), keys U..U+3 (and U+4..U+7 from the second read)
@@ -215,8 +206,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
       for (int tb = 0; tb < QB; ++tb) {
         const floatx16 z = {};
-        if constexpr (MODE == 1 && kAccOffset) s[ub][tb] = c_off[kAccOffset ? tb : 0];
-        else if constexpr (MODE == 1) s[ub][tb] = mfma32x32x16(a_off, q_off[tb], z);
+        if constexpr (MODE == 1) s[ub][tb] = c_off[tb];
         else s[ub][tb] = z;
       }
 #pragma unroll
@@ -255,15 +245,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
           for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[ub][tb][v]);
         mx = pair_max32(mx);
         if constexpr (MODE == 0) {
-          // the offset is -m0 rounded to bf16, so that the later tiles'
-          // MFMA-folded offset is the very same number
-          const uint32_t mb = pack_bf16x2(-mx, 0.f) & 0xffffu;
-          q_off[tb] = u32x4{lhalf == 0 ? mb : 0u, 0u, 0u, 0u};
-          sub = lo_bf16(mb);
-          if constexpr (kAccOffset) {
+          sub = -mx;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) c_off[tb][v] = sub;
-          }
+          for (int v = 0; v < 16; ++v) c_off[tb][v] = sub;
         } else {
           if (__any(mx > m_sc[tb] + kRescaleSlack)) {
             const float m_new = fmaxf(m_sc[tb], mx);
