@@ -788,8 +788,10 @@ hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
 #endif
 // q,k,v: 384 x 192 tiles (16 per row of tiles) put the 1540 x 1540 image's
 // 32 rows of tiles on the 256 CUs in exactly two rounds (measured 3.5%
-// faster than 256 x 192 in three); the fp8 variant keeps 256 x 192 (its
-// scale blocks are padded for tiles of at most 256 rows)
+// faster than 256 x 192 in three; on the packed 8-image batch, whose 384-row
+// tiles leave a last round 70% full, 256 x 192 tiles were no faster); the
+// fp8 variant keeps 256 x 192 (its scale blocks are padded for tiles of at
+// most 256 rows)
 #ifndef PV_GEMM_CFG_QKV
 #define PV_GEMM_CFG_QKV 384, 192, 4, 2, 2, 64
 #endif
@@ -797,23 +799,30 @@ hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
 #define PV_GEMM_CFG_QKV8 256, 192, 4, 2, 2, 64
 #endif
 
-// N = hidden products: a 192 x 256 round of the chip (one tile per CU) takes
-// about 5/3 of a 128 x 128 round (two tiles per CU) -- measured at 1540^2
-// with K = 4096 -- so the wide tiles pay only when they save a partly
-// filled last round (1540^2: 256 tiles in one round against 760 tiles in
-// two rounds of 512 slots).
-bool use_res_wide(const GemmArgs& g) {
+// N = hidden products: what a 192 x 256 round of the chip (one tile per CU)
+// costs against a 128 x 128 round (two tiles per CU, 2/3 of the outputs),
+// measured on the packed 8-image, 64-image and 16-tile workloads: about
+// 4/3 for the patch embedding (a plain fp32 store), 7/5 for down (16-bit,
+// K = 4096: the larger tile's fewer L2 bytes per flop pay over the long k
+// loop) and 5/3 for the out-projection (K = 1024: the one workgroup's
+// residual read-modify-write is not hidden behind another's k loop; also
+// the fp8 products, whose k loop runs at twice the rate).  The wide tiles
+// are taken when they need enough fewer rounds to pay that (1540^2: 256
+// tiles in one round against 760 tiles in two rounds of 512 slots).
+bool use_res_wide(const GemmArgs& g, int cost_num, int cost_den) {
   if (g.N % 256) return false;
   const long long t_res = (long long)((g.M + 127) / 128) * (g.N / 128);
   const long long t_wide = (long long)((g.M + 191) / 192) * (g.N / 256);
   const long long r_res = (t_res + 2 * kNumCUs - 1) / (2 * kNumCUs);
   const long long r_wide = (t_wide + kNumCUs - 1) / kNumCUs;
-  return 5 * r_wide < 3 * r_res;
+  return r_wide * cost_num < r_res * cost_den;
 }
 
 hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
-  const bool wide = use_res_wide(g);
+  const bool wide = kind == GEMM_PATCH                   ? use_res_wide(g, 4, 3)
+                    : (g.k8 == 0 && g.K >= 2048) ? use_res_wide(g, 7, 5)
+                                                 : use_res_wide(g, 5, 3);
   switch (kind) {
     case GEMM_PATCH:
       return wide ? launch_dense<PV_GEMM_CFG_RES_WIDE, A_DENSE, B_ONE, E_STORE_F32>(g, s)
