@@ -799,30 +799,44 @@ hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
 #define PV_GEMM_CFG_QKV8 256, 192, 4, 2, 2, 64
 #endif
 
-// N = hidden products: what a 192 x 256 round of the chip (one tile per CU)
-// costs against a 128 x 128 round (two tiles per CU, 2/3 of the outputs),
-// measured on the packed 8-image, 64-image and 16-tile workloads: about
-// 4/3 for the patch embedding (a plain fp32 store), 7/5 for down (16-bit,
-// K = 4096: the larger tile's fewer L2 bytes per flop pay over the long k
-// loop) and 5/3 for the out-projection (K = 1024: the one workgroup's
-// residual read-modify-write is not hidden behind another's k loop; also
-// the fp8 products, whose k loop runs at twice the rate).  The wide tiles
-// are taken when they need enough fewer rounds to pay that (1540^2: 256
-// tiles in one round against 760 tiles in two rounds of 512 slots).
-bool use_res_wide(const GemmArgs& g, int cost_num, int cost_den) {
-  if (g.N % 256) return false;
-  const long long t_res = (long long)((g.M + 127) / 128) * (g.N / 128);
-  const long long t_wide = (long long)((g.M + 191) / 192) * (g.N / 256);
-  const long long r_res = (t_res + 2 * kNumCUs - 1) / (2 * kNumCUs);
-  const long long r_wide = (t_wide + kNumCUs - 1) / kNumCUs;
-  return r_wide * cost_num < r_res * cost_den;
+// N = hidden products (out-projection, down, patch embedding): 128 x 128
+// tiles (two workgroups per CU), 192 x 256 (one per CU) or, for the 16-bit
+// down product, 256 x 256 (one per CU), whichever needs the fewest rounds
+// of the chip weighted by what a round costs.  Costs in 30ths of a 128 x
+// 128 round, measured on the 1540^2, packed 8-image, 64-image and 16-tile
+// workloads:
+//   192 x 256: 40 for the patch embedding (a plain fp32 store), 42 for the
+//     16-bit down product (4096-deep k: the larger tile's fewer L2 bytes per
+//     flop pay over the long k loop), 50 for the out-projection (1024-deep
+//     k: the one workgroup's residual read-modify-write is not hidden behind
+//     another's k loop) and the fp8 products (their k loop runs at twice the
+//     rate);
+//   256 x 256: 51 for the 16-bit down product (packed 8-image batch 0.305 ->
+//     0.263 ms, 16 tiles 0.654 -> 0.548 ms, 64 images 0.559 -> 0.532 ms;
+//     at 1540^2 its 192 tiles leave a quarter of the CUs idle, and 256
+//     tiles of 192 x 256 fill one round); for the out-projection 256 x 256
+//     tiles were slower (packed 8-image batch 0.096 -> 0.107 ms).
+// Ties keep the smaller tile.
+enum ResTile { TILE_RES, TILE_WIDE, TILE_BIG };
+ResTile res_tile(const GemmArgs& g, long long c_wide, long long c_big) {
+  if (g.N % 256) return TILE_RES;
+  const long long rows128 = (g.M + 127) / 128, rows192 = (g.M + 191) / 192, rows256 = (g.M + 255) / 256;
+  const long long r_res = (rows128 * (g.N / 128) + 2 * kNumCUs - 1) / (2 * kNumCUs);
+  const long long r_wide = (rows192 * (g.N / 256) + kNumCUs - 1) / kNumCUs;
+  const long long r_big = (rows256 * (g.N / 256) + kNumCUs - 1) / kNumCUs;
+  ResTile t = TILE_RES;
+  long long best = 30 * r_res;
+  if (r_wide * c_wide < best) t = TILE_WIDE, best = r_wide * c_wide;
+  if (c_big > 0 && r_big * c_big < best) t = TILE_BIG;
+  return t;
 }
 
 hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
-  const bool wide = kind == GEMM_PATCH                   ? use_res_wide(g, 4, 3)
-                    : (g.k8 == 0 && g.K >= 2048) ? use_res_wide(g, 7, 5)
-                                                 : use_res_wide(g, 5, 3);
+  const ResTile rt = kind == GEMM_PATCH                                 ? res_tile(g, 40, 0)
+                     : (kind == GEMM_DOWN && g.f16 && g.K >= 2048) ? res_tile(g, 42, 51)
+                                                                   : res_tile(g, 50, 0);
+  const bool wide = rt == TILE_WIDE;
   switch (kind) {
     case GEMM_PATCH:
       return wide ? launch_dense<PV_GEMM_CFG_RES_WIDE, A_DENSE, B_ONE, E_STORE_F32>(g, s)
@@ -834,6 +848,7 @@ hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
     case GEMM_DOWN:
       if (g.f16) {
         if (g.k8 > 0) return hipErrorInvalidValue;
+        if (rt == TILE_BIG) return launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_ONE, E_ADD_F32, 0, true>(g, s);
         return wide ? launch_dense<PV_GEMM_CFG_RES_WIDE, A_DENSE, B_ONE, E_ADD_F32, 0, true>(g, s)
                     : launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_ADD_F32, 0, true>(g, s);
       }
