@@ -301,6 +301,19 @@ def test_bf16_wide_tiles_for_the_hidden_width_products():
     check("out", to_np(c.run()), ref["out"], TOL["bf16"])
 
 
+def test_bf16_down_product_in_256_tiles():
+    """16 images of 448^2 (16,384 patches, D 1024, MLP 4096): the down
+    product takes 256 x 256 tiles (64 rows x 4 columns of tiles, one round
+    of the chip against two of 128 x 128 or 192 x 256), the out-projection
+    and patch embedding 128 x 128 -- the MLP block's output checked in full."""
+    wl = _bf16_small([(448, 448)] * 16, 1)
+    say(f"bf16 down in 256x256 tiles: {wl.n_patches} patches")
+    c = Case(wl)
+    ref = c.ref()
+    check("block_out[0]", to_np(c.stage("block_out", 0)), ref["block_out"][0], TOL["bf16"])
+    check("out", to_np(c.run()), ref["out"], TOL["bf16"])
+
+
 @pytest.mark.parametrize("hidden,heads,mlp", [(512, 8, 1024), (768, 12, 2048), (1536, 24, 3072), (2048, 32, 2048)])
 def test_bf16_other_widths(hidden, heads, mlp):
     """The other supported widths (norm kernels of 2, 3, 6, 8 row chunks; q,k,v

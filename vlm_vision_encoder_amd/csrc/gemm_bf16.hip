@@ -805,7 +805,8 @@ hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
 // of the chip weighted by what a round costs.  Costs in 30ths of a 128 x
 // 128 round, measured on the 1540^2, packed 8-image, 64-image and 16-tile
 // workloads:
-//   192 x 256: 40 for the patch embedding (a plain fp32 store), 42 for the
+//   192 x 256: 39 for the patch embedding (a plain fp32 store; 16 tiles
+//     0.306 -> 0.287 ms, packed 8-image batch 0.093 -> 0.097), 42 for the
 //     16-bit down product (4096-deep k: the larger tile's fewer L2 bytes per
 //     flop pay over the long k loop), 50 for the out-projection (1024-deep
 //     k: the one workgroup's residual read-modify-write is not hidden behind
@@ -833,7 +834,7 @@ ResTile res_tile(const GemmArgs& g, long long c_wide, long long c_big) {
 
 hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
-  const ResTile rt = kind == GEMM_PATCH                                 ? res_tile(g, 40, 0)
+  const ResTile rt = kind == GEMM_PATCH                                 ? res_tile(g, 39, 0)
                      : (kind == GEMM_DOWN && g.f16 && g.K >= 2048) ? res_tile(g, 42, 51)
                                                                    : res_tile(g, 50, 0);
   const bool wide = rt == TILE_WIDE;
