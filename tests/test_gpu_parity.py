@@ -301,15 +301,21 @@ def test_bf16_wide_tiles_for_the_hidden_width_products():
     check("out", to_np(c.run()), ref["out"], TOL["bf16"])
 
 
-def test_bf16_down_product_in_256_tiles():
-    """16 images of 448^2 (16,384 patches, D 1024, MLP 4096): the down
-    product takes 256 x 256 tiles (64 rows x 4 columns of tiles, one round
-    of the chip against two of 128 x 128 or 192 x 256), the out-projection
-    and patch embedding 128 x 128 -- the MLP block's output checked in full."""
-    wl = _bf16_small([(448, 448)] * 16, 1)
-    say(f"bf16 down in 256x256 tiles: {wl.n_patches} patches")
+@pytest.mark.parametrize("n_images,tiles", [(16, "256x256"), (11, "384x192")])
+def test_bf16_qkv_and_down_tile_shapes(n_images, tiles):
+    """Images of 448^2 (D 1024, MLP 4096), q,k,v and the MLP block checked in
+    full.  16 images (16,384 patches): q,k,v and down take 256 x 256 tiles
+    (q,k,v 768 tiles in three rounds against 688 tiles of 384 x 192, also
+    three rounds; down 256 tiles, one round against two of 128 x 128 or
+    192 x 256).  11 images (11,264 patches): q,k,v keeps 384 x 192 tiles
+    (480 tiles in two rounds against 528 of 256 x 256 in three)."""
+    wl = _bf16_small([(448, 448)] * n_images, 1)
+    say(f"bf16 q,k,v in {tiles} tiles: {wl.n_patches} patches")
     c = Case(wl)
     ref = c.ref()
+    t = c.stage("qkv", 0)
+    check("qkv[0]", to_np(t), oracle_stage(ref, wl, "qkv", 0, c.w), TOL["bf16"],
+          stored_bf16=True, ulp=storage_ulp(t))
     check("block_out[0]", to_np(c.stage("block_out", 0)), ref["block_out"][0], TOL["bf16"])
     check("out", to_np(c.run()), ref["out"], TOL["bf16"])
 

@@ -789,9 +789,9 @@ hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
 // q,k,v: 384 x 192 tiles (16 per row of tiles) put the 1540 x 1540 image's
 // 32 rows of tiles on the 256 CUs in exactly two rounds (measured 3.5%
 // faster than 256 x 192 in three; on the packed 8-image batch, whose 384-row
-// tiles leave a last round 70% full, 256 x 192 tiles were no faster); the
-// fp8 variant keeps 256 x 192 (its scale blocks are padded for tiles of at
-// most 256 rows)
+// tiles leave a last round 70% full, 256 x 192 tiles were no faster), or
+// 256 x 256 tiles per call (below); the fp8 variant keeps 256 x 192 (its
+// scale blocks are padded for tiles of at most 256 rows)
 #ifndef PV_GEMM_CFG_QKV
 #define PV_GEMM_CFG_QKV 384, 192, 4, 2, 2, 64
 #endif
@@ -818,6 +818,19 @@ hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
 //     tiles of 192 x 256 fill one round); for the out-projection 256 x 256
 //     tiles were slower (packed 8-image batch 0.096 -> 0.107 ms).
 // Ties keep the smaller tile.
+// q,k,v (16-bit): a round of 256 x 256 tiles costs about 0.85 of a round of
+// 384 x 192 tiles (fewer L2 bytes per output; measured on the four
+// workloads), so they are taken when 0.85 x their rounds is below the
+// 384-row rounds: the 16 tiles of 4,096 patches (12 rounds against 11:
+// 0.441 -> 0.415 ms), not 1540^2 (3 against 2: 0.082 -> 0.096 ms) nor the
+// packed 8- and 64-image batches (equal and 1.5% slower).
+bool use_qkv_big(const GemmArgs& g) {
+  if (g.N % 256) return false;
+  const long long r384 = ((g.M + 383) / 384 * (g.N / 192) + kNumCUs - 1) / kNumCUs;
+  const long long r256 = ((g.M + 255) / 256 * (g.N / 256) + kNumCUs - 1) / kNumCUs;
+  return r256 * 17 < r384 * 20;
+}
+
 enum ResTile { TILE_RES, TILE_WIDE, TILE_BIG };
 ResTile res_tile(const GemmArgs& g, long long c_wide, long long c_big) {
   if (g.N % 256) return TILE_RES;
@@ -843,8 +856,9 @@ hipError_t gemm_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
       return wide ? launch_dense<PV_GEMM_CFG_RES_WIDE, A_DENSE, B_ONE, E_STORE_F32>(g, s)
                   : launch_dense<PV_GEMM_CFG_RES, A_DENSE, B_ONE, E_STORE_F32>(g, s);
     case GEMM_QKV:
-      return g.k8 > 0 ? launch_dense<PV_GEMM_CFG_QKV8, A_DENSE, B_QKV, E_QKV_ROPE, 8>(g, s)
-                      : launch_dense<PV_GEMM_CFG_QKV, A_DENSE, B_QKV, E_QKV_ROPE>(g, s);
+      if (g.k8 > 0) return launch_dense<PV_GEMM_CFG_QKV8, A_DENSE, B_QKV, E_QKV_ROPE, 8>(g, s);
+      return use_qkv_big(g) ? launch_dense<PV_GEMM_CFG_BIG, A_DENSE, B_QKV, E_QKV_ROPE>(g, s)
+                            : launch_dense<PV_GEMM_CFG_QKV, A_DENSE, B_QKV, E_QKV_ROPE>(g, s);
     case GEMM_OPROJ:
     case GEMM_DOWN:
       if (g.f16) {
