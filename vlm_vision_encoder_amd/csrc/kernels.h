@@ -59,6 +59,7 @@ struct AttnArgs {
   int32_t hidden;
   int32_t online_max;  // 1: always use the running-max softmax (bf16 path)
   int32_t q_tile;      // queries per work item (bf16: kAttnQTileBf16 or kAttnQTileBf16Wide)
+  int32_t head_major;  // bf16: 1 when every image has the same length (work order below)
 };
 hipError_t attention_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t attention_f32(const AttnArgs& a, hipStream_t s);

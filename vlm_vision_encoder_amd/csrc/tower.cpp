@@ -375,6 +375,9 @@ pv_status run_tower(pv_tower* t, const PixelSource& px, const pv::Plan& plan, vo
   at.hidden = D;
   at.online_max = (c.flags & PV_FLAG_ATTN_ONLINE_MAX) ? 1 : 0;
   at.q_tile = plan.q_tile;
+  at.head_major = 1;
+  for (size_t i = 1; i + 1 < plan.cu.size(); ++i)
+    if (plan.cu[i + 1] - plan.cu[i] != plan.cu[1] - plan.cu[0]) at.head_major = 0;
 
   for (int l = 0; l < c.layers; ++l) {
     const pv_layer_weights& lw = t->layers[l];
