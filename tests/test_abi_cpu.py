@@ -143,6 +143,10 @@ def test_plan_attention_item_size(tower_handle):
     assert q_tile([(224, 224)]) == 256
     # 1,944 patches: fill 0.375 against 0.25, but 2,304 padded queries against 2,048
     assert q_tile([(252, 1512)]) == 256
+    # 17 images of 448^2 (the GPU test of the head-by-head order over two
+    # chunks): 1,088 items fill 0.71 of three rounds of 512, 816 fill 0.80
+    # of four rounds of 256, but 19,584 padded queries against 17,408
+    assert q_tile([(448, 448)] * 17) == 256
     # a subset of the images may choose the other size; the workspace of the
     # subset never exceeds that of the whole set (the embeddings cache
     # forwards the missed subset inside the whole set's workspace)

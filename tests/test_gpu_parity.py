@@ -320,6 +320,20 @@ def test_bf16_qkv_and_down_tile_shapes(n_images, tiles):
     check("out", to_np(c.run()), ref["out"], TOL["bf16"])
 
 
+def test_bf16_attention_head_by_head_order_across_chunks():
+    """17 images of 448^2, all one length: 68 attention items of 256 queries
+    per head, so each XCD walks a full chunk of 64 items head by head and
+    then a last chunk of 4 -- the attention stage checked in full, per
+    image."""
+    wl = _bf16_small([(448, 448)] * 17, 1)
+    say(f"bf16 attention head by head over chunks: {wl.n_patches} patches")
+    c = Case(wl)
+    ref = c.ref()
+    got = to_np(c.stage("attn", 0))
+    want = oracle_stage(ref, wl, "attn", 0, c.w)
+    check_per_image("attn[0]", got, want, ref["maps"]["cu_seqlens"], TOL["bf16"], stored_bf16=True)
+
+
 @pytest.mark.parametrize("hidden,heads,mlp", [(512, 8, 1024), (768, 12, 2048), (1536, 24, 3072), (2048, 32, 2048)])
 def test_bf16_other_widths(hidden, heads, mlp):
     """The other supported widths (norm kernels of 2, 3, 6, 8 row chunks; q,k,v
