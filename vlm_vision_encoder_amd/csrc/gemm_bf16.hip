@@ -799,6 +799,19 @@ hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
 #define PV_GEMM_CFG_QKV8 256, 192, 4, 2, 2, 64
 #endif
 
+// q,k,v (16-bit): a round of 256 x 256 tiles costs about 0.85 of a round of
+// 384 x 192 tiles (fewer L2 bytes per output; measured on the four
+// workloads), so they are taken when 0.85 x their rounds is below the
+// 384-row rounds: the 16 tiles of 4,096 patches (12 rounds against 11:
+// 0.441 -> 0.415 ms), not 1540^2 (3 against 2: 0.082 -> 0.096 ms) nor the
+// packed 8- and 64-image batches (equal and 1.5% slower).
+bool use_qkv_big(const GemmArgs& g) {
+  if (g.N % 256) return false;
+  const long long r384 = ((g.M + 383) / 384 * (g.N / 192) + kNumCUs - 1) / kNumCUs;
+  const long long r256 = ((g.M + 255) / 256 * (g.N / 256) + kNumCUs - 1) / kNumCUs;
+  return r256 * 17 < r384 * 20;
+}
+
 // N = hidden products (out-projection, down, patch embedding): 128 x 128
 // tiles (two workgroups per CU), 192 x 256 (one per CU) or, for the 16-bit
 // down product, 256 x 256 (one per CU), whichever needs the fewest rounds
@@ -818,19 +831,6 @@ hipError_t launch_dense(const GemmArgs& g, hipStream_t s) {
 //     tiles of 192 x 256 fill one round); for the out-projection 256 x 256
 //     tiles were slower (packed 8-image batch 0.096 -> 0.107 ms).
 // Ties keep the smaller tile.
-// q,k,v (16-bit): a round of 256 x 256 tiles costs about 0.85 of a round of
-// 384 x 192 tiles (fewer L2 bytes per output; measured on the four
-// workloads), so they are taken when 0.85 x their rounds is below the
-// 384-row rounds: the 16 tiles of 4,096 patches (12 rounds against 11:
-// 0.441 -> 0.415 ms), not 1540^2 (3 against 2: 0.082 -> 0.096 ms) nor the
-// packed 8- and 64-image batches (equal and 1.5% slower).
-bool use_qkv_big(const GemmArgs& g) {
-  if (g.N % 256) return false;
-  const long long r384 = ((g.M + 383) / 384 * (g.N / 192) + kNumCUs - 1) / kNumCUs;
-  const long long r256 = ((g.M + 255) / 256 * (g.N / 256) + kNumCUs - 1) / kNumCUs;
-  return r256 * 17 < r384 * 20;
-}
-
 enum ResTile { TILE_RES, TILE_WIDE, TILE_BIG };
 ResTile res_tile(const GemmArgs& g, long long c_wide, long long c_big) {
   if (g.N % 256) return TILE_RES;
