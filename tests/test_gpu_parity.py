@@ -220,6 +220,13 @@ def test_bf16_packed_ragged_batch():
     ref = c.ref()
     check("out", to_np(c.run()), ref["out"], TOL["bf16"])
     check("block_out[2]", to_np(c.stage("block_out", 2)), ref["block_out"][2], TOL["bf16"])
+    # q,k,v of blocks 1 and 2 (inputs from the down products and norms
+    # before them), every image of the ragged pack, with rows of the last
+    # tile past the end
+    for layer in (1, 2):
+        t = c.stage("qkv", layer)
+        check_per_image(f"qkv[{layer}]", to_np(t), oracle_stage(ref, wl, "qkv", layer, c.w),
+                        ref["maps"]["cu_seqlens"], TOL["bf16"], stored_bf16=True)
     # the same tower writing an fp32 output buffer: no storage rounding
     import torch
     tw = T.Tower(T.config_for(wl, out_dtype="f32"), c.dev_w)
